@@ -1,0 +1,321 @@
+"""Seeded synthetic workloads for the neuron-aware sparse FFN.
+
+Input generation only: weights, biases, inputs, neuron tables and the
+stand-in cold partial.  None of the method's arithmetic lives here.  Both the
+oracle (host arrays) and the HIP path (device buffers) take their inputs from
+this module; element values come from ``synth_rng.h``, compiled for the host
+(``libsynth.so``) and for the device (``libsynth_gpu.so``), so a tensor
+generated on either side has the same bits.
+
+Workload recipe (the pages give no weights or prompts; these stand in):
+  * every weight row ~ Irwin-Hall(4) scaled to std 1/sqrt(fan_in); inputs x
+    the same with std 1 (fresh per step, layer and batch row);
+  * per-layer activation probabilities p_i = min(0.95, c * rank_i^-alpha)
+    over a seeded random permutation (power-law hotness), with c solved so
+    that mean(p) equals the layer's target density;
+  * FC1 bias b1_i = Phi^-1(p_i): with unit-variance inputs and rows of unit
+    expected norm, P(W1_i.x + b1_i > 0) = p_i;
+  * predictor: P1 ~ std 1/sqrt(d), P2 ~ std 1/sqrt(H), c1 = 0 and c2 chosen
+    from each P2 row's stored sum and sum of squares so that the predicted
+    marginals follow the same p_i;
+  * the GPU neuron table holds all neurons, or (OPT-30B shape) the 40% with
+    the highest simulated profiling counts, Binomial(256, p_i) draws, ties to
+    the lower id, ascending; the CPU table is the ascending complement.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import functools
+import math
+import os
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+
+F32, F16, I4G128 = 0, 1, 2
+TAG_P1, TAG_P2, TAG_W1, TAG_W2, TAG_WUP, TAG_X, TAG_YC, TAG_PERM, TAG_PROF, TAG_LAYER = range(1, 11)
+P_CAP = 0.95
+SQRT3 = math.sqrt(3.0)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_HOST_LIB = os.path.join(_HERE, "libsynth.so")
+_GPU_LIB = os.path.join(_HERE, "libsynth_gpu.so")
+
+
+def value_scale(sigma: float) -> float:
+    """Multiplier from the Irwin-Hall(4) integer to a value of std sigma."""
+    return SQRT3 * sigma / 65536.0
+
+
+def build_host() -> str:
+    import subprocess
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared", "-Wall",
+                    "-o", _HOST_LIB, os.path.join(_HERE, "synth_host.c"), "-lm"], check=True)
+    return _HOST_LIB
+
+
+def build_gpu_cmd() -> list:
+    return ["hipcc", "--offload-arch=gfx950", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-o", _GPU_LIB, os.path.join(_HERE, "synth_gpu.hip")]
+
+
+_host = None
+_gpu = None
+
+
+def host_lib():
+    global _host
+    if _host is None:
+        if not os.path.exists(_HOST_LIB):
+            build_host()
+        L = C.CDLL(_HOST_LIB)
+        P, I64, U64, U32 = C.c_void_p, C.c_int64, C.c_uint64, C.c_uint32
+        L.sx_fill_rows.argtypes = [P, P, C.c_int, U64, U32, U32, P, I64, I64, I64, C.c_double]
+        L.sx_row_stats.argtypes = [P, P, C.c_int, U64, U32, U32, I64, I64, I64, C.c_double]
+        L.sx_perm.argtypes = [U64, U32, U32, C.c_int32, P]
+        L.sx_profile_counts.argtypes = [U64, U32, C.c_int32, P, C.c_int32, P]
+        L.sx_f16_bits.argtypes = [C.c_double]
+        L.sx_f16_bits.restype = C.c_uint16
+        L.sx_f16_value.argtypes = [C.c_uint16]
+        L.sx_f16_value.restype = C.c_double
+        L.sx_ih4_at.argtypes = [U64, U32, U32, U64, U64]
+        L.sx_ih4_at.restype = C.c_int32
+        _host = L
+    return _host
+
+
+def gpu_lib():
+    global _gpu
+    if _gpu is None:
+        if not os.path.exists(_GPU_LIB):
+            raise RuntimeError(f"{_GPU_LIB} is not built; run __graft_entry__.build()")
+        L = C.CDLL(_GPU_LIB)
+        P, I64, U64, U32 = C.c_void_p, C.c_int64, C.c_uint64, C.c_uint32
+        L.sxg_fill_rows.argtypes = [P, P, C.c_int, U64, U32, U32, P, I64, I64, I64, C.c_double, P]
+        L.sxg_fill_rows.restype = C.c_int
+        _gpu = L
+    return _gpu
+
+
+# ----------------------------------------------------------------------------- configs
+
+@dataclass(frozen=True)
+class Config:
+    key: str
+    desc: str
+    n_layers: int
+    d: int
+    N: int
+    wdtype: int                 # FFN weights
+    pdtype: int                 # predictor weights
+    bdtype: int                 # b1, c1, c2
+    gated: bool
+    density: Tuple[float, float]  # per-layer density drawn uniformly in [lo, hi]
+    alpha: float
+    H: Tuple[int, int]          # predictor hidden size, interpolated with the density
+    gpu_frac: float             # fraction of neurons in the GPU table
+    batches: Tuple[int, ...]
+    steps: int
+    seed: int
+    prof_tokens: int = 256
+
+    def rho(self, layer: int) -> float:
+        lo, hi = self.density
+        if lo == hi:
+            return lo
+        h = host_lib()
+        u = (h.sx_ih4_at(self.seed, TAG_LAYER, layer, 0, 0) + 131070) / 262140.0
+        return lo + (hi - lo) * u
+
+    def hidden(self, layer: int) -> int:
+        lo, hi = self.H
+        if lo == hi:
+            return lo
+        dlo, dhi = self.density
+        t = (self.rho(layer) - dlo) / (dhi - dlo)
+        return int(round((lo + t * (hi - lo)) / 64.0)) * 64
+
+
+CONFIGS = {
+    "opt-768": Config("opt-768", "single OPT-style ReLU FFN layer, fp32, d=768, N=3072",
+                      1, 768, 3072, F32, F32, F32, False, (0.10, 0.10), 1.1, (128, 128), 1.0, (1,), 64, 1),
+    "opt-6.7b": Config("opt-6.7b", "OPT-6.7B-shaped FFN stack, 32 layers, 4096/16384, fp16",
+                       32, 4096, 16384, F16, F16, F16, False, (0.10, 0.10), 1.1, (1024, 1024), 1.0, (1,), 128, 2),
+    "llama-13b-gated": Config("llama-13b-gated", "LLaMA-13B-shaped ReLU gated FFN, 40 layers, 5120/13824, fp16",
+                              40, 5120, 13824, F16, F16, F16, True, (0.08, 0.25), 1.1, (512, 1120), 1.0, (1,), 64, 3),
+    "opt-30b": Config("opt-30b", "OPT-30B-shaped FFN stack, 48 layers, 7168/28672, fp16, 40% of neurons on the GPU",
+                      48, 7168, 28672, F16, F16, F16, False, (0.10, 0.10), 1.1, (1024, 1024), 0.4, (1, 4, 16, 32), 64, 4),
+    "opt-175b-int4": Config("opt-175b-int4", "OPT-175B-shaped FFN stack, 96 layers, 12288/49152, int4 group 128",
+                            96, 12288, 49152, I4G128, F16, F16, False, (0.05, 0.10), 1.2, (1024, 4096), 1.0, (1,), 64, 5),
+}
+
+
+def small_config(key="tiny", d=256, N=1024, H=64, wdtype=F16, pdtype=F16, bdtype=F16, gated=False,
+                 rho=0.1, alpha=1.1, gpu_frac=1.0, n_layers=1, seed=11) -> Config:
+    """A reduced shape with the same construction, for parity tests."""
+    return Config(key, f"reduced {d}/{N}", n_layers, d, N, wdtype, pdtype, bdtype, gated, (rho, rho), alpha,
+                  (H, H), gpu_frac, (1,), 4, seed)
+
+
+# ----------------------------------------------------------------------------- per-neuron vectors
+
+def solve_scale(N: int, rho: float, alpha: float, cap: float = P_CAP) -> float:
+    """c such that mean_r min(cap, c r^-alpha) = rho over r = 1..N (bisection)."""
+    r = np.arange(1, N + 1, dtype=np.float64) ** (-alpha)
+    lo, hi = 1e-12, 1e12
+    for _ in range(200):
+        mid = math.sqrt(lo * hi)
+        if np.minimum(cap, mid * r).mean() < rho:
+            lo = mid
+        else:
+            hi = mid
+    return math.sqrt(lo * hi)
+
+
+def permutation(seed: int, layer: int, n: int) -> np.ndarray:
+    out = np.empty(n, np.int32)
+    host_lib().sx_perm(seed, TAG_PERM, layer, n, out.ctypes.data)
+    return out
+
+
+def ndtri(p: np.ndarray) -> np.ndarray:
+    from scipy.special import ndtri as _ndtri
+    return _ndtri(p)
+
+
+def to_stored(v: np.ndarray, dtype: int) -> np.ndarray:
+    """float64 vector -> stored float32 or fp16 bits (uint16), round to nearest even."""
+    if dtype == F32:
+        return v.astype(np.float32)
+    return v.astype(np.float16).view(np.uint16)
+
+
+def stored_to_f64(v: np.ndarray, dtype: int) -> np.ndarray:
+    return v.astype(np.float64) if dtype == F32 else v.view(np.float16).astype(np.float64)
+
+
+def row_stats(dtype: int, seed: int, tag: int, layer: int, rows: int, cols: int, sigma: float):
+    s1 = np.empty(rows, np.float64)
+    s2 = np.empty(rows, np.float64)
+    host_lib().sx_row_stats(s1.ctypes.data, s2.ctypes.data, dtype, seed, tag, layer, 0, rows, cols, value_scale(sigma))
+    return s1, s2
+
+
+@dataclass
+class LayerSpec:
+    cfg: Config
+    layer: int
+    rho: float
+    H: int
+    c: float
+    p: np.ndarray               # activation probability per original neuron id
+    b1: np.ndarray              # stored, per original id
+    c2: np.ndarray              # stored, per original id
+    T_g: np.ndarray             # int32 ascending
+    T_c: np.ndarray             # int32 ascending complement
+    counts: Optional[np.ndarray] = None
+
+    @property
+    def d(self):
+        return self.cfg.d
+
+    @property
+    def N(self):
+        return self.cfg.N
+
+    @property
+    def n_g(self):
+        return len(self.T_g)
+
+    def sigmas(self):
+        return {TAG_P1: 1 / math.sqrt(self.d), TAG_P2: 1 / math.sqrt(self.H), TAG_W1: 1 / math.sqrt(self.d),
+                TAG_WUP: 1 / math.sqrt(self.d), TAG_W2: 1 / math.sqrt(self.N), TAG_X: 1.0}
+
+
+def _table(cfg: Config, layer: int, p: np.ndarray):
+    N = cfg.N
+    if cfg.gpu_frac >= 1.0:
+        return np.arange(N, dtype=np.int32), np.zeros(0, np.int32), None
+    counts = np.empty(N, np.int32)
+    host_lib().sx_profile_counts(cfg.seed, layer, N, np.ascontiguousarray(p).ctypes.data, cfg.prof_tokens,
+                                 counts.ctypes.data)
+    n_g = int(math.floor(cfg.gpu_frac * N))
+    order = np.lexsort((np.arange(N), -counts))      # count descending, then id ascending
+    T_g = np.sort(order[:n_g]).astype(np.int32)
+    mask = np.zeros(N, bool)
+    mask[T_g] = True
+    T_c = np.flatnonzero(~mask).astype(np.int32)
+    return T_g, T_c, counts
+
+
+@functools.lru_cache(maxsize=256)
+def layer_spec(cfg: Config, layer: int) -> LayerSpec:
+    N, d = cfg.N, cfg.d
+    rho = cfg.rho(layer)
+    H = cfg.hidden(layer)
+    c = solve_scale(N, rho, cfg.alpha)
+    rank = permutation(cfg.seed, layer, N).astype(np.float64) + 1.0
+    p = np.minimum(P_CAP, c * rank ** (-cfg.alpha))
+    b1 = to_stored(ndtri(p), cfg.bdtype)
+    # predictor output bias from the stored P2 rows:  g_i = P2_i . ReLU(P1 x) has
+    # mean E[h] * sum_m P2[i,m] and variance Var(h) * sum_m P2[i,m]^2 with
+    # h = ReLU(N(0,1)):  E[h] = 1/sqrt(2 pi), Var(h) = 1/2 - 1/(2 pi).
+    s1, s2 = row_stats(cfg.pdtype if cfg.pdtype != I4G128 else F16, cfg.seed, TAG_P2, layer, N, H, 1 / math.sqrt(H))
+    mu = s1 / math.sqrt(2 * math.pi)
+    sd = np.sqrt(s2 * (0.5 - 1 / (2 * math.pi)))
+    c2 = to_stored(sd * ndtri(p) - mu, cfg.bdtype)
+    T_g, T_c, counts = _table(cfg, layer, p)
+    return LayerSpec(cfg, layer, rho, H, c, p, b1, c2, T_g, T_c, counts)
+
+
+# ----------------------------------------------------------------------------- host tensors
+
+def host_rows(dtype: int, seed: int, tag: int, layer: int, cols: int, sigma: float,
+              row_ids: Optional[np.ndarray] = None, row0: int = 0, nrows: Optional[int] = None):
+    """Generate rows on the host.  Returns (data, scales): float32 [n, cols],
+    uint16 fp16 bits [n, cols], or uint8 [n, cols/2] + uint16 scales [n, cols/128]."""
+    if row_ids is not None:
+        row_ids = np.ascontiguousarray(row_ids, dtype=np.int32)
+        n = len(row_ids)
+    else:
+        n = int(nrows)
+    if dtype == F32:
+        data = np.empty((n, cols), np.float32)
+    elif dtype == F16:
+        data = np.empty((n, cols), np.uint16)
+    else:
+        data = np.empty((n, cols // 2), np.uint8)
+    scales = np.empty((n, cols // 128), np.uint16) if dtype == I4G128 else None
+    if n:
+        host_lib().sx_fill_rows(data.ctypes.data, scales.ctypes.data if scales is not None else None, dtype, seed, tag,
+                                layer, row_ids.ctypes.data if row_ids is not None else None, row0, n, cols,
+                                value_scale(sigma))
+    return data, scales
+
+
+def x_row_ids(step: int, B: int) -> np.ndarray:
+    return (np.arange(B, dtype=np.int64) + step * 1024).astype(np.int32)
+
+
+def host_x(cfg_seed: int, layer: int, step: int, B: int, d: int) -> np.ndarray:
+    data, _ = host_rows(F32, cfg_seed, TAG_X, layer, d, 1.0, row_ids=x_row_ids(step, B))
+    return data
+
+
+def host_yc(cfg_seed: int, layer: int, step: int, B: int, d: int, sigma: float = 0.05) -> np.ndarray:
+    """Stand-in cold partial for timing runs (the parity tests use the oracle's)."""
+    data, _ = host_rows(F32, cfg_seed, TAG_YC, layer, d, sigma, row_ids=x_row_ids(step, B))
+    return data
+
+
+# ----------------------------------------------------------------------------- device fill
+
+def dev_fill(ptr: int, scales_ptr: Optional[int], dtype: int, seed: int, tag: int, layer: int, cols: int,
+             sigma: float, row_ids_ptr: Optional[int] = None, row0: int = 0, nrows: int = 0, stream: int = 0):
+    """Generate rows straight into device memory (same bits as host_rows)."""
+    rc = gpu_lib().sxg_fill_rows(ptr, scales_ptr, dtype, seed, tag, layer, row_ids_ptr, row0, nrows, cols,
+                                 value_scale(sigma), stream)
+    if rc != 0:
+        raise RuntimeError(f"sxg_fill_rows failed with code {rc}")
