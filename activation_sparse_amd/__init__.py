@@ -1,0 +1,145 @@
+"""Python binding of libpi, the gfx950 neuron-aware sparse FFN.
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libpi.so`` (declared in ``include/pi.h``).  Tensors are torch device
+tensors; torch supplies memory and streams and nothing else.  The binding
+raises :class:`PiError` if the library is missing or a call fails; there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+PI_F32, PI_F16, PI_I4G128 = 0, 1, 2
+PI_RELU, PI_GATED_RELU = 0, 1
+PI_OK, PI_EINVAL, PI_EWORKSPACE, PI_EUNSUPPORTED, PI_EHIP = 0, 1, 2, 3, 4
+PI_OP_PREDICT, PI_OP_COMPACT, PI_OP_SPARSE_FFN, PI_OP_MERGE = 0, 1, 2, 3
+PI_MAX_BATCH = 32
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpi.so")
+
+EXPORTS = ("pi_predict", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_workspace_bytes",
+           "pi_status_string", "pi_last_hip_error", "pi_abi_version")
+
+
+class PiError(RuntimeError):
+    pass
+
+
+class _Mat(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("scales", C.c_void_p), ("dtype", C.c_int32)]
+
+
+class _Vec(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("dtype", C.c_int32)]
+
+
+_lib = None
+
+
+def load():
+    """Load libpi.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise PiError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        P, I = C.c_void_p, C.c_int32
+        L.pi_predict.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Vec, P, P, C.c_size_t]
+        L.pi_compact.argtypes = [P, I, I, P, C.c_float, P, I, P, P, P, I, P, P, P, C.c_size_t]
+        L.pi_sparse_ffn.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Mat, P, P, P, P, C.c_size_t]
+        L.pi_merge.argtypes = [P, I, I, P, P, P, _Vec]
+        L.pi_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        L.pi_workspace_bytes.restype = C.c_size_t
+        L.pi_status_string.argtypes = [I]
+        L.pi_status_string.restype = C.c_char_p
+        L.pi_last_hip_error.restype = I
+        L.pi_abi_version.restype = I
+        for name in ("pi_predict", "pi_compact", "pi_sparse_ffn", "pi_merge"):
+            getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+@dataclass
+class Matrix:
+    """Device weights: float32 / float16 tensor [rows, cols], or uint8 packed
+    int4 [rows, cols/2] with int16 fp16-bit scales [rows, cols/128]."""
+    data: object
+    dtype: int
+    scales: object = None
+
+    def _c(self) -> _Mat:
+        return _Mat(_ptr(self.data), _ptr(self.scales), self.dtype)
+
+
+@dataclass
+class Vector:
+    """Device bias, float32 or float16 (fp16 bits); ``data=None`` = zero."""
+    data: object = None
+    dtype: int = PI_F32
+
+    def _c(self) -> _Vec:
+        return _Vec(_ptr(self.data), self.dtype)
+
+
+_NO_MAT = Matrix(None, PI_F16)
+_NO_VEC = Vector(None, PI_F32)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str) -> None:
+    if status != PI_OK:
+        L = load()
+        msg = L.pi_status_string(status).decode()
+        if status == PI_EHIP:
+            msg += f" (hipError {L.pi_last_hip_error()})"
+        raise PiError(f"{what}: {msg}")
+
+
+def pi_workspace_bytes(op: int, B: int, d: int, H: int = 0, N: int = 0, n_g: int = 0) -> int:
+    return int(load().pi_workspace_bytes(op, B, d, H, N, n_g))
+
+
+def pi_predict(B, d, H, N, x, P1: Matrix, c1: Vector, P2: Matrix, c2: Vector, logits, ws, ws_bytes=None,
+               stream=None) -> None:
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(load().pi_predict(_stream(stream), B, d, H, N, _ptr(x), P1._c(), (c1 or _NO_VEC)._c(), P2._c(),
+                             (c2 or _NO_VEC)._c(), _ptr(logits), _ptr(ws), nbytes), "pi_predict")
+
+
+def pi_compact(B, N, logits, tau, T_g, n_g, A_g, K, T_c=None, n_c=0, A_c=None, K_c=None, stream=None) -> None:
+    _check(load().pi_compact(_stream(stream), B, N, _ptr(logits), float(tau), _ptr(T_g), n_g, _ptr(A_g), _ptr(K),
+                             _ptr(T_c), n_c, _ptr(A_c), _ptr(K_c), None, 0), "pi_compact")
+
+
+def pi_sparse_ffn(B, d, n_g, kind, x, W1: Matrix, b1: Vector, Wup: Optional[Matrix], W2: Matrix, A_g, K, y_g, ws,
+                  ws_bytes=None, stream=None) -> None:
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    _check(load().pi_sparse_ffn(_stream(stream), B, d, n_g, kind, _ptr(x), W1._c(), (b1 or _NO_VEC)._c(),
+                                (Wup or _NO_MAT)._c(), W2._c(), _ptr(A_g), _ptr(K), _ptr(y_g), _ptr(ws), nbytes),
+           "pi_sparse_ffn")
+
+
+def pi_merge(B, d, y, y_c=None, K_c=None, b2: Optional[Vector] = None, stream=None) -> None:
+    _check(load().pi_merge(_stream(stream), B, d, _ptr(y), _ptr(y_c), _ptr(K_c), (b2 or _NO_VEC)._c()), "pi_merge")

@@ -1,0 +1,360 @@
+// pi_kernels.hip - the libpi kernels for gfx950 (wave64).
+//
+//  k_rowdot  : row-dot GEMV over dense rows (predictor layers) or over the
+//              rows listed in the active list (FC1), fused bias + ReLU (and
+//              the gate * up product of a gated FFN).  One wave per row, 16-B
+//              loads along the row, fp32 accumulate, x staged in LDS.
+//  k_compact : threshold + union over the batch + wave ballot + block prefix
+//              sum -> ascending slot list and its count (stays on device).
+//  k_fc2     : neuron-major axpy.  Grid = (column tile, row chunk); each block
+//              writes one partial per (chunk, batch row, column) and the last
+//              block of a column tile sums the partials in chunk order, so the
+//              result does not depend on block timing (no float atomics).
+//  k_merge   : y += y_c (+ b2), skipped on the device when no cold neuron is
+//              active.
+#include "pi_device.h"
+#include "pi_internal.h"
+
+namespace pi {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kXsMaxBytes = 64 * 1024;
+
+template <int DT, int NB, bool GATED>
+__global__ __launch_bounds__(kThreads) void k_rowdot(RowdotArgs a, int64_t n_rows, int stage_x,
+                                                      uint32_t* zero_ptr, int zero_n) {
+  constexpr int E = Fmt<DT>::E;
+  extern __shared__ float xs[];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  if (zero_ptr && blockIdx.x == 0)
+    for (int t = tid; t < zero_n; t += kThreads) zero_ptr[t] = 0u;
+  const int64_t cols = a.cols;
+  const int B = a.B;
+  const float* xp = a.x;
+  if (stage_x) {
+    const int64_t n4 = (int64_t)B * cols / 4;
+    const float4v* src = reinterpret_cast<const float4v*>(a.x);
+    float4v* dst = reinterpret_cast<float4v*>(xs);
+    for (int64_t t = tid; t < n4; t += kThreads) dst[t] = src[t];
+    __syncthreads();
+    xp = xs;
+  }
+  int64_t count = a.count_max;
+  if (a.list) {
+    int64_t kd = *a.count_dev;
+    count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
+  }
+  const int64_t rb = row_bytes(DT, cols);
+  const int nvec = (int)(rb / 16);
+  const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const int64_t nw = (int64_t)gridDim.x * kWavesPerBlock;
+  const int64_t groups = cols / 128;
+  for (int64_t j = gw; j < count; j += nw) {
+    const int64_t row = a.list ? (int64_t)a.list[j] : j;
+    float acc[NB], acc2[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) { acc[b] = 0.f; acc2[b] = 0.f; }
+    const bool row_ok = row >= 0 && row < n_rows;
+    if (row_ok) {
+      const char* rp = reinterpret_cast<const char*>(a.W) + row * rb;
+      const char* up = GATED ? reinterpret_cast<const char*>(a.Wup) + row * rb : nullptr;
+#pragma unroll 4
+      for (int v = lane; v < nvec; v += kWave) {
+        float wf[E], uf[E];
+        float sc = 1.f, scu = 1.f;
+        if constexpr (DT == 2) {
+          sc = h2f(a.Ws[row * groups + v / 4]);
+          if constexpr (GATED) scu = h2f(a.Wups[row * groups + v / 4]);
+        }
+        widen<DT>(ld16(rp + (int64_t)v * 16), sc, wf);
+        if constexpr (GATED) widen<DT>(ld16(up + (int64_t)v * 16), scu, uf);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if (b < B) {
+            const float* xb = xp + (int64_t)b * cols + (int64_t)v * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              acc[b] = fmaf(wf[e], xb[e], acc[b]);
+              if constexpr (GATED) acc2[b] = fmaf(uf[e], xb[e], acc2[b]);
+            }
+          }
+        }
+      }
+    }
+    const float bias = row_ok ? load_bias(a.bias, a.bias_dt, row) : 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < B) {
+        float z = wave_sum(acc[b]) + bias;
+        if (a.relu) z = z > 0.f ? z : 0.f;
+        if constexpr (GATED) z *= wave_sum(acc2[b]);
+        if (!row_ok) z = 0.f;
+        if (lane == 0) a.out[(int64_t)b * a.out_stride + j] = z;
+      }
+    }
+  }
+}
+
+constexpr int kCompactThreads = 1024;
+constexpr int kCompactWaves = kCompactThreads / kWave;   // 16
+constexpr int kCompactChunks = 64;                       // slots per pass: 64 * 1024
+
+__global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const float* __restrict__ logits,
+                                                             float tau, const int32_t* T_g, int n_g,
+                                                             int32_t* A_g, int32_t* K_g, const int32_t* T_c,
+                                                             int n_c, int32_t* A_c, int32_t* K_c) {
+  const int32_t* T = blockIdx.x == 0 ? T_g : T_c;
+  const int n = blockIdx.x == 0 ? n_g : n_c;
+  int32_t* A = blockIdx.x == 0 ? A_g : A_c;
+  int32_t* Kout = blockIdx.x == 0 ? K_g : K_c;
+  __shared__ int cnt[kCompactChunks * kCompactWaves];
+  __shared__ int wtot[kCompactWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int base = 0;
+  for (int s0 = 0; s0 < n; s0 += kCompactChunks * kCompactThreads) {
+    const int nch = min(kCompactChunks, (n - s0 + kCompactThreads - 1) / kCompactThreads);
+    int ids[kCompactChunks];
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      const int s = s0 + c * kCompactThreads + tid;
+      ids[c] = (c < nch && s < n) ? T[s] : -1;
+    }
+    uint64_t flags = 0;
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      bool f = false;
+      if (c < nch) {
+        const int id = ids[c];
+        if (id >= 0 && id < N)
+          for (int b = 0; b < B; ++b) f = f || (logits[(int64_t)b * N + id] > tau);
+        const uint64_t bal = __ballot(f);
+        if (lane == 0) cnt[c * kCompactWaves + wv] = __popcll(bal);
+      }
+      flags |= (uint64_t)f << c;
+    }
+    __syncthreads();
+    // exclusive scan of cnt[0 .. nch*16) in (chunk, wave) order, one entry per thread
+    const int nent = nch * kCompactWaves;
+    const int v = tid < nent ? cnt[tid] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    if (lane == kWave - 1) wtot[wv] = incl;
+    __syncthreads();
+    int wpre = 0, total = 0;
+    for (int w = 0; w < kCompactWaves; ++w) {
+      const int t = wtot[w];
+      if (w < wv) wpre += t;
+      total += t;
+    }
+    __syncthreads();
+    if (tid < nent) cnt[tid] = wpre + incl - v;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      if (c < nch) {
+        const bool f = (flags >> c) & 1ull;
+        const uint64_t bal = __ballot(f);
+        if (f) A[base + cnt[c * kCompactWaves + wv] + __popcll(bal & lt_mask)] = s0 + c * kCompactThreads + tid;
+      }
+    }
+    base += total;
+    __syncthreads();
+  }
+  if (tid == 0) *Kout = base;
+}
+
+template <int DT, int NBG>
+__global__ __launch_bounds__(kThreads) void k_fc2(Fc2Args a) {
+  constexpr int E = Fmt<DT>::E;
+  __shared__ float red[kWavesPerBlock][kWave * E];
+  __shared__ int last_flag;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tile = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
+  const int64_t d = a.d;
+  const int64_t rb = row_bytes(DT, d);
+  const int nvec = (int)(rb / 16);
+  const int v = tile * kWave + lane;
+  const bool vok = v < nvec;
+  const int64_t groups = d / 128;
+  int64_t K = *a.K;
+  K = K < 0 ? 0 : (K > a.n_g ? a.n_g : K);
+  const int64_t j0 = K * chunk / nchunks, j1 = K * (chunk + 1) / nchunks;
+  const int B = a.B;
+  const int64_t tile_col0 = (int64_t)tile * kWave * E;
+  for (int b0 = 0; b0 < B; b0 += NBG) {
+    float acc[NBG][E];
+#pragma unroll
+    for (int b = 0; b < NBG; ++b)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[b][e] = 0.f;
+    for (int64_t j = j0 + wave; j < j1; j += kWavesPerBlock) {
+      const int64_t s = a.list[j];
+      if (s < 0 || s >= a.n_g || !vok) continue;
+      float wf[E];
+      float sc = 1.f;
+      if constexpr (DT == 2) sc = h2f(a.W2s[s * groups + v / 4]);
+      widen<DT>(ld16(reinterpret_cast<const char*>(a.W2) + s * rb + (int64_t)v * 16), sc, wf);
+#pragma unroll
+      for (int b = 0; b < NBG; ++b) {
+        if (b0 + b < B) {
+          const float ab = a.a[(int64_t)(b0 + b) * a.n_g + j];
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc[b][e] = fmaf(ab, wf[e], acc[b][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NBG; ++b) {
+      if (b0 + b < B) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) red[wave][lane * E + e] = acc[b][e];
+        __syncthreads();
+        float* dst = a.partials + ((int64_t)chunk * B + b0 + b) * d + tile_col0;
+        for (int t = tid; t < kWave * E; t += kThreads) {
+          if (tile_col0 + t < d) {
+            float sum = red[0][t];
+#pragma unroll
+            for (int w = 1; w < kWavesPerBlock; ++w) sum += red[w][t];
+            dst[t] = sum;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  // The last block to finish this column tile sums the chunk partials in order.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t old = atomicAdd(&a.counters[tile], 1u);
+    last_flag = (old == (uint32_t)(nchunks - 1));
+  }
+  __syncthreads();
+  if (!last_flag) return;
+  __threadfence();
+  for (int b = 0; b < B; ++b) {
+    for (int t = tid; t < kWave * E; t += kThreads) {
+      const int64_t col = tile_col0 + t;
+      if (col < d) {
+        float sum = 0.f;
+        for (int c = 0; c < nchunks; ++c) sum += __builtin_nontemporal_load(a.partials + ((int64_t)c * B + b) * d + col);
+        a.y[(int64_t)b * d + col] = sum;
+      }
+    }
+  }
+  if (tid == 0) a.counters[tile] = 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void k_merge(int64_t n, int d, float* y, const float* y_c,
+                                                    const int32_t* K_c, const void* b2, int b2_dt) {
+  const bool add_c = y_c && (!K_c || *K_c != 0);
+  if (!add_c && !b2) return;
+  for (int64_t t = blockIdx.x * (int64_t)kThreads + threadIdx.x; t < n; t += (int64_t)gridDim.x * kThreads) {
+    float v = y[t];
+    if (add_c) v += y_c[t];
+    if (b2) v += load_bias(b2, b2_dt, t % d);
+    y[t] = v;
+  }
+}
+
+__global__ void k_zero_u32(uint32_t* p, int64_t n) {
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) p[t] = 0u;
+}
+
+template <int DT, bool GATED>
+hipError_t rowdot_dt(const RowdotArgs& a, int64_t n_rows, uint32_t* zero_ptr, int zero_n, hipStream_t s) {
+  const int64_t xbytes = (int64_t)a.B * a.cols * 4;
+  const int stage = xbytes <= kXsMaxBytes;
+  const size_t shm = stage ? (size_t)xbytes : 0;
+  int64_t blocks = (a.count_max + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;
+  dim3 g((unsigned)blocks), t(kThreads);
+  if (a.B <= 1) hipLaunchKernelGGL((k_rowdot<DT, 1, GATED>), g, t, shm, s, a, n_rows, stage, zero_ptr, zero_n);
+  else if (a.B <= 2) hipLaunchKernelGGL((k_rowdot<DT, 2, GATED>), g, t, shm, s, a, n_rows, stage, zero_ptr, zero_n);
+  else if (a.B <= 4) hipLaunchKernelGGL((k_rowdot<DT, 4, GATED>), g, t, shm, s, a, n_rows, stage, zero_ptr, zero_n);
+  else if (a.B <= 8) hipLaunchKernelGGL((k_rowdot<DT, 8, GATED>), g, t, shm, s, a, n_rows, stage, zero_ptr, zero_n);
+  else if (a.B <= 16) hipLaunchKernelGGL((k_rowdot<DT, 16, GATED>), g, t, shm, s, a, n_rows, stage, zero_ptr, zero_n);
+  else hipLaunchKernelGGL((k_rowdot<DT, 32, GATED>), g, t, shm, s, a, n_rows, stage, zero_ptr, zero_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// n_rows: rows in the matrix (bound for listed row ids).  For dense mode it
+// equals count_max.  zero_ptr/zero_n: u32 words block 0 clears first (the FC2
+// tile counters), or NULL.
+hipError_t launch_rowdot_ex(const RowdotArgs& a, int64_t n_rows, uint32_t* zero_ptr, int zero_n, hipStream_t s) {
+  if (a.gated) {
+    switch (a.dt) {
+      case PI_F32: return rowdot_dt<0, true>(a, n_rows, zero_ptr, zero_n, s);
+      case PI_F16: return rowdot_dt<1, true>(a, n_rows, zero_ptr, zero_n, s);
+      default: return rowdot_dt<2, true>(a, n_rows, zero_ptr, zero_n, s);
+    }
+  }
+  switch (a.dt) {
+    case PI_F32: return rowdot_dt<0, false>(a, n_rows, zero_ptr, zero_n, s);
+    case PI_F16: return rowdot_dt<1, false>(a, n_rows, zero_ptr, zero_n, s);
+    default: return rowdot_dt<2, false>(a, n_rows, zero_ptr, zero_n, s);
+  }
+}
+
+hipError_t launch_rowdot(const RowdotArgs& a, hipStream_t s) { return launch_rowdot_ex(a, a.count_max, nullptr, 0, s); }
+
+hipError_t launch_compact(int B, int N, const float* logits, float tau, const int32_t* T_g, int n_g,
+                          int32_t* A_g, int32_t* K, const int32_t* T_c, int n_c, int32_t* A_c,
+                          int32_t* K_c, hipStream_t s) {
+  const int blocks = T_c ? 2 : 1;
+  hipLaunchKernelGGL(k_compact, dim3(blocks), dim3(kCompactThreads), 0, s, B, N, logits, tau, T_g, n_g, A_g, K,
+                     T_c, n_c, A_c, K_c);
+  return hipGetLastError();
+}
+
+int fc2_tiles(int dt, int64_t d) {
+  const int64_t nvec = row_bytes(dt, d) / 16;
+  return (int)((nvec + kWave - 1) / kWave);
+}
+
+template <int DT>
+static hipError_t fc2_dt(const Fc2Args& a, hipStream_t s) {
+  dim3 g((unsigned)fc2_tiles(DT, a.d), (unsigned)kFc2Chunks), t(kThreads);
+  if constexpr (DT == 2) {
+    hipLaunchKernelGGL((k_fc2<DT, 1>), g, t, 0, s, a);
+  } else {
+    if (a.B <= 1) hipLaunchKernelGGL((k_fc2<DT, 1>), g, t, 0, s, a);
+    else if (a.B <= 2) hipLaunchKernelGGL((k_fc2<DT, 2>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((k_fc2<DT, 4>), g, t, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fc2(const Fc2Args& a, hipStream_t s) {
+  switch (a.dt) {
+    case PI_F32: return fc2_dt<0>(a, s);
+    case PI_F16: return fc2_dt<1>(a, s);
+    default: return fc2_dt<2>(a, s);
+  }
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(int B, int d, float* y, const float* y_c, const int32_t* K_c, const void* b2, int b2_dt,
+                        hipStream_t s) {
+  const int64_t n = (int64_t)B * d;
+  int64_t blocks = (n + kThreads - 1) / kThreads;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(k_merge, dim3((unsigned)blocks), dim3(kThreads), 0, s, n, d, y, y_c, K_c, b2, b2_dt);
+  return hipGetLastError();
+}
+
+}  // namespace pi

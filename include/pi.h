@@ -1,0 +1,147 @@
+/* pi.h - C ABI of libpi, the MI355X (gfx950) neuron-aware sparse FFN.
+ *
+ * The operation, per decoded token and FFN layer, follows PowerInfer as the
+ * pages describe it:
+ *   1. a small per-layer MLP predictor marks the neurons that will fire
+ *      (CSDN summary of "PowerInfer: Fast Large Language Model Serving with a
+ *      Consumer-grade GPU", section 自适应稀疏预测器; unite.ai French article
+ *      "PowerInfer : Moteur d'inférence ...", section "Prévisionnistes de
+ *      rareté adaptatifs");
+ *   2. the active neurons are looked up through the GPU neuron table, which
+ *      maps each GPU-resident neuron to its original position in the weight
+ *      matrices (CSDN summary, section 神经元放置和管理; French article,
+ *      section "Placement et gestion des neurones");
+ *   3. only those neurons' FC1 rows are multiplied, ReLU keeps the positive
+ *      ones, and only the matching FC2 rows (a neuron's FC2 column, stored
+ *      neuron-major) are accumulated (CSDN summary, background part on the MLP
+ *      block and section 神经元-觉察算子; French article, section "Opérateur
+ *      sensible aux neurones");
+ *   4. the partial result computed elsewhere for the cold neurons is merged
+ *      on the GPU, and the merge is skipped when there is none (CSDN summary,
+ *      section GPU-CPU混合执行).
+ *
+ * Conventions shared by every entry point
+ *  - Every array argument is a DEVICE pointer owned by the caller, 16-byte
+ *    aligned.  The library never allocates, frees or synchronises, and never
+ *    reads device memory from the host.  Work is enqueued on `stream` (a
+ *    hipStream_t; NULL = the null stream) in the order of the calls.
+ *  - Matrices are row-major.  Row r of a [rows x cols] matrix starts at
+ *    r * row_bytes, row_bytes = cols * 4 (PI_F32), cols * 2 (PI_F16) or
+ *    cols / 2 (PI_I4G128).  cols must be a multiple of 8 (PI_F32, PI_F16) or
+ *    of 128 (PI_I4G128).
+ *  - PI_I4G128: symmetric int4, two elements per byte, even element in the
+ *    low nibble, two's-complement value q in [-8, 7]; element value is
+ *    q * scale, one fp16 scale per 128 consecutive elements of a row,
+ *    scales[rows x cols/128].
+ *  - Counts (K, K_c) stay on the device, so a decode step needs no host
+ *    synchronisation.  Grids are bounded by the table sizes.
+ *  - Return value: PI_OK, or an error status with nothing enqueued
+ *    (PI_EINVAL, PI_EWORKSPACE, PI_EUNSUPPORTED), or PI_EHIP when the HIP
+ *    launch itself failed (pi_last_hip_error() then gives the hipError_t of
+ *    this thread's last failure).  Device faults surface at the caller's next
+ *    synchronisation.  No entry point prints, aborts or throws.
+ *  - Results are bitwise repeatable: the same inputs give the same bits.
+ *  - The library holds no mutable global state; calls on different streams
+ *    with disjoint outputs and workspaces may run concurrently.
+ */
+#ifndef PI_H
+#define PI_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PI_ABI_VERSION 1
+#define PI_MAX_BATCH 32
+
+enum pi_dtype { PI_F32 = 0, PI_F16 = 1, PI_I4G128 = 2 };
+enum pi_ffn_kind { PI_RELU = 0, PI_GATED_RELU = 1 };
+enum pi_status { PI_OK = 0, PI_EINVAL = 1, PI_EWORKSPACE = 2, PI_EUNSUPPORTED = 3, PI_EHIP = 4 };
+enum pi_op { PI_OP_PREDICT = 0, PI_OP_COMPACT = 1, PI_OP_SPARSE_FFN = 2, PI_OP_MERGE = 3 };
+
+/* A weight matrix on the device.  `scales` is used by PI_I4G128 only. */
+typedef struct pi_matrix {
+  const void* data;
+  const uint16_t* scales;
+  int32_t dtype; /* enum pi_dtype */
+} pi_matrix;
+
+/* A bias vector on the device, PI_F32 or PI_F16.  data == NULL means zero. */
+typedef struct pi_vector {
+  const void* data;
+  int32_t dtype;
+} pi_vector;
+
+/* Predictor (step 1).  For each batch row b < B:
+ *   h[b,m]      = max(0, sum_k P1[m,k] * x[b,k] + c1[m])      m < H
+ *   logits[b,i] = sum_m P2[i,m] * h[b,m] + c2[i]               i < N
+ * x      [B x d] fp32.   P1 [H x d], P2 [N x H] (PI_F32/PI_F16/PI_I4G128).
+ * logits [B x N] fp32, written.   h lives in the workspace.
+ * ws: at least pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0) bytes.
+ * Errors: PI_EINVAL for a NULL required pointer, B outside 1..PI_MAX_BATCH,
+ * a non-positive size, a column count the dtype forbids or an unknown dtype;
+ * PI_EWORKSPACE for a short workspace. */
+int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const float* x,
+               pi_matrix P1, pi_vector c1, pi_matrix P2, pi_vector c2,
+               float* logits, void* ws, size_t ws_bytes);
+
+/* Activation decision and compaction (step 2).
+ * Neuron i is active when logits[b,i] > tau (fp32 compare) for SOME b < B
+ * (the union over the batch).
+ *   A_g[0..K)   = the slots s < n_g with T_g[s] active, ascending; *K = count
+ *   A_c[0..K_c) = the slots c < n_c with T_c[c] active, ascending; *K_c = count
+ * T_g [n_g] int32: slot -> original neuron id (the GPU neuron table); the
+ * ids must lie in [0, N).  T_c [n_c] (optional, NULL = no cold side): the
+ * CPU neuron table.  A_g needs n_g entries, A_c n_c.  K, K_c: one device
+ * int32 each.  ws may be NULL (pi_workspace_bytes returns 0).
+ * Errors: PI_EINVAL for a NULL required pointer, B outside 1..PI_MAX_BATCH,
+ * n_g < 0, N <= 0, or T_c given without A_c/K_c. */
+int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float tau,
+               const int32_t* T_g, int32_t n_g, int32_t* A_g, int32_t* K,
+               const int32_t* T_c, int32_t n_c, int32_t* A_c, int32_t* K_c,
+               void* ws, size_t ws_bytes);
+
+/* Neuron-aware FFN over the GPU-resident neurons (step 3).
+ * W1, W2 (and Wup) hold the n_g GPU-resident neurons in slot order,
+ * [n_g x d] each; W2 is stored neuron-major (row s = the FC2 column of the
+ * neuron in slot s).  For j < *K, s = A_g[j]:
+ *   a[b,j] = max(0, W1[s].x_b + b1[s])                    (PI_RELU)
+ *   a[b,j] = max(0, W1[s].x_b + b1[s]) * (Wup[s].x_b)     (PI_GATED_RELU)
+ *   y_g[b,:] = sum_j a[b,j] * W2[s,:]                      (fixed-order sum)
+ * x [B x d] fp32; b1 [n_g]; y_g [B x d] fp32, fully written (zero if K = 0).
+ * A_g entries must be < n_g; *K <= n_g.
+ * ws: at least pi_workspace_bytes(PI_OP_SPARSE_FFN, B, d, 0, 0, n_g) bytes.
+ * Errors: as pi_predict, plus PI_EINVAL for a kind outside PI_RELU /
+ * PI_GATED_RELU or a gated call without Wup, and PI_EUNSUPPORTED when W1,
+ * Wup and W2 do not share one dtype. */
+int pi_sparse_ffn(void* stream, int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x,
+                  pi_matrix W1, pi_vector b1, pi_matrix Wup, pi_matrix W2,
+                  const int32_t* A_g, const int32_t* K, float* y_g, void* ws, size_t ws_bytes);
+
+/* Merge (step 4):  y[b,:] = y[b,:] + y_c[b,:] + b2   (in place, [B x d] fp32).
+ * y_c (device [B x d] fp32, the cold-neuron partial) is added only when it
+ * is non-NULL and, if K_c is non-NULL, *K_c != 0: with no active cold neuron
+ * the cold partial is skipped.  b2.data == NULL adds no bias.
+ * Errors: PI_EINVAL for a NULL y, B outside 1..PI_MAX_BATCH or d <= 0. */
+int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, const int32_t* K_c,
+             pi_vector b2);
+
+/* Workspace bytes an entry point needs for these sizes (0 when none).
+ * Arguments an op does not use are ignored. */
+size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g);
+
+/* Static description of a status code. */
+const char* pi_status_string(int32_t status);
+
+/* hipError_t of the calling thread's last PI_EHIP (0 if none). */
+int32_t pi_last_hip_error(void);
+
+/* PI_ABI_VERSION the library was built with. */
+int32_t pi_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

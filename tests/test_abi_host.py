@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/pi.h declares, and rejects bad arguments before any HIP call."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import activation_sparse_amd as pi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "pi.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t|const char\*)\s+(pi_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_symbols() == sorted(pi.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = pi.load()
+    for name in declared_symbols():
+        assert hasattr(L, name), name
+    assert L.pi_abi_version() == 1
+
+
+def test_status_strings():
+    L = pi.load()
+    for s in range(5):
+        assert L.pi_status_string(s).decode().startswith("PI_")
+    assert b"unknown" in L.pi_status_string(99)
+
+
+def test_workspace_sizes():
+    assert pi.pi_workspace_bytes(pi.PI_OP_PREDICT, 1, 7168, 1024, 28672, 0) >= 1024 * 4
+    assert pi.pi_workspace_bytes(pi.PI_OP_COMPACT, 1, 7168, 1024, 28672, 11468) == 0
+    w1 = pi.pi_workspace_bytes(pi.PI_OP_SPARSE_FFN, 1, 7168, 0, 0, 11468)
+    w32 = pi.pi_workspace_bytes(pi.PI_OP_SPARSE_FFN, 32, 7168, 0, 0, 11468)
+    assert w1 >= 11468 * 4 + 7168 * 4 and w32 > w1
+
+
+FAKE = 1 << 20       # a 16-byte aligned fake device address; never dereferenced on these paths
+
+
+def mat(dt=pi.PI_F16, ptr=FAKE, scales=None):
+    return pi.Matrix(ptr, dt, scales)
+
+
+def status(fn, *args):
+    try:
+        fn(*args)
+        return pi.PI_OK
+    except pi.PiError as e:
+        msg = str(e)
+        for code, name in [(pi.PI_EINVAL, "PI_EINVAL"), (pi.PI_EWORKSPACE, "PI_EWORKSPACE"),
+                           (pi.PI_EUNSUPPORTED, "PI_EUNSUPPORTED"), (pi.PI_EHIP, "PI_EHIP")]:
+            if name in msg:
+                return code
+        raise
+
+
+@pytest.mark.parametrize("B,d,H,N,dt,note", [
+    (0, 256, 64, 512, pi.PI_F16, "batch 0"),
+    (33, 256, 64, 512, pi.PI_F16, "batch above the maximum"),
+    (1, 0, 64, 512, pi.PI_F16, "d = 0"),
+    (1, 260, 64, 512, pi.PI_F16, "d not a multiple of 8"),
+    (1, 192, 64, 512, pi.PI_I4G128, "int4 with d not a multiple of 128"),
+    (1, 256, 64, 512, 7, "unknown dtype"),
+])
+def test_predict_rejects_bad_arguments(B, d, H, N, dt, note):
+    st = status(pi.pi_predict, B, d, H, N, FAKE, mat(dt, scales=FAKE), None, mat(dt, scales=FAKE), None, FAKE,
+                FAKE, 1 << 30, 0)
+    assert st == pi.PI_EINVAL, note
+
+
+def test_predict_rejects_short_workspace_and_misaligned_pointers():
+    assert status(pi.pi_predict, 1, 256, 64, 512, FAKE, mat(), None, mat(), None, FAKE, FAKE, 16, 0) == pi.PI_EWORKSPACE
+    assert status(pi.pi_predict, 1, 256, 64, 512, FAKE + 4, mat(), None, mat(), None, FAKE, FAKE, 1 << 30, 0) == pi.PI_EINVAL
+    assert status(pi.pi_predict, 1, 256, 64, 512, FAKE, mat(ptr=FAKE + 8), None, mat(), None, FAKE, FAKE, 1 << 30,
+                  0) == pi.PI_EINVAL
+    assert status(pi.pi_predict, 1, 256, 64, 512, FAKE, mat(pi.PI_I4G128), None, mat(), None, FAKE, FAKE, 1 << 30,
+                  0) == pi.PI_EINVAL    # int4 without scales
+
+
+def test_sparse_ffn_rejects_bad_arguments():
+    args = dict(B=1, d=256, n_g=100, kind=pi.PI_RELU)
+    ws = 1 << 30
+
+    def call(B=1, d=256, n_g=100, kind=pi.PI_RELU, W1=None, W2=None, Wup=None, A=FAKE, K=FAKE, wsb=ws):
+        return status(pi.pi_sparse_ffn, B, d, n_g, kind, FAKE, W1 or mat(), None, Wup, W2 or mat(), A, K, FAKE, FAKE,
+                      wsb, 0)
+
+    assert call(kind=5) == pi.PI_EINVAL
+    assert call(kind=pi.PI_GATED_RELU) == pi.PI_EINVAL              # gated without Wup
+    assert call(W2=mat(pi.PI_F32)) == pi.PI_EUNSUPPORTED             # mixed dtypes
+    assert call(K=None) == pi.PI_EINVAL
+    assert call(A=None) == pi.PI_EINVAL
+    assert call(n_g=-1) == pi.PI_EINVAL
+    assert call(wsb=64) == pi.PI_EWORKSPACE
+
+
+def test_compact_and_merge_reject_bad_arguments():
+    assert status(pi.pi_compact, 1, 0, FAKE, 0.0, FAKE, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL
+    assert status(pi.pi_compact, 1, 100, FAKE, 0.0, None, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL
+    assert status(pi.pi_compact, 1, 100, FAKE, 0.0, FAKE, 10, FAKE, FAKE, FAKE, 5, None, FAKE, 0) == pi.PI_EINVAL
+    assert status(pi.pi_merge, 0, 16, FAKE, FAKE, None, None, 0) == pi.PI_EINVAL
+    assert status(pi.pi_merge, 1, 16, None, FAKE, None, None, 0) == pi.PI_EINVAL
+    # nothing to add: accepted without any launch
+    assert status(pi.pi_merge, 1, 16, FAKE, None, None, None, 0) == pi.PI_OK

@@ -1,0 +1,116 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Sizes: reduced shapes that the oracle finishes in seconds yet span several
+tiles and ragged tails, then one layer of each full-size workload (the oracle
+handles one layer, with rows generated only for the neurons it needs).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from tests import parity_harness as ph
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _run(cfg, **kw):
+    print(f"[parity] cfg={cfg.key} d={cfg.d} N={cfg.N} kw={kw}", flush=True)
+    r = ph.run_layer_parity(cfg, **kw)
+    print(f"[parity]   -> {r}", flush=True)
+    ph.assert_report(r)
+    return r
+
+
+# --------------------------------------------------------------------------- generator identity
+
+@pytest.mark.parametrize("dtype,cols", [(synth.F32, 264), (synth.F16, 520), (synth.I4G128, 384)])
+def test_device_generator_matches_host_bits(dtype, cols):
+    torch = _dev()
+    rows = np.array([5, 0, 77, 1023, 4], np.int32)
+    host, hs = synth.host_rows(dtype, 9, synth.TAG_W1, 3, cols, 0.05, row_ids=rows)
+    m = ph.dev_matrix(len(rows), cols, dtype, "cuda:0")
+    ph.fill_matrix(m, dtype, 9, synth.TAG_W1, 3, cols, 0.05, torch.from_numpy(rows).cuda())
+    torch.cuda.synchronize()
+    dev = m.data.cpu().numpy()
+    if dtype == synth.F16:
+        dev = dev.view(np.uint16)
+    assert np.array_equal(dev.view(np.uint8), host.view(np.uint8))
+    if hs is not None:
+        assert np.array_equal(m.scales.cpu().numpy().view(np.uint16), hs)
+
+
+# --------------------------------------------------------------------------- reduced shapes
+
+SMALL = [
+    ph.small_case("f16-ragged", d=264, N=1000, H=72, wdtype=synth.F16),        # ragged tiles, N not /64
+    ph.small_case("f32", d=768, N=3072, H=128, wdtype=synth.F32, seed=12),
+    ph.small_case("f16", d=1024, N=4096, H=256, wdtype=synth.F16, seed=13),
+    ph.small_case("i4", d=1024, N=2048, H=128, wdtype=synth.I4G128, seed=14),
+    ph.small_case("gated", d=512, N=1536, H=128, wdtype=synth.F16, gated=True, rho=0.15, seed=15),
+    ph.small_case("gated-i4", d=640, N=1280, H=64, wdtype=synth.I4G128, gated=True, seed=16),
+    ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=17),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.key for c in SMALL])
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_small_layer_parity(cfg, B):
+    _dev()
+    _run(cfg, layer=0, step=1, B=B)
+
+
+@pytest.mark.parametrize("B", [16, 32])
+def test_large_batch_union(B):
+    _dev()
+    r = _run(SMALL[6], layer=0, step=2, B=B)
+    assert r["K"] > 0
+
+
+def test_all_active_list_is_the_whole_table():
+    _dev()
+    cfg = SMALL[2]
+    r = _run(cfg, layer=0, step=0, B=2, tau_all_active=True)
+    assert r["K"] == cfg.N
+
+
+def test_empty_list_gives_zero_output():
+    _dev()
+    r = _run(SMALL[6], layer=0, step=0, B=1, tau=1e30)
+    assert r["K"] == 0 and r["K_c"] == 0 and r["y_norm"] == 0.0
+
+
+def test_outputs_are_bitwise_repeatable():
+    torch = _dev()
+    cfg = SMALL[3]
+    spec = synth.layer_spec(cfg, 0)
+    dl = ph.DeviceLayer(spec)
+    outs = []
+    for _ in range(3):
+        buf = ph.DeviceBuffers(cfg, spec.H, spec.n_g, 0, 4)
+        buf.x.copy_(torch.from_numpy(synth.host_x(cfg.seed, 0, 5, 4, cfg.d)))
+        ph.run_gpu_layer(dl, buf, 4)
+        torch.cuda.synchronize()
+        outs.append((buf.logits.cpu().numpy().tobytes(), buf.A_g.cpu().numpy()[:int(buf.K.cpu()[0])].tobytes(),
+                     buf.y.cpu().numpy().tobytes()))
+    assert outs[0] == outs[1] == outs[2]
+
+
+# --------------------------------------------------------------------------- full-size workloads, one layer each
+
+FULL = [("opt-768", 0, 1), ("opt-6.7b", 5, 1), ("llama-13b-gated", 7, 1), ("opt-30b", 3, 1), ("opt-30b", 3, 4),
+        ("opt-30b", 11, 16), ("opt-30b", 11, 32), ("opt-175b-int4", 42, 1)]
+
+
+@pytest.mark.parametrize("key,layer,B", FULL, ids=[f"{k}-L{l}-B{b}" for k, l, b in FULL])
+def test_full_size_layer_parity(key, layer, B):
+    _dev()
+    _run(synth.CONFIGS[key], layer=layer, step=3, B=B)
