@@ -16,14 +16,14 @@ from typing import Optional
 PI_F32, PI_F16, PI_I4G128 = 0, 1, 2
 PI_RELU, PI_GATED_RELU = 0, 1
 PI_OK, PI_EINVAL, PI_EWORKSPACE, PI_EUNSUPPORTED, PI_EHIP = 0, 1, 2, 3, 4
-PI_OP_PREDICT, PI_OP_COMPACT, PI_OP_SPARSE_FFN, PI_OP_MERGE = 0, 1, 2, 3
+PI_OP_PREDICT, PI_OP_COMPACT, PI_OP_SPARSE_FFN, PI_OP_MERGE, PI_OP_FFN_LAYER = 0, 1, 2, 3, 4
 PI_MAX_BATCH = 32
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpi.so")
 
-EXPORTS = ("pi_predict", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_workspace_bytes",
-           "pi_status_string", "pi_last_hip_error", "pi_abi_version")
+EXPORTS = ("pi_predict", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes", "pi_table_prepare",
+           "pi_ffn_layer", "pi_workspace_bytes", "pi_status_string", "pi_last_hip_error", "pi_abi_version")
 
 
 class PiError(RuntimeError):
@@ -36,6 +36,12 @@ class _Mat(C.Structure):
 
 class _Vec(C.Structure):
     _fields_ = [("data", C.c_void_p), ("dtype", C.c_int32)]
+
+
+class _Layer(C.Structure):
+    _fields_ = [("d", C.c_int32), ("N", C.c_int32), ("H", C.c_int32), ("n_g", C.c_int32), ("kind", C.c_int32),
+                ("cold", C.c_int32), ("P1", _Mat), ("c1", _Vec), ("P2", _Mat), ("c2", _Vec), ("table", C.c_void_p),
+                ("W1", _Mat), ("b1", _Vec), ("Wup", _Mat), ("W2", _Mat), ("b2", _Vec)]
 
 
 _lib = None
@@ -53,6 +59,12 @@ def load():
         L.pi_compact.argtypes = [P, I, I, P, C.c_float, P, I, P, P, P, I, P, P, P, C.c_size_t]
         L.pi_sparse_ffn.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Mat, P, P, P, P, C.c_size_t]
         L.pi_merge.argtypes = [P, I, I, P, P, P, _Vec]
+        L.pi_table_bytes.argtypes = [I]
+        L.pi_table_bytes.restype = C.c_size_t
+        L.pi_table_prepare.argtypes = [I, P, I, P, C.c_size_t]
+        L.pi_table_prepare.restype = C.c_int
+        L.pi_ffn_layer.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P, P, C.c_size_t, P]
+        L.pi_ffn_layer.restype = C.c_int
         L.pi_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.pi_workspace_bytes.restype = C.c_size_t
         L.pi_status_string.argtypes = [I]
@@ -143,3 +155,67 @@ def pi_sparse_ffn(B, d, n_g, kind, x, W1: Matrix, b1: Vector, Wup: Optional[Matr
 
 def pi_merge(B, d, y, y_c=None, K_c=None, b2: Optional[Vector] = None, stream=None) -> None:
     _check(load().pi_merge(_stream(stream), B, d, _ptr(y), _ptr(y_c), _ptr(K_c), (b2 or _NO_VEC)._c()), "pi_merge")
+
+
+def pi_table_bytes(N: int) -> int:
+    return int(load().pi_table_bytes(N))
+
+
+def pi_table_prepare(N: int, T_g):
+    """Prepared neuron table (host numpy uint8 buffer) of an ascending host int32 T_g."""
+    import numpy as np
+    T = np.ascontiguousarray(T_g, dtype=np.int32)
+    nb = pi_table_bytes(N)
+    buf = np.zeros(max(nb, 1), np.uint8)
+    _check(load().pi_table_prepare(N, T.ctypes.data if len(T) else None, len(T), buf.ctypes.data, nb),
+           "pi_table_prepare")
+    return buf
+
+
+@dataclass
+class Layer:
+    """Arguments of pi_ffn_layer that describe one layer (device tensors)."""
+    d: int
+    N: int
+    H: int
+    n_g: int
+    kind: int
+    cold: bool
+    P1: Matrix
+    c1: Optional[Vector]
+    P2: Matrix
+    c2: Optional[Vector]
+    table: object
+    W1: Matrix
+    b1: Optional[Vector]
+    Wup: Optional[Matrix]
+    W2: Matrix
+    b2: Optional[Vector] = None
+
+    def _c(self) -> _Layer:
+        return _Layer(self.d, self.N, self.H, self.n_g, self.kind, int(bool(self.cold)), self.P1._c(),
+                      (self.c1 or _NO_VEC)._c(), self.P2._c(), (self.c2 or _NO_VEC)._c(), _ptr(self.table),
+                      self.W1._c(), (self.b1 or _NO_VEC)._c(), (self.Wup or _NO_MAT)._c(), self.W2._c(),
+                      (self.b2 or _NO_VEC)._c())
+
+
+def event_handles(events):
+    """Raw hipEvent_t handles of torch events (each recorded once so that it exists)."""
+    import torch
+    hs = []
+    for e in events:
+        if not e.cuda_event:
+            e.record()
+        hs.append(e.cuda_event)
+    torch.cuda.current_stream().synchronize()
+    return (C.c_void_p * len(hs))(*hs)
+
+
+def pi_ffn_layer(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_c, K_c, ws, ws_bytes=None,
+                 events=None, stream=None, _cstruct=None) -> None:
+    """One layer: predictor, compaction, FFN over the GPU-resident neurons, merge."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    cl = _cstruct if _cstruct is not None else layer._c()
+    _check(load().pi_ffn_layer(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
+                               _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c), _ptr(ws), nbytes, events),
+           "pi_ffn_layer")

@@ -2,6 +2,7 @@
 // kernel launches.  Declarations and their sources: include/pi.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 #include "../../include/pi.h"
 #include "pi_internal.h"
 
@@ -33,31 +34,58 @@ int hip_status(hipError_t e) {
   return PI_EHIP;
 }
 
+// Carve a workspace into 256-byte aligned regions.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t bytes) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
 struct FfnWs {
   float* a;
   float* partials;
-  uint32_t* counters;
   size_t bytes;
 };
 
-FfnWs ffn_ws_layout(void* ws, int32_t B, int32_t d, int32_t n_g, int32_t dt) {
+FfnWs ffn_ws_layout(void* ws, int32_t B, int32_t d, int32_t n_g) {
+  Carver c{static_cast<char*>(ws)};
   FfnWs w{};
-  const size_t a_bytes = align_up((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
-  const size_t p_bytes = align_up((size_t)pi::kFc2Chunks * B * (size_t)d * 4);
-  const size_t c_bytes = align_up((size_t)pi::fc2_tiles(dt, d) * 4);
-  char* base = static_cast<char*>(ws);
-  w.a = reinterpret_cast<float*>(base);
-  w.partials = reinterpret_cast<float*>(base + a_bytes);
-  w.counters = reinterpret_cast<uint32_t*>(base + a_bytes + p_bytes);
-  w.bytes = a_bytes + p_bytes + c_bytes;
+  w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
+  w.partials = c.take<float>((size_t)pi::kFc2Chunks * B * (size_t)d * 4);
+  w.bytes = c.off;
+  return w;
+}
+
+// Fused layer workspace: h, logits scratch, activation words, a, partials.
+struct LayerWs {
+  float* h;
+  float* logits;
+  uint32_t* mask;
+  float* a;
+  float* partials;
+  size_t bytes;
+};
+
+size_t table_words(int32_t N) { return 2 * (size_t)((N + 63) / 64); }
+
+LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g) {
+  Carver c{static_cast<char*>(ws)};
+  LayerWs w{};
+  w.h = c.take<float>((size_t)B * H * 4);
+  w.logits = c.take<float>((size_t)B * N * 4);
+  w.mask = c.take<uint32_t>(table_words(N) * 4);
+  w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
+  w.partials = c.take<float>((size_t)pi::kFc2Chunks * B * (size_t)d * 4);
+  w.bytes = c.off;
   return w;
 }
 
 }  // namespace
-
-namespace pi {
-hipError_t launch_rowdot_ex(const RowdotArgs& a, int64_t n_rows, uint32_t* zero_ptr, int zero_n, hipStream_t s);
-}
 
 extern "C" {
 
@@ -77,22 +105,30 @@ const char* pi_status_string(int32_t status) {
 }
 
 size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g) {
-  (void)N;
   if (B < 1) B = 1;
   switch (op) {
     case PI_OP_PREDICT: return H > 0 ? align_up((size_t)B * (size_t)H * 4) : 0;
-    case PI_OP_SPARSE_FFN: {
-      if (d <= 0) return 0;
-      // the largest layout over the three storage types
-      size_t m = 0;
-      for (int32_t dt = PI_F32; dt <= PI_I4G128; ++dt) {
-        const size_t b = ffn_ws_layout(nullptr, B, d, n_g, dt).bytes;
-        if (b > m) m = b;
-      }
-      return m;
-    }
+    case PI_OP_SPARSE_FFN:
+      return d > 0 ? ffn_ws_layout(nullptr, B, d, n_g).bytes : 0;
+    case PI_OP_FFN_LAYER:
+      return (d > 0 && N > 0) ? layer_ws_layout(nullptr, B, d, H > 0 ? H : 1, N, n_g).bytes : 0;
     default: return 0;
   }
+}
+
+size_t pi_table_bytes(int32_t N) { return N > 0 ? table_words(N) * 4 : 0; }
+
+int pi_table_prepare(int32_t N, const int32_t* T_g, int32_t n_g, void* table, size_t table_bytes) {
+  if (N <= 0 || n_g < 0 || n_g > N || !table || (n_g > 0 && !T_g)) return PI_EINVAL;
+  if (table_bytes < pi_table_bytes(N)) return PI_EWORKSPACE;
+  const size_t W = table_words(N);
+  uint32_t* bits = static_cast<uint32_t*>(table);
+  for (int32_t s = 0; s < n_g; ++s) {
+    if (T_g[s] < 0 || T_g[s] >= N || (s > 0 && T_g[s] <= T_g[s - 1])) return PI_EINVAL;
+  }
+  memset(bits, 0, W * 4);
+  for (int32_t s = 0; s < n_g; ++s) bits[T_g[s] / 32] |= 1u << (T_g[s] % 32);
+  return PI_OK;
 }
 
 int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const float* x, pi_matrix P1,
@@ -104,6 +140,17 @@ int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const f
   if (ws_bytes < pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0)) return PI_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* h = static_cast<float*>(ws);
+  if (B == 1 && pi::b1_supported(P1.dtype, d) && pi::b1_supported(P2.dtype, H)) {
+    pi::B1Gemv g{};
+    g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
+    g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
+    int st = hip_status(pi::launch_hidden_b1(g, s));
+    if (st != PI_OK) return st;
+    pi::B1Gemv o{};
+    o.W = P2.data; o.Ws = P2.scales; o.dt = P2.dtype; o.rows = N; o.cols = H; o.x = h;
+    o.bias = c2.data; o.bias_dt = c2.dtype; o.out = logits;
+    return hip_status(pi::launch_logits_b1(o, 0.f, nullptr, s));
+  }
   pi::RowdotArgs a{};
   a.W = P1.data; a.Ws = P1.scales; a.dt = P1.dtype; a.cols = d;
   a.count_max = H; a.x = x; a.B = B; a.bias = c1.data; a.bias_dt = c1.dtype;
@@ -129,43 +176,138 @@ int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float ta
                                        static_cast<hipStream_t>(stream)));
 }
 
-int pi_sparse_ffn(void* stream, int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x, pi_matrix W1,
-                  pi_vector b1, pi_matrix Wup, pi_matrix W2, const int32_t* A_g, const int32_t* K, float* y_g,
-                  void* ws, size_t ws_bytes) {
+namespace {
+
+int validate_ffn(int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x, const pi_matrix& W1,
+                 const pi_vector& b1, const pi_matrix& Wup, const pi_matrix& W2) {
   if (!valid_batch(B) || d <= 0 || n_g < 0) return PI_EINVAL;
   if (kind != PI_RELU && kind != PI_GATED_RELU) return PI_EINVAL;
-  if (!x || !aligned16(x) || !y_g || !aligned16(y_g) || !K) return PI_EINVAL;
-  if (n_g > 0 && !A_g) return PI_EINVAL;
+  if (!x || !aligned16(x)) return PI_EINVAL;
   if (!valid_matrix(W1, d) || !valid_matrix(W2, d) || !valid_vector(b1)) return PI_EINVAL;
   if (kind == PI_GATED_RELU) {
     if (!valid_matrix(Wup, d)) return PI_EINVAL;
     if (Wup.dtype != W1.dtype) return PI_EUNSUPPORTED;
   }
   if (W2.dtype != W1.dtype) return PI_EUNSUPPORTED;
-  if (!ws || !aligned16(ws)) return PI_EWORKSPACE;
-  const FfnWs w = ffn_ws_layout(ws, B, d, n_g, W1.dtype);
-  if (ws_bytes < w.bytes) return PI_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int tiles = pi::fc2_tiles(W1.dtype, d);
-  pi::RowdotArgs a{};
-  a.W = W1.data; a.Ws = W1.scales; a.dt = W1.dtype; a.cols = d;
-  a.gated = kind == PI_GATED_RELU;
-  if (a.gated) { a.Wup = Wup.data; a.Wups = Wup.scales; }
-  a.list = A_g; a.count_dev = K; a.count_max = n_g;
-  a.x = x; a.B = B; a.bias = b1.data; a.bias_dt = b1.dtype; a.relu = 1;
-  a.out = w.a; a.out_stride = n_g > 0 ? n_g : 1;
-  int st = hip_status(pi::launch_rowdot_ex(a, n_g, w.counters, tiles, s));
+  return PI_OK;
+}
+
+// FC1 (list given, or built from activation words when lc != NULL on the batch-1
+// path), then FC2 partials, then the ordered reduction + merge.
+int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x, const pi_matrix& W1,
+                const pi_vector& b1, const pi_matrix& Wup, const pi_matrix& W2, const int32_t* A_g, const int32_t* K,
+                const pi::ListCtx* lc, float* a, float* partials, float* y, const float* y_c, const int32_t* K_c,
+                const pi_vector& b2, const hipEvent_t* ev) {
+  const bool gated = kind == PI_GATED_RELU;
+  int st;
+  if (B == 1 && pi::b1_supported(W1.dtype, d)) {
+    pi::B1Gemv g{};
+    g.W = W1.data; g.Ws = W1.scales; g.dt = W1.dtype; g.rows = n_g; g.cols = d; g.x = x;
+    if (gated) { g.Wu = Wup.data; g.Wus = Wup.scales; }
+    g.bias = b1.data; g.bias_dt = b1.dtype; g.out = a; g.list = A_g; g.Kp = K;
+    st = hip_status(pi::launch_fc1_b1(g, gated, lc, s));
+  } else {
+    if (lc && (st = hip_status(pi::launch_list(*lc, n_g, s))) != PI_OK) return st;
+    pi::RowdotArgs r{};
+    r.W = W1.data; r.Ws = W1.scales; r.dt = W1.dtype; r.cols = d; r.gated = gated;
+    if (gated) { r.Wup = Wup.data; r.Wups = Wup.scales; }
+    r.list = A_g; r.count_dev = K; r.count_max = n_g;
+    r.x = x; r.B = B; r.bias = b1.data; r.bias_dt = b1.dtype; r.relu = 1;
+    r.out = a; r.out_stride = n_g > 0 ? n_g : 1;
+    st = hip_status(pi::launch_rowdot_ex(r, n_g, nullptr, 0, s));
+  }
   if (st != PI_OK) return st;
+  if (ev && ev[0] && (st = hip_status(hipEventRecord(ev[0], s))) != PI_OK) return st;
   pi::Fc2Args f{};
   f.W2 = W2.data; f.W2s = W2.scales; f.dt = W2.dtype; f.d = d; f.n_g = n_g;
-  f.list = A_g; f.K = K; f.a = w.a; f.B = B; f.partials = w.partials; f.counters = w.counters; f.y = y_g;
-  return hip_status(pi::launch_fc2(f, s));
+  f.list = A_g; f.K = K; f.a = a; f.B = B; f.partials = partials;
+  if ((st = hip_status(pi::launch_fc2(f, s))) != PI_OK) return st;
+  if (ev && ev[1] && (st = hip_status(hipEventRecord(ev[1], s))) != PI_OK) return st;
+  pi::ReduceArgs r{};
+  r.partials = partials; r.chunks = pi::kFc2Chunks; r.B = B; r.d = d; r.y = y;
+  r.y_c = y_c; r.K_c = K_c; r.b2 = b2.data; r.b2_dt = b2.dtype;
+  return hip_status(pi::launch_reduce(r, s));
+}
+
+}  // namespace
+
+int pi_sparse_ffn(void* stream, int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x, pi_matrix W1,
+                  pi_vector b1, pi_matrix Wup, pi_matrix W2, const int32_t* A_g, const int32_t* K, float* y_g,
+                  void* ws, size_t ws_bytes) {
+  int st = validate_ffn(B, d, n_g, kind, x, W1, b1, Wup, W2);
+  if (st != PI_OK) return st;
+  if (!y_g || !aligned16(y_g) || !K || (n_g > 0 && !A_g)) return PI_EINVAL;
+  if (!ws || !aligned16(ws)) return PI_EWORKSPACE;
+  const FfnWs w = ffn_ws_layout(ws, B, d, n_g);
+  if (ws_bytes < w.bytes) return PI_EWORKSPACE;
+  return enqueue_ffn(static_cast<hipStream_t>(stream), B, d, n_g, kind, x, W1, b1, Wup, W2, A_g, K, nullptr, w.a,
+                     w.partials, y_g, nullptr, nullptr, pi_vector{nullptr, PI_F32}, nullptr);
 }
 
 int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, const int32_t* K_c, pi_vector b2) {
   if (!valid_batch(B) || d <= 0 || !y || !valid_vector(b2)) return PI_EINVAL;
   if (!y_c && !b2.data) return PI_OK;  // nothing to add
   return hip_status(pi::launch_merge(B, d, y, y_c, K_c, b2.data, b2.dtype, static_cast<hipStream_t>(stream)));
+}
+
+int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c, float* y,
+                 float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes,
+                 void* const* events) {
+  if (!L) return PI_EINVAL;
+  const int32_t d = L->d, N = L->N, H = L->H, n_g = L->n_g;
+  if (N <= 0 || H <= 0 || n_g > N) return PI_EINVAL;
+  int st = validate_ffn(B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2);
+  if (st != PI_OK) return st;
+  if (!valid_matrix(L->P1, d) || !valid_matrix(L->P2, H) || !valid_vector(L->c1) || !valid_vector(L->c2) ||
+      !valid_vector(L->b2))
+    return PI_EINVAL;
+  if (!L->table || !y || !aligned16(y) || !K || (n_g > 0 && !A_g)) return PI_EINVAL;
+  if (L->cold && (!A_c || !K_c)) return PI_EINVAL;
+  if (!ws || !aligned16(ws)) return PI_EWORKSPACE;
+  const LayerWs w = layer_ws_layout(ws, B, d, H, N, n_g);
+  if (ws_bytes < w.bytes) return PI_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (events)
+    for (int i = 0; i < 6; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+  auto record = [&](int i) { return ev[i] ? hip_status(hipEventRecord(ev[i], s)) : PI_OK; };
+
+  pi::ListCtx lc{};
+  lc.mask = w.mask; lc.gbits = static_cast<const uint32_t*>(L->table); lc.W = (int)table_words(N);
+  lc.A_g = A_g; lc.K = K; lc.A_c = L->cold ? A_c : nullptr; lc.K_c = L->cold ? K_c : nullptr;
+  float* lg = logits ? logits : w.logits;
+
+  if ((st = record(0)) != PI_OK) return st;
+  const bool fast = B == 1 && pi::b1_supported(L->P1.dtype, d) && pi::b1_supported(L->P2.dtype, H);
+  if (fast) {
+    pi::B1Gemv g{};
+    g.W = L->P1.data; g.Ws = L->P1.scales; g.dt = L->P1.dtype; g.rows = H; g.cols = d; g.x = x;
+    g.bias = L->c1.data; g.bias_dt = L->c1.dtype; g.out = w.h;
+    if ((st = hip_status(pi::launch_hidden_b1(g, s))) != PI_OK) return st;
+    if ((st = record(1)) != PI_OK) return st;
+    pi::B1Gemv o{};
+    o.W = L->P2.data; o.Ws = L->P2.scales; o.dt = L->P2.dtype; o.rows = N; o.cols = H; o.x = w.h;
+    o.bias = L->c2.data; o.bias_dt = L->c2.dtype; o.out = logits;
+    if ((st = hip_status(pi::launch_logits_b1(o, tau, w.mask, s))) != PI_OK) return st;
+  } else {
+    pi::RowdotArgs a{};
+    a.W = L->P1.data; a.Ws = L->P1.scales; a.dt = L->P1.dtype; a.cols = d;
+    a.count_max = H; a.x = x; a.B = B; a.bias = L->c1.data; a.bias_dt = L->c1.dtype;
+    a.relu = 1; a.out = w.h; a.out_stride = H;
+    if ((st = hip_status(pi::launch_rowdot(a, s))) != PI_OK) return st;
+    if ((st = record(1)) != PI_OK) return st;
+    pi::RowdotArgs b{};
+    b.W = L->P2.data; b.Ws = L->P2.scales; b.dt = L->P2.dtype; b.cols = H;
+    b.count_max = N; b.x = w.h; b.B = B; b.bias = L->c2.data; b.bias_dt = L->c2.dtype;
+    b.relu = 0; b.out = lg; b.out_stride = N;
+    if ((st = hip_status(pi::launch_rowdot(b, s))) != PI_OK) return st;
+    if ((st = hip_status(pi::launch_mask(B, N, lg, tau, w.mask, s))) != PI_OK) return st;
+  }
+  if ((st = record(2)) != PI_OK) return st;
+  st = enqueue_ffn(s, B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2, A_g, K, &lc, w.a, w.partials, y, y_c,
+                   L->cold ? K_c : nullptr, L->b2, ev + 3);
+  if (st != PI_OK) return st;
+  return record(5);
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-// pi_kernels.hip - the libpi kernels for gfx950 (wave64).
+// pi_generic.hip - libpi kernels for any batch size and row length (gfx950, wave64).
 //
 //  k_rowdot  : row-dot GEMV over dense rows (predictor layers) or over the
 //              rows listed in the active list (FC1), fused bias + ReLU (and
@@ -6,14 +6,11 @@
 //              loads along the row, fp32 accumulate, x staged in LDS.
 //  k_compact : threshold + union over the batch + wave ballot + block prefix
 //              sum -> ascending slot list and its count (stays on device).
-//  k_fc2     : neuron-major axpy.  Grid = (column tile, row chunk); each block
-//              writes one partial per (chunk, batch row, column) and the last
-//              block of a column tile sums the partials in chunk order, so the
-//              result does not depend on block timing (no float atomics).
 //  k_merge   : y += y_c (+ b2), skipped on the device when no cold neuron is
 //              active.
 #include "pi_device.h"
 #include "pi_internal.h"
+#include "pi_list.h"
 
 namespace pi {
 namespace {
@@ -170,88 +167,6 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const
   if (tid == 0) *Kout = base;
 }
 
-template <int DT, int NBG>
-__global__ __launch_bounds__(kThreads) void k_fc2(Fc2Args a) {
-  constexpr int E = Fmt<DT>::E;
-  __shared__ float red[kWavesPerBlock][kWave * E];
-  __shared__ int last_flag;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const int tile = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
-  const int64_t d = a.d;
-  const int64_t rb = row_bytes(DT, d);
-  const int nvec = (int)(rb / 16);
-  const int v = tile * kWave + lane;
-  const bool vok = v < nvec;
-  const int64_t groups = d / 128;
-  int64_t K = *a.K;
-  K = K < 0 ? 0 : (K > a.n_g ? a.n_g : K);
-  const int64_t j0 = K * chunk / nchunks, j1 = K * (chunk + 1) / nchunks;
-  const int B = a.B;
-  const int64_t tile_col0 = (int64_t)tile * kWave * E;
-  for (int b0 = 0; b0 < B; b0 += NBG) {
-    float acc[NBG][E];
-#pragma unroll
-    for (int b = 0; b < NBG; ++b)
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[b][e] = 0.f;
-    for (int64_t j = j0 + wave; j < j1; j += kWavesPerBlock) {
-      const int64_t s = a.list[j];
-      if (s < 0 || s >= a.n_g || !vok) continue;
-      float wf[E];
-      float sc = 1.f;
-      if constexpr (DT == 2) sc = h2f(a.W2s[s * groups + v / 4]);
-      widen<DT>(ld16(reinterpret_cast<const char*>(a.W2) + s * rb + (int64_t)v * 16), sc, wf);
-#pragma unroll
-      for (int b = 0; b < NBG; ++b) {
-        if (b0 + b < B) {
-          const float ab = a.a[(int64_t)(b0 + b) * a.n_g + j];
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc[b][e] = fmaf(ab, wf[e], acc[b][e]);
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < NBG; ++b) {
-      if (b0 + b < B) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) red[wave][lane * E + e] = acc[b][e];
-        __syncthreads();
-        float* dst = a.partials + ((int64_t)chunk * B + b0 + b) * d + tile_col0;
-        for (int t = tid; t < kWave * E; t += kThreads) {
-          if (tile_col0 + t < d) {
-            float sum = red[0][t];
-#pragma unroll
-            for (int w = 1; w < kWavesPerBlock; ++w) sum += red[w][t];
-            dst[t] = sum;
-          }
-        }
-        __syncthreads();
-      }
-    }
-  }
-  // The last block to finish this column tile sums the chunk partials in order.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&a.counters[tile], 1u);
-    last_flag = (old == (uint32_t)(nchunks - 1));
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  for (int b = 0; b < B; ++b) {
-    for (int t = tid; t < kWave * E; t += kThreads) {
-      const int64_t col = tile_col0 + t;
-      if (col < d) {
-        float sum = 0.f;
-        for (int c = 0; c < nchunks; ++c) sum += __builtin_nontemporal_load(a.partials + ((int64_t)c * B + b) * d + col);
-        a.y[(int64_t)b * d + col] = sum;
-      }
-    }
-  }
-  if (tid == 0) a.counters[tile] = 0u;
-}
-
 __global__ __launch_bounds__(kThreads) void k_merge(int64_t n, int d, float* y, const float* y_c,
                                                     const int32_t* K_c, const void* b2, int b2_dt) {
   const bool add_c = y_c && (!K_c || *K_c != 0);
@@ -262,6 +177,30 @@ __global__ __launch_bounds__(kThreads) void k_merge(int64_t n, int d, float* y, 
     if (b2) v += load_bias(b2, b2_dt, t % d);
     y[t] = v;
   }
+}
+
+// Union activation words from stored logits [B x N]: one wave per 64 ids.
+__global__ __launch_bounds__(kWave) void k_mask(int B, int N, const float* __restrict__ logits, float tau,
+                                                 uint32_t* __restrict__ mask) {
+  const int lane = threadIdx.x;
+  const int64_t r = (int64_t)blockIdx.x * 64 + lane;
+  bool f = false;
+  if (r < N)
+    for (int b = 0; b < B; ++b) f = f || (logits[(int64_t)b * N + r] > tau);
+  const uint64_t M = __ballot(f);
+  if (lane == 0) {
+    mask[2 * blockIdx.x] = (uint32_t)M;
+    mask[2 * blockIdx.x + 1] = (uint32_t)(M >> 32);
+  }
+}
+
+// Lists from activation words + prepared table; each block writes a strided
+// share of A_g and A_c, block 0 the counts.
+__global__ __launch_bounds__(kThreads) void k_list(ListCtx c) {
+  extern __shared__ uint32_t lsm[];
+  const ListView v = list_build<kThreads>(c, lsm);
+  for (int j = blockIdx.x * kThreads + threadIdx.x; j < v.K; j += gridDim.x * kThreads) c.A_g[j] = list_slot(v, j);
+  list_write_cold_and_counts<kThreads>(c, v);
 }
 
 __global__ void k_zero_u32(uint32_t* p, int64_t n) {
@@ -317,30 +256,16 @@ hipError_t launch_compact(int B, int N, const float* logits, float tau, const in
   return hipGetLastError();
 }
 
-int fc2_tiles(int dt, int64_t d) {
-  const int64_t nvec = row_bytes(dt, d) / 16;
-  return (int)((nvec + kWave - 1) / kWave);
-}
-
-template <int DT>
-static hipError_t fc2_dt(const Fc2Args& a, hipStream_t s) {
-  dim3 g((unsigned)fc2_tiles(DT, a.d), (unsigned)kFc2Chunks), t(kThreads);
-  if constexpr (DT == 2) {
-    hipLaunchKernelGGL((k_fc2<DT, 1>), g, t, 0, s, a);
-  } else {
-    if (a.B <= 1) hipLaunchKernelGGL((k_fc2<DT, 1>), g, t, 0, s, a);
-    else if (a.B <= 2) hipLaunchKernelGGL((k_fc2<DT, 2>), g, t, 0, s, a);
-    else hipLaunchKernelGGL((k_fc2<DT, 4>), g, t, 0, s, a);
-  }
+hipError_t launch_mask(int B, int N, const float* logits, float tau, uint32_t* mask, hipStream_t s) {
+  hipLaunchKernelGGL(k_mask, dim3((unsigned)((N + 63) / 64)), dim3(kWave), 0, s, B, N, logits, tau, mask);
   return hipGetLastError();
 }
 
-hipError_t launch_fc2(const Fc2Args& a, hipStream_t s) {
-  switch (a.dt) {
-    case PI_F32: return fc2_dt<0>(a, s);
-    case PI_F16: return fc2_dt<1>(a, s);
-    default: return fc2_dt<2>(a, s);
-  }
+hipError_t launch_list(const ListCtx& c, int n_g, hipStream_t s) {
+  int blocks = (n_g + kThreads - 1) / kThreads;
+  blocks = blocks < 1 ? 1 : (blocks > 64 ? 64 : blocks);
+  hipLaunchKernelGGL(k_list, dim3((unsigned)blocks), dim3(kThreads), (size_t)list_smem_words(c.W) * 4, s, c);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {

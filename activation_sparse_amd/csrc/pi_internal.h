@@ -3,34 +3,68 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include "../../include/pi.h"
+#include "pi_list.h"
 
 namespace pi {
 
+// Generic row-dot GEMV (any batch, any row length): predictor layers and FC1.
 struct RowdotArgs {
-  const void* W;          // [rows x cols]
-  const uint16_t* Ws;     // int4 scales
-  const void* Wup;        // gated only
+  const void* W;             // [rows x cols]
+  const uint16_t* Ws;        // int4 scales
+  const void* Wup;           // gated only
   const uint16_t* Wups;
   int dt;
   int64_t cols;
-  const int32_t* list;    // gathered rows (NULL = dense rows 0..count)
+  const int32_t* list;       // gathered rows (NULL = dense rows 0..count)
   const int32_t* count_dev;  // device count for gathered mode
-  int64_t count_max;      // dense count, or the bound on *count_dev
-  const float* x;         // [B x cols]
+  int64_t count_max;         // dense count, or the bound on *count_dev
+  const float* x;            // [B x cols]
   int B;
-  const void* bias;       // per row (indexed by row id)
+  const void* bias;          // per row (indexed by row id)
   int bias_dt;
-  int relu;               // apply max(0, .)
+  int relu;                  // apply max(0, .)
   int gated;
-  float* out;             // [B x out_stride], column = output index
+  float* out;                // [B x out_stride], column = output index
   int64_t out_stride;
 };
 
 hipError_t launch_rowdot(const RowdotArgs& a, hipStream_t s);
+// n_rows bounds listed row ids; block 0 first clears zero_n u32 words at zero_ptr (or none).
+hipError_t launch_rowdot_ex(const RowdotArgs& a, int64_t n_rows, uint32_t* zero_ptr, int zero_n, hipStream_t s);
 
+// Standalone compaction (any table order, single block per table).
 hipError_t launch_compact(int B, int N, const float* logits, float tau, const int32_t* T_g, int n_g,
                           int32_t* A_g, int32_t* K, const int32_t* T_c, int n_c, int32_t* A_c,
                           int32_t* K_c, hipStream_t s);
+
+// Batch-1 register-x GEMV kernels.
+struct B1Gemv {
+  const void* W;
+  const uint16_t* Ws;
+  const void* Wu;            // gated FC1 only
+  const uint16_t* Wus;
+  int dt;
+  int rows;                  // dense rows, or n_g for FC1
+  int cols;
+  const float* x;            // [cols]
+  const void* bias;
+  int bias_dt;
+  float* out;
+  const int32_t* list;       // FC1
+  const int32_t* Kp;         // FC1
+  uint32_t* zero_ptr;        // hidden: words cleared by block 0
+  int zero_n;
+};
+bool b1_supported(int dt, int64_t cols);
+hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s);
+// lc == NULL: list and count are inputs; else the kernel builds them (see pi_list.h).
+hipError_t launch_fc1_b1(const B1Gemv& g, bool gated, const ListCtx* lc, hipStream_t s);
+// Output layer; mask != NULL also writes the activation words (2 per 64 rows).
+hipError_t launch_logits_b1(const B1Gemv& g, float tau, uint32_t* mask, hipStream_t s);
+
+// Activation words from stored logits (union over the batch), and the lists from them.
+hipError_t launch_mask(int B, int N, const float* logits, float tau, uint32_t* mask, hipStream_t s);
+hipError_t launch_list(const ListCtx& c, int n_g, hipStream_t s);
 
 struct Fc2Args {
   const void* W2;
@@ -40,16 +74,27 @@ struct Fc2Args {
   int n_g;
   const int32_t* list;
   const int32_t* K;
-  const float* a;         // [B x n_g]
+  const float* a;            // [B x n_g]
   int B;
-  float* partials;        // [chunks x B x d]
-  uint32_t* counters;     // [tiles]
-  float* y;               // [B x d]
+  float* partials;           // [chunks x B x d]
+};
+
+struct ReduceArgs {
+  const float* partials;     // [chunks x B x d]
+  int chunks;
+  int B;
+  int64_t d;
+  float* y;                  // [B x d]
+  const float* y_c;          // merged when non-NULL and (K_c == NULL or *K_c != 0)
+  const int32_t* K_c;
+  const void* b2;
+  int b2_dt;
 };
 
 int fc2_tiles(int dt, int64_t d);
 constexpr int kFc2Chunks = 32;
 hipError_t launch_fc2(const Fc2Args& a, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& r, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 
 hipError_t launch_merge(int B, int d, float* y, const float* y_c, const int32_t* K_c, const void* b2,

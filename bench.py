@@ -1,0 +1,310 @@
+"""Decode benchmark of the neuron-aware sparse FFN on one MI355X.
+
+One step = one decoded token (batch B) through every FFN layer of the stack:
+for each layer, pi_predict -> pi_compact -> pi_sparse_ffn -> pi_merge, all
+on one stream, layers serialised.  Weights and inputs are seeded synthetic
+tensors generated on the device before timing; each step has its own inputs.
+Steps are captured once into HIP graphs and replayed.
+
+Prints one JSON line (rank 0): throughput in tokens/s, the roofline of the
+dominant stage, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="opt-30b")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=0, help="0 = every layer of the config")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-layers", type=int, default=4)
+    return ap.parse_args()
+
+
+def wbytes(dt):
+    import synth
+    return {synth.F32: 4.0, synth.F16: 2.0, synth.I4G128: 0.5 + 2.0 / 128}[dt]
+
+
+def bias_bytes(dt):
+    import synth
+    return 4.0 if dt == synth.F32 else 2.0
+
+
+def layer_bytes(spec, B, K, K_c):
+    """Algorithmic HBM bytes of one layer's step: predictor weights and biases,
+    the active GPU-resident neurons (FC1 row + bias + FC2 row, + up row if
+    gated), and the small vectors (x, h, logits, lists, y, cold partial)."""
+    cfg = spec.cfg
+    d, N, H = cfg.d, cfg.N, spec.H
+    wp, w, wb = wbytes(cfg.pdtype), wbytes(cfg.wdtype), bias_bytes(cfg.bdtype)
+    pred = (H * d + N * H) * wp + N * wb
+    mats = 3 if cfg.gated else 2
+    ffn = K * (mats * d * w + wb)
+    small = B * d * 4 + 2 * B * H * 4 + 2 * B * N * 4 + spec.n_g * 4 + 2 * K * 4 + B * d * 4 * 2
+    if len(spec.T_c):
+        small += len(spec.T_c) * 4 + 2 * K_c * 4 + (B * d * 4 if K_c else 0)
+    return pred, ffn, small
+
+
+def kernel_bytes(spec, B, K, K_c):
+    """Algorithmic bytes of each kernel of one pi_ffn_layer call (weights, biases and the vectors each
+    kernel must read or write; not the FC2 partials, which are an implementation choice)."""
+    cfg = spec.cfg
+    d, N, H = cfg.d, cfg.N, spec.H
+    wp, w, wb = wbytes(cfg.pdtype), wbytes(cfg.wdtype), bias_bytes(cfg.bdtype)
+    mats1 = 2 if cfg.gated else 1
+    cold = len(spec.T_c) > 0
+    words = 2 * ((N + 63) // 64)
+    return {
+        "hidden": H * d * wp + B * d * 4 + B * H * 4,
+        "logits+mask": N * H * wp + N * wb + B * H * 4 + B * N * 4 + words * 4,
+        "fc1+list": K * (mats1 * d * w + wb) + B * d * 4 + 2 * words * 4 + (K + K_c) * 4 + B * K * 4,
+        "fc2": K * d * w + K * 4 + B * K * 4,
+        "reduce+merge": B * d * 4 + (B * d * 4 if (cold and K_c) else 0),
+    }
+
+
+def cpu_baseline(cfg, B, seconds, n_layers_sample):
+    """The oracle's full per-step pipeline on a bounded sample of the same workload."""
+    import oracle as orc
+    import synth
+    from tests import parity_harness as ph
+    Ls = min(n_layers_sample, cfg.n_layers)
+    layers = []
+    for L in range(Ls):
+        spec = synth.layer_spec(cfg, L)
+        sig = spec.sigmas()
+        P1 = ph.host_mat(cfg.pdtype, cfg.seed, synth.TAG_P1, L, cfg.d, sig[synth.TAG_P1], nrows=spec.H)
+        P2 = ph.host_mat(cfg.pdtype, cfg.seed, synth.TAG_P2, L, spec.H, sig[synth.TAG_P2], nrows=cfg.N)
+
+        def rows(tag, ids):
+            return ph.host_mat(cfg.wdtype, cfg.seed, tag, L, cfg.d, sig[tag], row_ids=ids)
+        g = dict(W1=rows(synth.TAG_W1, spec.T_g), W2=rows(synth.TAG_W2, spec.T_g),
+                 Wup=rows(synth.TAG_WUP, spec.T_g) if cfg.gated else None,
+                 b1=ph.host_vec(spec.b1[spec.T_g], cfg.bdtype))
+        c = None
+        if len(spec.T_c):
+            c = dict(W1=rows(synth.TAG_W1, spec.T_c), W2=rows(synth.TAG_W2, spec.T_c),
+                     Wup=rows(synth.TAG_WUP, spec.T_c) if cfg.gated else None,
+                     b1=ph.host_vec(spec.b1[spec.T_c], cfg.bdtype))
+        layers.append((spec, P1, P2, g, c))
+    kind = orc.GATED_RELU if cfg.gated else orc.RELU
+    t_total, n_done, step = 0.0, 0, 0
+    while True:
+        for (spec, P1, P2, g, c) in layers:
+            x = synth.host_x(cfg.seed, spec.layer, 10_000 + step, B, cfg.d)
+            t0 = time.perf_counter()
+            logits = orc.predict(x, P1, orc.Vec(None, cfg.bdtype), P2, ph.host_vec(spec.c2, cfg.bdtype))
+            A_g, A_c = orc.compact(logits, 0.0, spec.T_g, spec.T_c if c else None)
+            y_g = orc.sparse_ffn(x, g["W1"], g["b1"], g["W2"], A_g, kind=kind, Wup=g["Wup"])
+            y_c = orc.sparse_ffn(x, c["W1"], c["b1"], c["W2"], A_c, kind=kind, Wup=c["Wup"]) if c else None
+            orc.merge(y_g, y_c, len(A_c) if c else 0)
+            t_total += time.perf_counter() - t0
+            n_done += 1
+        step += 1
+        if t_total >= seconds:
+            break
+    per_layer = t_total / n_done
+    tok_s = B / (per_layer * cfg.n_layers)
+    return {"value": tok_s, "unit": "tokens/s", "cores": orc.get_threads(), "kind": "oracle",
+            "sample": f"{n_done} layer-steps (layers 0..{Ls - 1}, {step} steps, batch {B}) of the same workload "
+                      f"in {t_total:.1f} s, scaled to {cfg.n_layers} layers per token; includes the cold-neuron "
+                      f"side; weight generation not timed"}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
+              "(the multi-GPU sharding is a design note only).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import activation_sparse_amd as pi
+    from synth.device import DeviceLayer
+
+    cfg = synth.CONFIGS[args.config]
+    B = args.batch
+    n_layers = args.layers or cfg.n_layers
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    S = args.warmup + args.steps
+    t_setup = time.time()
+    specs = [synth.layer_spec(cfg, L) for L in range(n_layers)]
+    log(f"{cfg.key}: {n_layers} layer specs ready in {time.time() - t_setup:.1f} s")
+    dls = [DeviceLayer(s, dev) for s in specs]
+    torch.cuda.synchronize()
+    log(f"device weights generated ({torch.cuda.memory_allocated() / 2**30:.1f} GiB) at {time.time() - t_setup:.1f} s")
+    maxH = max(s.H for s in specs)
+    n_g = max(s.n_g for s in specs)
+    n_c = max(len(s.T_c) for s in specs)
+    d, N = cfg.d, cfg.N
+
+    class Buffers:
+        logits = torch.empty((B, N), dtype=torch.float32, device=dev)
+        A_g = torch.empty(max(n_g, 1), dtype=torch.int32, device=dev)
+        A_c = torch.empty(max(n_c, 1), dtype=torch.int32, device=dev)
+        y = torch.empty((B, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256),
+                         dtype=torch.uint8, device=dev)
+    buf = Buffers
+    # per-(step, layer) inputs, cold partials and counts
+    xs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev)
+    ycs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev) if n_c else None
+    Ks = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    Kcs = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in range(S):
+        rid = torch.from_numpy(synth.x_row_ids(t, B)).to(dev)
+        for L in range(n_layers):
+            synth.dev_fill(xs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_X, L, d, 1.0,
+                           row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+            if n_c:
+                synth.dev_fill(ycs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_YC, L, d, 0.05,
+                               row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+    torch.cuda.synchronize()
+    def layer_call(t, L, events=None):
+        spec, dl = specs[L], dls[L]
+        cold = len(spec.T_c) > 0
+        pi.pi_ffn_layer(dl.layer, B, xs[t, L], 0.0, ycs[t, L] if cold else None, buf.y, buf.logits, buf.A_g,
+                        Ks[t, L:L + 1], buf.A_c if cold else None, Kcs[t, L:L + 1] if cold else None, buf.ws,
+                        events=events, _cstruct=dl.layer_c)
+
+    def step_call(t):
+        for L in range(n_layers):
+            layer_call(t, L)
+
+    graphs = []
+    use_graph = not args.no_graph
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_call(0)          # eager warm-up of every kernel before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for t in range(S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_call(t)
+            graphs.append(g)
+        torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+    log(f"setup done in {setup_s:.1f} s (graphs: {len(graphs)}); timing {args.steps} steps")
+
+    def run_step(t):
+        if use_graph:
+            graphs[t].replay()
+        else:
+            step_call(t)
+
+    for t in range(args.warmup):
+        run_step(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for t in range(args.warmup, S):
+        run_step(t)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    elapsed_s = max(wall, gpu_ms / 1e3)
+    ms_per_step = elapsed_s * 1e3 / args.steps
+    tokens_s = B * args.steps / elapsed_s
+
+    # algorithmic bytes of the timed steps from the measured counts
+    Kh = Ks.cpu().numpy()
+    Kch = Kcs.cpu().numpy()
+    tot_pred = tot_ffn = tot_small = 0.0
+    for t in range(args.warmup, S):
+        for L in range(n_layers):
+            p, f, s = layer_bytes(specs[L], B, int(Kh[t, L]), int(Kch[t, L]))
+            tot_pred += p; tot_ffn += f; tot_small += s
+    step_bytes = (tot_pred + tot_ffn + tot_small) / args.steps
+    step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # per-kernel durations: pi_ffn_layer records 5 events between its kernels, over a few eager steps
+    names = ["hidden", "logits+mask", "fc1+list", "fc2", "reduce+merge"]
+    kern_ms = {k: [] for k in names}
+    kern_bytes = {k: [] for k in names}
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    handles = pi.event_handles(evs)
+    n_inst = min(4, S)
+    for t in range(S - n_inst, S):
+        for L in range(n_layers):
+            layer_call(t, L, events=handles)
+            torch.cuda.synchronize()
+            for i, k in enumerate(names):
+                kern_ms[k].append(evs[i].elapsed_time(evs[i + 1]))
+            kb = kernel_bytes(specs[L], B, int(Ks[t, L].item()), int(Kcs[t, L].item()))
+            for k in names:
+                kern_bytes[k].append(kb[k])
+    mean_ms = {k: float(np.mean(v)) for k, v in kern_ms.items()}
+    mean_bytes = {k: float(np.mean(v)) for k, v in kern_bytes.items()}
+    achieved = {k: mean_bytes[k] / (mean_ms[k] * 1e-3) / 1e9 for k in names}
+    dom = max(names, key=lambda k: mean_ms[k])
+    kernel_symbol = {"hidden": "k_hidden_b1", "logits+mask": "k_logits_b1", "fc1+list": "k_fc1_b1",
+                     "fc2": "k_fc2", "reduce+merge": "k_reduce"}
+    roofline = {"bound": "hbm", "achieved": round(achieved[dom], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved[dom] / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": kernel_symbol[dom] if B == 1 else dom,
+                "bytes_per_launch": round(mean_bytes[dom]), "avg_launch_us": round(mean_ms[dom] * 1e3, 2)}
+
+    log(f"timed: {ms_per_step:.4f} ms/step, {tokens_s:.1f} tokens/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(cfg, B, args.cpu_seconds, args.cpu_layers)
+
+    out = {
+        "metric": "sparse-FFN decode tokens/s at batch 1; achieved HBM GB/s vs peak",
+        "value": round(tokens_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {0: "f32", 1: "f16", 2: "int4"}[cfg.wdtype] + "-weights/f32-accumulate",
+        "data": "synthetic (seeded power-law-sparse layers, random-init weights, generated on device)",
+        "config": {"workload": cfg.desc, "key": cfg.key, "layers": n_layers, "batch": B, "d_model": d,
+                   "d_ffn": N, "predictor_hidden": maxH, "gpu_neurons": n_g, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": {"step_bytes": round(step_bytes), "step_gbps": round(step_gbs, 1),
+                   "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "bytes_split": {"predictor": round(tot_pred / args.steps), "ffn": round(tot_ffn / args.steps),
+                                   "small": round(tot_small / args.steps)},
+                   "mean_K": float(Kh[args.warmup:].mean()), "mean_K_cold": float(Kch[args.warmup:].mean()),
+                   "kernel_us": {k: round(v * 1e3, 2) for k, v in mean_ms.items()},
+                   "kernel_gbps": {k: round(v, 1) for k, v in achieved.items()},
+                   "graph": use_graph, "setup_s": round(setup_s, 1), "wall_s": round(wall, 4),
+                   "event_ms": round(gpu_ms, 3)},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

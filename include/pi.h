@@ -59,7 +59,7 @@ extern "C" {
 enum pi_dtype { PI_F32 = 0, PI_F16 = 1, PI_I4G128 = 2 };
 enum pi_ffn_kind { PI_RELU = 0, PI_GATED_RELU = 1 };
 enum pi_status { PI_OK = 0, PI_EINVAL = 1, PI_EWORKSPACE = 2, PI_EUNSUPPORTED = 3, PI_EHIP = 4 };
-enum pi_op { PI_OP_PREDICT = 0, PI_OP_COMPACT = 1, PI_OP_SPARSE_FFN = 2, PI_OP_MERGE = 3 };
+enum pi_op { PI_OP_PREDICT = 0, PI_OP_COMPACT = 1, PI_OP_SPARSE_FFN = 2, PI_OP_MERGE = 3, PI_OP_FFN_LAYER = 4 };
 
 /* A weight matrix on the device.  `scales` is used by PI_I4G128 only. */
 typedef struct pi_matrix {
@@ -127,6 +127,66 @@ int pi_sparse_ffn(void* stream, int32_t B, int32_t d, int32_t n_g, int32_t kind,
  * Errors: PI_EINVAL for a NULL y, B outside 1..PI_MAX_BATCH or d <= 0. */
 int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, const int32_t* K_c,
              pi_vector b2);
+
+/* ---------------------------------------------------------------------------
+ * Prepared neuron table and the fused layer call.
+ *
+ * The GPU neuron table T_g (slot -> original neuron id) in the form the fused
+ * kernels read: for each group of 32 original ids, a bitmap of the ids that
+ * are GPU-resident and the number of GPU-resident ids below the group.  The
+ * slot of a GPU-resident id is then its rank among the GPU-resident ids,
+ * which is what T_g gives when T_g is ascending; the CPU table is the
+ * ascending complement (CSDN summary, section 神经元放置和管理: one table per
+ * processing unit, both mapping neurons to their original positions).
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of a prepared table for N neurons. */
+size_t pi_table_bytes(int32_t N);
+
+/* Host-only (no HIP call): build the prepared table of T_g into the HOST
+ * buffer `table` (pi_table_bytes(N) bytes); the caller copies it to the
+ * device.  T_g [n_g] host int32 must be strictly ascending with ids in
+ * [0, N).  Errors: PI_EINVAL (NULL pointers, N <= 0, n_g outside 0..N, an id
+ * out of range or out of order), PI_EWORKSPACE (buffer too small). */
+int pi_table_prepare(int32_t N, const int32_t* T_g, int32_t n_g, void* table, size_t table_bytes);
+
+/* One FFN layer, all four steps: predictor, activation decision and
+ * compaction, neuron-aware FFN over the GPU-resident neurons, merge.
+ * Weights as for the separate calls; `table` is a device copy of the
+ * prepared table of the layer's T_g (W1, b1, Wup, W2 in that T_g's slot
+ * order).  With `cold` non-zero the neurons outside T_g are CPU-resident and
+ * their active ascending slots in the CPU table are listed in A_c / K_c. */
+typedef struct pi_layer {
+  int32_t d, N, H, n_g;
+  int32_t kind; /* PI_RELU | PI_GATED_RELU */
+  int32_t cold; /* non-zero: produce the CPU-side list A_c, K_c */
+  pi_matrix P1;
+  pi_vector c1;
+  pi_matrix P2;
+  pi_vector c2;
+  const void* table;
+  pi_matrix W1;
+  pi_vector b1;
+  pi_matrix Wup;
+  pi_matrix W2;
+  pi_vector b2;
+} pi_layer;
+
+/* y[b,:] = sum over active GPU-resident neurons (as pi_sparse_ffn)
+ *          + y_c[b,:] when y_c != NULL and (cold == 0 or *K_c != 0)
+ *          + b2.
+ * x [B x d] fp32, y [B x d] fp32 written.  logits [B x N] (optional, NULL =
+ * not stored).  A_g [n_g] and K (device) receive the GPU list and its count;
+ * A_c [N - n_g] and K_c the CPU list when cold != 0 (else they may be NULL).
+ * ws: pi_workspace_bytes(PI_OP_FFN_LAYER, B, d, H, N, n_g) bytes.
+ * events: NULL, or 6 hipEvent_t (any may be NULL) recorded on `stream`
+ * before the first kernel and after the predictor hidden layer, the output
+ * layer with the activation decision, FC1 with the list building, the FC2
+ * partial sums and the final ordered sum with the merge (per-kernel timing).
+ * Errors: as the separate calls. */
+int pi_ffn_layer(void* stream, const pi_layer* layer, int32_t B, const float* x, float tau,
+                 const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
+                 int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, void* const* events);
 
 /* Workspace bytes an entry point needs for these sizes (0 when none).
  * Arguments an op does not use are ignored. */

@@ -1,0 +1,78 @@
+"""Device-resident synthetic layers (weights generated on the GPU).
+
+Input generation only: allocates torch device tensors and fills them with the
+same bits the host generator produces.  Used by the GPU tests and the
+benchmark.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import synth
+from activation_sparse_amd import Matrix, Vector, PI_F32, PI_F16, PI_I4G128
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def dev_matrix(rows, cols, dtype, device):
+    torch = _torch()
+    if dtype == synth.F32:
+        return Matrix(torch.empty((rows, cols), dtype=torch.float32, device=device), PI_F32)
+    if dtype == synth.F16:
+        return Matrix(torch.empty((rows, cols), dtype=torch.float16, device=device), PI_F16)
+    return Matrix(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device), PI_I4G128,
+                  torch.empty((rows, cols // 128), dtype=torch.int16, device=device))
+
+
+def fill_matrix(m, dtype, seed, tag, layer, cols, sigma, row_ids_dev=None, nrows=None):
+    torch = _torch()
+    n = m.data.shape[0] if nrows is None else nrows
+    synth.dev_fill(m.data.data_ptr(), m.scales.data_ptr() if m.scales is not None else None, dtype, seed, tag,
+                   layer, cols, sigma, row_ids_ptr=row_ids_dev.data_ptr() if row_ids_dev is not None else None,
+                   nrows=n, stream=torch.cuda.current_stream().cuda_stream)
+
+
+def dev_vector(stored: np.ndarray, dtype: int, device):
+    torch = _torch()
+    if dtype == synth.F32:
+        return Vector(torch.from_numpy(np.ascontiguousarray(stored, np.float32)).to(device), PI_F32)
+    t = torch.from_numpy(np.ascontiguousarray(stored).view(np.int16)).to(device).view(torch.float16)
+    return Vector(t, PI_F16)
+
+
+class DeviceLayer:
+    """One layer's GPU-resident tensors, generated on the device."""
+
+    def __init__(self, spec: synth.LayerSpec, device="cuda:0"):
+        torch = _torch()
+        cfg, L = spec.cfg, spec.layer
+        sig = spec.sigmas()
+        self.spec = spec
+        d, N, H, n_g = cfg.d, cfg.N, spec.H, spec.n_g
+        self.T_g = torch.from_numpy(spec.T_g).to(device)
+        self.T_c = torch.from_numpy(spec.T_c).to(device) if len(spec.T_c) else None
+        self.P1 = dev_matrix(H, d, cfg.pdtype, device)
+        fill_matrix(self.P1, cfg.pdtype, cfg.seed, synth.TAG_P1, L, d, sig[synth.TAG_P1])
+        self.P2 = dev_matrix(N, H, cfg.pdtype, device)
+        fill_matrix(self.P2, cfg.pdtype, cfg.seed, synth.TAG_P2, L, H, sig[synth.TAG_P2])
+        self.c1 = None
+        self.c2 = dev_vector(spec.c2, cfg.bdtype, device)
+        self.W1 = dev_matrix(max(n_g, 1), d, cfg.wdtype, device)
+        self.W2 = dev_matrix(max(n_g, 1), d, cfg.wdtype, device)
+        self.Wup = dev_matrix(max(n_g, 1), d, cfg.wdtype, device) if cfg.gated else None
+        if n_g:
+            fill_matrix(self.W1, cfg.wdtype, cfg.seed, synth.TAG_W1, L, d, sig[synth.TAG_W1], self.T_g, n_g)
+            fill_matrix(self.W2, cfg.wdtype, cfg.seed, synth.TAG_W2, L, d, sig[synth.TAG_W2], self.T_g, n_g)
+            if cfg.gated:
+                fill_matrix(self.Wup, cfg.wdtype, cfg.seed, synth.TAG_WUP, L, d, sig[synth.TAG_WUP], self.T_g, n_g)
+        self.b1 = dev_vector(spec.b1[spec.T_g] if n_g else spec.b1[:1], cfg.bdtype, device)
+        from activation_sparse_amd import pi_table_prepare, Layer, PI_RELU, PI_GATED_RELU
+        self.table = torch.from_numpy(pi_table_prepare(N, spec.T_g)).to(device)
+        self.layer = Layer(d, N, H, n_g, PI_GATED_RELU if cfg.gated else PI_RELU, len(spec.T_c) > 0, self.P1,
+                           self.c1, self.P2, self.c2, self.table, self.W1, self.b1, self.Wup, self.W2, None)
+        self.layer_c = self.layer._c()
+
+

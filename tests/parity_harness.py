@@ -38,67 +38,14 @@ def small_case(key="small", d=256, N=1024, H=64, wdtype=synth.F16, pdtype=None, 
                               rho=rho, alpha=alpha, gpu_frac=gpu_frac, seed=seed)
 
 
-# ----------------------------------------------------------------------------- device tensors
+# ----------------------------------------------------------------------------- device buffers
+
+from synth.device import DeviceLayer, dev_matrix, fill_matrix, dev_vector  # noqa: E402,F401
+
 
 def _torch():
     import torch
     return torch
-
-
-def dev_matrix(rows, cols, dtype, device):
-    import activation_sparse_amd as pi
-    torch = _torch()
-    if dtype == synth.F32:
-        return pi.Matrix(torch.empty((rows, cols), dtype=torch.float32, device=device), pi.PI_F32)
-    if dtype == synth.F16:
-        return pi.Matrix(torch.empty((rows, cols), dtype=torch.float16, device=device), pi.PI_F16)
-    return pi.Matrix(torch.empty((rows, cols // 2), dtype=torch.uint8, device=device), pi.PI_I4G128,
-                     torch.empty((rows, cols // 128), dtype=torch.int16, device=device))
-
-
-def fill_matrix(m, dtype, seed, tag, layer, cols, sigma, row_ids_dev=None, nrows=None):
-    torch = _torch()
-    n = m.data.shape[0] if nrows is None else nrows
-    synth.dev_fill(m.data.data_ptr(), m.scales.data_ptr() if m.scales is not None else None, dtype, seed, tag,
-                   layer, cols, sigma, row_ids_ptr=row_ids_dev.data_ptr() if row_ids_dev is not None else None,
-                   nrows=n, stream=torch.cuda.current_stream().cuda_stream)
-
-
-def dev_vector(stored: np.ndarray, dtype: int, device):
-    import activation_sparse_amd as pi
-    torch = _torch()
-    if dtype == synth.F32:
-        return pi.Vector(torch.from_numpy(np.ascontiguousarray(stored, np.float32)).to(device), pi.PI_F32)
-    t = torch.from_numpy(np.ascontiguousarray(stored).view(np.int16)).to(device).view(torch.float16)
-    return pi.Vector(t, pi.PI_F16)
-
-
-class DeviceLayer:
-    """One layer's GPU-resident tensors, generated on the device."""
-
-    def __init__(self, spec: synth.LayerSpec, device="cuda:0"):
-        torch = _torch()
-        cfg, L = spec.cfg, spec.layer
-        sig = spec.sigmas()
-        self.spec = spec
-        d, N, H, n_g = cfg.d, cfg.N, spec.H, spec.n_g
-        self.T_g = torch.from_numpy(spec.T_g).to(device)
-        self.T_c = torch.from_numpy(spec.T_c).to(device) if len(spec.T_c) else None
-        self.P1 = dev_matrix(H, d, cfg.pdtype, device)
-        fill_matrix(self.P1, cfg.pdtype, cfg.seed, synth.TAG_P1, L, d, sig[synth.TAG_P1])
-        self.P2 = dev_matrix(N, H, cfg.pdtype, device)
-        fill_matrix(self.P2, cfg.pdtype, cfg.seed, synth.TAG_P2, L, H, sig[synth.TAG_P2])
-        self.c1 = None
-        self.c2 = dev_vector(spec.c2, cfg.bdtype, device)
-        self.W1 = dev_matrix(max(n_g, 1), d, cfg.wdtype, device)
-        self.W2 = dev_matrix(max(n_g, 1), d, cfg.wdtype, device)
-        self.Wup = dev_matrix(max(n_g, 1), d, cfg.wdtype, device) if cfg.gated else None
-        if n_g:
-            fill_matrix(self.W1, cfg.wdtype, cfg.seed, synth.TAG_W1, L, d, sig[synth.TAG_W1], self.T_g, n_g)
-            fill_matrix(self.W2, cfg.wdtype, cfg.seed, synth.TAG_W2, L, d, sig[synth.TAG_W2], self.T_g, n_g)
-            if cfg.gated:
-                fill_matrix(self.Wup, cfg.wdtype, cfg.seed, synth.TAG_WUP, L, d, sig[synth.TAG_WUP], self.T_g, n_g)
-        self.b1 = dev_vector(spec.b1[spec.T_g] if n_g else spec.b1[:1], cfg.bdtype, device)
 
 
 class DeviceBuffers:
@@ -120,6 +67,8 @@ class DeviceBuffers:
         wf = pi.pi_workspace_bytes(pi.PI_OP_SPARSE_FFN, B, d, H, N, n_g)
         self.ws_pred = torch.empty(max(wp, 256), dtype=torch.uint8, device=device)
         self.ws_ffn = torch.empty(max(wf, 256), dtype=torch.uint8, device=device)
+        wl = pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, H, N, n_g)
+        self.ws_layer = torch.empty(max(wl, 256), dtype=torch.uint8, device=device)
 
 
 def run_gpu_layer(dl: DeviceLayer, buf: DeviceBuffers, B: int, tau: float = 0.0, y_c=None, with_cold=True,
@@ -195,9 +144,28 @@ def rel_err(y_gpu: np.ndarray, y_or: np.ndarray) -> float:
     return worst
 
 
+def _gpu_stages(dl, buf, B, tau, with_cold, fused, y_c=None):
+    """Run the layer on the GPU; fused = one pi_ffn_layer call, else the four calls."""
+    import activation_sparse_amd as pi
+    spec = dl.spec
+    cold = with_cold and len(spec.T_c) > 0
+    if fused:
+        layer = dl.layer
+        if layer.cold != cold:
+            from dataclasses import replace as _r
+            layer = _r(layer, cold=cold)
+        ws = buf.ws_layer
+        pi.pi_ffn_layer(layer, B, buf.x, tau, y_c, buf.y, buf.logits, buf.A_g, buf.K, buf.A_c if cold else None,
+                        buf.K_c if cold else None, ws)
+    else:
+        run_gpu_layer(dl, buf, B, tau, y_c=None, with_cold=with_cold)
+        if y_c is not None:
+            pi.pi_merge(B, spec.cfg.d, buf.y, y_c, buf.K_c if cold else None, None)
+
+
 def run_layer_parity(cfg: synth.Config, layer: int = 0, step: int = 0, B: int = 1, tau: float = 0.0,
                      device="cuda:0", with_cold=True, x_override: Optional[np.ndarray] = None,
-                     tau_all_active: bool = False):
+                     tau_all_active: bool = False, fused: bool = False):
     """Full parity of one layer at batch B; returns a report dict."""
     torch = _torch()
     spec = synth.layer_spec(cfg, layer)
@@ -209,9 +177,7 @@ def run_layer_parity(cfg: synth.Config, layer: int = 0, step: int = 0, B: int = 
     dl = DeviceLayer(spec, device)
     buf = DeviceBuffers(cfg, spec.H, spec.n_g, n_c, B, device)
     buf.x.copy_(torch.from_numpy(x))
-    # oracle predictor and cold partial need the GPU's cold list first: run compaction, then merge
-    import activation_sparse_amd as pi
-    run_gpu_layer(dl, buf, B, tau, y_c=None, with_cold=with_cold)
+    _gpu_stages(dl, buf, B, tau, with_cold, fused)
     torch.cuda.synchronize()
     logits_gpu = buf.logits.cpu().numpy()
     K = int(buf.K.cpu()[0])
@@ -229,7 +195,7 @@ def run_layer_parity(cfg: synth.Config, layer: int = 0, step: int = 0, B: int = 
         mis_c, out_c, asc_c = list_check(A_c, A_c_or, spec.T_c, logits_or, tau)
 
     y_g_or = oracle_ffn_on_ids(spec, x, spec.T_g[A_g])
-    report = dict(cfg=cfg.key, layer=layer, step=step, B=B, K=K, K_c=K_c, n_g=spec.n_g,
+    report = dict(cfg=cfg.key, layer=layer, step=step, B=B, fused=fused, K=K, K_c=K_c, n_g=spec.n_g,
                   logit_max_abs_err=float(np.max(np.abs(logits_gpu.astype(np.float64) - logits_or))),
                   list_mismatch=mis_g + mis_c, list_outside_band=out_g + out_c, ascending=asc_g and asc_c,
                   rel_err_ffn=rel_err(y_g_gpu, y_g_or))
@@ -238,8 +204,15 @@ def run_layer_parity(cfg: synth.Config, layer: int = 0, step: int = 0, B: int = 
         y_c_or = oracle_ffn_on_ids(spec, x, spec.T_c[A_c])
         y_c32 = y_c_or.astype(np.float32)
         buf.y_c.copy_(torch.from_numpy(y_c32))
-        pi.pi_merge(B, d, buf.y, buf.y_c, buf.K_c, None)
+        if fused:
+            _gpu_stages(dl, buf, B, tau, with_cold, fused, y_c=buf.y_c)
+        else:
+            import activation_sparse_amd as pi
+            pi.pi_merge(B, d, buf.y, buf.y_c, buf.K_c, None)
         torch.cuda.synchronize()
+        if fused:   # the second call recomputes everything: its lists must be the same
+            assert int(buf.K.cpu()[0]) == K and np.array_equal(buf.A_g.cpu().numpy()[:K], A_g)
+            assert int(buf.K_c.cpu()[0]) == K_c
         y_final_or = orc.merge(y_g_or, y_c32.astype(np.float64), K_c)
     report["rel_err"] = rel_err(buf.y.cpu().numpy(), y_final_or)
     report["y_norm"] = float(np.max(np.abs(y_final_or))) if y_final_or.size else 0.0

@@ -61,31 +61,53 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("cfg", SMALL, ids=[c.key for c in SMALL])
 @pytest.mark.parametrize("B", [1, 3, 8])
-def test_small_layer_parity(cfg, B):
+def test_small_layer_parity(cfg, B, fused):
     _dev()
-    _run(cfg, layer=0, step=1, B=B)
+    _run(cfg, layer=0, step=1, B=B, fused=fused)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("B", [16, 32])
-def test_large_batch_union(B):
+def test_large_batch_union(B, fused):
     _dev()
-    r = _run(SMALL[6], layer=0, step=2, B=B)
+    r = _run(SMALL[6], layer=0, step=2, B=B, fused=fused)
     assert r["K"] > 0
 
 
-def test_all_active_list_is_the_whole_table():
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("B", [1, 2])
+def test_all_active_list_is_the_whole_table(B, fused):
     _dev()
     cfg = SMALL[2]
-    r = _run(cfg, layer=0, step=0, B=2, tau_all_active=True)
+    r = _run(cfg, layer=0, step=0, B=B, tau_all_active=True, fused=fused)
     assert r["K"] == cfg.N
 
 
-def test_empty_list_gives_zero_output():
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_empty_list_gives_zero_output(fused):
     _dev()
-    r = _run(SMALL[6], layer=0, step=0, B=1, tau=1e30)
+    r = _run(SMALL[6], layer=0, step=0, B=1, tau=1e30, fused=fused)
     assert r["K"] == 0 and r["K_c"] == 0 and r["y_norm"] == 0.0
+
+
+def test_fused_and_separate_paths_give_identical_bits():
+    torch = _dev()
+    for cfg in (SMALL[2], SMALL[6]):
+        spec = synth.layer_spec(cfg, 0)
+        dl = ph.DeviceLayer(spec)
+        outs = []
+        for fused in (False, True):
+            buf = ph.DeviceBuffers(cfg, spec.H, spec.n_g, len(spec.T_c), 1)
+            buf.x.copy_(torch.from_numpy(synth.host_x(cfg.seed, 0, 9, 1, cfg.d)))
+            ph._gpu_stages(dl, buf, 1, 0.0, True, fused)
+            torch.cuda.synchronize()
+            K = int(buf.K.cpu()[0])
+            outs.append((K, buf.A_g.cpu().numpy()[:K].tobytes(), buf.logits.cpu().numpy().tobytes(),
+                         buf.y.cpu().numpy().tobytes()))
+        assert outs[0] == outs[1], cfg.key
 
 
 def test_outputs_are_bitwise_repeatable():
@@ -110,7 +132,8 @@ FULL = [("opt-768", 0, 1), ("opt-6.7b", 5, 1), ("llama-13b-gated", 7, 1), ("opt-
         ("opt-30b", 11, 16), ("opt-30b", 11, 32), ("opt-175b-int4", 42, 1)]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("key,layer,B", FULL, ids=[f"{k}-L{l}-B{b}" for k, l, b in FULL])
-def test_full_size_layer_parity(key, layer, B):
+def test_full_size_layer_parity(key, layer, B, fused):
     _dev()
-    _run(synth.CONFIGS[key], layer=layer, step=3, B=B)
+    _run(synth.CONFIGS[key], layer=layer, step=3, B=B, fused=fused)
