@@ -22,7 +22,7 @@ PI_MAX_BATCH = 32
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpi.so")
 
-EXPORTS = ("pi_predict", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes", "pi_table_prepare",
+EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes", "pi_table_prepare",
            "pi_ffn_layer", "pi_workspace_bytes", "pi_status_string", "pi_last_hip_error", "pi_abi_version")
 
 
@@ -56,6 +56,8 @@ def load():
         L = C.CDLL(LIB_PATH)
         P, I = C.c_void_p, C.c_int32
         L.pi_predict.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Vec, P, P, C.c_size_t]
+        L.pi_predict_output.argtypes = [P, I, I, I, P, _Mat, _Vec, C.c_float, P, P]
+        L.pi_predict_output.restype = C.c_int
         L.pi_compact.argtypes = [P, I, I, P, C.c_float, P, I, P, P, P, I, P, P, P, C.c_size_t]
         L.pi_sparse_ffn.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Mat, P, P, P, P, C.c_size_t]
         L.pi_merge.argtypes = [P, I, I, P, P, P, _Vec]
@@ -138,6 +140,11 @@ def pi_predict(B, d, H, N, x, P1: Matrix, c1: Vector, P2: Matrix, c2: Vector, lo
     nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
     _check(load().pi_predict(_stream(stream), B, d, H, N, _ptr(x), P1._c(), (c1 or _NO_VEC)._c(), P2._c(),
                              (c2 or _NO_VEC)._c(), _ptr(logits), _ptr(ws), nbytes), "pi_predict")
+
+
+def pi_predict_output(B, H, N, h, P2: Matrix, c2: Vector, tau, logits, mask=None, stream=None) -> None:
+    _check(load().pi_predict_output(_stream(stream), B, H, N, _ptr(h), P2._c(), (c2 or _NO_VEC)._c(), float(tau),
+                                    _ptr(logits), _ptr(mask)), "pi_predict_output")
 
 
 def pi_compact(B, N, logits, tau, T_g, n_g, A_g, K, T_c=None, n_c=0, A_c=None, K_c=None, stream=None) -> None:

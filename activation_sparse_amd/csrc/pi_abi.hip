@@ -56,31 +56,44 @@ FfnWs ffn_ws_layout(void* ws, int32_t B, int32_t d, int32_t n_g) {
   Carver c{static_cast<char*>(ws)};
   FfnWs w{};
   w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
-  w.partials = c.take<float>((size_t)pi::kFc2Chunks * B * (size_t)d * 4);
+  w.partials = c.take<float>((size_t)pi::fc2_chunks(B) * B * (size_t)d * 4);
   w.bytes = c.off;
   return w;
 }
 
-// Fused layer workspace: h, logits scratch, activation words, a, partials.
+// Fused layer workspace: h, logits scratch, activation words, the per-64-id
+// block segments of the batch-1 path, a, partials.
 struct LayerWs {
   float* h;
   float* logits;
   uint32_t* mask;
+  int32_t* seg_slot;
+  float* seg_a;
+  int32_t* seg_cold;
+  uint32_t* cnt;
   float* a;
   float* partials;
   size_t bytes;
 };
 
 size_t table_words(int32_t N) { return 2 * (size_t)((N + 63) / 64); }
+size_t n_blocks64(int32_t N) { return (size_t)((N + 63) / 64); }
 
 LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g) {
   Carver c{static_cast<char*>(ws)};
   LayerWs w{};
+  const size_t nb = n_blocks64(N);
   w.h = c.take<float>((size_t)B * H * 4);
   w.logits = c.take<float>((size_t)B * N * 4);
   w.mask = c.take<uint32_t>(table_words(N) * 4);
+  w.seg_slot = c.take<int32_t>(nb * 64 * 4);
+  w.seg_a = c.take<float>(nb * 64 * 4);
+  w.seg_cold = c.take<int32_t>(nb * 64 * 4);
+  w.cnt = c.take<uint32_t>(nb * 4);
   w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
-  w.partials = c.take<float>((size_t)pi::kFc2Chunks * B * (size_t)d * 4);
+  const size_t ch = (size_t)pi::fc2_chunks(B) * B > (size_t)pi::kSegChunks ? (size_t)pi::fc2_chunks(B) * B
+                                                                          : (size_t)pi::kSegChunks;
+  w.partials = c.take<float>(ch * (size_t)d * 4);
   w.bytes = c.off;
   return w;
 }
@@ -116,7 +129,7 @@ size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N
   }
 }
 
-size_t pi_table_bytes(int32_t N) { return N > 0 ? table_words(N) * 4 : 0; }
+size_t pi_table_bytes(int32_t N) { return N > 0 ? (table_words(N) + n_blocks64(N)) * 4 : 0; }
 
 int pi_table_prepare(int32_t N, const int32_t* T_g, int32_t n_g, void* table, size_t table_bytes) {
   if (N <= 0 || n_g < 0 || n_g > N || !table || (n_g > 0 && !T_g)) return PI_EINVAL;
@@ -128,6 +141,12 @@ int pi_table_prepare(int32_t N, const int32_t* T_g, int32_t n_g, void* table, si
   }
   memset(bits, 0, W * 4);
   for (int32_t s = 0; s < n_g; ++s) bits[T_g[s] / 32] |= 1u << (T_g[s] % 32);
+  int32_t* pre = reinterpret_cast<int32_t*>(bits + W);
+  int32_t run = 0;
+  for (size_t b = 0; b < W / 2; ++b) {  // 64-id blocks
+    pre[b] = run;
+    run += __builtin_popcount(bits[2 * b]) + __builtin_popcount(bits[2 * b + 1]);
+  }
   return PI_OK;
 }
 
@@ -164,6 +183,27 @@ int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const f
   return hip_status(pi::launch_rowdot(b, s));
 }
 
+int pi_predict_output(void* stream, int32_t B, int32_t H, int32_t N, const float* h, pi_matrix P2, pi_vector c2,
+                      float tau, float* logits, uint32_t* mask) {
+  if (!valid_batch(B) || H <= 0 || N <= 0 || !h || !aligned16(h) || !valid_matrix(P2, H) || !valid_vector(c2))
+    return PI_EINVAL;
+  if (!logits && (B != 1 || !mask)) return PI_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (B == 1 && pi::b1_supported(P2.dtype, H)) {
+    pi::B1Gemv o{};
+    o.W = P2.data; o.Ws = P2.scales; o.dt = P2.dtype; o.rows = N; o.cols = H; o.x = h;
+    o.bias = c2.data; o.bias_dt = c2.dtype; o.out = logits;
+    return hip_status(pi::launch_logits_b1(o, tau, reinterpret_cast<uint8_t*>(mask), s));
+  }
+  pi::RowdotArgs b{};
+  b.W = P2.data; b.Ws = P2.scales; b.dt = P2.dtype; b.cols = H;
+  b.count_max = N; b.x = h; b.B = B; b.bias = c2.data; b.bias_dt = c2.dtype;
+  b.relu = 0; b.out = logits; b.out_stride = N;
+  int st = hip_status(pi::launch_rowdot(b, s));
+  if (st != PI_OK || !mask) return st;
+  return hip_status(pi::launch_mask(B, N, logits, tau, mask, s));
+}
+
 int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float tau, const int32_t* T_g,
                int32_t n_g, int32_t* A_g, int32_t* K, const int32_t* T_c, int32_t n_c, int32_t* A_c,
                int32_t* K_c, void* ws, size_t ws_bytes) {
@@ -192,12 +232,12 @@ int validate_ffn(int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x
   return PI_OK;
 }
 
-// FC1 (list given, or built from activation words when lc != NULL on the batch-1
-// path), then FC2 partials, then the ordered reduction + merge.
+// FC1 over a given list, then FC2 partials, then the ordered reduction + merge.
+// ev (optional, 2 entries) is recorded after FC1 and after FC2.
 int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x, const pi_matrix& W1,
                 const pi_vector& b1, const pi_matrix& Wup, const pi_matrix& W2, const int32_t* A_g, const int32_t* K,
-                const pi::ListCtx* lc, float* a, float* partials, float* y, const float* y_c, const int32_t* K_c,
-                const pi_vector& b2, const hipEvent_t* ev) {
+                float* a, float* partials, float* y, const float* y_c, const int32_t* K_c, const pi_vector& b2,
+                const hipEvent_t* ev) {
   const bool gated = kind == PI_GATED_RELU;
   int st;
   if (B == 1 && pi::b1_supported(W1.dtype, d)) {
@@ -205,9 +245,8 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
     g.W = W1.data; g.Ws = W1.scales; g.dt = W1.dtype; g.rows = n_g; g.cols = d; g.x = x;
     if (gated) { g.Wu = Wup.data; g.Wus = Wup.scales; }
     g.bias = b1.data; g.bias_dt = b1.dtype; g.out = a; g.list = A_g; g.Kp = K;
-    st = hip_status(pi::launch_fc1_b1(g, gated, lc, s));
+    st = n_g > 0 ? hip_status(pi::launch_fc1_b1(g, gated, s)) : PI_OK;
   } else {
-    if (lc && (st = hip_status(pi::launch_list(*lc, n_g, s))) != PI_OK) return st;
     pi::RowdotArgs r{};
     r.W = W1.data; r.Ws = W1.scales; r.dt = W1.dtype; r.cols = d; r.gated = gated;
     if (gated) { r.Wup = Wup.data; r.Wups = Wup.scales; }
@@ -224,7 +263,7 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
   if ((st = hip_status(pi::launch_fc2(f, s))) != PI_OK) return st;
   if (ev && ev[1] && (st = hip_status(hipEventRecord(ev[1], s))) != PI_OK) return st;
   pi::ReduceArgs r{};
-  r.partials = partials; r.chunks = pi::kFc2Chunks; r.B = B; r.d = d; r.y = y;
+  r.partials = partials; r.chunks = pi::fc2_chunks(B); r.B = B; r.d = d; r.y = y;
   r.y_c = y_c; r.K_c = K_c; r.b2 = b2.data; r.b2_dt = b2.dtype;
   return hip_status(pi::launch_reduce(r, s));
 }
@@ -240,8 +279,8 @@ int pi_sparse_ffn(void* stream, int32_t B, int32_t d, int32_t n_g, int32_t kind,
   if (!ws || !aligned16(ws)) return PI_EWORKSPACE;
   const FfnWs w = ffn_ws_layout(ws, B, d, n_g);
   if (ws_bytes < w.bytes) return PI_EWORKSPACE;
-  return enqueue_ffn(static_cast<hipStream_t>(stream), B, d, n_g, kind, x, W1, b1, Wup, W2, A_g, K, nullptr, w.a,
-                     w.partials, y_g, nullptr, nullptr, pi_vector{nullptr, PI_F32}, nullptr);
+  return enqueue_ffn(static_cast<hipStream_t>(stream), B, d, n_g, kind, x, W1, b1, Wup, W2, A_g, K, w.a, w.partials,
+                     y_g, nullptr, nullptr, pi_vector{nullptr, PI_F32}, nullptr);
 }
 
 int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, const int32_t* K_c, pi_vector b2) {
@@ -276,10 +315,14 @@ int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, flo
   lc.mask = w.mask; lc.gbits = static_cast<const uint32_t*>(L->table); lc.W = (int)table_words(N);
   lc.A_g = A_g; lc.K = K; lc.A_c = L->cold ? A_c : nullptr; lc.K_c = L->cold ? K_c : nullptr;
   float* lg = logits ? logits : w.logits;
+  const bool gated = L->kind == PI_GATED_RELU;
+  const bool b1_pred = B == 1 && pi::b1_supported(L->P1.dtype, d) && pi::b1_supported(L->P2.dtype, H);
+  const bool b1_ffn = B == 1 && pi::b1_supported(L->W1.dtype, d);
+  (void)b1_ffn;
 
   if ((st = record(0)) != PI_OK) return st;
-  const bool fast = B == 1 && pi::b1_supported(L->P1.dtype, d) && pi::b1_supported(L->P2.dtype, H);
-  if (fast) {
+  // predictor: hidden layer, then output layer with the activation decision
+  if (b1_pred) {
     pi::B1Gemv g{};
     g.W = L->P1.data; g.Ws = L->P1.scales; g.dt = L->P1.dtype; g.rows = H; g.cols = d; g.x = x;
     g.bias = L->c1.data; g.bias_dt = L->c1.dtype; g.out = w.h;
@@ -288,7 +331,7 @@ int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, flo
     pi::B1Gemv o{};
     o.W = L->P2.data; o.Ws = L->P2.scales; o.dt = L->P2.dtype; o.rows = N; o.cols = H; o.x = w.h;
     o.bias = L->c2.data; o.bias_dt = L->c2.dtype; o.out = logits;
-    if ((st = hip_status(pi::launch_logits_b1(o, tau, w.mask, s))) != PI_OK) return st;
+    if ((st = hip_status(pi::launch_logits_b1(o, tau, reinterpret_cast<uint8_t*>(w.mask), s))) != PI_OK) return st;
   } else {
     pi::RowdotArgs a{};
     a.W = L->P1.data; a.Ws = L->P1.scales; a.dt = L->P1.dtype; a.cols = d;
@@ -304,7 +347,34 @@ int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, flo
     if ((st = hip_status(pi::launch_mask(B, N, lg, tau, w.mask, s))) != PI_OK) return st;
   }
   if ((st = record(2)) != PI_OK) return st;
-  st = enqueue_ffn(s, B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2, A_g, K, &lc, w.a, w.partials, y, y_c,
+
+  const int nblk = (int)n_blocks64(N);
+  if (b1_pred && b1_ffn && pi::fc1_blk_supported(L->W1.dtype, d) && nblk <= 64 * pi::kSegChunks) {
+    // FC1 per 64-id block -> FC2 over the block segments -> ordered sum + merge + lists
+    pi::SegCtx sg{};
+    sg.gbits = lc.gbits; sg.gpre = reinterpret_cast<const int32_t*>(lc.gbits + table_words(N));
+    sg.W1 = L->W1.data; sg.W1s = L->W1.scales; sg.Wu = L->Wup.data; sg.Wus = L->Wup.scales; sg.d = d; sg.n_g = n_g;
+    sg.x = x; sg.b1 = L->b1.data; sg.b1_dt = L->b1.dtype;
+    sg.seg_slot = w.seg_slot; sg.seg_a = w.seg_a; sg.seg_cold = w.seg_cold; sg.cnt = w.cnt;
+    if ((st = hip_status(pi::launch_fc1_blk(w.mask, sg, L->W1.dtype, gated, nblk, s))) != PI_OK) return st;
+    if ((st = record(3)) != PI_OK) return st;
+    pi::Fc2SegArgs f{};
+    f.W2 = L->W2.data; f.W2s = L->W2.scales; f.dt = L->W2.dtype; f.d = d; f.n_g = n_g; f.nblk = nblk;
+    f.seg_slot = w.seg_slot; f.seg_a = w.seg_a; f.cnt = w.cnt; f.partials = w.partials;
+    if ((st = hip_status(pi::launch_fc2_seg(f, s))) != PI_OK) return st;
+    if ((st = record(4)) != PI_OK) return st;
+    pi::ReduceListArgs r{};
+    r.partials = w.partials; r.d = d; r.y = y; r.y_c = y_c; r.b2 = L->b2.data; r.b2_dt = L->b2.dtype;
+    r.nblk = nblk; r.cnt = w.cnt; r.seg_slot = w.seg_slot; r.seg_cold = w.seg_cold;
+    r.A_g = A_g; r.K = K; r.A_c = L->cold ? A_c : nullptr; r.K_c = L->cold ? K_c : nullptr;
+    r.n_g = n_g; r.n_c = N - n_g;
+    r.always_c = !L->cold;  // no cold side: y_c (if any) is always added
+    if ((st = hip_status(pi::launch_reduce_lists(r, s))) != PI_OK) return st;
+    return record(5);
+  }
+  // any batch: lists from the activation words, then FC1 / FC2 / reduction over the list
+  if ((st = hip_status(pi::launch_list(lc, n_g, s))) != PI_OK) return st;
+  st = enqueue_ffn(s, B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2, A_g, K, w.a, w.partials, y, y_c,
                    L->cold ? K_c : nullptr, L->b2, ev + 3);
   if (st != PI_OK) return st;
   return record(5);

@@ -58,15 +58,54 @@ __host__ __device__ __forceinline__ int64_t row_bytes(int dt, int64_t cols) {
   return dt == 0 ? cols * 4 : dt == 1 ? cols * 2 : cols / 2;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+// DPP move within a 16-lane row (CTRL: row_ror:n = 0x120 + n).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each 16-lane row, returned in every lane of the row (rotations by
+// 8, 4, 2, 1; each lane's association order is fixed).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_mov<0x128>(v);
+  v += dpp_mov<0x124>(v);
+  v += dpp_mov<0x122>(v);
+  v += dpp_mov<0x121>(v);
   return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes of a wave, wave-uniform, in a fixed order: the four
+// row sums (lanes 0, 16, 32, 48) added pairwise.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 __device__ __forceinline__ float load_bias(const void* p, int dt, int64_t i) {
   if (!p) return 0.f;
   return dt == 0 ? reinterpret_cast<const float*>(p)[i] : h2f(reinterpret_cast<const uint16_t*>(p)[i]);
 }
+
+// Zero read through by bias loads when a bias is absent (stride 0), so that the
+// loads stay branch-free.
+__device__ const uint32_t kZeroWord[4] = {0u, 0u, 0u, 0u};
+
+// Branch-free bias access for a bias dtype fixed at compile time (BDT: 0 fp32,
+// 1 fp16).  Issue it before the weight loads of the same row: the in-order
+// vmcnt then lets its value be used without waiting for the weights.
+template <int BDT>
+struct Bias {
+  const void* p;
+  int stride;
+  __device__ __forceinline__ Bias(const void* q) : p(q ? q : (const void*)kZeroWord), stride(q ? 1 : 0) {}
+  __device__ __forceinline__ float operator()(int64_t i) const {
+    if constexpr (BDT == 0) return reinterpret_cast<const float*>(p)[i * stride];
+    else return h2f(reinterpret_cast<const uint16_t*>(p)[i * stride]);
+  }
+};
 
 }  // namespace pi

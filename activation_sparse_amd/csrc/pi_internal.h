@@ -57,10 +57,69 @@ struct B1Gemv {
 };
 bool b1_supported(int dt, int64_t cols);
 hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s);
-// lc == NULL: list and count are inputs; else the kernel builds them (see pi_list.h).
-hipError_t launch_fc1_b1(const B1Gemv& g, bool gated, const ListCtx* lc, hipStream_t s);
-// Output layer; mask != NULL also writes the activation words (2 per 64 rows).
-hipError_t launch_logits_b1(const B1Gemv& g, float tau, uint32_t* mask, hipStream_t s);
+hipError_t launch_fc1_b1(const B1Gemv& g, bool gated, hipStream_t s);
+
+// Output layer; mask8 != NULL also writes the activation bits, 8 rows per byte.
+hipError_t launch_logits_b1(const B1Gemv& g, float tau, uint8_t* mask8, hipStream_t s);
+
+// FC1 of the fused batch-1 layer, one 64-id block per 512-thread block (see pi_fast.hip).
+struct SegCtx {
+  const uint32_t* gbits;     // prepared table: GPU-resident bitmap, 2 words per 64 ids
+  const int32_t* gpre;       // prepared table: GPU-resident ids below each 64-id block
+  const void* W1;
+  const uint16_t* W1s;
+  const void* Wu;
+  const uint16_t* Wus;
+  int d;
+  int n_g;
+  const float* x;
+  const void* b1;
+  int b1_dt;
+  int32_t* seg_slot;         // [nblk x 64] ascending slots of each block's active GPU neurons
+  float* seg_a;              // [nblk x 64] their activations (batch 1)
+  int32_t* seg_cold;         // [nblk x 64] ascending cold slots of each block's active CPU neurons
+  uint32_t* cnt;             // [nblk] GPU count | CPU count << 16
+};
+bool fc1_blk_supported(int dt, int64_t d);
+hipError_t launch_fc1_blk(const uint32_t* mask, const SegCtx& sg, int dtw, bool gated, int nblk, hipStream_t s);
+
+// Batch-1 FC2 and final reduction over those segments (see pi_fc2.hip).
+constexpr int kSegChunks = 64;   // id-block chunks of the segment FC2 (nblk <= 64 * kSegChunks)
+struct Fc2SegArgs {
+  const void* W2;
+  const uint16_t* W2s;
+  int dt;
+  int64_t d;
+  int n_g;
+  int nblk;
+  const int32_t* seg_slot;
+  const float* seg_a;
+  const uint32_t* cnt;
+  float* partials;           // [kSegChunks x d]
+};
+struct ReduceListArgs {
+  const float* partials;
+  int64_t d;
+  float* y;
+  const float* y_c;
+  const void* b2;
+  int b2_dt;
+  int nblk;
+  const uint32_t* cnt;
+  const int32_t* seg_slot;
+  const int32_t* seg_cold;
+  int32_t* A_g;
+  int32_t* K;
+  int32_t* A_c;              // NULL = no cold list
+  int32_t* K_c;
+  int n_g;
+  int n_c;
+  int always_c;              // add y_c even with no active cold neuron (no cold side)
+  int chunks;                // set by the launcher
+  int reduce_blocks;         // set by the launcher
+};
+hipError_t launch_fc2_seg(const Fc2SegArgs& a, hipStream_t s);
+hipError_t launch_reduce_lists(const ReduceListArgs& r, hipStream_t s);
 
 // Activation words from stored logits (union over the batch), and the lists from them.
 hipError_t launch_mask(int B, int N, const float* logits, float tau, uint32_t* mask, hipStream_t s);
@@ -92,7 +151,7 @@ struct ReduceArgs {
 };
 
 int fc2_tiles(int dt, int64_t d);
-constexpr int kFc2Chunks = 32;
+int fc2_chunks(int B);           // row chunks of FC2 for batch B (partials: chunks x B x d floats)
 hipError_t launch_fc2(const Fc2Args& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& r, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);

@@ -87,6 +87,17 @@ int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const f
                pi_matrix P1, pi_vector c1, pi_matrix P2, pi_vector c2,
                float* logits, void* ws, size_t ws_bytes);
 
+/* The predictor's output layer alone, with the activation decision:
+ *   logits[b,i] = sum_m P2[i,m] * h[b,m] + c2[i]                i < N
+ *   mask bit i  = (logits[b,i] > tau for some b < B)
+ * h [B x H] fp32 (the hidden layer, e.g. from a previous pi_predict).
+ * logits [B x N] fp32 (may be NULL when B == 1: not stored).  mask
+ * (optional, NULL = not stored): 2*ceil(N/64) uint32 words, bit i%32 of
+ * word i/32; bits of ids >= N are zero.  Uses no workspace.
+ * Errors: as pi_predict. */
+int pi_predict_output(void* stream, int32_t B, int32_t H, int32_t N, const float* h, pi_matrix P2, pi_vector c2,
+                      float tau, float* logits, uint32_t* mask);
+
 /* Activation decision and compaction (step 2).
  * Neuron i is active when logits[b,i] > tau (fp32 compare) for SOME b < B
  * (the union over the batch).

@@ -102,6 +102,31 @@ def test_sparse_ffn_rejects_bad_arguments():
     assert call(wsb=64) == pi.PI_EWORKSPACE
 
 
+def test_predict_output_rejects_bad_arguments():
+    f = pi.pi_predict_output
+    assert status(f, 0, 64, 100, FAKE, mat(), None, 0.0, FAKE, FAKE, 0) == pi.PI_EINVAL
+    assert status(f, 1, 60, 100, FAKE, mat(), None, 0.0, FAKE, FAKE, 0) == pi.PI_EINVAL    # H not a multiple of 8
+    assert status(f, 2, 64, 100, FAKE, mat(), None, 0.0, None, FAKE, 0) == pi.PI_EINVAL    # logits needed for B > 1
+    assert status(f, 1, 64, 100, FAKE, mat(), None, 0.0, None, None, 0) == pi.PI_EINVAL   # nothing to write
+
+
+def test_table_prepare_validates_and_builds_bitmap_and_prefix():
+    import numpy as np
+    N = 200
+    T = np.array([1, 5, 64, 65, 130, 199], np.int32)
+    buf = pi.pi_table_prepare(N, T)
+    W = 2 * ((N + 63) // 64)
+    bits = buf[:W * 4].view(np.uint32)
+    pre = buf[W * 4:].view(np.int32)
+    got = [i for i in range(N) if bits[i // 32] >> (i % 32) & 1]
+    assert got == T.tolist()
+    assert pre.tolist() == [0, 2, 4, 5]          # GPU-resident ids below each 64-id block
+    for bad in ([3, 3], [5, 4], [-1], [200]):
+        with pytest.raises(pi.PiError):
+            pi.pi_table_prepare(N, np.array(bad, np.int32))
+    assert len(pi.pi_table_prepare(N, np.zeros(0, np.int32))) == pi.pi_table_bytes(N)
+
+
 def test_compact_and_merge_reject_bad_arguments():
     assert status(pi.pi_compact, 1, 0, FAKE, 0.0, FAKE, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL
     assert status(pi.pi_compact, 1, 100, FAKE, 0.0, None, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL

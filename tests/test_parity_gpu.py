@@ -93,21 +93,25 @@ def test_empty_list_gives_zero_output(fused):
     assert r["K"] == 0 and r["K_c"] == 0 and r["y_norm"] == 0.0
 
 
-def test_fused_and_separate_paths_give_identical_bits():
+@pytest.mark.parametrize("B", [1, 4])
+def test_fused_and_separate_paths_agree(B):
+    """Same logits bits and lists; outputs agree to the parity tolerance (the FC2 chunking differs)."""
     torch = _dev()
-    for cfg in (SMALL[2], SMALL[6]):
+    for cfg in (SMALL[2], SMALL[6], SMALL[4]):
         spec = synth.layer_spec(cfg, 0)
         dl = ph.DeviceLayer(spec)
         outs = []
         for fused in (False, True):
-            buf = ph.DeviceBuffers(cfg, spec.H, spec.n_g, len(spec.T_c), 1)
-            buf.x.copy_(torch.from_numpy(synth.host_x(cfg.seed, 0, 9, 1, cfg.d)))
-            ph._gpu_stages(dl, buf, 1, 0.0, True, fused)
+            buf = ph.DeviceBuffers(cfg, spec.H, spec.n_g, len(spec.T_c), B)
+            buf.x.copy_(torch.from_numpy(synth.host_x(cfg.seed, 0, 9, B, cfg.d)))
+            ph._gpu_stages(dl, buf, B, 0.0, True, fused)
             torch.cuda.synchronize()
             K = int(buf.K.cpu()[0])
-            outs.append((K, buf.A_g.cpu().numpy()[:K].tobytes(), buf.logits.cpu().numpy().tobytes(),
-                         buf.y.cpu().numpy().tobytes()))
-        assert outs[0] == outs[1], cfg.key
+            Kc = int(buf.K_c.cpu()[0]) if len(spec.T_c) else 0
+            outs.append((K, buf.A_g.cpu().numpy()[:K].tobytes(), Kc, buf.A_c.cpu().numpy()[:Kc].tobytes(),
+                         buf.logits.cpu().numpy().tobytes(), buf.y.cpu().numpy().astype(np.float64)))
+        assert outs[0][:5] == outs[1][:5], cfg.key
+        assert ph.rel_err(outs[1][5], outs[0][5]) <= 1e-5, cfg.key
 
 
 def test_outputs_are_bitwise_repeatable():
@@ -137,3 +141,37 @@ FULL = [("opt-768", 0, 1), ("opt-6.7b", 5, 1), ("llama-13b-gated", 7, 1), ("opt-
 def test_full_size_layer_parity(key, layer, B, fused):
     _dev()
     _run(synth.CONFIGS[key], layer=layer, step=3, B=B, fused=fused)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[1], SMALL[2]], ids=["f16-ragged", "f32", "f16"])
+def test_predict_output_logits_and_mask(cfg, B):
+    """pi_predict_output on a given hidden activation: logits vs the oracle (the
+    output layer alone is the oracle's predictor with an identity first layer)."""
+    import oracle as orc
+    import activation_sparse_amd as pi
+    torch = _dev()
+    spec = synth.layer_spec(cfg, 0)
+    H, N = spec.H, cfg.N
+    dl = ph.DeviceLayer(spec)
+    g = np.random.default_rng(3)
+    h = np.abs(g.standard_normal((B, H))).astype(np.float32)
+    h[:, ::5] = 0.0
+    h_dev = torch.from_numpy(h).cuda()
+    logits = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    mask = torch.empty(2 * ((N + 63) // 64), dtype=torch.int32, device="cuda")
+    pi.pi_predict_output(B, H, N, h_dev, dl.P2, dl.c2, 0.0, logits, mask)
+    torch.cuda.synchronize()
+    P2 = ph.host_mat(cfg.pdtype, cfg.seed, synth.TAG_P2, 0, H, spec.sigmas()[synth.TAG_P2], nrows=N)
+    eye = orc.Mat(np.eye(H, dtype=np.float32), orc.F32, H)
+    ref = orc.predict(h, eye, orc.Vec(None), P2, ph.host_vec(spec.c2, cfg.bdtype))
+    lg = logits.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(lg - ref)) <= ph.LOGIT_ATOL
+    words = mask.cpu().numpy().view(np.uint32)
+    bits = ((words[np.arange(N) // 32] >> (np.arange(N) % 32)) & 1).astype(bool)
+    want = (lg.astype(np.float32) > np.float32(0.0)).any(axis=0)
+    assert np.array_equal(bits, want)        # the kernel's own logits decide its bits
+    tail = ((words[np.arange(N, 32 * len(words)) // 32] >> (np.arange(N, 32 * len(words)) % 32)) & 1)
+    assert not tail.any()
+    near = np.min(np.abs(ref), axis=0) <= ph.BAND
+    assert np.array_equal(bits[~near], (ref > 0).any(axis=0)[~near])
