@@ -38,6 +38,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--cpu-layers", type=int, default=4)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the measurement, run 3 plain device copies of this many MiB (the known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE scaling)")
+    ap.add_argument("--rocprof-summary", metavar="DIR", nargs="+", default=None,
+                    help="summarise the rocprofv3 CSV output under each DIR (kernel trace, counters) and "
+                         "exit; no GPU use")
+    ap.add_argument("--copy-mib", type=int, default=256, help="copy size the counters were taken with")
     return ap.parse_args()
 
 
@@ -139,8 +146,122 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _short_kernel(name):
+    import re
+    m = re.search(r"(k_\w+|__amd_rocclr_\w+)", name)
+    return m.group(1) if m else name[:60]
+
+
+KERNEL_SOURCES = ["activation_sparse_amd/csrc/pi_fast.hip", "activation_sparse_amd/csrc/pi_fc2.hip",
+                  "activation_sparse_amd/csrc/pi_device.h", "activation_sparse_amd/csrc/pi_internal.h"]
+TRAFFIC_PROFILE = "profiles/k_logits_b1.opt-30b.b1.hbm_traffic.txt"
+
+
+def kernel_source_digest():
+    """sha256 over the sources the batch-1 kernels are built from (a counter reading taken on other
+    sources no longer describes the kernel)."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when there is none
+    or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    digest, val = None, None
+    for line in open(path):
+        if line.startswith("kernel sources sha256: "):
+            digest = line.split(": ", 1)[1].strip()
+        if line.startswith(f"traffic {kernel} "):
+            val = float(line.split("total_bytes=")[1].split()[0])
+    return val if (digest == kernel_source_digest() and val is not None) else None
+
+
+def rocprof_summary(roots, copy_mib):
+    """Per-kernel durations from rocprofv3 `--kernel-trace --output-format csv`, and per-dispatch HBM
+    counters from `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs, found anywhere under the given
+    directories.
+
+    Durations: every launch of a kernel, and for k_logits_b1 also the launches that follow another
+    k_logits_b1 (the back-to-back pi_predict_output launches the roofline is timed on).  Counters: KiB
+    per dispatch, averaged per kernel, and scaled by what the same counter reads for the plain copies of
+    copy_mib MiB (the copy dispatches within 1% of the largest reading), whose true traffic is copy_mib
+    MiB read and copy_mib MiB written."""
+    import csv
+    import glob
+    import statistics as st
+    out = []
+    scaled = {}
+    for root in roots:
+        for path in sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)):
+            rows = list(csv.DictReader(open(path)))
+            rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+            per, iso = {}, []
+            prev = None
+            for r in rows:
+                k = _short_kernel(r["Kernel_Name"])
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                per.setdefault(k, []).append(dur)
+                if k == "k_logits_b1" and prev == "k_logits_b1":
+                    iso.append(dur)
+                prev = k
+            tot = sum(sum(v) for v in per.values())
+            out.append(f"kernel trace: {path} ({len(rows)} dispatches)")
+            out.append(f"{'kernel':32s} {'calls':>7s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>8s} {'share':>6s}")
+            for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+                out.append(f"{k:32s} {len(v):7d} {st.mean(v):9.2f} {st.median(v):9.2f} {min(v):8.2f} "
+                           f"{100 * sum(v) / tot:5.1f}%")
+            if iso:
+                out.append(f"{'k_logits_b1 back-to-back':32s} {len(iso):7d} {st.mean(iso):9.2f} "
+                           f"{st.median(iso):9.2f} {min(iso):8.2f}")
+            out.append("")
+        for path in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
+            rows = list(csv.DictReader(open(path)))
+            per = {}
+            for r in rows:
+                k = _short_kernel(r["Kernel_Name"])
+                per.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
+            out.append(f"counters: {path} ({len(rows)} records)")
+            for c in sorted({c for c, _ in per}):
+                scale = None
+                copy = per.get((c, "__amd_rocclr_copyBuffer"))
+                if copy:
+                    big = [v for v in copy if v >= 0.99 * max(copy)]
+                    scale = (copy_mib * 1024.0) / st.mean(big)
+                    out.append(f"{c}: plain copy of {copy_mib} MiB reads {st.mean(big):.1f} KiB per dispatch "
+                               f"({len(big)} dispatches) -> scale {scale:.4f}")
+                for (cc, k), v in sorted(per.items()):
+                    if cc != c or k.startswith("__amd") or not k.startswith("k_"):
+                        continue
+                    line = f"  {k:24s} n={len(v):5d} mean={st.mean(v):11.1f} KiB"
+                    if scale is not None:
+                        b = st.mean(v) * scale * 1024
+                        scaled[(c, k)] = b
+                        line += f"  scaled={b / 1e6:9.3f} MB per dispatch"
+                    out.append(line)
+            out.append("")
+    ks = sorted({k for _, k in scaled})
+    if any(("FETCH_SIZE", k) in scaled and ("WRITE_SIZE", k) in scaled for k in ks):
+        out.append("HBM traffic per dispatch (scaled FETCH_SIZE + WRITE_SIZE):")
+        for k in ks:
+            if ("FETCH_SIZE", k) in scaled and ("WRITE_SIZE", k) in scaled:
+                f_, w_ = scaled[("FETCH_SIZE", k)], scaled[("WRITE_SIZE", k)]
+                out.append(f"traffic {k} fetch_bytes={f_:.0f} write_bytes={w_:.0f} total_bytes={f_ + w_:.0f}")
+        out.append(f"kernel sources sha256: {kernel_source_digest()}")
+    return "\n".join(out)
+
+
 def main():
     args = parse()
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary, args.copy_mib))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
               "(the multi-GPU sharding is a design note only).", file=sys.stderr)
@@ -297,8 +418,10 @@ def main():
     dom = dom + " (isolated)"
     kernel_symbol = {"hidden": "k_hidden_b1", "output+mask": "k_logits_b1", "fc1": "k_fc1_blk",
                      "fc2": "k_fc2_seg", "reduce+merge+lists": "k_reduce_lists"}
+    traffic = committed_traffic("k_logits_b1") if (cfg.key == "opt-30b" and B == 1) else None
     roofline = {"bound": "hbm", "achieved": round(achieved[dom], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved[dom] / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved[dom] / HBM_PEAK_GBS, 4),
+                "traffic": round(traffic) if traffic is not None else None,
                 "kernel": kernel_symbol["output+mask"] + " (predictor output layer, pi_predict_output)",
                 "bytes_per_launch": round(mean_bytes[dom]), "avg_launch_us": round(mean_ms[dom] * 1e3, 2)}
 
@@ -307,6 +430,15 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(cfg, B, args.cpu_seconds, args.cpu_layers)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     out = {
         "metric": "sparse-FFN decode tokens/s at batch 1; achieved HBM GB/s vs peak",
