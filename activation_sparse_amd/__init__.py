@@ -16,14 +16,17 @@ from typing import Optional
 PI_F32, PI_F16, PI_I4G128 = 0, 1, 2
 PI_RELU, PI_GATED_RELU = 0, 1
 PI_OK, PI_EINVAL, PI_EWORKSPACE, PI_EUNSUPPORTED, PI_EHIP = 0, 1, 2, 3, 4
-PI_OP_PREDICT, PI_OP_COMPACT, PI_OP_SPARSE_FFN, PI_OP_MERGE, PI_OP_FFN_LAYER = 0, 1, 2, 3, 4
+PI_OP_PREDICT, PI_OP_COMPACT, PI_OP_SPARSE_FFN, PI_OP_MERGE, PI_OP_FFN_LAYER, PI_OP_PREDICT_OUTPUT = 0, 1, 2, 3, 4, 5
+PI_STAGE_HIDDEN, PI_STAGE_OUTPUT, PI_STAGE_FC1, PI_STAGE_FC2, PI_STAGE_SUM, PI_STAGE_ALL = 1, 2, 4, 8, 16, 31
 PI_MAX_BATCH = 32
+PI_ABI_VERSION = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpi.so")
 
-EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes", "pi_table_prepare",
-           "pi_ffn_layer", "pi_workspace_bytes", "pi_status_string", "pi_last_hip_error", "pi_abi_version")
+EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes",
+           "pi_table_prepare", "pi_ffn_layer", "pi_ffn_layer_stages", "pi_workspace_bytes", "pi_status_string",
+           "pi_last_hip_error", "pi_abi_version")
 
 
 class PiError(RuntimeError):
@@ -56,7 +59,7 @@ def load():
         L = C.CDLL(LIB_PATH)
         P, I = C.c_void_p, C.c_int32
         L.pi_predict.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Vec, P, P, C.c_size_t]
-        L.pi_predict_output.argtypes = [P, I, I, I, P, _Mat, _Vec, C.c_float, P, P]
+        L.pi_predict_output.argtypes = [P, I, I, I, P, _Mat, _Vec, C.c_float, P, P, P, C.c_size_t]
         L.pi_predict_output.restype = C.c_int
         L.pi_compact.argtypes = [P, I, I, P, C.c_float, P, I, P, P, P, I, P, P, P, C.c_size_t]
         L.pi_sparse_ffn.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Mat, P, P, P, P, C.c_size_t]
@@ -67,6 +70,9 @@ def load():
         L.pi_table_prepare.restype = C.c_int
         L.pi_ffn_layer.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P, P, C.c_size_t, P]
         L.pi_ffn_layer.restype = C.c_int
+        L.pi_ffn_layer_stages.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P, P, C.c_size_t, P,
+                                          C.c_uint32, P]
+        L.pi_ffn_layer_stages.restype = C.c_int
         L.pi_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.pi_workspace_bytes.restype = C.c_size_t
         L.pi_status_string.argtypes = [I]
@@ -90,7 +96,8 @@ def _ptr(t) -> Optional[int]:
 @dataclass
 class Matrix:
     """Device weights: float32 / float16 tensor [rows, cols], or uint8 packed
-    int4 [rows, cols/2] with int16 fp16-bit scales [rows, cols/128]."""
+    int4 [rows, cols/2] with int16 fp16-bit scales [rows, cols/128].  The
+    predictor's output layer P2 is stored hidden-major, [H, N]."""
     data: object
     dtype: int
     scales: object = None
@@ -142,9 +149,11 @@ def pi_predict(B, d, H, N, x, P1: Matrix, c1: Vector, P2: Matrix, c2: Vector, lo
                              (c2 or _NO_VEC)._c(), _ptr(logits), _ptr(ws), nbytes), "pi_predict")
 
 
-def pi_predict_output(B, H, N, h, P2: Matrix, c2: Vector, tau, logits, mask=None, stream=None) -> None:
+def pi_predict_output(B, H, N, h, P2: Matrix, c2: Vector, tau, logits, mask=None, ws=None, ws_bytes=None,
+                      stream=None) -> None:
+    nbytes = ws_bytes if ws_bytes is not None else (ws.numel() * ws.element_size() if ws is not None else 0)
     _check(load().pi_predict_output(_stream(stream), B, H, N, _ptr(h), P2._c(), (c2 or _NO_VEC)._c(), float(tau),
-                                    _ptr(logits), _ptr(mask)), "pi_predict_output")
+                                    _ptr(logits), _ptr(mask), _ptr(ws), nbytes), "pi_predict_output")
 
 
 def pi_compact(B, N, logits, tau, T_g, n_g, A_g, K, T_c=None, n_c=0, A_c=None, K_c=None, stream=None) -> None:
@@ -226,3 +235,13 @@ def pi_ffn_layer(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_
     _check(load().pi_ffn_layer(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
                                _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c), _ptr(ws), nbytes, events),
            "pi_ffn_layer")
+
+
+def pi_ffn_layer_stages(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_c, K_c, ws, stages: int,
+                        rows_read=None, ws_bytes=None, events=None, stream=None, _cstruct=None) -> None:
+    """pi_ffn_layer restricted to some stages (PI_STAGE_* bits), with the optional rows-read report."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    cl = _cstruct if _cstruct is not None else layer._c()
+    _check(load().pi_ffn_layer_stages(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
+                                      _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c), _ptr(ws), nbytes,
+                                      events, int(stages), _ptr(rows_read)), "pi_ffn_layer_stages")

@@ -61,41 +61,83 @@ FfnWs ffn_ws_layout(void* ws, int32_t B, int32_t d, int32_t n_g) {
   return w;
 }
 
+// Partial sums of the predictor output layer over its hidden-major rows (the
+// separate kernels: batch > 1, or more hidden units than the batch-1 kernel
+// compacts).
+// (the batch-1 kernel addresses P2 with 32-bit offsets: H * N * 4 bytes bounds any dtype)
+bool out_layer_needs_partials(int32_t B, int32_t H, int32_t N) {
+  return B > 1 || H > pi::kMaxHiddenB1 || (int64_t)H * N * 4 >= ((int64_t)1 << 31);
+}
+size_t out_partials_bytes(int32_t B, int32_t H, int32_t N) {
+  return out_layer_needs_partials(B, H, N) ? (size_t)pi::fc2_chunks(B) * B * (size_t)N * 4 : 0;
+}
+
+size_t table_words(int32_t N) { return 2 * (size_t)((N + 63) / 64); }
+size_t n_groups64(int32_t N) { return (size_t)((N + 63) / 64); }
+
 // Fused layer workspace: h, logits scratch, activation words, the per-64-id
-// block segments of the batch-1 path, a, partials.
+// group segments of the batch-1 path, a, and the partial sums (FC2 chunks,
+// or the output layer's when those are larger).
 struct LayerWs {
   float* h;
   float* logits;
   uint32_t* mask;
   int32_t* seg_slot;
-  float* seg_a;
   int32_t* seg_cold;
+  int32_t* pos_slot;
+  float* pos_a;
   uint32_t* cnt;
   float* a;
   float* partials;
   size_t bytes;
 };
 
-size_t table_words(int32_t N) { return 2 * (size_t)((N + 63) / 64); }
-size_t n_blocks64(int32_t N) { return (size_t)((N + 63) / 64); }
-
 LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g) {
   Carver c{static_cast<char*>(ws)};
   LayerWs w{};
-  const size_t nb = n_blocks64(N);
+  const size_t ng = n_groups64(N);
   w.h = c.take<float>((size_t)B * H * 4);
   w.logits = c.take<float>((size_t)B * N * 4);
   w.mask = c.take<uint32_t>(table_words(N) * 4);
-  w.seg_slot = c.take<int32_t>(nb * 64 * 4);
-  w.seg_a = c.take<float>(nb * 64 * 4);
-  w.seg_cold = c.take<int32_t>(nb * 64 * 4);
-  w.cnt = c.take<uint32_t>(nb * 4);
+  w.seg_slot = c.take<int32_t>(ng * 64 * 4);
+  w.seg_cold = c.take<int32_t>(ng * 64 * 4);
+  w.pos_slot = c.take<int32_t>(ng * 64 * 4);
+  w.pos_a = c.take<float>(ng * 64 * 4);
+  w.cnt = c.take<uint32_t>(ng * 4);
   w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
-  const size_t ch = (size_t)pi::fc2_chunks(B) * B > (size_t)pi::kSegChunks ? (size_t)pi::fc2_chunks(B) * B
-                                                                          : (size_t)pi::kSegChunks;
-  w.partials = c.take<float>(ch * (size_t)d * 4);
+  size_t pb = (size_t)pi::fc2_chunks(B) * B * (size_t)d * 4;
+  const size_t seg = (size_t)pi::kSegChunks * (size_t)d * 4;
+  pb = pb > seg ? pb : seg;
+  const size_t ob = out_partials_bytes(B, H, N);
+  w.partials = c.take<float>(pb > ob ? pb : ob);
   w.bytes = c.off;
   return w;
+}
+
+// The predictor's output layer, logits[b,i] = c2[i] + sum_m h[b,m] P2[m,i] with P2
+// hidden-major, and the activation words when mask != NULL.  Batch 1 (H within
+// the compaction bound): one tile kernel that reads only the rows of positive
+// hidden units.  Otherwise: the neuron-major axpy over every row, the ordered
+// sum with c2, then the words from the stored logits.
+int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const float* h, const pi_matrix& P2,
+                         const pi_vector& c2, float tau, float* logits, uint32_t* mask, float* partials,
+                         int32_t* rows_read = nullptr) {
+  if (!out_layer_needs_partials(B, H, N)) {
+    pi::PredFc1Args a{};
+    a.P2 = P2.data; a.P2s = P2.scales; a.pdt = P2.dtype; a.H = H; a.N = N; a.h = h;
+    a.c2 = c2.data; a.c2_dt = c2.dtype; a.tau = tau; a.logits = logits; a.mask = mask; a.rows_read = rows_read;
+    return hip_status(pi::launch_pred_out_b1(a, s));
+  }
+  pi::Fc2Args f{};
+  f.W2 = P2.data; f.W2s = P2.scales; f.dt = P2.dtype; f.d = N; f.n_g = H; f.list = nullptr; f.K = nullptr;
+  f.a = h; f.a_stride = H; f.a_by_row = 1; f.B = B; f.partials = partials;
+  int st = hip_status(pi::launch_fc2(f, s));
+  if (st != PI_OK) return st;
+  pi::ReduceArgs r{};
+  r.partials = partials; r.chunks = pi::fc2_chunks(B); r.B = B; r.d = N; r.y = logits;
+  r.y_c = nullptr; r.K_c = nullptr; r.b2 = c2.data; r.b2_dt = c2.dtype;
+  if ((st = hip_status(pi::launch_reduce(r, s))) != PI_OK) return st;
+  return mask ? hip_status(pi::launch_mask(B, N, logits, tau, mask, s)) : PI_OK;
 }
 
 }  // namespace
@@ -120,7 +162,8 @@ const char* pi_status_string(int32_t status) {
 size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g) {
   if (B < 1) B = 1;
   switch (op) {
-    case PI_OP_PREDICT: return H > 0 ? align_up((size_t)B * (size_t)H * 4) : 0;
+    case PI_OP_PREDICT: return H > 0 && N > 0 ? align_up((size_t)B * (size_t)H * 4) + out_partials_bytes(B, H, N) : 0;
+    case PI_OP_PREDICT_OUTPUT: return H > 0 && N > 0 ? out_partials_bytes(B, H, N) : 0;
     case PI_OP_SPARSE_FFN:
       return d > 0 ? ffn_ws_layout(nullptr, B, d, n_g).bytes : 0;
     case PI_OP_FFN_LAYER:
@@ -129,7 +172,7 @@ size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N
   }
 }
 
-size_t pi_table_bytes(int32_t N) { return N > 0 ? (table_words(N) + n_blocks64(N)) * 4 : 0; }
+size_t pi_table_bytes(int32_t N) { return N > 0 ? (table_words(N) + n_groups64(N)) * 4 : 0; }
 
 int pi_table_prepare(int32_t N, const int32_t* T_g, int32_t n_g, void* table, size_t table_bytes) {
   if (N <= 0 || n_g < 0 || n_g > N || !table || (n_g > 0 && !T_g)) return PI_EINVAL;
@@ -143,7 +186,7 @@ int pi_table_prepare(int32_t N, const int32_t* T_g, int32_t n_g, void* table, si
   for (int32_t s = 0; s < n_g; ++s) bits[T_g[s] / 32] |= 1u << (T_g[s] % 32);
   int32_t* pre = reinterpret_cast<int32_t*>(bits + W);
   int32_t run = 0;
-  for (size_t b = 0; b < W / 2; ++b) {  // 64-id blocks
+  for (size_t b = 0; b < W / 2; ++b) {  // 64-id groups
     pre[b] = run;
     run += __builtin_popcount(bits[2 * b]) + __builtin_popcount(bits[2 * b + 1]);
   }
@@ -153,55 +196,41 @@ int pi_table_prepare(int32_t N, const int32_t* T_g, int32_t n_g, void* table, si
 int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const float* x, pi_matrix P1,
                pi_vector c1, pi_matrix P2, pi_vector c2, float* logits, void* ws, size_t ws_bytes) {
   if (!valid_batch(B) || d <= 0 || H <= 0 || N <= 0) return PI_EINVAL;
-  if (!x || !aligned16(x) || !logits || !valid_matrix(P1, d) || !valid_matrix(P2, H)) return PI_EINVAL;
+  if (!x || !aligned16(x) || !logits || !valid_matrix(P1, d) || !valid_matrix(P2, N)) return PI_EINVAL;
   if (!valid_vector(c1) || !valid_vector(c2)) return PI_EINVAL;
   if (!ws || !aligned16(ws)) return ws_bytes ? PI_EINVAL : PI_EWORKSPACE;
   if (ws_bytes < pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0)) return PI_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* h = static_cast<float*>(ws);
-  if (B == 1 && pi::b1_supported(P1.dtype, d) && pi::b1_supported(P2.dtype, H)) {
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * (size_t)H * 4));
+  int st;
+  if (B == 1 && pi::b1_supported(P1.dtype, d)) {
     pi::B1Gemv g{};
     g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
     g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
-    int st = hip_status(pi::launch_hidden_b1(g, s));
-    if (st != PI_OK) return st;
-    pi::B1Gemv o{};
-    o.W = P2.data; o.Ws = P2.scales; o.dt = P2.dtype; o.rows = N; o.cols = H; o.x = h;
-    o.bias = c2.data; o.bias_dt = c2.dtype; o.out = logits;
-    return hip_status(pi::launch_logits_b1(o, 0.f, nullptr, s));
+    st = hip_status(pi::launch_hidden_b1(g, s));
+  } else {
+    pi::RowdotArgs a{};
+    a.W = P1.data; a.Ws = P1.scales; a.dt = P1.dtype; a.cols = d;
+    a.count_max = H; a.x = x; a.B = B; a.bias = c1.data; a.bias_dt = c1.dtype;
+    a.relu = 1; a.out = h; a.out_stride = H;
+    st = hip_status(pi::launch_rowdot(a, s));
   }
-  pi::RowdotArgs a{};
-  a.W = P1.data; a.Ws = P1.scales; a.dt = P1.dtype; a.cols = d;
-  a.count_max = H; a.x = x; a.B = B; a.bias = c1.data; a.bias_dt = c1.dtype;
-  a.relu = 1; a.out = h; a.out_stride = H;
-  int st = hip_status(pi::launch_rowdot(a, s));
   if (st != PI_OK) return st;
-  pi::RowdotArgs b{};
-  b.W = P2.data; b.Ws = P2.scales; b.dt = P2.dtype; b.cols = H;
-  b.count_max = N; b.x = h; b.B = B; b.bias = c2.data; b.bias_dt = c2.dtype;
-  b.relu = 0; b.out = logits; b.out_stride = N;
-  return hip_status(pi::launch_rowdot(b, s));
+  return enqueue_output_layer(s, B, H, N, h, P2, c2, 0.f, logits, nullptr, partials);
 }
 
 int pi_predict_output(void* stream, int32_t B, int32_t H, int32_t N, const float* h, pi_matrix P2, pi_vector c2,
-                      float tau, float* logits, uint32_t* mask) {
-  if (!valid_batch(B) || H <= 0 || N <= 0 || !h || !aligned16(h) || !valid_matrix(P2, H) || !valid_vector(c2))
+                      float tau, float* logits, uint32_t* mask, void* ws, size_t ws_bytes) {
+  if (!valid_batch(B) || H <= 0 || N <= 0 || !h || !aligned16(h) || !valid_matrix(P2, N) || !valid_vector(c2))
     return PI_EINVAL;
   if (!logits && (B != 1 || !mask)) return PI_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (B == 1 && pi::b1_supported(P2.dtype, H)) {
-    pi::B1Gemv o{};
-    o.W = P2.data; o.Ws = P2.scales; o.dt = P2.dtype; o.rows = N; o.cols = H; o.x = h;
-    o.bias = c2.data; o.bias_dt = c2.dtype; o.out = logits;
-    return hip_status(pi::launch_logits_b1(o, tau, reinterpret_cast<uint8_t*>(mask), s));
-  }
-  pi::RowdotArgs b{};
-  b.W = P2.data; b.Ws = P2.scales; b.dt = P2.dtype; b.cols = H;
-  b.count_max = N; b.x = h; b.B = B; b.bias = c2.data; b.bias_dt = c2.dtype;
-  b.relu = 0; b.out = logits; b.out_stride = N;
-  int st = hip_status(pi::launch_rowdot(b, s));
-  if (st != PI_OK || !mask) return st;
-  return hip_status(pi::launch_mask(B, N, logits, tau, mask, s));
+  const size_t need = pi_workspace_bytes(PI_OP_PREDICT_OUTPUT, B, 0, H, N, 0);
+  if (need && (!ws || !aligned16(ws))) return PI_EWORKSPACE;
+  if (ws_bytes < need) return PI_EWORKSPACE;
+  if (!logits && out_layer_needs_partials(B, H, N)) return PI_EINVAL;
+  return enqueue_output_layer(static_cast<hipStream_t>(stream), B, H, N, h, P2, c2, tau, logits, mask,
+                              static_cast<float*>(ws));
 }
 
 int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float tau, const int32_t* T_g,
@@ -237,35 +266,42 @@ int validate_ffn(int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x
 int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, const float* x, const pi_matrix& W1,
                 const pi_vector& b1, const pi_matrix& Wup, const pi_matrix& W2, const int32_t* A_g, const int32_t* K,
                 float* a, float* partials, float* y, const float* y_c, const int32_t* K_c, const pi_vector& b2,
-                const hipEvent_t* ev) {
+                const hipEvent_t* ev, uint32_t stages) {
   const bool gated = kind == PI_GATED_RELU;
-  int st;
-  if (B == 1 && pi::b1_supported(W1.dtype, d)) {
-    pi::B1Gemv g{};
-    g.W = W1.data; g.Ws = W1.scales; g.dt = W1.dtype; g.rows = n_g; g.cols = d; g.x = x;
-    if (gated) { g.Wu = Wup.data; g.Wus = Wup.scales; }
-    g.bias = b1.data; g.bias_dt = b1.dtype; g.out = a; g.list = A_g; g.Kp = K;
-    st = n_g > 0 ? hip_status(pi::launch_fc1_b1(g, gated, s)) : PI_OK;
-  } else {
-    pi::RowdotArgs r{};
-    r.W = W1.data; r.Ws = W1.scales; r.dt = W1.dtype; r.cols = d; r.gated = gated;
-    if (gated) { r.Wup = Wup.data; r.Wups = Wup.scales; }
-    r.list = A_g; r.count_dev = K; r.count_max = n_g;
-    r.x = x; r.B = B; r.bias = b1.data; r.bias_dt = b1.dtype; r.relu = 1;
-    r.out = a; r.out_stride = n_g > 0 ? n_g : 1;
-    st = hip_status(pi::launch_rowdot_ex(r, n_g, nullptr, 0, s));
+  int st = PI_OK;
+  if (stages & PI_STAGE_FC1) {
+    if (B == 1 && pi::b1_supported(W1.dtype, d)) {
+      pi::B1Gemv g{};
+      g.W = W1.data; g.Ws = W1.scales; g.dt = W1.dtype; g.rows = n_g; g.cols = d; g.x = x;
+      if (gated) { g.Wu = Wup.data; g.Wus = Wup.scales; }
+      g.bias = b1.data; g.bias_dt = b1.dtype; g.out = a; g.list = A_g; g.Kp = K;
+      st = n_g > 0 ? hip_status(pi::launch_fc1_b1(g, gated, s)) : PI_OK;
+    } else {
+      pi::RowdotArgs r{};
+      r.W = W1.data; r.Ws = W1.scales; r.dt = W1.dtype; r.cols = d; r.gated = gated;
+      if (gated) { r.Wup = Wup.data; r.Wups = Wup.scales; }
+      r.list = A_g; r.count_dev = K; r.count_max = n_g;
+      r.x = x; r.B = B; r.bias = b1.data; r.bias_dt = b1.dtype; r.relu = 1;
+      r.out = a; r.out_stride = n_g > 0 ? n_g : 1;
+      st = hip_status(pi::launch_rowdot_ex(r, n_g, nullptr, 0, s));
+    }
+    if (st != PI_OK) return st;
   }
-  if (st != PI_OK) return st;
   if (ev && ev[0] && (st = hip_status(hipEventRecord(ev[0], s))) != PI_OK) return st;
-  pi::Fc2Args f{};
-  f.W2 = W2.data; f.W2s = W2.scales; f.dt = W2.dtype; f.d = d; f.n_g = n_g;
-  f.list = A_g; f.K = K; f.a = a; f.B = B; f.partials = partials;
-  if ((st = hip_status(pi::launch_fc2(f, s))) != PI_OK) return st;
+  if (stages & PI_STAGE_FC2) {
+    pi::Fc2Args f{};
+    f.W2 = W2.data; f.W2s = W2.scales; f.dt = W2.dtype; f.d = d; f.n_g = n_g;
+    f.list = A_g; f.K = K; f.a = a; f.a_stride = n_g; f.a_by_row = 0; f.B = B; f.partials = partials;
+    if ((st = hip_status(pi::launch_fc2(f, s))) != PI_OK) return st;
+  }
   if (ev && ev[1] && (st = hip_status(hipEventRecord(ev[1], s))) != PI_OK) return st;
-  pi::ReduceArgs r{};
-  r.partials = partials; r.chunks = pi::fc2_chunks(B); r.B = B; r.d = d; r.y = y;
-  r.y_c = y_c; r.K_c = K_c; r.b2 = b2.data; r.b2_dt = b2.dtype;
-  return hip_status(pi::launch_reduce(r, s));
+  if (stages & PI_STAGE_SUM) {
+    pi::ReduceArgs r{};
+    r.partials = partials; r.chunks = pi::fc2_chunks(B); r.B = B; r.d = d; r.y = y;
+    r.y_c = y_c; r.K_c = K_c; r.b2 = b2.data; r.b2_dt = b2.dtype;
+    st = hip_status(pi::launch_reduce(r, s));
+  }
+  return st;
 }
 
 }  // namespace
@@ -280,7 +316,7 @@ int pi_sparse_ffn(void* stream, int32_t B, int32_t d, int32_t n_g, int32_t kind,
   const FfnWs w = ffn_ws_layout(ws, B, d, n_g);
   if (ws_bytes < w.bytes) return PI_EWORKSPACE;
   return enqueue_ffn(static_cast<hipStream_t>(stream), B, d, n_g, kind, x, W1, b1, Wup, W2, A_g, K, w.a, w.partials,
-                     y_g, nullptr, nullptr, pi_vector{nullptr, PI_F32}, nullptr);
+                     y_g, nullptr, nullptr, pi_vector{nullptr, PI_F32}, nullptr, PI_STAGE_ALL);
 }
 
 int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, const int32_t* K_c, pi_vector b2) {
@@ -289,15 +325,16 @@ int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, con
   return hip_status(pi::launch_merge(B, d, y, y_c, K_c, b2.data, b2.dtype, static_cast<hipStream_t>(stream)));
 }
 
-int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c, float* y,
-                 float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes,
-                 void* const* events) {
+int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c,
+                        float* y, float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws,
+                        size_t ws_bytes, void* const* events, uint32_t stages, int32_t* rows_read) {
   if (!L) return PI_EINVAL;
   const int32_t d = L->d, N = L->N, H = L->H, n_g = L->n_g;
   if (N <= 0 || H <= 0 || n_g > N) return PI_EINVAL;
+  if (stages == 0 || (stages & ~(uint32_t)PI_STAGE_ALL)) return PI_EINVAL;
   int st = validate_ffn(B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2);
   if (st != PI_OK) return st;
-  if (!valid_matrix(L->P1, d) || !valid_matrix(L->P2, H) || !valid_vector(L->c1) || !valid_vector(L->c2) ||
+  if (!valid_matrix(L->P1, d) || !valid_matrix(L->P2, N) || !valid_vector(L->c1) || !valid_vector(L->c2) ||
       !valid_vector(L->b2))
     return PI_EINVAL;
   if (!L->table || !y || !aligned16(y) || !K || (n_g > 0 && !A_g)) return PI_EINVAL;
@@ -310,74 +347,93 @@ int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, flo
   if (events)
     for (int i = 0; i < 6; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
   auto record = [&](int i) { return ev[i] ? hip_status(hipEventRecord(ev[i], s)) : PI_OK; };
+  auto want = [&](uint32_t bit) { return (stages & bit) != 0; };
 
-  pi::ListCtx lc{};
-  lc.mask = w.mask; lc.gbits = static_cast<const uint32_t*>(L->table); lc.W = (int)table_words(N);
-  lc.A_g = A_g; lc.K = K; lc.A_c = L->cold ? A_c : nullptr; lc.K_c = L->cold ? K_c : nullptr;
-  float* lg = logits ? logits : w.logits;
   const bool gated = L->kind == PI_GATED_RELU;
-  const bool b1_pred = B == 1 && pi::b1_supported(L->P1.dtype, d) && pi::b1_supported(L->P2.dtype, H);
-  const bool b1_ffn = B == 1 && pi::b1_supported(L->W1.dtype, d);
-  (void)b1_ffn;
+  const int32_t ngroups = (int32_t)n_groups64(N);
+  const int bdt = L->b1.data ? L->b1.dtype : (L->c2.data ? L->c2.dtype : PI_F16);
+  const int c2dt = L->c2.data ? L->c2.dtype : bdt;
+  const bool fused = B == 1 && pi::b1_supported(L->W1.dtype, d) && ngroups <= 64 * pi::kSegChunks &&
+                     pi::pred_fc1_supported(L->P2.dtype, L->W1.dtype, bdt, c2dt, gated, H, N, d);
+  float* lg = logits ? logits : w.logits;
 
   if ((st = record(0)) != PI_OK) return st;
-  // predictor: hidden layer, then output layer with the activation decision
-  if (b1_pred) {
-    pi::B1Gemv g{};
-    g.W = L->P1.data; g.Ws = L->P1.scales; g.dt = L->P1.dtype; g.rows = H; g.cols = d; g.x = x;
-    g.bias = L->c1.data; g.bias_dt = L->c1.dtype; g.out = w.h;
-    if ((st = hip_status(pi::launch_hidden_b1(g, s))) != PI_OK) return st;
-    if ((st = record(1)) != PI_OK) return st;
-    pi::B1Gemv o{};
-    o.W = L->P2.data; o.Ws = L->P2.scales; o.dt = L->P2.dtype; o.rows = N; o.cols = H; o.x = w.h;
-    o.bias = L->c2.data; o.bias_dt = L->c2.dtype; o.out = logits;
-    if ((st = hip_status(pi::launch_logits_b1(o, tau, reinterpret_cast<uint8_t*>(w.mask), s))) != PI_OK) return st;
-  } else {
-    pi::RowdotArgs a{};
-    a.W = L->P1.data; a.Ws = L->P1.scales; a.dt = L->P1.dtype; a.cols = d;
-    a.count_max = H; a.x = x; a.B = B; a.bias = L->c1.data; a.bias_dt = L->c1.dtype;
-    a.relu = 1; a.out = w.h; a.out_stride = H;
-    if ((st = hip_status(pi::launch_rowdot(a, s))) != PI_OK) return st;
-    if ((st = record(1)) != PI_OK) return st;
-    pi::RowdotArgs b{};
-    b.W = L->P2.data; b.Ws = L->P2.scales; b.dt = L->P2.dtype; b.cols = H;
-    b.count_max = N; b.x = w.h; b.B = B; b.bias = L->c2.data; b.bias_dt = L->c2.dtype;
-    b.relu = 0; b.out = lg; b.out_stride = N;
-    if ((st = hip_status(pi::launch_rowdot(b, s))) != PI_OK) return st;
-    if ((st = hip_status(pi::launch_mask(B, N, lg, tau, w.mask, s))) != PI_OK) return st;
+  // predictor hidden layer
+  if (want(PI_STAGE_HIDDEN)) {
+    if (B == 1 && pi::b1_supported(L->P1.dtype, d)) {
+      pi::B1Gemv g{};
+      g.W = L->P1.data; g.Ws = L->P1.scales; g.dt = L->P1.dtype; g.rows = H; g.cols = d; g.x = x;
+      g.bias = L->c1.data; g.bias_dt = L->c1.dtype; g.out = w.h;
+      st = hip_status(pi::launch_hidden_b1(g, s));
+    } else {
+      pi::RowdotArgs a{};
+      a.W = L->P1.data; a.Ws = L->P1.scales; a.dt = L->P1.dtype; a.cols = d;
+      a.count_max = H; a.x = x; a.B = B; a.bias = L->c1.data; a.bias_dt = L->c1.dtype;
+      a.relu = 1; a.out = w.h; a.out_stride = H;
+      st = hip_status(pi::launch_rowdot(a, s));
+    }
+    if (st != PI_OK) return st;
   }
-  if ((st = record(2)) != PI_OK) return st;
+  if ((st = record(1)) != PI_OK) return st;
 
-  const int nblk = (int)n_blocks64(N);
-  if (b1_pred && b1_ffn && pi::fc1_blk_supported(L->W1.dtype, d) && nblk <= 64 * pi::kSegChunks) {
-    // FC1 per 64-id block -> FC2 over the block segments -> ordered sum + merge + lists
-    pi::SegCtx sg{};
-    sg.gbits = lc.gbits; sg.gpre = reinterpret_cast<const int32_t*>(lc.gbits + table_words(N));
-    sg.W1 = L->W1.data; sg.W1s = L->W1.scales; sg.Wu = L->Wup.data; sg.Wus = L->Wup.scales; sg.d = d; sg.n_g = n_g;
-    sg.x = x; sg.b1 = L->b1.data; sg.b1_dt = L->b1.dtype;
-    sg.seg_slot = w.seg_slot; sg.seg_a = w.seg_a; sg.seg_cold = w.seg_cold; sg.cnt = w.cnt;
-    if ((st = hip_status(pi::launch_fc1_blk(w.mask, sg, L->W1.dtype, gated, nblk, s))) != PI_OK) return st;
-    if ((st = record(3)) != PI_OK) return st;
-    pi::Fc2SegArgs f{};
-    f.W2 = L->W2.data; f.W2s = L->W2.scales; f.dt = L->W2.dtype; f.d = d; f.n_g = n_g; f.nblk = nblk;
-    f.seg_slot = w.seg_slot; f.seg_a = w.seg_a; f.cnt = w.cnt; f.partials = w.partials;
-    if ((st = hip_status(pi::launch_fc2_seg(f, s))) != PI_OK) return st;
+  if (fused) {
+    // output layer + activation decision + FC1 per tile -> FC2 over the non-zero
+    // rows + lists -> ordered sum + merge
+    if (want(PI_STAGE_OUTPUT) || want(PI_STAGE_FC1)) {
+      pi::PredFc1Args a{};
+      a.P2 = L->P2.data; a.P2s = L->P2.scales; a.pdt = L->P2.dtype; a.H = H; a.N = N; a.h = w.h;
+      a.c2 = L->c2.data; a.c2_dt = L->c2.dtype; a.tau = tau; a.logits = logits; a.mask = nullptr;
+      a.gbits = static_cast<const uint32_t*>(L->table);
+      a.gpre = reinterpret_cast<const int32_t*>(a.gbits + table_words(N));
+      a.W1 = L->W1.data; a.W1s = L->W1.scales; a.Wu = L->Wup.data; a.Wus = L->Wup.scales; a.dt = L->W1.dtype;
+      a.d = d; a.n_g = n_g; a.x = x; a.b1 = L->b1.data; a.b1_dt = L->b1.dtype;
+      a.seg_slot = w.seg_slot; a.seg_cold = w.seg_cold; a.pos_slot = w.pos_slot; a.pos_a = w.pos_a; a.cnt = w.cnt;
+      a.rows_read = rows_read;
+      if ((st = hip_status(pi::launch_pred_fc1(a, gated, s))) != PI_OK) return st;
+    }
+    if ((st = record(2)) != PI_OK || (st = record(3)) != PI_OK) return st;
+    if (want(PI_STAGE_FC2)) {
+      pi::Fc2SegArgs f{};
+      f.W2 = L->W2.data; f.W2s = L->W2.scales; f.dt = L->W2.dtype; f.d = d; f.n_g = n_g; f.ngroups = ngroups;
+      f.pos_slot = w.pos_slot; f.pos_a = w.pos_a; f.seg_slot = w.seg_slot; f.seg_cold = w.seg_cold; f.cnt = w.cnt;
+      f.partials = w.partials; f.A_g = A_g; f.K = K; f.A_c = L->cold ? A_c : nullptr;
+      f.K_c = L->cold ? K_c : nullptr; f.n_c = N - n_g; f.rows_read = rows_read ? rows_read + 1 : nullptr;
+      if ((st = hip_status(pi::launch_fc2_seg(f, s))) != PI_OK) return st;
+    }
     if ((st = record(4)) != PI_OK) return st;
-    pi::ReduceListArgs r{};
-    r.partials = w.partials; r.d = d; r.y = y; r.y_c = y_c; r.b2 = L->b2.data; r.b2_dt = L->b2.dtype;
-    r.nblk = nblk; r.cnt = w.cnt; r.seg_slot = w.seg_slot; r.seg_cold = w.seg_cold;
-    r.A_g = A_g; r.K = K; r.A_c = L->cold ? A_c : nullptr; r.K_c = L->cold ? K_c : nullptr;
-    r.n_g = n_g; r.n_c = N - n_g;
-    r.always_c = !L->cold;  // no cold side: y_c (if any) is always added
-    if ((st = hip_status(pi::launch_reduce_lists(r, s))) != PI_OK) return st;
+    if (want(PI_STAGE_SUM)) {
+      pi::ReduceYArgs r{};
+      r.partials = w.partials; r.d = d; r.y = y; r.y_c = y_c; r.K_c = L->cold ? K_c : nullptr;
+      r.b2 = L->b2.data; r.b2_dt = L->b2.dtype;
+      if ((st = hip_status(pi::launch_reduce_y(r, s))) != PI_OK) return st;
+    }
     return record(5);
   }
-  // any batch: lists from the activation words, then FC1 / FC2 / reduction over the list
-  if ((st = hip_status(pi::launch_list(lc, n_g, s))) != PI_OK) return st;
+  // any batch: output layer + activation words, the lists, then FC1 / FC2 / ordered sum over the list
+  if (want(PI_STAGE_OUTPUT)) {
+    if ((st = enqueue_output_layer(s, B, H, N, w.h, L->P2, L->c2, tau, lg, w.mask, w.partials, rows_read)) != PI_OK)
+      return st;
+    pi::ListCtx lc{};
+    lc.mask = w.mask; lc.gbits = static_cast<const uint32_t*>(L->table); lc.W = (int)table_words(N);
+    lc.A_g = A_g; lc.K = K; lc.A_c = L->cold ? A_c : nullptr; lc.K_c = L->cold ? K_c : nullptr;
+    if ((st = hip_status(pi::launch_list(lc, n_g, s))) != PI_OK) return st;
+  }
+  if ((st = record(2)) != PI_OK) return st;
   st = enqueue_ffn(s, B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2, A_g, K, w.a, w.partials, y, y_c,
-                   L->cold ? K_c : nullptr, L->b2, ev + 3);
+                   L->cold ? K_c : nullptr, L->b2, ev + 3, stages);
   if (st != PI_OK) return st;
+  // these kernels read every hidden-major P2 row and every listed W2 row
+  if (rows_read &&
+      (st = hip_status(pi::launch_rows_read(rows_read, out_layer_needs_partials(B, H, N) ? H : -1, K, s))) != PI_OK)
+    return st;
   return record(5);
+}
+
+int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c, float* y,
+                 float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes,
+                 void* const* events) {
+  return pi_ffn_layer_stages(stream, L, B, x, tau, y_c, y, logits, A_g, K, A_c, K_c, ws, ws_bytes, events,
+                             PI_STAGE_ALL, nullptr);
 }
 
 }  // extern "C"

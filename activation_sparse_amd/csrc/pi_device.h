@@ -23,6 +23,29 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Buffer resources: a wave-uniform base, a byte range, and loads at 32-bit
+// offsets from it.  A load whose 16 (or 2) bytes lie past the range returns
+// zeros and issues no memory request, so lanes past a row's end need neither
+// a clamped address nor a branch.  Word 3 is the gfx9-family default
+// (untyped, no swizzle).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint16_t bload2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+// A pointer every lane of the wave holds, moved to scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float h2f(uint16_t bits) {
   _Float16 h = __builtin_bit_cast(_Float16, bits);
   return (float)h;
@@ -90,21 +113,18 @@ __device__ __forceinline__ float load_bias(const void* p, int dt, int64_t i) {
   return dt == 0 ? reinterpret_cast<const float*>(p)[i] : h2f(reinterpret_cast<const uint16_t*>(p)[i]);
 }
 
-// Zero read through by bias loads when a bias is absent (stride 0), so that the
-// loads stay branch-free.
-__device__ const uint32_t kZeroWord[4] = {0u, 0u, 0u, 0u};
-
-// Branch-free bias access for a bias dtype fixed at compile time (BDT: 0 fp32,
-// 1 fp16).  Issue it before the weight loads of the same row: the in-order
-// vmcnt then lets its value be used without waiting for the weights.
+// Bias access for a bias dtype fixed at compile time (BDT: 0 fp32, 1 fp16)
+// through a buffer resource over its n entries: an absent bias (NULL) is an
+// empty range, which reads zeros.  Buffer loads keep the vmcnt order exact, so
+// a bias issued before a row's weights is usable without waiting for them.
 template <int BDT>
 struct Bias {
-  const void* p;
-  int stride;
-  __device__ __forceinline__ Bias(const void* q) : p(q ? q : (const void*)kZeroWord), stride(q ? 1 : 0) {}
+  rsrc_t r;
+  __device__ __forceinline__ Bias(const void* q, uint32_t n)
+      : r(make_rsrc(uniform_ptr(q), q ? n * (BDT == 0 ? 4u : 2u) : 0u)) {}
   __device__ __forceinline__ float operator()(int64_t i) const {
-    if constexpr (BDT == 0) return reinterpret_cast<const float*>(p)[i * stride];
-    else return h2f(reinterpret_cast<const uint16_t*>(p)[i * stride]);
+    if constexpr (BDT == 0) return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)(i * 4), 0, 0));
+    else return h2f(bload2(r, (uint32_t)i * 2u));
   }
 };
 

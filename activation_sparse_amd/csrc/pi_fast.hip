@@ -1,41 +1,43 @@
-// pi_fast.hip - batch-1 kernels with the input held in registers, and the
-// mask + compaction epilogue shared by the fused and the batched paths.
+// pi_fast.hip - batch-1 kernels.
 //
-// Batch-1 row dots: every lane owns the same column slice of every row
-// (vectors v = u*64 + lane), so its slice of x is loaded once into VGPRs and
-// reused for all the rows the wave visits.  All 16-byte loads of a row (or of
-// RW rows) are issued before the first FMA.
+// Row dots with the input held in registers (the predictor's hidden layer and
+// the list-driven FC1 of pi_sparse_ffn): every lane owns the same column
+// slice of every row (vectors v = u*64 + lane), so its slice of x is loaded
+// once and reused; all 16-byte loads of a row are issued before the first FMA.
 //
-// In the fused layer the output-layer kernel also emits the activation bits;
-// the FC1 kernel works one 64-id block at a time from those bits and the
-// prepared table, so no kernel waits on another block.
+// The predictor's output layer with its weights stored hidden-major (row m =
+// hidden unit m's weights to the N outputs): only the rows of hidden units
+// whose ReLU output is positive are read, since a zero hidden unit adds
+// nothing to any logit.  One block owns a tile of 64 or 128 neuron ids: it
+// compacts the active hidden units in LDS, streams their row slices, and
+// decides the tile's activations.  In the fused layer the same block then
+// runs FC1 for the tile's active GPU-resident neurons (x staged in LDS) and
+// writes the tile's list segments, so no block waits for another.
 #include "pi_device.h"
 #include "pi_internal.h"
-#include "pi_list.h"
 
 namespace pi {
 namespace {
 
 constexpr int kT = 256;
 constexpr int kWpb = kT / kWave;
-constexpr int kFc1MaxBlocks = 1024;
-constexpr int kFc1T = 256;            // threads of the per-block FC1 kernel
 
+// The lane's slice of x (x[E*v .. E*v + E-1] for v = u*64 + lane) into
+// registers, through a buffer over x's nvec*E floats: slices past the end
+// read zeros, so no select waits on a load.
 template <int DT, int NV>
 __device__ __forceinline__ void load_xreg(const float* __restrict__ x, int nvec, int lane,
                                           float (&xr)[NV][Fmt<DT>::E]) {
   constexpr int E = Fmt<DT>::E;
+  const rsrc_t r = make_rsrc(uniform_ptr(x), (uint32_t)nvec * E * 4u);
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
-    const int v = u * kWave + lane;
-    const bool ok = v < nvec;
-    const int vc = ok ? v : nvec - 1;
-    const float4v* p = reinterpret_cast<const float4v*>(x + (int64_t)vc * E);
+    const uint32_t off = (uint32_t)(u * kWave + lane) * (E * 4u);
 #pragma unroll
     for (int q = 0; q < E / 4; ++q) {
-      const float4v t = p[q];
-      xr[u][4 * q + 0] = ok ? t.x : 0.f; xr[u][4 * q + 1] = ok ? t.y : 0.f;
-      xr[u][4 * q + 2] = ok ? t.z : 0.f; xr[u][4 * q + 3] = ok ? t.w : 0.f;
+      const uint4 t = bload16(r, off + 16u * q);
+      xr[u][4 * q + 0] = __uint_as_float(t.x); xr[u][4 * q + 1] = __uint_as_float(t.y);
+      xr[u][4 * q + 2] = __uint_as_float(t.z); xr[u][4 * q + 3] = __uint_as_float(t.w);
     }
   }
 }
@@ -46,22 +48,21 @@ template <int DT, int NV>
 struct LaneRow {
   uint4 w[NV];
   float sc[NV];
-  // Branch-free and select-free: lanes past the row end read the row's last vector
-  // and absent rows (rp == nullptr) read `fallback`; the caller zeroes those
-  // contributions (x is zero on lanes past the row end, and an absent row's
-  // result is discarded), so nothing waits on these loads before the dot product.
-  __device__ __forceinline__ void issue(const char* rp, const uint16_t* sp, int nvec, int lane,
-                                        const char* fallback, const uint16_t* sfallback) {
-    const bool row_ok = rp != nullptr;
-    const char* base = row_ok ? rp : fallback;
-    const uint16_t* sbase = row_ok ? sp : sfallback;
+  // rp: the row (wave-uniform; NULL = an absent row, which reads zeros), nvec
+  // 16-byte vectors long; sp: its int4 scales.  Lane vectors past the row end
+  // read zeros from the buffer range check: no clamped addresses, no branches,
+  // and nothing waits on these loads before the dot product.
+  __device__ __forceinline__ void issue(const char* rp, const uint16_t* sp, int nvec, int lane) {
+    const rsrc_t r = make_rsrc(uniform_ptr(rp), rp ? (uint32_t)nvec * 16u : 0u);
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int v = u * kWave + lane;
-      const int vc = v < nvec ? v : nvec - 1;
-      w[u] = ld16(base + (int64_t)vc * 16);
-      if constexpr (DT == 2) sc[u] = h2f(sbase[vc / 4]);
+    for (int u = 0; u < NV; ++u) w[u] = bload16(r, (uint32_t)(u * kWave + lane) * 16u);
+    if constexpr (DT == 2) {
+      const rsrc_t rs = make_rsrc(uniform_ptr(sp), sp ? (uint32_t)(nvec / 4) * 2u : 0u);
+#pragma unroll
+      for (int u = 0; u < NV; ++u) sc[u] = h2f(bload2(rs, (uint32_t)((u * kWave + lane) / 4) * 2u));
     }
+    // keep every load of the row ahead of the code that consumes them
+    __builtin_amdgcn_sched_barrier(0);
   }
   __device__ __forceinline__ float dot(const float (&xr)[NV][Fmt<DT>::E]) const {
     constexpr int E = Fmt<DT>::E;
@@ -85,20 +86,20 @@ __global__ __launch_bounds__(kT) void k_hidden_b1(const void* __restrict__ W, co
                                                    int rows, int cols, const float* __restrict__ x,
                                                    const void* __restrict__ bias, float* __restrict__ out) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  const int gw = blockIdx.x * kWpb + wave, nw = gridDim.x * kWpb;
+  const int gw = blockIdx.x * kWpb + wave;
   if (gw >= rows) return;
   const int64_t rb = row_bytes(DT, cols);
   const int nvec = (int)(rb / 16);
   const int groups = cols / 128;
-  (void)nw;
-  const Bias<BDT> bias_at(bias);
+  const Bias<BDT> bias_at(bias, (uint32_t)rows);
   const int j = gw;                 // the grid has one wave per row
   const float bj = bias_at(j);
   LaneRow<DT, NV> r;
   r.issue(reinterpret_cast<const char*>(W) + (int64_t)j * rb, DT == 2 ? Ws + (int64_t)j * groups : nullptr, nvec,
-          lane, reinterpret_cast<const char*>(W), Ws);
+          lane);
   float xr[NV][Fmt<DT>::E];
   load_xreg<DT, NV>(x, nvec, lane, xr);
+  __builtin_amdgcn_sched_barrier(0);   // all of x in flight before the first FMA
   float z = wave_sum(r.dot(xr)) + bj;
   z = z > 0.f ? z : 0.f;
   if (lane == 0) out[j] = z;
@@ -112,15 +113,14 @@ __global__ __launch_bounds__(kT) void k_fc1_b1(const void* __restrict__ W, const
                                                 const int32_t* __restrict__ Kp, int n_g, const float* __restrict__ x,
                                                 const void* __restrict__ bias, float* __restrict__ out) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  const int gw = blockIdx.x * kWpb + wave, nw = gridDim.x * kWpb;
+  const int gw = blockIdx.x * kWpb + wave;
   if (gw >= n_g) return;
   const int64_t rb = row_bytes(DT, cols);
   const int nvec = (int)(rb / 16);
   const int groups = cols / 128;
-  (void)nw;
-  const Bias<BDT> bias_at(bias);
+  const Bias<BDT> bias_at(bias, (uint32_t)n_g);
   int K = *Kp;                       // issued with the list entry (no dependency between them)
-  int s = list[gw];
+  int s = __builtin_amdgcn_readfirstlane(list[gw]);
   K = K < 0 ? 0 : (K > n_g ? n_g : K);
   if (gw >= K) return;
   {
@@ -129,12 +129,13 @@ __global__ __launch_bounds__(kT) void k_fc1_b1(const void* __restrict__ W, const
     const float bs = bias_at(ok ? s : 0);
     LaneRow<DT, NV> r, u;
     r.issue(ok ? reinterpret_cast<const char*>(W) + (int64_t)s * rb : nullptr,
-            DT == 2 && ok ? Ws + (int64_t)s * groups : nullptr, nvec, lane, reinterpret_cast<const char*>(W), Ws);
+            DT == 2 && ok ? Ws + (int64_t)s * groups : nullptr, nvec, lane);
     if constexpr (GATED)
       u.issue(ok ? reinterpret_cast<const char*>(Wu) + (int64_t)s * rb : nullptr,
-              DT == 2 && ok ? Wus + (int64_t)s * groups : nullptr, nvec, lane, reinterpret_cast<const char*>(Wu), Wus);
+              DT == 2 && ok ? Wus + (int64_t)s * groups : nullptr, nvec, lane);
     float xr[NV][Fmt<DT>::E];
     load_xreg<DT, NV>(x, nvec, lane, xr);
+    __builtin_amdgcn_sched_barrier(0);   // all of x in flight before the first FMA
     float z = wave_sum(r.dot(xr)) + bs;
     z = z > 0.f ? z : 0.f;
     if constexpr (GATED) z *= wave_sum(u.dot(xr));
@@ -149,7 +150,7 @@ __device__ __forceinline__ int nth_set_bit64(uint64_t x, int r) {
   int base = 0;
 #pragma unroll
   for (int half = 32; half >= 1; half >>= 1) {
-    const uint64_t lowmask = (half == 64) ? ~0ull : ((1ull << half) - 1ull);
+    const uint64_t lowmask = (1ull << half) - 1ull;
     const int c = __popcll(x & lowmask);
     const bool up = r >= c;
     r = up ? r - c : r;
@@ -159,117 +160,293 @@ __device__ __forceinline__ int nth_set_bit64(uint64_t x, int r) {
   return base;
 }
 
-// Output layer: each wave computes 8 consecutive rows (RW at a time; for the
-// usual short predictor rows all 8 rows' loads are in flight together), writes
-// their logits and, with mask8 != NULL, the 8-bit activation chunk (bit k set
-// when logit row0+k > tau).  One wave per 8-row group, up to a whole number
-// of 64-id blocks so that every activation word is written (ids >= N are
-// inactive).
-template <int DT, int NV, int RW, int BDT>
-__global__ __launch_bounds__(kT) void k_logits_b1(const void* __restrict__ W, const uint16_t* __restrict__ Ws, int N,
-                                                   int cols, const float* __restrict__ h,
-                                                   const void* __restrict__ bias,
-                                                   float* __restrict__ logits, float tau, uint8_t* __restrict__ mask8) {
-  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  const int gw = blockIdx.x * kWpb + wave, nw = gridDim.x * kWpb;
-  const int ngroups = 8 * ((N + 63) / 64);
-  if (gw >= ngroups) return;
-  const int64_t rb = row_bytes(DT, cols);
-  const int nvec = (int)(rb / 16);
-  const int groups = cols / 128;
-  (void)nw;
-  const Bias<BDT> bias_at(bias);
-  float xr[NV][Fmt<DT>::E];
-  load_xreg<DT, NV>(h, nvec, lane, xr);
-  {
-    const int g = gw;                // the grid has one wave per 8-row group
-    const int row0 = g * 8;
-    // lane k < 8 holds the bias of row0 + k, read before the weights
-    const float bl = bias_at(lane < 8 && row0 + lane < N ? row0 + lane : 0);
-    uint32_t bits = 0;
-#pragma unroll
-    for (int it = 0; it < 8 / RW; ++it) {
-      LaneRow<DT, NV> rr[RW];
-#pragma unroll
-      for (int k = 0; k < RW; ++k) {
-        const int r = row0 + it * RW + k;
-        const bool ok = r < N;
-        rr[k].issue(ok ? reinterpret_cast<const char*>(W) + (int64_t)r * rb : nullptr,
-                    DT == 2 && ok ? Ws + (int64_t)r * groups : nullptr, nvec, lane, reinterpret_cast<const char*>(W),
-                    Ws);
-      }
-#pragma unroll
-      for (int k = 0; k < RW; ++k) {
-        const int r = row0 + it * RW + k;
-        const float z = wave_sum(rr[k].dot(xr)) + lane_value(bl, it * RW + k);
-        if (r < N) {
-          if (z > tau) bits |= 1u << (it * RW + k);
-          if (logits && lane == 0) logits[r] = z;
-        }
-      }
-    }
-    if (mask8 && lane == 0) mask8[g] = (uint8_t)bits;
-  }
-}
+// Geometry of the output-layer tile kernel for T neuron ids per block.
+template <int T>
+struct TileGeom {
+  static constexpr int W = T / 8;                    // waves: 8 for 64 ids, 16 for 128 ids
+  static constexpr int NT = W * kWave;
+  static constexpr int NG = T / 64;                  // 64-id groups per tile
+  static constexpr int U = 16;                       // row loads in flight per lane (T=128: 1024 rows per pass)
+  static constexpr int CPW = kMaxHiddenB1 / 64 / W;  // hidden-unit chunks of 64 per wave
+};
 
-// FC1 of the fused batch-1 layer, one block of four waves per 64 neuron ids.
-// The block's active GPU-resident neurons (activation word AND table bitmap;
-// their slots from the table's per-block prefix) are spread over its waves, one
-// row per wave at a time; each wave keeps x in registers, loaded after its first
-// row's weights are in flight.  The block's segment receives the ascending
-// slots and activations of its active GPU-resident neurons, the ascending cold
-// slots of its active CPU-resident ones, and the two counts.  No block waits
-// for another.
-template <int DT, int NV, bool GATED, int BDT>
-__global__ __launch_bounds__(kFc1T) void k_fc1_blk(const uint32_t* __restrict__ mask, SegCtx sg) {
-  constexpr int WPB = kFc1T / kWave;
-  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  const int blk = blockIdx.x;
-  const uint64_t M = (uint64_t)mask[2 * blk] | ((uint64_t)mask[2 * blk + 1] << 32);
-  const uint64_t G = (uint64_t)sg.gbits[2 * blk] | ((uint64_t)sg.gbits[2 * blk + 1] << 32);
-  const int gp = sg.gpre[blk];
-  const uint64_t act = M & G;
-  const int k = __popcll(act);
-  const int64_t row0 = (int64_t)blk * 64;
-  if (wave == 0) {
-    const uint64_t ac = M & ~G;
-    const uint64_t bit = 1ull << lane, lt = bit - 1ull;
-    if (ac & bit) sg.seg_cold[row0 + __popcll(ac & lt)] = (int32_t)(row0 + lane - (gp + __popcll(G & lt)));
-    if (lane == 0) sg.cnt[blk] = (uint32_t)k | ((uint32_t)__popcll(ac) << 16);
+__host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+// LDS of k_pred_fc1 beyond its static arrays: the compacted active hidden units
+// (ids and values), then x in E/4 planes of float4 when FC1 runs.
+__host__ __device__ constexpr size_t pf_hidden_bytes(int H) { return 2 * align16((size_t)4 * H); }
+
+// Output layer (+ FC1) of one tile of T neuron ids [i0, i0 + T):
+//   z_i = c2_i + sum over hidden units m with h_m > 0 of h_m * P2[m, i]
+//   activation bit_i = z_i > tau   (ids >= N inactive)
+// and with FC1, for the tile's active GPU-resident neurons (activation AND the
+// prepared table's bitmap; slot = the table prefix of the 64-id group plus the
+// GPU-resident ids below it in the group):
+//   a = max(0, W1[slot].x + b1[slot]) (* Wup[slot].x when GATED)
+// Each 64-id group of the tile receives its ascending slot segment, its
+// ascending cold-slot segment, the (slot, a) pairs with a != 0 (the only FC2
+// rows that contribute) and the three counts.
+template <int PDT, int DT, int NV, bool GATED, int BDT, int T, bool FC1>
+__global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
+  using G = TileGeom<T>;
+  constexpr int W = G::W, NT = G::NT, NG = G::NG, U = G::U, CPW = G::CPW;
+  constexpr int EP = Fmt<PDT>::E;      // output-layer weights per 16-byte vector
+  constexpr int LPR = T / EP;          // lanes that cover one row slice of the tile
+  constexpr int RPL = kWave / LPR;     // row slices per wave-wide load
+  constexpr int E = Fmt<DT>::E;        // FC1 weights per 16-byte vector
+  constexpr int P = E / 4;             // x planes
+  constexpr int XQ = (NV * kWave * P + NT - 1) / NT;   // x float4 per thread
+  extern __shared__ __attribute__((aligned(16))) char pf_smem[];
+  __shared__ int s_cnt[kMaxHiddenB1 / 64 + 1];
+  __shared__ float red[W][T];
+  __shared__ uint64_t s_M[NG];
+  __shared__ float s_a[T];
+  __shared__ int s_slot[T];
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  const int H = a.H, N = a.N;
+  const int ngroups = (N + 63) / 64;
+  const int64_t i0 = (int64_t)blockIdx.x * T;
+  int* s_m = reinterpret_cast<int*>(pf_smem);
+  float* s_h = reinterpret_cast<float*>(pf_smem + align16((size_t)4 * H));
+  float4v* xs = reinterpret_cast<float4v*>(pf_smem + pf_hidden_bytes(H));
+
+  // ---- issue: table words, bias, x, h
+  uint64_t Gb[NG];
+  int gp[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int grp = blockIdx.x * NG + g;
+    const bool in = FC1 && grp < ngroups;
+    Gb[g] = in ? ((uint64_t)a.gbits[2 * grp] | ((uint64_t)a.gbits[2 * grp + 1] << 32)) : 0ull;
+    gp[g] = in ? a.gpre[grp] : 0;
   }
-  if (wave >= k) return;
-  const int64_t rb = row_bytes(DT, sg.d);
-  const int nvec = (int)(rb / 16);
-  const int groups = sg.d / 128;
-  const Bias<BDT> bias_at(sg.b1);
-  float xr[NV][Fmt<DT>::E];
-  // the first row is peeled so that x is loaded, without a branch, right after
-  // its weights are issued
-  auto row = [&](int t, bool first) {
-    // slot of this block's t-th active GPU-resident neuron; a table prepared
-    // from another T_g cannot index past W1
-    const int sl = gp + __popcll(G & ((1ull << nth_set_bit64(act, t)) - 1ull));
-    const int s = sl < sg.n_g ? sl : -1;
-    const float bs = bias_at(s >= 0 ? s : 0);
-    LaneRow<DT, NV> r, u;
-    r.issue(s >= 0 ? reinterpret_cast<const char*>(sg.W1) + (int64_t)s * rb : nullptr,
-            DT == 2 && s >= 0 ? sg.W1s + (int64_t)s * groups : nullptr, nvec, lane,
-            reinterpret_cast<const char*>(sg.W1), sg.W1s);
-    if constexpr (GATED)
-      u.issue(s >= 0 ? reinterpret_cast<const char*>(sg.Wu) + (int64_t)s * rb : nullptr,
-              DT == 2 && s >= 0 ? sg.Wus + (int64_t)s * groups : nullptr, nvec, lane,
-              reinterpret_cast<const char*>(sg.Wu), sg.Wus);
-    if (first) load_xreg<DT, NV>(sg.x, nvec, lane, xr);
-    float z = wave_sum(r.dot(xr)) + bs;
-    z = z > 0.f ? z : 0.f;
-    if constexpr (GATED) z *= wave_sum(u.dot(xr));
-    if (lane == 0) {
-      sg.seg_slot[row0 + t] = s;
-      sg.seg_a[row0 + t] = s >= 0 ? z : 0.f;
+  const int64_t id = i0 + tid;
+  const Bias<BDT> c2_at(a.c2, (uint32_t)N);
+  const float c2v = c2_at(tid < T && id < N ? id : 0);
+  const int nvec = FC1 ? (int)(row_bytes(DT, a.d) / 16) : 0;
+  const int npad = (nvec + kWave - 1) & ~(kWave - 1);
+  float4v xq[FC1 ? XQ : 1];
+  if constexpr (FC1) {
+    const int nq = a.d / 4;
+    const float4v* x4 = reinterpret_cast<const float4v*>(a.x);
+#pragma unroll
+    for (int r = 0; r < XQ; ++r) {
+      const int q = r * NT + tid;
+      xq[r] = x4[q < nq ? q : 0];
     }
-  };
-  row(wave, true);
-  for (int t = wave + WPB; t < k; t += WPB) row(t, false);
+  }
+  const int nch = (H + 63) / 64;
+  float hv[CPW];
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int c = q * W + wave;
+    const int m = c * 64 + lane;
+    hv[q] = (c < nch && m < H) ? a.h[m] : 0.f;
+  }
+  if constexpr (FC1) {
+    // x in planes: plane p, index v holds x[E*v + 4p .. +3]
+    const int nq = a.d / 4;
+#pragma unroll
+    for (int r = 0; r < XQ; ++r) {
+      const int q = r * NT + tid;
+      if (q < nq) xs[(q % P) * npad + q / P] = xq[r];
+    }
+  }
+
+  // ---- compact the active hidden units (h > 0) in id order
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int c = q * W + wave;
+    const uint64_t b = __ballot(hv[q] > 0.f);
+    if (c < nch && lane == 0) s_cnt[c] = __popcll(b);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int v = lane < nch ? s_cnt[lane] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    if (lane < nch) s_cnt[lane] = incl - v;
+    if (lane == kWave - 1) s_cnt[nch] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int c = q * W + wave;
+    const bool f = hv[q] > 0.f;
+    const uint64_t b = __ballot(f);
+    if (c < nch && f) {
+      const int pos = s_cnt[c] + __popcll(b & ((1ull << lane) - 1ull));
+      s_m[pos] = c * 64 + lane;
+      s_h[pos] = hv[q];
+    }
+  }
+  __syncthreads();
+  const int C = s_cnt[nch];
+  if (a.rows_read && blockIdx.x == 0 && tid == 0) *a.rows_read = C;
+
+  // ---- output layer over the active rows: lane (sub, cl) reads slice vector cl of row sub
+  {
+    const int sub = lane / LPR, cl = lane % LPR;
+    const int64_t prb = row_bytes(PDT, N);
+    const int pvec = (int)(prb / 16);
+    int colv = blockIdx.x * LPR + cl;
+    colv = colv < pvec ? colv : pvec - 1;          // past the row end: discarded ids
+    const int pgroups = N / 128;
+    // the whole matrix as one buffer (the host keeps H * row bytes below 2^31):
+    // rows past the active count read zeros without a memory request
+    const uint32_t pbytes = (uint32_t)(H * prb);
+    const rsrc_t rP = make_rsrc(a.P2, pbytes);
+    const rsrc_t rS = make_rsrc(PDT == 2 ? (const void*)a.P2s : a.P2, PDT == 2 ? (uint32_t)H * pgroups * 2u : 0u);
+    float acc[EP];
+#pragma unroll
+    for (int e = 0; e < EP; ++e) acc[e] = 0.f;
+    for (int j0 = 0; j0 < C; j0 += W * RPL * U) {
+      uint4 w[U];
+      float hs[U], sc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + (u * W + wave) * RPL + sub;
+        const bool ok = j < C;
+        const int m = ok ? s_m[j] : 0;
+        hs[u] = ok ? s_h[j] : 0.f;
+        w[u] = bload16(rP, ok ? (uint32_t)m * (uint32_t)prb + (uint32_t)colv * 16u : pbytes);
+        if constexpr (PDT == 2) sc[u] = h2f(bload2(rS, ok ? (uint32_t)(m * pgroups + colv / 4) * 2u : 0xFFFFFFF0u));
+        else sc[u] = 1.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float wf[EP];
+        widen<PDT>(w[u], PDT == 2 ? sc[u] : 1.f, wf);
+#pragma unroll
+        for (int e = 0; e < EP; ++e) acc[e] = fmaf(wf[e], hs[u], acc[e]);
+      }
+    }
+    // the RPL row groups of the wave hold partial sums of the same ids: butterfly
+    // sum (every lane ends with the same bits)
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
+    if (sub == 0)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) red[wave][cl * EP + e] = acc[e];
+  }
+  __syncthreads();
+  if (tid < T) {                      // waves 0 .. NG-1, one per 64-id group
+    float z = red[0][tid];
+#pragma unroll
+    for (int w2 = 1; w2 < W; ++w2) z += red[w2][tid];
+    z += c2v;
+    const bool valid = id < N;
+    if (a.logits && valid) a.logits[id] = z;
+    const uint64_t bits = __ballot(valid && z > a.tau);
+    if (lane == 0) s_M[wave] = bits;
+    const int grp = blockIdx.x * NG + wave;
+    if (!FC1 && a.mask && lane == 0 && grp < ngroups) {
+      a.mask[2 * grp] = (uint32_t)bits;
+      a.mask[2 * grp + 1] = (uint32_t)(bits >> 32);
+    }
+  }
+  if constexpr (!FC1) return;
+  __syncthreads();
+
+  // ---- FC1 of the tile's active GPU-resident neurons, row r by wave r % W
+  uint64_t act[NG];
+  int kg[NG];
+  int R = 0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    act[g] = s_M[g] & Gb[g];
+    kg[g] = __popcll(act[g]);
+    R += kg[g];
+  }
+  {
+    const int64_t rb = row_bytes(DT, a.d);
+    const int groups = a.d / 128;
+    const Bias<BDT> b1_at(a.b1, (uint32_t)a.n_g);
+    const char* W1 = reinterpret_cast<const char*>(a.W1);
+    const char* Wu = reinterpret_cast<const char*>(a.Wu);
+    for (int r = wave; r < R; r += W) {
+      const int g = (NG == 2 && r >= kg[0]) ? 1 : 0;
+      const int t = g ? r - kg[0] : r;
+      const int sl = gp[g] + __popcll(Gb[g] & ((1ull << nth_set_bit64(act[g], t)) - 1ull));
+      // a table prepared from another T_g cannot index past W1
+      const int s = __builtin_amdgcn_readfirstlane(sl < a.n_g ? sl : -1);
+      const float bs = b1_at(s >= 0 ? s : 0);
+      LaneRow<DT, NV> rw, ru;
+      rw.issue(s >= 0 ? W1 + (int64_t)s * rb : nullptr, DT == 2 && s >= 0 ? a.W1s + (int64_t)s * groups : nullptr,
+               nvec, lane);
+      if constexpr (GATED)
+        ru.issue(s >= 0 ? Wu + (int64_t)s * rb : nullptr, DT == 2 && s >= 0 ? a.Wus + (int64_t)s * groups : nullptr,
+                 nvec, lane);
+      float a0 = 0.f, g0 = 0.f;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int v = u * kWave + lane;
+        const bool vin = v < nvec;
+        const int vc = vin ? v : 0;
+        float xv[E];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const float4v t4 = xs[p * npad + vc];
+          xv[4 * p] = vin ? t4.x : 0.f; xv[4 * p + 1] = vin ? t4.y : 0.f;
+          xv[4 * p + 2] = vin ? t4.z : 0.f; xv[4 * p + 3] = vin ? t4.w : 0.f;
+        }
+        float wf[E];
+        widen<DT>(rw.w[u], DT == 2 ? rw.sc[u] : 1.f, wf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) a0 = fmaf(wf[e], xv[e], a0);
+        if constexpr (GATED) {
+          widen<DT>(ru.w[u], DT == 2 ? ru.sc[u] : 1.f, wf);
+#pragma unroll
+          for (int e = 0; e < E; ++e) g0 = fmaf(wf[e], xv[e], g0);
+        }
+        // x is read from LDS vector by vector: keeps only the row's weights in
+        // registers (other waves cover the LDS latency)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float z = wave_sum(a0) + bs;
+      z = z > 0.f ? z : 0.f;
+      if constexpr (GATED) z *= wave_sum(g0);
+      if (lane == 0) {
+        s_slot[r] = s;
+        s_a[r] = s >= 0 ? z : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- segments of each 64-id group, by wave g
+  if (wave < NG) {
+    const int g = wave;
+    const int grp = blockIdx.x * NG + g;
+    if (grp < ngroups) {
+      const int r0 = g == 0 ? 0 : kg[0];
+      const int k = kg[g];
+      const bool in = lane < k;
+      const int s = in ? s_slot[r0 + lane] : 0;
+      const float av = in ? s_a[r0 + lane] : 0.f;
+      const int64_t base = (int64_t)grp * 64;
+      const uint64_t lt = (1ull << lane) - 1ull;
+      if (in) a.seg_slot[base + lane] = s;
+      const bool nz = in && av != 0.f;
+      const uint64_t bn = __ballot(nz);
+      if (nz) {
+        const int p = __popcll(bn & lt);
+        a.pos_slot[base + p] = s;
+        a.pos_a[base + p] = av;
+      }
+      const uint64_t ac = s_M[g] & ~Gb[g];
+      if ((ac >> lane) & 1ull)
+        a.seg_cold[base + __popcll(ac & lt)] = (int32_t)(base + lane - (gp[g] + __popcll(Gb[g] & lt)));
+      if (lane == 0) a.cnt[grp] = (uint32_t)k | ((uint32_t)__popcll(ac) << 8) | ((uint32_t)__popcll(bn) << 16);
+    }
+  }
 }
 
 // Vectors-per-lane bound used for a row of nvec 16-byte vectors (0 = unsupported).
@@ -281,6 +458,14 @@ int pick_nv(int nvec) {
     if (nv * kWave >= nvec) return nv;
   }
   return 0;
+}
+
+int pick_nv_rt(int dt, int nvec) {
+  switch (dt) {
+    case 0: return pick_nv<0>(nvec);
+    case 1: return pick_nv<1>(nvec);
+    default: return pick_nv<2>(nvec);
+  }
 }
 
 int grid_for(int64_t waves, int cap) {
@@ -336,64 +521,60 @@ hipError_t fc1_dt(const B1Gemv& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT>
-hipError_t logits_dt(const B1Gemv& g, float tau, uint8_t* mask8, hipStream_t s) {
-  const int nvec = (int)(row_bytes(DT, g.cols) / 16);
-  const dim3 gr((unsigned)grid_for(8 * (((int64_t)g.rows + 63) / 64), 1 << 30)), bl(kT);
-#define PI_LOG(NVV, RWV)                                                                                  \
-  do {                                                                                                      \
-    if (g.bias && g.bias_dt == 0)                                                                          \
-      hipLaunchKernelGGL((k_logits_b1<DT, NVV, RWV, 0>), gr, bl, 0, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, \
-                         g.out, tau, mask8);                                                               \
-    else                                                                                                    \
-      hipLaunchKernelGGL((k_logits_b1<DT, NVV, RWV, 1>), gr, bl, 0, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, \
-                         g.out, tau, mask8);                                                               \
-  } while (0)
-  switch (pick_nv<DT>(nvec)) {
-    case 1: PI_LOG(1, 8); break;
-    case 2: PI_LOG(2, 8); break;
-    case 4: PI_LOG(4, 4); break;
-    case 8: if constexpr (Fmt<DT>::E <= 16) PI_LOG(8, 2); break;
-    case 16: if constexpr (Fmt<DT>::E <= 8) PI_LOG(16, 1); break;
-    default: return hipErrorInvalidValue;
+// Tile width: 128 ids (16 waves, at most 128 VGPRs) when that still gives most
+// CUs a block and one FC1 row fits the register budget, else 64 ids (8 waves).
+int pick_tile(int N, bool gated, int dt) {
+  const int t128 = (N + 127) / 128;
+  return (!gated && dt != 2 && t128 >= 160 && t128 <= 256) ? 128 : 64;
+}
+
+template <int PDT, int DT, int NV, bool GATED, int BDT, int T, bool FC1>
+hipError_t pf_launch(const PredFc1Args& a, hipStream_t s) {
+  const unsigned blocks = (unsigned)((a.N + T - 1) / T);
+  size_t shm = pf_hidden_bytes(a.H);
+  if constexpr (FC1) {
+    const int nvec = (int)(row_bytes(DT, a.d) / 16);
+    const int npad = (nvec + kWave - 1) & ~(kWave - 1);
+    shm += (size_t)(Fmt<DT>::E / 4) * npad * 16;
   }
-#undef PI_LOG
+  hipLaunchKernelGGL((k_pred_fc1<PDT, DT, NV, GATED, BDT, T, FC1>), dim3(blocks), dim3(T * 8), shm, s, a);
   return hipGetLastError();
 }
 
-template <int DT, bool GATED>
-hipError_t fc1_blk_dt(const uint32_t* mask, const SegCtx& sg, int nblk, hipStream_t s) {
-  const int nvec = (int)(row_bytes(DT, sg.d) / 16);
-  const dim3 gr((unsigned)nblk), bl(kFc1T);
-  const size_t shm = 0;
-#define PI_FB(NVV)                                                                    \
-  do {                                                                                 \
-    if (sg.b1 && sg.b1_dt == 0)                                                       \
-      hipLaunchKernelGGL((k_fc1_blk<DT, NVV, GATED, 0>), gr, bl, shm, s, mask, sg);   \
-    else                                                                               \
-      hipLaunchKernelGGL((k_fc1_blk<DT, NVV, GATED, 1>), gr, bl, shm, s, mask, sg);   \
+template <int PDT, int BDT>
+hipError_t pred_out_pdt(const PredFc1Args& a, hipStream_t s) {
+  return pick_tile(a.N, false, 0) == 128 ? pf_launch<PDT, 0, 1, false, BDT, 128, false>(a, s)
+                                      : pf_launch<PDT, 0, 1, false, BDT, 64, false>(a, s);
+}
+
+// Fused kernels exist for these (output-layer dtype, FFN dtype, bias dtype)
+// combinations: all fp32, fp16 predictor + fp16 FFN, fp16 predictor + int4 FFN
+// (fp16 biases); fp32 gated layers take the separate kernels.
+template <int PDT, int DT, int BDT, bool GATED>
+hipError_t pred_fc1_combo(const PredFc1Args& a, hipStream_t s) {
+  const int nv = pick_nv<DT>((int)(row_bytes(DT, a.d) / 16));
+  constexpr bool kWide = !GATED && DT != 2;
+  const bool t128 = pick_tile(a.N, GATED, DT) == 128;
+#define PI_PF(NVV)                                                                             \
+  do {                                                                                          \
+    if constexpr (kWide)                                                                        \
+      if (t128) return pf_launch<PDT, DT, NVV, GATED, BDT, kWide ? 128 : 64, true>(a, s);      \
+    return pf_launch<PDT, DT, NVV, GATED, BDT, 64, true>(a, s);                                \
   } while (0)
-  switch (pick_nv<DT>(nvec)) {
-    case 1: PI_FB(1); break;
-    case 2: PI_FB(2); break;
-    case 4: PI_FB(4); break;
-    case 8: if constexpr (Fmt<DT>::E <= 16) PI_FB(8); break;
-    case 16: if constexpr (Fmt<DT>::E <= 8) PI_FB(16); break;
+  switch (nv) {
+    case 1: case 2: case 4: PI_PF(4);
+    case 8: PI_PF(8);
+    case 16: if constexpr (Fmt<DT>::E <= 8) PI_PF(16);
     default: return hipErrorInvalidValue;
   }
-#undef PI_FB
-  return hipGetLastError();
+#undef PI_PF
 }
 
 }  // namespace
 
 bool b1_supported(int dt, int64_t cols) {
   const int nvec = (int)(row_bytes(dt, cols) / 16);
-  switch (dt) {
-    case 0: return pick_nv<0>(nvec) != 0;
-    case 1: return pick_nv<1>(nvec) != 0;
-    default: return pick_nv<2>(nvec) != 0;
-  }
+  return pick_nv_rt(dt, nvec) != 0;
 }
 
 hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s) {
@@ -412,25 +593,35 @@ hipError_t launch_fc1_b1(const B1Gemv& g, bool gated, hipStream_t s) {
   }
 }
 
-hipError_t launch_logits_b1(const B1Gemv& g, float tau, uint8_t* mask8, hipStream_t s) {
-  switch (g.dt) {
-    case 0: return logits_dt<0>(g, tau, mask8, s);
-    case 1: return logits_dt<1>(g, tau, mask8, s);
-    default: return logits_dt<2>(g, tau, mask8, s);
+bool pred_out_b1_supported(int pdt, int H, int N) {
+  // buffer offsets into P2 are 32-bit
+  return H >= 1 && H <= kMaxHiddenB1 && N >= 1 && (int64_t)H * row_bytes(pdt, N) < ((int64_t)1 << 31);
+}
+
+hipError_t launch_pred_out_b1(const PredFc1Args& a, hipStream_t s) {
+  const bool b32 = a.c2 && a.c2_dt == PI_F32;
+  switch (a.pdt) {
+    case 0: return b32 ? pred_out_pdt<0, 0>(a, s) : pred_out_pdt<0, 1>(a, s);
+    case 1: return b32 ? pred_out_pdt<1, 0>(a, s) : pred_out_pdt<1, 1>(a, s);
+    default: return b32 ? pred_out_pdt<2, 0>(a, s) : pred_out_pdt<2, 1>(a, s);
   }
 }
 
-bool fc1_blk_supported(int dt, int64_t d) {
-  // x staged through LDS by 512 threads x 8 float4
-  return b1_supported(dt, d);
+bool pred_fc1_supported(int pdt, int dt, int bdt, int c2dt, bool gated, int H, int N, int64_t d) {
+  if (!pred_out_b1_supported(pdt, H, N)) return false;
+  if (bdt != c2dt) return false;
+  const int nv = pick_nv_rt(dt, (int)(row_bytes(dt, d) / 16));
+  if (nv == 0) return false;
+  if (pdt == 0 && dt == 0 && bdt == 0) return !gated;
+  if (pdt == 1 && (dt == 1 || dt == 2) && bdt == 1) return true;
+  return false;
 }
 
-hipError_t launch_fc1_blk(const uint32_t* mask, const SegCtx& sg, int dtw, bool gated, int nblk, hipStream_t s) {
-  switch (dtw) {
-    case 0: return gated ? fc1_blk_dt<0, true>(mask, sg, nblk, s) : fc1_blk_dt<0, false>(mask, sg, nblk, s);
-    case 1: return gated ? fc1_blk_dt<1, true>(mask, sg, nblk, s) : fc1_blk_dt<1, false>(mask, sg, nblk, s);
-    default: return gated ? fc1_blk_dt<2, true>(mask, sg, nblk, s) : fc1_blk_dt<2, false>(mask, sg, nblk, s);
-  }
+hipError_t launch_pred_fc1(const PredFc1Args& a, bool gated, hipStream_t s) {
+  if (a.pdt == 0 && a.dt == 0) return pred_fc1_combo<0, 0, 0, false>(a, s);
+  if (a.pdt == 1 && a.dt == 1) return gated ? pred_fc1_combo<1, 1, 1, true>(a, s) : pred_fc1_combo<1, 1, 1, false>(a, s);
+  if (a.pdt == 1 && a.dt == 2) return gated ? pred_fc1_combo<1, 2, 1, true>(a, s) : pred_fc1_combo<1, 2, 1, false>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pi

@@ -4,10 +4,9 @@
 // chunk).  A block reads its chunk's rows over one tile of 64 16-byte vectors
 // (every row slice is one coalesced 1 KB wave load), accumulates in registers,
 // sums its four waves in LDS in a fixed order and writes one partial per
-// (chunk, batch row, column).  The last block to finish a column tile (tile
-// counter) sums the chunk partials in chunk order and applies the merge
-// (+ cold partial when it has active neurons, + b2).  No float atomics: the
-// bits do not depend on block timing.
+// (chunk, batch row, column).  A separate launch sums the chunk partials in
+// chunk order and applies the merge (+ cold partial when it has active
+// neurons, + b2).  No float atomics: the bits do not depend on block timing.
 #include "pi_device.h"
 #include "pi_internal.h"
 
@@ -33,7 +32,7 @@ __global__ __launch_bounds__(kT) void k_fc2(Fc2Args a) {
   const bool vok = v < nvec;
   const int vv = vok ? v : 0;
   const int64_t groups = d / 128;
-  int64_t K = *a.K;
+  int64_t K = a.list ? (int64_t)*a.K : (int64_t)a.n_g;
   K = K < 0 ? 0 : (K > a.n_g ? a.n_g : K);
   const int64_t j0 = K * chunk / nchunks, j1 = K * (chunk + 1) / nchunks;
   const int B = a.B;
@@ -54,10 +53,12 @@ __global__ __launch_bounds__(kT) void k_fc2(Fc2Args a) {
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t j = jb + (int64_t)u * kWpb;
         const bool in = j < j1;
-        const int64_t s = in ? (int64_t)a.list[j] : -1;
+        const int64_t s = in ? (a.list ? (int64_t)a.list[j] : j) : -1;
         sn[u] = (s >= 0 && s < a.n_g) ? s : -1;
+        const int64_t ai = a.a_by_row ? (sn[u] >= 0 ? sn[u] : 0) : j;
 #pragma unroll
-        for (int b = 0; b < NBG; ++b) an[u][b] = (in && b0 + b < B) ? a.a[(int64_t)(b0 + b) * a.n_g + j] : 0.f;
+        for (int b = 0; b < NBG; ++b)
+          an[u][b] = (in && sn[u] >= 0 && b0 + b < B) ? a.a[(int64_t)(b0 + b) * a.a_stride + ai] : 0.f;
       }
     };
     fetch(j0 + wave);
@@ -128,34 +129,89 @@ __global__ __launch_bounds__(kT) void k_reduce(ReduceArgs r) {
   }
 }
 
-// Batch-1 FC2 over the per-64-id-block segments of the fused layer: chunk c
-// covers the blocks [c*nblk/C, (c+1)*nblk/C); its rows are those blocks'
-// active GPU-resident neurons in block order (so in ascending slot order).
-// The block's segment entries are gathered into LDS first (one round trip).
+// Batch-1 FC2 over the group segments of the fused layer, and the list
+// assembly.  Blocks [0, tiles * kSegChunks) are FC2 blocks: block (tile,
+// chunk) takes the groups [c * ngroups / C, (c + 1) * ngroups / C); its rows are
+// those groups' (slot, a) pairs with a != 0 in group order (ascending slots),
+// gathered into LDS first (one round trip), then the listed W2 rows are
+// streamed over the block's column tile: 16-byte loads, kSegUnroll rows in
+// flight per wave.  It writes one partial per chunk.  The other blocks each
+// place 256 entries (four groups) of the ascending lists A_g / A_c, at offsets
+// from the counts of the groups below; list block 0 writes K and K_c.
 template <int DT>
-__global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a) {
+__global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
   constexpr int E = Fmt<DT>::E;
   extern __shared__ int32_t fsm[];
   __shared__ float red[kWpb][kWave * E];
   __shared__ int s_cnt[64], s_off[65];
+  __shared__ int s_red[5][kWpb];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int tile = blockIdx.x, chunk = blockIdx.y, nchunks = gridDim.y;
-  const int b0 = (int)((int64_t)a.nblk * chunk / nchunks), b1 = (int)((int64_t)a.nblk * (chunk + 1) / nchunks);
+  const int ngroups = a.ngroups;
+  if ((int)blockIdx.x >= tiles * kSegChunks) {
+    // ---- list assembly: groups [4 lb, 4 lb + 4), one entry per thread
+    const int lb = (int)blockIdx.x - tiles * kSegChunks;
+    const int g0 = 4 * lb;
+    const int e = g0 * 64 + tid;
+    const int grp = e / 64, i = e % 64;
+    const bool ein = grp < ngroups;
+    const int32_t es = ein ? a.seg_slot[e] : 0;
+    const int32_t ec = (ein && a.A_c) ? a.seg_cold[e] : 0;
+    const uint32_t mine = ein ? a.cnt[grp] : 0u;
+    // counts below g0 and in total, summed over a strided share of the groups
+    int below_g = 0, below_c = 0, tot_g = 0, tot_c = 0, tot_z = 0;
+    for (int q = tid; q < ngroups; q += kT) {
+      const uint32_t c = a.cnt[q];
+      const int cg = (int)cnt_gpu(c), cc = (int)cnt_cold(c);
+      tot_g += cg; tot_c += cc; tot_z += (int)cnt_nz(c);
+      if (q < g0) { below_g += cg; below_c += cc; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      below_g += __shfl_xor(below_g, off, kWave); below_c += __shfl_xor(below_c, off, kWave);
+      tot_g += __shfl_xor(tot_g, off, kWave); tot_c += __shfl_xor(tot_c, off, kWave);
+      tot_z += __shfl_xor(tot_z, off, kWave);
+    }
+    if (lane == 0) {
+      s_red[0][wave] = below_g; s_red[1][wave] = below_c; s_red[2][wave] = tot_g; s_red[3][wave] = tot_c;
+      s_red[4][wave] = tot_z;
+    }
+    if (lane == 0 && wave < 4) s_cnt[wave] = g0 + wave < ngroups ? (int)a.cnt[g0 + wave] : 0;
+    __syncthreads();
+    int bg = 0, bc = 0, tg = 0, tc = 0, tz = 0;
+#pragma unroll
+    for (int w = 0; w < kWpb; ++w) {
+      bg += s_red[0][w]; bc += s_red[1][w]; tg += s_red[2][w]; tc += s_red[3][w]; tz += s_red[4][w];
+    }
+    // offsets of this thread's group within the block's four
+    const int gi = tid / 64;
+    for (int w = 0; w < gi; ++w) { bg += (int)cnt_gpu((uint32_t)s_cnt[w]); bc += (int)cnt_cold((uint32_t)s_cnt[w]); }
+    if (ein && i < (int)cnt_gpu(mine) && bg + i < a.n_g) a.A_g[bg + i] = es;
+    if (ein && a.A_c && i < (int)cnt_cold(mine) && bc + i < a.n_c) a.A_c[bc + i] = ec;
+    if (lb == 0 && tid == 0) {
+      *a.K = tg < a.n_g ? tg : a.n_g;
+      if (a.K_c) *a.K_c = tc < a.n_c ? tc : a.n_c;
+      if (a.rows_read) *a.rows_read = tz;
+    }
+    return;
+  }
+  // ---- FC2
+  const int tile = (int)blockIdx.x % tiles, chunk = (int)blockIdx.x / tiles;
+  const int b0 = (int)((int64_t)ngroups * chunk / kSegChunks), b1 = (int)((int64_t)ngroups * (chunk + 1) / kSegChunks);
   const int nb = b1 - b0;
   int32_t* c_slot = fsm;
   float* c_a = reinterpret_cast<float*>(fsm + nb * 64);
-  // each thread's share of the raw segment entries, loaded together with the counts
+  // each thread's share of the raw (slot, a) entries, loaded together with the counts
   constexpr int RQ = 16;   // entries per thread: nb * 64 <= RQ * kT
   int32_t rs[RQ];
   float ra[RQ];
 #pragma unroll
   for (int q = 0; q < RQ; ++q) {
     const int e = q * kT + tid;
-    rs[q] = e < nb * 64 ? a.seg_slot[(int64_t)b0 * 64 + e] : -1;
-    ra[q] = e < nb * 64 ? a.seg_a[(int64_t)b0 * 64 + e] : 0.f;
+    rs[q] = e < nb * 64 ? a.pos_slot[(int64_t)b0 * 64 + e] : -1;
+    ra[q] = e < nb * 64 ? a.pos_a[(int64_t)b0 * 64 + e] : 0.f;
   }
-  if (tid < nb) s_cnt[tid] = (int)(a.cnt[b0 + tid] & 0xFFFFu);
+  if (tid < nb) s_cnt[tid] = (int)cnt_nz(a.cnt[b0 + tid]);
   __syncthreads();
   if (wave == 0) {
     const int v = lane < nb ? s_cnt[lane] : 0;
@@ -187,35 +243,36 @@ __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a) {
   const int nvec = (int)(rb / 16);
   const int v = tile * kWave + lane;
   const bool vok = v < nvec;
-  const int vv = vok ? v : 0;
   const int64_t groups = d / 128;
   const int64_t tile_col0 = (int64_t)tile * kWave * E;
   const char* W2 = reinterpret_cast<const char*>(a.W2);
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int jb = wave; jb < R; jb += kWpb * kUnroll) {
-    int64_t sl[kUnroll];
-    uint4 w[kUnroll];
-    float scl[kUnroll];
+  for (int jb = wave; jb < R; jb += kWpb * kSegUnroll) {
+    uint4 w[kSegUnroll];
+    float scl[kSegUnroll], ab[kSegUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kSegUnroll; ++u) {
+      // row j is the same for the whole wave: a buffer over it, empty for an
+      // absent row; lanes past the row end read zeros
       const int j = jb + u * kWpb;
-      int64_t s = j < R ? (int64_t)c_slot[j] : -1;
-      if (s >= a.n_g) s = -1;
-      sl[u] = s;
-      const int64_t s0 = s >= 0 ? s : 0;
-      w[u] = s >= 0 ? ld16(W2 + s0 * rb + (int64_t)vv * 16) : make_uint4(0, 0, 0, 0);
-      if constexpr (DT == 2) scl[u] = s >= 0 ? h2f(a.W2s[s0 * groups + vv / 4]) : 0.f;
+      int s = j < R ? c_slot[j] : -1;
+      s = __builtin_amdgcn_readfirstlane(s < a.n_g ? s : -1);
+      ab[u] = j < R ? c_a[j] : 0.f;
+      const rsrc_t rw = make_rsrc(W2 + (s >= 0 ? (int64_t)s * rb : 0), s >= 0 ? (uint32_t)rb : 0u);
+      w[u] = bload16(rw, (uint32_t)v * 16u);
+      if constexpr (DT == 2) {
+        const rsrc_t rs = make_rsrc(a.W2s + (s >= 0 ? (int64_t)s * groups : 0), s >= 0 ? (uint32_t)groups * 2u : 0u);
+        scl[u] = h2f(bload2(rs, (uint32_t)(v / 4) * 2u));
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (sl[u] < 0) continue;
+    for (int u = 0; u < kSegUnroll; ++u) {
       float wf[E];
       widen<DT>(w[u], DT == 2 ? scl[u] : 1.f, wf);
-      const float ab = c_a[jb + u * kWpb];
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(ab, wf[e], acc[e]);
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(ab[u], wf[e], acc[e]);
     }
   }
 #pragma unroll
@@ -232,97 +289,24 @@ __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a) {
   }
 }
 
-// Exclusive scans of two count arrays into LDS; returns the totals.
-__device__ void block_scan2(const int* c1, const int* c2, int n, int* o1, int* o2, int& t1, int& t2) {
-  __shared__ int ws1[kWpb], ws2[kWpb];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  const int per = (n + kT - 1) / kT, i0 = tid * per;
-  int s1 = 0, s2 = 0;
-  for (int k = 0; k < per; ++k)
-    if (i0 + k < n) { s1 += c1[i0 + k]; s2 += c2[i0 + k]; }
-  int a1 = s1, a2 = s2;
+// y[t] = the kSegChunks partials summed in chunk order (+ y_c when K_c is NULL
+// or *K_c != 0, + b2): one column per thread, every partial load in flight.
+__global__ __launch_bounds__(kWave) void k_reduce_y(ReduceYArgs r) {
+  const int64_t t = (int64_t)blockIdx.x * kWave + threadIdx.x;
+  if (t >= r.d) return;
+  const int kc = r.K_c ? *r.K_c : 1;
+  const float yc = r.y_c ? r.y_c[t] : 0.f;
+  const float bb = r.b2 ? load_bias(r.b2, r.b2_dt, t) : 0.f;
+  float p[kSegChunks];
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int u1 = __shfl_up(a1, off, kWave), u2 = __shfl_up(a2, off, kWave);
-    if (lane >= off) { a1 += u1; a2 += u2; }
-  }
-  if (lane == kWave - 1) { ws1[wv] = a1; ws2[wv] = a2; }
-  __syncthreads();
-  int p1 = 0, p2 = 0;
-  t1 = 0; t2 = 0;
-  for (int w = 0; w < kWpb; ++w) {
-    if (w < wv) { p1 += ws1[w]; p2 += ws2[w]; }
-    t1 += ws1[w]; t2 += ws2[w];
-  }
-  int r1 = p1 + a1 - s1, r2 = p2 + a2 - s2;
-  for (int k = 0; k < per; ++k)
-    if (i0 + k < n) { o1[i0 + k] = r1; o2[i0 + k] = r2; r1 += c1[i0 + k]; r2 += c2[i0 + k]; }
-  __syncthreads();
+  for (int c = 0; c < kSegChunks; ++c) p[c] = r.partials[(int64_t)c * r.d + t];
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < kSegChunks; ++c) sum += p[c];
+  if (r.y_c && kc != 0) sum += yc;
+  if (r.b2) sum += bb;
+  r.y[t] = sum;
 }
-
-// Blocks [0, reduce_blocks): y = ordered sum of the FC2 partials (+ cold partial
-// when the cold side has an active neuron, + b2).  The other blocks assemble
-// the ascending lists A_g / A_c from the segments, 256 entries each; the first
-// of them writes K and K_c.
-__global__ __launch_bounds__(kT) void k_reduce_lists(ReduceListArgs r) {
-  extern __shared__ int rsm[];
-  const int tid = threadIdx.x;
-  const int nblk = r.nblk;
-  if ((int)blockIdx.x < r.reduce_blocks) {
-    __shared__ int any_cold;
-    if (tid == 0) any_cold = 0;
-    __syncthreads();
-    bool mine = false;
-    if (r.y_c && !r.always_c)
-      for (int b = tid; b < nblk; b += kT) mine = mine || (r.cnt[b] >> 16) != 0u;
-    if (mine) any_cold = 1;
-    __syncthreads();
-    const bool add_c = r.y_c && (r.always_c || any_cold);
-    const int64_t n = r.d;
-    for (int64_t t = blockIdx.x * (int64_t)kT + tid; t < n; t += (int64_t)r.reduce_blocks * kT) {
-      float sum = 0.f;
-      for (int c0 = 0; c0 < r.chunks; c0 += 16) {
-        float p[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) p[c] = c0 + c < r.chunks ? r.partials[(int64_t)(c0 + c) * n + t] : 0.f;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) sum += p[c];
-      }
-      if (add_c) sum += r.y_c[t];
-      if (r.b2) sum += load_bias(r.b2, r.b2_dt, t);
-      r.y[t] = sum;
-    }
-    return;
-  }
-  const int lb = (int)blockIdx.x - r.reduce_blocks;
-  int* cg = rsm;
-  int* cc = rsm + nblk;
-  int* og = rsm + 2 * nblk;
-  int* oc = rsm + 3 * nblk;
-  // this block's entries: 4 id blocks x 64 = 256, one per thread, loaded with the counts
-  const int e = lb * kT + tid;
-  const bool ein = e < nblk * 64;
-  const int32_t es = ein ? r.seg_slot[e] : 0;
-  const int32_t ec = (ein && r.A_c) ? r.seg_cold[e] : 0;
-  for (int b = tid; b < nblk; b += kT) {
-    const uint32_t c = r.cnt[b];
-    cg[b] = (int)(c & 0xFFFFu);
-    cc[b] = (int)(c >> 16);
-  }
-  __syncthreads();
-  int tg, tc;
-  block_scan2(cg, cc, nblk, og, oc, tg, tc);
-  if (ein) {
-    const int b = e / 64, i = e % 64;
-    if (i < cg[b] && og[b] + i < r.n_g) r.A_g[og[b] + i] = es;
-    if (r.A_c && i < cc[b] && oc[b] + i < r.n_c) r.A_c[oc[b] + i] = ec;
-  }
-  if (lb == 0 && tid == 0) {
-    *r.K = tg < r.n_g ? tg : r.n_g;
-    if (r.K_c) *r.K_c = tc < r.n_c ? tc : r.n_c;
-  }
-}
-
 template <int DT>
 hipError_t fc2_dt(const Fc2Args& a, hipStream_t s) {
   const dim3 g((unsigned)fc2_tiles(DT, a.d), (unsigned)fc2_chunks(a.B)), t(kT);
@@ -354,24 +338,21 @@ hipError_t launch_fc2(const Fc2Args& a, hipStream_t s) {
 }
 
 hipError_t launch_fc2_seg(const Fc2SegArgs& a, hipStream_t s) {
-  const int nbmax = (a.nblk + kSegChunks - 1) / kSegChunks;
+  const int nbmax = (a.ngroups + kSegChunks - 1) / kSegChunks;
   const size_t shm = (size_t)nbmax * 64 * 4 * 2;
-  const dim3 g((unsigned)fc2_tiles(a.dt, a.d), (unsigned)kSegChunks), t(kT);
+  const int tiles = fc2_tiles(a.dt, a.d);
+  const int list_blocks = (a.ngroups + 3) / 4;
+  const dim3 g((unsigned)(tiles * kSegChunks + list_blocks)), t(kT);
   switch (a.dt) {
-    case PI_F32: hipLaunchKernelGGL(k_fc2_seg<0>, g, t, shm, s, a); break;
-    case PI_F16: hipLaunchKernelGGL(k_fc2_seg<1>, g, t, shm, s, a); break;
-    default: hipLaunchKernelGGL(k_fc2_seg<2>, g, t, shm, s, a); break;
+    case PI_F32: hipLaunchKernelGGL(k_fc2_seg<0>, g, t, shm, s, a, tiles); break;
+    case PI_F16: hipLaunchKernelGGL(k_fc2_seg<1>, g, t, shm, s, a, tiles); break;
+    default: hipLaunchKernelGGL(k_fc2_seg<2>, g, t, shm, s, a, tiles); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_lists(const ReduceListArgs& r, hipStream_t s) {
-  const int list_blocks = (int)(((int64_t)r.nblk * 64 + kT - 1) / kT);
-  ReduceListArgs q = r;
-  q.reduce_blocks = (int)((r.d + kT - 1) / kT);
-  q.chunks = kSegChunks;
-  hipLaunchKernelGGL(k_reduce_lists, dim3((unsigned)(q.reduce_blocks + list_blocks)), dim3(kT),
-                     (size_t)r.nblk * 4 * 4, s, q);
+hipError_t launch_reduce_y(const ReduceYArgs& r, hipStream_t s) {
+  hipLaunchKernelGGL(k_reduce_y, dim3((unsigned)((r.d + kWave - 1) / kWave)), dim3(kWave), 0, s, r);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 
 namespace pi {
 
-// Generic row-dot GEMV (any batch, any row length): predictor layers and FC1.
+// Generic row-dot GEMV (any batch, any row length): predictor hidden layer and FC1.
 struct RowdotArgs {
   const void* W;             // [rows x cols]
   const uint16_t* Ws;        // int4 scales
@@ -37,7 +37,7 @@ hipError_t launch_compact(int B, int N, const float* logits, float tau, const in
                           int32_t* A_g, int32_t* K, const int32_t* T_c, int n_c, int32_t* A_c,
                           int32_t* K_c, hipStream_t s);
 
-// Batch-1 register-x GEMV kernels.
+// Batch-1 register-x GEMV kernels (pi_fast.hip).
 struct B1Gemv {
   const void* W;
   const uint16_t* Ws;
@@ -52,88 +52,111 @@ struct B1Gemv {
   float* out;
   const int32_t* list;       // FC1
   const int32_t* Kp;         // FC1
-  uint32_t* zero_ptr;        // hidden: words cleared by block 0
-  int zero_n;
 };
 bool b1_supported(int dt, int64_t cols);
 hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s);
 hipError_t launch_fc1_b1(const B1Gemv& g, bool gated, hipStream_t s);
 
-// Output layer; mask8 != NULL also writes the activation bits, 8 rows per byte.
-hipError_t launch_logits_b1(const B1Gemv& g, float tau, uint8_t* mask8, hipStream_t s);
-
-// FC1 of the fused batch-1 layer, one 64-id block per 512-thread block (see pi_fast.hip).
-struct SegCtx {
+// Batch 1: the predictor output layer over the active hidden units (P2 stored
+// hidden-major), with the activation decision, and in the fused layer FC1 of
+// the tile's active GPU-resident neurons (pi_fast.hip).  One block per tile of
+// 64 or 128 neuron ids; no block waits for another.
+constexpr int kMaxHiddenB1 = 4096;   // hidden units the batch-1 output layer compacts in LDS
+struct PredFc1Args {
+  const void* P2;            // [H x N] hidden-major
+  const uint16_t* P2s;       // int4 scales [H x N/128]
+  int pdt;
+  int H;
+  int N;
+  const float* h;            // [H]
+  const void* c2;
+  int c2_dt;
+  float tau;
+  float* logits;             // [N], optional
+  uint32_t* mask;            // 2 words per 64 ids, optional (output-layer-only launches)
+  // FC1 (fused layer)
   const uint32_t* gbits;     // prepared table: GPU-resident bitmap, 2 words per 64 ids
-  const int32_t* gpre;       // prepared table: GPU-resident ids below each 64-id block
+  const int32_t* gpre;       // prepared table: GPU-resident ids below each 64-id group
   const void* W1;
   const uint16_t* W1s;
   const void* Wu;
   const uint16_t* Wus;
+  int dt;
   int d;
   int n_g;
   const float* x;
   const void* b1;
   int b1_dt;
-  int32_t* seg_slot;         // [nblk x 64] ascending slots of each block's active GPU neurons
-  float* seg_a;              // [nblk x 64] their activations (batch 1)
-  int32_t* seg_cold;         // [nblk x 64] ascending cold slots of each block's active CPU neurons
-  uint32_t* cnt;             // [nblk] GPU count | CPU count << 16
+  int32_t* seg_slot;         // [groups x 64] ascending slots of each group's active GPU-resident neurons
+  int32_t* seg_cold;         // [groups x 64] ascending cold slots of each group's active CPU-resident neurons
+  int32_t* pos_slot;         // [groups x 64] the group's slots whose FC1 output is non-zero, ascending
+  float* pos_a;              // [groups x 64] their FC1 outputs
+  uint32_t* cnt;             // [groups] GPU count | CPU count << 8 | non-zero count << 16
+  int32_t* rows_read;        // optional: block 0 writes the number of output-layer rows read
 };
-bool fc1_blk_supported(int dt, int64_t d);
-hipError_t launch_fc1_blk(const uint32_t* mask, const SegCtx& sg, int dtw, bool gated, int nblk, hipStream_t s);
+// Group count word fields.
+__host__ __device__ constexpr uint32_t cnt_gpu(uint32_t c) { return c & 0xFFu; }
+__host__ __device__ constexpr uint32_t cnt_cold(uint32_t c) { return (c >> 8) & 0xFFu; }
+__host__ __device__ constexpr uint32_t cnt_nz(uint32_t c) { return (c >> 16) & 0xFFu; }
 
-// Batch-1 FC2 and final reduction over those segments (see pi_fc2.hip).
-constexpr int kSegChunks = 64;   // id-block chunks of the segment FC2 (nblk <= 64 * kSegChunks)
+bool pred_out_b1_supported(int pdt, int H, int N);
+hipError_t launch_pred_out_b1(const PredFc1Args& a, hipStream_t s);
+// Fused output layer + FC1; false when this combination of dtypes and sizes has no fused kernel.
+bool pred_fc1_supported(int pdt, int dt, int bdt, int c2dt, bool gated, int H, int N, int64_t d);
+hipError_t launch_pred_fc1(const PredFc1Args& a, bool gated, hipStream_t s);
+
+// Batch-1 FC2 over the group segments, with the list assembly, and the final
+// ordered sum (pi_fc2.hip).
+constexpr int kSegChunks = 64;   // group chunks of the segment FC2 (groups <= 64 * kSegChunks)
 struct Fc2SegArgs {
   const void* W2;
   const uint16_t* W2s;
   int dt;
   int64_t d;
   int n_g;
-  int nblk;
-  const int32_t* seg_slot;
-  const float* seg_a;
-  const uint32_t* cnt;
-  float* partials;           // [kSegChunks x d]
-};
-struct ReduceListArgs {
-  const float* partials;
-  int64_t d;
-  float* y;
-  const float* y_c;
-  const void* b2;
-  int b2_dt;
-  int nblk;
-  const uint32_t* cnt;
+  int ngroups;
+  const int32_t* pos_slot;
+  const float* pos_a;
   const int32_t* seg_slot;
   const int32_t* seg_cold;
+  const uint32_t* cnt;
+  float* partials;           // [kSegChunks x d]
   int32_t* A_g;
   int32_t* K;
   int32_t* A_c;              // NULL = no cold list
   int32_t* K_c;
-  int n_g;
   int n_c;
-  int always_c;              // add y_c even with no active cold neuron (no cold side)
-  int chunks;                // set by the launcher
-  int reduce_blocks;         // set by the launcher
+  int32_t* rows_read;        // optional: list block 0 writes the number of W2 rows read
+};
+struct ReduceYArgs {
+  const float* partials;     // [kSegChunks x d]
+  int64_t d;
+  float* y;
+  const float* y_c;
+  const int32_t* K_c;        // the cold count written by the FC2 launch (NULL = always add y_c)
+  const void* b2;
+  int b2_dt;
 };
 hipError_t launch_fc2_seg(const Fc2SegArgs& a, hipStream_t s);
-hipError_t launch_reduce_lists(const ReduceListArgs& r, hipStream_t s);
+hipError_t launch_reduce_y(const ReduceYArgs& r, hipStream_t s);
 
 // Activation words from stored logits (union over the batch), and the lists from them.
 hipError_t launch_mask(int B, int N, const float* logits, float tau, uint32_t* mask, hipStream_t s);
 hipError_t launch_list(const ListCtx& c, int n_g, hipStream_t s);
 
+// Neuron-major axpy over listed rows: out[b,:] += a[b, j] * W[list[j], :]
+// (FC2, and the predictor output layer over its hidden-major weights).
 struct Fc2Args {
   const void* W2;
   const uint16_t* W2s;
   int dt;
-  int64_t d;
-  int n_g;
-  const int32_t* list;
-  const int32_t* K;
-  const float* a;            // [B x n_g]
+  int64_t d;                 // row length
+  int n_g;                   // rows in W2 (bound for listed rows)
+  const int32_t* list;       // NULL = rows 0 .. n_g in order
+  const int32_t* K;          // device count of listed rows (ignored when list == NULL)
+  const float* a;            // a[b * a_stride + (a_by_row ? row : j)]
+  int64_t a_stride;
+  int a_by_row;
   int B;
   float* partials;           // [chunks x B x d]
 };
@@ -155,6 +178,8 @@ int fc2_chunks(int B);           // row chunks of FC2 for batch B (partials: chu
 hipError_t launch_fc2(const Fc2Args& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& r, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+// stats[0] = rows0 (unless negative), stats[1] = *K1 (rows read by the separate kernels).
+hipError_t launch_rows_read(int32_t* stats, int32_t rows0, const int32_t* K1, hipStream_t s);
 
 hipError_t launch_merge(int B, int d, float* y, const float* y_c, const int32_t* K_c, const void* b2,
                         int b2_dt, hipStream_t s);

@@ -1,13 +1,14 @@
 """Decode benchmark of the neuron-aware sparse FFN on one MI355X.
 
 One step = one decoded token (batch B) through every FFN layer of the stack:
-for each layer, pi_predict -> pi_compact -> pi_sparse_ffn -> pi_merge, all
-on one stream, layers serialised.  Weights and inputs are seeded synthetic
-tensors generated on the device before timing; each step has its own inputs.
-Steps are captured once into HIP graphs and replayed.
+for each layer one pi_ffn_layer_stages call (predictor, activation decision
+and compaction, FFN over the GPU-resident neurons, merge), all on one stream,
+layers serialised.  Weights and inputs are seeded synthetic tensors
+generated on the device before timing; each step has its own inputs.  Steps
+are captured once into HIP graphs and replayed.
 
 Prints one JSON line (rank 0): throughput in tokens/s, the roofline of the
-dominant stage, and the CPU oracle timed on a bounded sample.
+dominant kernel, and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -58,39 +59,43 @@ def bias_bytes(dt):
     return 4.0 if dt == synth.F32 else 2.0
 
 
-def layer_bytes(spec, B, K, K_c):
-    """Algorithmic HBM bytes of one layer's step: predictor weights and biases,
-    the active GPU-resident neurons (FC1 row + bias + FC2 row, + up row if
-    gated), and the small vectors (x, h, logits, lists, y, cold partial)."""
+def layer_bytes(spec, B, K, K_c, rows_p2, rows_w2):
+    """Algorithmic HBM bytes of one layer's step: the predictor weights the method
+    reads (all of P1; the hidden-major P2 rows of the hidden units with h > 0,
+    rows_p2 of them; c2), the active GPU-resident neurons (FC1 row + bias for
+    each of the K listed neurons, + up row if gated; the FC2 row of each of the
+    rows_w2 neurons whose FC1 output is non-zero), and the small vectors (x, h,
+    logits, lists, y, cold partial)."""
     cfg = spec.cfg
     d, N, H = cfg.d, cfg.N, spec.H
     wp, w, wb = wbytes(cfg.pdtype), wbytes(cfg.wdtype), bias_bytes(cfg.bdtype)
-    pred = (H * d + N * H) * wp + N * wb
-    mats = 3 if cfg.gated else 2
-    ffn = K * (mats * d * w + wb)
+    pred = H * d * wp + rows_p2 * N * wp + N * wb
+    mats1 = 2 if cfg.gated else 1
+    ffn = K * (mats1 * d * w + wb) + rows_w2 * d * w
     small = B * d * 4 + 2 * B * H * 4 + 2 * B * N * 4 + spec.n_g * 4 + 2 * K * 4 + B * d * 4 * 2
     if len(spec.T_c):
         small += len(spec.T_c) * 4 + 2 * K_c * 4 + (B * d * 4 if K_c else 0)
     return pred, ffn, small
 
 
-def kernel_bytes(spec, B, K, K_c):
-    """Algorithmic bytes of each kernel of one pi_ffn_layer call (weights, biases and the vectors each
-    kernel must read or write; not the FC2 partials, which are an implementation choice)."""
+STAGES = ["hidden", "output+fc1", "fc2+lists", "sum+merge"]
+
+
+def kernel_bytes(spec, B, K, K_c, rows_p2, rows_w2):
+    """Algorithmic bytes of each kernel of one batch-1 pi_ffn_layer call: the weights
+    and biases each kernel must read and the vectors it must read or write (not the
+    FC2 partial sums, which are an implementation choice)."""
     cfg = spec.cfg
     d, N, H = cfg.d, cfg.N, spec.H
     wp, w, wb = wbytes(cfg.pdtype), wbytes(cfg.wdtype), bias_bytes(cfg.bdtype)
     mats1 = 2 if cfg.gated else 1
-    cold = len(spec.T_c) > 0
-    words = 2 * ((N + 63) // 64)
-    nblk = (N + 63) // 64
+    groups = (N + 63) // 64
     return {
         "hidden": H * d * wp + B * d * 4 + B * H * 4,
-        "output+mask": N * H * wp + N * wb + B * H * 4 + B * N * 4 + words * 4,
-        "fc1": K * (mats1 * d * w + wb) + B * d * 4 + 2 * words * 4 + nblk * 4 + (K + K_c) * 4 + B * K * 4
-               + nblk * 4,
-        "fc2": K * d * w + K * 4 + B * K * 4 + nblk * 4,
-        "reduce+merge+lists": B * d * 4 + (B * d * 4 if (cold and K_c) else 0) + 2 * (K + K_c) * 4 + nblk * 4,
+        "output+fc1": (rows_p2 * N * wp + N * wb + B * H * 4 + B * d * 4 + 3 * groups * 4
+                       + K * (mats1 * d * w + wb) + 4 * K + 8 * rows_w2 + 4 * K_c + 4 * groups),
+        "fc2+lists": rows_w2 * d * w + 8 * rows_w2 + 4 * groups + 2 * (4 * K + 4 * K_c) + B * d * 4 * 0,
+        "sum+merge": B * d * 4 + (B * d * 4 if (len(spec.T_c) and K_c) else 0),
     }
 
 
@@ -154,7 +159,8 @@ def _short_kernel(name):
 
 KERNEL_SOURCES = ["activation_sparse_amd/csrc/pi_fast.hip", "activation_sparse_amd/csrc/pi_fc2.hip",
                   "activation_sparse_amd/csrc/pi_device.h", "activation_sparse_amd/csrc/pi_internal.h"]
-TRAFFIC_PROFILE = "profiles/k_logits_b1.opt-30b.b1.hbm_traffic.txt"
+DOMINANT = "k_pred_fc1"
+TRAFFIC_PROFILE = "profiles/k_pred_fc1.opt-30b.b1.hbm_traffic.txt"
 
 
 def kernel_source_digest():
@@ -188,8 +194,8 @@ def rocprof_summary(roots, copy_mib):
     counters from `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs, found anywhere under the given
     directories.
 
-    Durations: every launch of a kernel, and for k_logits_b1 also the launches that follow another
-    k_logits_b1 (the back-to-back pi_predict_output launches the roofline is timed on).  Counters: KiB
+    Durations: every launch of a kernel, and for the dominant kernel also the launches that follow
+    another of its launches (the back-to-back isolated launches the roofline is timed on).  Counters: KiB
     per dispatch, averaged per kernel, and scaled by what the same counter reads for the plain copies of
     copy_mib MiB (the copy dispatches within 1% of the largest reading), whose true traffic is copy_mib
     MiB read and copy_mib MiB written."""
@@ -208,7 +214,7 @@ def rocprof_summary(roots, copy_mib):
                 k = _short_kernel(r["Kernel_Name"])
                 dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
                 per.setdefault(k, []).append(dur)
-                if k == "k_logits_b1" and prev == "k_logits_b1":
+                if k == DOMINANT and prev == DOMINANT:
                     iso.append(dur)
                 prev = k
             tot = sum(sum(v) for v in per.values())
@@ -218,7 +224,7 @@ def rocprof_summary(roots, copy_mib):
                 out.append(f"{k:32s} {len(v):7d} {st.mean(v):9.2f} {st.median(v):9.2f} {min(v):8.2f} "
                            f"{100 * sum(v) / tot:5.1f}%")
             if iso:
-                out.append(f"{'k_logits_b1 back-to-back':32s} {len(iso):7d} {st.mean(iso):9.2f} "
+                out.append(f"{DOMINANT + ' back-to-back':32s} {len(iso):7d} {st.mean(iso):9.2f} "
                            f"{st.median(iso):9.2f} {min(iso):8.2f}")
             out.append("")
         for path in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
@@ -293,14 +299,16 @@ def main():
         A_g = torch.empty(max(n_g, 1), dtype=torch.int32, device=dev)
         A_c = torch.empty(max(n_c, 1), dtype=torch.int32, device=dev)
         y = torch.empty((B, d), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256),
-                         dtype=torch.uint8, device=dev)
     buf = Buffers
-    # per-(step, layer) inputs, cold partials and counts
+    # one workspace per layer, so that a stage re-run alone sees its own layer's state
+    ws_bytes = max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256)
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+    # per-(step, layer) inputs, cold partials, counts and rows read
     xs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev)
     ycs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev) if n_c else None
     Ks = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
     Kcs = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    rows = torch.zeros((S, n_layers, 2), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     for t in range(S):
         rid = torch.from_numpy(synth.x_row_ids(t, B)).to(dev)
@@ -311,12 +319,13 @@ def main():
                 synth.dev_fill(ycs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_YC, L, d, 0.05,
                                row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
     torch.cuda.synchronize()
-    def layer_call(t, L, events=None):
+
+    def layer_call(t, L, events=None, stages=pi.PI_STAGE_ALL):
         spec, dl = specs[L], dls[L]
         cold = len(spec.T_c) > 0
-        pi.pi_ffn_layer(dl.layer, B, xs[t, L], 0.0, ycs[t, L] if cold else None, buf.y, buf.logits, buf.A_g,
-                        Ks[t, L:L + 1], buf.A_c if cold else None, Kcs[t, L:L + 1] if cold else None, buf.ws,
-                        events=events, _cstruct=dl.layer_c)
+        pi.pi_ffn_layer_stages(dl.layer, B, xs[t, L], 0.0, ycs[t, L] if cold else None, buf.y, None, buf.A_g,
+                               Ks[t, L:L + 1], buf.A_c if cold else None, Kcs[t, L:L + 1] if cold else None, wss[L],
+                               stages, rows_read=rows[t, L], events=events, _cstruct=dl.layer_c)
 
     def step_call(t):
         for L in range(n_layers):
@@ -362,21 +371,29 @@ def main():
     ms_per_step = elapsed_s * 1e3 / args.steps
     tokens_s = B * args.steps / elapsed_s
 
-    # algorithmic bytes of the timed steps from the measured counts
+    # algorithmic bytes of the timed steps from the measured counts and rows read
     Kh = Ks.cpu().numpy()
     Kch = Kcs.cpu().numpy()
+    Rh = rows.cpu().numpy()
     tot_pred = tot_ffn = tot_small = 0.0
     for t in range(args.warmup, S):
         for L in range(n_layers):
-            p, f, s = layer_bytes(specs[L], B, int(Kh[t, L]), int(Kch[t, L]))
-            tot_pred += p; tot_ffn += f; tot_small += s
+            p, f, sm = layer_bytes(specs[L], B, int(Kh[t, L]), int(Kch[t, L]), int(Rh[t, L, 0]), int(Rh[t, L, 1]))
+            tot_pred += p; tot_ffn += f; tot_small += sm
     step_bytes = (tot_pred + tot_ffn + tot_small) / args.steps
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # bytes a dense predictor (every P2 row) and an FC2 over every listed neuron would read
+    dense_bytes = 0.0
+    for t in range(args.warmup, S):
+        for L in range(n_layers):
+            p, f, sm = layer_bytes(specs[L], B, int(Kh[t, L]), int(Kch[t, L]), specs[L].H, int(Kh[t, L]))
+            dense_bytes += p + f + sm
+    dense_bytes /= args.steps
 
-    # per-kernel durations: pi_ffn_layer records 5 events between its kernels, over a few eager steps
-    names = ["hidden", "output+mask", "fc1", "fc2", "reduce+merge+lists"]
-    kern_ms = {k: [] for k in names}
-    kern_bytes = {k: [] for k in names}
+    # per-stage durations: pi_ffn_layer records events between its kernels, over a few eager steps
+    # (each layer call synchronised, so every interval holds one kernel and its launch)
+    kern_ms = {k: [] for k in STAGES}
+    kern_bytes = {k: [] for k in STAGES}
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
     handles = pi.event_handles(evs)
     n_inst = min(4, S)
@@ -384,46 +401,49 @@ def main():
         for L in range(n_layers):
             layer_call(t, L, events=handles)
             torch.cuda.synchronize()
-            for i, k in enumerate(names):
-                kern_ms[k].append(evs[i].elapsed_time(evs[i + 1]))
-            kb = kernel_bytes(specs[L], B, int(Ks[t, L].item()), int(Kcs[t, L].item()))
-            for k in names:
+            iv = [evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[3]), evs[3].elapsed_time(evs[4]),
+                  evs[4].elapsed_time(evs[5])]
+            for k, v in zip(STAGES, iv):
+                kern_ms[k].append(v)
+            r = rows[t, L].cpu().numpy()
+            kb = kernel_bytes(specs[L], B, int(Ks[t, L].item()), int(Kcs[t, L].item()), int(r[0]), int(r[1]))
+            for k in STAGES:
                 kern_bytes[k].append(kb[k])
     mean_ms = {k: float(np.mean(v)) for k, v in kern_ms.items()}
     mean_bytes = {k: float(np.mean(v)) for k, v in kern_bytes.items()}
-    achieved = {k: (mean_bytes[k] / (mean_ms[k] * 1e-3) / 1e9 if mean_ms[k] > 0 else 0.0) for k in names}
-    dom = max(names, key=lambda k: mean_ms[k])
-    # The dominant kernel timed on its own: its ABI call (pi_predict_output) launched once per layer
-    # back to back between two events on the launch stream, so that no event sits between kernels.
-    h_buf = torch.empty((B, maxH), dtype=torch.float32, device=dev).uniform_(0.0, 1.0)
-    mask_buf = torch.empty(2 * ((N + 63) // 64), dtype=torch.int32, device=dev)
-    def out_layer_pass():
+    achieved = {k: (mean_bytes[k] / (mean_ms[k] * 1e-3) / 1e9 if mean_ms[k] > 0 else 0.0) for k in STAGES}
+    # The dominant kernel (predictor output layer + activation decision + FC1, one launch per layer)
+    # timed on its own: re-run alone, back to back over the layers between two events on the launch
+    # stream, on the state the last step left in each layer's workspace (so each launch repeats that
+    # step's work exactly and its bytes are that step's).
+    dom = "output+fc1"
+    last = S - 1
+    dom_bytes = float(np.mean([kernel_bytes(specs[L], B, int(Kh[last, L]), int(Kch[last, L]), int(Rh[last, L, 0]),
+                                            int(Rh[last, L, 1]))[dom] for L in range(n_layers)]))
+
+    def dom_pass():
         for L in range(n_layers):
-            dl = dls[L]
-            pi.pi_predict_output(B, specs[L].H, N, h_buf, dl.P2, dl.c2, 0.0, buf.logits, mask_buf)
-    out_layer_pass()
+            layer_call(last, L, stages=pi.PI_STAGE_OUTPUT)
+    dom_pass()
     torch.cuda.synchronize()
     reps = 5
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     d0.record()
     for _ in range(reps):
-        out_layer_pass()
+        dom_pass()
     d1.record()
     torch.cuda.synchronize()
-    dom = "output+mask"
-    mean_ms[dom + " (isolated)"] = d0.elapsed_time(d1) / (reps * n_layers)
-    dom_bytes = float(np.mean([kernel_bytes(specs[L], B, 0, 0)[dom] for L in range(n_layers)]))
-    achieved[dom + " (isolated)"] = dom_bytes / (mean_ms[dom + " (isolated)"] * 1e-3) / 1e9
-    mean_bytes[dom + " (isolated)"] = dom_bytes
-    dom = dom + " (isolated)"
-    kernel_symbol = {"hidden": "k_hidden_b1", "output+mask": "k_logits_b1", "fc1": "k_fc1_blk",
-                     "fc2": "k_fc2_seg", "reduce+merge+lists": "k_reduce_lists"}
-    traffic = committed_traffic("k_logits_b1") if (cfg.key == "opt-30b" and B == 1) else None
-    roofline = {"bound": "hbm", "achieved": round(achieved[dom], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved[dom] / HBM_PEAK_GBS, 4),
+    iso = dom + " (isolated)"
+    mean_ms[iso] = d0.elapsed_time(d1) / (reps * n_layers)
+    mean_bytes[iso] = dom_bytes
+    achieved[iso] = dom_bytes / (mean_ms[iso] * 1e-3) / 1e9
+    traffic = committed_traffic(DOMINANT) if (cfg.key == "opt-30b" and B == 1) else None
+    roofline = {"bound": "hbm", "achieved": round(achieved[iso], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved[iso] / HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None,
-                "kernel": kernel_symbol["output+mask"] + " (predictor output layer, pi_predict_output)",
-                "bytes_per_launch": round(mean_bytes[dom]), "avg_launch_us": round(mean_ms[dom] * 1e3, 2)}
+                "kernel": DOMINANT + " (predictor output layer over the active hidden units + activation decision "
+                          "+ FC1; pi_ffn_layer_stages PI_STAGE_OUTPUT)",
+                "bytes_per_launch": round(mean_bytes[iso]), "avg_launch_us": round(mean_ms[iso] * 1e3, 2)}
 
     log(f"timed: {ms_per_step:.4f} ms/step, {tokens_s:.1f} tokens/s")
     cpu = None
@@ -454,7 +474,10 @@ def main():
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
                    "bytes_split": {"predictor": round(tot_pred / args.steps), "ffn": round(tot_ffn / args.steps),
                                    "small": round(tot_small / args.steps)},
+                   "step_bytes_if_dense_p2_and_full_fc2": round(dense_bytes),
                    "mean_K": float(Kh[args.warmup:].mean()), "mean_K_cold": float(Kch[args.warmup:].mean()),
+                   "mean_p2_rows_read": float(Rh[args.warmup:, :, 0].mean()),
+                   "mean_fc2_rows_read": float(Rh[args.warmup:, :, 1].mean()),
                    "kernel_us": {k: round(v * 1e3, 2) for k, v in mean_ms.items()},
                    "kernel_gbps": {k: round(v, 1) for k, v in achieved.items()},
                    "graph": use_graph, "setup_s": round(setup_s, 1), "wall_s": round(wall, 4),

@@ -53,13 +53,14 @@
 extern "C" {
 #endif
 
-#define PI_ABI_VERSION 1
+#define PI_ABI_VERSION 2
 #define PI_MAX_BATCH 32
 
 enum pi_dtype { PI_F32 = 0, PI_F16 = 1, PI_I4G128 = 2 };
 enum pi_ffn_kind { PI_RELU = 0, PI_GATED_RELU = 1 };
 enum pi_status { PI_OK = 0, PI_EINVAL = 1, PI_EWORKSPACE = 2, PI_EUNSUPPORTED = 3, PI_EHIP = 4 };
-enum pi_op { PI_OP_PREDICT = 0, PI_OP_COMPACT = 1, PI_OP_SPARSE_FFN = 2, PI_OP_MERGE = 3, PI_OP_FFN_LAYER = 4 };
+enum pi_op { PI_OP_PREDICT = 0, PI_OP_COMPACT = 1, PI_OP_SPARSE_FFN = 2, PI_OP_MERGE = 3, PI_OP_FFN_LAYER = 4,
+             PI_OP_PREDICT_OUTPUT = 5 };
 
 /* A weight matrix on the device.  `scales` is used by PI_I4G128 only. */
 typedef struct pi_matrix {
@@ -76,27 +77,33 @@ typedef struct pi_vector {
 
 /* Predictor (step 1).  For each batch row b < B:
  *   h[b,m]      = max(0, sum_k P1[m,k] * x[b,k] + c1[m])      m < H
- *   logits[b,i] = sum_m P2[i,m] * h[b,m] + c2[i]               i < N
- * x      [B x d] fp32.   P1 [H x d], P2 [N x H] (PI_F32/PI_F16/PI_I4G128).
+ *   logits[b,i] = sum_m P2[m,i] * h[b,m] + c2[i]               i < N
+ * x      [B x d] fp32.   P1 [H x d] (row m = hidden unit m's input weights).
+ * P2 [H x N] HIDDEN-MAJOR: row m holds hidden unit m's weights to the N
+ * outputs, the same neuron-major convention as W2 below, so that a hidden
+ * unit whose ReLU output is zero is one row that need not be read.  Both
+ * PI_F32/PI_F16/PI_I4G128 (int4 groups run along the row, i.e. along N).
  * logits [B x N] fp32, written.   h lives in the workspace.
  * ws: at least pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0) bytes.
  * Errors: PI_EINVAL for a NULL required pointer, B outside 1..PI_MAX_BATCH,
- * a non-positive size, a column count the dtype forbids or an unknown dtype;
- * PI_EWORKSPACE for a short workspace. */
+ * a non-positive size, a column count the dtype forbids (d for P1, N for P2)
+ * or an unknown dtype; PI_EWORKSPACE for a short workspace. */
 int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const float* x,
                pi_matrix P1, pi_vector c1, pi_matrix P2, pi_vector c2,
                float* logits, void* ws, size_t ws_bytes);
 
 /* The predictor's output layer alone, with the activation decision:
- *   logits[b,i] = sum_m P2[i,m] * h[b,m] + c2[i]                i < N
+ *   logits[b,i] = sum_m P2[m,i] * h[b,m] + c2[i]                i < N
  *   mask bit i  = (logits[b,i] > tau for some b < B)
- * h [B x H] fp32 (the hidden layer, e.g. from a previous pi_predict).
- * logits [B x N] fp32 (may be NULL when B == 1: not stored).  mask
- * (optional, NULL = not stored): 2*ceil(N/64) uint32 words, bit i%32 of
- * word i/32; bits of ids >= N are zero.  Uses no workspace.
+ * h [B x H] fp32 (the hidden layer, e.g. from a previous pi_predict); P2
+ * hidden-major as for pi_predict.  logits [B x N] fp32 (may be NULL when
+ * B == 1 and H <= 4096: not stored).  mask (optional, NULL = not stored):
+ * 2*ceil(N/64) uint32 words, bit i%32 of word i/32; bits of ids >= N are
+ * zero.  ws: pi_workspace_bytes(PI_OP_PREDICT_OUTPUT, B, 0, H, N, 0) bytes
+ * (zero at batch 1 with H <= 4096; ws may then be NULL).
  * Errors: as pi_predict. */
 int pi_predict_output(void* stream, int32_t B, int32_t H, int32_t N, const float* h, pi_matrix P2, pi_vector c2,
-                      float tau, float* logits, uint32_t* mask);
+                      float tau, float* logits, uint32_t* mask, void* ws, size_t ws_bytes);
 
 /* Activation decision and compaction (step 2).
  * Neuron i is active when logits[b,i] > tau (fp32 compare) for SOME b < B
@@ -163,7 +170,7 @@ int pi_table_prepare(int32_t N, const int32_t* T_g, int32_t n_g, void* table, si
 
 /* One FFN layer, all four steps: predictor, activation decision and
  * compaction, neuron-aware FFN over the GPU-resident neurons, merge.
- * Weights as for the separate calls; `table` is a device copy of the
+ * Weights as for the separate calls (P2 hidden-major); `table` is a device copy of the
  * prepared table of the layer's T_g (W1, b1, Wup, W2 in that T_g's slot
  * order).  With `cold` non-zero the neurons outside T_g are CPU-resident and
  * their active ascending slots in the CPU table are listed in A_c / K_c. */
@@ -191,13 +198,43 @@ typedef struct pi_layer {
  * A_c [N - n_g] and K_c the CPU list when cold != 0 (else they may be NULL).
  * ws: pi_workspace_bytes(PI_OP_FFN_LAYER, B, d, H, N, n_g) bytes.
  * events: NULL, or 6 hipEvent_t (any may be NULL) recorded on `stream`
- * before the first kernel and after the predictor hidden layer, the output
- * layer with the activation decision, FC1 with the list building, the FC2
- * partial sums and the final ordered sum with the merge (per-kernel timing).
+ * before the first kernel and after each stage: the predictor hidden layer,
+ * the output layer with the activation decision, FC1, FC2, and the final
+ * ordered sum with the merge (per-stage timing).  At batch 1 the output
+ * layer, the decision and FC1 run as one kernel per tile of neuron ids
+ * (events 2 and 3 are then recorded together) and FC2 also writes the lists.
  * Errors: as the separate calls. */
 int pi_ffn_layer(void* stream, const pi_layer* layer, int32_t B, const float* x, float tau,
                  const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
                  int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, void* const* events);
+
+/* Stages of pi_ffn_layer, as bits. */
+enum pi_stage {
+  PI_STAGE_HIDDEN = 1, /* predictor hidden layer -> h in the workspace */
+  PI_STAGE_OUTPUT = 2, /* output layer + activation decision (+ lists / FC1 segments) */
+  PI_STAGE_FC1 = 4,    /* FC1 over the active GPU-resident neurons */
+  PI_STAGE_FC2 = 8,    /* FC2 partial sums (+ lists at batch 1) */
+  PI_STAGE_SUM = 16,   /* ordered sum of the partials + merge -> y */
+  PI_STAGE_ALL = 31
+};
+
+/* pi_ffn_layer restricted to the stages in `stages` (a non-zero subset of
+ * PI_STAGE_ALL), for timing and profiling one kernel in isolation, with an
+ * optional report of the weight rows read.  A stage enqueued without the
+ * stages before it reads what an earlier call with the same layer, inputs and
+ * workspace left in the workspace; with PI_STAGE_ALL and rows_read == NULL it
+ * is pi_ffn_layer.  At batch 1 PI_STAGE_OUTPUT and PI_STAGE_FC1 name the same
+ * kernel.
+ * rows_read (optional device int32[2], written when the whole layer runs):
+ * [0] the rows of P2 read (at batch 1 only the hidden units with h > 0;
+ * else H), [1] the rows of W2 read (at batch 1 only the listed neurons whose
+ * FC1 output is non-zero, the only ones that add to y; else K).
+ * Errors: as pi_ffn_layer, plus PI_EINVAL for an empty or unknown stage
+ * set. */
+int pi_ffn_layer_stages(void* stream, const pi_layer* layer, int32_t B, const float* x, float tau,
+                        const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
+                        int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, void* const* events,
+                        uint32_t stages, int32_t* rows_read);
 
 /* Workspace bytes an entry point needs for these sizes (0 when none).
  * Arguments an op does not use are ignored. */

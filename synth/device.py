@@ -35,6 +35,19 @@ def fill_matrix(m, dtype, seed, tag, layer, cols, sigma, row_ids_dev=None, nrows
                    nrows=n, stream=torch.cuda.current_stream().cuda_stream)
 
 
+def dev_matrix_hidden_major(N, H, dtype, seed, tag, layer, sigma, device):
+    """The [N x H] generated matrix stored transposed, [H x N] (fp32 / fp16 bits unchanged)."""
+    torch = _torch()
+    if dtype == synth.I4G128:
+        raise NotImplementedError("synthetic int4 output-layer weights are not generated hidden-major")
+    tmp = dev_matrix(N, H, dtype, device)
+    fill_matrix(tmp, dtype, seed, tag, layer, H, sigma)
+    out = Matrix(tmp.data.t().contiguous(), tmp.dtype)
+    del tmp
+    torch.cuda.current_stream().synchronize()
+    return out
+
+
 def dev_vector(stored: np.ndarray, dtype: int, device):
     torch = _torch()
     if dtype == synth.F32:
@@ -56,8 +69,9 @@ class DeviceLayer:
         self.T_c = torch.from_numpy(spec.T_c).to(device) if len(spec.T_c) else None
         self.P1 = dev_matrix(H, d, cfg.pdtype, device)
         fill_matrix(self.P1, cfg.pdtype, cfg.seed, synth.TAG_P1, L, d, sig[synth.TAG_P1])
-        self.P2 = dev_matrix(N, H, cfg.pdtype, device)
-        fill_matrix(self.P2, cfg.pdtype, cfg.seed, synth.TAG_P2, L, H, sig[synth.TAG_P2])
+        # the output layer's weights P2[i, m] (neuron i, hidden unit m) are generated
+        # row by row per neuron and stored hidden-major, [H, N]
+        self.P2 = dev_matrix_hidden_major(N, H, cfg.pdtype, cfg.seed, synth.TAG_P2, L, sig[synth.TAG_P2], device)
         self.c1 = None
         self.c2 = dev_vector(spec.c2, cfg.bdtype, device)
         self.W1 = dev_matrix(max(n_g, 1), d, cfg.wdtype, device)

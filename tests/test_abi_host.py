@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     L = pi.load()
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert L.pi_abi_version() == 1
+    assert L.pi_abi_version() == pi.PI_ABI_VERSION == 2
 
 
 def test_status_strings():
@@ -104,10 +104,39 @@ def test_sparse_ffn_rejects_bad_arguments():
 
 def test_predict_output_rejects_bad_arguments():
     f = pi.pi_predict_output
-    assert status(f, 0, 64, 100, FAKE, mat(), None, 0.0, FAKE, FAKE, 0) == pi.PI_EINVAL
-    assert status(f, 1, 60, 100, FAKE, mat(), None, 0.0, FAKE, FAKE, 0) == pi.PI_EINVAL    # H not a multiple of 8
-    assert status(f, 2, 64, 100, FAKE, mat(), None, 0.0, None, FAKE, 0) == pi.PI_EINVAL    # logits needed for B > 1
-    assert status(f, 1, 64, 100, FAKE, mat(), None, 0.0, None, None, 0) == pi.PI_EINVAL   # nothing to write
+    # (B, H, N, h, P2 [H x N], c2, tau, logits, mask, ws, ws_bytes, stream)
+    assert status(f, 0, 64, 104, FAKE, mat(), None, 0.0, FAKE, FAKE, None, 0, 0) == pi.PI_EINVAL
+    assert status(f, 1, 64, 100, FAKE, mat(), None, 0.0, FAKE, FAKE, None, 0, 0) == pi.PI_EINVAL  # N not /8 (P2 rows)
+    assert status(f, 2, 64, 104, FAKE, mat(), None, 0.0, None, FAKE, FAKE, 1 << 30, 0) == pi.PI_EINVAL  # logits, B > 1
+    assert status(f, 1, 64, 104, FAKE, mat(), None, 0.0, None, None, None, 0, 0) == pi.PI_EINVAL  # nothing to write
+    # batch > 1 sums partials in the workspace
+    need = pi.pi_workspace_bytes(pi.PI_OP_PREDICT_OUTPUT, 2, 0, 64, 104)
+    assert need >= 2 * 104 * 4
+    assert pi.pi_workspace_bytes(pi.PI_OP_PREDICT_OUTPUT, 1, 0, 64, 104) == 0
+    assert status(f, 2, 64, 104, FAKE, mat(), None, 0.0, FAKE, None, None, 0, 0) == pi.PI_EWORKSPACE
+    assert status(f, 2, 64, 104, FAKE, mat(), None, 0.0, FAKE, None, FAKE, need - 1, 0) == pi.PI_EWORKSPACE
+
+
+def _layer(d=256, N=1024, H=64, n_g=1024):
+    return pi.Layer(d, N, H, n_g, pi.PI_RELU, False, mat(), None, mat(), None, FAKE, mat(), None, None, mat(), None)
+
+
+def test_ffn_layer_stages_rejects_bad_stage_sets_and_shapes():
+    L = _layer()
+    ws = 1 << 30
+
+    def call(stages, layer=L, B=1):
+        return status(pi.pi_ffn_layer_stages, layer, B, FAKE, 0.0, None, FAKE, None, FAKE, FAKE, None, None, FAKE,
+                      stages, None, ws, None, 0)
+
+    assert call(0) == pi.PI_EINVAL
+    assert call(pi.PI_STAGE_ALL + 1) == pi.PI_EINVAL
+    assert call(64) == pi.PI_EINVAL
+    assert call(pi.PI_STAGE_ALL, layer=_layer(N=1020)) == pi.PI_EINVAL     # P2 [H x N] rows need N % 8 == 0
+    assert call(pi.PI_STAGE_ALL, layer=_layer(n_g=2048)) == pi.PI_EINVAL   # more GPU neurons than N
+    assert call(pi.PI_STAGE_ALL, B=33) == pi.PI_EINVAL
+    assert status(pi.pi_ffn_layer_stages, L, 1, FAKE, 0.0, None, FAKE, None, FAKE, FAKE, None, None, FAKE,
+                  pi.PI_STAGE_ALL, None, 64, None, 0) == pi.PI_EWORKSPACE
 
 
 def test_table_prepare_validates_and_builds_bitmap_and_prefix():

@@ -160,7 +160,9 @@ def test_predict_output_logits_and_mask(cfg, B):
     h_dev = torch.from_numpy(h).cuda()
     logits = torch.empty((B, N), dtype=torch.float32, device="cuda")
     mask = torch.empty(2 * ((N + 63) // 64), dtype=torch.int32, device="cuda")
-    pi.pi_predict_output(B, H, N, h_dev, dl.P2, dl.c2, 0.0, logits, mask)
+    ws = torch.empty(max(pi.pi_workspace_bytes(pi.PI_OP_PREDICT_OUTPUT, B, 0, H, N), 256), dtype=torch.uint8,
+                     device="cuda")
+    pi.pi_predict_output(B, H, N, h_dev, dl.P2, dl.c2, 0.0, logits, mask, ws)
     torch.cuda.synchronize()
     P2 = ph.host_mat(cfg.pdtype, cfg.seed, synth.TAG_P2, 0, H, spec.sigmas()[synth.TAG_P2], nrows=N)
     eye = orc.Mat(np.eye(H, dtype=np.float32), orc.F32, H)
