@@ -8,8 +8,9 @@
 // The predictor's output layer with its weights stored hidden-major (row m =
 // hidden unit m's weights to the N outputs): only the rows of hidden units
 // whose ReLU output is positive are read, since a zero hidden unit adds
-// nothing to any logit.  One block owns a tile of 64 or 128 neuron ids: it
-// compacts the active hidden units in LDS, streams their row slices, and
+// nothing to any logit.  One block owns a tile of 64 or 128 neuron ids: each
+// lane reads h for its rows and then only the row slices of positive hidden
+// units (the others are skipped through the buffer range check), and the block
 // decides the tile's activations.  In the fused layer the same block then
 // runs FC1 for the tile's active GPU-resident neurons (x staged in LDS) and
 // writes the tile's list segments, so no block waits for another.
@@ -167,14 +168,10 @@ struct TileGeom {
   static constexpr int NT = W * kWave;
   static constexpr int NG = T / 64;                  // 64-id groups per tile
   static constexpr int U = 16;                       // row loads in flight per lane (T=128: 1024 rows per pass)
-  static constexpr int CPW = kMaxHiddenB1 / 64 / W;  // hidden-unit chunks of 64 per wave
 };
 
 __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
-// LDS of k_pred_fc1 beyond its static arrays: the compacted active hidden units
-// (ids and values), then x in E/4 planes of float4 when FC1 runs.
-__host__ __device__ constexpr size_t pf_hidden_bytes(int H) { return 2 * align16((size_t)4 * H); }
 
 // Output layer (+ FC1) of one tile of T neuron ids [i0, i0 + T):
 //   z_i = c2_i + sum over hidden units m with h_m > 0 of h_m * P2[m, i]
@@ -189,7 +186,7 @@ __host__ __device__ constexpr size_t pf_hidden_bytes(int H) { return 2 * align16
 template <int PDT, int DT, int NV, bool GATED, int BDT, int T, bool FC1>
 __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   using G = TileGeom<T>;
-  constexpr int W = G::W, NT = G::NT, NG = G::NG, U = G::U, CPW = G::CPW;
+  constexpr int W = G::W, NT = G::NT, NG = G::NG, U = G::U;
   constexpr int EP = Fmt<PDT>::E;      // output-layer weights per 16-byte vector
   constexpr int LPR = T / EP;          // lanes that cover one row slice of the tile
   constexpr int RPL = kWave / LPR;     // row slices per wave-wide load
@@ -197,7 +194,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   constexpr int P = E / 4;             // x planes
   constexpr int XQ = (NV * kWave * P + NT - 1) / NT;   // x float4 per thread
   extern __shared__ __attribute__((aligned(16))) char pf_smem[];
-  __shared__ int s_cnt[kMaxHiddenB1 / 64 + 1];
+  __shared__ int s_cnt[W];
   __shared__ float red[W][T];
   __shared__ uint64_t s_M[NG];
   __shared__ float s_a[T];
@@ -207,9 +204,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   const int H = a.H, N = a.N;
   const int ngroups = (N + 63) / 64;
   const int64_t i0 = (int64_t)blockIdx.x * T;
-  int* s_m = reinterpret_cast<int*>(pf_smem);
-  float* s_h = reinterpret_cast<float*>(pf_smem + align16((size_t)4 * H));
-  float4v* xs = reinterpret_cast<float4v*>(pf_smem + pf_hidden_bytes(H));
+  float4v* xs = reinterpret_cast<float4v*>(pf_smem);
 
   // ---- issue: table words, bias, x, h
   uint64_t Gb[NG];
@@ -236,14 +231,17 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
       xq[r] = x4[q < nq ? q : 0];
     }
   }
-  const int nch = (H + 63) / 64;
-  float hv[CPW];
+  // lane (sub, cl) reads slice vector cl of rows m = (i*W + wave)*RPL + sub of each
+  // pass of RP rows, and first its h[m]: rows with h[m] <= 0 get an offset past
+  // the buffer, which reads zeros without a memory request (no compaction, no
+  // barrier before the weight loads)
+  constexpr int RP = W * RPL * U;
+  const int sub = lane / LPR, cl = lane % LPR;
+  const rsrc_t rH = make_rsrc(a.h, (uint32_t)H * 4u);
+  float hv[U];
 #pragma unroll
-  for (int q = 0; q < CPW; ++q) {
-    const int c = q * W + wave;
-    const int m = c * 64 + lane;
-    hv[q] = (c < nch && m < H) ? a.h[m] : 0.f;
-  }
+  for (int i = 0; i < U; ++i)
+    hv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rH, ((i * W + wave) * RPL + sub) * 4, 0, 0));
   if constexpr (FC1) {
     // x in planes: plane p, index v holds x[E*v + 4p .. +3]
     const int nq = a.d / 4;
@@ -254,76 +252,46 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     }
   }
 
-  // ---- compact the active hidden units (h > 0) in id order
-#pragma unroll
-  for (int q = 0; q < CPW; ++q) {
-    const int c = q * W + wave;
-    const uint64_t b = __ballot(hv[q] > 0.f);
-    if (c < nch && lane == 0) s_cnt[c] = __popcll(b);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int v = lane < nch ? s_cnt[lane] : 0;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += t;
-    }
-    if (lane < nch) s_cnt[lane] = incl - v;
-    if (lane == kWave - 1) s_cnt[nch] = incl;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < CPW; ++q) {
-    const int c = q * W + wave;
-    const bool f = hv[q] > 0.f;
-    const uint64_t b = __ballot(f);
-    if (c < nch && f) {
-      const int pos = s_cnt[c] + __popcll(b & ((1ull << lane) - 1ull));
-      s_m[pos] = c * 64 + lane;
-      s_h[pos] = hv[q];
-    }
-  }
-  __syncthreads();
-  const int C = s_cnt[nch];
-  if (a.rows_read && blockIdx.x == 0 && tid == 0) *a.rows_read = C;
-
-  // ---- output layer over the active rows: lane (sub, cl) reads slice vector cl of row sub
+  // ---- output layer over the rows of positive hidden units
   {
-    const int sub = lane / LPR, cl = lane % LPR;
     const int64_t prb = row_bytes(PDT, N);
     const int pvec = (int)(prb / 16);
     int colv = blockIdx.x * LPR + cl;
     colv = colv < pvec ? colv : pvec - 1;          // past the row end: discarded ids
     const int pgroups = N / 128;
-    // the whole matrix as one buffer (the host keeps H * row bytes below 2^31):
-    // rows past the active count read zeros without a memory request
+    // the whole matrix as one buffer (the host keeps H * row bytes below 2^31)
     const uint32_t pbytes = (uint32_t)(H * prb);
     const rsrc_t rP = make_rsrc(a.P2, pbytes);
     const rsrc_t rS = make_rsrc(PDT == 2 ? (const void*)a.P2s : a.P2, PDT == 2 ? (uint32_t)H * pgroups * 2u : 0u);
     float acc[EP];
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[e] = 0.f;
-    for (int j0 = 0; j0 < C; j0 += W * RPL * U) {
-      uint4 w[U];
-      float hs[U], sc[U];
+    int nact = 0;                                  // this lane's rows with h > 0 (counted where cl == 0)
+    for (int m0 = 0; m0 < H; m0 += RP) {
+      if (m0 > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + (u * W + wave) * RPL + sub;
-        const bool ok = j < C;
-        const int m = ok ? s_m[j] : 0;
-        hs[u] = ok ? s_h[j] : 0.f;
-        w[u] = bload16(rP, ok ? (uint32_t)m * (uint32_t)prb + (uint32_t)colv * 16u : pbytes);
-        if constexpr (PDT == 2) sc[u] = h2f(bload2(rS, ok ? (uint32_t)(m * pgroups + colv / 4) * 2u : 0xFFFFFFF0u));
-        else sc[u] = 1.f;
+        for (int i = 0; i < U; ++i)
+          hv[i] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rH, (m0 + (i * W + wave) * RPL + sub) * 4, 0, 0));
+      }
+      uint4 w[U];
+      float sc[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int m = m0 + (i * W + wave) * RPL + sub;
+        const bool ok = hv[i] > 0.f;               // rows past H read h = 0
+        nact += ok ? 1 : 0;
+        w[i] = bload16(rP, ok ? (uint32_t)m * (uint32_t)prb + (uint32_t)colv * 16u : pbytes);
+        if constexpr (PDT == 2) sc[i] = h2f(bload2(rS, ok ? (uint32_t)(m * pgroups + colv / 4) * 2u : 0xFFFFFFF0u));
+        else sc[i] = 1.f;
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int i = 0; i < U; ++i) {
         float wf[EP];
-        widen<PDT>(w[u], PDT == 2 ? sc[u] : 1.f, wf);
+        widen<PDT>(w[i], PDT == 2 ? sc[i] : 1.f, wf);
+        const float hs = hv[i] > 0.f ? hv[i] : 0.f;
 #pragma unroll
-        for (int e = 0; e < EP; ++e) acc[e] = fmaf(wf[e], hs[u], acc[e]);
+        for (int e = 0; e < EP; ++e) acc[e] = fmaf(wf[e], hs, acc[e]);
       }
     }
     // the RPL row groups of the wave hold partial sums of the same ids: butterfly
@@ -335,8 +303,19 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     if (sub == 0)
 #pragma unroll
       for (int e = 0; e < EP; ++e) red[wave][cl * EP + e] = acc[e];
+    if (a.rows_read && blockIdx.x == 0) {
+      int c = cl == 0 ? nact : 0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
+      if (lane == 0) s_cnt[wave] = c;
+    }
   }
   __syncthreads();
+  if (a.rows_read && blockIdx.x == 0 && tid == 0) {
+    int c = 0;
+    for (int w2 = 0; w2 < W; ++w2) c += s_cnt[w2];
+    *a.rows_read = c;
+  }
   if (tid < T) {                      // waves 0 .. NG-1, one per 64-id group
     float z = red[0][tid];
 #pragma unroll
@@ -521,17 +500,15 @@ hipError_t fc1_dt(const B1Gemv& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile width: 128 ids (16 waves, at most 128 VGPRs) when that still gives most
-// CUs a block and one FC1 row fits the register budget, else 64 ids (8 waves).
-int pick_tile(int N, bool gated, int dt) {
-  const int t128 = (N + 127) / 128;
-  return (!gated && dt != 2 && t128 >= 160 && t128 <= 256) ? 128 : 64;
-}
+// Tile width: 64 ids per block of 8 waves.  (128-id tiles of 16 waves measured
+// slower at the OPT-30B shape: two co-resident 64-id blocks per CU hide each
+// other's barrier waits.)
+constexpr int kTile = 64;
 
 template <int PDT, int DT, int NV, bool GATED, int BDT, int T, bool FC1>
 hipError_t pf_launch(const PredFc1Args& a, hipStream_t s) {
   const unsigned blocks = (unsigned)((a.N + T - 1) / T);
-  size_t shm = pf_hidden_bytes(a.H);
+  size_t shm = 0;                     // x in E/4 planes of float4 when FC1 runs
   if constexpr (FC1) {
     const int nvec = (int)(row_bytes(DT, a.d) / 16);
     const int npad = (nvec + kWave - 1) & ~(kWave - 1);
@@ -543,8 +520,7 @@ hipError_t pf_launch(const PredFc1Args& a, hipStream_t s) {
 
 template <int PDT, int BDT>
 hipError_t pred_out_pdt(const PredFc1Args& a, hipStream_t s) {
-  return pick_tile(a.N, false, 0) == 128 ? pf_launch<PDT, 0, 1, false, BDT, 128, false>(a, s)
-                                      : pf_launch<PDT, 0, 1, false, BDT, 64, false>(a, s);
+  return pf_launch<PDT, 0, 1, false, BDT, kTile, false>(a, s);
 }
 
 // Fused kernels exist for these (output-layer dtype, FFN dtype, bias dtype)
@@ -553,14 +529,7 @@ hipError_t pred_out_pdt(const PredFc1Args& a, hipStream_t s) {
 template <int PDT, int DT, int BDT, bool GATED>
 hipError_t pred_fc1_combo(const PredFc1Args& a, hipStream_t s) {
   const int nv = pick_nv<DT>((int)(row_bytes(DT, a.d) / 16));
-  constexpr bool kWide = !GATED && DT != 2;
-  const bool t128 = pick_tile(a.N, GATED, DT) == 128;
-#define PI_PF(NVV)                                                                             \
-  do {                                                                                          \
-    if constexpr (kWide)                                                                        \
-      if (t128) return pf_launch<PDT, DT, NVV, GATED, BDT, kWide ? 128 : 64, true>(a, s);      \
-    return pf_launch<PDT, DT, NVV, GATED, BDT, 64, true>(a, s);                                \
-  } while (0)
+#define PI_PF(NVV) return pf_launch<PDT, DT, NVV, GATED, BDT, kTile, true>(a, s)
   switch (nv) {
     case 1: case 2: case 4: PI_PF(4);
     case 8: PI_PF(8);

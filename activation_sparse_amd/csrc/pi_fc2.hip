@@ -16,7 +16,7 @@ namespace {
 constexpr int kT = 256;
 constexpr int kWpb = kT / kWave;
 constexpr int kUnroll = 8;
-constexpr int kSegUnroll = 8;
+constexpr int kSegUnroll = 16;
 
 template <int DT, int NBG>
 __global__ __launch_bounds__(kT) void k_fc2(Fc2Args a) {

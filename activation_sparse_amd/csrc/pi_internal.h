@@ -61,7 +61,7 @@ hipError_t launch_fc1_b1(const B1Gemv& g, bool gated, hipStream_t s);
 // hidden-major), with the activation decision, and in the fused layer FC1 of
 // the tile's active GPU-resident neurons (pi_fast.hip).  One block per tile of
 // 64 or 128 neuron ids; no block waits for another.
-constexpr int kMaxHiddenB1 = 4096;   // hidden units the batch-1 output layer compacts in LDS
+constexpr int kMaxHiddenB1 = 4096;   // hidden units the batch-1 output-layer kernel takes
 struct PredFc1Args {
   const void* P2;            // [H x N] hidden-major
   const uint16_t* P2s;       // int4 scales [H x N/128]
@@ -107,7 +107,7 @@ hipError_t launch_pred_fc1(const PredFc1Args& a, bool gated, hipStream_t s);
 
 // Batch-1 FC2 over the group segments, with the list assembly, and the final
 // ordered sum (pi_fc2.hip).
-constexpr int kSegChunks = 64;   // group chunks of the segment FC2 (groups <= 64 * kSegChunks)
+constexpr int kSegChunks = 32;   // group chunks of the segment FC2 (groups <= 64 * kSegChunks)
 struct Fc2SegArgs {
   const void* W2;
   const uint16_t* W2s;
