@@ -22,7 +22,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              # packed fp32 instructions stay off (the compiler would otherwise form them)
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-PI_SOURCES = ["pi_generic.hip", "pi_fast.hip", "pi_fc2.hip", "pi_abi.hip"]
+PI_SOURCES = ["pi_generic.hip", "pi_fast.hip", "pi_fc2.hip", "pi_mfma.hip", "pi_abi.hip"]
 
 
 def _run(cmd):

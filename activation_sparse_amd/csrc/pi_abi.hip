@@ -52,11 +52,40 @@ struct FfnWs {
   size_t bytes;
 };
 
+// Partial sums of the batched matrix-core GEMMs, bounded over the weight dtypes
+// (workspace sizes are asked for without them).
+bool use_mm(int32_t B) { return B >= pi::kMmMinBatch; }
+size_t mm_row_partial_bytes(int32_t B, int64_t rows, int64_t cols, bool gated) {
+  if (!use_mm(B) || rows <= 0 || cols <= 0) return 0;
+  int ks = 1;
+  for (int dt = 0; dt < 3; ++dt) {
+    const int k = pi::mm_row_ks(dt, rows, cols);
+    ks = k > ks ? k : ks;
+  }
+  return (size_t)(gated ? 2 : 1) * ks * (size_t)rows * 16 * pi::mm_nbt(B) * 4;
+}
+size_t mm_axpy_partial_bytes(int32_t B, int64_t rows, int64_t cols) {
+  if (!use_mm(B) || rows <= 0 || cols <= 0) return 0;
+  int rc = 1;
+  for (int dt = 0; dt < 2; ++dt) {
+    const int r = pi::mm_axpy_row_chunks(dt, rows, cols);
+    rc = r > rc ? r : rc;
+  }
+  return (size_t)rc * B * (size_t)cols * 4;
+}
+size_t max3(size_t a, size_t b, size_t c) { return a > b ? (a > c ? a : c) : (b > c ? b : c); }
+
+// FC1 -> a, FC2 partials (VALU row chunks or matrix-core row chunks) -> y.
+size_t ffn_partial_bytes(int32_t B, int32_t d, int32_t n_g) {
+  return max3((size_t)pi::fc2_chunks(B) * B * (size_t)d * 4, mm_row_partial_bytes(B, n_g, d, true),
+              mm_axpy_partial_bytes(B, n_g, d));
+}
+
 FfnWs ffn_ws_layout(void* ws, int32_t B, int32_t d, int32_t n_g) {
   Carver c{static_cast<char*>(ws)};
   FfnWs w{};
   w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
-  w.partials = c.take<float>((size_t)pi::fc2_chunks(B) * B * (size_t)d * 4);
+  w.partials = c.take<float>(ffn_partial_bytes(B, d, n_g));
   w.bytes = c.off;
   return w;
 }
@@ -69,7 +98,14 @@ bool out_layer_needs_partials(int32_t B, int32_t H, int32_t N) {
   return B > 1 || H > pi::kMaxHiddenB1 || (int64_t)H * N * 4 >= ((int64_t)1 << 31);
 }
 size_t out_partials_bytes(int32_t B, int32_t H, int32_t N) {
-  return out_layer_needs_partials(B, H, N) ? (size_t)pi::fc2_chunks(B) * B * (size_t)N * 4 : 0;
+  if (!out_layer_needs_partials(B, H, N)) return 0;
+  const size_t v = (size_t)pi::fc2_chunks(B) * B * (size_t)N * 4, m = mm_axpy_partial_bytes(B, H, N);
+  return v > m ? v : m;
+}
+// Predictor scratch: the output layer's partials, or the hidden layer's split-K partials.
+size_t pred_partial_bytes(int32_t B, int32_t d, int32_t H, int32_t N) {
+  const size_t o = out_partials_bytes(B, H, N), r = mm_row_partial_bytes(B, H, d, false);
+  return o > r ? o : r;
 }
 
 size_t table_words(int32_t N) { return 2 * (size_t)((N + 63) / 64); }
@@ -105,13 +141,37 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
   w.pos_a = c.take<float>(ng * 64 * 4);
   w.cnt = c.take<uint32_t>(ng * 4);
   w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
-  size_t pb = (size_t)pi::fc2_chunks(B) * B * (size_t)d * 4;
+  const size_t pb = ffn_partial_bytes(B, d, n_g);
   const size_t seg = (size_t)pi::kSegChunks * (size_t)d * 4;
-  pb = pb > seg ? pb : seg;
-  const size_t ob = out_partials_bytes(B, H, N);
-  w.partials = c.take<float>(pb > ob ? pb : ob);
+  w.partials = c.take<float>(max3(pb, seg, pred_partial_bytes(B, d, H, N)));
   w.bytes = c.off;
   return w;
+}
+
+// The predictor's hidden layer, h[b,m] = max(0, P1[m].x_b + c1[m]): batch 1 on the
+// register-x GEMV, batches of kMmMinBatch and more on the matrix cores (split-K
+// partials in `partials`), others on the LDS-x row-dot kernel.
+int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* x, const pi_matrix& P1,
+                   const pi_vector& c1, float* h, float* partials) {
+  if (B == 1 && pi::b1_supported(P1.dtype, d)) {
+    pi::B1Gemv g{};
+    g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
+    g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
+    return hip_status(pi::launch_hidden_b1(g, s));
+  }
+  if (use_mm(B) && pi::mm_rowdot_supported(P1.dtype, H, d)) {
+    pi::MmRowArgs m{};
+    m.W = P1.data; m.Ws = P1.scales; m.dt = P1.dtype; m.gated = 0; m.cols = d; m.n_rows = H; m.list = nullptr;
+    m.count_dev = nullptr; m.count_max = H; m.x = x; m.B = B; m.nbt = pi::mm_nbt(B);
+    m.ks = pi::mm_row_ks(P1.dtype, H, d); m.kc = pi::mm_row_kc(P1.dtype, d, m.ks); m.partials = partials;
+    m.bias = c1.data; m.bias_dt = c1.dtype; m.relu = 1; m.out = h; m.out_stride = H;
+    return hip_status(pi::launch_mm_rowdot(m, s));
+  }
+  pi::RowdotArgs a{};
+  a.W = P1.data; a.Ws = P1.scales; a.dt = P1.dtype; a.cols = d;
+  a.count_max = H; a.x = x; a.B = B; a.bias = c1.data; a.bias_dt = c1.dtype;
+  a.relu = 1; a.out = h; a.out_stride = H;
+  return hip_status(pi::launch_rowdot(a, s));
 }
 
 // The predictor's output layer, logits[b,i] = c2[i] + sum_m h[b,m] P2[m,i] with P2
@@ -128,13 +188,26 @@ int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const f
     a.c2 = c2.data; a.c2_dt = c2.dtype; a.tau = tau; a.logits = logits; a.mask = mask; a.rows_read = rows_read;
     return hip_status(pi::launch_pred_out_b1(a, s));
   }
-  pi::Fc2Args f{};
-  f.W2 = P2.data; f.W2s = P2.scales; f.dt = P2.dtype; f.d = N; f.n_g = H; f.list = nullptr; f.K = nullptr;
-  f.a = h; f.a_stride = H; f.a_by_row = 1; f.B = B; f.partials = partials;
-  int st = hip_status(pi::launch_fc2(f, s));
+  int st, chunks;
+  if (use_mm(B) && pi::mm_axpy_supported(P2.dtype, H, N)) {
+    pi::MmAxpyArgs m{};
+    m.W = P2.data; m.Ws = P2.scales; m.dt = P2.dtype; m.cols = N; m.n_rows = H; m.list = nullptr;
+    m.count_dev = nullptr; m.count_max = H; m.a = h; m.a_stride = H; m.a_by_row = 1; m.B = B; m.nbt = pi::mm_nbt(B);
+    m.row_chunks = pi::mm_axpy_row_chunks(P2.dtype, H, N);
+    m.rows_per_chunk = ((H + m.row_chunks - 1) / m.row_chunks + 15) / 16 * 16;
+    m.partials = partials;
+    st = hip_status(pi::launch_mm_axpy(m, s));
+    chunks = m.row_chunks;
+  } else {
+    pi::Fc2Args f{};
+    f.W2 = P2.data; f.W2s = P2.scales; f.dt = P2.dtype; f.d = N; f.n_g = H; f.list = nullptr; f.K = nullptr;
+    f.a = h; f.a_stride = H; f.a_by_row = 1; f.B = B; f.partials = partials;
+    st = hip_status(pi::launch_fc2(f, s));
+    chunks = pi::fc2_chunks(B);
+  }
   if (st != PI_OK) return st;
   pi::ReduceArgs r{};
-  r.partials = partials; r.chunks = pi::fc2_chunks(B); r.B = B; r.d = N; r.y = logits;
+  r.partials = partials; r.chunks = chunks; r.B = B; r.d = N; r.y = logits;
   r.y_c = nullptr; r.K_c = nullptr; r.b2 = c2.data; r.b2_dt = c2.dtype;
   if ((st = hip_status(pi::launch_reduce(r, s))) != PI_OK) return st;
   return mask ? hip_status(pi::launch_mask(B, N, logits, tau, mask, s)) : PI_OK;
@@ -162,7 +235,8 @@ const char* pi_status_string(int32_t status) {
 size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g) {
   if (B < 1) B = 1;
   switch (op) {
-    case PI_OP_PREDICT: return H > 0 && N > 0 ? align_up((size_t)B * (size_t)H * 4) + out_partials_bytes(B, H, N) : 0;
+    case PI_OP_PREDICT:
+      return H > 0 && N > 0 && d > 0 ? align_up((size_t)B * (size_t)H * 4) + pred_partial_bytes(B, d, H, N) : 0;
     case PI_OP_PREDICT_OUTPUT: return H > 0 && N > 0 ? out_partials_bytes(B, H, N) : 0;
     case PI_OP_SPARSE_FFN:
       return d > 0 ? ffn_ws_layout(nullptr, B, d, n_g).bytes : 0;
@@ -203,19 +277,7 @@ int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const f
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* h = static_cast<float*>(ws);
   float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * (size_t)H * 4));
-  int st;
-  if (B == 1 && pi::b1_supported(P1.dtype, d)) {
-    pi::B1Gemv g{};
-    g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
-    g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
-    st = hip_status(pi::launch_hidden_b1(g, s));
-  } else {
-    pi::RowdotArgs a{};
-    a.W = P1.data; a.Ws = P1.scales; a.dt = P1.dtype; a.cols = d;
-    a.count_max = H; a.x = x; a.B = B; a.bias = c1.data; a.bias_dt = c1.dtype;
-    a.relu = 1; a.out = h; a.out_stride = H;
-    st = hip_status(pi::launch_rowdot(a, s));
-  }
+  const int st = enqueue_hidden(s, B, d, H, x, P1, c1, h, partials);
   if (st != PI_OK) return st;
   return enqueue_output_layer(s, B, H, N, h, P2, c2, 0.f, logits, nullptr, partials);
 }
@@ -270,7 +332,16 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
   const bool gated = kind == PI_GATED_RELU;
   int st = PI_OK;
   if (stages & PI_STAGE_FC1) {
-    if (B == 1 && pi::b1_supported(W1.dtype, d)) {
+    if (use_mm(B) && pi::mm_rowdot_supported(W1.dtype, n_g, d)) {
+      pi::MmRowArgs m{};
+      m.W = W1.data; m.Ws = W1.scales; m.dt = W1.dtype; m.gated = gated;
+      if (gated) { m.Wup = Wup.data; m.Wups = Wup.scales; }
+      m.cols = d; m.n_rows = n_g; m.list = A_g; m.count_dev = K; m.count_max = n_g; m.x = x; m.B = B;
+      m.nbt = pi::mm_nbt(B); m.ks = pi::mm_row_ks(W1.dtype, n_g, d); m.kc = pi::mm_row_kc(W1.dtype, d, m.ks);
+      m.partials = partials; m.bias = b1.data; m.bias_dt = b1.dtype; m.relu = 1; m.out = a;
+      m.out_stride = n_g > 0 ? n_g : 1;
+      st = n_g > 0 ? hip_status(pi::launch_mm_rowdot(m, s)) : PI_OK;
+    } else if (B == 1 && pi::b1_supported(W1.dtype, d)) {
       pi::B1Gemv g{};
       g.W = W1.data; g.Ws = W1.scales; g.dt = W1.dtype; g.rows = n_g; g.cols = d; g.x = x;
       if (gated) { g.Wu = Wup.data; g.Wus = Wup.scales; }
@@ -288,16 +359,28 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
     if (st != PI_OK) return st;
   }
   if (ev && ev[0] && (st = hip_status(hipEventRecord(ev[0], s))) != PI_OK) return st;
+  const bool mm2 = use_mm(B) && n_g > 0 && pi::mm_axpy_supported(W2.dtype, n_g, d);
+  const int chunks2 = mm2 ? pi::mm_axpy_row_chunks(W2.dtype, n_g, d) : pi::fc2_chunks(B);
   if (stages & PI_STAGE_FC2) {
-    pi::Fc2Args f{};
-    f.W2 = W2.data; f.W2s = W2.scales; f.dt = W2.dtype; f.d = d; f.n_g = n_g;
-    f.list = A_g; f.K = K; f.a = a; f.a_stride = n_g; f.a_by_row = 0; f.B = B; f.partials = partials;
-    if ((st = hip_status(pi::launch_fc2(f, s))) != PI_OK) return st;
+    if (mm2) {
+      pi::MmAxpyArgs m{};
+      m.W = W2.data; m.Ws = W2.scales; m.dt = W2.dtype; m.cols = d; m.n_rows = n_g; m.list = A_g; m.count_dev = K;
+      m.count_max = n_g; m.a = a; m.a_stride = n_g; m.a_by_row = 0; m.B = B; m.nbt = pi::mm_nbt(B);
+      m.row_chunks = chunks2;
+      m.rows_per_chunk = ((n_g + chunks2 - 1) / chunks2 + 15) / 16 * 16;
+      m.partials = partials;
+      if ((st = hip_status(pi::launch_mm_axpy(m, s))) != PI_OK) return st;
+    } else {
+      pi::Fc2Args f{};
+      f.W2 = W2.data; f.W2s = W2.scales; f.dt = W2.dtype; f.d = d; f.n_g = n_g;
+      f.list = A_g; f.K = K; f.a = a; f.a_stride = n_g; f.a_by_row = 0; f.B = B; f.partials = partials;
+      if ((st = hip_status(pi::launch_fc2(f, s))) != PI_OK) return st;
+    }
   }
   if (ev && ev[1] && (st = hip_status(hipEventRecord(ev[1], s))) != PI_OK) return st;
   if (stages & PI_STAGE_SUM) {
     pi::ReduceArgs r{};
-    r.partials = partials; r.chunks = pi::fc2_chunks(B); r.B = B; r.d = d; r.y = y;
+    r.partials = partials; r.chunks = chunks2; r.B = B; r.d = d; r.y = y;
     r.y_c = y_c; r.K_c = K_c; r.b2 = b2.data; r.b2_dt = b2.dtype;
     st = hip_status(pi::launch_reduce(r, s));
   }
@@ -359,21 +442,8 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
 
   if ((st = record(0)) != PI_OK) return st;
   // predictor hidden layer
-  if (want(PI_STAGE_HIDDEN)) {
-    if (B == 1 && pi::b1_supported(L->P1.dtype, d)) {
-      pi::B1Gemv g{};
-      g.W = L->P1.data; g.Ws = L->P1.scales; g.dt = L->P1.dtype; g.rows = H; g.cols = d; g.x = x;
-      g.bias = L->c1.data; g.bias_dt = L->c1.dtype; g.out = w.h;
-      st = hip_status(pi::launch_hidden_b1(g, s));
-    } else {
-      pi::RowdotArgs a{};
-      a.W = L->P1.data; a.Ws = L->P1.scales; a.dt = L->P1.dtype; a.cols = d;
-      a.count_max = H; a.x = x; a.B = B; a.bias = L->c1.data; a.bias_dt = L->c1.dtype;
-      a.relu = 1; a.out = w.h; a.out_stride = H;
-      st = hip_status(pi::launch_rowdot(a, s));
-    }
-    if (st != PI_OK) return st;
-  }
+  if (want(PI_STAGE_HIDDEN) && (st = enqueue_hidden(s, B, d, H, x, L->P1, L->c1, w.h, w.partials)) != PI_OK)
+    return st;
   if ((st = record(1)) != PI_OK) return st;
 
   if (fused) {

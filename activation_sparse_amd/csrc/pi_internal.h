@@ -184,4 +184,58 @@ hipError_t launch_rows_read(int32_t* stats, int32_t rows0, const int32_t* K1, hi
 hipError_t launch_merge(int B, int d, float* y, const float* y_c, const int32_t* K_c, const void* b2,
                         int b2_dt, hipStream_t s);
 
+// Batched GEMMs on the fp32-input matrix cores (pi_mfma.hip), for B >= kMmMinBatch.
+constexpr int kMmMinBatch = 8;
+struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b, k])
+  const void* W;
+  const uint16_t* Ws;
+  const void* Wup;              // gated only
+  const uint16_t* Wups;
+  int dt;
+  int gated;
+  int64_t cols;
+  int64_t n_rows;               // rows in W (bound for listed rows)
+  const int32_t* list;          // NULL = rows 0 .. count_max
+  const int32_t* count_dev;
+  int64_t count_max;
+  const float* x;               // [B x cols]
+  int B;
+  int nbt;                      // batch tiles of 16 (mm_nbt)
+  int ks;                       // k chunks (mm_row_ks), kc columns each (mm_row_kc)
+  int64_t kc;
+  float* partials;              // [(1 + gated) x ks x count_max x 16 nbt]
+  const void* bias;             // per row id
+  int bias_dt;
+  int relu;
+  float* out;                   // [B x out_stride], column = position
+  int64_t out_stride;
+};
+struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's rows j of a[b, j] W[row(j), c]
+  const void* W;
+  const uint16_t* Ws;
+  int dt;
+  int64_t cols;
+  int64_t n_rows;
+  const int32_t* list;          // NULL = rows 0 .. count_max
+  const int32_t* count_dev;
+  int64_t count_max;
+  const float* a;               // a[b * a_stride + (a_by_row ? row : j)]
+  int64_t a_stride;
+  int a_by_row;
+  int B;
+  int nbt;
+  int64_t rows_per_chunk;       // a multiple of 16
+  int row_chunks;               // mm_axpy_row_chunks
+  float* partials;              // [row_chunks x B x cols]
+};
+int mm_nbt(int B);
+int mm_row_ks(int dt, int64_t count_max, int64_t cols);
+int64_t mm_row_kc(int dt, int64_t cols, int ks);
+int mm_axpy_col_chunks(int dt, int64_t cols);
+int mm_axpy_row_chunks(int dt, int64_t count_max, int64_t cols);
+bool mm_rowdot_supported(int dt, int64_t rows, int64_t cols);
+bool mm_axpy_supported(int dt, int64_t rows, int64_t cols);
+hipError_t launch_mm_rowdot(const MmRowArgs& a, hipStream_t s);   // the GEMM, then the finish
+hipError_t launch_mm_axpy(const MmAxpyArgs& a, hipStream_t s);
+
 }  // namespace pi

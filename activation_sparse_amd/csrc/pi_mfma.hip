@@ -1,0 +1,360 @@
+// pi_mfma.hip - the batched (B >= kMmMinBatch) GEMMs on the fp32-input matrix
+// cores (v_mfma_f32_16x16x4_f32): the weights are widened to fp32 in registers
+// and x, h and a stay fp32, so the arithmetic is the VALU path's (fp32
+// products, fp32 accumulation) with the operand reuse of a matrix tile.
+//
+// One 16x16x4 instruction sums over k = 4 lane groups g = lane / 16.  Each lane
+// loads one 16-byte weight vector (E consecutive elements along k) and feeds
+// them to E consecutive instructions: at step s the lane group g supplies
+// k = kb + E*g + s, so E instructions cover the kb .. kb + 4E block once.
+//
+//  k_mm_rowdot : out[pos, b] = sum_k W[row(pos), k] * x[b, k] over a k-chunk
+//                (predictor hidden layer: dense rows; FC1: the listed rows).
+//                Tile 16 rows x 16*NBT batch rows per wave, split-K partials.
+//  k_mm_finish : sums the split-K partials in chunk order, + bias, ReLU
+//                (x the up product for a gated FFN) -> [B x stride].
+//  k_mm_axpy   : out[b, c] = sum_j a[b, j] * W[row(j), c] over a row chunk
+//                (predictor output layer over hidden-major P2: dense rows;
+//                FC2: the listed rows).  A lane's 16-byte row vector holds
+//                columns c0 + E*n + e (n = lane % 16): column tile e of the
+//                wave's 16E columns, so one load feeds E instructions.  The
+//                block's four waves take interleaved row steps and are summed
+//                in LDS in wave order; one partial per (row chunk, b, c).
+#include "pi_device.h"
+#include "pi_internal.h"
+
+namespace pi {
+namespace {
+
+typedef float float4v_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMmWaves = 4;
+constexpr int kMmThreads = kMmWaves * kWave;
+
+__device__ __forceinline__ float4v_t mfma4(float a, float b, float4v_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// E weights of one 16-byte vector, widened (int4: times its group scale).
+template <int DT>
+__device__ __forceinline__ void widen_vec(uint4 v, float scale, float* out) {
+  widen<DT>(v, scale, out);
+}
+
+template <int DT, int NBT, bool GATED>
+__global__ __launch_bounds__(kMmThreads) void k_mm_rowdot(MmRowArgs a) {
+  constexpr int E = Fmt<DT>::E;
+  constexpr int KB = 4 * E;                 // k per block of E instructions
+  constexpr int D = DT == 2 ? 1 : 4;        // k blocks in flight
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int tile = blockIdx.x * kMmWaves + wave;
+  const int ks = blockIdx.y;
+  int64_t count = a.count_max;
+  if (a.list) {
+    const int64_t kd = *a.count_dev;
+    count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
+  }
+  if ((int64_t)tile * 16 >= count) return;
+  const int g = lane / 16, ml = lane % 16;
+  // A operand row of this lane
+  const int64_t pos = (int64_t)tile * 16 + ml;
+  const bool pin = pos < count;
+  int64_t row = pin ? (a.list ? (int64_t)a.list[pos] : pos) : -1;
+  if (row >= a.n_rows) row = -1;
+  const int64_t rb = row_bytes(DT, a.cols);
+  const int64_t groups = a.cols / 128;
+  const char* W = reinterpret_cast<const char*>(a.W);
+  const char* Wu = reinterpret_cast<const char*>(a.Wup);
+  // one buffer over the whole matrix (the host keeps it below 2^31 bytes);
+  // an absent row reads zeros
+  const uint32_t wbytes = (uint32_t)(a.n_rows * rb);
+  const rsrc_t rW = make_rsrc(W, wbytes);
+  const rsrc_t rU = make_rsrc(GATED ? Wu : W, GATED ? wbytes : 0u);
+  const rsrc_t rS = make_rsrc(DT == 2 ? (const void*)a.Ws : W, DT == 2 ? (uint32_t)(a.n_rows * groups * 2) : 0u);
+  const rsrc_t rSu = make_rsrc(DT == 2 && GATED ? (const void*)a.Wups : W, DT == 2 && GATED ? (uint32_t)(a.n_rows * groups * 2) : 0u);
+  const uint32_t roff = row >= 0 ? (uint32_t)(row * rb) : 0u;
+  const uint32_t soff = row >= 0 ? (uint32_t)(row * groups * 2) : 0u;
+  // B operand: x rows b = 16 t + lane % 16 (zeros past B)
+  const rsrc_t rX = make_rsrc(a.x, (uint32_t)(a.B * a.cols * 4));
+  uint32_t xoff[NBT];
+  bool xok[NBT];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+    const int b = 16 * t + ml;
+    xok[t] = b < a.B;
+    xoff[t] = xok[t] ? (uint32_t)(b * a.cols * 4) : 0u;
+  }
+  // every load whose predicate fails takes this offset, past every range
+  constexpr uint32_t kOut = 0xFFFFFFF0u;
+  const int64_t k0 = (int64_t)ks * a.kc, k1 = k0 + a.kc < a.cols ? k0 + a.kc : a.cols;
+  float4v_t acc[NBT], accu[NBT];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+    acc[t] = float4v_t{0.f, 0.f, 0.f, 0.f};
+    accu[t] = float4v_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int64_t kb = k0; kb < k1; kb += (int64_t)D * KB) {
+    uint4 wv[D], uv[D];
+    float sc[D], scu[D];
+    float4v xv[D][NBT][E / 4];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int64_t kk = kb + (int64_t)i * KB + (int64_t)E * g;   // this lane's first k
+      const bool kin = kb + (int64_t)i * KB < k1;                  // whole blocks: cols % KB == 0
+      const bool wok = kin && row >= 0;
+      const uint32_t eoff = (uint32_t)(row_bytes(DT, kk));
+      wv[i] = bload16(rW, wok ? roff + eoff : kOut);
+      if constexpr (GATED) uv[i] = bload16(rU, wok ? roff + eoff : kOut);
+      if constexpr (DT == 2) {
+        sc[i] = h2f(bload2(rS, wok ? soff + (uint32_t)(kk / 128) * 2u : kOut));
+        if constexpr (GATED) scu[i] = h2f(bload2(rSu, wok ? soff + (uint32_t)(kk / 128) * 2u : kOut));
+      }
+#pragma unroll
+      for (int t = 0; t < NBT; ++t)
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          const uint4 v = bload16(rX, kin && xok[t] ? xoff[t] + (uint32_t)(kk * 4 + 16 * q) : kOut);
+          xv[i][t][q] = float4v{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      float wf[E], uf[E];
+      widen_vec<DT>(wv[i], DT == 2 ? sc[i] : 1.f, wf);
+      if constexpr (GATED) widen_vec<DT>(uv[i], DT == 2 ? scu[i] : 1.f, uf);
+#pragma unroll
+      for (int s = 0; s < E; ++s) {
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) {
+          const float xs = xv[i][t][s / 4][s % 4];
+          acc[t] = mfma4(wf[s], xs, acc[t]);
+          if constexpr (GATED) accu[t] = mfma4(uf[s], xs, accu[t]);
+        }
+      }
+    }
+  }
+  // D[m = 4g + r][n = lane % 16]: row position tile*16 + 4g + r, batch 16t + lane % 16
+  const int NBP = 16 * NBT;
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t p = (int64_t)tile * 16 + 4 * g + r;
+      if (p < count) {
+        const int64_t o = ((int64_t)ks * a.count_max + p) * NBP + 16 * t + ml;
+        a.partials[o] = acc[t][r];
+        if constexpr (GATED) a.partials[(int64_t)a.ks * a.count_max * NBP + o] = accu[t][r];
+      }
+    }
+  }
+}
+
+// out[b * out_stride + pos] = finish(sum over ks of partials[ks][pos][b]) for pos < count, b < B.
+template <bool GATED>
+__global__ __launch_bounds__(256) void k_mm_finish(MmRowArgs a) {
+  const int NBP = 16 * a.nbt;
+  int64_t count = a.count_max;
+  if (a.list) {
+    const int64_t kd = *a.count_dev;
+    count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
+  }
+  const int64_t n = count * NBP;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t pos = t / NBP;
+    const int b = (int)(t % NBP);
+    if (b >= a.B) continue;
+    float z = 0.f, u = 0.f;
+    for (int ks = 0; ks < a.ks; ++ks) z += a.partials[((int64_t)ks * a.count_max + pos) * NBP + b];
+    if constexpr (GATED)
+      for (int ks = 0; ks < a.ks; ++ks)
+        u += a.partials[((int64_t)(a.ks + ks) * a.count_max + pos) * NBP + b];
+    int64_t row = a.list ? (int64_t)a.list[pos] : pos;
+    const bool ok = row >= 0 && row < a.n_rows;
+    if (a.bias && ok) z += load_bias(a.bias, a.bias_dt, row);
+    if (a.relu) z = z > 0.f ? z : 0.f;
+    if constexpr (GATED) z *= u;
+    a.out[(int64_t)b * a.out_stride + pos] = ok ? z : 0.f;
+  }
+}
+
+template <int DT, int NBT>
+__global__ __launch_bounds__(kMmThreads) void k_mm_axpy(MmAxpyArgs a) {
+  constexpr int E = Fmt<DT>::E;
+  constexpr int D = 8;                      // row steps (4 rows each) in flight per wave
+  __shared__ float red[kMmWaves][NBT * E * 4][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int g = lane / 16, nl = lane % 16;
+  const int cchunk = blockIdx.x, rchunk = blockIdx.y;
+  int64_t count = a.count_max;
+  if (a.list) {
+    const int64_t kd = *a.count_dev;
+    count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
+  }
+  const int64_t r0 = (int64_t)rchunk * a.rows_per_chunk;
+  int64_t r1 = r0 + a.rows_per_chunk;
+  r1 = r1 < count ? r1 : count;
+  const int64_t rb = row_bytes(DT, a.cols);
+  const int64_t groups = a.cols / 128;
+  const int nvec = (int)(rb / 16);
+  const int v = cchunk * 16 + nl;           // this lane's 16-byte vector of each row
+  const bool vin = v < nvec;
+  const uint32_t wbytes = (uint32_t)(a.n_rows * rb);
+  const rsrc_t rW = make_rsrc(a.W, wbytes);
+  const rsrc_t rS = make_rsrc(DT == 2 ? (const void*)a.Ws : a.W, DT == 2 ? (uint32_t)(a.n_rows * groups * 2) : 0u);
+  const rsrc_t rA = make_rsrc(a.a, (uint32_t)(a.B * a.a_stride * 4));
+  float4v_t acc[NBT][E];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[t][e] = float4v_t{0.f, 0.f, 0.f, 0.f};
+  // row steps of 4 rows: step st covers rows r0 + 4 st .. +3, wave st % 4
+  for (int64_t j0 = r0 + 4 * wave; j0 < r1; j0 += 4 * kMmWaves * D) {
+    uint4 wv[D];
+    float sc[D], av[D][NBT];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const int64_t j = j0 + (int64_t)4 * kMmWaves * i + g;
+      const bool jin = j < r1;
+      int64_t row = jin ? (a.list ? (int64_t)a.list[j] : j) : -1;
+      if (row >= a.n_rows) row = -1;
+      const bool ok = row >= 0 && vin;
+      wv[i] = bload16(rW, ok ? (uint32_t)(row * rb) + (uint32_t)v * 16u : 0xFFFFFFF0u);
+      if constexpr (DT == 2) sc[i] = h2f(bload2(rS, ok ? (uint32_t)(row * groups + v / 4) * 2u : 0xFFFFFFF0u));
+#pragma unroll
+      for (int t = 0; t < NBT; ++t) {
+        const int b = 16 * t + nl;
+        const int64_t ai = a.a_by_row ? (row >= 0 ? row : 0) : j;
+        av[i][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+            rA, (jin && row >= 0 && b < a.B) ? (int)((b * a.a_stride + ai) * 4) : -16, 0, 0));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      float wf[E];
+      widen_vec<DT>(wv[i], DT == 2 ? sc[i] : 1.f, wf);
+      // A[m = b][k = row g] = a[b][row], B[k = row g][n] = W[row][column of tile e]
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) acc[t][e] = mfma4(av[i][t], wf[e], acc[t][e]);
+    }
+  }
+  // sum the four waves in wave order; lane holds D[m = 4g + r][n = lane % 16] of each tile
+#pragma unroll
+  for (int t = 0; t < NBT; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][(t * E + e) * 4 + r][lane] = acc[t][e][r];
+  __syncthreads();
+  const int64_t cols = a.cols;
+  for (int q = threadIdx.x; q < NBT * E * 4 * kWave; q += kMmThreads) {
+    const int ln = q % kWave, idx = q / kWave;
+    const int r = idx % 4, te = idx / 4, e = te % E, t = te / E;
+    const int b = 16 * t + 4 * (ln / 16) + r;
+    const int64_t c = (int64_t)(cchunk * 16 + (ln % 16)) * E + e;
+    if (b < a.B && c < cols) {
+      float s = red[0][idx][ln];
+#pragma unroll
+      for (int w = 1; w < kMmWaves; ++w) s += red[w][idx][ln];
+      a.partials[((int64_t)rchunk * a.B + b) * cols + c] = s;
+    }
+  }
+}
+
+template <int DT>
+hipError_t rowdot_dt(const MmRowArgs& a, hipStream_t s) {
+  const int tiles = (int)((a.count_max + 15) / 16);
+  const dim3 g((unsigned)((tiles + kMmWaves - 1) / kMmWaves), (unsigned)a.ks), t(kMmThreads);
+  if (a.nbt == 1) {
+    if (a.gated) hipLaunchKernelGGL((k_mm_rowdot<DT, 1, true>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((k_mm_rowdot<DT, 1, false>), g, t, 0, s, a);
+  } else {
+    if (a.gated) hipLaunchKernelGGL((k_mm_rowdot<DT, 2, true>), g, t, 0, s, a);
+    else hipLaunchKernelGGL((k_mm_rowdot<DT, 2, false>), g, t, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t axpy_dt(const MmAxpyArgs& a, hipStream_t s) {
+  const dim3 g((unsigned)mm_axpy_col_chunks(a.dt, a.cols), (unsigned)a.row_chunks), t(kMmThreads);
+  if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy<DT, 1>), g, t, 0, s, a);
+  else hipLaunchKernelGGL((k_mm_axpy<DT, 2>), g, t, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int mm_nbt(int B) { return B <= 16 ? 1 : 2; }
+
+int mm_row_ks(int dt, int64_t count_max, int64_t cols) {
+  // about 2048 waves, each over at least 8 k blocks
+  const int64_t kb = 4 * (dt == 0 ? 4 : dt == 1 ? 8 : 32);
+  const int64_t tiles = (count_max + 15) / 16;
+  int64_t ks = (2048 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  const int64_t kmax = cols / (8 * kb);
+  ks = ks > kmax ? kmax : ks;
+  return (int)(ks < 1 ? 1 : ks);
+}
+
+int64_t mm_row_kc(int dt, int64_t cols, int ks) {
+  const int64_t kb = 4 * (dt == 0 ? 4 : dt == 1 ? 8 : 32);
+  const int64_t blocks = (cols + kb - 1) / kb;
+  return ((blocks + ks - 1) / ks) * kb;
+}
+
+int mm_axpy_col_chunks(int dt, int64_t cols) {
+  const int64_t nvec = row_bytes(dt, cols) / 16;
+  return (int)((nvec + 15) / 16);
+}
+
+int mm_axpy_row_chunks(int dt, int64_t count_max, int64_t cols) {
+  // about 1024 blocks of four waves
+  const int64_t cc = mm_axpy_col_chunks(dt, cols);
+  int64_t rc = (1024 + cc - 1) / cc;
+  const int64_t rmax = (count_max + 63) / 64;   // at least 64 rows per block
+  rc = rc > rmax ? rmax : rc;
+  return (int)(rc < 1 ? 1 : rc);
+}
+
+bool mm_rowdot_supported(int dt, int64_t rows, int64_t cols) {
+  if (dt < 0 || dt > 2) return false;
+  const int64_t kb = 4 * (dt == 0 ? 4 : dt == 1 ? 8 : 32);
+  return cols % kb == 0 && rows * row_bytes(dt, cols) < ((int64_t)1 << 31);
+}
+
+bool mm_axpy_supported(int dt, int64_t rows, int64_t cols) {
+  // int4 rows would give 32 column tiles per lane vector: the VALU axpy takes them
+  return (dt == 0 || dt == 1) && rows * row_bytes(dt, cols) < ((int64_t)1 << 31);
+}
+
+hipError_t launch_mm_rowdot(const MmRowArgs& a, hipStream_t s) {
+  hipError_t e;
+  switch (a.dt) {
+    case 0: e = rowdot_dt<0>(a, s); break;
+    case 1: e = rowdot_dt<1>(a, s); break;
+    default: e = rowdot_dt<2>(a, s); break;
+  }
+  if (e != hipSuccess) return e;
+  const int64_t n = a.count_max * 16 * a.nbt;
+  int64_t blocks = (n + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+  if (a.gated) hipLaunchKernelGGL(k_mm_finish<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_mm_finish<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mm_axpy(const MmAxpyArgs& a, hipStream_t s) {
+  switch (a.dt) {
+    case 0: return axpy_dt<0>(a, s);
+    case 1: return axpy_dt<1>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pi
