@@ -1,0 +1,161 @@
+"""GPU tests of the paths beside the four-step parity: the stage-restricted
+layer call and its rows-read report, the hidden-major output layer with int4
+weights and with more hidden units than one pass covers, and batches whose
+size is not a multiple of the matrix-core tile.  Every check is against the
+CPU oracle (or a property the oracle's outputs fix)."""
+import numpy as np
+import pytest
+
+import synth
+import oracle as orc
+from tests import parity_harness as ph
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _layer_call(pi, dl, buf, B, stages, rows=None, cold=False):
+    pi.pi_ffn_layer_stages(dl.layer, B, buf.x, 0.0, None, buf.y, buf.logits, buf.A_g, buf.K,
+                           buf.A_c if cold else None, buf.K_c if cold else None, buf.ws_layer, stages, rows_read=rows)
+
+
+def _state(buf, cold):
+    K = int(buf.K.cpu()[0])
+    Kc = int(buf.K_c.cpu()[0]) if cold else 0
+    return (K, buf.A_g.cpu().numpy()[:K].tobytes(), Kc, buf.A_c.cpu().numpy()[:Kc].tobytes(),
+            buf.logits.cpu().numpy().tobytes(), buf.y.cpu().numpy().tobytes())
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_stages_one_by_one_reproduce_the_full_call(B):
+    """Enqueueing the stages separately, in order, gives the full call's bits."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    cfg = ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=17)
+    spec = synth.layer_spec(cfg, 0)
+    dl = ph.DeviceLayer(spec)
+    cold = len(spec.T_c) > 0
+    assert cold and dl.layer.cold
+    outs = []
+    for split in (False, True):
+        buf = ph.DeviceBuffers(cfg, spec.H, spec.n_g, len(spec.T_c), B)
+        buf.x.copy_(torch.from_numpy(synth.host_x(cfg.seed, 0, 4, B, cfg.d)))
+        if split:
+            for st in (pi.PI_STAGE_HIDDEN, pi.PI_STAGE_OUTPUT, pi.PI_STAGE_FC1, pi.PI_STAGE_FC2, pi.PI_STAGE_SUM):
+                _layer_call(pi, dl, buf, B, st, cold=cold)
+        else:
+            _layer_call(pi, dl, buf, B, pi.PI_STAGE_ALL, cold=cold)
+        torch.cuda.synchronize()
+        outs.append(_state(buf, cold))
+    assert outs[0] == outs[1]
+
+
+def _count_with_band(z, band=1e-4):
+    """(certain, possible) number of pre-activations > 0, given the fp32-vs-fp64 difference
+    of the GPU's sums (far below the band at these sizes)."""
+    return int(np.sum(z > band)), int(np.sum(z > -band))
+
+
+def _f64(m):
+    """Exact float64 values of stored fp32 / fp16 rows."""
+    return m.data.astype(np.float64) if m.dtype == synth.F32 else m.data.view(np.float16).astype(np.float64)
+
+
+@pytest.mark.parametrize("key,layer,B", [("opt-30b", 2, 1), ("opt-6.7b", 1, 1), ("opt-30b", 2, 4)])
+def test_rows_read_report(key, layer, B):
+    """rows_read[0] = P2 rows read: at batch 1 the hidden units with h > 0, else H;
+    rows_read[1] = W2 rows read: at batch 1 the listed neurons whose FC1 output is
+    non-zero, else K.  The pre-activations are recomputed in float64 from the stored bits
+    (a plain matrix product, c1 = 0)."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    cfg = synth.CONFIGS[key]
+    spec = synth.layer_spec(cfg, layer)
+    dl = ph.DeviceLayer(spec)
+    cold = len(spec.T_c) > 0
+    buf = ph.DeviceBuffers(cfg, spec.H, spec.n_g, len(spec.T_c), B)
+    x = synth.host_x(cfg.seed, layer, 6, B, cfg.d)
+    buf.x.copy_(torch.from_numpy(x))
+    rows = torch.full((2,), -1, dtype=torch.int32, device="cuda")
+    _layer_call(pi, dl, buf, B, pi.PI_STAGE_ALL, rows=rows, cold=cold)
+    torch.cuda.synchronize()
+    r = rows.cpu().numpy()
+    K = int(buf.K.cpu()[0])
+    A_g = buf.A_g.cpu().numpy()[:K]
+    if B > 1:
+        assert r[0] == spec.H and r[1] == K
+        return
+    sig = spec.sigmas()
+    x64 = x[0].astype(np.float64)
+    P1 = ph.host_mat(cfg.pdtype, cfg.seed, synth.TAG_P1, layer, cfg.d, sig[synth.TAG_P1], nrows=spec.H)
+    lo, hi = _count_with_band(_f64(P1) @ x64)
+    assert lo <= r[0] <= hi and hi - lo <= 2, (r, lo, hi)
+    ids = spec.T_g[A_g]
+    W1 = ph.host_mat(cfg.wdtype, cfg.seed, synth.TAG_W1, layer, cfg.d, sig[synth.TAG_W1], row_ids=ids)
+    b1 = synth.stored_to_f64(spec.b1[ids], cfg.bdtype)
+    lo, hi = _count_with_band(_f64(W1) @ x64 + b1)
+    assert lo <= r[1] <= hi and hi - lo <= 4, (r, lo, hi)
+
+
+def test_output_layer_int4_hidden_major():
+    """pi_predict_output with int4-g128 P2 stored hidden-major (groups run along N): logits
+    against the oracle on the exactly dequantised weights, and the activation bits."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    H, N, B = 96, 1280, 1
+    data, scales = synth.host_rows(synth.I4G128, 21, synth.TAG_P2, 0, N, 1 / np.sqrt(H), nrows=H)
+    # exact values q * s of the stored bits, [H x N]
+    q = np.empty((H, N), np.float64)
+    q[:, 0::2] = (data & 0xF).astype(np.int64)
+    q[:, 1::2] = (data >> 4).astype(np.int64)
+    q = np.where(q >= 8, q - 16, q)
+    s = scales.view(np.float16).astype(np.float64)
+    w = q * np.repeat(s, 128, axis=1)
+    P2t_dev = pi.Matrix(torch.from_numpy(data).cuda(), pi.PI_I4G128, torch.from_numpy(scales.view(np.int16)).cuda())
+    g = np.random.default_rng(5)
+    c2 = (g.standard_normal(N) * 0.3).astype(np.float32)
+    h = np.abs(g.standard_normal((B, H))).astype(np.float32)
+    h[:, ::3] = 0.0
+    logits = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    mask = torch.empty(2 * ((N + 63) // 64), dtype=torch.int32, device="cuda")
+    pi.pi_predict_output(B, H, N, torch.from_numpy(h).cuda(), P2t_dev, pi.Vector(torch.from_numpy(c2).cuda(), pi.PI_F32),
+                         0.0, logits, mask, None)
+    torch.cuda.synchronize()
+    eye = orc.Mat(np.eye(H, dtype=np.float32), orc.F32, H)
+    ref = orc.predict(h, eye, orc.Vec(None), orc.Mat(np.ascontiguousarray(w.T.astype(np.float32)), orc.F32, H),
+                      orc.Vec(c2, orc.F32))
+    lg = logits.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(lg - ref)) <= ph.LOGIT_ATOL
+    words = mask.cpu().numpy().view(np.uint32)
+    bits = ((words[np.arange(N) // 32] >> (np.arange(N) % 32)) & 1).astype(bool)
+    assert np.array_equal(bits, lg[0].astype(np.float32) > 0)
+
+
+# more hidden units than one pass of the batch-1 output-layer kernel reads (1024 rows a pass)
+BIG_H = ph.small_case("h1536", d=512, N=2048, H=1536, wdtype=synth.F16, seed=23)
+# batch sizes that leave the matrix-core batch tiles partly empty
+RAGGED_B = ph.small_case("mm-ragged", d=1024, N=2048, H=256, wdtype=synth.F16, gpu_frac=0.4, seed=24)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_output_layer_two_passes(fused):
+    _dev()
+    r = ph.run_layer_parity(BIG_H, layer=0, step=1, B=1, fused=fused)
+    print("[parity]", r)
+    ph.assert_report(r)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("B", [8, 9, 17, 31])
+def test_matrix_core_batches(B, fused):
+    _dev()
+    r = ph.run_layer_parity(RAGGED_B, layer=0, step=2, B=B, fused=fused)
+    print("[parity]", r)
+    ph.assert_report(r)
+    assert r["K"] > 0 and r["K_c"] > 0
