@@ -55,6 +55,13 @@ struct FfnWs {
 // Partial sums of the batched matrix-core GEMMs, bounded over the weight dtypes
 // (workspace sizes are asked for without them).
 bool use_mm(int32_t B) { return B >= pi::kMmMinBatch; }
+// Rows of an activation buffer (h, a): B, or the padded batch 16 * nbt when the
+// matrix-core kernels keep it neuron-major.
+size_t act_rows(int32_t B) {
+  if (!use_mm(B)) return (size_t)B;
+  const size_t p = (size_t)16 * pi::mm_nbt(B);
+  return p > (size_t)B ? p : (size_t)B;
+}
 size_t mm_row_partial_bytes(int32_t B, int64_t rows, int64_t cols, bool gated) {
   if (!use_mm(B) || rows <= 0 || cols <= 0) return 0;
   int ks = 1;
@@ -84,7 +91,7 @@ size_t ffn_partial_bytes(int32_t B, int32_t d, int32_t n_g) {
 FfnWs ffn_ws_layout(void* ws, int32_t B, int32_t d, int32_t n_g) {
   Carver c{static_cast<char*>(ws)};
   FfnWs w{};
-  w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
+  w.a = c.take<float>(act_rows(B) * (size_t)(n_g > 0 ? n_g : 1) * 4);
   w.partials = c.take<float>(ffn_partial_bytes(B, d, n_g));
   w.bytes = c.off;
   return w;
@@ -132,7 +139,7 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
   Carver c{static_cast<char*>(ws)};
   LayerWs w{};
   const size_t ng = n_groups64(N);
-  w.h = c.take<float>((size_t)B * H * 4);
+  w.h = c.take<float>(act_rows(B) * H * 4);
   w.logits = c.take<float>((size_t)B * N * 4);
   w.mask = c.take<uint32_t>(table_words(N) * 4);
   w.seg_slot = c.take<int32_t>(ng * 64 * 4);
@@ -140,7 +147,7 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
   w.pos_slot = c.take<int32_t>(ng * 64 * 4);
   w.pos_a = c.take<float>(ng * 64 * 4);
   w.cnt = c.take<uint32_t>(ng * 4);
-  w.a = c.take<float>((size_t)B * (size_t)(n_g > 0 ? n_g : 1) * 4);
+  w.a = c.take<float>(act_rows(B) * (size_t)(n_g > 0 ? n_g : 1) * 4);
   const size_t pb = ffn_partial_bytes(B, d, n_g);
   const size_t seg = (size_t)pi::kSegChunks * (size_t)d * 4;
   w.partials = c.take<float>(max3(pb, seg, pred_partial_bytes(B, d, H, N)));
@@ -151,8 +158,13 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
 // The predictor's hidden layer, h[b,m] = max(0, P1[m].x_b + c1[m]): batch 1 on the
 // register-x GEMV, batches of kMmMinBatch and more on the matrix cores (split-K
 // partials in `partials`), others on the LDS-x row-dot kernel.
+// h kept neuron-major ([H x 16 nbt]) between the two matrix-core predictor layers.
+bool h_neuron_major(int32_t B, int32_t d, int32_t H, int32_t N, const pi_matrix& P1, const pi_matrix& P2) {
+  return use_mm(B) && pi::mm_rowdot_supported(P1.dtype, H, d) && pi::mm_axpy_supported(P2.dtype, H, N);
+}
+
 int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* x, const pi_matrix& P1,
-                   const pi_vector& c1, float* h, float* partials) {
+                   const pi_vector& c1, float* h, float* partials, bool h_tr) {
   if (B == 1 && pi::b1_supported(P1.dtype, d)) {
     pi::B1Gemv g{};
     g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
@@ -164,7 +176,8 @@ int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* 
     m.W = P1.data; m.Ws = P1.scales; m.dt = P1.dtype; m.gated = 0; m.cols = d; m.n_rows = H; m.list = nullptr;
     m.count_dev = nullptr; m.count_max = H; m.x = x; m.B = B; m.nbt = pi::mm_nbt(B);
     m.ks = pi::mm_row_ks(P1.dtype, H, d); m.kc = pi::mm_row_kc(P1.dtype, d, m.ks); m.partials = partials;
-    m.bias = c1.data; m.bias_dt = c1.dtype; m.relu = 1; m.out = h; m.out_stride = H;
+    m.bias = c1.data; m.bias_dt = c1.dtype; m.relu = 1; m.out = h; m.out_tr = h_tr;
+    m.out_stride = h_tr ? 16 * m.nbt : H;
     return hip_status(pi::launch_mm_rowdot(m, s));
   }
   pi::RowdotArgs a{};
@@ -181,7 +194,7 @@ int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* 
 // sum with c2, then the words from the stored logits.
 int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const float* h, const pi_matrix& P2,
                          const pi_vector& c2, float tau, float* logits, uint32_t* mask, float* partials,
-                         int32_t* rows_read = nullptr) {
+                         int32_t* rows_read = nullptr, bool h_tr = false) {
   if (!out_layer_needs_partials(B, H, N)) {
     pi::PredFc1Args a{};
     a.P2 = P2.data; a.P2s = P2.scales; a.pdt = P2.dtype; a.H = H; a.N = N; a.h = h;
@@ -192,7 +205,8 @@ int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const f
   if (use_mm(B) && pi::mm_axpy_supported(P2.dtype, H, N)) {
     pi::MmAxpyArgs m{};
     m.W = P2.data; m.Ws = P2.scales; m.dt = P2.dtype; m.cols = N; m.n_rows = H; m.list = nullptr;
-    m.count_dev = nullptr; m.count_max = H; m.a = h; m.a_stride = H; m.a_by_row = 1; m.B = B; m.nbt = pi::mm_nbt(B);
+    m.count_dev = nullptr; m.count_max = H; m.a = h; m.a_stride = H; m.a_by_row = 1; m.a_tr = h_tr; m.B = B;
+    m.nbt = pi::mm_nbt(B);
     m.row_chunks = pi::mm_axpy_row_chunks(P2.dtype, H, N);
     m.rows_per_chunk = ((H + m.row_chunks - 1) / m.row_chunks + 15) / 16 * 16;
     m.partials = partials;
@@ -236,7 +250,7 @@ size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N
   if (B < 1) B = 1;
   switch (op) {
     case PI_OP_PREDICT:
-      return H > 0 && N > 0 && d > 0 ? align_up((size_t)B * (size_t)H * 4) + pred_partial_bytes(B, d, H, N) : 0;
+      return H > 0 && N > 0 && d > 0 ? align_up(act_rows(B) * (size_t)H * 4) + pred_partial_bytes(B, d, H, N) : 0;
     case PI_OP_PREDICT_OUTPUT: return H > 0 && N > 0 ? out_partials_bytes(B, H, N) : 0;
     case PI_OP_SPARSE_FFN:
       return d > 0 ? ffn_ws_layout(nullptr, B, d, n_g).bytes : 0;
@@ -276,10 +290,11 @@ int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const f
   if (ws_bytes < pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0)) return PI_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* h = static_cast<float*>(ws);
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up((size_t)B * (size_t)H * 4));
-  const int st = enqueue_hidden(s, B, d, H, x, P1, c1, h, partials);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(act_rows(B) * (size_t)H * 4));
+  const bool h_tr = h_neuron_major(B, d, H, N, P1, P2);
+  const int st = enqueue_hidden(s, B, d, H, x, P1, c1, h, partials, h_tr);
   if (st != PI_OK) return st;
-  return enqueue_output_layer(s, B, H, N, h, P2, c2, 0.f, logits, nullptr, partials);
+  return enqueue_output_layer(s, B, H, N, h, P2, c2, 0.f, logits, nullptr, partials, nullptr, h_tr);
 }
 
 int pi_predict_output(void* stream, int32_t B, int32_t H, int32_t N, const float* h, pi_matrix P2, pi_vector c2,
@@ -331,15 +346,18 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
                 const hipEvent_t* ev, uint32_t stages) {
   const bool gated = kind == PI_GATED_RELU;
   int st = PI_OK;
+  const bool mm1 = use_mm(B) && pi::mm_rowdot_supported(W1.dtype, n_g, d);
+  const bool mm2 = use_mm(B) && n_g > 0 && pi::mm_axpy_supported(W2.dtype, n_g, d);
+  const bool a_tr = mm1 && mm2;      // a kept neuron-major between the two matrix-core GEMMs
   if (stages & PI_STAGE_FC1) {
-    if (use_mm(B) && pi::mm_rowdot_supported(W1.dtype, n_g, d)) {
+    if (mm1) {
       pi::MmRowArgs m{};
       m.W = W1.data; m.Ws = W1.scales; m.dt = W1.dtype; m.gated = gated;
       if (gated) { m.Wup = Wup.data; m.Wups = Wup.scales; }
       m.cols = d; m.n_rows = n_g; m.list = A_g; m.count_dev = K; m.count_max = n_g; m.x = x; m.B = B;
       m.nbt = pi::mm_nbt(B); m.ks = pi::mm_row_ks(W1.dtype, n_g, d); m.kc = pi::mm_row_kc(W1.dtype, d, m.ks);
-      m.partials = partials; m.bias = b1.data; m.bias_dt = b1.dtype; m.relu = 1; m.out = a;
-      m.out_stride = n_g > 0 ? n_g : 1;
+      m.partials = partials; m.bias = b1.data; m.bias_dt = b1.dtype; m.relu = 1; m.out = a; m.out_tr = a_tr;
+      m.out_stride = a_tr ? 16 * m.nbt : (n_g > 0 ? n_g : 1);
       st = n_g > 0 ? hip_status(pi::launch_mm_rowdot(m, s)) : PI_OK;
     } else if (B == 1 && pi::b1_supported(W1.dtype, d)) {
       pi::B1Gemv g{};
@@ -359,13 +377,12 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
     if (st != PI_OK) return st;
   }
   if (ev && ev[0] && (st = hip_status(hipEventRecord(ev[0], s))) != PI_OK) return st;
-  const bool mm2 = use_mm(B) && n_g > 0 && pi::mm_axpy_supported(W2.dtype, n_g, d);
   const int chunks2 = mm2 ? pi::mm_axpy_row_chunks(W2.dtype, n_g, d) : pi::fc2_chunks(B);
   if (stages & PI_STAGE_FC2) {
     if (mm2) {
       pi::MmAxpyArgs m{};
       m.W = W2.data; m.Ws = W2.scales; m.dt = W2.dtype; m.cols = d; m.n_rows = n_g; m.list = A_g; m.count_dev = K;
-      m.count_max = n_g; m.a = a; m.a_stride = n_g; m.a_by_row = 0; m.B = B; m.nbt = pi::mm_nbt(B);
+      m.count_max = n_g; m.a = a; m.a_stride = n_g; m.a_by_row = 0; m.a_tr = a_tr; m.B = B; m.nbt = pi::mm_nbt(B);
       m.row_chunks = chunks2;
       m.rows_per_chunk = ((n_g + chunks2 - 1) / chunks2 + 15) / 16 * 16;
       m.partials = partials;
@@ -442,7 +459,8 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
 
   if ((st = record(0)) != PI_OK) return st;
   // predictor hidden layer
-  if (want(PI_STAGE_HIDDEN) && (st = enqueue_hidden(s, B, d, H, x, L->P1, L->c1, w.h, w.partials)) != PI_OK)
+  const bool h_tr = h_neuron_major(B, d, H, N, L->P1, L->P2);
+  if (want(PI_STAGE_HIDDEN) && (st = enqueue_hidden(s, B, d, H, x, L->P1, L->c1, w.h, w.partials, h_tr)) != PI_OK)
     return st;
   if ((st = record(1)) != PI_OK) return st;
 
@@ -481,7 +499,8 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
   }
   // any batch: output layer + activation words, the lists, then FC1 / FC2 / ordered sum over the list
   if (want(PI_STAGE_OUTPUT)) {
-    if ((st = enqueue_output_layer(s, B, H, N, w.h, L->P2, L->c2, tau, lg, w.mask, w.partials, rows_read)) != PI_OK)
+    if ((st = enqueue_output_layer(s, B, H, N, w.h, L->P2, L->c2, tau, lg, w.mask, w.partials, rows_read, h_tr)) !=
+        PI_OK)
       return st;
     pi::ListCtx lc{};
     lc.mask = w.mask; lc.gbits = static_cast<const uint32_t*>(L->table); lc.W = (int)table_words(N);

@@ -207,8 +207,9 @@ struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b
   const void* bias;             // per row id
   int bias_dt;
   int relu;
-  float* out;                   // [B x out_stride], column = position
-  int64_t out_stride;
+  float* out;                   // [B x out_stride], column = position; or, with out_tr,
+  int64_t out_stride;           // [count_max x 16 nbt] neuron-major (zeros past B)
+  int out_tr;
 };
 struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's rows j of a[b, j] W[row(j), c]
   const void* W;
@@ -219,9 +220,10 @@ struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's 
   const int32_t* list;          // NULL = rows 0 .. count_max
   const int32_t* count_dev;
   int64_t count_max;
-  const float* a;               // a[b * a_stride + (a_by_row ? row : j)]
-  int64_t a_stride;
+  const float* a;               // a[b * a_stride + idx], or with a_tr a[idx * 16 nbt + b];
+  int64_t a_stride;             // idx = a_by_row ? row : j
   int a_by_row;
+  int a_tr;
   int B;
   int nbt;
   int64_t rows_per_chunk;       // a multiple of 16

@@ -165,11 +165,21 @@ __global__ __launch_bounds__(256) void k_mm_finish(MmRowArgs a) {
     const int64_t pos = t / NBP;
     const int b = (int)(t % NBP);
     if (b >= a.B) continue;
-    float z = 0.f, u = 0.f;
-    for (int ks = 0; ks < a.ks; ++ks) z += a.partials[((int64_t)ks * a.count_max + pos) * NBP + b];
-    if constexpr (GATED)
-      for (int ks = 0; ks < a.ks; ++ks)
-        u += a.partials[((int64_t)(a.ks + ks) * a.count_max + pos) * NBP + b];
+    // partials loaded eight at a time (all in flight), summed in chunk order
+    auto chunk_sum = [&](int half) {
+      float acc = 0.f;
+      for (int k0 = 0; k0 < a.ks; k0 += 8) {
+        float p[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          p[q] = k0 + q < a.ks ? a.partials[((int64_t)(half * a.ks + k0 + q) * a.count_max + pos) * NBP + b] : 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc += p[q];
+      }
+      return acc;
+    };
+    float z = chunk_sum(0), u = 0.f;
+    if constexpr (GATED) u = chunk_sum(1);
     int64_t row = a.list ? (int64_t)a.list[pos] : pos;
     const bool ok = row >= 0 && row < a.n_rows;
     if (a.bias && ok) z += load_bias(a.bias, a.bias_dt, row);
@@ -179,11 +189,49 @@ __global__ __launch_bounds__(256) void k_mm_finish(MmRowArgs a) {
   }
 }
 
+// The same, written neuron-major: out[pos * NBP + b], zeros for b >= B.
+template <bool GATED>
+__global__ __launch_bounds__(256) void k_mm_finish_tr(MmRowArgs a) {
+  const int NBP = 16 * a.nbt;
+  int64_t count = a.count_max;
+  if (a.list) {
+    const int64_t kd = *a.count_dev;
+    count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
+  }
+  const int64_t n = count * NBP;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t pos = t / NBP;
+    const int b = (int)(t % NBP);
+    float z = 0.f, u = 0.f;
+    for (int k0 = 0; k0 < a.ks; k0 += 8) {
+      float p[8], q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = k0 + i < a.ks ? a.partials[((int64_t)(k0 + i) * a.count_max + pos) * NBP + b] : 0.f;
+        if constexpr (GATED)
+          q[i] = k0 + i < a.ks ? a.partials[((int64_t)(a.ks + k0 + i) * a.count_max + pos) * NBP + b] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        z += p[i];
+        if constexpr (GATED) u += q[i];
+      }
+    }
+    int64_t row = a.list ? (int64_t)a.list[pos] : pos;
+    const bool ok = row >= 0 && row < a.n_rows && b < a.B;
+    if (a.bias && ok) z += load_bias(a.bias, a.bias_dt, row);
+    if (a.relu) z = z > 0.f ? z : 0.f;
+    if constexpr (GATED) z *= u;
+    a.out[pos * NBP + b] = ok ? z : 0.f;
+  }
+}
+
 template <int DT, int NBT>
 __global__ __launch_bounds__(kMmThreads) void k_mm_axpy(MmAxpyArgs a) {
   constexpr int E = Fmt<DT>::E;
   constexpr int D = 8;                      // row steps (4 rows each) in flight per wave
   __shared__ float red[kMmWaves][NBT * E * 4][kWave];
+  extern __shared__ int32_t ax_rows[];     // the chunk's row ids (rows_per_chunk entries)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const int g = lane / 16, nl = lane % 16;
@@ -196,6 +244,13 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy(MmAxpyArgs a) {
   const int64_t r0 = (int64_t)rchunk * a.rows_per_chunk;
   int64_t r1 = r0 + a.rows_per_chunk;
   r1 = r1 < count ? r1 : count;
+  // row ids of the chunk, looked up once (listed rows) so that no weight load
+  // waits on a list load inside the loop
+  for (int64_t j = r0 + threadIdx.x; j < r1; j += kMmThreads) {
+    int64_t row = a.list ? (int64_t)a.list[j] : j;
+    ax_rows[j - r0] = (row >= 0 && row < a.n_rows) ? (int32_t)row : -1;
+  }
+  __syncthreads();
   const int64_t rb = row_bytes(DT, a.cols);
   const int64_t groups = a.cols / 128;
   const int nvec = (int)(rb / 16);
@@ -204,44 +259,66 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy(MmAxpyArgs a) {
   const uint32_t wbytes = (uint32_t)(a.n_rows * rb);
   const rsrc_t rW = make_rsrc(a.W, wbytes);
   const rsrc_t rS = make_rsrc(DT == 2 ? (const void*)a.Ws : a.W, DT == 2 ? (uint32_t)(a.n_rows * groups * 2) : 0u);
-  const rsrc_t rA = make_rsrc(a.a, (uint32_t)(a.B * a.a_stride * 4));
+  const int NBP = 16 * NBT;
+  const rsrc_t rA = make_rsrc(a.a, a.a_tr ? (uint32_t)((a.a_by_row ? a.n_rows : a.count_max) * NBP * 4)
+                                          : (uint32_t)(a.B * a.a_stride * 4));
   float4v_t acc[NBT][E];
 #pragma unroll
   for (int t = 0; t < NBT; ++t)
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[t][e] = float4v_t{0.f, 0.f, 0.f, 0.f};
-  // row steps of 4 rows: step st covers rows r0 + 4 st .. +3, wave st % 4
-  for (int64_t j0 = r0 + 4 * wave; j0 < r1; j0 += 4 * kMmWaves * D) {
+  // row steps of 4 rows: step st covers rows r0 + 4 st .. +3, wave st % 4.  A round
+  // is D steps of one wave, all its loads issued before its instructions.  (Issuing
+  // round i+1 before computing round i needs twice the registers, and the
+  // occupancy lost costs more than the overlap gains.)
+  struct Round {
     uint4 wv[D];
     float sc[D], av[D][NBT];
+  };
+  constexpr int64_t kStep = 4 * kMmWaves * D;
+  auto issue = [&](int64_t j0, Round& rd) {
+    int32_t rowv[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {                 // every row id of the round first (one LDS wait)
+      const int64_t j = j0 + (int64_t)4 * kMmWaves * i + g;
+      rowv[i] = j < r1 ? ax_rows[j - r0] : -1;
+    }
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       const int64_t j = j0 + (int64_t)4 * kMmWaves * i + g;
-      const bool jin = j < r1;
-      int64_t row = jin ? (a.list ? (int64_t)a.list[j] : j) : -1;
-      if (row >= a.n_rows) row = -1;
+      const int64_t row = rowv[i];
       const bool ok = row >= 0 && vin;
-      wv[i] = bload16(rW, ok ? (uint32_t)(row * rb) + (uint32_t)v * 16u : 0xFFFFFFF0u);
-      if constexpr (DT == 2) sc[i] = h2f(bload2(rS, ok ? (uint32_t)(row * groups + v / 4) * 2u : 0xFFFFFFF0u));
+      rd.wv[i] = bload16(rW, ok ? (uint32_t)(row * rb) + (uint32_t)v * 16u : 0xFFFFFFF0u);
+      if constexpr (DT == 2) rd.sc[i] = h2f(bload2(rS, ok ? (uint32_t)(row * groups + v / 4) * 2u : 0xFFFFFFF0u));
+      const int64_t ai = a.a_by_row ? (row >= 0 ? row : 0) : j;
 #pragma unroll
       for (int t = 0; t < NBT; ++t) {
         const int b = 16 * t + nl;
-        const int64_t ai = a.a_by_row ? (row >= 0 ? row : 0) : j;
-        av[i][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-            rA, (jin && row >= 0 && b < a.B) ? (int)((b * a.a_stride + ai) * 4) : -16, 0, 0));
+        // neuron-major activations: the 16 lanes of a row group read 64 contiguous bytes
+        const uint32_t off = a.a_tr ? (uint32_t)((ai * NBP + b) * 4) : (uint32_t)((b * a.a_stride + ai) * 4);
+        rd.av[i][t] = __uint_as_float(
+            __builtin_amdgcn_raw_buffer_load_b32(rA, (row >= 0 && b < a.B) ? (int)off : -16, 0, 0));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute = [&](const Round& rd) {
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       float wf[E];
-      widen_vec<DT>(wv[i], DT == 2 ? sc[i] : 1.f, wf);
+      widen_vec<DT>(rd.wv[i], DT == 2 ? rd.sc[i] : 1.f, wf);
       // A[m = b][k = row g] = a[b][row], B[k = row g][n] = W[row][column of tile e]
 #pragma unroll
       for (int e = 0; e < E; ++e)
 #pragma unroll
-        for (int t = 0; t < NBT; ++t) acc[t][e] = mfma4(av[i][t], wf[e], acc[t][e]);
+        for (int t = 0; t < NBT; ++t) acc[t][e] = mfma4(rd.av[i][t], wf[e], acc[t][e]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int64_t j0 = r0 + 4 * wave; j0 < r1; j0 += kStep) {
+    Round rd;
+    issue(j0, rd);
+    compute(rd);
   }
   // sum the four waves in wave order; lane holds D[m = 4g + r][n = lane % 16] of each tile
 #pragma unroll
@@ -283,8 +360,9 @@ hipError_t rowdot_dt(const MmRowArgs& a, hipStream_t s) {
 template <int DT>
 hipError_t axpy_dt(const MmAxpyArgs& a, hipStream_t s) {
   const dim3 g((unsigned)mm_axpy_col_chunks(a.dt, a.cols), (unsigned)a.row_chunks), t(kMmThreads);
-  if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy<DT, 1>), g, t, 0, s, a);
-  else hipLaunchKernelGGL((k_mm_axpy<DT, 2>), g, t, 0, s, a);
+  const size_t shm = (size_t)a.rows_per_chunk * 4;
+  if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy<DT, 1>), g, t, shm, s, a);
+  else hipLaunchKernelGGL((k_mm_axpy<DT, 2>), g, t, shm, s, a);
   return hipGetLastError();
 }
 
@@ -344,8 +422,13 @@ hipError_t launch_mm_rowdot(const MmRowArgs& a, hipStream_t s) {
   const int64_t n = a.count_max * 16 * a.nbt;
   int64_t blocks = (n + 255) / 256;
   blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
-  if (a.gated) hipLaunchKernelGGL(k_mm_finish<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_mm_finish<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  if (a.out_tr) {
+    if (a.gated) hipLaunchKernelGGL(k_mm_finish_tr<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_mm_finish_tr<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  } else {
+    if (a.gated) hipLaunchKernelGGL(k_mm_finish<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_mm_finish<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
