@@ -54,17 +54,18 @@ struct FfnWs {
 
 // Partial sums of the batched matrix-core GEMMs, bounded over the weight dtypes
 // (workspace sizes are asked for without them).
-bool use_mm(int32_t B) { return B >= pi::kMmMinBatch; }
+bool use_mm_row(int32_t B) { return B >= pi::kMmRowMinBatch; }
+bool use_mm_axpy(int32_t B) { return B >= pi::kMmAxpyMinBatch; }
 // Rows of an activation buffer (h, a): B, or the padded batch 16 * nbt when the
 // matrix-core kernels keep it neuron-major.
 size_t act_rows(int32_t B) {
-  if (!use_mm(B)) return (size_t)B;
+  if (!use_mm_row(B)) return (size_t)B;
   const size_t p = (size_t)16 * pi::mm_nbt(B);
   return p > (size_t)B ? p : (size_t)B;
 }
 size_t mm_row_partial_bytes(int32_t B, int64_t rows, int64_t cols, bool gated) {
-  if (!use_mm(B) || rows <= 0 || cols <= 0) return 0;
-  int ks = 1;
+  if (!use_mm_row(B) || rows <= 0 || cols <= 0) return 0;
+  int ks = pi::mm_row16_ks(rows, cols, pi::mm_nbt(B), gated);
   for (int dt = 0; dt < 3; ++dt) {
     const int k = pi::mm_row_ks(dt, rows, cols);
     ks = k > ks ? k : ks;
@@ -72,7 +73,7 @@ size_t mm_row_partial_bytes(int32_t B, int64_t rows, int64_t cols, bool gated) {
   return (size_t)(gated ? 2 : 1) * ks * (size_t)rows * 16 * pi::mm_nbt(B) * 4;
 }
 size_t mm_axpy_partial_bytes(int32_t B, int64_t rows, int64_t cols) {
-  if (!use_mm(B) || rows <= 0 || cols <= 0) return 0;
+  if (!use_mm_axpy(B) || rows <= 0 || cols <= 0) return 0;
   int rc = 1;
   for (int dt = 0; dt < 2; ++dt) {
     const int r = pi::mm_axpy_row_chunks(dt, rows, cols);
@@ -156,11 +157,12 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
 }
 
 // The predictor's hidden layer, h[b,m] = max(0, P1[m].x_b + c1[m]): batch 1 on the
-// register-x GEMV, batches of kMmMinBatch and more on the matrix cores (split-K
+// register-x GEMV, batches of kMmRowMinBatch and more on the matrix cores (split-K
 // partials in `partials`), others on the LDS-x row-dot kernel.
 // h kept neuron-major ([H x 16 nbt]) between the two matrix-core predictor layers.
 bool h_neuron_major(int32_t B, int32_t d, int32_t H, int32_t N, const pi_matrix& P1, const pi_matrix& P2) {
-  return use_mm(B) && pi::mm_rowdot_supported(P1.dtype, H, d) && pi::mm_axpy_supported(P2.dtype, H, N);
+  return use_mm_row(B) && use_mm_axpy(B) && pi::mm_rowdot_supported(P1.dtype, H, d) &&
+         pi::mm_axpy_supported(P2.dtype, H, N);
 }
 
 int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* x, const pi_matrix& P1,
@@ -171,7 +173,7 @@ int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* 
     g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
     return hip_status(pi::launch_hidden_b1(g, s));
   }
-  if (use_mm(B) && pi::mm_rowdot_supported(P1.dtype, H, d)) {
+  if (use_mm_row(B) && pi::mm_rowdot_supported(P1.dtype, H, d)) {
     pi::MmRowArgs m{};
     m.W = P1.data; m.Ws = P1.scales; m.dt = P1.dtype; m.gated = 0; m.cols = d; m.n_rows = H; m.list = nullptr;
     m.count_dev = nullptr; m.count_max = H; m.x = x; m.B = B; m.nbt = pi::mm_nbt(B);
@@ -202,7 +204,7 @@ int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const f
     return hip_status(pi::launch_pred_out_b1(a, s));
   }
   int st, chunks;
-  if (use_mm(B) && pi::mm_axpy_supported(P2.dtype, H, N)) {
+  if (use_mm_axpy(B) && pi::mm_axpy_supported(P2.dtype, H, N)) {
     pi::MmAxpyArgs m{};
     m.W = P2.data; m.Ws = P2.scales; m.dt = P2.dtype; m.cols = N; m.n_rows = H; m.list = nullptr;
     m.count_dev = nullptr; m.count_max = H; m.a = h; m.a_stride = H; m.a_by_row = 1; m.a_tr = h_tr; m.B = B;
@@ -346,8 +348,8 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
                 const hipEvent_t* ev, uint32_t stages) {
   const bool gated = kind == PI_GATED_RELU;
   int st = PI_OK;
-  const bool mm1 = use_mm(B) && pi::mm_rowdot_supported(W1.dtype, n_g, d);
-  const bool mm2 = use_mm(B) && n_g > 0 && pi::mm_axpy_supported(W2.dtype, n_g, d);
+  const bool mm1 = use_mm_row(B) && pi::mm_rowdot_supported(W1.dtype, n_g, d);
+  const bool mm2 = use_mm_axpy(B) && n_g > 0 && pi::mm_axpy_supported(W2.dtype, n_g, d);
   const bool a_tr = mm1 && mm2;      // a kept neuron-major between the two matrix-core GEMMs
   if (stages & PI_STAGE_FC1) {
     if (mm1) {
@@ -355,7 +357,9 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
       m.W = W1.data; m.Ws = W1.scales; m.dt = W1.dtype; m.gated = gated;
       if (gated) { m.Wup = Wup.data; m.Wups = Wup.scales; }
       m.cols = d; m.n_rows = n_g; m.list = A_g; m.count_dev = K; m.count_max = n_g; m.x = x; m.B = B;
-      m.nbt = pi::mm_nbt(B); m.ks = pi::mm_row_ks(W1.dtype, n_g, d); m.kc = pi::mm_row_kc(W1.dtype, d, m.ks);
+      m.nbt = pi::mm_nbt(B); m.x_f16 = W1.dtype == PI_F16;
+      m.ks = m.x_f16 ? pi::mm_row16_ks(n_g, d, m.nbt, gated) : pi::mm_row_ks(W1.dtype, n_g, d);
+      m.kc = pi::mm_row_kc(W1.dtype, d, m.ks);
       m.partials = partials; m.bias = b1.data; m.bias_dt = b1.dtype; m.relu = 1; m.out = a; m.out_tr = a_tr;
       m.out_stride = a_tr ? 16 * m.nbt : (n_g > 0 ? n_g : 1);
       st = n_g > 0 ? hip_status(pi::launch_mm_rowdot(m, s)) : PI_OK;

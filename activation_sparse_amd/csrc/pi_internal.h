@@ -184,8 +184,11 @@ hipError_t launch_rows_read(int32_t* stats, int32_t rows0, const int32_t* K1, hi
 hipError_t launch_merge(int B, int d, float* y, const float* y_c, const int32_t* K_c, const void* b2,
                         int b2_dt, hipStream_t s);
 
-// Batched GEMMs on the fp32-input matrix cores (pi_mfma.hip), for B >= kMmMinBatch.
-constexpr int kMmMinBatch = 8;
+// Batched GEMMs on the matrix cores (pi_mfma.hip): the row-dot GEMMs (predictor
+// hidden layer, FC1) from kMmRowMinBatch batch rows, the axpy GEMMs (output
+// layer, FC2) from kMmAxpyMinBatch (below that the VALU kernels measure faster).
+constexpr int kMmRowMinBatch = 2;
+constexpr int kMmAxpyMinBatch = 3;
 struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b, k])
   const void* W;
   const uint16_t* Ws;
@@ -210,6 +213,7 @@ struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b
   float* out;                   // [B x out_stride], column = position; or, with out_tr,
   int64_t out_stride;           // [count_max x 16 nbt] neuron-major (zeros past B)
   int out_tr;
+  int x_f16;                    // fp16 weights: x may be rounded to fp16 (fp16 matrix cores; FC1 only)
 };
 struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's rows j of a[b, j] W[row(j), c]
   const void* W;
@@ -233,6 +237,9 @@ struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's 
 int mm_nbt(int B);
 int mm_row_ks(int dt, int64_t count_max, int64_t cols);
 int64_t mm_row_kc(int dt, int64_t cols, int ks);
+// the fp16 matrix-core row-dot (x rounded to fp16, its k chunk staged in LDS)
+bool mm_row16_used(const MmRowArgs& a);
+int mm_row16_ks(int64_t count_max, int64_t cols, int nbt, bool gated);
 int mm_axpy_col_chunks(int dt, int64_t cols);
 int mm_axpy_row_chunks(int dt, int64_t count_max, int64_t cols);
 bool mm_rowdot_supported(int dt, int64_t rows, int64_t cols);

@@ -1,7 +1,13 @@
-// pi_mfma.hip - the batched (B >= kMmMinBatch) GEMMs on the fp32-input matrix
-// cores (v_mfma_f32_16x16x4_f32): the weights are widened to fp32 in registers
-// and x, h and a stay fp32, so the arithmetic is the VALU path's (fp32
-// products, fp32 accumulation) with the operand reuse of a matrix tile.
+// pi_mfma.hip - the batched GEMMs on the matrix cores.
+//
+// The predictor's layers and FC2 use the fp32-input instruction
+// (v_mfma_f32_16x16x4_f32): the weights are widened to fp32 in registers and
+// x, h and a stay fp32, so the arithmetic is the VALU path's (fp32 products,
+// fp32 accumulation) with the operand reuse of a matrix tile; the logits keep
+// the precision the activation decision's parity band is set by.  FC1 with
+// fp16 weights uses the fp16 instruction (v_mfma_f32_16x16x32_f16, ten times
+// the fp32 instruction's measured rate): x is rounded to fp16, the products
+// of two fp16 values are exact and accumulate in fp32 (k_mm_rowdot16).
 //
 // One 16x16x4 instruction sums over k = 4 lane groups g = lane / 16.  Each lane
 // loads one 16-byte weight vector (E consecutive elements along k) and feeds
@@ -144,6 +150,106 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_rowdot(MmRowArgs a) {
       const int64_t p = (int64_t)tile * 16 + 4 * g + r;
       if (p < count) {
         const int64_t o = ((int64_t)ks * a.count_max + p) * NBP + 16 * t + ml;
+        a.partials[o] = acc[t][r];
+        if constexpr (GATED) a.partials[(int64_t)a.ks * a.count_max * NBP + o] = accu[t][r];
+      }
+    }
+  }
+}
+
+// fp16 weights with x rounded to fp16 (FC1 of the batched path): one
+// v_mfma_f32_16x16x32_f16 per 32 k takes the lane's 16-byte weight vector as
+// it is (row m = lane % 16, k = 8 g .. 8 g + 7, g = lane / 16) and 8 fp16 x of
+// batch row lane % 16 at the same k, accumulating in fp32.  The block's four
+// waves share one k chunk: x[16 nbt][chunk] is rounded to fp16 once, into LDS
+// (rows padded by 16 bytes, so the 16 lanes of a lane group hit distinct banks).
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+// waves per block, sharing the block's x chunk (more for 32 batch rows, whose chunk is twice the size)
+constexpr int r16_waves(int nbt) { return nbt == 1 ? 4 : 16; }
+// largest k chunk: x[16 nbt][chunk] in fp16 within 64 KB of LDS
+constexpr int row16_kcmax(int nbt, bool) { return nbt == 1 ? 1024 : 960; }
+
+__device__ __forceinline__ float4v_t mfma16(half8_t a, half8_t b, float4v_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <int NBT, bool GATED>
+__global__ __launch_bounds__(r16_waves(NBT) * kWave) void k_mm_rowdot16(MmRowArgs a) {
+  constexpr int WPB = r16_waves(NBT), NT = WPB * kWave;
+  constexpr int D = 8;                      // k blocks of 32 in flight
+  extern __shared__ __attribute__((aligned(16))) _Float16 xh[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  int64_t count = a.count_max;
+  if (a.list) {
+    const int64_t kd = *a.count_dev;
+    count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
+  }
+  if ((int64_t)blockIdx.x * WPB * 16 >= count) return;   // the whole block: before the barrier
+  const int NBP = 16 * NBT;
+  const int64_t k0 = (int64_t)blockIdx.y * a.kc, k1 = k0 + a.kc < a.cols ? k0 + a.kc : a.cols;
+  const int kn = (int)(k1 - k0);            // a multiple of 32
+  const int xs = (int)a.kc + 8;             // LDS row stride (halves)
+  {
+    const int q4 = kn / 4;
+    for (int idx = threadIdx.x; idx < NBP * q4; idx += NT) {
+      const int b = idx / q4, q = idx % q4;
+      float4v v = float4v{0.f, 0.f, 0.f, 0.f};
+      if (b < a.B) v = *reinterpret_cast<const float4v*>(a.x + (int64_t)b * a.cols + k0 + 4 * q);
+      half4_t h;
+      h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
+      *reinterpret_cast<half4_t*>(xh + b * xs + 4 * q) = h;
+    }
+  }
+  __syncthreads();
+  const int tile = blockIdx.x * WPB + wave;
+  if ((int64_t)tile * 16 >= count) return;
+  const int g = lane / 16, ml = lane % 16;
+  const int64_t pos = (int64_t)tile * 16 + ml;
+  int64_t row = pos < count ? (a.list ? (int64_t)a.list[pos] : pos) : -1;
+  if (row >= a.n_rows) row = -1;
+  const int64_t rb = a.cols * 2;
+  const uint32_t wbytes = (uint32_t)(a.n_rows * rb);
+  const rsrc_t rW = make_rsrc(a.W, wbytes);
+  const rsrc_t rU = make_rsrc(GATED ? a.Wup : a.W, GATED ? wbytes : 0u);
+  const uint32_t roff = row >= 0 ? (uint32_t)(row * rb + (k0 + 8 * g) * 2) : 0u;
+  constexpr uint32_t kOut = 0xFFFFFFF0u;
+  float4v_t acc[NBT], accu[NBT];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+    acc[t] = float4v_t{0.f, 0.f, 0.f, 0.f};
+    accu[t] = float4v_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int kk = 0; kk < kn; kk += D * 32) {
+    uint4 wv[D], uv[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      const bool in = row >= 0 && kk + 32 * i < kn;
+      const uint32_t o = in ? roff + (uint32_t)((kk + 32 * i) * 2) : kOut;
+      wv[i] = bload16(rW, o);
+      if constexpr (GATED) uv[i] = bload16(rU, o);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+      if (kk + 32 * i < kn) {
+#pragma unroll
+        for (int t = 0; t < NBT; ++t) {
+          const half8_t xb = *reinterpret_cast<const half8_t*>(xh + (16 * t + ml) * xs + kk + 32 * i + 8 * g);
+          acc[t] = mfma16(__builtin_bit_cast(half8_t, wv[i]), xb, acc[t]);
+          if constexpr (GATED) accu[t] = mfma16(__builtin_bit_cast(half8_t, uv[i]), xb, accu[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NBT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t p = (int64_t)tile * 16 + 4 * g + r;
+      if (p < count) {
+        const int64_t o = ((int64_t)blockIdx.y * a.count_max + p) * NBP + 16 * t + ml;
         a.partials[o] = acc[t][r];
         if constexpr (GATED) a.partials[(int64_t)a.ks * a.count_max * NBP + o] = accu[t][r];
       }
@@ -347,6 +453,19 @@ template <int DT>
 hipError_t rowdot_dt(const MmRowArgs& a, hipStream_t s) {
   const int tiles = (int)((a.count_max + 15) / 16);
   const dim3 g((unsigned)((tiles + kMmWaves - 1) / kMmWaves), (unsigned)a.ks), t(kMmThreads);
+  if (mm_row16_used(a)) {
+    const size_t shm = (size_t)16 * a.nbt * (size_t)(a.kc + 8) * 2;
+    const int wpb = r16_waves(a.nbt);
+    const dim3 g((unsigned)((tiles + wpb - 1) / wpb), (unsigned)a.ks), t(wpb * kWave);
+    if (a.nbt == 1) {
+      if (a.gated) hipLaunchKernelGGL((k_mm_rowdot16<1, true>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_rowdot16<1, false>), g, t, shm, s, a);
+    } else {
+      if (a.gated) hipLaunchKernelGGL((k_mm_rowdot16<2, true>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_rowdot16<2, false>), g, t, shm, s, a);
+    }
+    return hipGetLastError();
+  }
   if (a.nbt == 1) {
     if (a.gated) hipLaunchKernelGGL((k_mm_rowdot<DT, 1, true>), g, t, 0, s, a);
     else hipLaunchKernelGGL((k_mm_rowdot<DT, 1, false>), g, t, 0, s, a);
@@ -377,6 +496,22 @@ int mm_row_ks(int dt, int64_t count_max, int64_t cols) {
   int64_t ks = (2048 + tiles - 1) / (tiles > 0 ? tiles : 1);
   const int64_t kmax = cols / (8 * kb);
   ks = ks > kmax ? kmax : ks;
+  return (int)(ks < 1 ? 1 : ks);
+}
+
+bool mm_row16_used(const MmRowArgs& a) {
+  return a.x_f16 && a.dt == PI_F16 && a.cols % 32 == 0 && a.kc <= row16_kcmax(a.nbt, a.gated) && a.kc % 32 == 0;
+}
+
+int mm_row16_ks(int64_t count_max, int64_t cols, int nbt, bool gated) {
+  // the k chunk fits the LDS bound, and about 4096 waves
+  const int64_t kcmax = row16_kcmax(nbt, gated);
+  const int64_t tiles = (count_max + 15) / 16;
+  int64_t ks = (4096 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  const int64_t kmax = cols / 256;          // at least 8 k blocks per wave
+  ks = ks > kmax ? kmax : ks;
+  const int64_t kmin = (cols + kcmax - 1) / kcmax;
+  ks = ks < kmin ? kmin : ks;
   return (int)(ks < 1 ? 1 : ks);
 }
 
