@@ -57,11 +57,16 @@ struct FfnWs {
 bool use_mm_row(int32_t B) { return B >= pi::kMmRowMinBatch; }
 bool use_mm_axpy(int32_t B) { return B >= pi::kMmAxpyMinBatch; }
 // Rows of an activation buffer (h, a): B, or the padded batch 16 * nbt when the
-// matrix-core kernels keep it neuron-major.
+// matrix-core kernels keep it neuron-major (a in fp16 also pads the neurons to 32).
 size_t act_rows(int32_t B) {
   if (!use_mm_row(B)) return (size_t)B;
   const size_t p = (size_t)16 * pi::mm_nbt(B);
   return p > (size_t)B ? p : (size_t)B;
+}
+size_t act_bytes(int32_t B, int32_t n) {
+  const size_t n1 = (size_t)(n > 0 ? n : 1);
+  const size_t f32 = act_rows(B) * n1 * 4, f16 = act_rows(B) * ((n1 + 31) / 32 * 32) * 2;
+  return f32 > f16 ? f32 : f16;
 }
 size_t mm_row_partial_bytes(int32_t B, int64_t rows, int64_t cols, bool gated) {
   if (!use_mm_row(B) || rows <= 0 || cols <= 0) return 0;
@@ -92,7 +97,7 @@ size_t ffn_partial_bytes(int32_t B, int32_t d, int32_t n_g) {
 FfnWs ffn_ws_layout(void* ws, int32_t B, int32_t d, int32_t n_g) {
   Carver c{static_cast<char*>(ws)};
   FfnWs w{};
-  w.a = c.take<float>(act_rows(B) * (size_t)(n_g > 0 ? n_g : 1) * 4);
+  w.a = c.take<float>(act_bytes(B, n_g));
   w.partials = c.take<float>(ffn_partial_bytes(B, d, n_g));
   w.bytes = c.off;
   return w;
@@ -148,7 +153,7 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
   w.pos_slot = c.take<int32_t>(ng * 64 * 4);
   w.pos_a = c.take<float>(ng * 64 * 4);
   w.cnt = c.take<uint32_t>(ng * 4);
-  w.a = c.take<float>(act_rows(B) * (size_t)(n_g > 0 ? n_g : 1) * 4);
+  w.a = c.take<float>(act_bytes(B, n_g));
   const size_t pb = ffn_partial_bytes(B, d, n_g);
   const size_t seg = (size_t)pi::kSegChunks * (size_t)d * 4;
   w.partials = c.take<float>(max3(pb, seg, pred_partial_bytes(B, d, H, N)));
@@ -210,7 +215,7 @@ int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const f
     m.count_dev = nullptr; m.count_max = H; m.a = h; m.a_stride = H; m.a_by_row = 1; m.a_tr = h_tr; m.B = B;
     m.nbt = pi::mm_nbt(B);
     m.row_chunks = pi::mm_axpy_row_chunks(P2.dtype, H, N);
-    m.rows_per_chunk = ((H + m.row_chunks - 1) / m.row_chunks + 15) / 16 * 16;
+    m.rows_per_chunk = pi::mm_axpy_rows_per_chunk(m);
     m.partials = partials;
     st = hip_status(pi::launch_mm_axpy(m, s));
     chunks = m.row_chunks;
@@ -351,6 +356,7 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
   const bool mm1 = use_mm_row(B) && pi::mm_rowdot_supported(W1.dtype, n_g, d);
   const bool mm2 = use_mm_axpy(B) && n_g > 0 && pi::mm_axpy_supported(W2.dtype, n_g, d);
   const bool a_tr = mm1 && mm2;      // a kept neuron-major between the two matrix-core GEMMs
+  const bool a16 = a_tr && pi::mm_axpy16_supported(W2.dtype, d);   // ... in fp16, for the fp16 FC2
   if (stages & PI_STAGE_FC1) {
     if (mm1) {
       pi::MmRowArgs m{};
@@ -361,7 +367,7 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
       m.ks = m.x_f16 ? pi::mm_row16_ks(n_g, d, m.nbt, gated) : pi::mm_row_ks(W1.dtype, n_g, d);
       m.kc = pi::mm_row_kc(W1.dtype, d, m.ks);
       m.partials = partials; m.bias = b1.data; m.bias_dt = b1.dtype; m.relu = 1; m.out = a; m.out_tr = a_tr;
-      m.out_stride = a_tr ? 16 * m.nbt : (n_g > 0 ? n_g : 1);
+      m.out_h8 = a16; m.out_stride = a_tr ? 16 * m.nbt : (n_g > 0 ? n_g : 1);
       st = n_g > 0 ? hip_status(pi::launch_mm_rowdot(m, s)) : PI_OK;
     } else if (B == 1 && pi::b1_supported(W1.dtype, d)) {
       pi::B1Gemv g{};
@@ -386,9 +392,8 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
     if (mm2) {
       pi::MmAxpyArgs m{};
       m.W = W2.data; m.Ws = W2.scales; m.dt = W2.dtype; m.cols = d; m.n_rows = n_g; m.list = A_g; m.count_dev = K;
-      m.count_max = n_g; m.a = a; m.a_stride = n_g; m.a_by_row = 0; m.a_tr = a_tr; m.B = B; m.nbt = pi::mm_nbt(B);
-      m.row_chunks = chunks2;
-      m.rows_per_chunk = ((n_g + chunks2 - 1) / chunks2 + 15) / 16 * 16;
+      m.count_max = n_g; m.a = a; m.a_stride = n_g; m.a_by_row = 0; m.a_tr = a_tr; m.a_h8 = a16; m.B = B;
+      m.nbt = pi::mm_nbt(B); m.row_chunks = chunks2; m.rows_per_chunk = pi::mm_axpy_rows_per_chunk(m);
       m.partials = partials;
       if ((st = hip_status(pi::launch_mm_axpy(m, s))) != PI_OK) return st;
     } else {

@@ -213,6 +213,8 @@ struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b
   float* out;                   // [B x out_stride], column = position; or, with out_tr,
   int64_t out_stride;           // [count_max x 16 nbt] neuron-major (zeros past B)
   int out_tr;
+  int out_h8;                   // with out_tr: fp16 [pos / 8][16 nbt][8] (zeros past B and up to the next
+                                // multiple of 32 positions), the activations of the fp16 axpy
   int x_f16;                    // fp16 weights: x may be rounded to fp16 (fp16 matrix cores; FC1 only)
 };
 struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's rows j of a[b, j] W[row(j), c]
@@ -228,6 +230,7 @@ struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's 
   int64_t a_stride;             // idx = a_by_row ? row : j
   int a_by_row;
   int a_tr;
+  int a_h8;                     // fp16 weights, a in the out_h8 layout: the fp16 matrix cores (FC2)
   int B;
   int nbt;
   int64_t rows_per_chunk;       // a multiple of 16
@@ -244,6 +247,8 @@ int mm_axpy_col_chunks(int dt, int64_t cols);
 int mm_axpy_row_chunks(int dt, int64_t count_max, int64_t cols);
 bool mm_rowdot_supported(int dt, int64_t rows, int64_t cols);
 bool mm_axpy_supported(int dt, int64_t rows, int64_t cols);
+bool mm_axpy16_supported(int dt, int64_t cols);
+int64_t mm_axpy_rows_per_chunk(const MmAxpyArgs& a);   // from count_max and row_chunks
 hipError_t launch_mm_rowdot(const MmRowArgs& a, hipStream_t s);   // the GEMM, then the finish
 hipError_t launch_mm_axpy(const MmAxpyArgs& a, hipStream_t s);
 

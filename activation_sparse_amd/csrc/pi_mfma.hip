@@ -304,10 +304,17 @@ __global__ __launch_bounds__(256) void k_mm_finish_tr(MmRowArgs a) {
     const int64_t kd = *a.count_dev;
     count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
   }
-  const int64_t n = count * NBP;
+  // the fp16 layout is written up to the next multiple of 32 positions (zeros), so
+  // that the axpy's 8-position vectors never hold stale values
+  const int64_t npos = a.out_h8 ? (count + 31) / 32 * 32 : count;
+  const int64_t n = npos * NBP;
   for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t pos = t / NBP;
     const int b = (int)(t % NBP);
+    if (pos >= count) {
+      reinterpret_cast<_Float16*>(a.out)[((pos / 8) * NBP + b) * 8 + pos % 8] = (_Float16)0.f;
+      continue;
+    }
     float z = 0.f, u = 0.f;
     for (int k0 = 0; k0 < a.ks; k0 += 8) {
       float p[8], q[8];
@@ -328,7 +335,8 @@ __global__ __launch_bounds__(256) void k_mm_finish_tr(MmRowArgs a) {
     if (a.bias && ok) z += load_bias(a.bias, a.bias_dt, row);
     if (a.relu) z = z > 0.f ? z : 0.f;
     if constexpr (GATED) z *= u;
-    a.out[pos * NBP + b] = ok ? z : 0.f;
+    if (a.out_h8) reinterpret_cast<_Float16*>(a.out)[((pos / 8) * NBP + b) * 8 + pos % 8] = (_Float16)(ok ? z : 0.f);
+    else a.out[pos * NBP + b] = ok ? z : 0.f;
   }
 }
 
@@ -449,6 +457,119 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy(MmAxpyArgs a) {
   }
 }
 
+// fp16 weights, fp16 activations (FC2 of the batched path): one
+// v_mfma_f32_16x16x32_f16 sums 32 listed rows: A = a (batch row lane % 16,
+// rows 8 g .. 8 g + 7, one 16-byte vector of the fp16 activation layout),
+// B = W (the same 8 rows at column lane % 16).  A W column is not contiguous, so
+// each row step (32 rows x the wave's 128 columns) is read as eight 4-row x
+// 256-byte loads into the wave's LDS tile and the B operands are gathered from
+// it 2 bytes at a time.  The tile's 16-byte chunks are stored at chunk
+// c ^ 2 ((row / 8) & 3): the four lane groups, reading rows 8 g + i, then fall
+// in different banks.  The block's four waves take interleaved row steps and
+// are summed in LDS in wave order.
+template <int NBT>
+__global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
+  constexpr int DS = 2;                     // row steps in flight per wave
+  __shared__ uint4 wt[kMmWaves][32 * 16];
+  __shared__ float red[NBT * 8 * 4][kWave];
+  extern __shared__ int32_t ax_rows[];     // the chunk's row ids (rows_per_chunk entries)
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  const int g = lane / 16, nl = lane % 16;
+  const int cchunk = blockIdx.x, rchunk = blockIdx.y;
+  int64_t count = a.count_max;
+  if (a.list) {
+    const int64_t kd = *a.count_dev;
+    count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
+  }
+  const int64_t r0 = (int64_t)rchunk * a.rows_per_chunk;
+  int64_t r1 = r0 + a.rows_per_chunk;
+  r1 = r1 < count ? r1 : count;
+  for (int64_t j = r0 + threadIdx.x; j < r1; j += kMmThreads) {
+    const int64_t row = a.list ? (int64_t)a.list[j] : j;
+    ax_rows[j - r0] = (row >= 0 && row < a.n_rows) ? (int32_t)row : -1;
+  }
+  __syncthreads();
+  const int NBP = 16 * NBT;
+  const int64_t rb = a.cols * 2;
+  const int nvec = (int)(rb / 16);
+  const int v = cchunk * 16 + nl;           // this lane's 16-byte chunk of each row it loads
+  const bool vin = v < nvec;
+  const rsrc_t rW = make_rsrc(a.W, (uint32_t)(a.n_rows * rb));
+  const rsrc_t rA = make_rsrc(a.a, (uint32_t)((a.count_max + 31) / 32 * 32 * NBP * 2));
+  constexpr uint32_t kOut = 0xFFFFFFF0u;
+  uint4* tw = wt[wave];
+  const _Float16* th = reinterpret_cast<const _Float16*>(wt[wave]);
+  float4v_t acc[NBT][8];
+#pragma unroll
+  for (int t = 0; t < NBT; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) acc[t][s2] = float4v_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int kBlockStep = 32 * kMmWaves;
+  for (int64_t j0 = r0 + 32 * wave; j0 < r1; j0 += (int64_t)kBlockStep * DS) {
+    uint4 wv[DS][8], av[DS][NBT];
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      const int64_t js = j0 + (int64_t)kBlockStep * st;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t j = js + 4 * i + g;
+        const int32_t row = j < r1 ? ax_rows[j - r0] : -1;
+        wv[st][i] = bload16(rW, row >= 0 && vin ? (uint32_t)(row * rb) + (uint32_t)v * 16u : kOut);
+      }
+#pragma unroll
+      for (int t = 0; t < NBT; ++t) {
+        const int64_t jv = js + 8 * g;      // the lane's 8 rows (positions), a multiple of 8
+        av[st][t] = bload16(rA, jv < r1 ? (uint32_t)(((jv / 8) * NBP + 16 * t + nl) * 16) : kOut);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      if (j0 + (int64_t)kBlockStep * st < r1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int lr = 4 * i + g;
+          tw[lr * 16 + (nl ^ (2 * ((lr >> 3) & 3)))] = wv[st][i];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2) {
+          // column 16 s2 + nl of rows 8 g .. 8 g + 7: chunk 2 s2 + nl / 8, swizzled by 2 g
+          const int pc = (2 * s2 + nl / 8) ^ (2 * g);
+          half8_t wb;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) wb[i] = th[((8 * g + i) * 16 + pc) * 8 + nl % 8];
+#pragma unroll
+          for (int t = 0; t < NBT; ++t) acc[t][s2] = mfma16(__builtin_bit_cast(half8_t, av[st][t]), wb, acc[t][s2]);
+        }
+      }
+    }
+  }
+  // sum the four waves in wave order; lane holds D[m = 4g + r][n = nl] of each (t, s2)
+  for (int w = 0; w < kMmWaves; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int t = 0; t < NBT; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float* cell = &red[(t * 8 + s2) * 4 + r][lane];
+            *cell = w == 0 ? acc[t][s2][r] : *cell + acc[t][s2][r];
+          }
+    }
+    __syncthreads();
+  }
+  const int64_t cols = a.cols;
+  for (int q = threadIdx.x; q < NBT * 8 * 4 * kWave; q += kMmThreads) {
+    const int ln = q % kWave, idx = q / kWave;
+    const int r = idx % 4, ts = idx / 4, s2 = ts % 8, t = ts / 8;
+    const int b = 16 * t + 4 * (ln / 16) + r;
+    const int64_t c = (int64_t)cchunk * 128 + 16 * s2 + ln % 16;
+    if (b < a.B && c < cols) a.partials[((int64_t)rchunk * a.B + b) * cols + c] = red[idx][ln];
+  }
+}
+
 template <int DT>
 hipError_t rowdot_dt(const MmRowArgs& a, hipStream_t s) {
   const int tiles = (int)((a.count_max + 15) / 16);
@@ -480,6 +601,11 @@ template <int DT>
 hipError_t axpy_dt(const MmAxpyArgs& a, hipStream_t s) {
   const dim3 g((unsigned)mm_axpy_col_chunks(a.dt, a.cols), (unsigned)a.row_chunks), t(kMmThreads);
   const size_t shm = (size_t)a.rows_per_chunk * 4;
+  if (DT == 1 && a.a_h8) {
+    if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1>), g, t, shm, s, a);
+    else hipLaunchKernelGGL((k_mm_axpy16<2>), g, t, shm, s, a);
+    return hipGetLastError();
+  }
   if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy<DT, 1>), g, t, shm, s, a);
   else hipLaunchKernelGGL((k_mm_axpy<DT, 2>), g, t, shm, s, a);
   return hipGetLastError();
@@ -539,6 +665,14 @@ bool mm_rowdot_supported(int dt, int64_t rows, int64_t cols) {
   if (dt < 0 || dt > 2) return false;
   const int64_t kb = 4 * (dt == 0 ? 4 : dt == 1 ? 8 : 32);
   return cols % kb == 0 && rows * row_bytes(dt, cols) < ((int64_t)1 << 31);
+}
+
+bool mm_axpy16_supported(int dt, int64_t cols) { return dt == PI_F16 && cols % 8 == 0; }
+
+int64_t mm_axpy_rows_per_chunk(const MmAxpyArgs& a) {
+  // a multiple of 16 rows (128 for the fp16 kernel, whose block step is 128 rows)
+  const int64_t q = a.a_h8 ? 128 : 16;
+  return ((a.count_max + a.row_chunks - 1) / a.row_chunks + q - 1) / q * q;
 }
 
 bool mm_axpy_supported(int dt, int64_t rows, int64_t cols) {
