@@ -68,6 +68,14 @@ size_t act_bytes(int32_t B, int32_t n) {
   const size_t f32 = act_rows(B) * n1 * 4, f16 = act_rows(B) * ((n1 + 31) / 32 * 32) * 2;
   return f32 > f16 ? f32 : f16;
 }
+// h: [B x H] fp32, neuron-major fp32, or two fp16 parts (hi, then lo) in the fp16 layout
+size_t h_bytes(int32_t B, int32_t H) {
+  const size_t f32 = act_rows(B) * (size_t)H * 4, f16 = 2 * act_rows(B) * (((size_t)H + 31) / 32 * 32) * 2;
+  return f32 > f16 ? f32 : f16;
+}
+float* h_lo_part(float* h, int32_t B, int32_t H) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(h) + act_rows(B) * (((size_t)H + 31) / 32 * 32) * 2);
+}
 size_t mm_row_partial_bytes(int32_t B, int64_t rows, int64_t cols, bool gated) {
   if (!use_mm_row(B) || rows <= 0 || cols <= 0) return 0;
   int ks = pi::mm_row16_ks(rows, cols, pi::mm_nbt(B), gated);
@@ -145,7 +153,7 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
   Carver c{static_cast<char*>(ws)};
   LayerWs w{};
   const size_t ng = n_groups64(N);
-  w.h = c.take<float>(act_rows(B) * H * 4);
+  w.h = c.take<float>(h_bytes(B, H));
   w.logits = c.take<float>((size_t)B * N * 4);
   w.mask = c.take<uint32_t>(table_words(N) * 4);
   w.seg_slot = c.take<int32_t>(ng * 64 * 4);
@@ -164,14 +172,19 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
 // The predictor's hidden layer, h[b,m] = max(0, P1[m].x_b + c1[m]): batch 1 on the
 // register-x GEMV, batches of kMmRowMinBatch and more on the matrix cores (split-K
 // partials in `partials`), others on the LDS-x row-dot kernel.
-// h kept neuron-major ([H x 16 nbt]) between the two matrix-core predictor layers.
-bool h_neuron_major(int32_t B, int32_t d, int32_t H, int32_t N, const pi_matrix& P1, const pi_matrix& P2) {
-  return use_mm_row(B) && use_mm_axpy(B) && pi::mm_rowdot_supported(P1.dtype, H, d) &&
-         pi::mm_axpy_supported(P2.dtype, H, N);
+// Layout of h between the two predictor layers: 0 [B x H]; 1 neuron-major fp32
+// ([H x 16 nbt]) between the two matrix-core layers; 2 two fp16 parts in the fp16
+// layout when the output layer runs on the fp16 matrix cores (fp16 P2).
+int h_layout(int32_t B, int32_t d, int32_t H, int32_t N, const pi_matrix& P1, const pi_matrix& P2) {
+  if (!(use_mm_row(B) && use_mm_axpy(B) && pi::mm_rowdot_supported(P1.dtype, H, d) &&
+        pi::mm_axpy_supported(P2.dtype, H, N)))
+    return 0;
+  return pi::mm_axpy16_supported(P2.dtype, N) ? 2 : 1;
 }
 
 int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* x, const pi_matrix& P1,
-                   const pi_vector& c1, float* h, float* partials, bool h_tr) {
+                   const pi_vector& c1, float* h, float* partials, int h_lay) {
+  const bool h_tr = h_lay != 0;
   if (B == 1 && pi::b1_supported(P1.dtype, d)) {
     pi::B1Gemv g{};
     g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
@@ -184,6 +197,7 @@ int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* 
     m.count_dev = nullptr; m.count_max = H; m.x = x; m.B = B; m.nbt = pi::mm_nbt(B);
     m.ks = pi::mm_row_ks(P1.dtype, H, d); m.kc = pi::mm_row_kc(P1.dtype, d, m.ks); m.partials = partials;
     m.bias = c1.data; m.bias_dt = c1.dtype; m.relu = 1; m.out = h; m.out_tr = h_tr;
+    m.out_h8 = h_lay == 2; m.out_lo = h_lay == 2 ? h_lo_part(h, B, H) : nullptr;
     m.out_stride = h_tr ? 16 * m.nbt : H;
     return hip_status(pi::launch_mm_rowdot(m, s));
   }
@@ -201,7 +215,7 @@ int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* 
 // sum with c2, then the words from the stored logits.
 int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const float* h, const pi_matrix& P2,
                          const pi_vector& c2, float tau, float* logits, uint32_t* mask, float* partials,
-                         int32_t* rows_read = nullptr, bool h_tr = false) {
+                         int32_t* rows_read = nullptr, int h_lay = 0) {
   if (!out_layer_needs_partials(B, H, N)) {
     pi::PredFc1Args a{};
     a.P2 = P2.data; a.P2s = P2.scales; a.pdt = P2.dtype; a.H = H; a.N = N; a.h = h;
@@ -212,7 +226,8 @@ int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const f
   if (use_mm_axpy(B) && pi::mm_axpy_supported(P2.dtype, H, N)) {
     pi::MmAxpyArgs m{};
     m.W = P2.data; m.Ws = P2.scales; m.dt = P2.dtype; m.cols = N; m.n_rows = H; m.list = nullptr;
-    m.count_dev = nullptr; m.count_max = H; m.a = h; m.a_stride = H; m.a_by_row = 1; m.a_tr = h_tr; m.B = B;
+    m.count_dev = nullptr; m.count_max = H; m.a = h; m.a_stride = H; m.a_by_row = 1; m.a_tr = h_lay != 0; m.B = B;
+    m.a_h8 = h_lay == 2; m.a_lo = h_lay == 2 ? h_lo_part(const_cast<float*>(h), B, H) : nullptr;
     m.nbt = pi::mm_nbt(B);
     m.row_chunks = pi::mm_axpy_row_chunks(P2.dtype, H, N);
     m.rows_per_chunk = pi::mm_axpy_rows_per_chunk(m);
@@ -257,7 +272,7 @@ size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N
   if (B < 1) B = 1;
   switch (op) {
     case PI_OP_PREDICT:
-      return H > 0 && N > 0 && d > 0 ? align_up(act_rows(B) * (size_t)H * 4) + pred_partial_bytes(B, d, H, N) : 0;
+      return H > 0 && N > 0 && d > 0 ? align_up(h_bytes(B, H)) + pred_partial_bytes(B, d, H, N) : 0;
     case PI_OP_PREDICT_OUTPUT: return H > 0 && N > 0 ? out_partials_bytes(B, H, N) : 0;
     case PI_OP_SPARSE_FFN:
       return d > 0 ? ffn_ws_layout(nullptr, B, d, n_g).bytes : 0;
@@ -297,11 +312,11 @@ int pi_predict(void* stream, int32_t B, int32_t d, int32_t H, int32_t N, const f
   if (ws_bytes < pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0)) return PI_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* h = static_cast<float*>(ws);
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(act_rows(B) * (size_t)H * 4));
-  const bool h_tr = h_neuron_major(B, d, H, N, P1, P2);
-  const int st = enqueue_hidden(s, B, d, H, x, P1, c1, h, partials, h_tr);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(h_bytes(B, H)));
+  const int h_lay = h_layout(B, d, H, N, P1, P2);
+  const int st = enqueue_hidden(s, B, d, H, x, P1, c1, h, partials, h_lay);
   if (st != PI_OK) return st;
-  return enqueue_output_layer(s, B, H, N, h, P2, c2, 0.f, logits, nullptr, partials, nullptr, h_tr);
+  return enqueue_output_layer(s, B, H, N, h, P2, c2, 0.f, logits, nullptr, partials, nullptr, h_lay);
 }
 
 int pi_predict_output(void* stream, int32_t B, int32_t H, int32_t N, const float* h, pi_matrix P2, pi_vector c2,
@@ -468,8 +483,8 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
 
   if ((st = record(0)) != PI_OK) return st;
   // predictor hidden layer
-  const bool h_tr = h_neuron_major(B, d, H, N, L->P1, L->P2);
-  if (want(PI_STAGE_HIDDEN) && (st = enqueue_hidden(s, B, d, H, x, L->P1, L->c1, w.h, w.partials, h_tr)) != PI_OK)
+  const int h_lay = h_layout(B, d, H, N, L->P1, L->P2);
+  if (want(PI_STAGE_HIDDEN) && (st = enqueue_hidden(s, B, d, H, x, L->P1, L->c1, w.h, w.partials, h_lay)) != PI_OK)
     return st;
   if ((st = record(1)) != PI_OK) return st;
 
@@ -508,7 +523,7 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
   }
   // any batch: output layer + activation words, the lists, then FC1 / FC2 / ordered sum over the list
   if (want(PI_STAGE_OUTPUT)) {
-    if ((st = enqueue_output_layer(s, B, H, N, w.h, L->P2, L->c2, tau, lg, w.mask, w.partials, rows_read, h_tr)) !=
+    if ((st = enqueue_output_layer(s, B, H, N, w.h, L->P2, L->c2, tau, lg, w.mask, w.partials, rows_read, h_lay)) !=
         PI_OK)
       return st;
     pi::ListCtx lc{};

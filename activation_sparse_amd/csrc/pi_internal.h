@@ -215,6 +215,7 @@ struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b
   int out_tr;
   int out_h8;                   // with out_tr: fp16 [pos / 8][16 nbt][8] (zeros past B and up to the next
                                 // multiple of 32 positions), the activations of the fp16 axpy
+  float* out_lo;                // with out_h8, optional: the same layout holding fp16(z - fp16(z))
   int x_f16;                    // fp16 weights: x may be rounded to fp16 (fp16 matrix cores; FC1 only)
 };
 struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's rows j of a[b, j] W[row(j), c]
@@ -231,6 +232,7 @@ struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's 
   int a_by_row;
   int a_tr;
   int a_h8;                     // fp16 weights, a in the out_h8 layout: the fp16 matrix cores (FC2)
+  const float* a_lo;            // with a_h8, optional: the low fp16 parts (a = hi + lo, ~22 bits)
   int B;
   int nbt;
   int64_t rows_per_chunk;       // a multiple of 16

@@ -311,8 +311,10 @@ __global__ __launch_bounds__(256) void k_mm_finish_tr(MmRowArgs a) {
   for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t pos = t / NBP;
     const int b = (int)(t % NBP);
+    const int64_t h8 = ((pos / 8) * NBP + b) * 8 + pos % 8;
     if (pos >= count) {
-      reinterpret_cast<_Float16*>(a.out)[((pos / 8) * NBP + b) * 8 + pos % 8] = (_Float16)0.f;
+      reinterpret_cast<_Float16*>(a.out)[h8] = (_Float16)0.f;
+      if (a.out_lo) reinterpret_cast<_Float16*>(a.out_lo)[h8] = (_Float16)0.f;
       continue;
     }
     float z = 0.f, u = 0.f;
@@ -335,8 +337,14 @@ __global__ __launch_bounds__(256) void k_mm_finish_tr(MmRowArgs a) {
     if (a.bias && ok) z += load_bias(a.bias, a.bias_dt, row);
     if (a.relu) z = z > 0.f ? z : 0.f;
     if constexpr (GATED) z *= u;
-    if (a.out_h8) reinterpret_cast<_Float16*>(a.out)[((pos / 8) * NBP + b) * 8 + pos % 8] = (_Float16)(ok ? z : 0.f);
-    else a.out[pos * NBP + b] = ok ? z : 0.f;
+    if (a.out_h8) {
+      const float v = ok ? z : 0.f;
+      const _Float16 hi = (_Float16)v;
+      reinterpret_cast<_Float16*>(a.out)[h8] = hi;
+      if (a.out_lo) reinterpret_cast<_Float16*>(a.out_lo)[h8] = (_Float16)(v - (float)hi);
+    } else {
+      a.out[pos * NBP + b] = ok ? z : 0.f;
+    }
   }
 }
 
@@ -466,8 +474,10 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy(MmAxpyArgs a) {
 // it 2 bytes at a time.  The tile's 16-byte chunks are stored at chunk
 // c ^ 2 ((row / 8) & 3): the four lane groups, reading rows 8 g + i, then fall
 // in different banks.  The block's four waves take interleaved row steps and
-// are summed in LDS in wave order.
-template <int NBT>
+// are summed in LDS in wave order.  With LO, a = hi + lo in two fp16 parts
+// (about 22 bits): two exact products per weight, for the predictor's output
+// layer, whose logits keep near-fp32 precision.
+template <int NBT, bool LO>
 __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
   constexpr int DS = 2;                     // row steps in flight per wave
   __shared__ uint4 wt[kMmWaves][32 * 16];
@@ -496,7 +506,9 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
   const int v = cchunk * 16 + nl;           // this lane's 16-byte chunk of each row it loads
   const bool vin = v < nvec;
   const rsrc_t rW = make_rsrc(a.W, (uint32_t)(a.n_rows * rb));
-  const rsrc_t rA = make_rsrc(a.a, (uint32_t)((a.count_max + 31) / 32 * 32 * NBP * 2));
+  const uint32_t abytes = (uint32_t)((a.count_max + 31) / 32 * 32 * NBP * 2);
+  const rsrc_t rA = make_rsrc(a.a, abytes);
+  const rsrc_t rL = make_rsrc(LO ? (const void*)a.a_lo : (const void*)a.a, LO ? abytes : 0u);
   constexpr uint32_t kOut = 0xFFFFFFF0u;
   uint4* tw = wt[wave];
   const _Float16* th = reinterpret_cast<const _Float16*>(wt[wave]);
@@ -507,7 +519,7 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
     for (int s2 = 0; s2 < 8; ++s2) acc[t][s2] = float4v_t{0.f, 0.f, 0.f, 0.f};
   constexpr int kBlockStep = 32 * kMmWaves;
   for (int64_t j0 = r0 + 32 * wave; j0 < r1; j0 += (int64_t)kBlockStep * DS) {
-    uint4 wv[DS][8], av[DS][NBT];
+    uint4 wv[DS][8], av[DS][NBT], al[DS][NBT];
 #pragma unroll
     for (int st = 0; st < DS; ++st) {
       const int64_t js = j0 + (int64_t)kBlockStep * st;
@@ -520,7 +532,9 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
 #pragma unroll
       for (int t = 0; t < NBT; ++t) {
         const int64_t jv = js + 8 * g;      // the lane's 8 rows (positions), a multiple of 8
-        av[st][t] = bload16(rA, jv < r1 ? (uint32_t)(((jv / 8) * NBP + 16 * t + nl) * 16) : kOut);
+        const uint32_t ao = jv < r1 ? (uint32_t)(((jv / 8) * NBP + 16 * t + nl) * 16) : kOut;
+        av[st][t] = bload16(rA, ao);
+        if constexpr (LO) al[st][t] = bload16(rL, ao);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -540,7 +554,10 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) wb[i] = th[((8 * g + i) * 16 + pc) * 8 + nl % 8];
 #pragma unroll
-          for (int t = 0; t < NBT; ++t) acc[t][s2] = mfma16(__builtin_bit_cast(half8_t, av[st][t]), wb, acc[t][s2]);
+          for (int t = 0; t < NBT; ++t) {
+            acc[t][s2] = mfma16(__builtin_bit_cast(half8_t, av[st][t]), wb, acc[t][s2]);
+            if constexpr (LO) acc[t][s2] = mfma16(__builtin_bit_cast(half8_t, al[st][t]), wb, acc[t][s2]);
+          }
         }
       }
     }
@@ -602,8 +619,13 @@ hipError_t axpy_dt(const MmAxpyArgs& a, hipStream_t s) {
   const dim3 g((unsigned)mm_axpy_col_chunks(a.dt, a.cols), (unsigned)a.row_chunks), t(kMmThreads);
   const size_t shm = (size_t)a.rows_per_chunk * 4;
   if (DT == 1 && a.a_h8) {
-    if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1>), g, t, shm, s, a);
-    else hipLaunchKernelGGL((k_mm_axpy16<2>), g, t, shm, s, a);
+    if (a.a_lo) {
+      if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1, true>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_axpy16<2, true>), g, t, shm, s, a);
+    } else {
+      if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1, false>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_axpy16<2, false>), g, t, shm, s, a);
+    }
     return hipGetLastError();
   }
   if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy<DT, 1>), g, t, shm, s, a);
