@@ -245,8 +245,7 @@ int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const f
   pi::ReduceArgs r{};
   r.partials = partials; r.chunks = chunks; r.B = B; r.d = N; r.y = logits;
   r.y_c = nullptr; r.K_c = nullptr; r.b2 = c2.data; r.b2_dt = c2.dtype;
-  if ((st = hip_status(pi::launch_reduce(r, s))) != PI_OK) return st;
-  return mask ? hip_status(pi::launch_mask(B, N, logits, tau, mask, s)) : PI_OK;
+  return hip_status(mask ? pi::launch_reduce_mask(r, tau, mask, s) : pi::launch_reduce(r, s));
 }
 
 }  // namespace

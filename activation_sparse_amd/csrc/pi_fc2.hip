@@ -307,6 +307,48 @@ __global__ __launch_bounds__(kWave) void k_reduce_y(ReduceYArgs r) {
   if (r.b2) sum += bb;
   r.y[t] = sum;
 }
+// The output layer's ordered sum (as k_reduce: chunks in order, then + c2) fused
+// with the activation decision: one wave per 64 ids, every batch row's logit
+// stored, and the union over the batch written as the group's two words.
+__global__ __launch_bounds__(kWave) void k_reduce_mask(ReduceArgs r, float tau, uint32_t* mask) {
+  const int lane = threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * kWave + lane;
+  const int64_t N = r.d;
+  const bool in = i < N;
+  const float cb = (r.b2 && in) ? load_bias(r.b2, r.b2_dt, i) : 0.f;
+  bool f = false;
+  for (int b0 = 0; b0 < r.B; b0 += 4) {
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < r.chunks; c0 += 8) {
+      float p[4][8];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          p[bb][c] = (in && b0 + bb < r.B && c0 + c < r.chunks)
+                         ? r.partials[((int64_t)(c0 + c) * r.B + b0 + bb) * N + i] : 0.f;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sum[bb] += p[bb][c];
+    }
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      if (in && b0 + bb < r.B) {
+        float z = sum[bb];
+        if (r.b2) z += cb;
+        r.y[(int64_t)(b0 + bb) * N + i] = z;
+        f = f || z > tau;
+      }
+    }
+  }
+  const uint64_t M = __ballot(f);
+  if (lane == 0) {
+    mask[2 * blockIdx.x] = (uint32_t)M;
+    mask[2 * blockIdx.x + 1] = (uint32_t)(M >> 32);
+  }
+}
+
 template <int DT>
 hipError_t fc2_dt(const Fc2Args& a, hipStream_t s) {
   const dim3 g((unsigned)fc2_tiles(DT, a.d), (unsigned)fc2_chunks(a.B)), t(kT);
@@ -353,6 +395,11 @@ hipError_t launch_fc2_seg(const Fc2SegArgs& a, hipStream_t s) {
 
 hipError_t launch_reduce_y(const ReduceYArgs& r, hipStream_t s) {
   hipLaunchKernelGGL(k_reduce_y, dim3((unsigned)((r.d + kWave - 1) / kWave)), dim3(kWave), 0, s, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_mask(const ReduceArgs& r, float tau, uint32_t* mask, hipStream_t s) {
+  hipLaunchKernelGGL(k_reduce_mask, dim3((unsigned)((r.d + kWave - 1) / kWave)), dim3(kWave), 0, s, r, tau, mask);
   return hipGetLastError();
 }
 

@@ -180,20 +180,6 @@ __global__ __launch_bounds__(kThreads) void k_merge(int64_t n, int d, float* y, 
 }
 
 // Union activation words from stored logits [B x N]: one wave per 64 ids.
-__global__ __launch_bounds__(kWave) void k_mask(int B, int N, const float* __restrict__ logits, float tau,
-                                                 uint32_t* __restrict__ mask) {
-  const int lane = threadIdx.x;
-  const int64_t r = (int64_t)blockIdx.x * 64 + lane;
-  bool f = false;
-  if (r < N)
-    for (int b = 0; b < B; ++b) f = f || (logits[(int64_t)b * N + r] > tau);
-  const uint64_t M = __ballot(f);
-  if (lane == 0) {
-    mask[2 * blockIdx.x] = (uint32_t)M;
-    mask[2 * blockIdx.x + 1] = (uint32_t)(M >> 32);
-  }
-}
-
 // Lists from activation words + prepared table; each block writes a strided
 // share of A_g and A_c, block 0 the counts.
 __global__ __launch_bounds__(kThreads) void k_list(ListCtx c) {
@@ -260,11 +246,6 @@ hipError_t launch_compact(int B, int N, const float* logits, float tau, const in
   const int blocks = T_c ? 2 : 1;
   hipLaunchKernelGGL(k_compact, dim3(blocks), dim3(kCompactThreads), 0, s, B, N, logits, tau, T_g, n_g, A_g, K,
                      T_c, n_c, A_c, K_c);
-  return hipGetLastError();
-}
-
-hipError_t launch_mask(int B, int N, const float* logits, float tau, uint32_t* mask, hipStream_t s) {
-  hipLaunchKernelGGL(k_mask, dim3((unsigned)((N + 63) / 64)), dim3(kWave), 0, s, B, N, logits, tau, mask);
   return hipGetLastError();
 }
 

@@ -140,8 +140,7 @@ struct ReduceYArgs {
 hipError_t launch_fc2_seg(const Fc2SegArgs& a, hipStream_t s);
 hipError_t launch_reduce_y(const ReduceYArgs& r, hipStream_t s);
 
-// Activation words from stored logits (union over the batch), and the lists from them.
-hipError_t launch_mask(int B, int N, const float* logits, float tau, uint32_t* mask, hipStream_t s);
+// The lists from the activation words.
 hipError_t launch_list(const ListCtx& c, int n_g, hipStream_t s);
 
 // Neuron-major axpy over listed rows: out[b,:] += a[b, j] * W[list[j], :]
@@ -177,6 +176,8 @@ int fc2_tiles(int dt, int64_t d);
 int fc2_chunks(int B);           // row chunks of FC2 for batch B (partials: chunks x B x d floats)
 hipError_t launch_fc2(const Fc2Args& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& r, hipStream_t s);
+// The same sum for the logits (no merge), with the activation words (2 per 64 ids) of the union over B.
+hipError_t launch_reduce_mask(const ReduceArgs& r, float tau, uint32_t* mask, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 // stats[0] = rows0 (unless negative), stats[1] = *K1 (rows read by the separate kernels).
 hipError_t launch_rows_read(int32_t* stats, int32_t rows0, const int32_t* K1, hipStream_t s);
