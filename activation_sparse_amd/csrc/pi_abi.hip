@@ -230,8 +230,14 @@ int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const f
     m.a_h8 = h_lay == 2; m.a_lo = h_lay == 2 ? h_lo_part(const_cast<float*>(h), B, H) : nullptr;
     m.nbt = pi::mm_nbt(B);
     m.row_chunks = pi::mm_axpy_row_chunks(P2.dtype, H, N);
-    m.rows_per_chunk = pi::mm_axpy_rows_per_chunk(m);
     m.partials = partials;
+    if (m.a_h8) {
+      // every hidden unit in one block per 128 logits: logits, c2 and the words in the same launch
+      m.row_chunks = 1; m.rows_per_chunk = pi::mm_axpy_rows_per_chunk(m);
+      m.final_out = logits; m.bias = c2.data; m.bias_dt = c2.dtype; m.tau = tau; m.mask = mask;
+      return hip_status(pi::launch_mm_axpy(m, s));
+    }
+    m.rows_per_chunk = pi::mm_axpy_rows_per_chunk(m);
     st = hip_status(pi::launch_mm_axpy(m, s));
     chunks = m.row_chunks;
   } else {

@@ -239,6 +239,13 @@ struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's 
   int64_t rows_per_chunk;       // a multiple of 16
   int row_chunks;               // mm_axpy_row_chunks
   float* partials;              // [row_chunks x B x cols]
+  // the fp16 kernel with one row chunk: out[b, c] = 0 + sum + bias[c] written directly
+  // (no partials), and with mask the words of the union over b of out[b, c] > tau (2 per 64 columns)
+  float* final_out;             // [B x cols], or NULL
+  const void* bias;
+  int bias_dt;
+  float tau;
+  uint32_t* mask;
 };
 int mm_nbt(int B);
 int mm_row_ks(int dt, int64_t count_max, int64_t cols);

@@ -578,6 +578,32 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
     __syncthreads();
   }
   const int64_t cols = a.cols;
+  if (a.final_out) {
+    // one row chunk: the whole sum is here.  Thread cc of the block's first two
+    // waves takes column c0 + cc over every batch row, so each wave's ballot is
+    // the union word of one 64-column group.
+    if (threadIdx.x < 128) {
+      const int cc = threadIdx.x, s2 = cc / 16, n = cc % 16;
+      const int64_t c = (int64_t)cchunk * 128 + cc;
+      const bool cin = c < cols;
+      const float cb = (a.bias && cin) ? load_bias(a.bias, a.bias_dt, c) : 0.f;
+      bool f = false;
+      for (int b = 0; b < a.B; ++b) {
+        const int t = b / 16, g2 = (b % 16) / 4, r = b % 4;
+        float z = 0.f + red[(t * 8 + s2) * 4 + r][16 * g2 + n];
+        if (a.bias) z += cb;
+        if (cin) a.final_out[(int64_t)b * cols + c] = z;
+        f = f || (cin && z > a.tau);
+      }
+      const uint64_t M = __ballot(f);
+      const int64_t grp = (int64_t)cchunk * 2 + threadIdx.x / kWave;
+      if (a.mask && (threadIdx.x & (kWave - 1)) == 0 && grp * 64 < cols) {
+        a.mask[2 * grp] = (uint32_t)M;
+        a.mask[2 * grp + 1] = (uint32_t)(M >> 32);
+      }
+    }
+    return;
+  }
   for (int q = threadIdx.x; q < NBT * 8 * 4 * kWave; q += kMmThreads) {
     const int ln = q % kWave, idx = q / kWave;
     const int r = idx % 4, ts = idx / 4, s2 = ts % 8, t = ts / 8;
