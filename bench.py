@@ -46,6 +46,10 @@ def parse():
                     help="summarise the rocprofv3 CSV output under each DIR (kernel trace, counters) and "
                          "exit; no GPU use")
     ap.add_argument("--copy-mib", type=int, default=256, help="copy size the counters were taken with")
+    ap.add_argument("--sweep", default="4,16,32",
+                    help="after the batch-1 measurement, time the same stack at these batch sizes (union active "
+                         "set, matrix-core path) and report them under detail.batch_sweep; empty = none")
+    ap.add_argument("--sweep-steps", type=int, default=8)
     return ap.parse_args()
 
 
@@ -263,6 +267,89 @@ def rocprof_summary(roots, copy_mib):
     return "\n".join(out)
 
 
+def batch_sweep(cfg, specs, dls, batches, steps, warmup):
+    """The stack at other batch sizes: same layers, per-(step, layer) seeded inputs, one HIP graph per
+    step, `steps` timed steps after `warmup`.  Tokens/s counts every batch row; bytes are each step's
+    algorithmic bytes from its measured counts (every P2 row and every listed W2 row at batch > 1)."""
+    import torch
+    import synth
+    import activation_sparse_amd as pi
+    dev = "cuda:0"
+    n_layers = len(specs)
+    maxH = max(s.H for s in specs)
+    n_g = max(s.n_g for s in specs)
+    n_c = max(len(s.T_c) for s in specs)
+    d, N = cfg.d, cfg.N
+    out = {}
+    for B in batches:
+        S = warmup + steps
+        ws_bytes = max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256)
+        wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+        xs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev)
+        ycs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev) if n_c else None
+        Ks = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+        Kcs = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+        rows = torch.zeros((S, n_layers, 2), dtype=torch.int32, device=dev)
+        y = torch.empty((B, d), dtype=torch.float32, device=dev)
+        A_g = torch.empty(max(n_g, 1), dtype=torch.int32, device=dev)
+        A_c = torch.empty(max(n_c, 1), dtype=torch.int32, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+        for t in range(S):
+            rid = torch.from_numpy(synth.x_row_ids(1000 + t, B)).to(dev)
+            for L in range(n_layers):
+                synth.dev_fill(xs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_X, L, d, 1.0,
+                               row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+                if n_c:
+                    synth.dev_fill(ycs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_YC, L, d, 0.05,
+                                   row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+        torch.cuda.synchronize()
+
+        def step_call(t):
+            for L in range(n_layers):
+                cold = len(specs[L].T_c) > 0
+                pi.pi_ffn_layer_stages(dls[L].layer, B, xs[t, L], 0.0, ycs[t, L] if cold else None, y, None, A_g,
+                                       Ks[t, L:L + 1], A_c if cold else None, Kcs[t, L:L + 1] if cold else None,
+                                       wss[L], pi.PI_STAGE_ALL, rows_read=rows[t, L], _cstruct=dls[L].layer_c)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_call(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for t in range(S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_call(t)
+            graphs.append(g)
+        for t in range(warmup):
+            graphs[t].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(warmup, S):
+            graphs[t].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        Kh, Kch, Rh = Ks.cpu().numpy(), Kcs.cpu().numpy(), rows.cpu().numpy()
+        tot = 0.0
+        for t in range(warmup, S):
+            for L in range(n_layers):
+                tot += sum(layer_bytes(specs[L], B, int(Kh[t, L]), int(Kch[t, L]), int(Rh[t, L, 0]), int(Rh[t, L, 1])))
+        step_bytes = tot / steps
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        out[str(B)] = {"tokens_per_s": round(B * 1e3 / ms, 1), "ms_per_step": round(ms, 4),
+                       "step_bytes": round(step_bytes), "step_gbps": round(gbs, 1),
+                       "step_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "mean_K": float(Kh[warmup:].mean()),
+                       "steps": steps}
+        log(f"batch {B}: {ms:.3f} ms/step, {B * 1e3 / ms:.1f} tokens/s, {gbs:.0f} GB/s")
+        del graphs, wss, xs, ycs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.rocprof_summary:
@@ -451,6 +538,12 @@ def main():
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(cfg, B, args.cpu_seconds, args.cpu_layers)
 
+    sweep = None
+    batches = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []
+    if batches and B == 1:
+        log(f"batch sweep {batches} ...")
+        sweep = batch_sweep(cfg, specs, dls, batches, args.sweep_steps, 2)
+
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * 2**20 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -481,7 +574,8 @@ def main():
                    "kernel_us": {k: round(v * 1e3, 2) for k, v in mean_ms.items()},
                    "kernel_gbps": {k: round(v, 1) for k, v in achieved.items()},
                    "graph": use_graph, "setup_s": round(setup_s, 1), "wall_s": round(wall, 4),
-                   "event_ms": round(gpu_ms, 3)},
+                   "event_ms": round(gpu_ms, 3),
+                   "batch_sweep": sweep},
     }
     print(json.dumps(out), flush=True)
 
