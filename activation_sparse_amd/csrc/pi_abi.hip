@@ -534,16 +534,15 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
     pi::ListCtx lc{};
     lc.mask = w.mask; lc.gbits = static_cast<const uint32_t*>(L->table); lc.W = (int)table_words(N);
     lc.A_g = A_g; lc.K = K; lc.A_c = L->cold ? A_c : nullptr; lc.K_c = L->cold ? K_c : nullptr;
+    // these kernels read every hidden-major P2 row (the batch-1 tile kernel reports its own count)
+    // and every listed W2 row
+    lc.rows_read = rows_read; lc.rows0 = out_layer_needs_partials(B, H, N) ? H : -1;
     if ((st = hip_status(pi::launch_list(lc, n_g, s))) != PI_OK) return st;
   }
   if ((st = record(2)) != PI_OK) return st;
   st = enqueue_ffn(s, B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2, A_g, K, w.a, w.partials, y, y_c,
                    L->cold ? K_c : nullptr, L->b2, ev + 3, stages);
   if (st != PI_OK) return st;
-  // these kernels read every hidden-major P2 row and every listed W2 row
-  if (rows_read &&
-      (st = hip_status(pi::launch_rows_read(rows_read, out_layer_needs_partials(B, H, N) ? H : -1, K, s))) != PI_OK)
-    return st;
   return record(5);
 }
 

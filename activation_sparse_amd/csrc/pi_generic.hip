@@ -193,13 +193,6 @@ __global__ void k_zero_u32(uint32_t* p, int64_t n) {
   for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) p[t] = 0u;
 }
 
-__global__ void k_rows_read(int32_t* stats, int32_t rows0, const int32_t* K1) {
-  if (threadIdx.x == 0) {
-    if (rows0 >= 0) stats[0] = rows0;
-    stats[1] = *K1;
-  }
-}
-
 template <int DT, bool GATED>
 hipError_t rowdot_dt(const RowdotArgs& a, int64_t n_rows, uint32_t* zero_ptr, int zero_n, hipStream_t s) {
   const int64_t xbytes = (int64_t)a.B * a.cols * 4;
@@ -258,11 +251,6 @@ hipError_t launch_list(const ListCtx& c, int n_g, hipStream_t s) {
 
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_rows_read(int32_t* stats, int32_t rows0, const int32_t* K1, hipStream_t s) {
-  hipLaunchKernelGGL(k_rows_read, dim3(1), dim3(64), 0, s, stats, rows0, K1);
   return hipGetLastError();
 }
 

@@ -179,8 +179,6 @@ hipError_t launch_reduce(const ReduceArgs& r, hipStream_t s);
 // The same sum for the logits (no merge), with the activation words (2 per 64 ids) of the union over B.
 hipError_t launch_reduce_mask(const ReduceArgs& r, float tau, uint32_t* mask, hipStream_t s);
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
-// stats[0] = rows0 (unless negative), stats[1] = *K1 (rows read by the separate kernels).
-hipError_t launch_rows_read(int32_t* stats, int32_t rows0, const int32_t* K1, hipStream_t s);
 
 hipError_t launch_merge(int B, int d, float* y, const float* y_c, const int32_t* K_c, const void* b2,
                         int b2_dt, hipStream_t s);

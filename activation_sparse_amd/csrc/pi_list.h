@@ -21,6 +21,8 @@ struct ListCtx {
   int32_t* K;
   int32_t* A_c;           // NULL = no cold list
   int32_t* K_c;
+  int32_t* rows_read;     // optional: [1] = K, and [0] = rows0 when rows0 >= 0
+  int32_t rows0;
 };
 
 // LDS words needed by list_build for W words.
@@ -128,6 +130,10 @@ __device__ void list_write_cold_and_counts(const ListCtx& c, const ListView& v) 
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *c.K = v.K;
     if (c.K_c) *c.K_c = v.Kc;
+    if (c.rows_read) {
+      if (c.rows0 >= 0) c.rows_read[0] = c.rows0;
+      c.rows_read[1] = v.K;
+    }
   }
 }
 

@@ -193,6 +193,39 @@ def committed_traffic(kernel):
     return val if (digest == kernel_source_digest() and val is not None) else None
 
 
+LAYER_HEADS = ("k_hidden_b1", "k_mm_rowdot", "k_rowdot")   # the predictor hidden layer opens every layer call
+
+
+def _layer_call_sites(rows):
+    """Per call site within a layer: the dispatches (in start order) cut into sequences at each
+    predictor hidden-layer kernel; over the sequences equal to the most common one, the duration of
+    each position (a kernel launched twice per layer is reported at each of its sites)."""
+    import collections
+    import statistics as st
+    seqs, cur = [], None
+    for r in rows:
+        k = _short_kernel(r["Kernel_Name"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if k in LAYER_HEADS:
+            cur = []
+            seqs.append(cur)
+        if cur is not None:
+            cur.append((k, dur))
+    if not seqs:
+        return []
+    common, n = collections.Counter(tuple(k for k, _ in q) for q in seqs).most_common(1)[0]
+    sel = [q for q in seqs if tuple(k for k, _ in q) == common]
+    out = [f"per layer call ({n} layer sequences of {len(common)} kernels):",
+           f"{'site':4s} {'kernel':28s} {'avg_us':>9s} {'median_us':>9s}"]
+    tot = 0.0
+    for i, k in enumerate(common):
+        v = [q[i][1] for q in sel]
+        tot += st.mean(v)
+        out.append(f"{i:4d} {k:28s} {st.mean(v):9.2f} {st.median(v):9.2f}")
+    out.append(f"     {'sum':28s} {tot:9.2f}")
+    return out
+
+
 def rocprof_summary(roots, copy_mib):
     """Per-kernel durations from rocprofv3 `--kernel-trace --output-format csv`, and per-dispatch HBM
     counters from `--pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs, found anywhere under the given
@@ -230,6 +263,7 @@ def rocprof_summary(roots, copy_mib):
             if iso:
                 out.append(f"{DOMINANT + ' back-to-back':32s} {len(iso):7d} {st.mean(iso):9.2f} "
                            f"{st.median(iso):9.2f} {min(iso):8.2f}")
+            out.extend(_layer_call_sites(rows))
             out.append("")
         for path in sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True)):
             rows = list(csv.DictReader(open(path)))
@@ -508,9 +542,12 @@ def main():
     dom_bytes = float(np.mean([kernel_bytes(specs[L], B, int(Kh[last, L]), int(Kch[last, L]), int(Rh[last, L, 0]),
                                             int(Rh[last, L, 1]))[dom] for L in range(n_layers)]))
 
+    # at batch 1 one kernel; at larger batches the output layer, the lists and FC1 (several kernels)
+    dom_stages = pi.PI_STAGE_OUTPUT if B == 1 else (pi.PI_STAGE_OUTPUT | pi.PI_STAGE_FC1)
+
     def dom_pass():
         for L in range(n_layers):
-            layer_call(last, L, stages=pi.PI_STAGE_OUTPUT)
+            layer_call(last, L, stages=dom_stages)
     dom_pass()
     torch.cuda.synchronize()
     reps = 5
@@ -528,8 +565,10 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved[iso], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved[iso] / HBM_PEAK_GBS, 4),
                 "traffic": round(traffic) if traffic is not None else None,
-                "kernel": DOMINANT + " (predictor output layer over the active hidden units + activation decision "
-                          "+ FC1; pi_ffn_layer_stages PI_STAGE_OUTPUT)",
+                "kernel": (DOMINANT + " (predictor output layer over the active hidden units + activation decision "
+                           "+ FC1; pi_ffn_layer_stages PI_STAGE_OUTPUT)") if B == 1 else
+                          ("output layer + lists + FC1, several kernels (pi_ffn_layer_stages PI_STAGE_OUTPUT | "
+                           "PI_STAGE_FC1)"),
                 "bytes_per_launch": round(mean_bytes[iso]), "avg_launch_us": round(mean_ms[iso] * 1e3, 2)}
 
     log(f"timed: {ms_per_step:.4f} ms/step, {tokens_s:.1f} tokens/s")
