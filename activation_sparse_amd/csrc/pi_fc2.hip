@@ -7,6 +7,7 @@
 // (chunk, batch row, column).  A separate launch sums the chunk partials in
 // chunk order and applies the merge (+ cold partial when it has active
 // neurons, + b2).  No float atomics: the bits do not depend on block timing.
+// (The batch-1 layer's FC2 over its group segments is in pi_fast.hip.)
 #include "pi_device.h"
 #include "pi_internal.h"
 
@@ -16,7 +17,6 @@ namespace {
 constexpr int kT = 256;
 constexpr int kWpb = kT / kWave;
 constexpr int kUnroll = 8;
-constexpr int kSegUnroll = 16;
 
 template <int DT, int NBG>
 __global__ __launch_bounds__(kT) void k_fc2(Fc2Args a) {
@@ -129,184 +129,6 @@ __global__ __launch_bounds__(kT) void k_reduce(ReduceArgs r) {
   }
 }
 
-// Batch-1 FC2 over the group segments of the fused layer, and the list
-// assembly.  Blocks [0, tiles * kSegChunks) are FC2 blocks: block (tile,
-// chunk) takes the groups [c * ngroups / C, (c + 1) * ngroups / C); its rows are
-// those groups' (slot, a) pairs with a != 0 in group order (ascending slots),
-// gathered into LDS first (one round trip), then the listed W2 rows are
-// streamed over the block's column tile: 16-byte loads, kSegUnroll rows in
-// flight per wave.  It writes one partial per chunk.  The other blocks each
-// place 256 entries (four groups) of the ascending lists A_g / A_c, at offsets
-// from the counts of the groups below; list block 0 writes K and K_c.
-template <int DT>
-__global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
-  constexpr int E = Fmt<DT>::E;
-  extern __shared__ int32_t fsm[];
-  __shared__ float red[kWpb][kWave * E];
-  __shared__ int s_cnt[64], s_off[65];
-  __shared__ int s_red[5][kWpb];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int ngroups = a.ngroups;
-  if ((int)blockIdx.x >= tiles * kSegChunks) {
-    // ---- list assembly: groups [4 lb, 4 lb + 4), one entry per thread
-    const int lb = (int)blockIdx.x - tiles * kSegChunks;
-    const int g0 = 4 * lb;
-    const int e = g0 * 64 + tid;
-    const int grp = e / 64, i = e % 64;
-    const bool ein = grp < ngroups;
-    const int32_t es = ein ? a.seg_slot[e] : 0;
-    const int32_t ec = (ein && a.A_c) ? a.seg_cold[e] : 0;
-    const uint32_t mine = ein ? a.cnt[grp] : 0u;
-    // counts below g0 and in total, summed over a strided share of the groups
-    int below_g = 0, below_c = 0, tot_g = 0, tot_c = 0, tot_z = 0;
-    for (int q = tid; q < ngroups; q += kT) {
-      const uint32_t c = a.cnt[q];
-      const int cg = (int)cnt_gpu(c), cc = (int)cnt_cold(c);
-      tot_g += cg; tot_c += cc; tot_z += (int)cnt_nz(c);
-      if (q < g0) { below_g += cg; below_c += cc; }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      below_g += __shfl_xor(below_g, off, kWave); below_c += __shfl_xor(below_c, off, kWave);
-      tot_g += __shfl_xor(tot_g, off, kWave); tot_c += __shfl_xor(tot_c, off, kWave);
-      tot_z += __shfl_xor(tot_z, off, kWave);
-    }
-    if (lane == 0) {
-      s_red[0][wave] = below_g; s_red[1][wave] = below_c; s_red[2][wave] = tot_g; s_red[3][wave] = tot_c;
-      s_red[4][wave] = tot_z;
-    }
-    if (lane == 0 && wave < 4) s_cnt[wave] = g0 + wave < ngroups ? (int)a.cnt[g0 + wave] : 0;
-    __syncthreads();
-    int bg = 0, bc = 0, tg = 0, tc = 0, tz = 0;
-#pragma unroll
-    for (int w = 0; w < kWpb; ++w) {
-      bg += s_red[0][w]; bc += s_red[1][w]; tg += s_red[2][w]; tc += s_red[3][w]; tz += s_red[4][w];
-    }
-    // offsets of this thread's group within the block's four
-    const int gi = tid / 64;
-    for (int w = 0; w < gi; ++w) { bg += (int)cnt_gpu((uint32_t)s_cnt[w]); bc += (int)cnt_cold((uint32_t)s_cnt[w]); }
-    if (ein && i < (int)cnt_gpu(mine) && bg + i < a.n_g) a.A_g[bg + i] = es;
-    if (ein && a.A_c && i < (int)cnt_cold(mine) && bc + i < a.n_c) a.A_c[bc + i] = ec;
-    if (lb == 0 && tid == 0) {
-      *a.K = tg < a.n_g ? tg : a.n_g;
-      if (a.K_c) *a.K_c = tc < a.n_c ? tc : a.n_c;
-      if (a.rows_read) *a.rows_read = tz;
-    }
-    return;
-  }
-  // ---- FC2
-  const int tile = (int)blockIdx.x % tiles, chunk = (int)blockIdx.x / tiles;
-  const int b0 = (int)((int64_t)ngroups * chunk / kSegChunks), b1 = (int)((int64_t)ngroups * (chunk + 1) / kSegChunks);
-  const int nb = b1 - b0;
-  int32_t* c_slot = fsm;
-  float* c_a = reinterpret_cast<float*>(fsm + nb * 64);
-  // each thread's share of the raw (slot, a) entries, loaded together with the counts
-  constexpr int RQ = 16;   // entries per thread: nb * 64 <= RQ * kT
-  int32_t rs[RQ];
-  float ra[RQ];
-#pragma unroll
-  for (int q = 0; q < RQ; ++q) {
-    const int e = q * kT + tid;
-    rs[q] = e < nb * 64 ? a.pos_slot[(int64_t)b0 * 64 + e] : -1;
-    ra[q] = e < nb * 64 ? a.pos_a[(int64_t)b0 * 64 + e] : 0.f;
-  }
-  if (tid < nb) s_cnt[tid] = (int)cnt_nz(a.cnt[b0 + tid]);
-  __syncthreads();
-  if (wave == 0) {
-    const int v = lane < nb ? s_cnt[lane] : 0;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += t;
-    }
-    if (lane < nb) s_off[lane] = incl - v;
-    if (lane == kWave - 1) s_off[nb] = incl;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < RQ; ++q) {
-    const int e = q * kT + tid;
-    if (e < nb * 64) {
-      const int bb = e / 64, i = e % 64;
-      if (i < s_cnt[bb]) {
-        c_slot[s_off[bb] + i] = rs[q];
-        c_a[s_off[bb] + i] = ra[q];
-      }
-    }
-  }
-  __syncthreads();
-  const int R = s_off[nb];
-  const int64_t d = a.d;
-  const int64_t rb = row_bytes(DT, d);
-  const int nvec = (int)(rb / 16);
-  const int v = tile * kWave + lane;
-  const bool vok = v < nvec;
-  const int64_t groups = d / 128;
-  const int64_t tile_col0 = (int64_t)tile * kWave * E;
-  const char* W2 = reinterpret_cast<const char*>(a.W2);
-  float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int jb = wave; jb < R; jb += kWpb * kSegUnroll) {
-    uint4 w[kSegUnroll];
-    float scl[kSegUnroll], ab[kSegUnroll];
-#pragma unroll
-    for (int u = 0; u < kSegUnroll; ++u) {
-      // row j is the same for the whole wave: a buffer over it, empty for an
-      // absent row; lanes past the row end read zeros
-      const int j = jb + u * kWpb;
-      int s = j < R ? c_slot[j] : -1;
-      s = __builtin_amdgcn_readfirstlane(s < a.n_g ? s : -1);
-      ab[u] = j < R ? c_a[j] : 0.f;
-      const rsrc_t rw = make_rsrc(W2 + (s >= 0 ? (int64_t)s * rb : 0), s >= 0 ? (uint32_t)rb : 0u);
-      w[u] = bload16(rw, (uint32_t)v * 16u);
-      if constexpr (DT == 2) {
-        const rsrc_t rs = make_rsrc(a.W2s + (s >= 0 ? (int64_t)s * groups : 0), s >= 0 ? (uint32_t)groups * 2u : 0u);
-        scl[u] = h2f(bload2(rs, (uint32_t)(v / 4) * 2u));
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kSegUnroll; ++u) {
-      float wf[E];
-      widen<DT>(w[u], DT == 2 ? scl[u] : 1.f, wf);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(ab[u], wf[e], acc[e]);
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e) red[wave][lane * E + e] = vok ? acc[e] : 0.f;
-  __syncthreads();
-  float* dst = a.partials + (int64_t)chunk * d + tile_col0;
-  for (int t = tid; t < kWave * E; t += kT) {
-    if (tile_col0 + t < d) {
-      float sum = red[0][t];
-#pragma unroll
-      for (int ww = 1; ww < kWpb; ++ww) sum += red[ww][t];
-      dst[t] = sum;
-    }
-  }
-}
-
-// y[t] = the kSegChunks partials summed in chunk order (+ y_c when K_c is NULL
-// or *K_c != 0, + b2): one column per thread, every partial load in flight.
-__global__ __launch_bounds__(kWave) void k_reduce_y(ReduceYArgs r) {
-  const int64_t t = (int64_t)blockIdx.x * kWave + threadIdx.x;
-  if (t >= r.d) return;
-  const int kc = r.K_c ? *r.K_c : 1;
-  const float yc = r.y_c ? r.y_c[t] : 0.f;
-  const float bb = r.b2 ? load_bias(r.b2, r.b2_dt, t) : 0.f;
-  float p[kSegChunks];
-#pragma unroll
-  for (int c = 0; c < kSegChunks; ++c) p[c] = r.partials[(int64_t)c * r.d + t];
-  float sum = 0.f;
-#pragma unroll
-  for (int c = 0; c < kSegChunks; ++c) sum += p[c];
-  if (r.y_c && kc != 0) sum += yc;
-  if (r.b2) sum += bb;
-  r.y[t] = sum;
-}
 // The output layer's ordered sum (as k_reduce: chunks in order, then + c2) fused
 // with the activation decision: one wave per 64 ids, every batch row's logit
 // stored, and the union over the batch written as the group's two words.
@@ -377,25 +199,6 @@ hipError_t launch_fc2(const Fc2Args& a, hipStream_t s) {
     case PI_F16: return fc2_dt<1>(a, s);
     default: return fc2_dt<2>(a, s);
   }
-}
-
-hipError_t launch_fc2_seg(const Fc2SegArgs& a, hipStream_t s) {
-  const int nbmax = (a.ngroups + kSegChunks - 1) / kSegChunks;
-  const size_t shm = (size_t)nbmax * 64 * 4 * 2;
-  const int tiles = fc2_tiles(a.dt, a.d);
-  const int list_blocks = (a.ngroups + 3) / 4;
-  const dim3 g((unsigned)(tiles * kSegChunks + list_blocks)), t(kT);
-  switch (a.dt) {
-    case PI_F32: hipLaunchKernelGGL(k_fc2_seg<0>, g, t, shm, s, a, tiles); break;
-    case PI_F16: hipLaunchKernelGGL(k_fc2_seg<1>, g, t, shm, s, a, tiles); break;
-    default: hipLaunchKernelGGL(k_fc2_seg<2>, g, t, shm, s, a, tiles); break;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_reduce_y(const ReduceYArgs& r, hipStream_t s) {
-  hipLaunchKernelGGL(k_reduce_y, dim3((unsigned)((r.d + kWave - 1) / kWave)), dim3(kWave), 0, s, r);
-  return hipGetLastError();
 }
 
 hipError_t launch_reduce_mask(const ReduceArgs& r, float tau, uint32_t* mask, hipStream_t s) {

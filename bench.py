@@ -161,8 +161,8 @@ def _short_kernel(name):
     return m.group(1) if m else name[:60]
 
 
-KERNEL_SOURCES = ["activation_sparse_amd/csrc/pi_fast.hip", "activation_sparse_amd/csrc/pi_fc2.hip",
-                  "activation_sparse_amd/csrc/pi_device.h", "activation_sparse_amd/csrc/pi_internal.h"]
+KERNEL_SOURCES = ["activation_sparse_amd/csrc/pi_fast.hip", "activation_sparse_amd/csrc/pi_b1.h",
+                  "activation_sparse_amd/csrc/pi_device.h", "include/pi.h"]
 DOMINANT = "k_pred_fc1"
 TRAFFIC_PROFILE = "profiles/k_pred_fc1.opt-30b.b1.hbm_traffic.txt"
 
