@@ -89,7 +89,7 @@ size_t mm_axpy_partial_bytes(int32_t B, int64_t rows, int64_t cols) {
   if (!use_mm_axpy(B) || rows <= 0 || cols <= 0) return 0;
   int rc = 1;
   for (int dt = 0; dt < 2; ++dt) {
-    const int r = pi::mm_axpy_row_chunks(dt, rows, cols);
+    const int r = pi::mm_axpy_row_chunks(dt, pi::mm_nbt(B), rows, cols);
     rc = r > rc ? r : rc;
   }
   return (size_t)rc * B * (size_t)cols * 4;
@@ -229,7 +229,7 @@ int enqueue_output_layer(hipStream_t s, int32_t B, int32_t H, int32_t N, const f
     m.count_dev = nullptr; m.count_max = H; m.a = h; m.a_stride = H; m.a_by_row = 1; m.a_tr = h_lay != 0; m.B = B;
     m.a_h8 = h_lay == 2; m.a_lo = h_lay == 2 ? h_lo_part(const_cast<float*>(h), B, H) : nullptr;
     m.nbt = pi::mm_nbt(B);
-    m.row_chunks = pi::mm_axpy_row_chunks(P2.dtype, H, N);
+    m.row_chunks = pi::mm_axpy_row_chunks(P2.dtype, pi::mm_nbt(B), H, N);
     m.partials = partials;
     if (m.a_h8) {
       // every hidden unit in one block per 128 logits: logits, c2 and the words in the same launch
@@ -407,7 +407,7 @@ int enqueue_ffn(hipStream_t s, int32_t B, int32_t d, int32_t n_g, int32_t kind, 
     if (st != PI_OK) return st;
   }
   if (ev && ev[0] && (st = hip_status(hipEventRecord(ev[0], s))) != PI_OK) return st;
-  const int chunks2 = mm2 ? pi::mm_axpy_row_chunks(W2.dtype, n_g, d) : pi::fc2_chunks(B);
+  const int chunks2 = mm2 ? pi::mm_axpy_row_chunks(W2.dtype, pi::mm_nbt(B), n_g, d) : pi::fc2_chunks(B);
   if (stages & PI_STAGE_FC2) {
     if (mm2) {
       pi::MmAxpyArgs m{};

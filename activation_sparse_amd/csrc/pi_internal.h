@@ -150,7 +150,7 @@ int64_t mm_row_kc(int dt, int64_t cols, int ks);
 bool mm_row16_used(const MmRowArgs& a);
 int mm_row16_ks(int64_t count_max, int64_t cols, int nbt, bool gated);
 int mm_axpy_col_chunks(int dt, int64_t cols);
-int mm_axpy_row_chunks(int dt, int64_t count_max, int64_t cols);
+int mm_axpy_row_chunks(int dt, int nbt, int64_t count_max, int64_t cols);
 bool mm_rowdot_supported(int dt, int64_t rows, int64_t cols);
 bool mm_axpy_supported(int dt, int64_t rows, int64_t cols);
 bool mm_axpy16_supported(int dt, int64_t cols);

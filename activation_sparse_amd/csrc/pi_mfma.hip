@@ -35,6 +35,7 @@ namespace {
 typedef float float4v_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMmWaves = 4;
+constexpr int kNumCU = 256;                 // compute units of the gfx950 parts (MI350X / MI355X)
 constexpr int kMmThreads = kMmWaves * kWave;
 
 __device__ __forceinline__ float4v_t mfma4(float a, float b, float4v_t c) {
@@ -492,8 +493,12 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
     const int64_t kd = *a.count_dev;
     count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
   }
-  const int64_t r0 = (int64_t)rchunk * a.rows_per_chunk;
-  int64_t r1 = r0 + a.rows_per_chunk;
+  // the row chunks split the device count evenly (multiples of 32 rows; no more than the
+  // rows_per_chunk the LDS row ids are sized for, which bounds count_max / row_chunks)
+  int64_t rpc = ((count + a.row_chunks - 1) / a.row_chunks + 31) / 32 * 32;
+  rpc = rpc < a.rows_per_chunk ? rpc : a.rows_per_chunk;
+  const int64_t r0 = (int64_t)rchunk * rpc;
+  int64_t r1 = r0 + rpc;
   r1 = r1 < count ? r1 : count;
   for (int64_t j = r0 + threadIdx.x; j < r1; j += kMmThreads) {
     const int64_t row = a.list ? (int64_t)a.list[j] : j;
@@ -700,10 +705,12 @@ int mm_axpy_col_chunks(int dt, int64_t cols) {
   return (int)((nvec + 15) / 16);
 }
 
-int mm_axpy_row_chunks(int dt, int64_t count_max, int64_t cols) {
-  // about 1024 blocks of four waves
+int mm_axpy_row_chunks(int dt, int nbt, int64_t count_max, int64_t cols) {
+  // fp16: one resident round of blocks (3 per CU for 16 batch rows, 2 for 32, set by
+  // the registers); others: about 1024 blocks of four waves
   const int64_t cc = mm_axpy_col_chunks(dt, cols);
-  int64_t rc = (1024 + cc - 1) / cc;
+  const int64_t target = dt == PI_F16 ? (int64_t)(nbt == 1 ? 3 : 2) * kNumCU : 1024;
+  int64_t rc = dt == PI_F16 ? target / cc : (target + cc - 1) / cc;
   const int64_t rmax = (count_max + 63) / 64;   // at least 64 rows per block
   rc = rc > rmax ? rmax : rc;
   return (int)(rc < 1 ? 1 : rc);
