@@ -130,6 +130,11 @@ int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float ta
  *   y_g[b,:] = sum_j a[b,j] * W2[s,:]                      (fixed-order sum)
  * x [B x d] fp32; b1 [n_g]; y_g [B x d] fp32, fully written (zero if K = 0).
  * A_g entries must be < n_g; *K <= n_g.
+ * Precision: accumulation is fp32.  With fp16 weights and B >= 2 the matrix
+ * cores take x rounded to fp16 for FC1 and a rounded to fp16 for FC2 (each
+ * product of two fp16 values is exact), so |x| must stay below 65504; the
+ * predictor's logits keep near-fp32 precision (h enters as two fp16 parts).
+ * Other cases use fp32 products.
  * ws: at least pi_workspace_bytes(PI_OP_SPARSE_FFN, B, d, 0, 0, n_g) bytes.
  * Errors: as pi_predict, plus PI_EINVAL for a kind outside PI_RELU /
  * PI_GATED_RELU or a gated call without Wup, and PI_EUNSUPPORTED when W1,
