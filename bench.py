@@ -162,7 +162,7 @@ def _short_kernel(name):
 
 
 KERNEL_SOURCES = ["activation_sparse_amd/csrc/pi_fast.hip", "activation_sparse_amd/csrc/pi_b1.h",
-                  "activation_sparse_amd/csrc/pi_device.h", "include/pi.h"]
+                  "activation_sparse_amd/csrc/pi_device.h"]
 DOMINANT = "k_pred_fc1"
 TRAFFIC_PROFILE = "profiles/k_pred_fc1.opt-30b.b1.hbm_traffic.txt"
 
