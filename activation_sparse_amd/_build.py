@@ -1,6 +1,7 @@
 """Build commands for every native part of the repository.
 
-libpi.so (the HIP library, gfx950), libsynth.so / libsynth_gpu.so (the
+libpi.so (the HIP library, gfx950), libpi_host.so (the CPU side of the hybrid
+layer), libsynth.so / libsynth_gpu.so (the
 synthetic-input generator, host and device) and liboracle.so (the CPU
 oracle, test infrastructure only).  Everything is built in-tree so the
 shared objects travel with the source tree.
@@ -23,6 +24,10 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 PI_SOURCES = ["pi_generic.hip", "pi_fast.hip", "pi_fc2.hip", "pi_mfma.hip", "pi_abi.hip"]
+LIBHOST = os.path.join(PKG, "libpi_host.so")
+# the host (CPU) operator: no target-wide vector flags (its AVX2 path is chosen at run time),
+# no contraction of separate multiplies and adds (its sums have one fixed rounding order)
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fopenmp", "-ffp-contract=off"]
 
 
 def _run(cmd):
@@ -45,13 +50,20 @@ def build_libpi(jobs: int = 8) -> str:
     return LIBPI
 
 
+def build_libpi_host() -> str:
+    tmp_so = LIBHOST + ".tmp"
+    _run(["g++", *HOST_FLAGS, "-shared", os.path.join(CSRC, "pi_host.cpp"), "-o", tmp_so])
+    os.replace(tmp_so, LIBHOST)
+    return LIBHOST
+
+
 def build_all() -> None:
     sys.path.insert(0, ROOT)
     import synth
     import oracle
     with ThreadPoolExecutor(max_workers=4) as ex:
-        futs = [ex.submit(build_libpi), ex.submit(synth.build_host), ex.submit(oracle.build),
-                ex.submit(_run, synth.build_gpu_cmd())]
+        futs = [ex.submit(build_libpi), ex.submit(build_libpi_host), ex.submit(synth.build_host),
+                ex.submit(oracle.build), ex.submit(_run, synth.build_gpu_cmd())]
         for f in futs:
             f.result()
 

@@ -1,0 +1,257 @@
+// pi_host.cpp - libpi_host: the FFN over the CPU-resident (cold) neurons, on
+// the host, for the pages' GPU-CPU hybrid layer.
+//
+// FC1: each listed neuron's row is read once and dotted with every batch row
+// of x (threads take fixed ranges of the list).  FC2: the d columns are split
+// into one fixed range per thread; each thread streams its slice of the W2 row
+// of every neuron with a non-zero output, in list order, into its slice of
+// y_c.  A dot product keeps 32 partial sums (4 x 8 lanes, k = 32 i + 8 q + l)
+// and adds them in one fixed tree, with fused multiply-adds; the AVX2 path
+// and the scalar path follow the same order, so the bits are the same on
+// either and for any thread count.
+#include <immintrin.h>
+#include <omp.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <cmath>
+#include <vector>
+
+#include "../../include/pi_host.h"
+
+namespace {
+
+// IEEE binary16 -> binary32 (exact).
+inline float half_to_float(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t exp = (h >> 10) & 0x1Fu;
+  uint32_t man = h & 0x3FFu;
+  uint32_t bits;
+  if (exp == 0) {
+    if (man == 0) {
+      bits = sign;
+    } else {                      // subnormal: m * 2^-24, renormalised
+      int shift = 0;
+      while (!(man & 0x400u)) { man <<= 1; ++shift; }
+      bits = sign | ((uint32_t)(113 - shift) << 23) | ((man & 0x3FFu) << 13);
+    }
+  } else if (exp == 31) {
+    bits = sign | 0x7F800000u | (man << 13);
+  } else {
+    bits = sign | ((exp + 112u) << 23) | (man << 13);
+  }
+  float f;
+  memcpy(&f, &bits, 4);
+  return f;
+}
+
+struct Rows {
+  const char* data;
+  const uint16_t* scales;
+  int dt;
+  int64_t rb;      // bytes per row
+  int64_t groups;  // int4 scale groups per row
+  const char* row(int64_t r) const { return data + r * rb; }
+};
+
+int64_t row_bytes(int dt, int64_t d) { return dt == PI_F32 ? d * 4 : dt == PI_F16 ? d * 2 : d / 2; }
+
+// Eight consecutive weights k0 .. k0 + 7 of row r as floats (k0 a multiple of 8).
+inline void load8_scalar(const Rows& w, int64_t r, int64_t k0, float* out) {
+  const char* p = w.row(r);
+  if (w.dt == PI_F32) {
+    memcpy(out, p + k0 * 4, 32);
+  } else if (w.dt == PI_F16) {
+    uint16_t h[8];
+    memcpy(h, p + k0 * 2, 16);
+    for (int l = 0; l < 8; ++l) out[l] = half_to_float(h[l]);
+  } else {
+    const float s = half_to_float(w.scales[r * w.groups + k0 / 128]);
+    uint8_t b[4];
+    memcpy(b, p + k0 / 2, 4);
+    for (int l = 0; l < 8; ++l) {
+      const int nib = (l & 1) ? (b[l / 2] >> 4) : (b[l / 2] & 0xF);
+      out[l] = (float)(nib >= 8 ? nib - 16 : nib) * s;
+    }
+  }
+}
+
+float bias_at(const pi_vector& v, int64_t i) {
+  if (!v.data) return 0.f;
+  if (v.dtype == PI_F32) return static_cast<const float*>(v.data)[i];
+  return half_to_float(static_cast<const uint16_t*>(v.data)[i]);
+}
+
+// The fixed tree over the 32 partial sums: lanes of the 4 groups, then halves.
+inline float tree32(const float (&acc)[4][8]) {
+  float t[8];
+  for (int l = 0; l < 8; ++l) t[l] = (acc[0][l] + acc[1][l]) + (acc[2][l] + acc[3][l]);
+  float u[4];
+  for (int l = 0; l < 4; ++l) u[l] = t[l] + t[l + 4];
+  return (u[0] + u[2]) + (u[1] + u[3]);
+}
+
+// dot[b] = W[r] . x_b for b < B (scalar path).
+void dots_scalar(const Rows& w, int64_t r, const float* x, int B, int64_t d, float* dot) {
+  for (int b = 0; b < B; ++b) {
+    const float* xb = x + (int64_t)b * d;
+    float acc[4][8] = {};
+    float wv[8];
+    for (int64_t k0 = 0; k0 < d; k0 += 32)
+      for (int q = 0; q < 4 && k0 + 8 * q < d; ++q) {
+        load8_scalar(w, r, k0 + 8 * q, wv);
+        for (int l = 0; l < 8; ++l) acc[q][l] = std::fma(wv[l], xb[k0 + 8 * q + l], acc[q][l]);
+      }
+    dot[b] = tree32(acc);
+  }
+}
+
+// y[b, c0 .. c1) += a[b] * W[r, c0 .. c1) for the b with a[b] != 0 (scalar path).
+void axpy_scalar(const Rows& w, int64_t r, const float* a, int B, int64_t d, int64_t c0, int64_t c1, float* y) {
+  float wv[8];
+  for (int64_t c = c0; c < c1; c += 8) {
+    load8_scalar(w, r, c, wv);
+    for (int b = 0; b < B; ++b) {
+      if (a[b] == 0.f) continue;
+      float* yb = y + (int64_t)b * d + c;
+      for (int l = 0; l < 8; ++l) yb[l] = std::fma(a[b], wv[l], yb[l]);
+    }
+  }
+}
+
+#define PI_AVX2 __attribute__((target("avx2,fma,f16c")))
+
+PI_AVX2 inline __m256 load8_avx2(const Rows& w, int64_t r, int64_t k0) {
+  const char* p = w.row(r);
+  if (w.dt == PI_F32) return _mm256_loadu_ps(reinterpret_cast<const float*>(p) + k0);
+  if (w.dt == PI_F16) return _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i*>(p + k0 * 2)));
+  float f[8];
+  load8_scalar(w, r, k0, f);
+  return _mm256_loadu_ps(f);
+}
+
+PI_AVX2 float tree32_avx2(__m256 a0, __m256 a1, __m256 a2, __m256 a3) {
+  const __m256 t = _mm256_add_ps(_mm256_add_ps(a0, a1), _mm256_add_ps(a2, a3));
+  const __m128 u = _mm_add_ps(_mm256_castps256_ps128(t), _mm256_extractf128_ps(t, 1));   // t[l] + t[l+4]
+  // (u0 + u2) + (u1 + u3)
+  const __m128 v = _mm_add_ps(u, _mm_movehl_ps(u, u));                                  // [u0+u2, u1+u3, ...]
+  return _mm_cvtss_f32(_mm_add_ss(v, _mm_shuffle_ps(v, v, 1)));
+}
+
+PI_AVX2 void dots_avx2(const Rows& w, int64_t r, const float* x, int B, int64_t d, float* dot) {
+  for (int b0 = 0; b0 < B; b0 += 4) {
+    const int nb = B - b0 < 4 ? B - b0 : 4;
+    __m256 acc[4][4];
+    for (int i = 0; i < 4; ++i)
+      for (int q = 0; q < 4; ++q) acc[i][q] = _mm256_setzero_ps();
+    for (int64_t k0 = 0; k0 < d; k0 += 32) {
+      const int nq = (d - k0) / 8 < 4 ? (int)((d - k0) / 8) : 4;
+      for (int q = 0; q < nq; ++q) {
+        const __m256 wv = load8_avx2(w, r, k0 + 8 * q);
+        for (int i = 0; i < nb; ++i)
+          acc[i][q] = _mm256_fmadd_ps(wv, _mm256_loadu_ps(x + (int64_t)(b0 + i) * d + k0 + 8 * q), acc[i][q]);
+      }
+    }
+    for (int i = 0; i < nb; ++i) dot[b0 + i] = tree32_avx2(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  }
+}
+
+PI_AVX2 void axpy_avx2(const Rows& w, int64_t r, const float* a, int B, int64_t d, int64_t c0, int64_t c1, float* y) {
+  for (int64_t c = c0; c < c1; c += 8) {
+    const __m256 wv = load8_avx2(w, r, c);
+    for (int b = 0; b < B; ++b) {
+      if (a[b] == 0.f) continue;
+      float* yb = y + (int64_t)b * d + c;
+      _mm256_storeu_ps(yb, _mm256_fmadd_ps(_mm256_set1_ps(a[b]), wv, _mm256_loadu_ps(yb)));
+    }
+  }
+}
+
+bool have_avx2() {
+  static const bool ok = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma") &&
+                         __builtin_cpu_supports("f16c");
+  return ok;
+}
+
+bool valid_dtype(int dt) { return dt == PI_F32 || dt == PI_F16 || dt == PI_I4G128; }
+
+}  // namespace
+
+extern "C" int pi_host_vector_path(void) { return have_avx2() ? 1 : 0; }
+
+extern "C" int pi_cold_ffn_ex(int32_t B, int32_t d, int32_t n_c, int32_t kind, const float* x, pi_matrix W1,
+                              pi_vector b1, pi_matrix Wup, pi_matrix W2, const int32_t* A_c, int32_t K_c, float* y_c,
+                              int32_t threads, int32_t path) {
+  if (B < 1 || B > PI_MAX_BATCH || d <= 0 || K_c < 0 || n_c < K_c || !x || !y_c) return PI_EINVAL;
+  if (path < -1 || path > 1) return PI_EINVAL;
+  if (path == 1 && !have_avx2()) return PI_EUNSUPPORTED;
+  if (kind != PI_RELU && kind != PI_GATED_RELU) return PI_EINVAL;
+  const bool gated = kind == PI_GATED_RELU;
+  if (!valid_dtype(W1.dtype) || !valid_dtype(W2.dtype) || (gated && !valid_dtype(Wup.dtype))) return PI_EINVAL;
+  if (d % (W1.dtype == PI_I4G128 ? 128 : 8) != 0) return PI_EINVAL;
+  if (b1.data && b1.dtype != PI_F32 && b1.dtype != PI_F16) return PI_EINVAL;
+  if (K_c > 0 && (!A_c || !W1.data || !W2.data || (gated && !Wup.data))) return PI_EINVAL;
+  if (W2.dtype != W1.dtype || (gated && Wup.dtype != W1.dtype)) return PI_EUNSUPPORTED;
+  if (W1.dtype == PI_I4G128 && (!W1.scales || !W2.scales || (gated && !Wup.scales))) return PI_EINVAL;
+  for (int32_t j = 0; j < K_c; ++j)
+    if (A_c[j] < 0 || A_c[j] >= n_c) return PI_EINVAL;
+
+  const int64_t dd = d;
+  const int64_t rb = row_bytes(W1.dtype, dd);
+  const Rows w1{static_cast<const char*>(W1.data), W1.scales, W1.dtype, rb, dd / 128};
+  const Rows wu{static_cast<const char*>(gated ? Wup.data : W1.data), gated ? Wup.scales : W1.scales, W1.dtype, rb,
+                dd / 128};
+  const Rows w2{static_cast<const char*>(W2.data), W2.scales, W2.dtype, rb, dd / 128};
+  const bool vec = path == -1 ? have_avx2() : path == 1;
+  const int nt = threads > 0 ? threads : omp_get_max_threads();
+
+  // FC1: a[j * B + b]
+  std::vector<float> a((size_t)K_c * B);
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int32_t j = 0; j < K_c; ++j) {
+    const int64_t c = A_c[j];
+    float z[PI_MAX_BATCH], u[PI_MAX_BATCH];
+    if (vec) dots_avx2(w1, c, x, B, dd, z);
+    else dots_scalar(w1, c, x, B, dd, z);
+    if (gated) {
+      if (vec) dots_avx2(wu, c, x, B, dd, u);
+      else dots_scalar(wu, c, x, B, dd, u);
+    }
+    const float bias = bias_at(b1, c);
+    for (int b = 0; b < B; ++b) {
+      float v = z[b] + bias;
+      v = v > 0.f ? v : 0.f;
+      if (gated) v *= u[b];
+      a[(size_t)j * B + b] = v;
+    }
+  }
+  // the neurons that add to y (a != 0 in some batch row), in list order
+  std::vector<int32_t> act;
+  act.reserve(K_c);
+  for (int32_t j = 0; j < K_c; ++j) {
+    bool any = false;
+    for (int b = 0; b < B; ++b) any = any || a[(size_t)j * B + b] != 0.f;
+    if (any) act.push_back(j);
+  }
+  // FC2 over fixed column ranges (multiples of 8 columns)
+  const int64_t nvec = dd / 8;
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int t = 0; t < nt; ++t) {
+    const int64_t c0 = nvec * t / nt * 8, c1 = nvec * (t + 1) / nt * 8;
+    for (int b = 0; b < B; ++b)
+      for (int64_t c = c0; c < c1; ++c) y_c[(int64_t)b * dd + c] = 0.f;
+    if (c0 == c1) continue;
+    for (size_t q = 0; q < act.size(); ++q) {
+      const int32_t j = act[q];
+      if (vec) axpy_avx2(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
+      else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
+    }
+  }
+  return PI_OK;
+}
+
+extern "C" int pi_cold_ffn(int32_t B, int32_t d, int32_t n_c, int32_t kind, const float* x, pi_matrix W1,
+                           pi_vector b1, pi_matrix Wup, pi_matrix W2, const int32_t* A_c, int32_t K_c, float* y_c,
+                           int32_t threads) {
+  return pi_cold_ffn_ex(B, d, n_c, kind, x, W1, b1, Wup, W2, A_c, K_c, y_c, threads, -1);
+}

@@ -50,6 +50,9 @@ def parse():
                     help="after the batch-1 measurement, time the same stack at these batch sizes (union active "
                          "set, matrix-core path) and report them under detail.batch_sweep; empty = none")
     ap.add_argument("--sweep-steps", type=int, default=8)
+    ap.add_argument("--hybrid-steps", type=int, default=4,
+                    help="after the batch-1 measurement, time the pages' GPU-CPU hybrid layer (cold neurons on "
+                         "the host CPU) over this many steps; 0 = skip")
     return ap.parse_args()
 
 
@@ -384,6 +387,63 @@ def batch_sweep(cfg, specs, dls, batches, steps, warmup):
     return out
 
 
+def hybrid_bench(cfg, specs, dls, steps, warmup):
+    """The pages' hybrid layer at batch 1: the CPU-table neurons live in host memory and run on the
+    host CPU (libpi_host) while the GPU runs the predictor, the compaction and its own neurons; the
+    CPU's partial is copied over and merged on the GPU (skipped when it has no active neuron).
+    Layers are serialised as in the GPU-only measurement.  Returns None when every neuron is on
+    the GPU."""
+    import torch
+    import synth
+    from synth.device import HostColdLayer
+    from activation_sparse_amd.hybrid import HybridLayer
+    from activation_sparse_amd import host
+    if not any(len(s.T_c) for s in specs):
+        return None
+    dev = "cuda:0"
+    t0 = time.time()
+    hls = [HostColdLayer(s, dev) for s in specs]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    host_bytes = sum(t.numel() * t.element_size() for hl in hls for m in (hl.W1, hl.W2, hl.Wup) if m is not None
+                     for t in (m.data, m.scales) if t is not None)
+    hys = [HybridLayer(dl, hl, 1) for dl, hl in zip(dls, hls)]
+    S, L, d = warmup + steps, len(specs), cfg.d
+    xs = torch.empty((S, L, 1, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in range(S):
+        rid = torch.from_numpy(synth.x_row_ids(2000 + t, 1)).to(dev)
+        for l in range(L):
+            synth.dev_fill(xs[t, l].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_X, l, d, 1.0,
+                           row_ids_ptr=rid.data_ptr(), nrows=1, stream=stream)
+    xh = xs.cpu().numpy()
+    y = torch.empty((1, d), dtype=torch.float32, device=dev)
+    for t in range(warmup):
+        for l in range(L):
+            hys[l](xs[t, l], xh[t, l], y)
+    torch.cuda.synchronize()
+    for h in hys:
+        h.host_s = 0.0
+    kcs = []
+    t1 = time.perf_counter()
+    for t in range(warmup, S):
+        for l in range(L):
+            kcs.append(hys[l](xs[t, l], xh[t, l], y))
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t1
+    host_s = sum(h.host_s for h in hys)
+    out = {"tokens_per_s": round(steps / el, 2), "ms_per_step": round(el * 1e3 / steps, 3), "steps": steps,
+           "layers": L, "host_weights_gib": round(host_bytes / 2**30, 2),
+           "cpu_threads": int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count(),
+           "cpu_vector_path": "avx2+fma+f16c" if host.vector_path() else "scalar",
+           "cpu_cold_ffn_us_per_layer": round(host_s * 1e6 / (steps * L), 1),
+           "mean_K_c": float(np.mean(kcs)), "host_weight_setup_s": round(gen_s, 1)}
+    log(f"hybrid: {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s, cold FFN on the CPU "
+        f"{out['cpu_cold_ffn_us_per_layer']} us per layer")
+    del hys, hls
+    return out
+
+
 def main():
     args = parse()
     if args.rocprof_summary:
@@ -577,6 +637,11 @@ def main():
         log("cpu baseline (oracle) ...")
         cpu = cpu_baseline(cfg, B, args.cpu_seconds, args.cpu_layers)
 
+    hybrid = None
+    if args.hybrid_steps > 0 and B == 1:
+        log("hybrid layer (cold neurons on the host CPU) ...")
+        hybrid = hybrid_bench(cfg, specs, dls, args.hybrid_steps, 1)
+
     sweep = None
     batches = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []
     if batches and B == 1:
@@ -614,7 +679,7 @@ def main():
                    "kernel_gbps": {k: round(v, 1) for k, v in achieved.items()},
                    "graph": use_graph, "setup_s": round(setup_s, 1), "wall_s": round(wall, 4),
                    "event_ms": round(gpu_ms, 3),
-                   "batch_sweep": sweep},
+                   "batch_sweep": sweep, "hybrid": hybrid},
     }
     print(json.dumps(out), flush=True)
 

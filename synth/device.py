@@ -90,3 +90,30 @@ class DeviceLayer:
         self.layer_c = self.layer._c()
 
 
+
+
+class HostColdLayer:
+    """One layer's CPU-resident (cold) neurons in host memory, generated on the device
+    (the same bits as the host generator) and copied out: W1, W2 (and Wup) rows of the
+    CPU table's neurons in CPU-table slot order, and their b1."""
+
+    def __init__(self, spec: synth.LayerSpec, device="cuda:0"):
+        torch = _torch()
+        cfg, L = spec.cfg, spec.layer
+        sig = spec.sigmas()
+        d, n_c = cfg.d, len(spec.T_c)
+        self.n_c = n_c
+        T_c = torch.from_numpy(spec.T_c).to(device)
+
+        def host_rows(tag):
+            m = dev_matrix(max(n_c, 1), d, cfg.wdtype, device)
+            if n_c:
+                fill_matrix(m, cfg.wdtype, cfg.seed, tag, L, d, sig[tag], T_c, n_c)
+            out = Matrix(m.data.cpu(), m.dtype, m.scales.cpu() if m.scales is not None else None)
+            del m
+            return out
+        self.W1 = host_rows(synth.TAG_W1)
+        self.W2 = host_rows(synth.TAG_W2)
+        self.Wup = host_rows(synth.TAG_WUP) if cfg.gated else None
+        b = np.ascontiguousarray(spec.b1[spec.T_c] if n_c else spec.b1[:1])
+        self.b1 = Vector(b if cfg.bdtype == synth.F32 else b.view(np.uint16), PI_F32 if cfg.bdtype == synth.F32 else PI_F16)

@@ -1,0 +1,126 @@
+"""The CPU side of the hybrid layer (libpi_host, include/pi_host.h), on the CPU:
+parity with the oracle's sparse FFN over the cold rows, bitwise repeatability
+over thread counts and between the AVX2 and scalar paths, the exported
+symbols and the argument checks."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+import oracle as orc
+import activation_sparse_amd as pi
+from activation_sparse_amd import host
+from tests import parity_harness as ph
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_host_symbols():
+    text = open(os.path.join(ROOT, "include", "pi_host.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|int32_t|size_t)\s+(pi_\w+)\s*\(", text, re.M)))
+
+
+def test_host_header_and_library_agree():
+    assert declared_host_symbols() == sorted(host.EXPORTS)
+    L = host.load()
+    for name in declared_host_symbols():
+        assert hasattr(L, name), name
+
+
+def _case(dt, n_c, d, seed, gated=False, bias=True):
+    """Cold rows of one layer: W1 (+ Wup), b1 placing each neuron's activation
+    probability near 1/2, W2; stored as the formats of pi.h."""
+    W1 = ph.host_mat(dt, seed, synth.TAG_W1, 0, d, 1 / np.sqrt(d), nrows=n_c)
+    W2 = ph.host_mat(dt, seed, synth.TAG_W2, 0, d, 1 / np.sqrt(4 * d), nrows=n_c)
+    Wup = ph.host_mat(dt, seed, synth.TAG_WUP, 0, d, 1 / np.sqrt(d), nrows=n_c) if gated else None
+    b1 = None
+    if bias:
+        g = np.random.default_rng(seed)
+        b1 = orc.Vec((g.standard_normal(n_c) * 0.3).astype(np.float16).view(np.uint16), orc.F16)
+    return W1, b1, Wup, W2
+
+
+def _pm(m):
+    return None if m is None else pi.Matrix(m.data, m.dtype, m.scales)
+
+
+def _pv(v):
+    return pi.Vector(None, pi.PI_F32) if v is None else pi.Vector(v.data, v.dtype)
+
+
+def _run_host(x, W1, b1, Wup, W2, A_c, n_c, threads=0, path=-1):
+    B, d = x.shape
+    y = np.full((B, d), np.nan, np.float32)
+    host.pi_cold_ffn(B, d, n_c, x, _pm(W1), _pv(b1), _pm(W2), A_c, len(A_c), y,
+                     kind=pi.PI_GATED_RELU if Wup is not None else pi.PI_RELU, Wup=_pm(Wup), threads=threads, path=path)
+    return y
+
+
+CASES = [("f16", synth.F16, False), ("f32", synth.F32, False), ("i4", synth.I4G128, False),
+         ("f16-gated", synth.F16, True)]
+
+
+@pytest.mark.parametrize("B", [1, 3, 32])
+@pytest.mark.parametrize("key,dt,gated", CASES, ids=[c[0] for c in CASES])
+def test_cold_ffn_matches_the_oracle(key, dt, gated, B):
+    """y_c against the oracle's fp64 sparse FFN on the same stored weights and list
+    (the cold side computes exactly what the GPU side computes, over the CPU table)."""
+    n_c, d = 700, 512
+    W1, b1, Wup, W2 = _case(dt, n_c, d, 31 + B, gated)
+    g = np.random.default_rng(7 + B)
+    A_c = np.sort(g.choice(n_c, size=230, replace=False)).astype(np.int32)
+    x = g.standard_normal((B, d)).astype(np.float32)
+    y = _run_host(x, W1, b1, Wup, W2, A_c, n_c)
+    ref = orc.sparse_ffn(x, W1, b1 if b1 is not None else orc.Vec(None), W2, A_c,
+                         kind=orc.GATED_RELU if gated else orc.RELU, Wup=Wup)
+    assert ph.rel_err(y.astype(np.float64), ref) <= ph.RTOL
+    # fp32 sums of unit-scale terms over d = 512: far inside the bound
+    assert ph.rel_err(y.astype(np.float64), ref) <= 1e-5
+
+
+def test_bits_do_not_depend_on_threads_or_vector_unit():
+    n_c, d, B = 900, 1024, 4
+    W1, b1, _, W2 = _case(synth.F16, n_c, d, 5)
+    g = np.random.default_rng(11)
+    A_c = np.sort(g.choice(n_c, size=400, replace=False)).astype(np.int32)
+    x = g.standard_normal((B, d)).astype(np.float32)
+    outs = [_run_host(x, W1, b1, None, W2, A_c, n_c, threads=t) for t in (1, 3, 8)]
+    outs.append(_run_host(x, W1, b1, None, W2, A_c, n_c, threads=4, path=0))
+    if host.vector_path() == 1:
+        outs.append(_run_host(x, W1, b1, None, W2, A_c, n_c, threads=2, path=1))
+    for o in outs[1:]:
+        assert o.tobytes() == outs[0].tobytes()
+
+
+def test_empty_list_and_inactive_neurons():
+    """K_c = 0 gives y_c = 0; neurons whose FC1 output is 0 add nothing (ReLU gate)."""
+    n_c, d = 64, 256
+    W1, _, _, W2 = _case(synth.F16, n_c, d, 3, bias=False)
+    x = np.random.default_rng(2).standard_normal((2, d)).astype(np.float32)
+    y = _run_host(x, W1, None, None, W2, np.zeros(0, np.int32), n_c)
+    assert not np.any(y)
+    # a bias of -1e4 turns every listed neuron off
+    off = orc.Vec(np.full(n_c, -1e4, np.float32), orc.F32)
+    y = _run_host(x, W1, off, None, W2, np.arange(n_c, dtype=np.int32), n_c)
+    assert not np.any(y)
+
+
+def test_argument_checks():
+    n_c, d = 16, 64
+    W1, b1, _, W2 = _case(synth.F16, n_c, d, 9)
+    x = np.zeros((1, d), np.float32)
+    y = np.zeros((1, d), np.float32)
+    bad_slot = np.array([0, n_c], np.int32)
+    with pytest.raises(pi.PiError, match="EINVAL"):
+        host.pi_cold_ffn(1, d, n_c, x, _pm(W1), _pv(b1), _pm(W2), bad_slot, 2, y)
+    with pytest.raises(pi.PiError, match="EINVAL"):
+        host.pi_cold_ffn(33, d, n_c, x, _pm(W1), _pv(b1), _pm(W2), bad_slot[:1], 1, y)
+    with pytest.raises(pi.PiError, match="EINVAL"):
+        host.pi_cold_ffn(1, 60, n_c, x, _pm(W1), _pv(b1), _pm(W2), bad_slot[:1], 1, y)
+    W2_32 = pi.Matrix(np.zeros((n_c, d), np.float32), pi.PI_F32)
+    with pytest.raises(pi.PiError, match="EUNSUPPORTED"):
+        host.pi_cold_ffn(1, d, n_c, x, _pm(W1), _pv(b1), W2_32, bad_slot[:1], 1, y)
+    with pytest.raises(pi.PiError, match="EINVAL"):
+        host.pi_cold_ffn(1, d, n_c, x, _pm(W1), _pv(b1), _pm(W2), bad_slot[:1], 1, y, kind=pi.PI_GATED_RELU)
