@@ -19,6 +19,7 @@ PI_OK, PI_EINVAL, PI_EWORKSPACE, PI_EUNSUPPORTED, PI_EHIP = 0, 1, 2, 3, 4
 PI_OP_PREDICT, PI_OP_COMPACT, PI_OP_SPARSE_FFN, PI_OP_MERGE, PI_OP_FFN_LAYER, PI_OP_PREDICT_OUTPUT = 0, 1, 2, 3, 4, 5
 PI_STAGE_HIDDEN, PI_STAGE_OUTPUT, PI_STAGE_FC1, PI_STAGE_FC2, PI_STAGE_SUM, PI_STAGE_ALL = 1, 2, 4, 8, 16, 31
 PI_MAX_BATCH = 32
+PI_MAX_NEURONS = 65536
 PI_ABI_VERSION = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -50,9 +50,16 @@ def build_libpi(jobs: int = 8) -> str:
     return LIBPI
 
 
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
 def build_libpi_host() -> str:
+    """libpi_host.so: the host operator and the hybrid executor, which drives libpi and the HIP
+    runtime (so libpi.so must be built first; found next to it at run time)."""
     tmp_so = LIBHOST + ".tmp"
-    _run(["g++", *HOST_FLAGS, "-shared", os.path.join(CSRC, "pi_host.cpp"), "-o", tmp_so])
+    _run(["g++", *HOST_FLAGS, "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", "-shared",
+          os.path.join(CSRC, "pi_host.cpp"), os.path.join(CSRC, "pi_hybrid.cpp"), "-o", tmp_so,
+          f"-L{PKG}", "-lpi", f"-L{ROCM}/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN", f"-Wl,-rpath,{ROCM}/lib"])
     os.replace(tmp_so, LIBHOST)
     return LIBHOST
 
@@ -62,7 +69,7 @@ def build_all() -> None:
     import synth
     import oracle
     with ThreadPoolExecutor(max_workers=4) as ex:
-        futs = [ex.submit(build_libpi), ex.submit(build_libpi_host), ex.submit(synth.build_host),
+        futs = [ex.submit(lambda: (build_libpi(), build_libpi_host())), ex.submit(synth.build_host),
                 ex.submit(oracle.build), ex.submit(_run, synth.build_gpu_cmd())]
         for f in futs:
             f.result()

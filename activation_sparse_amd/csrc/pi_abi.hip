@@ -344,6 +344,7 @@ int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float ta
   if (!valid_batch(B) || N <= 0 || n_g < 0 || !logits || !K) return PI_EINVAL;
   if (n_g > 0 && (!T_g || !A_g)) return PI_EINVAL;
   if (T_c && (n_c < 0 || !A_c || !K_c)) return PI_EINVAL;
+  if (N > PI_MAX_NEURONS) return PI_EUNSUPPORTED;
   if (!T_c) n_c = 0;
   return hip_status(pi::launch_compact(B, N, logits, tau, T_g, n_g, A_g, K, T_c, n_c, A_c, K_c,
                                        static_cast<hipStream_t>(stream)));
@@ -460,6 +461,7 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
   if (!L) return PI_EINVAL;
   const int32_t d = L->d, N = L->N, H = L->H, n_g = L->n_g;
   if (N <= 0 || H <= 0 || n_g > N) return PI_EINVAL;
+  if (N > PI_MAX_NEURONS) return PI_EUNSUPPORTED;
   if (stages == 0 || (stages & ~(uint32_t)PI_STAGE_ALL)) return PI_EINVAL;
   int st = validate_ffn(B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2);
   if (st != PI_OK) return st;

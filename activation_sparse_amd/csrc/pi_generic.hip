@@ -96,75 +96,91 @@ __global__ __launch_bounds__(kThreads) void k_rowdot(RowdotArgs a, int64_t n_row
 
 constexpr int kCompactThreads = 1024;
 constexpr int kCompactWaves = kCompactThreads / kWave;   // 16
-constexpr int kCompactChunks = 64;                       // slots per pass: 64 * 1024
+constexpr int kCompactIn = 8;                            // loads in flight per lane in phases 1 and 2
 
+// Standalone compaction over any table order, in blocks that wait for no other:
+// block (c, t) owns slots [c0, c1) of table t (0: GPU, 1: CPU).  It first
+// rebuilds every activation word in LDS from the logits (union over the batch,
+// one wave ballot per 64 ids), then counts the table's active slots below c0
+// (T[s] looked up in those words), and then writes its own active slots in
+// ascending order at that offset, a wave ballot and a block prefix sum per pass
+// of kCompactThreads slots.  The block owning the last slot writes the count.
 __global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const float* __restrict__ logits,
                                                              float tau, const int32_t* T_g, int n_g,
                                                              int32_t* A_g, int32_t* K_g, const int32_t* T_c,
-                                                             int n_c, int32_t* A_c, int32_t* K_c) {
-  const int32_t* T = blockIdx.x == 0 ? T_g : T_c;
-  const int n = blockIdx.x == 0 ? n_g : n_c;
-  int32_t* A = blockIdx.x == 0 ? A_g : A_c;
-  int32_t* Kout = blockIdx.x == 0 ? K_g : K_c;
-  __shared__ int cnt[kCompactChunks * kCompactWaves];
+                                                             int n_c, int32_t* A_c, int32_t* K_c, int chunk) {
+  const int32_t* T = blockIdx.y == 0 ? T_g : T_c;
+  const int n = blockIdx.y == 0 ? n_g : n_c;
+  int32_t* A = blockIdx.y == 0 ? A_g : A_c;
+  int32_t* Kout = blockIdx.y == 0 ? K_g : K_c;
+  const int c0 = (int)blockIdx.x * chunk;
+  if (c0 >= n && !(c0 == 0 && n == 0)) return;            // past the table (block-uniform)
+  const int c1 = c0 + chunk < n ? c0 + chunk : n;
+  extern __shared__ uint64_t words[];                      // ceil(N / 64)
   __shared__ int wtot[kCompactWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int nw = (N + 63) / 64;
+  // 1. the activation words, kCompactIn groups of 64 ids per wave per round (all loads in flight)
+  for (int g0 = wv * kCompactIn; g0 < nw; g0 += kCompactWaves * kCompactIn) {
+    bool f[kCompactIn];
+#pragma unroll
+    for (int q = 0; q < kCompactIn; ++q) f[q] = false;
+    for (int b = 0; b < B; ++b) {
+      float z[kCompactIn];
+#pragma unroll
+      for (int q = 0; q < kCompactIn; ++q) {
+        const int id = (g0 + q) * 64 + lane;
+        z[q] = (g0 + q < nw && id < N) ? logits[(int64_t)b * N + id] : tau;
+      }
+#pragma unroll
+      for (int q = 0; q < kCompactIn; ++q) f[q] = f[q] || z[q] > tau;
+    }
+#pragma unroll
+    for (int q = 0; q < kCompactIn; ++q) {
+      const uint64_t w = __ballot(f[q]);
+      if (lane == 0 && g0 + q < nw) words[g0 + q] = w;
+    }
+  }
+  __syncthreads();
+  auto bit = [&](int id) { return id >= 0 && id < N && ((words[id >> 6] >> (id & 63)) & 1ull); };
+  auto active = [&](int s) { return bit(T[s]); };
+  // 2. active slots below c0 (kCompactIn table entries per lane in flight)
+  int below = 0;
+  for (int s0 = tid; s0 < c0; s0 += kCompactThreads * kCompactIn) {
+    int ids[kCompactIn];
+#pragma unroll
+    for (int q = 0; q < kCompactIn; ++q) {
+      const int s = s0 + q * kCompactThreads;
+      ids[q] = s < c0 ? T[s] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < kCompactIn; ++q) below += bit(ids[q]) ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) below += __shfl_xor(below, off, kWave);
+  if (lane == 0) wtot[wv] = below;
+  __syncthreads();
   int base = 0;
-  for (int s0 = 0; s0 < n; s0 += kCompactChunks * kCompactThreads) {
-    const int nch = min(kCompactChunks, (n - s0 + kCompactThreads - 1) / kCompactThreads);
-    int ids[kCompactChunks];
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) {
-      const int s = s0 + c * kCompactThreads + tid;
-      ids[c] = (c < nch && s < n) ? T[s] : -1;
-    }
-    uint64_t flags = 0;
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) {
-      bool f = false;
-      if (c < nch) {
-        const int id = ids[c];
-        if (id >= 0 && id < N)
-          for (int b = 0; b < B; ++b) f = f || (logits[(int64_t)b * N + id] > tau);
-        const uint64_t bal = __ballot(f);
-        if (lane == 0) cnt[c * kCompactWaves + wv] = __popcll(bal);
-      }
-      flags |= (uint64_t)f << c;
-    }
+  for (int w = 0; w < kCompactWaves; ++w) base += wtot[w];
+  __syncthreads();
+  // 3. this block's slots, ascending
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int p0 = c0; p0 < c1; p0 += kCompactThreads) {
+    const int s = p0 + tid;
+    const bool f = s < c1 && active(s);
+    const uint64_t bal = __ballot(f);
+    if (lane == 0) wtot[wv] = __popcll(bal);
     __syncthreads();
-    // exclusive scan of cnt[0 .. nch*16) in (chunk, wave) order, one entry per thread
-    const int nent = nch * kCompactWaves;
-    const int v = tid < nent ? cnt[tid] : 0;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += t;
-    }
-    if (lane == kWave - 1) wtot[wv] = incl;
-    __syncthreads();
-    int wpre = 0, total = 0;
+    int pre = 0, tot = 0;
     for (int w = 0; w < kCompactWaves; ++w) {
-      const int t = wtot[w];
-      if (w < wv) wpre += t;
-      total += t;
+      if (w < wv) pre += wtot[w];
+      tot += wtot[w];
     }
-    __syncthreads();
-    if (tid < nent) cnt[tid] = wpre + incl - v;
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < kCompactChunks; ++c) {
-      if (c < nch) {
-        const bool f = (flags >> c) & 1ull;
-        const uint64_t bal = __ballot(f);
-        if (f) A[base + cnt[c * kCompactWaves + wv] + __popcll(bal & lt_mask)] = s0 + c * kCompactThreads + tid;
-      }
-    }
-    base += total;
+    if (f) A[base + pre + __popcll(bal & lt_mask)] = s;
+    base += tot;
     __syncthreads();
   }
-  if (tid == 0) *Kout = base;
+  if (c1 == n && tid == 0) *Kout = base;
 }
 
 __global__ __launch_bounds__(kThreads) void k_merge(int64_t n, int d, float* y, const float* y_c,
@@ -236,9 +252,15 @@ hipError_t launch_rowdot(const RowdotArgs& a, hipStream_t s) { return launch_row
 hipError_t launch_compact(int B, int N, const float* logits, float tau, const int32_t* T_g, int n_g,
                           int32_t* A_g, int32_t* K, const int32_t* T_c, int n_c, int32_t* A_c,
                           int32_t* K_c, hipStream_t s) {
-  const int blocks = T_c ? 2 : 1;
-  hipLaunchKernelGGL(k_compact, dim3(blocks), dim3(kCompactThreads), 0, s, B, N, logits, tau, T_g, n_g, A_g, K,
-                     T_c, n_c, A_c, K_c);
+  // about 32 blocks per table, whole passes of slots each
+  const int nmax = n_g > n_c ? n_g : n_c;
+  int chunk = (nmax + 31) / 32;
+  chunk = (chunk + kCompactThreads - 1) / kCompactThreads * kCompactThreads;
+  if (chunk < kCompactThreads) chunk = kCompactThreads;
+  const int blocks = (nmax + chunk - 1) / chunk > 0 ? (nmax + chunk - 1) / chunk : 1;
+  const size_t shm = (size_t)((N + 63) / 64) * 8;
+  hipLaunchKernelGGL(k_compact, dim3((unsigned)blocks, T_c ? 2u : 1u), dim3(kCompactThreads), shm, s, B, N, logits,
+                     tau, T_g, n_g, A_g, K, T_c, n_c, A_c, K_c, chunk);
   return hipGetLastError();
 }
 

@@ -11,10 +11,22 @@ import ctypes as C
 import os
 from typing import Optional
 
-from . import PiError, Matrix, Vector, _Mat, _Vec, PI_OK, PI_RELU
+from . import PiError, Matrix, Vector, _Mat, _Vec, _Layer, PI_OK, PI_RELU
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpi_host.so")
-EXPORTS = ("pi_cold_ffn", "pi_cold_ffn_ex", "pi_host_vector_path")
+EXPORTS = ("pi_cold_ffn", "pi_cold_ffn_ex", "pi_host_vector_path", "pi_hybrid_layer")
+
+class _HostCold(C.Structure):
+    _fields_ = [("n_c", C.c_int32), ("W1", _Mat), ("b1", _Vec), ("Wup", _Mat), ("W2", _Mat)]
+
+
+class _HybridScratch(C.Structure):
+    _fields_ = [("logits", C.c_void_p), ("A_g", C.c_void_p), ("K", C.c_void_p), ("A_c", C.c_void_p),
+                ("K_c", C.c_void_p), ("y_c", C.c_void_p), ("ws_pred", C.c_void_p), ("ws_pred_bytes", C.c_size_t),
+                ("ws_ffn", C.c_void_p), ("ws_ffn_bytes", C.c_size_t), ("x_host", C.c_void_p),
+                ("A_c_host", C.c_void_p), ("K_c_host", C.c_void_p), ("y_c_host", C.c_void_p),
+                ("event", C.c_void_p)]
+
 
 _lib = None
 
@@ -32,6 +44,9 @@ def load():
         L.pi_cold_ffn_ex.argtypes = [I, I, I, I, P, _Mat, _Vec, _Mat, _Mat, P, I, P, I, I]
         L.pi_cold_ffn_ex.restype = C.c_int
         L.pi_host_vector_path.restype = C.c_int
+        L.pi_hybrid_layer.argtypes = [P, C.POINTER(_Layer), P, P, C.POINTER(_HostCold), I, P, C.c_float, P,
+                                      C.POINTER(_HybridScratch), I, C.POINTER(C.c_int32)]
+        L.pi_hybrid_layer.restype = C.c_int
         _lib = L
     return _lib
 
@@ -74,3 +89,14 @@ def pi_cold_ffn(B: int, d: int, n_c: int, x, W1: Matrix, b1: Optional[Vector], W
 def vector_path() -> int:
     """1 when pi_cold_ffn runs its AVX2 + FMA + F16C loops on this CPU, 0 for the scalar ones."""
     return load().pi_host_vector_path()
+
+
+def pi_hybrid_layer(stream: int, layer_c, T_g: int, T_c: Optional[int], cold_c, B: int, x: int, tau: float, y: int,
+                    scratch_c, threads: int = 0) -> int:
+    """One hybrid layer (see pi_host.h); pointers are ints, the structs prebuilt; returns K_c."""
+    kc = C.c_int32(0)
+    st = load().pi_hybrid_layer(stream, C.byref(layer_c), T_g, T_c, C.byref(cold_c) if cold_c is not None else None,
+                                B, x, float(tau), y, C.byref(scratch_c), threads, C.byref(kc))
+    if st != PI_OK:
+        raise PiError(f"pi_hybrid_layer: {_STATUS.get(st, st)}")
+    return kc.value

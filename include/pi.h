@@ -55,6 +55,10 @@ extern "C" {
 
 #define PI_ABI_VERSION 2
 #define PI_MAX_BATCH 32
+/* Largest neuron count N of pi_compact and the layer entry points: each
+ * workgroup that builds the active lists holds the activation decision of
+ * every neuron id in its LDS. */
+#define PI_MAX_NEURONS 65536
 
 enum pi_dtype { PI_F32 = 0, PI_F16 = 1, PI_I4G128 = 2 };
 enum pi_ffn_kind { PI_RELU = 0, PI_GATED_RELU = 1 };
@@ -115,7 +119,8 @@ int pi_predict_output(void* stream, int32_t B, int32_t H, int32_t N, const float
  * CPU neuron table.  A_g needs n_g entries, A_c n_c.  K, K_c: one device
  * int32 each.  ws may be NULL (pi_workspace_bytes returns 0).
  * Errors: PI_EINVAL for a NULL required pointer, B outside 1..PI_MAX_BATCH,
- * n_g < 0, N <= 0, or T_c given without A_c/K_c. */
+ * n_g < 0, N <= 0, or T_c given without A_c/K_c; PI_EUNSUPPORTED for
+ * N > PI_MAX_NEURONS. */
 int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float tau,
                const int32_t* T_g, int32_t n_g, int32_t* A_g, int32_t* K,
                const int32_t* T_c, int32_t n_c, int32_t* A_c, int32_t* K_c,
@@ -208,7 +213,7 @@ typedef struct pi_layer {
  * ordered sum with the merge (per-stage timing).  At batch 1 the output
  * layer, the decision and FC1 run as one kernel per tile of neuron ids
  * (events 2 and 3 are then recorded together) and FC2 also writes the lists.
- * Errors: as the separate calls. */
+ * Errors: as the separate calls (PI_EUNSUPPORTED for N > PI_MAX_NEURONS). */
 int pi_ffn_layer(void* stream, const pi_layer* layer, int32_t B, const float* x, float tau,
                  const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
                  int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, void* const* events);

@@ -135,6 +135,8 @@ def test_ffn_layer_stages_rejects_bad_stage_sets_and_shapes():
     assert call(pi.PI_STAGE_ALL, layer=_layer(N=1020)) == pi.PI_EINVAL     # P2 [H x N] rows need N % 8 == 0
     assert call(pi.PI_STAGE_ALL, layer=_layer(n_g=2048)) == pi.PI_EINVAL   # more GPU neurons than N
     assert call(pi.PI_STAGE_ALL, B=33) == pi.PI_EINVAL
+    big = pi.PI_MAX_NEURONS + 8                                          # the lists' LDS bound
+    assert call(pi.PI_STAGE_ALL, layer=_layer(N=big, n_g=big)) == pi.PI_EUNSUPPORTED
     assert status(pi.pi_ffn_layer_stages, L, 1, FAKE, 0.0, None, FAKE, None, FAKE, FAKE, None, None, FAKE,
                   pi.PI_STAGE_ALL, None, 64, None, 0) == pi.PI_EWORKSPACE
 
@@ -160,6 +162,8 @@ def test_compact_and_merge_reject_bad_arguments():
     assert status(pi.pi_compact, 1, 0, FAKE, 0.0, FAKE, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL
     assert status(pi.pi_compact, 1, 100, FAKE, 0.0, None, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL
     assert status(pi.pi_compact, 1, 100, FAKE, 0.0, FAKE, 10, FAKE, FAKE, FAKE, 5, None, FAKE, 0) == pi.PI_EINVAL
+    big = pi.PI_MAX_NEURONS + 1
+    assert status(pi.pi_compact, 1, big, FAKE, 0.0, FAKE, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EUNSUPPORTED
     assert status(pi.pi_merge, 0, 16, FAKE, FAKE, None, None, 0) == pi.PI_EINVAL
     assert status(pi.pi_merge, 1, 16, None, FAKE, None, None, 0) == pi.PI_EINVAL
     # nothing to add: accepted without any launch

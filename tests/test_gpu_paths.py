@@ -174,7 +174,7 @@ def test_hybrid_layer(B):
     hy = HybridLayer(ph.DeviceLayer(spec), HostColdLayer(spec), B)
     x = synth.host_x(cfg.seed, 0, 5, B, cfg.d)
     y = torch.empty((B, cfg.d), dtype=torch.float32, device="cuda")
-    kc = hy(torch.from_numpy(x).cuda(), x, y)
+    kc = hy(torch.from_numpy(x).cuda(), y)
     torch.cuda.synchronize()
     K = int(hy.K.cpu()[0])
     A_g, A_c = hy.A_g.cpu().numpy()[:K], hy.A_c.cpu().numpy()[:kc]
@@ -197,6 +197,53 @@ def test_hybrid_layer_skips_the_merge_without_cold_neurons():
     hy = HybridLayer(ph.DeviceLayer(spec), HostColdLayer(spec), 1)
     x = synth.host_x(cfg.seed, 0, 5, 1, cfg.d)
     y = torch.full((1, cfg.d), 7.0, dtype=torch.float32, device="cuda")
-    kc = hy(torch.from_numpy(x).cuda(), x, y, tau=1e30)
+    kc = hy(torch.from_numpy(x).cuda(), y, tau=1e30)
     torch.cuda.synchronize()
     assert kc == 0 and int(hy.K.cpu()[0]) == 0 and not torch.any(y).item()
+
+
+COMPACT_CASES = [  # (N, n_g, B, density): ragged table sizes, both tables split over many blocks
+    (28672, 20071, 1, 0.1), (28672, 20071, 3, 0.05), (28672, 9000, 32, 0.01), (4097, 4097, 2, 0.5),
+    (65536, 40000, 4, 0.2), (1000, 0, 1, 0.3), (2048, 1, 5, 0.9)]
+
+
+@pytest.mark.parametrize("N,n_g,B,density", COMPACT_CASES)
+def test_compact_lists_are_exact_over_any_table_order(N, n_g, B, density):
+    """pi_compact against the oracle's compaction, bit for bit: tables in a random order
+    (slot order need not follow the ids), logits that tie with tau (not active: the
+    compare is strict), neurons active for one batch row only (the union)."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    g = np.random.default_rng(N + 7 * n_g + B)
+    perm = g.permutation(N).astype(np.int32)
+    T_g, T_c = perm[:n_g].copy(), perm[n_g:].copy()
+    tau = 0.25
+    z = g.standard_normal((B, N)).astype(np.float32) - 2.0
+    on = g.random((B, N)) < density / B
+    z[on] = tau + np.abs(z[on]) + 1e-3
+    z[g.random((B, N)) < 0.02] = tau                      # ties: inactive
+    A_g_or, A_c_or = orc.compact(z.astype(np.float64), tau, T_g, T_c)
+    dev = "cuda:0"
+    i32 = torch.int32
+    logits = torch.from_numpy(z).to(dev)
+    Tg = torch.from_numpy(T_g if n_g else np.zeros(1, np.int32)).to(dev)
+    Tc = torch.from_numpy(T_c if len(T_c) else np.zeros(1, np.int32)).to(dev)   # n_c = 0: a table, empty
+    A_g = torch.full((max(n_g, 1),), -7, dtype=i32, device=dev)
+    A_c = torch.full((max(N - n_g, 1),), -7, dtype=i32, device=dev)
+    K = torch.full((1,), -1, dtype=i32, device=dev)
+    K_c = torch.full((1,), -1, dtype=i32, device=dev)
+    print(f"pi_compact N={N} n_g={n_g} B={B}", flush=True)
+    for _ in range(2):                                    # the second call overwrites the first
+        pi.pi_compact(B, N, logits, tau, Tg, n_g, A_g, K, Tc, N - n_g, A_c, K_c)
+    torch.cuda.synchronize()
+    k, kc = int(K.cpu()[0]), int(K_c.cpu()[0])
+    assert k == len(A_g_or) and kc == len(A_c_or)
+    assert np.array_equal(A_g.cpu().numpy()[:k], A_g_or)
+    assert np.array_equal(A_c.cpu().numpy()[:kc], A_c_or)
+    # entries past the counts are untouched
+    assert np.all(A_g.cpu().numpy()[k:] == -7) and np.all(A_c.cpu().numpy()[kc:] == -7)
+    # without the cold table only the GPU list is written
+    K.fill_(-1)
+    pi.pi_compact(B, N, logits, tau, Tg, n_g, A_g, K)
+    torch.cuda.synchronize()
+    assert int(K.cpu()[0]) == k and np.array_equal(A_g.cpu().numpy()[:k], A_g_or)
