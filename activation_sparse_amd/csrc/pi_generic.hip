@@ -96,15 +96,19 @@ __global__ __launch_bounds__(kThreads) void k_rowdot(RowdotArgs a, int64_t n_row
 
 constexpr int kCompactThreads = 1024;
 constexpr int kCompactWaves = kCompactThreads / kWave;   // 16
-constexpr int kCompactIn = 8;                            // loads in flight per lane in phases 1 and 2
+constexpr int kCompactLogits = 32;                       // logit loads in flight per lane: 32768 ids per round
+constexpr int kCompactBelow = 16;                        // table loads in flight per lane for the count below c0
+constexpr int kCompactOwn = 2;                           // own slots per lane (chunk <= 2 * kCompactThreads)
 
-// Standalone compaction over any table order, in blocks that wait for no other:
-// block (c, t) owns slots [c0, c1) of table t (0: GPU, 1: CPU).  It first
-// rebuilds every activation word in LDS from the logits (union over the batch,
-// one wave ballot per 64 ids), then counts the table's active slots below c0
-// (T[s] looked up in those words), and then writes its own active slots in
-// ascending order at that offset, a wave ballot and a block prefix sum per pass
-// of kCompactThreads slots.  The block owning the last slot writes the count.
+// Standalone compaction over any table order, in blocks that wait for no other
+// and keep their global loads in flight together (the stage sits between two
+// dependent launches, so its latency is what counts): block (c, t) owns slots
+// [c0, c1) of table t (0: GPU, 1: CPU).  It issues the table loads of its own
+// slots and of the first slots below c0, rebuilds every activation word in LDS
+// from the logits (union over the batch, one wave ballot per 64 ids), counts
+// the table's active slots below c0, and writes its own active slots in
+// ascending order at that offset (wave ballot + block prefix sum per pass of
+// kCompactThreads slots).  The block owning the last slot writes the count.
 __global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const float* __restrict__ logits,
                                                              float tau, const int32_t* T_g, int n_g,
                                                              int32_t* A_g, int32_t* K_g, const int32_t* T_c,
@@ -120,41 +124,52 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const
   __shared__ int wtot[kCompactWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int nw = (N + 63) / 64;
-  // 1. the activation words, kCompactIn groups of 64 ids per wave per round (all loads in flight)
-  for (int g0 = wv * kCompactIn; g0 < nw; g0 += kCompactWaves * kCompactIn) {
-    bool f[kCompactIn];
+  // table ids: own slots (at most kCompactOwn passes) and the first round below c0
+  int own[kCompactOwn], low[kCompactBelow];
 #pragma unroll
-    for (int q = 0; q < kCompactIn; ++q) f[q] = false;
+  for (int q = 0; q < kCompactOwn; ++q) {
+    const int s = c0 + q * kCompactThreads + tid;
+    own[q] = s < c1 ? T[s] : -1;
+  }
+#pragma unroll
+  for (int q = 0; q < kCompactBelow; ++q) {
+    const int s = q * kCompactThreads + tid;
+    low[q] = s < c0 ? T[s] : -1;
+  }
+  // 1. the activation words: group g of 64 ids is wave (g / kCompactLogits) % kCompactWaves's
+  for (int g0 = wv * kCompactLogits; g0 < nw; g0 += kCompactWaves * kCompactLogits) {
+    uint32_t f = 0;                                        // bit q: group g0 + q active at this lane
     for (int b = 0; b < B; ++b) {
-      float z[kCompactIn];
+      const float* row = logits + (int64_t)b * N;
+      float z[kCompactLogits];
 #pragma unroll
-      for (int q = 0; q < kCompactIn; ++q) {
+      for (int q = 0; q < kCompactLogits; ++q) {
         const int id = (g0 + q) * 64 + lane;
-        z[q] = (g0 + q < nw && id < N) ? logits[(int64_t)b * N + id] : tau;
+        z[q] = id < N ? row[id] : tau;
       }
 #pragma unroll
-      for (int q = 0; q < kCompactIn; ++q) f[q] = f[q] || z[q] > tau;
+      for (int q = 0; q < kCompactLogits; ++q) f |= (z[q] > tau ? 1u : 0u) << q;
     }
 #pragma unroll
-    for (int q = 0; q < kCompactIn; ++q) {
-      const uint64_t w = __ballot(f[q]);
+    for (int q = 0; q < kCompactLogits; ++q) {
+      const uint64_t w = __ballot((f >> q) & 1u);
       if (lane == 0 && g0 + q < nw) words[g0 + q] = w;
     }
   }
   __syncthreads();
   auto bit = [&](int id) { return id >= 0 && id < N && ((words[id >> 6] >> (id & 63)) & 1ull); };
-  auto active = [&](int s) { return bit(T[s]); };
-  // 2. active slots below c0 (kCompactIn table entries per lane in flight)
+  // 2. active slots below c0
   int below = 0;
-  for (int s0 = tid; s0 < c0; s0 += kCompactThreads * kCompactIn) {
-    int ids[kCompactIn];
 #pragma unroll
-    for (int q = 0; q < kCompactIn; ++q) {
+  for (int q = 0; q < kCompactBelow; ++q) below += bit(low[q]) ? 1 : 0;
+  for (int s0 = kCompactBelow * kCompactThreads + tid; s0 < c0; s0 += kCompactThreads * kCompactBelow) {
+#pragma unroll
+    for (int q = 0; q < kCompactBelow; ++q) {
       const int s = s0 + q * kCompactThreads;
-      ids[q] = s < c0 ? T[s] : -1;
+      low[q] = s < c0 ? T[s] : -1;
     }
 #pragma unroll
-    for (int q = 0; q < kCompactIn; ++q) below += bit(ids[q]) ? 1 : 0;
+    for (int q = 0; q < kCompactBelow; ++q) below += bit(low[q]) ? 1 : 0;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) below += __shfl_xor(below, off, kWave);
@@ -165,9 +180,10 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const
   __syncthreads();
   // 3. this block's slots, ascending
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int p0 = c0; p0 < c1; p0 += kCompactThreads) {
-    const int s = p0 + tid;
-    const bool f = s < c1 && active(s);
+#pragma unroll
+  for (int q = 0; q < kCompactOwn; ++q) {
+    if (c0 + q * kCompactThreads >= c1) break;              // block-uniform
+    const bool f = bit(own[q]);
     const uint64_t bal = __ballot(f);
     if (lane == 0) wtot[wv] = __popcll(bal);
     __syncthreads();
@@ -176,7 +192,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const
       if (w < wv) pre += wtot[w];
       tot += wtot[w];
     }
-    if (f) A[base + pre + __popcll(bal & lt_mask)] = s;
+    if (f) A[base + pre + __popcll(bal & lt_mask)] = c0 + q * kCompactThreads + tid;
     base += tot;
     __syncthreads();
   }
@@ -252,11 +268,10 @@ hipError_t launch_rowdot(const RowdotArgs& a, hipStream_t s) { return launch_row
 hipError_t launch_compact(int B, int N, const float* logits, float tau, const int32_t* T_g, int n_g,
                           int32_t* A_g, int32_t* K, const int32_t* T_c, int n_c, int32_t* A_c,
                           int32_t* K_c, hipStream_t s) {
-  // about 32 blocks per table, whole passes of slots each
+  // whole passes of slots per block, at most kCompactOwn of them (up to 32 blocks per table at
+  // PI_MAX_NEURONS)
   const int nmax = n_g > n_c ? n_g : n_c;
-  int chunk = (nmax + 31) / 32;
-  chunk = (chunk + kCompactThreads - 1) / kCompactThreads * kCompactThreads;
-  if (chunk < kCompactThreads) chunk = kCompactThreads;
+  const int chunk = nmax > 32 * kCompactThreads ? kCompactOwn * kCompactThreads : kCompactThreads;
   const int blocks = (nmax + chunk - 1) / chunk > 0 ? (nmax + chunk - 1) / chunk : 1;
   const size_t shm = (size_t)((N + 63) / 64) * 8;
   hipLaunchKernelGGL(k_compact, dim3((unsigned)blocks, T_c ? 2u : 1u), dim3(kCompactThreads), shm, s, B, N, logits,

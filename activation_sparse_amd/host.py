@@ -21,11 +21,10 @@ class _HostCold(C.Structure):
 
 
 class _HybridScratch(C.Structure):
-    _fields_ = [("logits", C.c_void_p), ("A_g", C.c_void_p), ("K", C.c_void_p), ("A_c", C.c_void_p),
-                ("K_c", C.c_void_p), ("y_c", C.c_void_p), ("ws_pred", C.c_void_p), ("ws_pred_bytes", C.c_size_t),
+    _fields_ = [("logits", C.c_void_p), ("A_g", C.c_void_p), ("K", C.c_void_p), ("cold_list", C.c_void_p),
+                ("y_c", C.c_void_p), ("ws_pred", C.c_void_p), ("ws_pred_bytes", C.c_size_t),
                 ("ws_ffn", C.c_void_p), ("ws_ffn_bytes", C.c_size_t), ("x_host", C.c_void_p),
-                ("A_c_host", C.c_void_p), ("K_c_host", C.c_void_p), ("y_c_host", C.c_void_p),
-                ("event", C.c_void_p)]
+                ("cold_list_host", C.c_void_p), ("y_c_host", C.c_void_p), ("event", C.c_void_p)]
 
 
 _lib = None

@@ -33,30 +33,37 @@ class HybridLayer:
         self.logits = torch.empty((B, self.N), dtype=f32, device=device)
         self.A_g = torch.empty(max(self.n_g, 1), dtype=i32, device=device)
         self.K = torch.zeros(1, dtype=i32, device=device)
-        self.A_c = torch.empty(max(self.n_c, 1), dtype=i32, device=device)
-        self.K_c = torch.zeros(1, dtype=i32, device=device)
+        self.cold_list = torch.zeros(4 + max(self.n_c, 1), dtype=i32, device=device)
         self.y_c = torch.empty((B, self.d), dtype=f32, device=device)
         wsp = max(pi.pi_workspace_bytes(pi.PI_OP_PREDICT, B, self.d, self.H, self.N, 0), 256)
         wsf = max(pi.pi_workspace_bytes(pi.PI_OP_SPARSE_FFN, B, self.d, 0, 0, self.n_g), 256)
         self.ws_pred = torch.empty(wsp, dtype=torch.uint8, device=device)
         self.ws_ffn = torch.empty(wsf, dtype=torch.uint8, device=device)
         self.x_h = torch.empty((B, self.d), dtype=f32, pin_memory=True)
-        self.A_c_h = torch.empty(max(self.n_c, 1), dtype=i32, pin_memory=True)
-        self.K_c_h = torch.zeros(1, dtype=i32, pin_memory=True)
+        self.cold_list_h = torch.zeros(4 + max(self.n_c, 1), dtype=i32, pin_memory=True)
         self.y_c_h = torch.empty((B, self.d), dtype=f32, pin_memory=True)
         self.event = torch.cuda.Event()
         self.event.record()            # creates the underlying hipEvent_t
         self.scratch = host._HybridScratch(
-            self.logits.data_ptr(), self.A_g.data_ptr(), self.K.data_ptr(), self.A_c.data_ptr(),
-            self.K_c.data_ptr(), self.y_c.data_ptr(), self.ws_pred.data_ptr(), wsp, self.ws_ffn.data_ptr(), wsf,
-            self.x_h.data_ptr(), self.A_c_h.data_ptr(), self.K_c_h.data_ptr(), self.y_c_h.data_ptr(),
-            self.event.cuda_event)
+            self.logits.data_ptr(), self.A_g.data_ptr(), self.K.data_ptr(), self.cold_list.data_ptr(),
+            self.y_c.data_ptr(), self.ws_pred.data_ptr(), wsp, self.ws_ffn.data_ptr(), wsf, self.x_h.data_ptr(),
+            self.cold_list_h.data_ptr(), self.y_c_h.data_ptr(), self.event.cuda_event)
         self.cold = None
         if self.n_c:
             self.cold = host._HostCold(self.n_c, host._hmat(hl.W1), host._hvec(hl.b1), host._hmat(hl.Wup),
                                        host._hmat(hl.W2))
         self.T_g = dl.T_g.data_ptr()
         self.T_c = dl.T_c.data_ptr() if self.n_c else None
+
+    @property
+    def K_c_h(self):
+        """The last call's K_c (pinned host)."""
+        return self.cold_list_h[:1]
+
+    @property
+    def A_c_h(self):
+        """The last call's CPU list (pinned host; the first K_c entries are valid)."""
+        return self.cold_list_h[4:]
 
     def __call__(self, x, y, tau: float = 0.0, stream=None) -> int:
         """y [B x d] (device) = the layer's output for x [B x d] (device); returns the number

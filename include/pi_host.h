@@ -12,7 +12,8 @@
  * the CPU table, on host memory.  Its result goes to pi_merge (or to the
  * y_c argument of pi_ffn_layer) after a copy to the device.
  *
- * Every pointer here is a HOST pointer owned by the caller.  Matrix formats
+ * pi_cold_ffn's pointers are HOST pointers owned by the caller (pi_hybrid_layer
+ * states which of its own are device pointers).  Matrix formats
  * are those of pi.h (row-major, fp32 / fp16 / int4-g128 with fp16 scales).
  * The work is split over threads in fixed ranges (neurons for FC1, columns for
  * FC2) and every sum runs in one fixed order, so the result bits depend
@@ -70,41 +71,43 @@ typedef struct pi_host_cold {
 
 /* Buffers of one pi_hybrid_layer call, owned by the caller: device buffers for the
  * predictor, the lists and the cold partial, the two device workspaces, pinned
- * host buffers for the copies, and a hipEvent_t. */
+ * host buffers for the copies, and a hipEvent_t.
+ * The CPU list travels as one block, cold_list = [K_c, 0, 0, 0, A_c...]: K_c in
+ * entry 0 and the list from entry 4 (16-byte aligned), so that one copy moves
+ * the count and the list. */
 typedef struct pi_hybrid_scratch {
-  float* logits;        /* device [B x N] */
-  int32_t* A_g;         /* device [n_g] */
-  int32_t* K;           /* device [1] */
-  int32_t* A_c;         /* device [n_c] */
-  int32_t* K_c;         /* device [1] */
-  float* y_c;           /* device [B x d] */
-  void* ws_pred;        /* device, pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0) bytes */
+  float* logits;           /* device [B x N] */
+  int32_t* A_g;            /* device [n_g] */
+  int32_t* K;              /* device [1] */
+  int32_t* cold_list;      /* device [4 + n_c] */
+  float* y_c;              /* device [B x d] */
+  void* ws_pred;           /* device, pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0) bytes */
   size_t ws_pred_bytes;
-  void* ws_ffn;         /* device, pi_workspace_bytes(PI_OP_SPARSE_FFN, B, d, 0, 0, n_g) bytes */
+  void* ws_ffn;            /* device, pi_workspace_bytes(PI_OP_SPARSE_FFN, B, d, 0, 0, n_g) bytes */
   size_t ws_ffn_bytes;
-  float* x_host;        /* pinned host [B x d] */
-  int32_t* A_c_host;    /* pinned host [n_c] */
-  int32_t* K_c_host;    /* pinned host [1] */
-  float* y_c_host;      /* pinned host [B x d] */
-  void* event;          /* hipEvent_t */
+  float* x_host;           /* pinned host [B x d] */
+  int32_t* cold_list_host; /* pinned host [4 + n_c] */
+  float* y_c_host;         /* pinned host [B x d] */
+  void* event;             /* hipEvent_t: x and the cold list are on the host */
 } pi_hybrid_scratch;
 
 /* One layer of the pages' GPU-CPU hybrid execution (CSDN summary, section
  * GPU-CPU混合执行: each unit computes its own active neurons, the GPU merges,
  * and the synchronisation is skipped when the CPU side has no active neuron).
  * The calling thread is the CPU executor and `stream` the GPU's:
- *  1. enqueues pi_predict and pi_compact (layer's predictor; T_g / T_c the raw
- *     device neuron tables), then copies of x, K_c and A_c into the pinned host
- *     buffers, and records the event;
+ *  1. enqueues pi_predict and pi_compact (the layer's predictor; T_g / T_c
+ *     the raw device neuron tables), then the copies of x and of the CPU list
+ *     block to the pinned host buffers, back to back, and records the event;
  *  2. enqueues pi_sparse_ffn over the GPU-resident neurons (y = y_g);
- *  3. waits for the event and runs pi_cold_ffn on the host rows;
+ *  3. waits for the copies and runs pi_cold_ffn on the host rows;
  *  4. when K_c > 0, enqueues the copy of y_c to the device and pi_merge (which also
  *     adds b2); with K_c = 0 only b2, if any, is added.
  * Returns with step 4 enqueued (not finished); *K_c_out (optional) gets K_c.
  * x, y: device [B x d] fp32.  A layer with no CPU table (T_c NULL or n_c = 0)
- * runs steps 1-2 and the b2 merge only.
- * Errors: those of the calls it makes; PI_EHIP when a copy, the event record or
- * the wait fails (pi_last_hip_error() in libpi does not see these). */
+ * runs steps 1-2 (without copies) and the b2 merge only.
+ * Errors: those of the calls it makes; PI_EINVAL for a missing buffer or event;
+ * PI_EHIP when a copy, an event record or a wait fails (pi_last_hip_error() in
+ * libpi does not see these). */
 int pi_hybrid_layer(void* stream, const pi_layer* layer, const int32_t* T_g, const int32_t* T_c,
                     const pi_host_cold* cold, int32_t B, const float* x, float tau, float* y,
                     const pi_hybrid_scratch* scratch, int32_t threads, int32_t* K_c_out);

@@ -165,26 +165,31 @@ def test_matrix_core_batches(B, fused):
 def test_hybrid_layer(B):
     """The hybrid executor: the GPU predicts, compacts and computes its hot neurons while the
     CPU (libpi_host) computes the cold ones, merged on the GPU; lists and the merged output
-    against the oracle."""
+    against the oracle, over three calls in a row with different inputs (each call's copies
+    and lists are its own)."""
     torch = _dev()
     from activation_sparse_amd.hybrid import HybridLayer
     from synth.device import HostColdLayer
     cfg = ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=17)
     spec = synth.layer_spec(cfg, 0)
     hy = HybridLayer(ph.DeviceLayer(spec), HostColdLayer(spec), B)
-    x = synth.host_x(cfg.seed, 0, 5, B, cfg.d)
     y = torch.empty((B, cfg.d), dtype=torch.float32, device="cuda")
-    kc = hy(torch.from_numpy(x).cuda(), y)
-    torch.cuda.synchronize()
-    K = int(hy.K.cpu()[0])
-    A_g, A_c = hy.A_g.cpu().numpy()[:K], hy.A_c.cpu().numpy()[:kc]
-    logits_or, _ = ph.oracle_predict(spec, x)
-    A_g_or, A_c_or = orc.compact(logits_or, 0.0, spec.T_g, spec.T_c)
-    _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
-    _, out_c, asc_c = ph.list_check(A_c, A_c_or, spec.T_c, logits_or, 0.0)
-    assert kc > 0 and K > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c
-    y_or = ph.oracle_ffn_on_ids(spec, x, spec.T_g[A_g]) + ph.oracle_ffn_on_ids(spec, x, spec.T_c[A_c])
-    assert ph.rel_err(y.cpu().numpy(), y_or) <= ph.RTOL
+    for step in (5, 6, 7):
+        x = synth.host_x(cfg.seed, 0, step, B, cfg.d)
+        kc = hy(torch.from_numpy(x).cuda(), y)
+        torch.cuda.synchronize()
+        K = int(hy.K.cpu()[0])
+        A_g = hy.A_g.cpu().numpy()[:K]
+        A_c = hy.A_c_h.numpy()[:kc].copy()
+        assert int(hy.K_c_h[0]) == kc and np.array_equal(hy.cold_list.cpu().numpy()[4:4 + kc], A_c)
+        assert np.array_equal(hy.x_h.numpy(), x)
+        logits_or, _ = ph.oracle_predict(spec, x)
+        A_g_or, A_c_or = orc.compact(logits_or, 0.0, spec.T_g, spec.T_c)
+        _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
+        _, out_c, asc_c = ph.list_check(A_c, A_c_or, spec.T_c, logits_or, 0.0)
+        assert kc > 0 and K > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c
+        y_or = ph.oracle_ffn_on_ids(spec, x, spec.T_g[A_g]) + ph.oracle_ffn_on_ids(spec, x, spec.T_c[A_c])
+        assert ph.rel_err(y.cpu().numpy(), y_or) <= ph.RTOL, step
 
 
 def test_hybrid_layer_skips_the_merge_without_cold_neurons():
