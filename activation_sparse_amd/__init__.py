@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libpi.so")
 
 EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes",
            "pi_table_prepare", "pi_ffn_layer", "pi_ffn_layer_stages", "pi_workspace_bytes", "pi_status_string",
-           "pi_last_hip_error", "pi_abi_version")
+           "pi_last_hip_error", "pi_abi_version", "pi_read_probe")
 
 
 class PiError(RuntimeError):
@@ -65,6 +65,8 @@ def load():
         L.pi_compact.argtypes = [P, I, I, P, C.c_float, P, I, P, P, P, I, P, P, P, C.c_size_t]
         L.pi_sparse_ffn.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Mat, P, P, P, P, C.c_size_t]
         L.pi_merge.argtypes = [P, I, I, P, P, P, _Vec]
+        L.pi_read_probe.argtypes = [P, P, C.c_size_t, I, P]
+        L.pi_read_probe.restype = C.c_int
         L.pi_table_bytes.argtypes = [I]
         L.pi_table_bytes.restype = C.c_size_t
         L.pi_table_prepare.argtypes = [I, P, I, P, C.c_size_t]
@@ -168,6 +170,11 @@ def pi_sparse_ffn(B, d, n_g, kind, x, W1: Matrix, b1: Vector, Wup: Optional[Matr
     _check(load().pi_sparse_ffn(_stream(stream), B, d, n_g, kind, _ptr(x), W1._c(), (b1 or _NO_VEC)._c(),
                                 (Wup or _NO_MAT)._c(), W2._c(), _ptr(A_g), _ptr(K), _ptr(y_g), _ptr(ws), nbytes),
            "pi_sparse_ffn")
+
+
+def pi_read_probe(buf, nbytes: int, out, blocks: int = 0, stream=None) -> None:
+    """Streaming read of nbytes of buf (the bandwidth reference); out: uint32 [4 * blocks]."""
+    _check(load().pi_read_probe(_stream(stream), _ptr(buf), int(nbytes), int(blocks), _ptr(out)), "pi_read_probe")
 
 
 def pi_merge(B, d, y, y_c=None, K_c=None, b2: Optional[Vector] = None, stream=None) -> None:

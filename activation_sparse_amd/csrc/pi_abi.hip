@@ -455,6 +455,12 @@ int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, con
   return hip_status(pi::launch_merge(B, d, y, y_c, K_c, b2.data, b2.dtype, static_cast<hipStream_t>(stream)));
 }
 
+int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, uint32_t* out) {
+  if (!buf || !out || bytes == 0 || bytes % 16 != 0 || !aligned16(buf) || blocks > 65536) return PI_EINVAL;
+  if (blocks <= 0) blocks = 8 * pi::kNumCU;
+  return hip_status(pi::launch_read_probe(buf, (int64_t)bytes, blocks, out, static_cast<hipStream_t>(stream)));
+}
+
 int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c,
                         float* y, float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws,
                         size_t ws_bytes, void* const* events, uint32_t stages, int32_t* rows_read) {

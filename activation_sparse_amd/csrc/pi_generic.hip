@@ -199,6 +199,28 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const
   if (c1 == n && tid == 0) *Kout = base;
 }
 
+// Streaming read: 256 threads per block, grid-stride over 16-byte vectors,
+// eight loads per lane in flight; each wave's XOR of what it read is stored.
+__global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, int64_t n16, uint32_t* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = p[i + q * stride];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc ^= __shfl_xor(acc, off, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) out[blockIdx.x * 4 + threadIdx.x / kWave] = acc;
+}
+
 __global__ __launch_bounds__(kThreads) void k_merge(int64_t n, int d, float* y, const float* y_c,
                                                     const int32_t* K_c, const void* b2, int b2_dt) {
   const bool add_c = y_c && (!K_c || *K_c != 0);
@@ -276,6 +298,12 @@ hipError_t launch_compact(int B, int N, const float* logits, float tau, const in
   const size_t shm = (size_t)((N + 63) / 64) * 8;
   hipLaunchKernelGGL(k_compact, dim3((unsigned)blocks, T_c ? 2u : 1u), dim3(kCompactThreads), shm, s, B, N, logits,
                      tau, T_g, n_g, A_g, K, T_c, n_c, A_c, K_c, chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int blocks, uint32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint4*>(buf),
+                     bytes / 16, out);
   return hipGetLastError();
 }
 

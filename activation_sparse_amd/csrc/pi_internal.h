@@ -39,6 +39,7 @@ hipError_t launch_compact(int B, int N, const float* logits, float tau, const in
                           int32_t* K_c, hipStream_t s);
 
 // The lists from the activation words.
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int blocks, uint32_t* out, hipStream_t s);
 hipError_t launch_list(const ListCtx& c, int n_g, hipStream_t s);
 
 // Neuron-major axpy over listed rows: out[b,:] += a[b, j] * W[list[j], :]
@@ -84,6 +85,7 @@ hipError_t launch_merge(int B, int d, float* y, const float* y_c, const int32_t*
 // Batched GEMMs on the matrix cores (pi_mfma.hip): the row-dot GEMMs (predictor
 // hidden layer, FC1) from kMmRowMinBatch batch rows, the axpy GEMMs (output
 // layer, FC2) from kMmAxpyMinBatch (below that the VALU kernels measure faster).
+constexpr int kNumCU = 256;   // compute units of the gfx950 parts (MI350X / MI355X)
 constexpr int kMmRowMinBatch = 2;
 constexpr int kMmAxpyMinBatch = 3;
 struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b, k])

@@ -35,7 +35,6 @@ namespace {
 typedef float float4v_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMmWaves = 4;
-constexpr int kNumCU = 256;                 // compute units of the gfx950 parts (MI350X / MI355X)
 constexpr int kMmThreads = kMmWaves * kWave;
 
 __device__ __forceinline__ float4v_t mfma4(float a, float b, float4v_t c) {

@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--hybrid-steps", type=int, default=4,
                     help="after the batch-1 measurement, time the pages' GPU-CPU hybrid layer (cold neurons on "
                          "the host CPU) over this many steps; 0 = skip")
+    ap.add_argument("--lookahead-steps", type=int, default=16,
+                    help="after the batch-1 measurement, time look-ahead prediction (layer L+1's predictor hidden "
+                         "layer from layer L's input, beside layer L's FFN) over this many steps; 0 = skip")
     return ap.parse_args()
 
 
@@ -392,6 +395,91 @@ def pi_kind(cfg):
     return pi.PI_GATED_RELU if cfg.gated else pi.PI_RELU
 
 
+def lookahead_bench(cfg, specs, dls, steps, warmup, B=1):
+    """Look-ahead prediction (the pages: activations can be predicted some layers ahead while the
+    model runs): layer L+1's predictor hidden layer is computed from layer L's input, on a second
+    stream, while layer L's output layer, decision, FC1, FC2 and sum run on the first; layer L+1's
+    remaining stages wait for it and take layer L+1's own input.  Layer 0 predicts from its own input.
+    Same layers, seeded inputs and one HIP graph per step as the measured run; returns tokens/s."""
+    import torch
+    import synth
+    import activation_sparse_amd as pi
+    dev = "cuda:0"
+    n_layers = len(specs)
+    maxH = max(s.H for s in specs)
+    n_g = max(s.n_g for s in specs)
+    n_c = max(len(s.T_c) for s in specs)
+    d, N = cfg.d, cfg.N
+    S = warmup + steps
+    ws_bytes = max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256)
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+    xs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev)
+    ycs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev) if n_c else None
+    Ks = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    Kcs = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    y = torch.empty((B, d), dtype=torch.float32, device=dev)
+    A_g = torch.empty(max(n_g, 1), dtype=torch.int32, device=dev)
+    A_c = torch.empty(max(n_c, 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in range(S):
+        rid = torch.from_numpy(synth.x_row_ids(t, B)).to(dev)
+        for L in range(n_layers):
+            synth.dev_fill(xs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_X, L, d, 1.0,
+                           row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+            if n_c:
+                synth.dev_fill(ycs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_YC, L, d, 0.05,
+                               row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+    torch.cuda.synchronize()
+    rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
+    ahead = torch.cuda.Stream()            # default priority
+
+    def stage(t, L, x, stages, st):
+        cold = len(specs[L].T_c) > 0
+        pi.pi_ffn_layer_stages(dls[L].layer, B, x, 0.0, ycs[t, L] if cold else None, y, None, A_g, Ks[t, L:L + 1],
+                               A_c if cold else None, Kcs[t, L:L + 1] if cold else None, wss[L], stages,
+                               stream=st, _cstruct=dls[L].layer_c)
+
+    def step_call(t):
+        main = torch.cuda.current_stream()
+        stage(t, 0, xs[t, 0], pi.PI_STAGE_HIDDEN, main)
+        for L in range(n_layers):
+            if L + 1 < n_layers:          # layer L's input is there: predict layer L + 1 beside layer L
+                ahead.wait_stream(main)
+                stage(t, L + 1, xs[t, L], pi.PI_STAGE_HIDDEN, ahead)
+            stage(t, L, xs[t, L], rest, main)
+            if L + 1 < n_layers:
+                main.wait_stream(ahead)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_call(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for t in range(S):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_call(t)
+        graphs.append(g)
+    for t in range(warmup):
+        graphs[t].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warmup, S):
+        graphs[t].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    out = {"tokens_per_s": round(B * 1e3 / ms, 2), "ms_per_step": round(ms, 4), "steps": steps, "batch": B,
+           "mean_K": float(Ks[warmup:].float().mean().item()),
+           "predictor_input": "layer L+1's hidden layer from layer L's input (layer 0: its own)"}
+    log(f"look-ahead prediction: {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s")
+    del graphs
+    return out
+
+
 def hybrid_bench(cfg, specs, dls, steps, warmup):
     """The pages' hybrid layer at batch 1: the CPU-table neurons live in host memory and run on the
     host CPU (libpi_host) while the GPU runs the predictor, the compaction and its own neurons; the
@@ -641,7 +729,35 @@ def main():
                            "PI_STAGE_FC1)"),
                 "bytes_per_launch": round(mean_bytes[iso]), "avg_launch_us": round(mean_ms[iso] * 1e3, 2)}
 
+    # the streaming-read reference: a plain read of the dominant kernel's bytes per launch, of one
+    # layer-token's bytes and of 1 GiB, best over a few grid sizes, back to back on the launch stream.
+    # Successive launches read different regions of a 2 GiB buffer, as the layers read different
+    # weights, so that no launch finds its bytes in the last-level cache (256 MB) from the one before.
+    stream_read = {}
+    probe = torch.empty(2**29 + 4, dtype=torch.int32, device=dev)
+    probe_out = torch.empty(4 * 8192, dtype=torch.int32, device=dev)
+    layer_bytes_mean = step_bytes / n_layers
+    for nb in (int(dom_bytes) // 16 * 16, int(layer_bytes_mean) // 16 * 16, 2**30):
+        best = 0.0
+        regions = 2**31 // nb
+        views = [probe[k * (nb // 4):(k + 1) * (nb // 4)] for k in range(regions)]
+        for blocks in (1024, 2048, 4096, 8192):
+            pi.pi_read_probe(views[0], nb, probe_out, blocks)
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n_rep = 20
+            r0.record()
+            for k in range(n_rep):
+                pi.pi_read_probe(views[(k + 1) % regions], nb, probe_out, blocks)
+            r1.record()
+            torch.cuda.synchronize()
+            best = max(best, nb * n_rep / (r0.elapsed_time(r1) * 1e-3) / 1e9)
+        stream_read[f"{nb / 1e6:.1f} MB"] = round(best, 1)
+    del probe, probe_out
+    dom_ref = list(stream_read.values())[0]
+
     log(f"timed: {ms_per_step:.4f} ms/step, {tokens_s:.1f} tokens/s")
+    log(f"streaming read: {stream_read} GB/s; dominant kernel at {achieved[iso] / dom_ref:.3f} of the read "
+        f"of its own size")
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -651,6 +767,11 @@ def main():
     if args.hybrid_steps > 0 and B == 1:
         log("hybrid layer (cold neurons on the host CPU) ...")
         hybrid = hybrid_bench(cfg, specs, dls, args.hybrid_steps, 1)
+
+    lookahead = None
+    if args.lookahead_steps > 0 and B == 1:
+        log("look-ahead prediction ...")
+        lookahead = lookahead_bench(cfg, specs, dls, args.lookahead_steps, 3)
 
     sweep = None
     batches = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []
@@ -689,7 +810,9 @@ def main():
                    "kernel_gbps": {k: round(v, 1) for k, v in achieved.items()},
                    "graph": use_graph, "setup_s": round(setup_s, 1), "wall_s": round(wall, 4),
                    "event_ms": round(gpu_ms, 3),
-                   "batch_sweep": sweep, "hybrid": hybrid},
+                   "stream_read_gbps": stream_read,
+                   "dominant_frac_of_stream_read": round(achieved[iso] / dom_ref, 4),
+                   "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead},
     }
     print(json.dumps(out), flush=True)
 

@@ -246,6 +246,16 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* layer, int32_t B, const fl
                         int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, void* const* events,
                         uint32_t stages, int32_t* rows_read);
 
+/* The streaming-read reference that the kernels' bandwidths are read against:
+ * reads `bytes` bytes of `buf` once, in 16-byte vectors, with `blocks`
+ * workgroups of 256 threads (blocks <= 0: 8 per compute unit) each keeping
+ * eight loads per lane in flight, and writes the XOR of the words each wave
+ * read to out[4 * block + wave] (so that no load can be dropped).
+ * buf: device, 16-byte aligned; bytes a multiple of 16; out: device uint32
+ * [4 * blocks].  Errors: PI_EINVAL for a NULL pointer, bytes == 0 or not a
+ * multiple of 16, or blocks > 65536. */
+int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, uint32_t* out);
+
 /* Workspace bytes an entry point needs for these sizes (0 when none).
  * Arguments an op does not use are ignored. */
 size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g);

@@ -158,6 +158,16 @@ def test_table_prepare_validates_and_builds_bitmap_and_prefix():
     assert len(pi.pi_table_prepare(N, np.zeros(0, np.int32))) == pi.pi_table_bytes(N)
 
 
+def test_read_probe_rejects_bad_arguments():
+    # (buf, bytes, out, blocks, stream)
+    assert status(pi.pi_read_probe, None, 1024, FAKE, 0, 0) == pi.PI_EINVAL
+    assert status(pi.pi_read_probe, FAKE, 0, FAKE, 0, 0) == pi.PI_EINVAL
+    assert status(pi.pi_read_probe, FAKE, 1000, FAKE, 0, 0) == pi.PI_EINVAL          # not whole 16-byte vectors
+    assert status(pi.pi_read_probe, FAKE, 1024, FAKE, 65537, 0) == pi.PI_EINVAL
+    assert status(pi.pi_read_probe, FAKE, 1024, None, 0, 0) == pi.PI_EINVAL
+    assert status(pi.pi_read_probe, FAKE + 8, 1024, FAKE, 0, 0) == pi.PI_EINVAL      # unaligned
+
+
 def test_compact_and_merge_reject_bad_arguments():
     assert status(pi.pi_compact, 1, 0, FAKE, 0.0, FAKE, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL
     assert status(pi.pi_compact, 1, 100, FAKE, 0.0, None, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL

@@ -252,3 +252,73 @@ def test_compact_lists_are_exact_over_any_table_order(N, n_g, B, density):
     pi.pi_compact(B, N, logits, tau, Tg, n_g, A_g, K)
     torch.cuda.synchronize()
     assert int(K.cpu()[0]) == k and np.array_equal(A_g.cpu().numpy()[:k], A_g_or)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_lookahead_prediction_on_two_streams(B):
+    """Look-ahead prediction: layer l+1's predictor hidden layer runs on layer l's input, on a
+    second stream beside layer l's FFN; its remaining stages take layer l+1's own input.  Each
+    layer's logits and lists against the oracle's prediction from that earlier input (and not
+    from its own), its output against the oracle's FFN on its own input over the GPU's list."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    cfg = ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=17)
+    nl = 3
+    specs = [synth.layer_spec(cfg, l) for l in range(nl)]
+    dls = [ph.DeviceLayer(s) for s in specs]
+    bufs = [ph.DeviceBuffers(cfg, s.H, s.n_g, len(s.T_c), B) for s in specs]
+    xs = [synth.host_x(cfg.seed, l, 3, B, cfg.d) for l in range(nl)]
+    for b, x in zip(bufs, xs):
+        b.x.copy_(torch.from_numpy(x))
+    torch.cuda.synchronize()
+    main, ahead = torch.cuda.current_stream(), torch.cuda.Stream()
+    rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
+
+    def stage(l, x, stages, st):
+        b = bufs[l]
+        pi.pi_ffn_layer_stages(dls[l].layer, B, x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c, b.ws_layer,
+                               stages, stream=st)
+
+    print(f"look-ahead B={B}", flush=True)
+    stage(0, bufs[0].x, pi.PI_STAGE_HIDDEN, main)
+    for l in range(nl):
+        if l + 1 < nl:
+            ahead.wait_stream(main)
+            stage(l + 1, bufs[l].x, pi.PI_STAGE_HIDDEN, ahead)
+        stage(l, bufs[l].x, rest, main)
+        if l + 1 < nl:
+            main.wait_stream(ahead)
+    torch.cuda.synchronize()
+    for l in range(nl):
+        spec, b = specs[l], bufs[l]
+        logits_or, _ = ph.oracle_predict(spec, xs[max(l - 1, 0)])
+        assert np.max(np.abs(b.logits.cpu().numpy().astype(np.float64) - logits_or)) <= ph.LOGIT_ATOL, l
+        K, K_c = int(b.K.cpu()[0]), int(b.K_c.cpu()[0])
+        A_g, A_c = b.A_g.cpu().numpy()[:K], b.A_c.cpu().numpy()[:K_c]
+        A_g_or, A_c_or = orc.compact(logits_or, 0.0, spec.T_g, spec.T_c)
+        _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
+        _, out_c, asc_c = ph.list_check(A_c, A_c_or, spec.T_c, logits_or, 0.0)
+        assert K > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
+        if l > 0:      # the list is the earlier input's, not the layer's own
+            own, _ = orc.compact(ph.oracle_predict(spec, xs[l])[0], 0.0, spec.T_g)
+            assert not np.array_equal(own, A_g_or)
+        y_or = ph.oracle_ffn_on_ids(spec, xs[l], spec.T_g[A_g])
+        assert ph.rel_err(b.y.cpu().numpy(), y_or) <= ph.RTOL, l
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(16, 1), (4096 + 48, 3), (63 * 2**20 + 16, 0), (2**26, 4096)])
+def test_read_probe_reads_every_word(nbytes, blocks):
+    """The streaming-read reference reads each 16-byte vector once: the XOR of what every wave
+    reports equals the XOR of all the buffer's words (a skipped or repeated vector changes it)."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    g = np.random.default_rng(nbytes)
+    host = g.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    nb = blocks if blocks > 0 else 8 * 256
+    out = torch.zeros(4 * nb, dtype=torch.int32, device="cuda")
+    print(f"read probe {nbytes} B, {nb} blocks", flush=True)
+    pi.pi_read_probe(buf, nbytes, out, blocks)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host)
