@@ -197,8 +197,10 @@ __host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(siz
 template <int PDT, int DT, int NV, bool GATED, int BDT, int T, bool FC1>
 __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   using G = TileGeom<T>;
-  constexpr int W = G::W, NT = G::NT, NG = G::NG, U = G::U;
   constexpr int EP = Fmt<PDT>::E;      // output-layer weights per 16-byte vector
+  // row loads in flight per lane: int4 rows hold 32 weights per vector, so a quarter of
+  // the loads covers the same rows per pass (and keeps two blocks per compute unit)
+  constexpr int W = G::W, NT = G::NT, NG = G::NG, U = PDT == 2 ? G::U / 4 : G::U;
   constexpr int LPR = T / EP;          // lanes that cover one row slice of the tile
   constexpr int RPL = kWave / LPR;     // row slices per wave-wide load
   constexpr int E = Fmt<DT>::E;        // FC1 weights per 16-byte vector
@@ -298,11 +300,23 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
       }
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        float wf[EP];
-        widen<PDT>(w[i], PDT == 2 ? sc[i] : 1.f, wf);
         const float hs = hv[i] > 0.f ? hv[i] : 0.f;
+        if constexpr (PDT == 2) {
+          // int4: the group scale folds into h once per row, and each weight is one
+          // signed bit-field extract, one convert and one fma
+          const float hsc = hs * sc[i];
+          const uint32_t wq[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
 #pragma unroll
-        for (int e = 0; e < EP; ++e) acc[e] = fmaf(wf[e], hs, acc[e]);
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+              acc[k * 8 + n] = fmaf((float)((int32_t)(wq[k] << (28 - 4 * n)) >> 28), hsc, acc[k * 8 + n]);
+        } else {
+          float wf[EP];
+          widen<PDT>(w[i], 1.f, wf);
+#pragma unroll
+          for (int e = 0; e < EP; ++e) acc[e] = fmaf(wf[e], hs, acc[e]);
+        }
       }
     }
     // the RPL row groups of the wave hold partial sums of the same ids: butterfly
@@ -535,8 +549,9 @@ hipError_t pred_out_pdt(const PredFc1Args& a, hipStream_t s) {
 }
 
 // Fused kernels exist for these (output-layer dtype, FFN dtype, bias dtype)
-// combinations: all fp32, fp16 predictor + fp16 FFN, fp16 predictor + int4 FFN
-// (fp16 biases); fp32 gated layers take the separate kernels.
+// combinations: all fp32, fp16 predictor + fp16 FFN, fp16 predictor + int4 FFN,
+// int4 predictor + fp16 FFN (fp16 biases); fp32 gated layers take the separate
+// kernels.
 template <int PDT, int DT, int BDT, bool GATED>
 hipError_t pred_fc1_combo(const PredFc1Args& a, hipStream_t s) {
   const int nv = pick_nv<DT>((int)(row_bytes(DT, a.d) / 16));
@@ -772,6 +787,7 @@ bool pred_fc1_supported(int pdt, int dt, int bdt, int c2dt, bool gated, int H, i
   if (nv == 0) return false;
   if (pdt == 0 && dt == 0 && bdt == 0) return !gated;
   if (pdt == 1 && (dt == 1 || dt == 2) && bdt == 1) return true;
+  if (pdt == 2 && dt == 1 && bdt == 1) return true;     // int4 predictor, fp16 FFN
   return false;
 }
 
@@ -779,6 +795,7 @@ hipError_t launch_pred_fc1(const PredFc1Args& a, bool gated, hipStream_t s) {
   if (a.pdt == 0 && a.dt == 0) return pred_fc1_combo<0, 0, 0, false>(a, s);
   if (a.pdt == 1 && a.dt == 1) return gated ? pred_fc1_combo<1, 1, 1, true>(a, s) : pred_fc1_combo<1, 1, 1, false>(a, s);
   if (a.pdt == 1 && a.dt == 2) return gated ? pred_fc1_combo<1, 2, 1, true>(a, s) : pred_fc1_combo<1, 2, 1, false>(a, s);
+  if (a.pdt == 2 && a.dt == 1) return gated ? pred_fc1_combo<2, 1, 1, true>(a, s) : pred_fc1_combo<2, 1, 1, false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--hybrid-steps", type=int, default=4,
                     help="after the batch-1 measurement, time the pages' GPU-CPU hybrid layer (cold neurons on "
                          "the host CPU) over this many steps; 0 = skip")
+    ap.add_argument("--i4pred-steps", type=int, default=16,
+                    help="after the batch-1 measurement, time the stack with int4-g128 predictor weights over "
+                         "this many steps; 0 = skip")
     ap.add_argument("--lookahead-steps", type=int, default=16,
                     help="after the batch-1 measurement, time look-ahead prediction (layer L+1's predictor hidden "
                          "layer from layer L's input, beside layer L's FFN) over this many steps; 0 = skip")
@@ -480,6 +483,109 @@ def lookahead_bench(cfg, specs, dls, steps, warmup, B=1):
     return out
 
 
+def i4pred_bench(cfg, specs, dls, steps, warmup):
+    """Predictor-cost variant: the same stack, inputs and FFN weights with int4-g128 predictor
+    weights (P1 as int4 rows; P2's fp16 values quantised hidden-major, groups along N), through
+    the same batch-1 layer call and one HIP graph per step.  Returns tokens/s and the step's
+    algorithmic bytes at the int4 widths.  None unless the stack is the OPT-30B one."""
+    import torch
+    import synth
+    import activation_sparse_amd as pi
+    from dataclasses import replace
+    from synth.device import dev_matrix, fill_matrix, dev_matrix_hidden_major
+    vkey = cfg.key + "-i4pred"
+    if vkey not in synth.CONFIGS:
+        return None
+    vcfg = synth.CONFIGS[vkey]
+    dev = "cuda:0"
+    B, n_layers = 1, len(specs)
+    d, N = cfg.d, cfg.N
+    vspecs, lays, keep = [], [], []
+    for spec, dl in zip(specs, dls):
+        vs = synth.layer_spec(vcfg, spec.layer)
+        assert np.array_equal(vs.c2, spec.c2) and np.array_equal(vs.T_g, spec.T_g)
+        sig = vs.sigmas()
+        P1 = dev_matrix(vs.H, d, synth.I4G128, dev)
+        fill_matrix(P1, synth.I4G128, vcfg.seed, synth.TAG_P1, spec.layer, d, sig[synth.TAG_P1])
+        P2 = dev_matrix_hidden_major(N, vs.H, synth.I4G128, vcfg.seed, synth.TAG_P2, spec.layer, sig[synth.TAG_P2], dev)
+        lay = replace(dl.layer, P1=P1, P2=P2)
+        vspecs.append(vs)
+        lays.append(lay._c())
+        keep.append((P1, P2))
+    torch.cuda.synchronize()
+    maxH = max(s.H for s in specs)
+    n_g = max(s.n_g for s in specs)
+    n_c = max(len(s.T_c) for s in specs)
+    S = warmup + steps
+    ws_bytes = max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256)
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+    xs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev)
+    ycs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev) if n_c else None
+    Ks = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    Kcs = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    rows = torch.zeros((S, n_layers, 2), dtype=torch.int32, device=dev)
+    y = torch.empty((B, d), dtype=torch.float32, device=dev)
+    A_g = torch.empty(max(n_g, 1), dtype=torch.int32, device=dev)
+    A_c = torch.empty(max(n_c, 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in range(S):
+        rid = torch.from_numpy(synth.x_row_ids(t, B)).to(dev)
+        for L in range(n_layers):
+            synth.dev_fill(xs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_X, L, d, 1.0,
+                           row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+            if n_c:
+                synth.dev_fill(ycs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_YC, L, d, 0.05,
+                               row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+    torch.cuda.synchronize()
+
+    def step_call(t):
+        for L in range(n_layers):
+            cold = len(specs[L].T_c) > 0
+            pi.pi_ffn_layer_stages(dls[L].layer, B, xs[t, L], 0.0, ycs[t, L] if cold else None, y, None, A_g,
+                                   Ks[t, L:L + 1], A_c if cold else None, Kcs[t, L:L + 1] if cold else None,
+                                   wss[L], pi.PI_STAGE_ALL, rows_read=rows[t, L], _cstruct=lays[L])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_call(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for t in range(S):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_call(t)
+        graphs.append(g)
+    for t in range(warmup):
+        graphs[t].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warmup, S):
+        graphs[t].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    Kh, Kch, Rh = Ks.cpu().numpy(), Kcs.cpu().numpy(), rows.cpu().numpy()
+    tot = [0.0, 0.0, 0.0]
+    for t in range(warmup, S):
+        for L in range(n_layers):
+            for i, v in enumerate(layer_bytes(vspecs[L], B, int(Kh[t, L]), int(Kch[t, L]), int(Rh[t, L, 0]),
+                                              int(Rh[t, L, 1]))):
+                tot[i] += v
+    step_bytes = sum(tot) / steps
+    out = {"tokens_per_s": round(B * 1e3 / ms, 2), "ms_per_step": round(ms, 4), "steps": steps,
+           "config": vcfg.desc, "step_bytes": round(step_bytes),
+           "bytes_split": {"predictor": round(tot[0] / steps), "ffn": round(tot[1] / steps),
+                           "small": round(tot[2] / steps)},
+           "step_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1), "mean_K": float(Kh[warmup:].mean()),
+           "mean_p2_rows_read": float(Rh[warmup:, :, 0].mean())}
+    log(f"int4 predictor: {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s, "
+        f"{out['step_bytes'] / 1e9:.2f} GB per step")
+    del graphs
+    return out
+
+
 def hybrid_bench(cfg, specs, dls, steps, warmup):
     """The pages' hybrid layer at batch 1: the CPU-table neurons live in host memory and run on the
     host CPU (libpi_host) while the GPU runs the predictor, the compaction and its own neurons; the
@@ -768,6 +874,11 @@ def main():
         log("hybrid layer (cold neurons on the host CPU) ...")
         hybrid = hybrid_bench(cfg, specs, dls, args.hybrid_steps, 1)
 
+    i4pred = None
+    if args.i4pred_steps > 0 and B == 1:
+        log("int4 predictor weights ...")
+        i4pred = i4pred_bench(cfg, specs, dls, args.i4pred_steps, 3)
+
     lookahead = None
     if args.lookahead_steps > 0 and B == 1:
         log("look-ahead prediction ...")
@@ -812,7 +923,7 @@ def main():
                    "event_ms": round(gpu_ms, 3),
                    "stream_read_gbps": stream_read,
                    "dominant_frac_of_stream_read": round(achieved[iso] / dom_ref, 4),
-                   "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead},
+                   "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead, "int4_predictor": i4pred},
     }
     print(json.dumps(out), flush=True)
 

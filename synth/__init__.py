@@ -152,6 +152,43 @@ CONFIGS = {
 }
 
 
+# The OPT-30B stack with int4 (group 128) predictor weights: a predictor-cost variant.  P1 is
+# generated as int4 rows; the output layer's fp16 values are the fp16 variant's, quantised in
+# the hidden-major layout (groups of 128 along N), so that the output bias calibrated on the
+# fp16 values still places each neuron's predicted activation probability.
+CONFIGS["opt-30b-i4pred"] = Config(
+    "opt-30b-i4pred", "OPT-30B-shaped FFN stack, 48 layers, 7168/28672, fp16 FFN, int4-g128 predictor, "
+    "40% of neurons on the GPU", 48, 7168, 28672, F16, I4G128, F16, False, (0.10, 0.10), 1.1, (1024, 1024), 0.4,
+    (1,), 64, 4)
+
+
+def i4_quantize_rows(bits16: np.ndarray):
+    """fp16 values [rows, cols] (uint16 bits), cols a multiple of 128 -> int4-g128 rows: per
+    group of 128 the scale s = fp16(max|w| / 7) and q = clamp(rint(w / s), -8, 7), both in fp32
+    (q = 0 for an all-zero group); two q per byte, the even element in the low nibble.  Returns
+    (uint8 [rows, cols/2], uint16 fp16-bit scales [rows, cols/128]).  The device twin is
+    synth.device.i4_quantize_rows_dev."""
+    w = bits16.view(np.float16).astype(np.float32)
+    rows, cols = w.shape
+    g = w.reshape(rows, cols // 128, 128)
+    s = (np.max(np.abs(g), axis=2) / np.float32(7.0)).astype(np.float16)
+    sf = s.astype(np.float32)[..., None]
+    safe = np.where(sf > 0, sf, np.float32(1.0))
+    q = np.where(sf > 0, np.clip(np.rint(g / safe), -8, 7), np.float32(0.0)).astype(np.int16).reshape(rows, cols)
+    packed = ((q[:, 0::2] & 0xF) | ((q[:, 1::2] & 0xF) << 4)).astype(np.uint8)
+    return packed, s.view(np.uint16)
+
+
+def i4_dequant(packed: np.ndarray, scales_bits: np.ndarray) -> np.ndarray:
+    """Exact float64 values q * s of int4-g128 rows."""
+    rows = packed.shape[0]
+    q = np.empty((rows, packed.shape[1] * 2), np.int64)
+    q[:, 0::2] = packed & 0xF
+    q[:, 1::2] = packed >> 4
+    q = np.where(q >= 8, q - 16, q)
+    return q * np.repeat(scales_bits.view(np.float16).astype(np.float64), 128, axis=1)
+
+
 def small_config(key="tiny", d=256, N=1024, H=64, wdtype=F16, pdtype=F16, bdtype=F16, gated=False,
                  rho=0.1, alpha=1.1, gpu_frac=1.0, n_layers=1, seed=11) -> Config:
     """A reduced shape with the same construction, for parity tests."""

@@ -35,15 +35,31 @@ def fill_matrix(m, dtype, seed, tag, layer, cols, sigma, row_ids_dev=None, nrows
                    nrows=n, stream=torch.cuda.current_stream().cuda_stream)
 
 
-def dev_matrix_hidden_major(N, H, dtype, seed, tag, layer, sigma, device):
-    """The [N x H] generated matrix stored transposed, [H x N] (fp32 / fp16 bits unchanged)."""
+def i4_quantize_rows_dev(t16):
+    """Device twin of synth.i4_quantize_rows (same rule, fp32 arithmetic): fp16 tensor
+    [rows, cols] -> Matrix int4-g128 (uint8 [rows, cols/2], int16 scales [rows, cols/128])."""
     torch = _torch()
-    if dtype == synth.I4G128:
-        raise NotImplementedError("synthetic int4 output-layer weights are not generated hidden-major")
-    tmp = dev_matrix(N, H, dtype, device)
-    fill_matrix(tmp, dtype, seed, tag, layer, H, sigma)
+    rows, cols = t16.shape
+    g = t16.float().view(rows, cols // 128, 128)
+    s = (g.abs().amax(dim=2) / 7.0).half()
+    sf = s.float().unsqueeze(2)
+    safe = torch.where(sf > 0, sf, torch.ones_like(sf))
+    q = torch.where(sf > 0, torch.round(g / safe).clamp(-8, 7), torch.zeros_like(g)).to(torch.int16).view(rows, cols)
+    packed = ((q[:, 0::2] & 0xF) | ((q[:, 1::2] & 0xF) << 4)).to(torch.uint8)
+    return Matrix(packed.contiguous(), PI_I4G128, s.view(torch.int16).contiguous())
+
+
+def dev_matrix_hidden_major(N, H, dtype, seed, tag, layer, sigma, device):
+    """The [N x H] generated matrix stored transposed, [H x N] (fp32 / fp16 bits unchanged).
+    int4: the fp16 values, transposed, then quantised in groups of 128 along N."""
+    torch = _torch()
+    gen = synth.F16 if dtype == synth.I4G128 else dtype
+    tmp = dev_matrix(N, H, gen, device)
+    fill_matrix(tmp, gen, seed, tag, layer, H, sigma)
     out = Matrix(tmp.data.t().contiguous(), tmp.dtype)
     del tmp
+    if dtype == synth.I4G128:
+        out = i4_quantize_rows_dev(out.data)
     torch.cuda.current_stream().synchronize()
     return out
 

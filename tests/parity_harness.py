@@ -29,9 +29,8 @@ LOGIT_ATOL = 1e-4
 
 def small_case(key="small", d=256, N=1024, H=64, wdtype=synth.F16, pdtype=None, bdtype=None, gated=False,
                rho=0.1, alpha=1.1, gpu_frac=1.0, seed=11):
-    pdtype = wdtype if pdtype is None else pdtype
-    if pdtype == synth.I4G128:
-        pdtype = synth.F16
+    if pdtype is None:     # int4 FFN weights come with an fp16 predictor unless asked otherwise
+        pdtype = synth.F16 if wdtype == synth.I4G128 else wdtype
     if bdtype is None:
         bdtype = synth.F32 if wdtype == synth.F32 else synth.F16
     return synth.small_config(key, d=d, N=N, H=H, wdtype=wdtype, pdtype=pdtype, bdtype=bdtype, gated=gated,
@@ -101,11 +100,24 @@ def host_vec(stored, dtype):
     return orc.Vec(np.ascontiguousarray(stored), dtype)
 
 
+def oracle_p2(spec):
+    """The output layer's stored weights as the oracle takes them, [N x H].  An int4 predictor
+    stores them hidden-major with groups along N: the exact values q * s, transposed back, in
+    fp32 (exact: an fp16 scale times a 4-bit integer)."""
+    cfg, L, sig = spec.cfg, spec.layer, spec.sigmas()
+    if cfg.pdtype != synth.I4G128:
+        return host_mat(cfg.pdtype, cfg.seed, synth.TAG_P2, L, spec.H, sig[synth.TAG_P2], nrows=cfg.N)
+    v16, _ = synth.host_rows(synth.F16, cfg.seed, synth.TAG_P2, L, spec.H, sig[synth.TAG_P2], nrows=cfg.N)
+    packed, scales = synth.i4_quantize_rows(np.ascontiguousarray(v16.T))
+    w = synth.i4_dequant(packed, scales)                   # [H x N]
+    return orc.Mat(np.ascontiguousarray(w.T.astype(np.float32)), orc.F32, spec.H)
+
+
 def oracle_predict(spec, x):
     cfg, L, sig = spec.cfg, spec.layer, spec.sigmas()
     P1 = host_mat(cfg.pdtype, cfg.seed, synth.TAG_P1, L, cfg.d, sig[synth.TAG_P1], nrows=spec.H)
-    P2 = host_mat(cfg.pdtype, cfg.seed, synth.TAG_P2, L, spec.H, sig[synth.TAG_P2], nrows=cfg.N)
-    return orc.predict(x, P1, orc.Vec(None, cfg.bdtype), P2, host_vec(spec.c2, cfg.bdtype), return_hidden=True)
+    return orc.predict(x, P1, orc.Vec(None, cfg.bdtype), oracle_p2(spec), host_vec(spec.c2, cfg.bdtype),
+                       return_hidden=True)
 
 
 def oracle_ffn_on_ids(spec, x, ids: np.ndarray):

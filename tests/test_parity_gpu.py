@@ -48,6 +48,18 @@ def test_device_generator_matches_host_bits(dtype, cols):
         assert np.array_equal(m.scales.cpu().numpy().view(np.uint16), hs)
 
 
+def test_device_int4_quantiser_matches_host_bits():
+    """The hidden-major int4 predictor weights: the device quantiser gives the host's bits."""
+    torch = _dev()
+    from synth.device import i4_quantize_rows_dev
+    v16, _ = synth.host_rows(synth.F16, 4, synth.TAG_P2, 2, 640, 1 / np.sqrt(640), nrows=96)
+    v16[3, :128] = 0                                     # an all-zero group
+    m = i4_quantize_rows_dev(torch.from_numpy(v16.view(np.float16)).cuda())
+    packed, scales = synth.i4_quantize_rows(v16)
+    assert np.array_equal(m.data.cpu().numpy(), packed)
+    assert np.array_equal(m.scales.cpu().numpy().view(np.uint16), scales)
+
+
 # --------------------------------------------------------------------------- reduced shapes
 
 SMALL = [
@@ -58,6 +70,7 @@ SMALL = [
     ph.small_case("gated", d=512, N=1536, H=128, wdtype=synth.F16, gated=True, rho=0.15, seed=15),
     ph.small_case("gated-i4", d=640, N=1280, H=64, wdtype=synth.I4G128, gated=True, seed=16),
     ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=17),
+    ph.small_case("i4pred", d=768, N=2560, H=192, wdtype=synth.F16, pdtype=synth.I4G128, gpu_frac=0.4, seed=18),
 ]
 
 
@@ -133,7 +146,7 @@ def test_outputs_are_bitwise_repeatable():
 # --------------------------------------------------------------------------- full-size workloads, one layer each
 
 FULL = [("opt-768", 0, 1), ("opt-6.7b", 5, 1), ("llama-13b-gated", 7, 1), ("opt-30b", 3, 1), ("opt-30b", 3, 4),
-        ("opt-30b", 11, 16), ("opt-30b", 11, 32), ("opt-175b-int4", 42, 1)]
+        ("opt-30b", 11, 16), ("opt-30b", 11, 32), ("opt-175b-int4", 42, 1), ("opt-30b-i4pred", 3, 1)]
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])

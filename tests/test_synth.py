@@ -103,3 +103,25 @@ def test_top40_table_from_simulated_profiling():
     assert spec.counts[spec.T_g].min() >= spec.counts[spec.T_c].max()
     share = spec.p[spec.T_g].sum() / spec.p.sum()
     assert 0.80 < share < 0.86            # hot neurons carry most activations
+
+
+def test_int4_quantiser_rule_and_packing():
+    """synth.i4_quantize_rows: the scale is fp16(max|w| / 7) per 128 values, each value is
+    within half a step of q * s with q in [-8, 7], the even element sits in the low nibble, and
+    an all-zero group stores zeros."""
+    g = np.random.default_rng(3)
+    w = (g.standard_normal((5, 384)) * 0.05).astype(np.float16)
+    w[2, 128:256] = 0
+    w[4, 7] = np.float16(-0.5)                        # the group's largest magnitude, negative
+    packed, scales = synth.i4_quantize_rows(w.view(np.uint16))
+    assert packed.shape == (5, 192) and scales.shape == (5, 3)
+    s = scales.view(np.float16).astype(np.float64)
+    grp = np.abs(w.astype(np.float64)).reshape(5, 3, 128).max(axis=2)
+    assert np.array_equal(s, (grp / 7).astype(np.float16).astype(np.float64))
+    v = synth.i4_dequant(packed, scales)
+    err = np.abs(v - w.astype(np.float64))
+    assert np.all(err <= np.repeat(s, 128, axis=1) / 2 * (1 + 1e-6) + 1e-12)
+    assert not np.any(v[2, 128:256])
+    q0 = int(packed[4, 3] & 0xF)                       # element 6 (even): low nibble
+    q1 = int(packed[4, 3] >> 4)                        # element 7 (odd): high nibble, the -0.5
+    assert (q1 - 16 if q1 >= 8 else q1) == -7 and v[4, 6] == ((q0 - 16 if q0 >= 8 else q0) * s[4, 0])
