@@ -154,10 +154,42 @@ def cpu_baseline(cfg, B, seconds, n_layers_sample):
             break
     per_layer = t_total / n_done
     tok_s = B / (per_layer * cfg.n_layers)
-    return {"value": tok_s, "unit": "tokens/s", "cores": orc.get_threads(), "kind": "oracle",
+    cores = orc.get_threads()
+    # the same pipeline on one thread, over a few layer-steps of the same sample
+    one = None
+    saved = cores
+    orc.set_threads(1)
+    try:
+        t1, n1 = 0.0, 0
+        for (spec, P1, P2, g, c) in layers[:2]:
+            x = synth.host_x(cfg.seed, spec.layer, 20_000, B, cfg.d)
+            t0 = time.perf_counter()
+            logits = orc.predict(x, P1, orc.Vec(None, cfg.bdtype), P2, ph.host_vec(spec.c2, cfg.bdtype))
+            A_g, A_c = orc.compact(logits, 0.0, spec.T_g, spec.T_c if c else None)
+            y_g = orc.sparse_ffn(x, g["W1"], g["b1"], g["W2"], A_g, kind=kind, Wup=g["Wup"])
+            y_c = orc.sparse_ffn(x, c["W1"], c["b1"], c["W2"], A_c, kind=kind, Wup=c["Wup"]) if c else None
+            orc.merge(y_g, y_c, len(A_c) if c else 0)
+            t1 += time.perf_counter() - t0
+            n1 += 1
+        one = B / (t1 / n1 * cfg.n_layers)
+    finally:
+        orc.set_threads(saved)
+    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{n_done} layer-steps (layers 0..{Ls - 1}, {step} steps, batch {B}) of the same workload "
                       f"in {t_total:.1f} s, scaled to {cfg.n_layers} layers per token; includes the cold-neuron "
-                      f"side; weight generation not timed"}
+                      f"side; weight generation not timed",
+            "value_1_thread": one, "cpu_model": cpu_model(), "nproc": os.cpu_count()}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where there is none)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def log(msg):
@@ -743,15 +775,18 @@ def main():
     for t in range(args.warmup):
         run_step(t)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the first and last bracket the timed region, the others
+    # give each step's duration (for the median)
+    evs_step = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    e0.record()
-    for t in range(args.warmup, S):
+    evs_step[0].record()
+    for i, t in enumerate(range(args.warmup, S)):
         run_step(t)
-    e1.record()
+        evs_step[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
+    gpu_ms = evs_step[0].elapsed_time(evs_step[-1])
+    step_ms = [evs_step[i].elapsed_time(evs_step[i + 1]) for i in range(args.steps)]
     elapsed_s = max(wall, gpu_ms / 1e3)
     ms_per_step = elapsed_s * 1e3 / args.steps
     tokens_s = B * args.steps / elapsed_s
@@ -767,6 +802,7 @@ def main():
             tot_pred += p; tot_ffn += f; tot_small += sm
     step_bytes = (tot_pred + tot_ffn + tot_small) / args.steps
     step_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    step_ms_median = float(np.median(step_ms))
     # bytes a dense predictor (every P2 row) and an FC2 over every listed neuron would read
     dense_bytes = 0.0
     for t in range(args.warmup, S):
@@ -911,6 +947,8 @@ def main():
         "cpu_baseline": cpu,
         "detail": {"step_bytes": round(step_bytes), "step_gbps": round(step_gbs, 1),
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "step_ms_median": round(step_ms_median, 4),
+                   "step_frac_of_peak_median": round(step_bytes / (step_ms_median * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                    "bytes_split": {"predictor": round(tot_pred / args.steps), "ffn": round(tot_ffn / args.steps),
                                    "small": round(tot_small / args.steps)},
                    "step_bytes_if_dense_p2_and_full_fc2": round(dense_bytes),
