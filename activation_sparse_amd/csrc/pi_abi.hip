@@ -79,6 +79,8 @@ float* h_lo_part(float* h, int32_t B, int32_t H) {
 size_t mm_row_partial_bytes(int32_t B, int64_t rows, int64_t cols, bool gated) {
   if (!use_mm_row(B) || rows <= 0 || cols <= 0) return 0;
   int ks = pi::mm_row16_ks(rows, cols, pi::mm_nbt(B), gated);
+  const int kh = pi::mm_row16_ks(rows, cols, pi::mm_nbt(B), false, true);
+  ks = kh > ks ? kh : ks;
   for (int dt = 0; dt < 3; ++dt) {
     const int k = pi::mm_row_ks(dt, rows, cols);
     ks = k > ks ? k : ks;
@@ -195,7 +197,10 @@ int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* 
     pi::MmRowArgs m{};
     m.W = P1.data; m.Ws = P1.scales; m.dt = P1.dtype; m.gated = 0; m.cols = d; m.n_rows = H; m.list = nullptr;
     m.count_dev = nullptr; m.count_max = H; m.x = x; m.B = B; m.nbt = pi::mm_nbt(B);
-    m.ks = pi::mm_row_ks(P1.dtype, H, d); m.kc = pi::mm_row_kc(P1.dtype, d, m.ks); m.partials = partials;
+    // fp16 P1: the fp16 matrix cores with x in two fp16 parts (the logits keep near-fp32 precision)
+    m.x_hilo = P1.dtype == PI_F16;
+    m.ks = m.x_hilo ? pi::mm_row16_ks(H, d, m.nbt, false, true) : pi::mm_row_ks(P1.dtype, H, d);
+    m.kc = pi::mm_row_kc(P1.dtype, d, m.ks); m.partials = partials;
     m.bias = c1.data; m.bias_dt = c1.dtype; m.relu = 1; m.out = h; m.out_tr = h_tr;
     m.out_h8 = h_lay == 2; m.out_lo = h_lay == 2 ? h_lo_part(h, B, H) : nullptr;
     m.out_stride = h_tr ? 16 * m.nbt : H;

@@ -116,6 +116,8 @@ struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b
                                 // multiple of 32 positions), the activations of the fp16 axpy
   float* out_lo;                // with out_h8, optional: the same layout holding fp16(z - fp16(z))
   int x_f16;                    // fp16 weights: x may be rounded to fp16 (fp16 matrix cores; FC1 only)
+  int x_hilo;                   // fp16 weights: x as two fp16 parts, hi = fp16(x) and lo = fp16(x - hi),
+                                // both multiplied exactly (fp16 matrix cores at about 22 bits of x)
 };
 struct MmAxpyArgs {             // partials[chunk, b, c] = sum over the chunk's rows j of a[b, j] W[row(j), c]
   const void* W;
@@ -150,7 +152,7 @@ int mm_row_ks(int dt, int64_t count_max, int64_t cols);
 int64_t mm_row_kc(int dt, int64_t cols, int ks);
 // the fp16 matrix-core row-dot (x rounded to fp16, its k chunk staged in LDS)
 bool mm_row16_used(const MmRowArgs& a);
-int mm_row16_ks(int64_t count_max, int64_t cols, int nbt, bool gated);
+int mm_row16_ks(int64_t count_max, int64_t cols, int nbt, bool gated, bool hilo = false);
 int mm_axpy_col_chunks(int dt, int64_t cols);
 int mm_axpy_row_chunks(int dt, int nbt, int64_t count_max, int64_t cols);
 bool mm_rowdot_supported(int dt, int64_t rows, int64_t cols);

@@ -167,14 +167,14 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 // waves per block, sharing the block's x chunk (more for 32 batch rows, whose chunk is twice the size)
 constexpr int r16_waves(int nbt) { return nbt == 1 ? 4 : 16; }
-// largest k chunk: x[16 nbt][chunk] in fp16 within 64 KB of LDS
-constexpr int row16_kcmax(int nbt, bool) { return nbt == 1 ? 1024 : 960; }
+// largest k chunk: x[16 nbt][chunk] in fp16 within 64 KB of LDS (two such planes with hi / lo x)
+constexpr int row16_kcmax(int nbt, bool hilo = false) { return hilo ? (nbt == 1 ? 992 : 480) : (nbt == 1 ? 1024 : 960); }
 
 __device__ __forceinline__ float4v_t mfma16(half8_t a, half8_t b, float4v_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-template <int NBT, bool GATED>
+template <int NBT, bool GATED, bool HILO>
 __global__ __launch_bounds__(r16_waves(NBT) * kWave) void k_mm_rowdot16(MmRowArgs a) {
   constexpr int WPB = r16_waves(NBT), NT = WPB * kWave;
   constexpr int D = 8;                      // k blocks of 32 in flight
@@ -200,6 +200,12 @@ __global__ __launch_bounds__(r16_waves(NBT) * kWave) void k_mm_rowdot16(MmRowArg
       half4_t h;
       h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
       *reinterpret_cast<half4_t*>(xh + b * xs + 4 * q) = h;
+      if constexpr (HILO) {
+        half4_t l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l[e] = (_Float16)(v[e] - (float)h[e]);
+        *reinterpret_cast<half4_t*>(xh + (NBP + b) * xs + 4 * q) = l;
+      }
     }
   }
   __syncthreads();
@@ -239,6 +245,11 @@ __global__ __launch_bounds__(r16_waves(NBT) * kWave) void k_mm_rowdot16(MmRowArg
           const half8_t xb = *reinterpret_cast<const half8_t*>(xh + (16 * t + ml) * xs + kk + 32 * i + 8 * g);
           acc[t] = mfma16(__builtin_bit_cast(half8_t, wv[i]), xb, acc[t]);
           if constexpr (GATED) accu[t] = mfma16(__builtin_bit_cast(half8_t, uv[i]), xb, accu[t]);
+          if constexpr (HILO) {
+            const half8_t xl =
+                *reinterpret_cast<const half8_t*>(xh + (NBP + 16 * t + ml) * xs + kk + 32 * i + 8 * g);
+            acc[t] = mfma16(__builtin_bit_cast(half8_t, wv[i]), xl, acc[t]);
+          }
         }
       }
     }
@@ -622,15 +633,18 @@ hipError_t rowdot_dt(const MmRowArgs& a, hipStream_t s) {
   const int tiles = (int)((a.count_max + 15) / 16);
   const dim3 g((unsigned)((tiles + kMmWaves - 1) / kMmWaves), (unsigned)a.ks), t(kMmThreads);
   if (mm_row16_used(a)) {
-    const size_t shm = (size_t)16 * a.nbt * (size_t)(a.kc + 8) * 2;
+    const size_t shm = (size_t)16 * a.nbt * (size_t)(a.kc + 8) * 2 * (a.x_hilo ? 2 : 1);
     const int wpb = r16_waves(a.nbt);
     const dim3 g((unsigned)((tiles + wpb - 1) / wpb), (unsigned)a.ks), t(wpb * kWave);
-    if (a.nbt == 1) {
-      if (a.gated) hipLaunchKernelGGL((k_mm_rowdot16<1, true>), g, t, shm, s, a);
-      else hipLaunchKernelGGL((k_mm_rowdot16<1, false>), g, t, shm, s, a);
+    if (a.x_hilo) {          // the predictor's hidden layer: never gated
+      if (a.nbt == 1) hipLaunchKernelGGL((k_mm_rowdot16<1, false, true>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_rowdot16<2, false, true>), g, t, shm, s, a);
+    } else if (a.nbt == 1) {
+      if (a.gated) hipLaunchKernelGGL((k_mm_rowdot16<1, true, false>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_rowdot16<1, false, false>), g, t, shm, s, a);
     } else {
-      if (a.gated) hipLaunchKernelGGL((k_mm_rowdot16<2, true>), g, t, shm, s, a);
-      else hipLaunchKernelGGL((k_mm_rowdot16<2, false>), g, t, shm, s, a);
+      if (a.gated) hipLaunchKernelGGL((k_mm_rowdot16<2, true, false>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_rowdot16<2, false, false>), g, t, shm, s, a);
     }
     return hipGetLastError();
   }
@@ -678,12 +692,15 @@ int mm_row_ks(int dt, int64_t count_max, int64_t cols) {
 }
 
 bool mm_row16_used(const MmRowArgs& a) {
-  return a.x_f16 && a.dt == PI_F16 && a.cols % 32 == 0 && a.kc <= row16_kcmax(a.nbt, a.gated) && a.kc % 32 == 0;
+  if (a.x_hilo && a.gated) return false;
+  return (a.x_f16 || a.x_hilo) && a.dt == PI_F16 && a.cols % 32 == 0 && a.kc <= row16_kcmax(a.nbt, a.x_hilo) &&
+         a.kc % 32 == 0;
 }
 
-int mm_row16_ks(int64_t count_max, int64_t cols, int nbt, bool gated) {
+int mm_row16_ks(int64_t count_max, int64_t cols, int nbt, bool gated, bool hilo) {
   // the k chunk fits the LDS bound, and about 4096 waves
-  const int64_t kcmax = row16_kcmax(nbt, gated);
+  (void)gated;
+  const int64_t kcmax = row16_kcmax(nbt, hilo);
   const int64_t tiles = (count_max + 15) / 16;
   int64_t ks = (4096 + tiles - 1) / (tiles > 0 ? tiles : 1);
   const int64_t kmax = cols / 256;          // at least 8 k blocks per wave
