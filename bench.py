@@ -234,24 +234,23 @@ def committed_traffic(kernel):
     return val if (digest == kernel_source_digest() and val is not None) else None
 
 
-LAYER_HEADS = ("k_hidden_b1", "k_mm_rowdot", "k_rowdot")   # the predictor hidden layer opens every layer call
+LAYER_TAILS = ("k_reduce_y", "k_reduce")   # the ordered sum with the merge closes every layer call
 
 
 def _layer_call_sites(rows):
-    """Per call site within a layer: the dispatches (in start order) cut into sequences at each
-    predictor hidden-layer kernel; over the sequences equal to the most common one, the duration of
-    each position (a kernel launched twice per layer is reported at each of its sites)."""
+    """Per call site within a layer: the dispatches (in start order) cut into sequences after each
+    ordered-sum kernel that closes a layer call; over the sequences equal to the most common one
+    (whatever else ran between two layer calls makes a sequence differ), the duration of each
+    position (a kernel launched twice per layer is reported at each of its sites)."""
     import collections
     import statistics as st
-    seqs, cur = [], None
+    seqs, cur = [], []
     for r in rows:
         k = _short_kernel(r["Kernel_Name"])
-        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        if k in LAYER_HEADS:
-            cur = []
+        cur.append((k, (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        if k in LAYER_TAILS:
             seqs.append(cur)
-        if cur is not None:
-            cur.append((k, dur))
+            cur = []
     if not seqs:
         return []
     common, n = collections.Counter(tuple(k for k, _ in q) for q in seqs).most_common(1)[0]

@@ -88,6 +88,10 @@ typedef struct pi_vector {
  * unit whose ReLU output is zero is one row that need not be read.  Both
  * PI_F32/PI_F16/PI_I4G128 (int4 groups run along the row, i.e. along N).
  * logits [B x N] fp32, written.   h lives in the workspace.
+ * Precision: fp32 accumulation.  With fp16 weights and B >= 2 the matrix
+ * cores take x and h each as two fp16 parts, hi = fp16(v) and lo =
+ * fp16(v - hi) (about 22 bits; every product exact), so |x| must stay below
+ * 65504.
  * ws: at least pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0) bytes.
  * Errors: PI_EINVAL for a NULL required pointer, B outside 1..PI_MAX_BATCH,
  * a non-positive size, a column count the dtype forbids (d for P1, N for P2)
@@ -138,7 +142,8 @@ int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float ta
  * Precision: accumulation is fp32.  With fp16 weights and B >= 2 the matrix
  * cores take x rounded to fp16 for FC1 and a rounded to fp16 for FC2 (each
  * product of two fp16 values is exact), so |x| must stay below 65504; the
- * predictor's logits keep near-fp32 precision (h enters as two fp16 parts).
+ * predictor's logits keep near-fp32 precision (x and h enter it as two fp16
+ * parts each).
  * Other cases use fp32 products.
  * ws: at least pi_workspace_bytes(PI_OP_SPARSE_FFN, B, d, 0, 0, n_g) bytes.
  * Errors: as pi_predict, plus PI_EINVAL for a kind outside PI_RELU /

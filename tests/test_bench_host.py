@@ -42,12 +42,30 @@ def test_summary_of_a_kernel_trace(tmp_path):
     # four of the five isolated launches follow another k_pred_fc1
     iso = [l for l in out.splitlines() if l.startswith("k_pred_fc1 back-to-back")][0].split()
     assert iso[2] == "4"
-    # the per-layer table: ten sequences headed by the hidden-layer kernel (the last one carries
-    # the isolated launches and so is not the common sequence)
-    assert "per layer call (9 layer sequences of 4 kernels)" in out
+    # the per-layer table: ten sequences closed by the ordered sum (the isolated launches after them
+    # close no layer call)
+    assert "per layer call (10 layer sequences of 4 kernels)" in out
     assert any(l.split()[:2] == ["2", "k_fc2_seg"] for l in out.splitlines())
     total = [l for l in out.splitlines() if l.strip().startswith("sum")][0].split()
     assert float(total[1]) == pytest.approx(34.0)
+
+
+def test_batched_layer_call_sites(tmp_path):
+    """A kernel launched twice per layer (the matrix-core row-dot for the hidden layer and FC1) is
+    reported at both of its sites; setup kernels before the first call are not a layer call."""
+    layer = [("k_mm_rowdot16<1, false, true>(...)", 5.0), ("k_mm_finish_tr<false>(...)", 4.0),
+             ("k_mm_axpy16<1, true>(...)", 16.0), ("k_list(...)", 5.0), ("k_mm_rowdot16<1, false, false>(...)", 23.0),
+             ("k_mm_finish_tr<false>(...)", 4.5), ("k_mm_axpy16<1, false>(...)", 20.0), ("k_reduce(...)", 4.0)]
+    d = tmp_path / "prof"
+    d.mkdir()
+    _trace(d / "run_kernel_trace.csv", [("k_fill_dense(...)", 30.0)] * 3 + layer * 6)
+    out = bench.rocprof_summary([str(d)], 256)
+    assert "per layer call (5 layer sequences of 8 kernels)" in out
+    sites = [l.split() for l in out.splitlines() if l[:4].strip().isdigit() and len(l.split()) == 4]
+    assert [r[1] for r in sites if r[1] == "k_mm_rowdot16"] == ["k_mm_rowdot16"] * 2
+    assert float([r for r in sites if r[0] == "4"][0][2]) == pytest.approx(23.0)
+    total = [l for l in out.splitlines() if l.strip().startswith("sum")][0].split()
+    assert float(total[1]) == pytest.approx(81.5)
 
 
 def test_counter_scaling_by_the_plain_copy(tmp_path):
