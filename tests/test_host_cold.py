@@ -124,3 +124,32 @@ def test_argument_checks():
         host.pi_cold_ffn(1, d, n_c, x, _pm(W1), _pv(b1), W2_32, bad_slot[:1], 1, y)
     with pytest.raises(pi.PiError, match="EINVAL"):
         host.pi_cold_ffn(1, d, n_c, x, _pm(W1), _pv(b1), _pm(W2), bad_slot[:1], 1, y, kind=pi.PI_GATED_RELU)
+
+
+def test_hybrid_layer_rejects_bad_arguments():
+    """pi_hybrid_layer checks its arguments before any HIP call: a missing layer, scratch, input,
+    output or GPU table, a batch outside 1..PI_MAX_BATCH, and a CPU table without the host
+    buffers and the event it needs."""
+    import ctypes as C
+    FAKE = 1 << 20
+    lay = pi.Layer(256, 1024, 64, 512, pi.PI_RELU, True, pi.Matrix(FAKE, pi.PI_F16), None,
+                   pi.Matrix(FAKE, pi.PI_F16), None, FAKE, pi.Matrix(FAKE, pi.PI_F16), None, None,
+                   pi.Matrix(FAKE, pi.PI_F16), None)._c()
+    full = host._HybridScratch(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, FAKE, 1 << 20, FAKE, FAKE, FAKE, FAKE)
+    cold = host._HostCold(512, host._Mat(FAKE, None, pi.PI_F16), host._Vec(None, 0), host._Mat(None, None, 0),
+                          host._Mat(FAKE, None, pi.PI_F16))
+    L = host.load()
+
+    def call(layer=lay, T_g=FAKE, T_c=FAKE, cold_c=cold, B=1, x=FAKE, y=FAKE, scratch=full):
+        return L.pi_hybrid_layer(0, C.byref(layer) if layer is not None else None, T_g, T_c,
+                                 C.byref(cold_c) if cold_c is not None else None, B, x, 0.0, y,
+                                 C.byref(scratch) if scratch is not None else None, 0, None)
+
+    assert call(layer=None) == pi.PI_EINVAL
+    assert call(scratch=None) == pi.PI_EINVAL
+    assert call(x=None) == pi.PI_EINVAL and call(y=None) == pi.PI_EINVAL and call(T_g=None) == pi.PI_EINVAL
+    assert call(B=0) == pi.PI_EINVAL and call(B=pi.PI_MAX_BATCH + 1) == pi.PI_EINVAL
+    for field in ("cold_list", "y_c", "x_host", "cold_list_host", "y_c_host", "event"):
+        s = host._HybridScratch.from_buffer_copy(full)
+        setattr(s, field, None)
+        assert call(scratch=s) == pi.PI_EINVAL, field
