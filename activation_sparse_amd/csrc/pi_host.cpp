@@ -2,18 +2,21 @@
 // the host, for the pages' GPU-CPU hybrid layer.
 //
 // FC1: each listed neuron's row is read once and dotted with every batch row
-// of x (threads take fixed ranges of the list).  FC2: the d columns are split
-// into one fixed range per thread; each thread streams its slice of the W2 row
-// of every neuron with a non-zero output, in list order, into its slice of
-// y_c.  A dot product keeps 32 partial sums (4 x 8 lanes, k = 32 i + 8 q + l)
-// and adds them in one fixed tree, with fused multiply-adds; the AVX2 path
-// and the scalar path follow the same order, so the bits are the same on
-// either and for any thread count.
+// of x (threads take fixed ranges of the list).  FC2: the neurons with a
+// non-zero output, in list order, are cut into chunks of a size fixed by their
+// count alone; a thread streams whole W2 rows of a chunk into that chunk's
+// partial y (each row one contiguous run, which the hardware prefetchers
+// follow), and then y_c is the sum of the chunks' partials in chunk order,
+// column ranges split over the threads.  A dot product keeps 32 partial sums
+// (4 x 8 lanes, k = 32 i + 8 q + l) and adds them in one fixed tree, with fused
+// multiply-adds; the AVX2 path and the scalar path follow the same order, so
+// the bits are the same on either and for any thread count.
 #include <immintrin.h>
 #include <omp.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -44,6 +47,9 @@ inline float half_to_float(uint16_t h) {
   memcpy(&f, &bits, 4);
   return f;
 }
+
+constexpr int64_t kFc2ChunkRows = 16;   // FC2: fewest rows per chunk
+constexpr int64_t kFc2MaxChunks = 64;   // FC2: most chunks (bounds the partials at 64 x B x d floats)
 
 struct Rows {
   const char* data;
@@ -233,18 +239,38 @@ extern "C" int pi_cold_ffn_ex(int32_t B, int32_t d, int32_t n_c, int32_t kind, c
     for (int b = 0; b < B; ++b) any = any || a[(size_t)j * B + b] != 0.f;
     if (any) act.push_back(j);
   }
-  // FC2 over fixed column ranges (multiples of 8 columns)
+  // FC2: chunks of the contributing rows (at least kFc2ChunkRows rows, at most kFc2MaxChunks
+  // chunks), each into its own partial [B x d]; then the partials summed in chunk order
+  const int64_t R = (int64_t)act.size();
+  int64_t crows = (R + kFc2MaxChunks - 1) / kFc2MaxChunks;
+  crows = crows < kFc2ChunkRows ? kFc2ChunkRows : crows;
+  const int64_t nch = (R + crows - 1) / crows;
+  const int64_t plane = (int64_t)B * dd;
+  static thread_local std::vector<float> part;          // reused by the calling thread
+  if ((int64_t)part.size() < nch * plane) part.resize((size_t)(nch * plane));
+  float* pp = part.data();
+#pragma omp parallel for schedule(static) num_threads(nt)
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    float* yp = pp + ch * plane;
+    std::fill(yp, yp + plane, 0.f);
+    const int64_t q1 = (ch + 1) * crows < R ? (ch + 1) * crows : R;
+    for (int64_t q = ch * crows; q < q1; ++q) {
+      const int32_t j = act[(size_t)q];
+      if (vec) axpy_avx2(w2, A_c[j], &a[(size_t)j * B], B, dd, 0, dd, yp);
+      else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, 0, dd, yp);
+    }
+  }
   const int64_t nvec = dd / 8;
 #pragma omp parallel for schedule(static) num_threads(nt)
   for (int t = 0; t < nt; ++t) {
     const int64_t c0 = nvec * t / nt * 8, c1 = nvec * (t + 1) / nt * 8;
-    for (int b = 0; b < B; ++b)
-      for (int64_t c = c0; c < c1; ++c) y_c[(int64_t)b * dd + c] = 0.f;
-    if (c0 == c1) continue;
-    for (size_t q = 0; q < act.size(); ++q) {
-      const int32_t j = act[q];
-      if (vec) axpy_avx2(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
-      else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
+    for (int b = 0; b < B; ++b) {
+      float* yb = y_c + (int64_t)b * dd;
+      for (int64_t c = c0; c < c1; ++c) yb[c] = 0.f;
+      for (int64_t ch = 0; ch < nch; ++ch) {
+        const float* pb = pp + ch * plane + (int64_t)b * dd;
+        for (int64_t c = c0; c < c1; ++c) yb[c] += pb[c];
+      }
     }
   }
   return PI_OK;

@@ -35,13 +35,17 @@ extern "C" {
  * [n_c x d] each, W2 neuron-major; b1 [n_c] (optional).  For j < K_c, c = A_c[j]:
  *   a[b,j] = max(0, W1[c].x_b + b1[c])                    (PI_RELU)
  *   a[b,j] = max(0, W1[c].x_b + b1[c]) * (Wup[c].x_b)     (PI_GATED_RELU)
- *   y_c[b,:] = sum_j a[b,j] * W2[c,:]   (list order; a neuron whose a is 0 in
- *                                        every batch row adds nothing and its
- *                                        W2 row is not read)
+ *   y_c[b,:] = sum_j a[b,j] * W2[c,:]   (a neuron whose a is 0 in every
+ *                                        batch row adds nothing and its W2 row
+ *                                        is not read; the others are summed in
+ *                                        list order within chunks whose size
+ *                                        depends on their count only, and the
+ *                                        chunk sums in chunk order)
  * x [B x d] fp32; A_c [K_c] int32 (the CPU-table slots pi_compact lists);
  * y_c [B x d] fp32, fully written (zero when K_c = 0).  threads: the number
  * of threads (<= 0: the OpenMP default).  Host scratch of B * K_c floats is
- * allocated for the FC1 outputs.
+ * allocated for the FC1 outputs; the FC2 chunks' partial sums (at most
+ * 64 * B * d floats) live in a buffer the calling thread keeps between calls.
  * Errors: PI_EINVAL for a NULL required pointer, B outside 1..PI_MAX_BATCH,
  * d <= 0 or not a multiple of 8 (128 for int4), K_c < 0, n_c < K_c, a slot
  * outside [0, n_c), a kind outside PI_RELU / PI_GATED_RELU or a gated call
