@@ -2,12 +2,13 @@
 // the host, for the pages' GPU-CPU hybrid layer.
 //
 // FC1: each listed neuron's row is read once and dotted with every batch row
-// of x (threads take fixed ranges of the list).  FC2: the neurons with a
-// non-zero output, in list order, are cut into chunks of a size fixed by their
-// count alone; a thread streams whole W2 rows of a chunk into that chunk's
-// partial y (each row one contiguous run, which the hardware prefetchers
-// follow), and then y_c is the sum of the chunks' partials in chunk order,
-// column ranges split over the threads.  A dot product keeps 32 partial sums
+// of x (threads take fixed ranges of the list).  FC2 over the neurons with a
+// non-zero output, in list order: when they are few, each thread streams its
+// fixed column slice of every such row into its slice of y_c; when they are
+// many, they are cut into chunks of a size fixed by their count alone, a
+// thread streams whole W2 rows of a chunk into that chunk's partial y (each
+// row one contiguous run, which the hardware prefetchers follow), and y_c is
+// the sum of the chunks' partials in chunk order.  A dot product keeps 32 partial sums
 // (4 x 8 lanes, k = 32 i + 8 q + l) and adds them in one fixed tree, with fused
 // multiply-adds; the AVX2 path and the scalar path follow the same order, so
 // the bits are the same on either and for any thread count.
@@ -48,6 +49,8 @@ inline float half_to_float(uint16_t h) {
   return f;
 }
 
+constexpr int64_t kFc1PrefetchBytes = 2048;   // FC1: leading bytes of the next row requested early
+constexpr int64_t kFc2ChunkMinRows = 128;   // FC2: fewer contributing rows take column ranges
 constexpr int64_t kFc2ChunkRows = 16;   // FC2: fewest rows per chunk
 constexpr int64_t kFc2MaxChunks = 64;   // FC2: most chunks (bounds the partials at 64 x B x d floats)
 
@@ -216,6 +219,11 @@ extern "C" int pi_cold_ffn_ex(int32_t B, int32_t d, int32_t n_c, int32_t kind, c
 #pragma omp parallel for schedule(static) num_threads(nt)
   for (int32_t j = 0; j < K_c; ++j) {
     const int64_t c = A_c[j];
+    // the next listed row starts a new stream: request its first lines before this row's dot
+    if (j + 1 < K_c) {
+      const char* pn = w1.row(A_c[j + 1]);
+      for (int64_t o = 0; o < kFc1PrefetchBytes && o < rb; o += 64) _mm_prefetch(pn + o, _MM_HINT_T0);
+    }
     float z[PI_MAX_BATCH], u[PI_MAX_BATCH];
     if (vec) dots_avx2(w1, c, x, B, dd, z);
     else dots_scalar(w1, c, x, B, dd, z);
@@ -239,9 +247,28 @@ extern "C" int pi_cold_ffn_ex(int32_t B, int32_t d, int32_t n_c, int32_t kind, c
     for (int b = 0; b < B; ++b) any = any || a[(size_t)j * B + b] != 0.f;
     if (any) act.push_back(j);
   }
-  // FC2: chunks of the contributing rows (at least kFc2ChunkRows rows, at most kFc2MaxChunks
-  // chunks), each into its own partial [B x d]; then the partials summed in chunk order
+  // FC2.  Few contributing rows: every thread takes a fixed range of columns over all the rows
+  // (all threads busy).  Many: chunks of whole rows (at least kFc2ChunkRows, at most
+  // kFc2MaxChunks chunks), each into its own partial [B x d], then the partials summed in chunk
+  // order (contiguous runs the hardware prefetchers follow).  Which one depends on the row count
+  // only.
   const int64_t R = (int64_t)act.size();
+  const int64_t nvec = dd / 8;
+  if (R < kFc2ChunkMinRows) {
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int t = 0; t < nt; ++t) {
+      const int64_t c0 = nvec * t / nt * 8, c1 = nvec * (t + 1) / nt * 8;
+      for (int b = 0; b < B; ++b)
+        for (int64_t c = c0; c < c1; ++c) y_c[(int64_t)b * dd + c] = 0.f;
+      if (c0 == c1) continue;
+      for (int64_t q = 0; q < R; ++q) {
+        const int32_t j = act[(size_t)q];
+        if (vec) axpy_avx2(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
+        else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
+      }
+    }
+    return PI_OK;
+  }
   int64_t crows = (R + kFc2MaxChunks - 1) / kFc2MaxChunks;
   crows = crows < kFc2ChunkRows ? kFc2ChunkRows : crows;
   const int64_t nch = (R + crows - 1) / crows;
@@ -260,7 +287,6 @@ extern "C" int pi_cold_ffn_ex(int32_t B, int32_t d, int32_t n_c, int32_t kind, c
       else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, 0, dd, yp);
     }
   }
-  const int64_t nvec = dd / 8;
 #pragma omp parallel for schedule(static) num_threads(nt)
   for (int t = 0; t < nt; ++t) {
     const int64_t c0 = nvec * t / nt * 8, c1 = nvec * (t + 1) / nt * 8;

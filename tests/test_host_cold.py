@@ -153,3 +153,21 @@ def test_hybrid_layer_rejects_bad_arguments():
         s = host._HybridScratch.from_buffer_copy(full)
         setattr(s, field, None)
         assert call(scratch=s) == pi.PI_EINVAL, field
+
+
+@pytest.mark.parametrize("K", [40, 127, 128, 600, 1500])
+def test_both_fc2_orders_match_the_oracle(K):
+    """FC2 takes column ranges over few contributing rows and chunks of whole rows over many
+    (which, by the row count alone): both against the oracle, and bitwise across thread counts.
+    A bias of +4 makes every listed neuron contribute, so K is the row count."""
+    n_c, d, B = 1600, 256, 2
+    W1, _, _, W2 = _case(synth.F16, n_c, d, 21 + K, bias=False)
+    on = orc.Vec(np.full(n_c, 4.0, np.float32), orc.F32)
+    g = np.random.default_rng(K)
+    A_c = np.sort(g.choice(n_c, size=K, replace=False)).astype(np.int32)
+    x = g.standard_normal((B, d)).astype(np.float32)
+    ys = [_run_host(x, W1, on, None, W2, A_c, n_c, threads=t) for t in (1, 5, 16)]
+    for y in ys[1:]:
+        assert y.tobytes() == ys[0].tobytes()
+    ref = orc.sparse_ffn(x, W1, on, W2, A_c, kind=orc.RELU)
+    assert ph.rel_err(ys[0].astype(np.float64), ref) <= 1e-5
