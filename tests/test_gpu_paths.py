@@ -322,3 +322,60 @@ def test_read_probe_reads_every_word(nbytes, blocks):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_graph_replays_match_the_eager_call(B):
+    """A three-layer stack captured in a HIP graph (as the benchmark times it) and replayed four
+    times, with eager layer calls on other buffers and host synchronisations between the replays:
+    every replay's outputs (y, logits, lists and counts) equal the eager call's bits."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    cfg = ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=17)
+    specs = [synth.layer_spec(cfg, l) for l in range(3)]
+    dls = [ph.DeviceLayer(s) for s in specs]
+    bufs = [ph.DeviceBuffers(cfg, s.H, s.n_g, len(s.T_c), B) for s in specs]
+    other = ph.DeviceBuffers(cfg, specs[0].H, specs[0].n_g, len(specs[0].T_c), B)
+    g = np.random.default_rng(B)
+    for l, b in enumerate(bufs):
+        b.x.copy_(torch.from_numpy(synth.host_x(cfg.seed, l, 9, B, cfg.d)))
+        b.y_c.copy_(torch.from_numpy((g.standard_normal((B, cfg.d)) * 0.05).astype(np.float32)))
+    other.x.copy_(torch.from_numpy(synth.host_x(cfg.seed, 0, 10, B, cfg.d)))
+
+    def call(l, b):
+        pi.pi_ffn_layer(dls[l].layer, B, b.x, 0.0, b.y_c, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c, b.ws_layer)
+
+    def state():
+        out = []
+        for b in bufs:
+            K, Kc = int(b.K.cpu()[0]), int(b.K_c.cpu()[0])
+            out.append((b.y.cpu().numpy().tobytes(), b.logits.cpu().numpy().tobytes(), K, Kc,
+                        b.A_g.cpu().numpy()[:K].tobytes(), b.A_c.cpu().numpy()[:Kc].tobytes()))
+        return out
+
+    def clear():
+        for b in bufs:
+            b.y.fill_(float("nan")); b.logits.fill_(float("nan")); b.K.fill_(-1); b.K_c.fill_(-1)
+            b.A_g.fill_(-1); b.A_c.fill_(-1)
+
+    print(f"graph replays B={B}", flush=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for l, b in enumerate(bufs):
+            call(l, b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = state()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for l, b in enumerate(bufs):
+            call(l, b)
+    torch.cuda.synchronize()
+    for r in range(4):
+        clear()
+        call(0, other)                       # eager work of its own between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert state() == eager, r
