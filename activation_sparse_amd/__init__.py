@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libpi.so")
 
 EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes",
            "pi_table_prepare", "pi_ffn_layer", "pi_ffn_layer_stages", "pi_workspace_bytes", "pi_status_string",
-           "pi_last_hip_error", "pi_abi_version", "pi_read_probe")
+           "pi_last_hip_error", "pi_abi_version", "pi_read_probe", "pi_ffn_layer_ahead")
 
 
 class PiError(RuntimeError):
@@ -76,6 +76,9 @@ def load():
         L.pi_ffn_layer_stages.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P, P, C.c_size_t, P,
                                           C.c_uint32, P]
         L.pi_ffn_layer_stages.restype = C.c_int
+        L.pi_ffn_layer_ahead.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P, P, C.c_size_t,
+                                         C.c_uint32, C.POINTER(_Layer), P, C.c_size_t]
+        L.pi_ffn_layer_ahead.restype = C.c_int
         L.pi_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.pi_workspace_bytes.restype = C.c_size_t
         L.pi_status_string.argtypes = [I]
@@ -243,6 +246,19 @@ def pi_ffn_layer(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_
     _check(load().pi_ffn_layer(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
                                _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c), _ptr(ws), nbytes, events),
            "pi_ffn_layer")
+
+
+def pi_ffn_layer_ahead(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_c, K_c, ws, stages: int,
+                       next_layer: Layer, ws_next, ws_bytes=None, ws_next_bytes=None, stream=None, _cstruct=None,
+                       _next_cstruct=None) -> None:
+    """pi_ffn_layer_stages on `layer`, plus `next_layer`'s predictor hidden layer from this x into ws_next."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    nnext = ws_next_bytes if ws_next_bytes is not None else ws_next.numel() * ws_next.element_size()
+    cl = _cstruct if _cstruct is not None else layer._c()
+    cn = _next_cstruct if _next_cstruct is not None else next_layer._c()
+    _check(load().pi_ffn_layer_ahead(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
+                                     _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c), _ptr(ws), nbytes,
+                                     int(stages), C.byref(cn), _ptr(ws_next), nnext), "pi_ffn_layer_ahead")
 
 
 def pi_ffn_layer_stages(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_c, K_c, ws, stages: int,

@@ -466,9 +466,19 @@ int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, u
   return hip_status(pi::launch_read_probe(buf, (int64_t)bytes, blocks, out, static_cast<hipStream_t>(stream)));
 }
 
-int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c,
-                        float* y, float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws,
-                        size_t ws_bytes, void* const* events, uint32_t stages, int32_t* rows_read) {
+namespace {
+
+// The next layer's predictor hidden layer, computed ahead on this layer's input.
+struct Ahead {
+  const pi_layer* next;
+  float* h;              // next's h in its workspace
+  float* partials;       // next's predictor partials in its workspace
+  int h_lay;
+};
+
+int layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c, float* y,
+                 float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes,
+                 void* const* events, uint32_t stages, int32_t* rows_read, const Ahead* ah) {
   if (!L) return PI_EINVAL;
   const int32_t d = L->d, N = L->N, H = L->H, n_g = L->n_g;
   if (N <= 0 || H <= 0 || n_g > N) return PI_EINVAL;
@@ -519,6 +529,13 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
       a.d = d; a.n_g = n_g; a.x = x; a.b1 = L->b1.data; a.b1_dt = L->b1.dtype;
       a.seg_slot = w.seg_slot; a.seg_cold = w.seg_cold; a.pos_slot = w.pos_slot; a.pos_a = w.pos_a; a.cnt = w.cnt;
       a.rows_read = rows_read;
+      // the next layer's hidden layer rides in this launch when its rows have the FC1 weights' format
+      if (ah && ah->h_lay == 0 && ah->next->P1.dtype == L->W1.dtype &&
+          (!ah->next->c1.data || ah->next->c1.dtype == bdt)) {
+        a.nP1 = ah->next->P1.data; a.nP1s = ah->next->P1.scales; a.nc1 = ah->next->c1.data; a.nH = ah->next->H;
+        a.nh = ah->h;
+        ah = nullptr;
+      }
       if ((st = hip_status(pi::launch_pred_fc1(a, gated, s))) != PI_OK) return st;
     }
     if ((st = record(2)) != PI_OK || (st = record(3)) != PI_OK) return st;
@@ -537,7 +554,9 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
       r.b2 = L->b2.data; r.b2_dt = L->b2.dtype;
       if ((st = hip_status(pi::launch_reduce_y(r, s))) != PI_OK) return st;
     }
-    return record(5);
+    if ((st = record(5)) != PI_OK) return st;
+    return ah ? enqueue_hidden(s, B, d, ah->next->H, x, ah->next->P1, ah->next->c1, ah->h, ah->partials, ah->h_lay)
+              : PI_OK;
   }
   // any batch: output layer + activation words, the lists, then FC1 / FC2 / ordered sum over the list
   if (want(PI_STAGE_OUTPUT)) {
@@ -556,7 +575,34 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float*
   st = enqueue_ffn(s, B, d, n_g, L->kind, x, L->W1, L->b1, L->Wup, L->W2, A_g, K, w.a, w.partials, y, y_c,
                    L->cold ? K_c : nullptr, L->b2, ev + 3, stages);
   if (st != PI_OK) return st;
-  return record(5);
+  if ((st = record(5)) != PI_OK) return st;
+  return ah ? enqueue_hidden(s, B, d, ah->next->H, x, ah->next->P1, ah->next->c1, ah->h, ah->partials, ah->h_lay)
+            : PI_OK;
+}
+
+}  // namespace
+
+int pi_ffn_layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c,
+                        float* y, float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws,
+                        size_t ws_bytes, void* const* events, uint32_t stages, int32_t* rows_read) {
+  return layer_stages(stream, L, B, x, tau, y_c, y, logits, A_g, K, A_c, K_c, ws, ws_bytes, events, stages, rows_read,
+                      nullptr);
+}
+
+int pi_ffn_layer_ahead(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c,
+                       float* y, float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws,
+                       size_t ws_bytes, uint32_t stages, const pi_layer* next, void* ws_next, size_t ws_next_bytes) {
+  if (!L || !next) return PI_EINVAL;
+  if (next->d != L->d || next->H <= 0 || next->N <= 0 || next->n_g < 0 || next->n_g > next->N ||
+      !valid_matrix(next->P1, next->d) || !valid_vector(next->c1))
+    return PI_EINVAL;
+  if (!ws_next || !aligned16(ws_next)) return PI_EWORKSPACE;
+  const LayerWs wn = layer_ws_layout(ws_next, B, next->d, next->H, next->N, next->n_g);
+  if (ws_next_bytes < wn.bytes) return PI_EWORKSPACE;
+  if (ws_next == ws) return PI_EINVAL;                  // the next layer's h would overwrite this one's
+  Ahead ah{next, wn.h, wn.partials, h_layout(B, next->d, next->H, next->N, next->P1, next->P2)};
+  return layer_stages(stream, L, B, x, tau, y_c, y, logits, A_g, K, A_c, K_c, ws, ws_bytes, nullptr, stages, nullptr,
+                      &ah);
 }
 
 int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c, float* y,

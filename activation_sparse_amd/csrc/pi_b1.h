@@ -63,6 +63,14 @@ struct PredFc1Args {
   float* pos_a;              // [groups x 64] their FC1 outputs
   uint32_t* cnt;             // [groups] GPU count | CPU count << 8 | non-zero count << 16
   int32_t* rows_read;        // optional: block 0 writes the number of output-layer rows read
+  // look-ahead (FC1 launches only): blocks past the N/T tiles each take T/8 rows of the next
+  // layer's predictor hidden layer, nh[m] = max(0, nP1[m].x + nc1[m]), on this layer's x (nP1 in
+  // the FC1 weights' format, nc1 in b1's); nh == NULL: none
+  const void* nP1;
+  const uint16_t* nP1s;
+  const void* nc1;
+  int nH;
+  float* nh;
 };
 // Group count word fields.
 __host__ __device__ constexpr uint32_t cnt_gpu(uint32_t c) { return c & 0xFFu; }

@@ -265,6 +265,47 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     }
   }
 
+  if constexpr (FC1) {
+    // ---- look-ahead blocks: one row of the next layer's predictor hidden layer per wave, on
+    // the x this block has staged (block-uniform branch)
+    const int ntiles = (N + T - 1) / T;
+    if (a.nh && (int)blockIdx.x >= ntiles) {
+      __syncthreads();
+      const int m = ((int)blockIdx.x - ntiles) * W + wave;
+      if (m < a.nH) {
+        const int64_t rb = row_bytes(DT, a.d);
+        const int groups = a.d / 128;
+        const Bias<BDT> c1_at(a.nc1, (uint32_t)a.nH);
+        LaneRow<DT, NV> rw;
+        rw.issue(reinterpret_cast<const char*>(a.nP1) + (int64_t)m * rb, DT == 2 ? a.nP1s + (int64_t)m * groups : nullptr,
+                 nvec, lane);
+        float a0 = 0.f;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int v = u * kWave + lane;
+          const bool vin = v < nvec;
+          const int vc = vin ? v : 0;
+          float xv[E];
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const float4v t4 = xs[p * npad + vc];
+            xv[4 * p] = vin ? t4.x : 0.f; xv[4 * p + 1] = vin ? t4.y : 0.f;
+            xv[4 * p + 2] = vin ? t4.z : 0.f; xv[4 * p + 3] = vin ? t4.w : 0.f;
+          }
+          float wf[E];
+          widen<DT>(rw.w[u], DT == 2 ? rw.sc[u] : 1.f, wf);
+#pragma unroll
+          for (int e = 0; e < E; ++e) a0 = fmaf(wf[e], xv[e], a0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        float z = wave_sum(a0) + c1_at(m);
+        z = z > 0.f ? z : 0.f;
+        if (lane == 0) a.nh[m] = z;
+      }
+      return;
+    }
+  }
+
   // ---- output layer over the rows of positive hidden units
   {
     const int64_t prb = row_bytes(PDT, N);
@@ -532,7 +573,8 @@ constexpr int kTile = 64;
 
 template <int PDT, int DT, int NV, bool GATED, int BDT, int T, bool FC1>
 hipError_t pf_launch(const PredFc1Args& a, hipStream_t s) {
-  const unsigned blocks = (unsigned)((a.N + T - 1) / T);
+  unsigned blocks = (unsigned)((a.N + T - 1) / T);
+  if (FC1 && a.nh) blocks += (unsigned)((a.nH + 7) / 8);   // look-ahead rows, T / 8 = 8 waves per block
   size_t shm = 0;                     // x in E/4 planes of float4 when FC1 runs
   if constexpr (FC1) {
     const int nvec = (int)(row_bytes(DT, a.d) / 16);

@@ -431,10 +431,10 @@ def pi_kind(cfg):
 
 def lookahead_bench(cfg, specs, dls, steps, warmup, B=1):
     """Look-ahead prediction (the pages: activations can be predicted some layers ahead while the
-    model runs): layer L+1's predictor hidden layer is computed from layer L's input, on a second
-    stream, while layer L's output layer, decision, FC1, FC2 and sum run on the first; layer L+1's
-    remaining stages wait for it and take layer L+1's own input.  Layer 0 predicts from its own input.
-    Same layers, seeded inputs and one HIP graph per step as the measured run; returns tokens/s."""
+    model runs): layer L+1's predictor hidden layer is computed from layer L's input by
+    pi_ffn_layer_ahead, in the launch that runs layer L's output layer and FC1; layer L+1's
+    remaining stages take layer L+1's own input.  Layer 0 predicts from its own input.  Same
+    layers, seeded inputs and one HIP graph per step as the measured run; returns tokens/s."""
     import torch
     import synth
     import activation_sparse_amd as pi
@@ -465,24 +465,21 @@ def lookahead_bench(cfg, specs, dls, steps, warmup, B=1):
                                row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
     torch.cuda.synchronize()
     rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
-    ahead = torch.cuda.Stream()            # default priority
 
-    def stage(t, L, x, stages, st):
+    def stage(t, L, stages, ahead=False):
         cold = len(specs[L].T_c) > 0
-        pi.pi_ffn_layer_stages(dls[L].layer, B, x, 0.0, ycs[t, L] if cold else None, y, None, A_g, Ks[t, L:L + 1],
-                               A_c if cold else None, Kcs[t, L:L + 1] if cold else None, wss[L], stages,
-                               stream=st, _cstruct=dls[L].layer_c)
+        args = (B, xs[t, L], 0.0, ycs[t, L] if cold else None, y, None, A_g, Ks[t, L:L + 1], A_c if cold else None,
+                Kcs[t, L:L + 1] if cold else None, wss[L], stages)
+        if ahead:
+            pi.pi_ffn_layer_ahead(dls[L].layer, *args, dls[L + 1].layer, wss[L + 1], _cstruct=dls[L].layer_c,
+                                  _next_cstruct=dls[L + 1].layer_c)
+        else:
+            pi.pi_ffn_layer_stages(dls[L].layer, *args, _cstruct=dls[L].layer_c)
 
     def step_call(t):
-        main = torch.cuda.current_stream()
-        stage(t, 0, xs[t, 0], pi.PI_STAGE_HIDDEN, main)
+        stage(t, 0, pi.PI_STAGE_HIDDEN)
         for L in range(n_layers):
-            if L + 1 < n_layers:          # layer L's input is there: predict layer L + 1 beside layer L
-                ahead.wait_stream(main)
-                stage(t, L + 1, xs[t, L], pi.PI_STAGE_HIDDEN, ahead)
-            stage(t, L, xs[t, L], rest, main)
-            if L + 1 < n_layers:
-                main.wait_stream(ahead)
+            stage(t, L, rest, ahead=L + 1 < n_layers)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -251,6 +251,26 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* layer, int32_t B, const fl
                         int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, void* const* events,
                         uint32_t stages, int32_t* rows_read);
 
+/* Look-ahead prediction (a variant of the method; the pages note that
+ * activations can be predicted some layers ahead while the model runs):
+ * pi_ffn_layer_stages on `layer` (events and rows_read not taken), and the
+ * predictor hidden layer of `next` computed from this call's x, the input of
+ * `layer`, into the workspace ws_next.  A later call on `next` with its own
+ * input and without PI_STAGE_HIDDEN then predicts `next`'s neurons from
+ * `layer`'s input.  At batch 1, when next->P1 has the format of layer->W1,
+ * the hidden rows are computed by extra workgroups of the launch that runs
+ * `layer`'s output layer and FC1, on the x it stages; otherwise by the
+ * separate hidden-layer kernels after `layer`'s stages.
+ * next: d equal to layer->d; its P1, c1, H, N and n_g are used.  ws_next:
+ * pi_workspace_bytes(PI_OP_FFN_LAYER, B, d, next->H, next->N, next->n_g)
+ * bytes, not ws.
+ * Errors: as pi_ffn_layer_stages; PI_EINVAL for a NULL next, another d, a bad
+ * P1 / c1 of next, or ws_next == ws; PI_EWORKSPACE for a short ws_next. */
+int pi_ffn_layer_ahead(void* stream, const pi_layer* layer, int32_t B, const float* x, float tau,
+                       const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
+                       int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, uint32_t stages,
+                       const pi_layer* next, void* ws_next, size_t ws_next_bytes);
+
 /* The streaming-read reference that the kernels' bandwidths are read against:
  * reads `bytes` bytes of `buf` once, in 16-byte vectors, with `blocks`
  * workgroups of 256 threads (blocks <= 0: 8 per compute unit) each keeping

@@ -141,6 +141,22 @@ def test_ffn_layer_stages_rejects_bad_stage_sets_and_shapes():
                   pi.PI_STAGE_ALL, None, 64, None, 0) == pi.PI_EWORKSPACE
 
 
+def test_ffn_layer_ahead_rejects_bad_arguments():
+    L = _layer()
+    ws = 1 << 30
+
+    def call(next_layer=L, ws_next=FAKE + (1 << 24), nbytes=ws, layer=L):
+        return status(pi.pi_ffn_layer_ahead, layer, 1, FAKE, 0.0, None, FAKE, None, FAKE, FAKE, None, None, FAKE,
+                      pi.PI_STAGE_ALL, next_layer, ws_next, ws, nbytes, 0)
+
+    assert call(next_layer=_layer(d=512)) == pi.PI_EINVAL          # another d
+    assert call(next_layer=_layer(n_g=2048)) == pi.PI_EINVAL       # more GPU neurons than N
+    assert call(ws_next=FAKE) == pi.PI_EINVAL                      # the same workspace
+    assert call(ws_next=None) == pi.PI_EWORKSPACE
+    assert call(nbytes=64) == pi.PI_EWORKSPACE
+    assert call(layer=_layer(N=1020)) == pi.PI_EINVAL              # this layer's own checks still apply
+
+
 def test_table_prepare_validates_and_builds_bitmap_and_prefix():
     import numpy as np
     N = 200

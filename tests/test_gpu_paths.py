@@ -379,3 +379,49 @@ def test_graph_replays_match_the_eager_call(B):
         graph.replay()
         torch.cuda.synchronize()
         assert state() == eager, r
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_lookahead_entry_point(B):
+    """pi_ffn_layer_ahead: layer l's stages and, in the same call, layer l+1's predictor hidden
+    layer from layer l's input (at batch 1 inside the launch that runs layer l's output layer
+    and FC1; at batch 4 by the separate kernels).  Each layer's logits and lists against the
+    oracle's prediction from the earlier input, its output against the oracle's FFN on its own
+    input over the GPU's list."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    cfg = ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=17)
+    nl = 3
+    specs = [synth.layer_spec(cfg, l) for l in range(nl)]
+    dls = [ph.DeviceLayer(s) for s in specs]
+    bufs = [ph.DeviceBuffers(cfg, s.H, s.n_g, len(s.T_c), B) for s in specs]
+    xs = [synth.host_x(cfg.seed, l, 4, B, cfg.d) for l in range(nl)]
+    for b, x in zip(bufs, xs):
+        b.x.copy_(torch.from_numpy(x))
+    torch.cuda.synchronize()
+    rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
+    print(f"look-ahead entry point B={B}", flush=True)
+    b0 = bufs[0]
+    pi.pi_ffn_layer_stages(dls[0].layer, B, b0.x, 0.0, None, b0.y, b0.logits, b0.A_g, b0.K, b0.A_c, b0.K_c,
+                           b0.ws_layer, pi.PI_STAGE_HIDDEN)
+    for l in range(nl):
+        b = bufs[l]
+        if l + 1 < nl:
+            pi.pi_ffn_layer_ahead(dls[l].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c,
+                                  b.ws_layer, rest, dls[l + 1].layer, bufs[l + 1].ws_layer)
+        else:
+            pi.pi_ffn_layer_stages(dls[l].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c,
+                                   b.ws_layer, rest)
+    torch.cuda.synchronize()
+    for l in range(nl):
+        spec, b = specs[l], bufs[l]
+        logits_or, _ = ph.oracle_predict(spec, xs[max(l - 1, 0)])
+        assert np.max(np.abs(b.logits.cpu().numpy().astype(np.float64) - logits_or)) <= ph.LOGIT_ATOL, l
+        K, K_c = int(b.K.cpu()[0]), int(b.K_c.cpu()[0])
+        A_g, A_c = b.A_g.cpu().numpy()[:K], b.A_c.cpu().numpy()[:K_c]
+        A_g_or, A_c_or = orc.compact(logits_or, 0.0, spec.T_g, spec.T_c)
+        _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
+        _, out_c, asc_c = ph.list_check(A_c, A_c_or, spec.T_c, logits_or, 0.0)
+        assert K > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
+        y_or = ph.oracle_ffn_on_ids(spec, xs[l], spec.T_g[A_g])
+        assert ph.rel_err(b.y.cpu().numpy(), y_or) <= ph.RTOL, l
