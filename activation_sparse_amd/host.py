@@ -14,7 +14,8 @@ from typing import Optional
 from . import PiError, Matrix, Vector, _Mat, _Vec, _Layer, PI_OK, PI_RELU
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpi_host.so")
-EXPORTS = ("pi_cold_ffn", "pi_cold_ffn_ex", "pi_host_vector_path", "pi_hybrid_layer")
+EXPORTS = ("pi_cold_ffn", "pi_cold_ffn_ex", "pi_host_vector_path", "pi_hybrid_layer", "pi_hybrid_prime",
+           "pi_hybrid_layer_ahead")
 
 class _HostCold(C.Structure):
     _fields_ = [("n_c", C.c_int32), ("W1", _Mat), ("b1", _Vec), ("Wup", _Mat), ("W2", _Mat)]
@@ -25,6 +26,14 @@ class _HybridScratch(C.Structure):
                 ("y_c", C.c_void_p), ("ws_pred", C.c_void_p), ("ws_pred_bytes", C.c_size_t),
                 ("ws_ffn", C.c_void_p), ("ws_ffn_bytes", C.c_size_t), ("x_host", C.c_void_p),
                 ("cold_list_host", C.c_void_p), ("y_c_host", C.c_void_p), ("event", C.c_void_p)]
+
+
+class _HybridAheadScratch(C.Structure):
+    _fields_ = [("logits", C.c_void_p), ("ws_pred", C.c_void_p), ("ws_pred_bytes", C.c_size_t),
+                ("ws_ffn", C.c_void_p), ("ws_ffn_bytes", C.c_size_t), ("A_g", C.c_void_p * 2), ("K", C.c_void_p * 2),
+                ("cold_list", C.c_void_p * 2), ("cold_list_host", C.c_void_p * 2), ("list_event", C.c_void_p * 2),
+                ("y_c", C.c_void_p), ("x_host", C.c_void_p), ("y_c_host", C.c_void_p), ("x_event", C.c_void_p),
+                ("cur", C.c_int32)]
 
 
 _lib = None
@@ -46,6 +55,11 @@ def load():
         L.pi_hybrid_layer.argtypes = [P, C.POINTER(_Layer), P, P, C.POINTER(_HostCold), I, P, C.c_float, P,
                                       C.POINTER(_HybridScratch), I, C.POINTER(C.c_int32)]
         L.pi_hybrid_layer.restype = C.c_int
+        L.pi_hybrid_prime.argtypes = [P, C.POINTER(_Layer), P, P, I, I, P, C.c_float, C.POINTER(_HybridAheadScratch)]
+        L.pi_hybrid_prime.restype = C.c_int
+        L.pi_hybrid_layer_ahead.argtypes = [P, C.POINTER(_Layer), C.POINTER(_HostCold), C.POINTER(_Layer), P, P, I, I,
+                                            P, C.c_float, P, C.POINTER(_HybridAheadScratch), I, C.POINTER(C.c_int32)]
+        L.pi_hybrid_layer_ahead.restype = C.c_int
         _lib = L
     return _lib
 
@@ -98,4 +112,24 @@ def pi_hybrid_layer(stream: int, layer_c, T_g: int, T_c: Optional[int], cold_c, 
                                 B, x, float(tau), y, C.byref(scratch_c), threads, C.byref(kc))
     if st != PI_OK:
         raise PiError(f"pi_hybrid_layer: {_STATUS.get(st, st)}")
+    return kc.value
+
+
+def pi_hybrid_prime(stream: int, layer_c, T_g: int, T_c: Optional[int], n_c: int, B: int, x: int, tau: float,
+                    scratch_c) -> None:
+    """Predict `layer` from x into the scratch's current list set (see pi_host.h)."""
+    st = load().pi_hybrid_prime(stream, C.byref(layer_c), T_g, T_c, n_c, B, x, float(tau), C.byref(scratch_c))
+    if st != PI_OK:
+        raise PiError(f"pi_hybrid_prime: {_STATUS.get(st, st)}")
+
+
+def pi_hybrid_layer_ahead(stream: int, layer_c, cold_c, next_c, T_g_next: Optional[int], T_c_next: Optional[int],
+                          n_c_next: int, B: int, x: int, tau: float, y: int, scratch_c, threads: int = 0) -> int:
+    """One look-ahead hybrid layer (see pi_host.h); returns K_c."""
+    kc = C.c_int32(0)
+    st = load().pi_hybrid_layer_ahead(stream, C.byref(layer_c), C.byref(cold_c) if cold_c is not None else None,
+                                      C.byref(next_c) if next_c is not None else None, T_g_next, T_c_next, n_c_next,
+                                      B, x, float(tau), y, C.byref(scratch_c), threads, C.byref(kc))
+    if st != PI_OK:
+        raise PiError(f"pi_hybrid_layer_ahead: {_STATUS.get(st, st)}")
     return kc.value

@@ -70,3 +70,69 @@ class HybridLayer:
         of active cold neurons (0: no cold partial was merged)."""
         return host.pi_hybrid_layer(pi._stream(stream), self.dl.layer_c, self.T_g, self.T_c, self.cold, self.B,
                                     x.data_ptr(), tau, y.data_ptr(), self.scratch, self.threads)
+
+
+class HybridStack:
+    """The look-ahead hybrid over a stack of layers (pi_hybrid_prime / pi_hybrid_layer_ahead): each
+    layer's neurons are predicted from the previous layer's input while the CPU computes that
+    layer's cold neurons.  dls / hls: DeviceLayer-like and host objects per layer, as for
+    HybridLayer.  One scratch serves every layer (sized for the largest)."""
+
+    def __init__(self, dls, hls, B: int, threads: int = 0, device="cuda:0"):
+        import torch
+        self.dls, self.hls, self.B, self.threads = dls, hls, B, threads
+        specs = [dl.spec for dl in dls]
+        cfg = specs[0].cfg
+        self.d = cfg.d
+        N = max(s.cfg.N for s in specs)
+        H = max(s.H for s in specs)
+        n_g = max(s.n_g for s in specs)
+        self.n_cs = [len(s.T_c) for s in specs]
+        n_c = max(self.n_cs)
+        i32, f32 = torch.int32, torch.float32
+        self.logits = torch.empty((B, N), dtype=f32, device=device)
+        wsp = max(pi.pi_workspace_bytes(pi.PI_OP_PREDICT, B, self.d, H, N, 0), 256)
+        wsf = max(pi.pi_workspace_bytes(pi.PI_OP_SPARSE_FFN, B, self.d, 0, 0, n_g), 256)
+        self.ws_pred = torch.empty(wsp, dtype=torch.uint8, device=device)
+        self.ws_ffn = torch.empty(wsf, dtype=torch.uint8, device=device)
+        self.A_g = [torch.empty(max(n_g, 1), dtype=i32, device=device) for _ in range(2)]
+        self.K = [torch.zeros(1, dtype=i32, device=device) for _ in range(2)]
+        self.cold_list = [torch.zeros(4 + max(n_c, 1), dtype=i32, device=device) for _ in range(2)]
+        self.cold_list_h = [torch.zeros(4 + max(n_c, 1), dtype=i32, pin_memory=True) for _ in range(2)]
+        self.y_c = torch.empty((B, self.d), dtype=f32, device=device)
+        self.x_h = torch.empty((B, self.d), dtype=f32, pin_memory=True)
+        self.y_c_h = torch.empty((B, self.d), dtype=f32, pin_memory=True)
+        self.events = [torch.cuda.Event() for _ in range(3)]
+        for e in self.events:
+            e.record()                 # creates the underlying hipEvent_t
+        P2 = host.C.c_void_p * 2
+        self.scratch = host._HybridAheadScratch(
+            self.logits.data_ptr(), self.ws_pred.data_ptr(), wsp, self.ws_ffn.data_ptr(), wsf,
+            P2(*(t.data_ptr() for t in self.A_g)), P2(*(t.data_ptr() for t in self.K)),
+            P2(*(t.data_ptr() for t in self.cold_list)), P2(*(t.data_ptr() for t in self.cold_list_h)),
+            P2(self.events[0].cuda_event, self.events[1].cuda_event), self.y_c.data_ptr(), self.x_h.data_ptr(),
+            self.y_c_h.data_ptr(), self.events[2].cuda_event, 0)
+        self.colds = [host._HostCold(len(dl.spec.T_c), host._hmat(hl.W1), host._hvec(hl.b1), host._hmat(hl.Wup),
+                                     host._hmat(hl.W2)) if len(dl.spec.T_c) else None for dl, hl in zip(dls, hls)]
+
+    def _tables(self, L):
+        dl = self.dls[L]
+        return dl.T_g.data_ptr(), (dl.T_c.data_ptr() if self.n_cs[L] else None), self.n_cs[L]
+
+    def __call__(self, xs, ys, tau: float = 0.0, stream=None):
+        """ys[L] (device [B x d]) = layer L's output for xs[L]; layer L's neurons predicted from
+        xs[L - 1] (layer 0 from xs[0]).  Returns each layer's K_c."""
+        st = pi._stream(stream)
+        T_g, T_c, n_c = self._tables(0)
+        host.pi_hybrid_prime(st, self.dls[0].layer_c, T_g, T_c, n_c, self.B, xs[0].data_ptr(), tau, self.scratch)
+        kcs = []
+        n = len(self.dls)
+        for L in range(n):
+            if L + 1 < n:
+                T_g, T_c, n_c = self._tables(L + 1)
+                nxt = self.dls[L + 1].layer_c
+            else:
+                T_g, T_c, n_c, nxt = None, None, 0, None
+            kcs.append(host.pi_hybrid_layer_ahead(st, self.dls[L].layer_c, self.colds[L], nxt, T_g, T_c, n_c, self.B,
+                                                  xs[L].data_ptr(), tau, ys[L].data_ptr(), self.scratch, self.threads))
+        return kcs

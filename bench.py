@@ -655,6 +655,19 @@ def hybrid_bench(cfg, specs, dls, steps, warmup):
             kcs.append(hys[l](xs[t, l], y))
     torch.cuda.synchronize()
     el = time.perf_counter() - t1
+    # look-ahead: each layer's neurons predicted from the previous layer's input while the CPU works
+    from activation_sparse_amd.hybrid import HybridStack
+    stk = HybridStack(dls, hls, 1)
+    ys = [torch.empty((1, d), dtype=torch.float32, device=dev) for _ in range(L)]
+    for t in range(warmup):
+        stk([xs[t, l] for l in range(L)], ys)
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    for t in range(warmup, S):
+        stk([xs[t, l] for l in range(L)], ys)
+    torch.cuda.synchronize()
+    el_ahead = time.perf_counter() - t3
+    del stk
     # the CPU side alone: each layer's last cold list and input again, through pi_cold_ffn
     y_h = np.empty((1, d), np.float32)
     t2 = time.perf_counter()
@@ -669,9 +682,11 @@ def hybrid_bench(cfg, specs, dls, steps, warmup):
            "cpu_threads": int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count(),
            "cpu_vector_path": "avx2+fma+f16c" if host.vector_path() else "scalar",
            "cpu_cold_ffn_us_per_layer": round(host_s * 1e6 / (steps * L), 1),
-           "mean_K_c": float(np.mean(kcs)), "host_weight_setup_s": round(gen_s, 1)}
+           "mean_K_c": float(np.mean(kcs)), "host_weight_setup_s": round(gen_s, 1),
+           "lookahead_tokens_per_s": round(steps / el_ahead, 2), "lookahead_ms_per_step": round(el_ahead * 1e3 / steps, 3)}
     log(f"hybrid: {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s, cold FFN on the CPU "
-        f"{out['cpu_cold_ffn_us_per_layer']} us per layer (timed alone)")
+        f"{out['cpu_cold_ffn_us_per_layer']} us per layer (timed alone); with look-ahead prediction "
+        f"{out['lookahead_ms_per_step']} ms/step, {out['lookahead_tokens_per_s']} tokens/s")
     del hys, hls
     return out
 

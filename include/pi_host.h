@@ -116,6 +116,57 @@ int pi_hybrid_layer(void* stream, const pi_layer* layer, const int32_t* T_g, con
                     const pi_host_cold* cold, int32_t B, const float* x, float tau, float* y,
                     const pi_hybrid_scratch* scratch, int32_t threads, int32_t* K_c_out);
 
+/* Buffers of the look-ahead hybrid executor, owned by the caller.  Two list
+ * sets: the one `cur` names holds the lists of the layer the next
+ * pi_hybrid_layer_ahead call runs; that call predicts the layer after it into
+ * the other set and flips `cur`.  Sizes are the largest over the layers the
+ * scratch serves. */
+typedef struct pi_hybrid_ahead_scratch {
+  float* logits;               /* device [B x N] */
+  void* ws_pred;               /* device, pi_workspace_bytes(PI_OP_PREDICT, ...) bytes */
+  size_t ws_pred_bytes;
+  void* ws_ffn;                /* device, pi_workspace_bytes(PI_OP_SPARSE_FFN, ...) bytes */
+  size_t ws_ffn_bytes;
+  int32_t* A_g[2];             /* device [n_g] each */
+  int32_t* K[2];               /* device [1] each */
+  int32_t* cold_list[2];       /* device [4 + n_c] each, as in pi_hybrid_scratch */
+  int32_t* cold_list_host[2];  /* pinned host [4 + n_c] each */
+  void* list_event[2];         /* hipEvent_t each: that set's cold list is on the host */
+  float* y_c;                  /* device [B x d] */
+  float* x_host;               /* pinned host [B x d] */
+  float* y_c_host;             /* pinned host [B x d] */
+  void* x_event;               /* hipEvent_t: x is on the host */
+  int32_t cur;                 /* 0 or 1, updated by the calls */
+} pi_hybrid_ahead_scratch;
+
+/* Look-ahead prediction in the hybrid layer (a variant of the method; the
+ * pages note that activations can be predicted some layers ahead while the
+ * model runs).  pi_hybrid_prime predicts `layer`'s neurons from x (pi_predict,
+ * pi_compact with the raw device tables T_g / T_c of n_c entries) into list
+ * set scratch->cur and copies its CPU list to the host (no wait).
+ * pi_hybrid_layer_ahead runs `layer` on its input x with the lists in set cur,
+ * which an earlier prime or look-ahead call produced:
+ *  1. copies x to the host and enqueues pi_sparse_ffn over the GPU's list;
+ *  2. when `next` is given, enqueues next's prediction from this x into the
+ *     other set (pi_predict, pi_compact with T_g_next / T_c_next of
+ *     n_c_next entries, the copy of its CPU list), so that it runs on the GPU
+ *     while this thread computes the cold neurons;
+ *  3. waits for x and set cur's CPU list, runs pi_cold_ffn, and when K_c > 0
+ *     enqueues the copy of y_c and pi_merge (else the b2 merge only);
+ *  4. flips scratch->cur.
+ * The GPU's predictor work thus leaves the path between two layers: the
+ * thread waits only for the copy of x.  cold: the CPU rows of `layer` (NULL:
+ * none).  Returns with the merge enqueued; *K_c_out (optional) gets K_c.
+ * Errors: PI_EINVAL for a NULL required pointer or buffer, B outside
+ * 1..PI_MAX_BATCH, or cur outside 0..1; those of the calls it makes; PI_EHIP
+ * when a copy, an event record or a wait fails. */
+int pi_hybrid_prime(void* stream, const pi_layer* layer, const int32_t* T_g, const int32_t* T_c, int32_t n_c,
+                    int32_t B, const float* x, float tau, pi_hybrid_ahead_scratch* scratch);
+int pi_hybrid_layer_ahead(void* stream, const pi_layer* layer, const pi_host_cold* cold, const pi_layer* next,
+                          const int32_t* T_g_next, const int32_t* T_c_next, int32_t n_c_next, int32_t B,
+                          const float* x, float tau, float* y, pi_hybrid_ahead_scratch* scratch, int32_t threads,
+                          int32_t* K_c_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -425,3 +425,39 @@ def test_lookahead_entry_point(B):
         assert K > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
         y_or = ph.oracle_ffn_on_ids(spec, xs[l], spec.T_g[A_g])
         assert ph.rel_err(b.y.cpu().numpy(), y_or) <= ph.RTOL, l
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_hybrid_lookahead_stack(B):
+    """The look-ahead hybrid over two layers: layer 0 predicted from its own input (prime), layer 1
+    from layer 0's input while the CPU computes layer 0's cold neurons.  Each layer's lists (both
+    list sets survive a two-layer call) against the oracle's prediction from that input, and each
+    output against the oracle's FFN on the layer's own input over the GPU's and the CPU's lists."""
+    torch = _dev()
+    from activation_sparse_amd.hybrid import HybridStack
+    from synth.device import HostColdLayer
+    cfg = ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=17)
+    specs = [synth.layer_spec(cfg, l) for l in range(2)]
+    dls = [ph.DeviceLayer(s) for s in specs]
+    hy = HybridStack(dls, [HostColdLayer(s) for s in specs], B)
+    xs_h = [synth.host_x(cfg.seed, l, 8, B, cfg.d) for l in range(2)]
+    xs = [torch.from_numpy(x).cuda() for x in xs_h]
+    ys = [torch.empty((B, cfg.d), dtype=torch.float32, device="cuda") for _ in range(2)]
+    print(f"hybrid look-ahead B={B}", flush=True)
+    for rep in range(2):                           # a second call reuses the scratch
+        kcs = hy(xs, ys)
+        torch.cuda.synchronize()
+    for l in range(2):
+        spec = specs[l]
+        K = int(hy.K[l].cpu()[0])
+        A_g = hy.A_g[l].cpu().numpy()[:K]
+        kc = int(hy.cold_list_h[l][0])
+        A_c = hy.cold_list_h[l].numpy()[4:4 + kc].copy()
+        assert kc == kcs[l]
+        logits_or, _ = ph.oracle_predict(spec, xs_h[max(l - 1, 0)])
+        A_g_or, A_c_or = orc.compact(logits_or, 0.0, spec.T_g, spec.T_c)
+        _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
+        _, out_c, asc_c = ph.list_check(A_c, A_c_or, spec.T_c, logits_or, 0.0)
+        assert K > 0 and kc > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
+        y_or = ph.oracle_ffn_on_ids(spec, xs_h[l], spec.T_g[A_g]) + ph.oracle_ffn_on_ids(spec, xs_h[l], spec.T_c[A_c])
+        assert ph.rel_err(ys[l].cpu().numpy(), y_or) <= ph.RTOL, l
