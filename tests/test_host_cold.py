@@ -171,3 +171,37 @@ def test_both_fc2_orders_match_the_oracle(K):
         assert y.tobytes() == ys[0].tobytes()
     ref = orc.sparse_ffn(x, W1, on, W2, A_c, kind=orc.RELU)
     assert ph.rel_err(ys[0].astype(np.float64), ref) <= 1e-5
+
+
+def test_lookahead_hybrid_rejects_bad_arguments():
+    """pi_hybrid_prime and pi_hybrid_layer_ahead check their arguments before any HIP call."""
+    import ctypes as C
+    FAKE = 1 << 20
+    lay = pi.Layer(256, 1024, 64, 512, pi.PI_RELU, True, pi.Matrix(FAKE, pi.PI_F16), None,
+                   pi.Matrix(FAKE, pi.PI_F16), None, FAKE, pi.Matrix(FAKE, pi.PI_F16), None, None,
+                   pi.Matrix(FAKE, pi.PI_F16), None)._c()
+    P2 = C.c_void_p * 2
+    full = host._HybridAheadScratch(FAKE, FAKE, 1 << 20, FAKE, 1 << 20, P2(FAKE, FAKE), P2(FAKE, FAKE),
+                                    P2(FAKE, FAKE), P2(FAKE, FAKE), P2(FAKE, FAKE), FAKE, FAKE, FAKE, FAKE, 0)
+    L = host.load()
+
+    def prime(s=full, n_c=10, T_c=FAKE, B=1):
+        return L.pi_hybrid_prime(0, C.byref(lay), FAKE, T_c, n_c, B, FAKE, 0.0, C.byref(s))
+
+    def ahead(s=full, nxt=lay, T_g_next=FAKE, B=1, y=FAKE):
+        return L.pi_hybrid_layer_ahead(0, C.byref(lay), None, C.byref(nxt) if nxt is not None else None, T_g_next,
+                                       FAKE, 10, B, FAKE, 0.0, y, C.byref(s), 0, None)
+
+    assert prime(n_c=-1) == pi.PI_EINVAL and prime(T_c=None) == pi.PI_EINVAL and prime(B=0) == pi.PI_EINVAL
+    assert ahead(T_g_next=None) == pi.PI_EINVAL and ahead(y=None) == pi.PI_EINVAL
+    assert ahead(B=pi.PI_MAX_BATCH + 1) == pi.PI_EINVAL
+    bad = host._HybridAheadScratch.from_buffer_copy(full)
+    bad.cur = 2
+    assert prime(s=bad) == pi.PI_EINVAL and ahead(s=bad) == pi.PI_EINVAL
+    for field in ("logits", "y_c", "x_host", "y_c_host", "x_event"):
+        s = host._HybridAheadScratch.from_buffer_copy(full)
+        setattr(s, field, None)
+        assert prime(s=s) == pi.PI_EINVAL and ahead(s=s) == pi.PI_EINVAL, field
+    s = host._HybridAheadScratch.from_buffer_copy(full)
+    s.list_event[1] = None
+    assert ahead(s=s) == pi.PI_EINVAL
