@@ -461,3 +461,44 @@ def test_hybrid_lookahead_stack(B):
         assert K > 0 and kc > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
         y_or = ph.oracle_ffn_on_ids(spec, xs_h[l], spec.T_g[A_g]) + ph.oracle_ffn_on_ids(spec, xs_h[l], spec.T_c[A_c])
         assert ph.rel_err(ys[l].cpu().numpy(), y_or) <= ph.RTOL, l
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_lookahead_gated_layers_of_different_hidden_sizes(B):
+    """pi_ffn_layer_ahead across gated layers whose predictors differ in size (H = 128, then
+    192): the next layer's hidden rows, computed in this layer's launch at batch 1 (separately at
+    batch 2), give lists and outputs that match the oracle's prediction from this layer's input."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    cfg = synth.Config("gated-h", "reduced 512/1536 gated", 2, 512, 1536, synth.F16, synth.F16, synth.F16, True,
+                       (0.08, 0.25), 1.1, (128, 256), 0.4, (1,), 4, 39)
+    specs = [synth.layer_spec(cfg, l) for l in range(2)]
+    assert [s.H for s in specs] == [128, 192]
+    dls = [ph.DeviceLayer(s) for s in specs]
+    bufs = [ph.DeviceBuffers(cfg, s.H, s.n_g, len(s.T_c), B) for s in specs]
+    xs = [synth.host_x(cfg.seed, l, 2, B, cfg.d) for l in range(2)]
+    for b, x in zip(bufs, xs):
+        b.x.copy_(torch.from_numpy(x))
+    torch.cuda.synchronize()
+    rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
+    print(f"look-ahead gated B={B}", flush=True)
+    b0, b1 = bufs
+    pi.pi_ffn_layer_stages(dls[0].layer, B, b0.x, 0.0, None, b0.y, b0.logits, b0.A_g, b0.K, b0.A_c, b0.K_c,
+                           b0.ws_layer, pi.PI_STAGE_HIDDEN)
+    pi.pi_ffn_layer_ahead(dls[0].layer, B, b0.x, 0.0, None, b0.y, b0.logits, b0.A_g, b0.K, b0.A_c, b0.K_c,
+                          b0.ws_layer, rest, dls[1].layer, b1.ws_layer)
+    pi.pi_ffn_layer_stages(dls[1].layer, B, b1.x, 0.0, None, b1.y, b1.logits, b1.A_g, b1.K, b1.A_c, b1.K_c,
+                           b1.ws_layer, rest)
+    torch.cuda.synchronize()
+    for l in range(2):
+        spec, b = specs[l], bufs[l]
+        logits_or, _ = ph.oracle_predict(spec, xs[0])
+        assert np.max(np.abs(b.logits.cpu().numpy().astype(np.float64) - logits_or)) <= ph.LOGIT_ATOL, l
+        K, K_c = int(b.K.cpu()[0]), int(b.K_c.cpu()[0])
+        A_g, A_c = b.A_g.cpu().numpy()[:K], b.A_c.cpu().numpy()[:K_c]
+        A_g_or, A_c_or = orc.compact(logits_or, 0.0, spec.T_g, spec.T_c)
+        _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
+        _, out_c, asc_c = ph.list_check(A_c, A_c_or, spec.T_c, logits_or, 0.0)
+        assert K > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
+        y_or = ph.oracle_ffn_on_ids(spec, xs[l], spec.T_g[A_g])
+        assert ph.rel_err(b.y.cpu().numpy(), y_or) <= ph.RTOL, l
