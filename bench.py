@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--hybrid-steps", type=int, default=4,
                     help="after the batch-1 measurement, time the pages' GPU-CPU hybrid layer (cold neurons on "
                          "the host CPU) over this many steps; 0 = skip")
+    ap.add_argument("--no-placement", dest="placement", action="store_false",
+                    help="skip the host-side placement-solver report")
     ap.add_argument("--i4pred-steps", type=int, default=16,
                     help="after the batch-1 measurement, time the stack with int4-g128 predictor weights over "
                          "this many steps; 0 = skip")
@@ -614,6 +616,34 @@ def i4pred_bench(cfg, specs, dls, steps, warmup):
     return out
 
 
+def placement_report(keys):
+    """The offline placement solver against the fixed per-layer top-40% rule, on the host: each
+    config's layers profiled (seeded), the solver given the same GPU budget (40% of all neurons,
+    every neuron one unit, no per-layer minimum), and the expected share of all activations the GPU
+    tables hold under the true probabilities."""
+    import math
+    import synth
+    from activation_sparse_amd.placement import solve_placement, gpu_impact_share
+    out = {}
+    for key in keys:
+        cfg = synth.CONFIGS[key]
+        specs = [synth.layer_spec(cfg, l) for l in range(cfg.n_layers)]
+        counts = [synth.profile_counts(cfg, l, sp.p) for l, sp in enumerate(specs)]
+        k = int(math.floor(0.4 * cfg.N))
+        fixed = [np.sort(np.lexsort((np.arange(cfg.N), -c))[:k]).astype(np.int32) for c in counts]
+        t0 = time.perf_counter()
+        sol = solve_placement(counts, [1] * len(counts), k * len(counts))
+        solve_s = time.perf_counter() - t0
+        p = [sp.p for sp in specs]
+        shares = [len(t) / cfg.N for t in sol]
+        out[key] = {"gpu_activation_share_fixed_top40": round(gpu_impact_share(p, fixed), 4),
+                    "gpu_activation_share_solver": round(gpu_impact_share(p, sol), 4),
+                    "solver_layer_share_min": round(min(shares), 4), "solver_layer_share_max": round(max(shares), 4),
+                    "solve_s": round(solve_s, 3), "layers": cfg.n_layers}
+    log(f"placement: {out}")
+    return out
+
+
 def hybrid_bench(cfg, specs, dls, steps, warmup):
     """The pages' hybrid layer at batch 1: the CPU-table neurons live in host memory and run on the
     host CPU (libpi_host) while the GPU runs the predictor, the compaction and its own neurons; the
@@ -931,6 +961,11 @@ def main():
         log("look-ahead prediction ...")
         lookahead = lookahead_bench(cfg, specs, dls, args.lookahead_steps, 3)
 
+    placement = None
+    if args.placement and B == 1:
+        log("placement solver (host) ...")
+        placement = placement_report([cfg.key] + (["llama-13b-gated"] if cfg.key != "llama-13b-gated" else []))
+
     sweep = None
     batches = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []
     if batches and B == 1:
@@ -972,7 +1007,8 @@ def main():
                    "event_ms": round(gpu_ms, 3),
                    "stream_read_gbps": stream_read,
                    "dominant_frac_of_stream_read": round(achieved[iso] / dom_ref, 4),
-                   "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead, "int4_predictor": i4pred},
+                   "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead, "int4_predictor": i4pred,
+                   "placement": placement},
     }
     print(json.dumps(out), flush=True)
 

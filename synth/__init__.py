@@ -271,13 +271,20 @@ class LayerSpec:
                 TAG_WUP: 1 / math.sqrt(self.d), TAG_W2: 1 / math.sqrt(self.N), TAG_X: 1.0}
 
 
+def profile_counts(cfg: Config, layer: int, p: np.ndarray) -> np.ndarray:
+    """Simulated profiling: each neuron's activation count over cfg.prof_tokens seeded tokens,
+    Binomial(prof_tokens, p_i) draws."""
+    counts = np.empty(cfg.N, np.int32)
+    host_lib().sx_profile_counts(cfg.seed, layer, cfg.N, np.ascontiguousarray(p, dtype=np.float64).ctypes.data,
+                                 cfg.prof_tokens, counts.ctypes.data)
+    return counts
+
+
 def _table(cfg: Config, layer: int, p: np.ndarray):
     N = cfg.N
     if cfg.gpu_frac >= 1.0:
         return np.arange(N, dtype=np.int32), np.zeros(0, np.int32), None
-    counts = np.empty(N, np.int32)
-    host_lib().sx_profile_counts(cfg.seed, layer, N, np.ascontiguousarray(p).ctypes.data, cfg.prof_tokens,
-                                 counts.ctypes.data)
+    counts = profile_counts(cfg, layer, p)
     n_g = int(math.floor(cfg.gpu_frac * N))
     order = np.lexsort((np.arange(N), -counts))      # count descending, then id ascending
     T_g = np.sort(order[:n_g]).astype(np.int32)
