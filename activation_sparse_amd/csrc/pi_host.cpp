@@ -50,6 +50,7 @@ inline float half_to_float(uint16_t h) {
 }
 
 constexpr int64_t kFc1PrefetchBytes = 2048;   // FC1: leading bytes of the next row requested early
+constexpr int64_t kRowPrefetchBytes = 2048;   // distance of the software prefetch inside a row
 constexpr int64_t kFc2ChunkMinRows = 128;   // FC2: fewer contributing rows take column ranges
 constexpr int64_t kFc2ChunkRows = 16;   // FC2: fewest rows per chunk
 constexpr int64_t kFc2MaxChunks = 64;   // FC2: most chunks (bounds the partials at 64 x B x d floats)
@@ -153,7 +154,11 @@ PI_AVX2 void dots_avx2(const Rows& w, int64_t r, const float* x, int B, int64_t 
     __m256 acc[4][4];
     for (int i = 0; i < 4; ++i)
       for (int q = 0; q < 4; ++q) acc[i][q] = _mm256_setzero_ps();
+    const char* rowp = w.row(r);
     for (int64_t k0 = 0; k0 < d; k0 += 32) {
+      // the row's lines kRowPrefetchBytes ahead (the hardware prefetchers stop at page ends)
+      const int64_t po = k0 * w.rb / d + kRowPrefetchBytes;
+      if (po < w.rb) _mm_prefetch(rowp + po, _MM_HINT_T0);
       const int nq = (d - k0) / 8 < 4 ? (int)((d - k0) / 8) : 4;
       for (int q = 0; q < nq; ++q) {
         const __m256 wv = load8_avx2(w, r, k0 + 8 * q);
@@ -166,7 +171,13 @@ PI_AVX2 void dots_avx2(const Rows& w, int64_t r, const float* x, int B, int64_t 
 }
 
 PI_AVX2 void axpy_avx2(const Rows& w, int64_t r, const float* a, int B, int64_t d, int64_t c0, int64_t c1, float* y) {
+  const char* rowp = w.row(r);
+  const int64_t end = c1 * w.rb / d;
   for (int64_t c = c0; c < c1; c += 8) {
+    if ((c & 31) == 0) {             // one line per 32 columns of fp16 (two of fp32)
+      const int64_t po = c * w.rb / d + kRowPrefetchBytes;
+      if (po < end) _mm_prefetch(rowp + po, _MM_HINT_T0);
+    }
     const __m256 wv = load8_avx2(w, r, c);
     for (int b = 0; b < B; ++b) {
       if (a[b] == 0.f) continue;
