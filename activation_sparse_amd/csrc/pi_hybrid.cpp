@@ -136,3 +136,21 @@ extern "C" int pi_hybrid_layer_ahead(void* stream, const pi_layer* L, const pi_h
   }
   return L->b2.data ? pi_merge(stream, B, d, y, nullptr, nullptr, L->b2) : PI_OK;
 }
+
+extern "C" int pi_hybrid_stack_ahead(void* stream, int32_t n_layers, const pi_layer* layers,
+                                     const pi_host_cold* const* colds, const int32_t* const* T_g,
+                                     const int32_t* const* T_c, const int32_t* n_c, int32_t B, const float* const* xs,
+                                     float tau, float* const* ys, pi_hybrid_ahead_scratch* s, int32_t threads,
+                                     int32_t* K_c_out) {
+  if (n_layers < 1 || !layers || !colds || !T_g || !T_c || !n_c || !xs || !ys) return PI_EINVAL;
+  int r = pi_hybrid_prime(stream, &layers[0], T_g[0], T_c[0], n_c[0], B, xs[0], tau, s);
+  if (r != PI_OK) return r;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    const bool more = l + 1 < n_layers;
+    r = pi_hybrid_layer_ahead(stream, &layers[l], colds[l], more ? &layers[l + 1] : nullptr, more ? T_g[l + 1] : nullptr,
+                              more ? T_c[l + 1] : nullptr, more ? n_c[l + 1] : 0, B, xs[l], tau, ys[l], s, threads,
+                              K_c_out ? K_c_out + l : nullptr);
+    if (r != PI_OK) return r;
+  }
+  return PI_OK;
+}

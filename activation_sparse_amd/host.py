@@ -15,7 +15,7 @@ from . import PiError, Matrix, Vector, _Mat, _Vec, _Layer, PI_OK, PI_RELU
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpi_host.so")
 EXPORTS = ("pi_cold_ffn", "pi_cold_ffn_ex", "pi_host_vector_path", "pi_hybrid_layer", "pi_hybrid_prime",
-           "pi_hybrid_layer_ahead")
+           "pi_hybrid_layer_ahead", "pi_hybrid_stack_ahead")
 
 class _HostCold(C.Structure):
     _fields_ = [("n_c", C.c_int32), ("W1", _Mat), ("b1", _Vec), ("Wup", _Mat), ("W2", _Mat)]
@@ -60,6 +60,9 @@ def load():
         L.pi_hybrid_layer_ahead.argtypes = [P, C.POINTER(_Layer), C.POINTER(_HostCold), C.POINTER(_Layer), P, P, I, I,
                                             P, C.c_float, P, C.POINTER(_HybridAheadScratch), I, C.POINTER(C.c_int32)]
         L.pi_hybrid_layer_ahead.restype = C.c_int
+        L.pi_hybrid_stack_ahead.argtypes = [P, I, P, P, P, P, P, I, P, C.c_float, P, C.POINTER(_HybridAheadScratch), I,
+                                            P]
+        L.pi_hybrid_stack_ahead.restype = C.c_int
         _lib = L
     return _lib
 
@@ -133,3 +136,16 @@ def pi_hybrid_layer_ahead(stream: int, layer_c, cold_c, next_c, T_g_next: Option
     if st != PI_OK:
         raise PiError(f"pi_hybrid_layer_ahead: {_STATUS.get(st, st)}")
     return kc.value
+
+
+def pi_hybrid_stack_ahead(stream: int, layers_arr, colds_arr, T_g_arr, T_c_arr, n_c_arr, n_layers: int, B: int,
+                          xs_arr, tau: float, ys_arr, scratch_c, threads: int = 0, K_c_out=None) -> None:
+    """A stack of look-ahead hybrid layers in one native call (see pi_host.h); the arrays are
+    prebuilt ctypes arrays (pi_layer structs, pointers), K_c_out an int32 array or None."""
+    st = load().pi_hybrid_stack_ahead(stream, n_layers, C.cast(layers_arr, C.c_void_p), C.cast(colds_arr, C.c_void_p),
+                                      C.cast(T_g_arr, C.c_void_p), C.cast(T_c_arr, C.c_void_p),
+                                      C.cast(n_c_arr, C.c_void_p), B, C.cast(xs_arr, C.c_void_p), float(tau),
+                                      C.cast(ys_arr, C.c_void_p), C.byref(scratch_c), threads,
+                                      _hptr(K_c_out) if K_c_out is not None else None)
+    if st != PI_OK:
+        raise PiError(f"pi_hybrid_stack_ahead: {_STATUS.get(st, st)}")

@@ -115,6 +115,27 @@ class HybridStack:
         self.colds = [host._HostCold(len(dl.spec.T_c), host._hmat(hl.W1), host._hvec(hl.b1), host._hmat(hl.Wup),
                                      host._hmat(hl.W2)) if len(dl.spec.T_c) else None for dl, hl in zip(dls, hls)]
 
+    def native(self, xs, ys, tau: float = 0.0, stream=None):
+        """The same stack in one native call (pi_hybrid_stack_ahead): no per-layer Python call.
+        Returns each layer's K_c."""
+        import numpy as np
+        C = host.C
+        n = len(self.dls)
+        if getattr(self, "_arrs", None) is None or self._arrs[0] != n:
+            layers = (pi._Layer * n)(*[dl.layer_c for dl in self.dls])
+            colds = (C.c_void_p * n)(*[C.addressof(c) if c is not None else None for c in self.colds])
+            tg = (C.c_void_p * n)(*[dl.T_g.data_ptr() for dl in self.dls])
+            tc = (C.c_void_p * n)(*[dl.T_c.data_ptr() if self.n_cs[L] else None for L, dl in enumerate(self.dls)])
+            nc = (C.c_int32 * n)(*self.n_cs)
+            self._arrs = (n, layers, colds, tg, tc, nc)
+        _, layers, colds, tg, tc, nc = self._arrs
+        xa = (C.c_void_p * n)(*[x.data_ptr() for x in xs])
+        ya = (C.c_void_p * n)(*[y.data_ptr() for y in ys])
+        kc = np.zeros(n, np.int32)
+        host.pi_hybrid_stack_ahead(pi._stream(stream), layers, colds, tg, tc, nc, n, self.B, xa, tau, ya, self.scratch,
+                                   self.threads, kc)
+        return kc.tolist()
+
     def _tables(self, L):
         dl = self.dls[L]
         return dl.T_g.data_ptr(), (dl.T_c.data_ptr() if self.n_cs[L] else None), self.n_cs[L]

@@ -697,6 +697,12 @@ def hybrid_bench(cfg, specs, dls, steps, warmup):
         stk([xs[t, l] for l in range(L)], ys)
     torch.cuda.synchronize()
     el_ahead = time.perf_counter() - t3
+    # the same in one native call per step (no per-layer Python call)
+    t4 = time.perf_counter()
+    for t in range(warmup, S):
+        stk.native([xs[t, l] for l in range(L)], ys)
+    torch.cuda.synchronize()
+    el_native = time.perf_counter() - t4
     del stk
     # the CPU side alone: each layer's last cold list and input again, through pi_cold_ffn
     y_h = np.empty((1, d), np.float32)
@@ -713,10 +719,13 @@ def hybrid_bench(cfg, specs, dls, steps, warmup):
            "cpu_vector_path": "avx2+fma+f16c" if host.vector_path() else "scalar",
            "cpu_cold_ffn_us_per_layer": round(host_s * 1e6 / (steps * L), 1),
            "mean_K_c": float(np.mean(kcs)), "host_weight_setup_s": round(gen_s, 1),
-           "lookahead_tokens_per_s": round(steps / el_ahead, 2), "lookahead_ms_per_step": round(el_ahead * 1e3 / steps, 3)}
+           "lookahead_tokens_per_s": round(steps / el_ahead, 2), "lookahead_ms_per_step": round(el_ahead * 1e3 / steps, 3),
+           "lookahead_native_tokens_per_s": round(steps / el_native, 2),
+           "lookahead_native_ms_per_step": round(el_native * 1e3 / steps, 3)}
     log(f"hybrid: {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s, cold FFN on the CPU "
         f"{out['cpu_cold_ffn_us_per_layer']} us per layer (timed alone); with look-ahead prediction "
-        f"{out['lookahead_ms_per_step']} ms/step, {out['lookahead_tokens_per_s']} tokens/s")
+        f"{out['lookahead_ms_per_step']} ms/step, {out['lookahead_tokens_per_s']} tokens/s; in one native call per "
+        f"step {out['lookahead_native_ms_per_step']} ms/step, {out['lookahead_native_tokens_per_s']} tokens/s")
     del hys, hls
     return out
 

@@ -168,6 +168,19 @@ int pi_hybrid_layer_ahead(void* stream, const pi_layer* layer, const pi_host_col
                           const float* x, float tau, float* y, pi_hybrid_ahead_scratch* scratch, int32_t threads,
                           int32_t* K_c_out);
 
+/* A stack of n_layers look-ahead hybrid layers in one call: pi_hybrid_prime on
+ * layer 0 and xs[0], then pi_hybrid_layer_ahead on each layer l with its input
+ * xs[l] and output ys[l] (device [B x d] each), next = layer l + 1.  The
+ * executor loop of one decode step over the FFN layers, for callers whose
+ * layers' inputs are ready (layers[l], colds[l], T_g[l], T_c[l], n_c[l] per
+ * layer; colds[l] NULL for a layer without CPU rows).  K_c_out (optional,
+ * n_layers entries) gets each layer's K_c.
+ * Errors: PI_EINVAL for n_layers < 1 or a NULL array; those of the calls. */
+int pi_hybrid_stack_ahead(void* stream, int32_t n_layers, const pi_layer* layers, const pi_host_cold* const* colds,
+                          const int32_t* const* T_g, const int32_t* const* T_c, const int32_t* n_c, int32_t B,
+                          const float* const* xs, float tau, float* const* ys, pi_hybrid_ahead_scratch* scratch,
+                          int32_t threads, int32_t* K_c_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -461,6 +461,13 @@ def test_hybrid_lookahead_stack(B):
         assert K > 0 and kc > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
         y_or = ph.oracle_ffn_on_ids(spec, xs_h[l], spec.T_g[A_g]) + ph.oracle_ffn_on_ids(spec, xs_h[l], spec.T_c[A_c])
         assert ph.rel_err(ys[l].cpu().numpy(), y_or) <= ph.RTOL, l
+    # the same stack in one native call (pi_hybrid_stack_ahead): the same bits and counts
+    ys2 = [torch.full((B, cfg.d), float("nan"), dtype=torch.float32, device="cuda") for _ in range(2)]
+    kcs2 = hy.native(xs, ys2)
+    torch.cuda.synchronize()
+    assert kcs2 == kcs
+    for l in range(2):
+        assert ys2[l].cpu().numpy().tobytes() == ys[l].cpu().numpy().tobytes(), l
 
 
 @pytest.mark.parametrize("B", [1, 2])
