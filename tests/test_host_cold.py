@@ -205,3 +205,18 @@ def test_lookahead_hybrid_rejects_bad_arguments():
     s = host._HybridAheadScratch.from_buffer_copy(full)
     s.list_event[1] = None
     assert ahead(s=s) == pi.PI_EINVAL
+
+
+def test_hybrid_stack_rejects_bad_arguments():
+    import ctypes as C
+    L = host.load()
+    FAKE = 1 << 20
+    arr = (C.c_void_p * 1)(FAKE)
+    s = host._HybridAheadScratch()
+
+    def call(n=1, layers=FAKE, xs=arr):
+        return L.pi_hybrid_stack_ahead(0, n, layers, arr, arr, arr, arr, 1, xs, 0.0, arr, C.byref(s), 0, None)
+
+    assert call(n=0) == pi.PI_EINVAL
+    assert call(layers=None) == pi.PI_EINVAL
+    assert call(xs=None) == pi.PI_EINVAL
