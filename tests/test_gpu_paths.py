@@ -509,3 +509,41 @@ def test_lookahead_gated_layers_of_different_hidden_sizes(B):
         assert K > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
         y_or = ph.oracle_ffn_on_ids(spec, xs[l], spec.T_g[A_g])
         assert ph.rel_err(b.y.cpu().numpy(), y_or) <= ph.RTOL, l
+
+
+def test_lookahead_ragged_shapes():
+    """pi_ffn_layer_ahead at batch 1 on ragged shapes: N not a multiple of the 64-id tile, d not a
+    multiple of the lane width, and a next-layer H that leaves the last look-ahead workgroup part
+    empty (76 rows, 8 per workgroup)."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    cfg = ph.small_case("ragged-ahead", d=264, N=1000, H=76, wdtype=synth.F16, gpu_frac=0.4, seed=23)
+    cfg = synth.Config(cfg.key, cfg.desc, 2, cfg.d, cfg.N, cfg.wdtype, cfg.pdtype, cfg.bdtype, cfg.gated,
+                       cfg.density, cfg.alpha, cfg.H, cfg.gpu_frac, cfg.batches, cfg.steps, cfg.seed)
+    specs = [synth.layer_spec(cfg, l) for l in range(2)]
+    dls = [ph.DeviceLayer(s) for s in specs]
+    bufs = [ph.DeviceBuffers(cfg, s.H, s.n_g, len(s.T_c), 1) for s in specs]
+    xs = [synth.host_x(cfg.seed, l, 6, 1, cfg.d) for l in range(2)]
+    for b, x in zip(bufs, xs):
+        b.x.copy_(torch.from_numpy(x))
+    torch.cuda.synchronize()
+    rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
+    b0, b1 = bufs
+    print("look-ahead ragged", flush=True)
+    pi.pi_ffn_layer_stages(dls[0].layer, 1, b0.x, 0.0, None, b0.y, b0.logits, b0.A_g, b0.K, b0.A_c, b0.K_c,
+                           b0.ws_layer, pi.PI_STAGE_HIDDEN)
+    pi.pi_ffn_layer_ahead(dls[0].layer, 1, b0.x, 0.0, None, b0.y, b0.logits, b0.A_g, b0.K, b0.A_c, b0.K_c,
+                          b0.ws_layer, rest, dls[1].layer, b1.ws_layer)
+    pi.pi_ffn_layer_stages(dls[1].layer, 1, b1.x, 0.0, None, b1.y, b1.logits, b1.A_g, b1.K, b1.A_c, b1.K_c,
+                           b1.ws_layer, rest)
+    torch.cuda.synchronize()
+    spec, b = specs[1], b1
+    logits_or, _ = ph.oracle_predict(spec, xs[0])
+    assert np.max(np.abs(b.logits.cpu().numpy().astype(np.float64) - logits_or)) <= ph.LOGIT_ATOL
+    K = int(b.K.cpu()[0])
+    A_g = b.A_g.cpu().numpy()[:K]
+    A_g_or, _ = orc.compact(logits_or, 0.0, spec.T_g, spec.T_c)
+    _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
+    assert K > 0 and out_g == 0 and asc_g
+    y_or = ph.oracle_ffn_on_ids(spec, xs[1], spec.T_g[A_g])
+    assert ph.rel_err(b.y.cpu().numpy(), y_or) <= ph.RTOL
