@@ -165,8 +165,9 @@ int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, con
  * Prepared neuron table and the fused layer call.
  *
  * The GPU neuron table T_g (slot -> original neuron id) in the form the fused
- * kernels read: for each group of 32 original ids, a bitmap of the ids that
- * are GPU-resident and the number of GPU-resident ids below the group.  The
+ * kernels read: a bitmap of the GPU-resident original ids (one bit per id,
+ * 32 per word), then, for each group of 64 ids, the number of GPU-resident
+ * ids below the group.  The
  * slot of a GPU-resident id is then its rank among the GPU-resident ids,
  * which is what T_g gives when T_g is ascending; the CPU table is the
  * ascending complement (CSDN summary, section 神经元放置和管理: one table per
