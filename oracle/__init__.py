@@ -58,6 +58,7 @@ def lib():
         L.or_sparse_ffn.argtypes = [C.c_int, C.c_int, C.c_int, P, _OrMat, _OrVec, _OrMat, _OrMat, P, C.c_int, P, P]
         L.or_dense_ffn.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, _OrMat, _OrVec, _OrMat, _OrMat, _OrVec, P]
         L.or_merge.argtypes = [C.c_int, C.c_int, P, P, C.c_int, _OrVec, P]
+        L.or_layer_norm.argtypes = [C.c_int, C.c_int, P, C.c_double, P]
         L.or_set_threads.argtypes = [C.c_int]
         L.or_get_threads.restype = C.c_int
         _lib = L
@@ -185,3 +186,15 @@ def merge(y_g: np.ndarray, y_c: Optional[np.ndarray], K_c: int, b2: Optional[Vec
     lib().or_merge(B, d, y_g.ctypes.data, yc.ctypes.data if yc is not None else None, int(K_c),
                    (b2 or Vec(None))._c(), y.ctypes.data)
     return y
+
+
+def layer_norm(y: np.ndarray, eps: float) -> np.ndarray:
+    """Chained-layer input from a layer's output: per row, subtract the mean and divide by
+    sqrt(population variance + eps), in fp64 from the fp32 y -> [B, d] float64."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    if y.ndim == 1:
+        y = y[None, :]
+    B, d = y.shape
+    x = np.empty((B, d), np.float64)
+    lib().or_layer_norm(B, d, y.ctypes.data, float(eps), x.ctypes.data)
+    return x

@@ -141,3 +141,16 @@ void or_merge(int B, int d, const double* y_g, const double* y_c, int K_c, or_ve
       y[t] = v + or_vec_at(b2, c);
     }
 }
+
+void or_layer_norm(int B, int d, const float* y, double eps, double* x) {
+  for (int b = 0; b < B; ++b) {
+    const float* r = y + (size_t)b * d;
+    double mu = 0.0, var = 0.0;
+    for (int k = 0; k < d; ++k) mu += (double)r[k];
+    mu /= (double)d;
+    for (int k = 0; k < d; ++k) var += ((double)r[k] - mu) * ((double)r[k] - mu);
+    var /= (double)d;
+    const double sd = sqrt(var + eps);
+    for (int k = 0; k < d; ++k) x[(size_t)b * d + k] = ((double)r[k] - mu) / sd;
+  }
+}

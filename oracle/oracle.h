@@ -22,6 +22,11 @@
  *    active neuron).
  *  - same page, section "神经元-觉察算子" (first decide whether a neuron is
  *    active, then process its row or column of the weight matrix).
+ *  - same page, background part on the MLP block (its output goes on to the
+ *    next layer): or_layer_norm, the normalisation that turns one layer's
+ *    output into the next layer's input in a chained stack, is not on the
+ *    pages; it is a reading (layer normalisation with unit gain and zero
+ *    bias, as in front of each FFN of the OPT models the pages serve).
  */
 #ifndef PI_ORACLE_H
 #define PI_ORACLE_H
@@ -70,6 +75,11 @@ void or_dense_ffn(int B, int d, int n, int kind, const float* x, or_mat W1, or_v
 
 /* y = y_g + y_c (+ b2): y_c is added only when y_c != NULL and K_c != 0. */
 void or_merge(int B, int d, const double* y_g, const double* y_c, int K_c, or_vec b2, double* y);
+
+/* Chained layers:  x[b,k] = (y[b,k] - mu_b) / sqrt(var_b + eps), with mu_b the
+ * mean and var_b the population variance (divided by d) of row b of y [B x d].
+ * In-place use (x aliasing y) is not supported: y is fp32, x is double. */
+void or_layer_norm(int B, int d, const float* y, double eps, double* x);
 
 /* Threads the oracle's OpenMP loops may use (0 = library default). */
 void or_set_threads(int n);

@@ -290,3 +290,41 @@ def test_fp16_and_int4_weights_are_widened_exactly():
     z = x.astype(np.float64) @ Wdq.T + b1.astype(np.float64)
     ref4 = np.maximum(z, 0) @ Wdq
     assert np.allclose(y4, ref4, rtol=1e-12, atol=1e-13)
+
+
+# ---- chained layers: the normalisation between one layer's output and the next layer's input ----
+# (not on the pages; reading: layer normalisation with unit gain and zero bias)
+
+def test_layer_norm_hand_example():
+    # mean 2.5, population variance (2.25 + 0.25 + 0.25 + 2.25) / 4 = 1.25
+    y = np.array([[1.0, 2.0, 3.0, 4.0]], np.float32)
+    x = orc.layer_norm(y, 0.0)
+    assert np.allclose(x, np.array([[-1.5, -0.5, 0.5, 1.5]]) / np.sqrt(1.25), rtol=0, atol=1e-15)
+    # eps enters under the root: y = (-1, 1) has variance 1
+    x = orc.layer_norm(np.array([[-1.0, 1.0]], np.float32), 0.25)
+    assert np.allclose(x, [[-1.0 / np.sqrt(1.25), 1.0 / np.sqrt(1.25)]], rtol=0, atol=1e-15)
+
+
+def test_layer_norm_invariants():
+    rng = np.random.default_rng(41)
+    y = rng.standard_normal((5, 96)).astype(np.float32) * 3.0 + 0.7
+    x = orc.layer_norm(y, 0.0)
+    # zero mean and unit population variance per row (a sample variance would give (d-1)/d)
+    assert np.allclose(x.mean(axis=1), 0.0, atol=1e-13)
+    assert np.allclose((x * x).mean(axis=1), 1.0, rtol=0, atol=1e-12)
+    # invariant under a positive scale and a shift of each row (exact in fp32: powers of two)
+    y2 = (y * np.float32(4.0) + np.float32(-8.0)).astype(np.float32)
+    assert np.allclose(orc.layer_norm(y2, 0.0), x, rtol=0, atol=1e-5)
+    # rows are independent
+    assert np.array_equal(orc.layer_norm(y[2:3], 0.0), x[2:3])
+    # a constant row gives zeros (eps > 0)
+    c = np.full((1, 33), 3.25, np.float32)
+    assert np.array_equal(orc.layer_norm(c, 1e-5), np.zeros((1, 33)))
+
+
+def test_layer_norm_matches_torch_functional():
+    import torch
+    rng = np.random.default_rng(42)
+    y = (rng.standard_normal((3, 7168)) * 0.05).astype(np.float32)
+    want = torch.nn.functional.layer_norm(torch.from_numpy(y).double(), (7168,), eps=1e-5).numpy()
+    assert np.allclose(orc.layer_norm(y, 1e-5), want, rtol=0, atol=1e-12)
