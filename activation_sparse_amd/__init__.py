@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libpi.so")
 
 EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes",
            "pi_table_prepare", "pi_ffn_layer", "pi_ffn_layer_stages", "pi_workspace_bytes", "pi_status_string",
-           "pi_last_hip_error", "pi_abi_version", "pi_read_probe", "pi_ffn_layer_ahead")
+           "pi_last_hip_error", "pi_abi_version", "pi_read_probe", "pi_ffn_layer_ahead",
+           "pi_layer_norm")
 
 
 class PiError(RuntimeError):
@@ -65,6 +66,8 @@ def load():
         L.pi_compact.argtypes = [P, I, I, P, C.c_float, P, I, P, P, P, I, P, P, P, C.c_size_t]
         L.pi_sparse_ffn.argtypes = [P, I, I, I, I, P, _Mat, _Vec, _Mat, _Mat, P, P, P, P, C.c_size_t]
         L.pi_merge.argtypes = [P, I, I, P, P, P, _Vec]
+        L.pi_layer_norm.argtypes = [P, I, I, P, C.c_float, P]
+        L.pi_layer_norm.restype = C.c_int
         L.pi_read_probe.argtypes = [P, P, C.c_size_t, I, P]
         L.pi_read_probe.restype = C.c_int
         L.pi_table_bytes.argtypes = [I]
@@ -178,6 +181,11 @@ def pi_sparse_ffn(B, d, n_g, kind, x, W1: Matrix, b1: Vector, Wup: Optional[Matr
 def pi_read_probe(buf, nbytes: int, out, blocks: int = 0, stream=None) -> None:
     """Streaming read of nbytes of buf (the bandwidth reference); out: uint32 [4 * blocks]."""
     _check(load().pi_read_probe(_stream(stream), _ptr(buf), int(nbytes), int(blocks), _ptr(out)), "pi_read_probe")
+
+
+def pi_layer_norm(B, d, y, x, eps: float = 1e-5, stream=None) -> None:
+    """Chained layers: x[b] = (y[b] - mean) / sqrt(var + eps) per row (x may be y)."""
+    _check(load().pi_layer_norm(_stream(stream), int(B), int(d), _ptr(y), float(eps), _ptr(x)), "pi_layer_norm")
 
 
 def pi_merge(B, d, y, y_c=None, K_c=None, b2: Optional[Vector] = None, stream=None) -> None:

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
+#include <cmath>
 #include "../../include/pi.h"
 #include "pi_internal.h"
 
@@ -458,6 +459,14 @@ int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, con
   if (!valid_batch(B) || d <= 0 || !y || !valid_vector(b2)) return PI_EINVAL;
   if (!y_c && !b2.data) return PI_OK;  // nothing to add
   return hip_status(pi::launch_merge(B, d, y, y_c, K_c, b2.data, b2.dtype, static_cast<hipStream_t>(stream)));
+}
+
+int pi_layer_norm(void* stream, int32_t B, int32_t d, const float* y, float eps, float* x) {
+  if (B <= 0 || d <= 0 || !y || !x || !(eps >= 0.f) || !std::isfinite(eps)) return PI_EINVAL;
+  const int64_t n = (int64_t)B * d;
+  const float* x0 = x;
+  if (x0 != y && x0 < y + n && y < x0 + n) return PI_EINVAL;   // partial overlap
+  return hip_status(pi::launch_layer_norm(B, d, y, eps, x, static_cast<hipStream_t>(stream)));
 }
 
 int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, uint32_t* out) {

@@ -8,6 +8,9 @@
 //              sum -> ascending slot list and its count (stays on device).
 //  k_merge   : y += y_c (+ b2), skipped on the device when no cold neuron is
 //              active.
+//  k_layer_norm : chained layers; one layer's output row normalised (mean 0,
+//              unit variance) into the next layer's input.  One workgroup per
+//              row, the row held in registers up to 16 Ki elements.
 #include "pi_device.h"
 #include "pi_internal.h"
 #include "pi_list.h"
@@ -221,6 +224,72 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p,
   if ((threadIdx.x & (kWave - 1)) == 0) out[blockIdx.x * 4 + threadIdx.x / kWave] = acc;
 }
 
+constexpr int kLnThreads = 1024;
+constexpr int kLnReg = 16;   // elements per thread held in registers: rows up to 16 Ki
+
+// Sum over the workgroup in a fixed order: butterfly within each wave, then the
+// waves' sums in wave order.  Every thread returns the same value.
+__device__ __forceinline__ float ln_block_sum(float v, float* red) {
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLnThreads / kWave; ++i) s += red[i];
+  __syncthreads();          // red is reused by the next sum
+  return s;
+}
+
+// x[b,:] = (y[b,:] - mean) / sqrt(var + eps), population variance.  Rows past
+// what the registers hold are read again from memory in each pass.  Each
+// element is read and written by one thread, after both sums: x may be y.
+__global__ __launch_bounds__(kLnThreads) void k_layer_norm(int d, const float* y, float eps, float* x) {
+  __shared__ float red[kLnThreads / kWave];
+  const float* r = y + (int64_t)blockIdx.x * d;
+  float* o = x + (int64_t)blockIdx.x * d;
+  const int t = threadIdx.x;
+  const bool held = d <= kLnReg * kLnThreads;
+  float v[kLnReg];
+  float s = 0.f;
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kLnReg; ++i) {
+      const int k = t + i * kLnThreads;
+      v[i] = k < d ? r[k] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kLnReg; ++i) s += v[i];
+  } else {
+    for (int k = t; k < d; k += kLnThreads) s += r[k];
+  }
+  const float mu = ln_block_sum(s, red) / (float)d;
+  float q = 0.f;
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kLnReg; ++i) {
+      const float e = v[i] - mu;
+      if (t + i * kLnThreads < d) q += e * e;
+    }
+  } else {
+    for (int k = t; k < d; k += kLnThreads) {
+      const float e = r[k] - mu;
+      q += e * e;
+    }
+  }
+  const float var = ln_block_sum(q, red) / (float)d;
+  const float inv = 1.0f / sqrtf(var + eps);
+  if (held) {
+#pragma unroll
+    for (int i = 0; i < kLnReg; ++i) {
+      const int k = t + i * kLnThreads;
+      if (k < d) o[k] = (v[i] - mu) * inv;
+    }
+  } else {
+    for (int k = t; k < d; k += kLnThreads) o[k] = (r[k] - mu) * inv;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void k_merge(int64_t n, int d, float* y, const float* y_c,
                                                     const int32_t* K_c, const void* b2, int b2_dt) {
   const bool add_c = y_c && (!K_c || *K_c != 0);
@@ -316,6 +385,11 @@ hipError_t launch_list(const ListCtx& c, int n_g, hipStream_t s) {
 
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
   hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_layer_norm(int B, int d, const float* y, float eps, float* x, hipStream_t s) {
+  hipLaunchKernelGGL(k_layer_norm, dim3((unsigned)B), dim3(kLnThreads), 0, s, d, y, eps, x);
   return hipGetLastError();
 }
 

@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--lookahead-steps", type=int, default=16,
                     help="after the batch-1 measurement, time look-ahead prediction (layer L+1's predictor hidden "
                          "layer from layer L's input, beside layer L's FFN) over this many steps; 0 = skip")
+    ap.add_argument("--chained-steps", type=int, default=16,
+                    help="after the batch-1 measurement, time chained layers (layer L+1's input is the layer "
+                         "normalisation of layer L's output, made on the GPU) over this many steps; 0 = skip")
     return ap.parse_args()
 
 
@@ -510,6 +513,123 @@ def lookahead_bench(cfg, specs, dls, steps, warmup, B=1):
            "predictor_input": "layer L+1's hidden layer from layer L's input (layer 0: its own)"}
     log(f"look-ahead prediction: {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s")
     del graphs
+    return out
+
+
+def chained_bench(cfg, specs, dls, steps, warmup, B=1, eps=1e-5):
+    """Chained layers: layer L+1's input is the layer normalisation of layer L's output
+    (pi_layer_norm on the GPU), so every layer's input is made by the step itself; layer 0's input
+    is seeded per step.  Timed with exact prediction (pi_ffn_layer) and with look-ahead prediction
+    (pi_ffn_layer_ahead: layer L+1's predictor hidden layer from layer L's input).  The cold
+    partials stay seeded, as in the measured run.  One HIP graph per step; returns tokens/s of both
+    and the normalisation kernel's own time."""
+    import torch
+    import synth
+    import activation_sparse_amd as pi
+    dev = "cuda:0"
+    n_layers = len(specs)
+    maxH = max(s.H for s in specs)
+    n_g = max(s.n_g for s in specs)
+    n_c = max(len(s.T_c) for s in specs)
+    d, N = cfg.d, cfg.N
+    S = warmup + steps
+    ws_bytes = max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256)
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+    x0 = torch.empty((S, B, d), dtype=torch.float32, device=dev)
+    xl = torch.empty((n_layers, B, d), dtype=torch.float32, device=dev)
+    ycs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev) if n_c else None
+    Ks = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    Kcs = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    y = torch.empty((B, d), dtype=torch.float32, device=dev)
+    A_g = torch.empty(max(n_g, 1), dtype=torch.int32, device=dev)
+    A_c = torch.empty(max(n_c, 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in range(S):
+        rid = torch.from_numpy(synth.x_row_ids(t, B)).to(dev)
+        synth.dev_fill(x0[t].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_X, 0, d, 1.0,
+                       row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+        if n_c:
+            for L in range(n_layers):
+                synth.dev_fill(ycs[t, L].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_YC, L, d, 0.05,
+                               row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+    torch.cuda.synchronize()
+    rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
+
+    def step_call(t, ahead):
+        for L in range(n_layers):
+            x = x0[t] if L == 0 else xl[L]
+            cold = len(specs[L].T_c) > 0
+            args = (B, x, 0.0, ycs[t, L] if cold else None, y, None, A_g, Ks[t, L:L + 1], A_c if cold else None,
+                    Kcs[t, L:L + 1] if cold else None, wss[L])
+            if ahead and L == 0:
+                pi.pi_ffn_layer_stages(dls[0].layer, *args, pi.PI_STAGE_HIDDEN, _cstruct=dls[0].layer_c)
+            if ahead and L + 1 < n_layers:
+                pi.pi_ffn_layer_ahead(dls[L].layer, *args, rest, dls[L + 1].layer, wss[L + 1],
+                                      _cstruct=dls[L].layer_c, _next_cstruct=dls[L + 1].layer_c)
+            else:
+                pi.pi_ffn_layer_stages(dls[L].layer, *args, rest if ahead else pi.PI_STAGE_ALL,
+                                       _cstruct=dls[L].layer_c)
+            if L + 1 < n_layers:
+                pi.pi_layer_norm(B, d, y, xl[L + 1], eps)
+
+    def timed(ahead):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_call(0, ahead)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for t in range(S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_call(t, ahead)
+            graphs.append(g)
+        for t in range(warmup):
+            graphs[t].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(warmup, S):
+            graphs[t].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del graphs
+        return e0.elapsed_time(e1) / steps
+
+    ms_exact = timed(False)
+    K_exact = float(Ks[warmup:].float().mean().item())
+    ms_ahead = timed(True)
+    K_ahead = float(Ks[warmup:].float().mean().item())
+    # the normalisation alone: a graph of back-to-back calls on [B x d] (kernel + the gap to the next)
+    n_norm = 200
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        pi.pi_layer_norm(B, d, y, xl[1], eps)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_norm):
+            pi.pi_layer_norm(B, d, y, xl[1], eps)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    out = {"batch": B, "steps": steps, "eps": eps,
+           "tokens_per_s": round(B * 1e3 / ms_exact, 2), "ms_per_step": round(ms_exact, 4), "mean_K": K_exact,
+           "lookahead_tokens_per_s": round(B * 1e3 / ms_ahead, 2), "lookahead_ms_per_step": round(ms_ahead, 4),
+           "lookahead_mean_K": K_ahead,
+           "layer_norm_us": round(e0.elapsed_time(e1) * 1e3 / n_norm, 2),
+           "input": "layer 0 seeded per step; layer L+1 = layer norm of layer L's output (unit gain, zero bias)"}
+    log(f"chained layers: exact {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s; look-ahead "
+        f"{out['lookahead_ms_per_step']} ms/step, {out['lookahead_tokens_per_s']} tokens/s; "
+        f"layer norm {out['layer_norm_us']} us")
     return out
 
 
@@ -970,6 +1090,11 @@ def main():
         log("look-ahead prediction ...")
         lookahead = lookahead_bench(cfg, specs, dls, args.lookahead_steps, 3)
 
+    chained = None
+    if args.chained_steps > 0 and B == 1:
+        log("chained layers ...")
+        chained = chained_bench(cfg, specs, dls, args.chained_steps, 3)
+
     placement = None
     if args.placement and B == 1:
         log("placement solver (host) ...")
@@ -1016,7 +1141,7 @@ def main():
                    "event_ms": round(gpu_ms, 3),
                    "stream_read_gbps": stream_read,
                    "dominant_frac_of_stream_read": round(achieved[iso] / dom_ref, 4),
-                   "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead, "int4_predictor": i4pred,
+                   "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead, "chained": chained, "int4_predictor": i4pred,
                    "placement": placement},
     }
     print(json.dumps(out), flush=True)

@@ -272,6 +272,22 @@ int pi_ffn_layer_ahead(void* stream, const pi_layer* layer, int32_t B, const flo
                        int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, uint32_t stages,
                        const pi_layer* next, void* ws_next, size_t ws_next_bytes);
 
+/* Chained layers: the next layer's input from this layer's output (CSDN
+ * summary, background part on the MLP block: the block's output goes on to
+ * the next layer).  The pages name no normalisation between layers; the
+ * reading here is layer normalisation with unit gain and zero bias, as in
+ * front of each FFN of the OPT models they serve:
+ *   x[b,k] = (y[b,k] - mean_b) / sqrt(var_b + eps),
+ * mean_b and the population variance var_b (divided by d) over row b.
+ * y, x: device [B x d] fp32 row-major; x may be y itself (in place) but may
+ * not overlap it otherwise.  One workgroup per row; fp32 sums in a fixed
+ * order, so the result is bitwise repeatable.  A constant row gives zeros
+ * (eps > 0).  Rows whose squares overflow fp32 give inf/NaN, as the formula
+ * in fp32 does.  No workspace.
+ * Errors: PI_EINVAL for a NULL pointer, B <= 0, d <= 0, eps negative or not
+ * finite, or x overlapping y without being equal to it. */
+int pi_layer_norm(void* stream, int32_t B, int32_t d, const float* y, float eps, float* x);
+
 /* The streaming-read reference that the kernels' bandwidths are read against:
  * reads `bytes` bytes of `buf` once, in 16-byte vectors, with `blocks`
  * workgroups of 256 threads (blocks <= 0: 8 per compute unit) each keeping

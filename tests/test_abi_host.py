@@ -184,6 +184,21 @@ def test_read_probe_rejects_bad_arguments():
     assert status(pi.pi_read_probe, FAKE + 8, 1024, FAKE, 0, 0) == pi.PI_EINVAL      # unaligned
 
 
+def test_layer_norm_rejects_bad_arguments():
+    # (B, d, y, x, eps, stream)
+    n = 4 * 16
+    assert status(pi.pi_layer_norm, 0, 16, FAKE, FAKE, 1e-5, 0) == pi.PI_EINVAL
+    assert status(pi.pi_layer_norm, 4, 0, FAKE, FAKE, 1e-5, 0) == pi.PI_EINVAL
+    assert status(pi.pi_layer_norm, 4, 16, None, FAKE, 1e-5, 0) == pi.PI_EINVAL
+    assert status(pi.pi_layer_norm, 4, 16, FAKE, None, 1e-5, 0) == pi.PI_EINVAL
+    assert status(pi.pi_layer_norm, 4, 16, FAKE, FAKE + 4 * n, -1e-5, 0) == pi.PI_EINVAL
+    assert status(pi.pi_layer_norm, 4, 16, FAKE, FAKE + 4 * n, float("nan"), 0) == pi.PI_EINVAL
+    assert status(pi.pi_layer_norm, 4, 16, FAKE, FAKE + 4 * n, float("inf"), 0) == pi.PI_EINVAL
+    # x overlapping y without being y
+    assert status(pi.pi_layer_norm, 4, 16, FAKE, FAKE + 4, 1e-5, 0) == pi.PI_EINVAL
+    assert status(pi.pi_layer_norm, 4, 16, FAKE + 4 * (n - 1), FAKE, 1e-5, 0) == pi.PI_EINVAL
+
+
 def test_compact_and_merge_reject_bad_arguments():
     assert status(pi.pi_compact, 1, 0, FAKE, 0.0, FAKE, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL
     assert status(pi.pi_compact, 1, 100, FAKE, 0.0, None, 10, FAKE, FAKE, None, 0, None, None, 0) == pi.PI_EINVAL

@@ -547,3 +547,108 @@ def test_lookahead_ragged_shapes():
     assert K > 0 and out_g == 0 and asc_g
     y_or = ph.oracle_ffn_on_ids(spec, xs[1], spec.T_g[A_g])
     assert ph.rel_err(b.y.cpu().numpy(), y_or) <= ph.RTOL
+
+
+# Layer normalisation between chained layers, fp32 on the GPU against the oracle's fp64 on the
+# same fp32 rows.  Each fp32 sum runs at most 16 terms per thread, 6 butterfly levels and 16 wave
+# sums in sequence, so its error is below 38 u sum|y| (u = 2^-24); for rows whose mean is within
+# 3 standard deviations the mean and the deviation are then off by < 38 u (|m| + sigma) / sigma
+# <= 1e-5 of sigma, and the unit-scale output by about that plus a few ulps of |x|.
+LN_ATOL = 2e-5
+
+
+@pytest.mark.parametrize("B,d,scale,offset", [
+    (1, 7168, 0.05, 0.0),       # an OPT-30B layer output at batch 1
+    (4, 7168, 3.0, 1.0),
+    (32, 7168, 0.02, -0.01),    # the largest batch
+    (3, 768, 1.0, 0.5),
+    (2, 13, 1.0, 0.0),          # ragged: fewer elements than one wave
+    (2, 1000, 1e15, 0.0),       # large magnitudes (squares still within fp32)
+    (2, 1000, 1e-15, 0.0),      # small magnitudes (eps dominates the variance)
+    (1, 16384, 1.0, 0.0),       # the most elements the registers hold
+    (2, 16385, 1.0, 0.0),       # one more: the rows are read again in each pass
+    (1, 50000, 2.0, -1.0),
+])
+def test_layer_norm_parity(B, d, scale, offset):
+    import activation_sparse_amd as pi
+    torch = _dev()
+    rng = np.random.default_rng(B * 7919 + d)
+    y = (rng.standard_normal((B, d)) * scale + offset * scale).astype(np.float32)
+    print(f"layer norm B={B} d={d} scale={scale}", flush=True)
+    yd = torch.from_numpy(y).cuda()
+    x = torch.empty_like(yd)
+    pi.pi_layer_norm(B, d, yd, x, 1e-5)
+    x2 = torch.empty_like(yd)
+    pi.pi_layer_norm(B, d, yd, x2, 1e-5)
+    yi = yd.clone()
+    pi.pi_layer_norm(B, d, yi, yi, 1e-5)              # in place
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    assert np.max(np.abs(got.astype(np.float64) - orc.layer_norm(y, 1e-5))) <= LN_ATOL
+    assert np.array_equal(got.view(np.uint32), x2.cpu().numpy().view(np.uint32))     # repeatable
+    assert np.array_equal(got.view(np.uint32), yi.cpu().numpy().view(np.uint32))     # in place: same bits
+    assert np.array_equal(yd.cpu().numpy(), y)                                        # input untouched
+
+
+def test_layer_norm_constant_rows_give_zeros():
+    import activation_sparse_amd as pi
+    torch = _dev()
+    y = np.stack([np.full(7168, 3.25, np.float32), np.zeros(7168, np.float32)])
+    yd = torch.from_numpy(y).cuda()
+    x = torch.full_like(yd, 7.0)
+    print("layer norm constant rows", flush=True)
+    pi.pi_layer_norm(2, 7168, yd, x, 1e-5)
+    torch.cuda.synchronize()
+    assert np.array_equal(x.cpu().numpy(), orc.layer_norm(y, 1e-5).astype(np.float32))
+    assert not np.any(x.cpu().numpy())
+
+
+@pytest.mark.parametrize("B,ahead", [(1, False), (1, True), (4, False), (4, True)])
+def test_chained_layers(B, ahead):
+    """Three chained layers: layer l+1's input is the layer normalisation of layer l's output, made
+    on the GPU (pi_layer_norm).  Exact prediction (pi_ffn_layer) or look-ahead (pi_ffn_layer_ahead:
+    layer l+1's hidden layer from layer l's input).  Each layer against the oracle on the input the
+    GPU gave it: logits and lists from the predictor's input, the output over the GPU's list, and
+    the next input against the oracle's normalisation of the GPU's output."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    cfg = ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=29)
+    nl = 3
+    specs = [synth.layer_spec(cfg, l) for l in range(nl)]
+    dls = [ph.DeviceLayer(s) for s in specs]
+    bufs = [ph.DeviceBuffers(cfg, s.H, s.n_g, len(s.T_c), B) for s in specs]
+    bufs[0].x.copy_(torch.from_numpy(synth.host_x(cfg.seed, 0, 5, B, cfg.d)))
+    torch.cuda.synchronize()
+    rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
+    print(f"chained layers B={B} ahead={ahead}", flush=True)
+    if ahead:
+        b0 = bufs[0]
+        pi.pi_ffn_layer_stages(dls[0].layer, B, b0.x, 0.0, None, b0.y, b0.logits, b0.A_g, b0.K, b0.A_c, b0.K_c,
+                               b0.ws_layer, pi.PI_STAGE_HIDDEN)
+    for l in range(nl):
+        b = bufs[l]
+        if ahead and l + 1 < nl:
+            pi.pi_ffn_layer_ahead(dls[l].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c,
+                                  b.ws_layer, rest, dls[l + 1].layer, bufs[l + 1].ws_layer)
+        else:
+            pi.pi_ffn_layer_stages(dls[l].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c,
+                                   b.ws_layer, rest if ahead else pi.PI_STAGE_ALL)
+        if l + 1 < nl:
+            pi.pi_layer_norm(B, cfg.d, b.y, bufs[l + 1].x, 1e-5)
+    torch.cuda.synchronize()
+    xs = [b.x.cpu().numpy() for b in bufs]
+    for l in range(nl):
+        spec, b = specs[l], bufs[l]
+        x_pred = xs[max(l - 1, 0)] if ahead else xs[l]
+        logits_or, _ = ph.oracle_predict(spec, x_pred)
+        assert np.max(np.abs(b.logits.cpu().numpy().astype(np.float64) - logits_or)) <= ph.LOGIT_ATOL, l
+        K, K_c = int(b.K.cpu()[0]), int(b.K_c.cpu()[0])
+        A_g, A_c = b.A_g.cpu().numpy()[:K], b.A_c.cpu().numpy()[:K_c]
+        A_g_or, A_c_or = orc.compact(logits_or, 0.0, spec.T_g, spec.T_c)
+        _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
+        _, out_c, asc_c = ph.list_check(A_c, A_c_or, spec.T_c, logits_or, 0.0)
+        assert K > 0 and out_g == 0 and out_c == 0 and asc_g and asc_c, l
+        y = b.y.cpu().numpy()
+        assert ph.rel_err(y, ph.oracle_ffn_on_ids(spec, xs[l], spec.T_g[A_g])) <= ph.RTOL, l
+        if l + 1 < nl:
+            assert np.max(np.abs(xs[l + 1].astype(np.float64) - orc.layer_norm(y, 1e-5))) <= LN_ATOL, l
