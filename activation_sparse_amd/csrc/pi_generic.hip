@@ -10,7 +10,8 @@
 //              active.
 //  k_layer_norm : chained layers; one layer's output row normalised (mean 0,
 //              unit variance) into the next layer's input.  One workgroup per
-//              row, the row held in registers up to 16 Ki elements.
+//              row, 16-byte loads, the row held in registers up to 16 Ki
+//              elements.
 #include "pi_device.h"
 #include "pi_internal.h"
 #include "pi_list.h"
@@ -241,52 +242,103 @@ __device__ __forceinline__ float ln_block_sum(float v, float* red) {
   return s;
 }
 
-// x[b,:] = (y[b,:] - mean) / sqrt(var + eps), population variance.  Rows past
-// what the registers hold are read again from memory in each pass.  Each
-// element is read and written by one thread, after both sums: x may be y.
+template <int V>
+__device__ __forceinline__ void ln_load(const float* p, float* e) {
+  if constexpr (V == 4) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    e[0] = q.x; e[1] = q.y; e[2] = q.z; e[3] = q.w;
+  } else {
+    e[0] = *p;
+  }
+}
+
+template <int V>
+__device__ __forceinline__ void ln_store(float* p, const float* e) {
+  if constexpr (V == 4) *reinterpret_cast<float4*>(p) = make_float4(e[0], e[1], e[2], e[3]);
+  else *p = e[0];
+}
+
+// x[b,:] = (y[b,:] - mean) / sqrt(var + eps), population variance.  V = 4:
+// 16-byte loads and stores (d % 4 == 0, aligned rows), else single floats.
+// Rows past what the registers hold are read again from memory in each pass.
+// Each element is read and written by one thread, after both sums: x may be y.
+template <int V>
 __global__ __launch_bounds__(kLnThreads) void k_layer_norm(int d, const float* y, float eps, float* x) {
+  constexpr int G = kLnReg / V;             // loads per thread held in registers
   __shared__ float red[kLnThreads / kWave];
   const float* r = y + (int64_t)blockIdx.x * d;
   float* o = x + (int64_t)blockIdx.x * d;
-  const int t = threadIdx.x;
-  const bool held = d <= kLnReg * kLnThreads;
-  float v[kLnReg];
+  const int t = threadIdx.x, ng = d / V;
+  const bool held = ng <= G * kLnThreads;
+  float v[G][V];
   float s = 0.f;
   if (held) {
 #pragma unroll
-    for (int i = 0; i < kLnReg; ++i) {
-      const int k = t + i * kLnThreads;
-      v[i] = k < d ? r[k] : 0.f;
+    for (int j = 0; j < G; ++j) {
+      const int q = t + j * kLnThreads;
+      if (q < ng) {
+        ln_load<V>(r + (int64_t)q * V, v[j]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[j][e] = 0.f;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < kLnReg; ++i) s += v[i];
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int e = 0; e < V; ++e) s += v[j][e];
   } else {
-    for (int k = t; k < d; k += kLnThreads) s += r[k];
+    for (int q = t; q < ng; q += kLnThreads) {
+      float e4[V];
+      ln_load<V>(r + (int64_t)q * V, e4);
+#pragma unroll
+      for (int e = 0; e < V; ++e) s += e4[e];
+    }
   }
   const float mu = ln_block_sum(s, red) / (float)d;
-  float q = 0.f;
+  float sq = 0.f;
   if (held) {
 #pragma unroll
-    for (int i = 0; i < kLnReg; ++i) {
-      const float e = v[i] - mu;
-      if (t + i * kLnThreads < d) q += e * e;
-    }
+    for (int j = 0; j < G; ++j)
+      if (t + j * kLnThreads < ng) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float dv = v[j][e] - mu;
+          sq += dv * dv;
+        }
+      }
   } else {
-    for (int k = t; k < d; k += kLnThreads) {
-      const float e = r[k] - mu;
-      q += e * e;
+    for (int q = t; q < ng; q += kLnThreads) {
+      float e4[V];
+      ln_load<V>(r + (int64_t)q * V, e4);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float dv = e4[e] - mu;
+        sq += dv * dv;
+      }
     }
   }
-  const float var = ln_block_sum(q, red) / (float)d;
+  const float var = ln_block_sum(sq, red) / (float)d;
   const float inv = 1.0f / sqrtf(var + eps);
   if (held) {
 #pragma unroll
-    for (int i = 0; i < kLnReg; ++i) {
-      const int k = t + i * kLnThreads;
-      if (k < d) o[k] = (v[i] - mu) * inv;
+    for (int j = 0; j < G; ++j) {
+      const int q = t + j * kLnThreads;
+      if (q < ng) {
+        float e4[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) e4[e] = (v[j][e] - mu) * inv;
+        ln_store<V>(o + (int64_t)q * V, e4);
+      }
     }
   } else {
-    for (int k = t; k < d; k += kLnThreads) o[k] = (r[k] - mu) * inv;
+    for (int q = t; q < ng; q += kLnThreads) {
+      float e4[V];
+      ln_load<V>(r + (int64_t)q * V, e4);
+#pragma unroll
+      for (int e = 0; e < V; ++e) e4[e] = (e4[e] - mu) * inv;
+      ln_store<V>(o + (int64_t)q * V, e4);
+    }
   }
 }
 
@@ -389,7 +441,9 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
 }
 
 hipError_t launch_layer_norm(int B, int d, const float* y, float eps, float* x, hipStream_t s) {
-  hipLaunchKernelGGL(k_layer_norm, dim3((unsigned)B), dim3(kLnThreads), 0, s, d, y, eps, x);
+  const bool vec = d % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  if (vec) hipLaunchKernelGGL(k_layer_norm<4>, dim3((unsigned)B), dim3(kLnThreads), 0, s, d, y, eps, x);
+  else hipLaunchKernelGGL(k_layer_norm<1>, dim3((unsigned)B), dim3(kLnThreads), 0, s, d, y, eps, x);
   return hipGetLastError();
 }
 

@@ -568,6 +568,8 @@ LN_ATOL = 2e-5
     (1, 16384, 1.0, 0.0),       # the most elements the registers hold
     (2, 16385, 1.0, 0.0),       # one more: the rows are read again in each pass
     (1, 50000, 2.0, -1.0),
+    (1, 50002, 1.0, 0.0),       # long and not a multiple of 4
+    (300, 64, 1.0, 0.0),        # many short rows
 ])
 def test_layer_norm_parity(B, d, scale, offset):
     import activation_sparse_amd as pi
@@ -588,6 +590,29 @@ def test_layer_norm_parity(B, d, scale, offset):
     assert np.array_equal(got.view(np.uint32), x2.cpu().numpy().view(np.uint32))     # repeatable
     assert np.array_equal(got.view(np.uint32), yi.cpu().numpy().view(np.uint32))     # in place: same bits
     assert np.array_equal(yd.cpu().numpy(), y)                                        # input untouched
+
+
+def test_layer_norm_unaligned_rows():
+    """Rows that do not start on a 16-byte boundary take the single-float loads; same values."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    B, d = 3, 7168
+    rng = np.random.default_rng(77)
+    y = rng.standard_normal((B, d)).astype(np.float32)
+    big = torch.zeros(B * d + 8, dtype=torch.float32, device="cuda")
+    yv = big[1:1 + B * d]                              # 4 bytes past an aligned start
+    yv.copy_(torch.from_numpy(y.reshape(-1)))
+    out = torch.zeros(B * d + 8, dtype=torch.float32, device="cuda")
+    xv = out[3:3 + B * d]
+    xa = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    print("layer norm unaligned", flush=True)
+    pi.pi_layer_norm(B, d, yv, xv, 1e-5)
+    pi.pi_layer_norm(B, d, torch.from_numpy(y).cuda(), xa, 1e-5)
+    torch.cuda.synchronize()
+    got = xv.cpu().numpy().reshape(B, d)
+    assert np.max(np.abs(got.astype(np.float64) - orc.layer_norm(y, 1e-5))) <= LN_ATOL
+    assert np.max(np.abs(xa.cpu().numpy().astype(np.float64) - orc.layer_norm(y, 1e-5))) <= LN_ATOL
+    assert not np.any(out[:3].cpu().numpy()) and not np.any(out[3 + B * d:].cpu().numpy())   # nothing outside
 
 
 def test_layer_norm_constant_rows_give_zeros():
