@@ -462,7 +462,7 @@ int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, con
 }
 
 int pi_layer_norm(void* stream, int32_t B, int32_t d, const float* y, float eps, float* x) {
-  if (B <= 0 || d <= 0 || !y || !x || !(eps >= 0.f) || !std::isfinite(eps)) return PI_EINVAL;
+  if (B <= 0 || d <= 0 || d > (1 << 30) || !y || !x || !(eps >= 0.f) || !std::isfinite(eps)) return PI_EINVAL;
   const int64_t n = (int64_t)B * d;
   const float* x0 = x;
   if (x0 != y && x0 < y + n && y < x0 + n) return PI_EINVAL;   // partial overlap

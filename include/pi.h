@@ -284,8 +284,8 @@ int pi_ffn_layer_ahead(void* stream, const pi_layer* layer, int32_t B, const flo
  * order, so the result is bitwise repeatable.  A constant row gives zeros
  * (eps > 0).  Rows whose squares overflow fp32 give inf/NaN, as the formula
  * in fp32 does.  No workspace.
- * Errors: PI_EINVAL for a NULL pointer, B <= 0, d <= 0, eps negative or not
- * finite, or x overlapping y without being equal to it. */
+ * Errors: PI_EINVAL for a NULL pointer, B <= 0, d outside 1..2^30, eps
+ * negative or not finite, or x overlapping y without being equal to it. */
 int pi_layer_norm(void* stream, int32_t B, int32_t d, const float* y, float eps, float* x);
 
 /* The streaming-read reference that the kernels' bandwidths are read against:

@@ -189,6 +189,7 @@ def test_layer_norm_rejects_bad_arguments():
     n = 4 * 16
     assert status(pi.pi_layer_norm, 0, 16, FAKE, FAKE, 1e-5, 0) == pi.PI_EINVAL
     assert status(pi.pi_layer_norm, 4, 0, FAKE, FAKE, 1e-5, 0) == pi.PI_EINVAL
+    assert status(pi.pi_layer_norm, 1, (1 << 30) + 1, FAKE, FAKE + (1 << 33), 1e-5, 0) == pi.PI_EINVAL
     assert status(pi.pi_layer_norm, 4, 16, None, FAKE, 1e-5, 0) == pi.PI_EINVAL
     assert status(pi.pi_layer_norm, 4, 16, FAKE, None, 1e-5, 0) == pi.PI_EINVAL
     assert status(pi.pi_layer_norm, 4, 16, FAKE, FAKE + 4 * n, -1e-5, 0) == pi.PI_EINVAL
