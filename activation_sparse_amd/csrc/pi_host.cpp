@@ -199,6 +199,56 @@ bool valid_dtype(int dt) { return dt == PI_F32 || dt == PI_F16 || dt == PI_I4G12
 
 extern "C" int pi_host_vector_path(void) { return have_avx2() ? 1 : 0; }
 
+namespace {
+
+// XOR of the 64-byte lines [l0, l1) of p, four 32-byte accumulators.
+PI_AVX2 uint64_t xor_lines_avx2(const uint8_t* p, int64_t l0, int64_t l1) {
+  __m256i s0 = _mm256_setzero_si256(), s1 = s0, s2 = s0, s3 = s0;
+  int64_t l = l0;
+  for (; l + 2 <= l1; l += 2) {
+    const __m256i* q = reinterpret_cast<const __m256i*>(p + l * 64);
+    s0 = _mm256_xor_si256(s0, _mm256_load_si256(q));
+    s1 = _mm256_xor_si256(s1, _mm256_load_si256(q + 1));
+    s2 = _mm256_xor_si256(s2, _mm256_load_si256(q + 2));
+    s3 = _mm256_xor_si256(s3, _mm256_load_si256(q + 3));
+  }
+  if (l < l1) {
+    const __m256i* q = reinterpret_cast<const __m256i*>(p + l * 64);
+    s0 = _mm256_xor_si256(s0, _mm256_load_si256(q));
+    s1 = _mm256_xor_si256(s1, _mm256_load_si256(q + 1));
+  }
+  const __m256i s = _mm256_xor_si256(_mm256_xor_si256(s0, s1), _mm256_xor_si256(s2, s3));
+  alignas(32) uint64_t w[4];
+  _mm256_store_si256(reinterpret_cast<__m256i*>(w), s);
+  return w[0] ^ w[1] ^ w[2] ^ w[3];
+}
+
+uint64_t xor_lines_scalar(const uint8_t* p, int64_t l0, int64_t l1) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  uint64_t s = 0;
+  for (int64_t i = l0 * 8; i < l1 * 8; ++i) s ^= q[i];
+  return s;
+}
+
+}  // namespace
+
+extern "C" int pi_host_read_probe(const void* buf, size_t bytes, int32_t threads, uint64_t* out) {
+  if (!buf || !out || bytes == 0 || bytes % 64 != 0 || (reinterpret_cast<uintptr_t>(buf) & 63) != 0)
+    return PI_EINVAL;
+  const int nt = threads > 0 ? threads : omp_get_max_threads();
+  const uint8_t* p = static_cast<const uint8_t*>(buf);
+  const int64_t lines = (int64_t)(bytes / 64);
+  const bool vec = have_avx2();
+  uint64_t acc = 0;
+#pragma omp parallel for schedule(static) num_threads(nt) reduction(^ : acc)
+  for (int t = 0; t < nt; ++t) {
+    const int64_t l0 = lines * t / nt, l1 = lines * (t + 1) / nt;
+    acc ^= vec ? xor_lines_avx2(p, l0, l1) : xor_lines_scalar(p, l0, l1);
+  }
+  *out = acc;
+  return PI_OK;
+}
+
 extern "C" int pi_cold_ffn_ex(int32_t B, int32_t d, int32_t n_c, int32_t kind, const float* x, pi_matrix W1,
                               pi_vector b1, pi_matrix Wup, pi_matrix W2, const int32_t* A_c, int32_t K_c, float* y_c,
                               int32_t threads, int32_t path) {
@@ -225,88 +275,99 @@ extern "C" int pi_cold_ffn_ex(int32_t B, int32_t d, int32_t n_c, int32_t kind, c
   const bool vec = path == -1 ? have_avx2() : path == 1;
   const int nt = threads > 0 ? threads : omp_get_max_threads();
 
-  // FC1: a[j * B + b]
-  std::vector<float> a((size_t)K_c * B);
-#pragma omp parallel for schedule(static) num_threads(nt)
-  for (int32_t j = 0; j < K_c; ++j) {
-    const int64_t c = A_c[j];
-    // the next listed row starts a new stream: request its first lines before this row's dot
-    if (j + 1 < K_c) {
-      const char* pn = w1.row(A_c[j + 1]);
-      for (int64_t o = 0; o < kFc1PrefetchBytes && o < rb; o += 64) _mm_prefetch(pn + o, _MM_HINT_T0);
-    }
-    float z[PI_MAX_BATCH], u[PI_MAX_BATCH];
-    if (vec) dots_avx2(w1, c, x, B, dd, z);
-    else dots_scalar(w1, c, x, B, dd, z);
-    if (gated) {
-      if (vec) dots_avx2(wu, c, x, B, dd, u);
-      else dots_scalar(wu, c, x, B, dd, u);
-    }
-    const float bias = bias_at(b1, c);
-    for (int b = 0; b < B; ++b) {
-      float v = z[b] + bias;
-      v = v > 0.f ? v : 0.f;
-      if (gated) v *= u[b];
-      a[(size_t)j * B + b] = v;
-    }
-  }
-  // the neurons that add to y (a != 0 in some batch row), in list order
-  std::vector<int32_t> act;
-  act.reserve(K_c);
-  for (int32_t j = 0; j < K_c; ++j) {
-    bool any = false;
-    for (int b = 0; b < B; ++b) any = any || a[(size_t)j * B + b] != 0.f;
-    if (any) act.push_back(j);
-  }
-  // FC2.  Few contributing rows: every thread takes a fixed range of columns over all the rows
-  // (all threads busy).  Many: chunks of whole rows (at least kFc2ChunkRows, at most
-  // kFc2MaxChunks chunks), each into its own partial [B x d], then the partials summed in chunk
-  // order (contiguous runs the hardware prefetchers follow).  Which one depends on the row count
-  // only.
-  const int64_t R = (int64_t)act.size();
+  // One parallel region for the whole call: FC1, the list of contributing neurons, FC2 (and the
+  // chunk sum), separated by barriers rather than a fork and a join per phase.
+  std::vector<float> a((size_t)K_c * B);               // FC1 outputs, a[j * B + b]
+  std::vector<int32_t> act;                              // neurons with a != 0, in list order
+  act.reserve((size_t)K_c);
+  static thread_local std::vector<float> part;           // the calling thread's, reused between calls
+  std::vector<float>* const partp = &part;
   const int64_t nvec = dd / 8;
-  if (R < kFc2ChunkMinRows) {
-#pragma omp parallel for schedule(static) num_threads(nt)
-    for (int t = 0; t < nt; ++t) {
-      const int64_t c0 = nvec * t / nt * 8, c1 = nvec * (t + 1) / nt * 8;
-      for (int b = 0; b < B; ++b)
-        for (int64_t c = c0; c < c1; ++c) y_c[(int64_t)b * dd + c] = 0.f;
-      if (c0 == c1) continue;
-      for (int64_t q = 0; q < R; ++q) {
-        const int32_t j = act[(size_t)q];
-        if (vec) axpy_avx2(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
-        else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
+  const int64_t plane = (int64_t)B * dd;
+  int64_t R = 0, crows = 0, nch = 0;
+  float* pp = nullptr;
+#pragma omp parallel num_threads(nt)
+  {
+#pragma omp for schedule(static)
+    for (int32_t j = 0; j < K_c; ++j) {
+      const int64_t c = A_c[j];
+      // the next listed row starts a new stream: request its first lines before this row's dot
+      if (j + 1 < K_c) {
+        const char* pn = w1.row(A_c[j + 1]);
+        for (int64_t o = 0; o < kFc1PrefetchBytes && o < rb; o += 64) _mm_prefetch(pn + o, _MM_HINT_T0);
+      }
+      float z[PI_MAX_BATCH], u[PI_MAX_BATCH];
+      if (vec) dots_avx2(w1, c, x, B, dd, z);
+      else dots_scalar(w1, c, x, B, dd, z);
+      if (gated) {
+        if (vec) dots_avx2(wu, c, x, B, dd, u);
+        else dots_scalar(wu, c, x, B, dd, u);
+      }
+      const float bias = bias_at(b1, c);
+      for (int b = 0; b < B; ++b) {
+        float v = z[b] + bias;
+        v = v > 0.f ? v : 0.f;
+        if (gated) v *= u[b];
+        a[(size_t)j * B + b] = v;
       }
     }
-    return PI_OK;
-  }
-  int64_t crows = (R + kFc2MaxChunks - 1) / kFc2MaxChunks;
-  crows = crows < kFc2ChunkRows ? kFc2ChunkRows : crows;
-  const int64_t nch = (R + crows - 1) / crows;
-  const int64_t plane = (int64_t)B * dd;
-  static thread_local std::vector<float> part;          // reused by the calling thread
-  if ((int64_t)part.size() < nch * plane) part.resize((size_t)(nch * plane));
-  float* pp = part.data();
-#pragma omp parallel for schedule(static) num_threads(nt)
-  for (int64_t ch = 0; ch < nch; ++ch) {
-    float* yp = pp + ch * plane;
-    std::fill(yp, yp + plane, 0.f);
-    const int64_t q1 = (ch + 1) * crows < R ? (ch + 1) * crows : R;
-    for (int64_t q = ch * crows; q < q1; ++q) {
-      const int32_t j = act[(size_t)q];
-      if (vec) axpy_avx2(w2, A_c[j], &a[(size_t)j * B], B, dd, 0, dd, yp);
-      else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, 0, dd, yp);
+    // FC2.  Few contributing rows: every thread takes a fixed range of columns over all the rows
+    // (all threads busy).  Many: chunks of whole rows (at least kFc2ChunkRows, at most
+    // kFc2MaxChunks chunks), each into its own partial [B x d], then the partials summed in chunk
+    // order (contiguous runs the hardware prefetchers follow).  Which one depends on the row count
+    // only.
+#pragma omp single
+    {
+      for (int32_t j = 0; j < K_c; ++j) {
+        bool any = false;
+        for (int b = 0; b < B; ++b) any = any || a[(size_t)j * B + b] != 0.f;
+        if (any) act.push_back(j);
+      }
+      R = (int64_t)act.size();
+      if (R >= kFc2ChunkMinRows) {
+        crows = (R + kFc2MaxChunks - 1) / kFc2MaxChunks;
+        crows = crows < kFc2ChunkRows ? kFc2ChunkRows : crows;
+        nch = (R + crows - 1) / crows;
+        if ((int64_t)partp->size() < nch * plane) partp->resize((size_t)(nch * plane));
+        pp = partp->data();
+      }
     }
-  }
-#pragma omp parallel for schedule(static) num_threads(nt)
-  for (int t = 0; t < nt; ++t) {
-    const int64_t c0 = nvec * t / nt * 8, c1 = nvec * (t + 1) / nt * 8;
-    for (int b = 0; b < B; ++b) {
-      float* yb = y_c + (int64_t)b * dd;
-      for (int64_t c = c0; c < c1; ++c) yb[c] = 0.f;
+    if (R < kFc2ChunkMinRows) {
+#pragma omp for schedule(static)
+      for (int t = 0; t < nt; ++t) {
+        const int64_t c0 = nvec * t / nt * 8, c1 = nvec * (t + 1) / nt * 8;
+        for (int b = 0; b < B; ++b)
+          for (int64_t c = c0; c < c1; ++c) y_c[(int64_t)b * dd + c] = 0.f;
+        if (c0 == c1) continue;
+        for (int64_t q = 0; q < R; ++q) {
+          const int32_t j = act[(size_t)q];
+          if (vec) axpy_avx2(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
+          else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, c0, c1, y_c);
+        }
+      }
+    } else {
+#pragma omp for schedule(static)
       for (int64_t ch = 0; ch < nch; ++ch) {
-        const float* pb = pp + ch * plane + (int64_t)b * dd;
-        for (int64_t c = c0; c < c1; ++c) yb[c] += pb[c];
+        float* yp = pp + ch * plane;
+        std::fill(yp, yp + plane, 0.f);
+        const int64_t q1 = (ch + 1) * crows < R ? (ch + 1) * crows : R;
+        for (int64_t q = ch * crows; q < q1; ++q) {
+          const int32_t j = act[(size_t)q];
+          if (vec) axpy_avx2(w2, A_c[j], &a[(size_t)j * B], B, dd, 0, dd, yp);
+          else axpy_scalar(w2, A_c[j], &a[(size_t)j * B], B, dd, 0, dd, yp);
+        }
+      }
+#pragma omp for schedule(static)
+      for (int t = 0; t < nt; ++t) {
+        const int64_t c0 = nvec * t / nt * 8, c1 = nvec * (t + 1) / nt * 8;
+        for (int b = 0; b < B; ++b) {
+          float* yb = y_c + (int64_t)b * dd;
+          for (int64_t c = c0; c < c1; ++c) yb[c] = 0.f;
+          for (int64_t ch = 0; ch < nch; ++ch) {
+            const float* pb = pp + ch * plane + (int64_t)b * dd;
+            for (int64_t c = c0; c < c1; ++c) yb[c] += pb[c];
+          }
+        }
       }
     }
   }

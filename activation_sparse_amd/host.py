@@ -14,8 +14,8 @@ from typing import Optional
 from . import PiError, Matrix, Vector, _Mat, _Vec, _Layer, PI_OK, PI_RELU
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpi_host.so")
-EXPORTS = ("pi_cold_ffn", "pi_cold_ffn_ex", "pi_host_vector_path", "pi_hybrid_layer", "pi_hybrid_prime",
-           "pi_hybrid_layer_ahead", "pi_hybrid_stack_ahead")
+EXPORTS = ("pi_cold_ffn", "pi_cold_ffn_ex", "pi_host_vector_path", "pi_host_read_probe", "pi_hybrid_layer",
+           "pi_hybrid_prime", "pi_hybrid_layer_ahead", "pi_hybrid_stack_ahead")
 
 class _HostCold(C.Structure):
     _fields_ = [("n_c", C.c_int32), ("W1", _Mat), ("b1", _Vec), ("Wup", _Mat), ("W2", _Mat)]
@@ -52,6 +52,8 @@ def load():
         L.pi_cold_ffn_ex.argtypes = [I, I, I, I, P, _Mat, _Vec, _Mat, _Mat, P, I, P, I, I]
         L.pi_cold_ffn_ex.restype = C.c_int
         L.pi_host_vector_path.restype = C.c_int
+        L.pi_host_read_probe.argtypes = [P, C.c_size_t, I, C.POINTER(C.c_uint64)]
+        L.pi_host_read_probe.restype = C.c_int
         L.pi_hybrid_layer.argtypes = [P, C.POINTER(_Layer), P, P, C.POINTER(_HostCold), I, P, C.c_float, P,
                                       C.POINTER(_HybridScratch), I, C.POINTER(C.c_int32)]
         L.pi_hybrid_layer.restype = C.c_int
@@ -105,6 +107,17 @@ def pi_cold_ffn(B: int, d: int, n_c: int, x, W1: Matrix, b1: Optional[Vector], W
 def vector_path() -> int:
     """1 when pi_cold_ffn runs its AVX2 + FMA + F16C loops on this CPU, 0 for the scalar ones."""
     return load().pi_host_vector_path()
+
+
+def pi_host_read_probe(buf, nbytes: int, threads: int = 0) -> int:
+    """Streaming read of nbytes of host memory at buf (address or numpy array) by `threads`
+    threads; returns the XOR of every 8-byte word read."""
+    out = C.c_uint64(0)
+    ptr = buf.ctypes.data if hasattr(buf, "ctypes") else buf
+    st = load().pi_host_read_probe(ptr, int(nbytes), int(threads), C.byref(out))
+    if st != PI_OK:
+        raise PiError(f"pi_host_read_probe: {_STATUS.get(st, st)}")
+    return int(out.value)
 
 
 def pi_hybrid_layer(stream: int, layer_c, T_g: int, T_c: Optional[int], cold_c, B: int, x: int, tau: float, y: int,

@@ -833,6 +833,24 @@ def hybrid_bench(cfg, specs, dls, steps, warmup):
             host.pi_cold_ffn(1, d, h.n_c, h.x_h, h.hl.W1, h.hl.b1, h.hl.W2, h.A_c_h, kc, y_h,
                              kind=pi_kind(cfg), Wup=h.hl.Wup)
     host_s = (time.perf_counter() - t2) * steps
+    # the host's own streaming read with the same threads, over a 2 GiB buffer (successive reads
+    # take different regions, as successive layers read different rows): the CPU side's reference
+    w_cold = wbytes(cfg.wdtype) * d * (2 if cfg.gated else 1)
+    fc1_bytes = float(np.mean(kcs)) * w_cold
+    span = 2**31
+    raw = np.ones(span // 8 + 8, np.uint64)
+    base = raw.ctypes.data + (-raw.ctypes.data % 64)
+    host_read = {}
+    for nb in (int(fc1_bytes) // 64 * 64, 256 * 2**20):
+        best = 0.0
+        for k in range(24):
+            off = (k * ((nb + 4095) // 4096 * 4096)) % (span - nb - 64)
+            t5 = time.perf_counter()
+            host.pi_host_read_probe(base + off, nb, 0)
+            best = max(best, nb / (time.perf_counter() - t5) / 1e9)
+        host_read[f"{nb / 1e6:.1f} MB"] = round(best, 1)
+    del raw
+    cold_gbps = fc1_bytes / (host_s / (steps * L)) / 1e9
     out = {"tokens_per_s": round(steps / el, 2), "ms_per_step": round(el * 1e3 / steps, 3), "steps": steps,
            "layers": L, "host_weights_gib": round(host_bytes / 2**30, 2),
            "cpu_threads": int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or os.cpu_count(),
@@ -841,7 +859,11 @@ def hybrid_bench(cfg, specs, dls, steps, warmup):
            "mean_K_c": float(np.mean(kcs)), "host_weight_setup_s": round(gen_s, 1),
            "lookahead_tokens_per_s": round(steps / el_ahead, 2), "lookahead_ms_per_step": round(el_ahead * 1e3 / steps, 3),
            "lookahead_native_tokens_per_s": round(steps / el_native, 2),
-           "lookahead_native_ms_per_step": round(el_native * 1e3 / steps, 3)}
+           "lookahead_native_ms_per_step": round(el_native * 1e3 / steps, 3),
+           "cold_fc1_bytes_per_layer": round(fc1_bytes), "cold_ffn_gbps_fc1_only": round(cold_gbps, 1),
+           "host_stream_read_gbps": host_read}
+    log(f"hybrid: host streaming read {host_read} GB/s; the cold FFN moves at least {out['cold_ffn_gbps_fc1_only']} "
+        f"GB/s (its FC1 rows alone)")
     log(f"hybrid: {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s, cold FFN on the CPU "
         f"{out['cpu_cold_ffn_us_per_layer']} us per layer (timed alone); with look-ahead prediction "
         f"{out['lookahead_ms_per_step']} ms/step, {out['lookahead_tokens_per_s']} tokens/s; in one native call per "

@@ -63,6 +63,16 @@ int pi_cold_ffn_ex(int32_t B, int32_t d, int32_t n_c, int32_t kind, const float*
 /* The path pi_cold_ffn takes on this CPU: 1 = AVX2 + FMA + F16C, 0 = scalar. */
 int pi_host_vector_path(void);
 
+/* The host streaming-read reference that the CPU side's bandwidth is read
+ * against: `threads` threads (<= 0: the OpenMP default) read `bytes` bytes of
+ * `buf` once, each a contiguous share of whole 64-byte lines, with 32-byte
+ * loads when the CPU has AVX2 (8-byte loads otherwise), and *out receives the
+ * XOR of every 8-byte word (so that no load can be dropped; the same for any
+ * thread count).  buf: host memory, 64-byte aligned; bytes a multiple of 64.
+ * Errors: PI_EINVAL for a NULL pointer, bytes == 0 or not a multiple of 64,
+ * or an unaligned buf. */
+int pi_host_read_probe(const void* buf, size_t bytes, int32_t threads, uint64_t* out);
+
 /* The CPU-resident neurons of one layer in HOST memory, rows in CPU-table slot
  * order (the arguments pi_cold_ffn takes). */
 typedef struct pi_host_cold {

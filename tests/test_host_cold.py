@@ -220,3 +220,29 @@ def test_hybrid_stack_rejects_bad_arguments():
     assert call(n=0) == pi.PI_EINVAL
     assert call(layers=None) == pi.PI_EINVAL
     assert call(xs=None) == pi.PI_EINVAL
+
+
+def _aligned_words(n_words, seed):
+    """uint64 words in a numpy buffer whose start is 64-byte aligned."""
+    raw = np.empty(n_words + 8, np.uint64)
+    off = (-raw.ctypes.data % 64) // 8
+    w = raw[off:off + n_words]
+    w[:] = np.random.default_rng(seed).integers(0, 2**63, n_words, dtype=np.uint64)
+    return raw, w
+
+
+@pytest.mark.parametrize("n_words,threads", [(8, 1), (8 * 1000, 3), (8 * 99991, 0), (8 * 4096, 16)])
+def test_host_read_probe_reads_every_word(n_words, threads):
+    raw, w = _aligned_words(n_words, n_words + threads)
+    want = int(np.bitwise_xor.reduce(w))
+    assert host.pi_host_read_probe(w.ctypes.data, w.nbytes, threads) == want
+    w[n_words // 2] ^= np.uint64(1 << 17)                 # one flipped bit changes the result
+    assert host.pi_host_read_probe(w.ctypes.data, w.nbytes, threads) == want ^ (1 << 17)
+
+
+def test_host_read_probe_argument_checks():
+    raw, w = _aligned_words(64, 5)
+    p = w.ctypes.data
+    for args in [(0, 64, 1), (p, 0, 1), (p, 96, 1), (p + 8, 64, 1)]:
+        with pytest.raises(pi.PiError):
+            host.pi_host_read_probe(*args)
