@@ -463,9 +463,9 @@ int pi_merge(void* stream, int32_t B, int32_t d, float* y, const float* y_c, con
 
 int pi_layer_norm(void* stream, int32_t B, int32_t d, const float* y, float eps, float* x) {
   if (B <= 0 || d <= 0 || d > (1 << 30) || !y || !x || !(eps >= 0.f) || !std::isfinite(eps)) return PI_EINVAL;
-  const int64_t n = (int64_t)B * d;
-  const float* x0 = x;
-  if (x0 != y && x0 < y + n && y < x0 + n) return PI_EINVAL;   // partial overlap
+  const uintptr_t nb = (uintptr_t)B * (uintptr_t)d * sizeof(float);
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
+  if (xa != ya && xa < ya + nb && ya < xa + nb) return PI_EINVAL;   // partial overlap
   return hip_status(pi::launch_layer_norm(B, d, y, eps, x, static_cast<hipStream_t>(stream)));
 }
 
