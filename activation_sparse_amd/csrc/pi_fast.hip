@@ -21,7 +21,6 @@
 #include "../../include/pi.h"
 #include "pi_device.h"
 #include "pi_b1.h"
-#include "pi_b1_dev.h"
 
 namespace pi {
 namespace {
@@ -55,6 +54,43 @@ __device__ __forceinline__ void load_xreg(const float* __restrict__ x, int nvec,
   }
 }
 
+// The 16-byte vectors one lane reads from one row (issued together), widened and
+// dotted with the lane's x slice later.
+template <int DT, int NV>
+struct LaneRow {
+  uint4 w[NV];
+  float sc[NV];
+  // rp: the row (wave-uniform; NULL = an absent row, which reads zeros), nvec
+  // 16-byte vectors long; sp: its int4 scales.  Lane vectors past the row end
+  // read zeros from the buffer range check: no clamped addresses, no branches,
+  // and nothing waits on these loads before the dot product.
+  __device__ __forceinline__ void issue(const char* rp, const uint16_t* sp, int nvec, int lane) {
+    const rsrc_t r = make_rsrc(uniform_ptr(rp), rp ? (uint32_t)nvec * 16u : 0u);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) w[u] = bload16(r, (uint32_t)(u * kWave + lane) * 16u);
+    if constexpr (DT == 2) {
+      const rsrc_t rs = make_rsrc(uniform_ptr(sp), sp ? (uint32_t)(nvec / 4) * 2u : 0u);
+#pragma unroll
+      for (int u = 0; u < NV; ++u) sc[u] = h2f(bload2(rs, (uint32_t)((u * kWave + lane) / 4) * 2u));
+    }
+    // keep every load of the row ahead of the code that consumes them
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ float dot(const float (&xr)[NV][Fmt<DT>::E]) const {
+    constexpr int E = Fmt<DT>::E;
+    float acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      float wf[E];
+      widen<DT>(w[u], DT == 2 ? sc[u] : 1.f, wf);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc = fmaf(wf[e], xr[u][e], acc);
+    }
+    return acc;
+  }
+};
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
 
 // h[j] = max(0, W[j].x + bias[j]) for j < rows: one row per wave.
 template <int DT, int NV, int BDT>
@@ -119,68 +155,150 @@ __global__ __launch_bounds__(kT) void k_fc1_b1(const void* __restrict__ W, const
   }
 }
 
-// Output layer (+ FC1) of one tile of 64 neuron ids [i0, i0 + 64):
+// Position of the r-th (0-based) set bit of x (r < popcount(x)): a popcount
+// descent without branches, so that no control flow separates loads that are
+// in flight from their uses.
+__device__ __forceinline__ int nth_set_bit64(uint64_t x, int r) {
+  int base = 0;
+#pragma unroll
+  for (int half = 32; half >= 1; half >>= 1) {
+    const uint64_t lowmask = (1ull << half) - 1ull;
+    const int c = __popcll(x & lowmask);
+    const bool up = r >= c;
+    r = up ? r - c : r;
+    x = up ? (x >> half) : x;
+    base = up ? base + half : base;
+  }
+  return base;
+}
+
+// Geometry of the output-layer tile kernel for T neuron ids per block.
+template <int T>
+struct TileGeom {
+  static constexpr int W = T / 8;                    // waves: 8 for 64 ids, 16 for 128 ids
+  static constexpr int NT = W * kWave;
+  static constexpr int NG = T / 64;                  // 64-id groups per tile
+  static constexpr int U = 16;                       // row loads in flight per lane (T=128: 1024 rows per pass)
+};
+
+__host__ __device__ constexpr size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+
+// Output layer (+ FC1) of one tile of T neuron ids [i0, i0 + T):
 //   z_i = c2_i + sum over hidden units m with h_m > 0 of h_m * P2[m, i]
 //   activation bit_i = z_i > tau   (ids >= N inactive)
 // and with FC1, for the tile's active GPU-resident neurons (activation AND the
 // prepared table's bitmap; slot = the table prefix of the 64-id group plus the
 // GPU-resident ids below it in the group):
 //   a = max(0, W1[slot].x + b1[slot]) (* Wup[slot].x when GATED)
-// The tile (one 64-id group) receives its ascending slot segment, its
+// Each 64-id group of the tile receives its ascending slot segment, its
 // ascending cold-slot segment, the (slot, a) pairs with a != 0 (the only FC2
 // rows that contribute) and the three counts.
-template <int PDT, int DT, int NV, bool GATED, int BDT, bool FC1>
-__global__ __launch_bounds__(kTileThreads) void k_pred_fc1(PredFc1Args a) {
-  using G = P2Geom<PDT>;
-  constexpr int U = G::U, LPR = G::LPR, RPL = G::RPL;
+template <int PDT, int DT, int NV, bool GATED, int BDT, int T, bool FC1>
+__global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
+  using G = TileGeom<T>;
+  constexpr int EP = Fmt<PDT>::E;      // output-layer weights per 16-byte vector
+  // row loads in flight per lane: int4 rows hold 32 weights per vector, so a quarter of
+  // the loads covers the same rows per pass (and keeps two blocks per compute unit)
+  constexpr int W = G::W, NT = G::NT, NG = G::NG, U = PDT == 2 ? G::U / 4 : G::U;
+  constexpr int LPR = T / EP;          // lanes that cover one row slice of the tile
+  constexpr int RPL = kWave / LPR;     // row slices per wave-wide load
+  constexpr int E = Fmt<DT>::E;        // FC1 weights per 16-byte vector
+  constexpr int P = E / 4;             // x planes
+  constexpr int XQ = (NV * kWave * P + NT - 1) / NT;   // x float4 per thread
   extern __shared__ __attribute__((aligned(16))) char pf_smem[];
-  __shared__ int s_cnt[kTileWaves];
-  __shared__ float red[kTileWaves][kTileIds];
-  __shared__ uint64_t s_M;
-  __shared__ float s_a[kTileIds];
-  __shared__ int s_slot[kTileIds];
+  __shared__ int s_cnt[W];
+  __shared__ float red[W][T];
+  __shared__ uint64_t s_M[NG];
+  __shared__ float s_a[T];
+  __shared__ int s_slot[T];
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const int H = a.H, N = a.N;
   const int ngroups = (N + 63) / 64;
-  const int tile = blockIdx.x;
+  const int64_t i0 = (int64_t)blockIdx.x * T;
   float4v* xs = reinterpret_cast<float4v*>(pf_smem);
 
   // ---- issue: table words, bias, x, h
-  const bool gin = FC1 && tile < ngroups;
-  const uint64_t Gb = gin ? ((uint64_t)a.gbits[2 * tile] | ((uint64_t)a.gbits[2 * tile + 1] << 32)) : 0ull;
-  const int gp = gin ? a.gpre[tile] : 0;
-  const int64_t id = (int64_t)tile * kTileIds + tid;
+  uint64_t Gb[NG];
+  int gp[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int grp = blockIdx.x * NG + g;
+    const bool in = FC1 && grp < ngroups;
+    Gb[g] = in ? ((uint64_t)a.gbits[2 * grp] | ((uint64_t)a.gbits[2 * grp + 1] << 32)) : 0ull;
+    gp[g] = in ? a.gpre[grp] : 0;
+  }
+  const int64_t id = i0 + tid;
   const Bias<BDT> c2_at(a.c2, (uint32_t)N);
-  const float c2v = c2_at(tid < kTileIds && id < N ? id : 0);
-  const int npad = FC1 ? x_npad(DT, a.d) : 0;
-  XStage<DT, NV, kTileThreads> xq;
-  if constexpr (FC1) xq.load(a.x, a.d);
-  // h of this lane's rows in the first pass; rows past H read 0.  The loads complete
-  // in issue order, so staging x below does not wait for them.
-  const int sub = lane / LPR;
+  const float c2v = c2_at(tid < T && id < N ? id : 0);
+  const int nvec = FC1 ? (int)(row_bytes(DT, a.d) / 16) : 0;
+  const int npad = (nvec + kWave - 1) & ~(kWave - 1);
+  float4v xq[FC1 ? XQ : 1];
+  if constexpr (FC1) {
+    const int nq = a.d / 4;
+    const float4v* x4 = reinterpret_cast<const float4v*>(a.x);
+#pragma unroll
+    for (int r = 0; r < XQ; ++r) {
+      const int q = r * NT + tid;
+      xq[r] = x4[q < nq ? q : 0];
+    }
+  }
+  // lane (sub, cl) reads slice vector cl of rows m = (i*W + wave)*RPL + sub of each
+  // pass of RP rows, and first its h[m]: rows with h[m] <= 0 get an offset past
+  // the buffer, which reads zeros without a memory request (no compaction, no
+  // barrier before the weight loads)
+  constexpr int RP = W * RPL * U;
+  const int sub = lane / LPR, cl = lane % LPR;
   const rsrc_t rH = make_rsrc(a.h, (uint32_t)H * 4u);
-  float hv0[U];
+  float hv[U];
 #pragma unroll
   for (int i = 0; i < U; ++i)
-    hv0[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rH, ((i * kTileWaves + wave) * RPL + sub) * 4, 0, 0));
-  if constexpr (FC1) xq.store(xs, a.d, npad);
+    hv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rH, ((i * W + wave) * RPL + sub) * 4, 0, 0));
+  if constexpr (FC1) {
+    // x in planes: plane p, index v holds x[E*v + 4p .. +3]
+    const int nq = a.d / 4;
+#pragma unroll
+    for (int r = 0; r < XQ; ++r) {
+      const int q = r * NT + tid;
+      if (q < nq) xs[(q % P) * npad + q / P] = xq[r];
+    }
+  }
 
   if constexpr (FC1) {
     // ---- look-ahead blocks: one row of the next layer's predictor hidden layer per wave, on
     // the x this block has staged (block-uniform branch)
-    if (a.nh && tile >= ngroups) {
+    const int ntiles = (N + T - 1) / T;
+    if (a.nh && (int)blockIdx.x >= ntiles) {
       __syncthreads();
-      const int m = (tile - ngroups) * kTileWaves + wave;
+      const int m = ((int)blockIdx.x - ntiles) * W + wave;
       if (m < a.nH) {
         const int64_t rb = row_bytes(DT, a.d);
-        const int nvec = (int)(rb / 16);
         const int groups = a.d / 128;
         const Bias<BDT> c1_at(a.nc1, (uint32_t)a.nH);
         LaneRow<DT, NV> rw;
         rw.issue(reinterpret_cast<const char*>(a.nP1) + (int64_t)m * rb, DT == 2 ? a.nP1s + (int64_t)m * groups : nullptr,
                  nvec, lane);
-        float z = wave_sum(lds_dot<DT, NV>(rw, xs, npad, 0, nvec, lane)) + c1_at(m);
+        float a0 = 0.f;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int v = u * kWave + lane;
+          const bool vin = v < nvec;
+          const int vc = vin ? v : 0;
+          float xv[E];
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const float4v t4 = xs[p * npad + vc];
+            xv[4 * p] = vin ? t4.x : 0.f; xv[4 * p + 1] = vin ? t4.y : 0.f;
+            xv[4 * p + 2] = vin ? t4.z : 0.f; xv[4 * p + 3] = vin ? t4.w : 0.f;
+          }
+          float wf[E];
+          widen<DT>(rw.w[u], DT == 2 ? rw.sc[u] : 1.f, wf);
+#pragma unroll
+          for (int e = 0; e < E; ++e) a0 = fmaf(wf[e], xv[e], a0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        float z = wave_sum(a0) + c1_at(m);
         z = z > 0.f ? z : 0.f;
         if (lane == 0) a.nh[m] = z;
       }
@@ -189,52 +307,191 @@ __global__ __launch_bounds__(kTileThreads) void k_pred_fc1(PredFc1Args a) {
   }
 
   // ---- output layer over the rows of positive hidden units
-  auto hload = [&](int m0, float (&hv)[U]) {
-    if (m0 == 0) {
+  {
+    const int64_t prb = row_bytes(PDT, N);
+    const int pvec = (int)(prb / 16);
+    int colv = blockIdx.x * LPR + cl;
+    colv = colv < pvec ? colv : pvec - 1;          // past the row end: discarded ids
+    const int pgroups = N / 128;
+    // the whole matrix as one buffer (the host keeps H * row bytes below 2^31)
+    const uint32_t pbytes = (uint32_t)(H * prb);
+    const rsrc_t rP = make_rsrc(a.P2, pbytes);
+    const rsrc_t rS = make_rsrc(PDT == 2 ? (const void*)a.P2s : a.P2, PDT == 2 ? (uint32_t)H * pgroups * 2u : 0u);
+    float acc[EP];
 #pragma unroll
-      for (int i = 0; i < U; ++i) hv[i] = hv0[i];
-    } else {
+    for (int e = 0; e < EP; ++e) acc[e] = 0.f;
+    int nact = 0;                                  // this lane's rows with h > 0 (counted where cl == 0)
+    for (int m0 = 0; m0 < H; m0 += RP) {
+      if (m0 > 0) {
 #pragma unroll
-      for (int i = 0; i < U; ++i)
-        hv[i] = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rH, (m0 + (i * kTileWaves + wave) * RPL + sub) * 4, 0, 0));
+        for (int i = 0; i < U; ++i)
+          hv[i] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rH, (m0 + (i * W + wave) * RPL + sub) * 4, 0, 0));
+      }
+      uint4 w[U];
+      float sc[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int m = m0 + (i * W + wave) * RPL + sub;
+        const bool ok = hv[i] > 0.f;               // rows past H read h = 0
+        nact += ok ? 1 : 0;
+        w[i] = bload16(rP, ok ? (uint32_t)m * (uint32_t)prb + (uint32_t)colv * 16u : pbytes);
+        if constexpr (PDT == 2) sc[i] = h2f(bload2(rS, ok ? (uint32_t)(m * pgroups + colv / 4) * 2u : 0xFFFFFFF0u));
+        else sc[i] = 1.f;
+      }
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const float hs = hv[i] > 0.f ? hv[i] : 0.f;
+        if constexpr (PDT == 2) {
+          // int4: the group scale folds into h once per row, and each weight is one
+          // signed bit-field extract, one convert and one fma
+          const float hsc = hs * sc[i];
+          const uint32_t wq[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+              acc[k * 8 + n] = fmaf((float)((int32_t)(wq[k] << (28 - 4 * n)) >> 28), hsc, acc[k * 8 + n]);
+        } else {
+          float wf[EP];
+          widen<PDT>(w[i], 1.f, wf);
+#pragma unroll
+          for (int e = 0; e < EP; ++e) acc[e] = fmaf(wf[e], hs, acc[e]);
+        }
+      }
     }
-  };
-  const int nact = p2_tile_partial<PDT>(a, tile, wave, lane, hload, red);
-  if (a.rows_read && tile == 0) {
-    int c = nact;
+    // the RPL row groups of the wave hold partial sums of the same ids: butterfly
+    // sum (every lane ends with the same bits)
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
-    if (lane == 0) s_cnt[wave] = c;
+    for (int off = LPR; off < kWave; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
+    if (sub == 0)
+#pragma unroll
+      for (int e = 0; e < EP; ++e) red[wave][cl * EP + e] = acc[e];
+    if (a.rows_read && blockIdx.x == 0) {
+      int c = cl == 0 ? nact : 0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
+      if (lane == 0) s_cnt[wave] = c;
+    }
   }
   __syncthreads();
-  if (a.rows_read && tile == 0 && tid == 0) {
+  if (a.rows_read && blockIdx.x == 0 && tid == 0) {
     int c = 0;
-    for (int w2 = 0; w2 < kTileWaves; ++w2) c += s_cnt[w2];
+    for (int w2 = 0; w2 < W; ++w2) c += s_cnt[w2];
     *a.rows_read = c;
   }
-  if (tid < kTileIds) {                // wave 0: the tile's 64 ids
+  if (tid < T) {                      // waves 0 .. NG-1, one per 64-id group
     float z = red[0][tid];
 #pragma unroll
-    for (int w2 = 1; w2 < kTileWaves; ++w2) z += red[w2][tid];
+    for (int w2 = 1; w2 < W; ++w2) z += red[w2][tid];
     z += c2v;
     const bool valid = id < N;
     if (a.logits && valid) a.logits[id] = z;
     const uint64_t bits = __ballot(valid && z > a.tau);
-    if (lane == 0) s_M = bits;
-    if (!FC1 && a.mask && lane == 0 && tile < ngroups) {
-      a.mask[2 * tile] = (uint32_t)bits;
-      a.mask[2 * tile + 1] = (uint32_t)(bits >> 32);
+    if (lane == 0) s_M[wave] = bits;
+    const int grp = blockIdx.x * NG + wave;
+    if (!FC1 && a.mask && lane == 0 && grp < ngroups) {
+      a.mask[2 * grp] = (uint32_t)bits;
+      a.mask[2 * grp + 1] = (uint32_t)(bits >> 32);
     }
   }
   if constexpr (!FC1) return;
   __syncthreads();
 
-  // ---- FC1 of the tile's active GPU-resident neurons, then the tile's segments
-  const uint64_t M = s_M;
-  fc1_tile_rows<DT, NV, GATED, BDT>(a, M & Gb, Gb, gp, xs, npad, wave, lane, s_slot, s_a);
+  // ---- FC1 of the tile's active GPU-resident neurons, row r by wave r % W
+  uint64_t act[NG];
+  int kg[NG];
+  int R = 0;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    act[g] = s_M[g] & Gb[g];
+    kg[g] = __popcll(act[g]);
+    R += kg[g];
+  }
+  {
+    const int64_t rb = row_bytes(DT, a.d);
+    const int groups = a.d / 128;
+    const Bias<BDT> b1_at(a.b1, (uint32_t)a.n_g);
+    const char* W1 = reinterpret_cast<const char*>(a.W1);
+    const char* Wu = reinterpret_cast<const char*>(a.Wu);
+    for (int r = wave; r < R; r += W) {
+      const int g = (NG == 2 && r >= kg[0]) ? 1 : 0;
+      const int t = g ? r - kg[0] : r;
+      const int sl = gp[g] + __popcll(Gb[g] & ((1ull << nth_set_bit64(act[g], t)) - 1ull));
+      // a table prepared from another T_g cannot index past W1
+      const int s = __builtin_amdgcn_readfirstlane(sl < a.n_g ? sl : -1);
+      const float bs = b1_at(s >= 0 ? s : 0);
+      LaneRow<DT, NV> rw, ru;
+      rw.issue(s >= 0 ? W1 + (int64_t)s * rb : nullptr, DT == 2 && s >= 0 ? a.W1s + (int64_t)s * groups : nullptr,
+               nvec, lane);
+      if constexpr (GATED)
+        ru.issue(s >= 0 ? Wu + (int64_t)s * rb : nullptr, DT == 2 && s >= 0 ? a.Wus + (int64_t)s * groups : nullptr,
+                 nvec, lane);
+      float a0 = 0.f, g0 = 0.f;
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const int v = u * kWave + lane;
+        const bool vin = v < nvec;
+        const int vc = vin ? v : 0;
+        float xv[E];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const float4v t4 = xs[p * npad + vc];
+          xv[4 * p] = vin ? t4.x : 0.f; xv[4 * p + 1] = vin ? t4.y : 0.f;
+          xv[4 * p + 2] = vin ? t4.z : 0.f; xv[4 * p + 3] = vin ? t4.w : 0.f;
+        }
+        float wf[E];
+        widen<DT>(rw.w[u], DT == 2 ? rw.sc[u] : 1.f, wf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) a0 = fmaf(wf[e], xv[e], a0);
+        if constexpr (GATED) {
+          widen<DT>(ru.w[u], DT == 2 ? ru.sc[u] : 1.f, wf);
+#pragma unroll
+          for (int e = 0; e < E; ++e) g0 = fmaf(wf[e], xv[e], g0);
+        }
+        // x is read from LDS vector by vector: keeps only the row's weights in
+        // registers (other waves cover the LDS latency)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float z = wave_sum(a0) + bs;
+      z = z > 0.f ? z : 0.f;
+      if constexpr (GATED) z *= wave_sum(g0);
+      if (lane == 0) {
+        s_slot[r] = s;
+        s_a[r] = s >= 0 ? z : 0.f;
+      }
+    }
+  }
   __syncthreads();
-  if (wave == 0 && tile < ngroups) write_tile_segments(a, tile, M, Gb, gp, s_slot, s_a, lane);
+
+  // ---- segments of each 64-id group, by wave g
+  if (wave < NG) {
+    const int g = wave;
+    const int grp = blockIdx.x * NG + g;
+    if (grp < ngroups) {
+      const int r0 = g == 0 ? 0 : kg[0];
+      const int k = kg[g];
+      const bool in = lane < k;
+      const int s = in ? s_slot[r0 + lane] : 0;
+      const float av = in ? s_a[r0 + lane] : 0.f;
+      const int64_t base = (int64_t)grp * 64;
+      const uint64_t lt = (1ull << lane) - 1ull;
+      if (in) a.seg_slot[base + lane] = s;
+      const bool nz = in && av != 0.f;
+      const uint64_t bn = __ballot(nz);
+      if (nz) {
+        const int p = __popcll(bn & lt);
+        a.pos_slot[base + p] = s;
+        a.pos_a[base + p] = av;
+      }
+      const uint64_t ac = s_M[g] & ~Gb[g];
+      if ((ac >> lane) & 1ull)
+        a.seg_cold[base + __popcll(ac & lt)] = (int32_t)(base + lane - (gp[g] + __popcll(Gb[g] & lt)));
+      if (lane == 0) a.cnt[grp] = (uint32_t)k | ((uint32_t)__popcll(ac) << 8) | ((uint32_t)__popcll(bn) << 16);
+    }
+  }
 }
 
 // Vectors-per-lane bound used for a row of nvec 16-byte vectors (0 = unsupported).
@@ -312,18 +569,25 @@ hipError_t fc1_dt(const B1Gemv& g, hipStream_t s) {
 // Tile width: 64 ids per block of 8 waves.  (128-id tiles of 16 waves measured
 // slower at the OPT-30B shape: two co-resident 64-id blocks per CU hide each
 // other's barrier waits.)
-template <int PDT, int DT, int NV, bool GATED, int BDT, bool FC1>
+constexpr int kTile = 64;
+
+template <int PDT, int DT, int NV, bool GATED, int BDT, int T, bool FC1>
 hipError_t pf_launch(const PredFc1Args& a, hipStream_t s) {
-  unsigned blocks = (unsigned)((a.N + kTileIds - 1) / kTileIds);
-  if (FC1 && a.nh) blocks += (unsigned)((a.nH + kTileWaves - 1) / kTileWaves);   // look-ahead rows, one per wave
-  const size_t shm = FC1 ? x_planes_bytes(DT, a.d) : 0;   // x in E/4 planes of float4 when FC1 runs
-  hipLaunchKernelGGL((k_pred_fc1<PDT, DT, NV, GATED, BDT, FC1>), dim3(blocks), dim3(kTileThreads), shm, s, a);
+  unsigned blocks = (unsigned)((a.N + T - 1) / T);
+  if (FC1 && a.nh) blocks += (unsigned)((a.nH + 7) / 8);   // look-ahead rows, T / 8 = 8 waves per block
+  size_t shm = 0;                     // x in E/4 planes of float4 when FC1 runs
+  if constexpr (FC1) {
+    const int nvec = (int)(row_bytes(DT, a.d) / 16);
+    const int npad = (nvec + kWave - 1) & ~(kWave - 1);
+    shm += (size_t)(Fmt<DT>::E / 4) * npad * 16;
+  }
+  hipLaunchKernelGGL((k_pred_fc1<PDT, DT, NV, GATED, BDT, T, FC1>), dim3(blocks), dim3(T * 8), shm, s, a);
   return hipGetLastError();
 }
 
 template <int PDT, int BDT>
 hipError_t pred_out_pdt(const PredFc1Args& a, hipStream_t s) {
-  return pf_launch<PDT, 0, 1, false, BDT, false>(a, s);
+  return pf_launch<PDT, 0, 1, false, BDT, kTile, false>(a, s);
 }
 
 // Fused kernels exist for these (output-layer dtype, FFN dtype, bias dtype)
@@ -333,7 +597,7 @@ hipError_t pred_out_pdt(const PredFc1Args& a, hipStream_t s) {
 template <int PDT, int DT, int BDT, bool GATED>
 hipError_t pred_fc1_combo(const PredFc1Args& a, hipStream_t s) {
   const int nv = pick_nv<DT>((int)(row_bytes(DT, a.d) / 16));
-#define PI_PF(NVV) return pf_launch<PDT, DT, NVV, GATED, BDT, true>(a, s)
+#define PI_PF(NVV) return pf_launch<PDT, DT, NVV, GATED, BDT, kTile, true>(a, s)
   switch (nv) {
     case 1: case 2: case 4: PI_PF(4);
     case 8: PI_PF(8);
