@@ -61,6 +61,11 @@ def parse():
     ap.add_argument("--lookahead-steps", type=int, default=16,
                     help="after the batch-1 measurement, time look-ahead prediction (layer L+1's predictor hidden "
                          "layer from layer L's input, beside layer L's FFN) over this many steps; 0 = skip")
+    ap.add_argument("--truth-steps", type=int, default=8,
+                    help="steps of the sensitivity run whose mask is the true activation set (0 = skip)")
+    ap.add_argument("--configs", default="opt-6.7b,llama-13b-gated,opt-175b-int4:4,opt-30b-rho20",
+                    help="other configurations timed at batch 1 (key or key:layer-stride; empty = skip)")
+    ap.add_argument("--config-steps", type=int, default=8)
     ap.add_argument("--chained-steps", type=int, default=16,
                     help="after the batch-1 measurement, time chained layers (layer L+1's input is the layer "
                          "normalisation of layer L's output, made on the GPU) over this many steps; 0 = skip")
@@ -633,6 +638,217 @@ def chained_bench(cfg, specs, dls, steps, warmup, B=1, eps=1e-5):
     return out
 
 
+def stack_timing(cfg, specs, dls, steps, warmup, B=1, c2_of=None):
+    """Times the exact batch-1 layer stack `specs` (one HIP graph per step, the headline's seeded
+    inputs and cold partials) and each stage set alone (back-to-back launches over the layers on the
+    state the last step left).  c2_of(t, L), when given, is the device pointer of the output bias to
+    use at step t and layer L (the truth-mode leg).  Returns the step time, the algorithmic bytes
+    from the kernels' own row counts, the dominant stage and the mean counts."""
+    import torch
+    import synth
+    import activation_sparse_amd as pi
+    dev = "cuda:0"
+    n_layers = len(specs)
+    maxH = max(s.H for s in specs)
+    n_g = max(s.n_g for s in specs)
+    n_c = max(len(s.T_c) for s in specs)
+    d, N = cfg.d, cfg.N
+    S = warmup + steps
+    ws_bytes = max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256)
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
+    xs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev)
+    ycs = torch.empty((S, n_layers, B, d), dtype=torch.float32, device=dev) if n_c else None
+    Ks = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    Kcs = torch.zeros((S, n_layers), dtype=torch.int32, device=dev)
+    rows = torch.zeros((S, n_layers, 2), dtype=torch.int32, device=dev)
+    y = torch.empty((B, d), dtype=torch.float32, device=dev)
+    A_g = torch.empty(max(n_g, 1), dtype=torch.int32, device=dev)
+    A_c = torch.empty(max(n_c, 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in range(S):
+        rid = torch.from_numpy(synth.x_row_ids(t, B)).to(dev)
+        for i, spec in enumerate(specs):
+            synth.dev_fill(xs[t, i].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_X, spec.layer, d, 1.0,
+                           row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+            if n_c:
+                synth.dev_fill(ycs[t, i].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_YC, spec.layer, d, 0.05,
+                               row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+    torch.cuda.synchronize()
+    structs = {}
+
+    def cstruct(t, i):
+        if c2_of is None:
+            return dls[i].layer_c
+        key = (t, i)
+        if key not in structs:
+            c = pi._Layer.from_buffer_copy(dls[i].layer_c)
+            c.c2 = pi._Vec(c2_of(t, i), c.c2.dtype)
+            structs[key] = c
+        return structs[key]
+
+    def call(t, i, stages, with_rows=True):
+        cold = len(specs[i].T_c) > 0
+        pi.pi_ffn_layer_stages(dls[i].layer, B, xs[t, i], 0.0, ycs[t, i] if cold else None, y, None, A_g,
+                               Ks[t, i:i + 1], A_c if cold else None, Kcs[t, i:i + 1] if cold else None, wss[i],
+                               stages, rows_read=rows[t, i] if with_rows else None, _cstruct=cstruct(t, i))
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n_layers):
+            call(0, i, pi.PI_STAGE_ALL)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for t in range(S):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_layers):
+                call(t, i, pi.PI_STAGE_ALL)
+        graphs.append(g)
+    for t in range(warmup):
+        graphs[t].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(warmup, S):
+        graphs[t].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del graphs
+    Kh, Kch, Rh = Ks.cpu().numpy(), Kcs.cpu().numpy(), rows.cpu().numpy()
+    tot = [0.0, 0.0, 0.0]
+    for t in range(warmup, S):
+        for i, spec in enumerate(specs):
+            for k, v in enumerate(layer_bytes(spec, B, int(Kh[t, i]), int(Kch[t, i]), int(Rh[t, i, 0]),
+                                              int(Rh[t, i, 1]))):
+                tot[k] += v
+    step_bytes = sum(tot) / steps
+    # each stage set alone, back to back over the layers, repeating the last step's work
+    last = S - 1
+    stage_sets = {"hidden": pi.PI_STAGE_HIDDEN, "output+fc1": pi.PI_STAGE_OUTPUT | pi.PI_STAGE_FC1,
+                  "fc2+lists": pi.PI_STAGE_FC2, "sum+merge": pi.PI_STAGE_SUM}
+    kb = [kernel_bytes(spec, B, int(Kh[last, i]), int(Kch[last, i]), int(Rh[last, i, 0]), int(Rh[last, i, 1]))
+          for i, spec in enumerate(specs)]
+    stage_us, stage_gbps = {}, {}
+    reps = 4
+    for name, bits in stage_sets.items():
+        # one HIP graph of `reps` passes over the layers, so that launch overhead is not timed
+        with torch.cuda.stream(side):
+            for i in range(n_layers):
+                call(last, i, bits, with_rows=False)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                for i in range(n_layers):
+                    call(last, i, bits, with_rows=False)
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n_layers)
+        stage_us[name] = round(us, 2)
+        stage_gbps[name] = round(float(np.mean([k[name] for k in kb])) / (us * 1e-6) / 1e9, 1)
+    dom = max(stage_us, key=stage_us.get)
+    out = {"ms_per_step_timed_layers": round(ms, 4), "layers_timed": n_layers, "step_bytes_timed_layers": round(step_bytes),
+           "step_gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+           "step_frac_of_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "bytes_split": {"predictor": round(tot[0] / steps), "ffn": round(tot[1] / steps), "small": round(tot[2] / steps)},
+           "mean_K": float(Kh[warmup:].mean()), "mean_K_cold": float(Kch[warmup:].mean()),
+           "mean_p2_rows_read": float(Rh[warmup:, :, 0].mean()), "mean_fc2_rows_read": float(Rh[warmup:, :, 1].mean()),
+           "stage_us_alone": stage_us, "stage_gbps_alone": stage_gbps,
+           "dominant_stage": dom, "dominant_frac_of_peak": round(stage_gbps[dom] / HBM_PEAK_GBS, 4), "steps": steps}
+    del wss, xs, ycs
+    return out
+
+
+# sentinel output biases of the truth-mode leg: far beyond any |P2 . h| of these workloads, inside fp16
+TRUTH_BIAS = 60000.0
+
+
+def truth_bench(cfg, specs, dls, steps, warmup):
+    """Sensitivity run with a predictor that is always right: the activation set of each (step,
+    layer) is the true one, z = W1 x + b1 > 0 over all N neurons (computed in fp32 by PyTorch from
+    the same stored fp16 weights, generated on the device), fed to the unchanged layer call through
+    its output bias (c2 = +TRUTH_BIAS where z > 0, -TRUTH_BIAS elsewhere) so that every predictor
+    weight is still read.  Every listed neuron then has a non-zero FC1 output, so FC2 reads them all.
+    Returns the stack timing, the true density and the GPU share of the true activations."""
+    import torch
+    import synth
+    from synth.device import dev_matrix, fill_matrix
+    dev = "cuda:0"
+    n_layers = len(specs)
+    d, N, B = cfg.d, cfg.N, 1
+    S = warmup + steps
+    c2s = torch.empty((S, n_layers, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    dens, share = [], []
+    x = torch.empty((S, B, d), dtype=torch.float32, device=dev)
+    all_ids = torch.arange(N, dtype=torch.int32, device=dev)
+    for i, spec in enumerate(specs):
+        for t in range(S):
+            rid = torch.from_numpy(synth.x_row_ids(t, B)).to(dev)
+            synth.dev_fill(x[t].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_X, spec.layer, d, 1.0,
+                           row_ids_ptr=rid.data_ptr(), nrows=B, stream=stream)
+        W1 = dev_matrix(N, d, cfg.wdtype, dev)
+        fill_matrix(W1, cfg.wdtype, cfg.seed, synth.TAG_W1, spec.layer, d, spec.sigmas()[synth.TAG_W1], all_ids, N)
+        b1 = torch.from_numpy(synth.stored_to_f64(spec.b1, cfg.bdtype)).to(dev).float()
+        W1f = W1.data.float()                                                   # [N, d]
+        z = torch.matmul(W1f, x[:, 0, :].t().contiguous()).t() + b1             # [S, N]
+        act = z > 0
+        c2s[:, i, :] = torch.where(act, TRUTH_BIAS, -TRUTH_BIAS).to(torch.float16)
+        g = torch.zeros(N, dtype=torch.bool, device=dev)
+        g[torch.from_numpy(spec.T_g.astype(np.int64)).to(dev)] = True
+        dens.append(float(act[warmup:].float().mean()))
+        share.append(float((act[warmup:] & g).float().sum() / max(1.0, float(act[warmup:].float().sum()))))
+        del W1, W1f, z
+    torch.cuda.synchronize()
+    out = stack_timing(cfg, specs, dls, steps, warmup, c2_of=lambda t, i: c2s[t, i].data_ptr())
+    out.update({"tokens_per_s": round(1e3 / out["ms_per_step_timed_layers"], 2),
+                "true_density": round(float(np.mean(dens)), 4),
+                "gpu_share_of_true_activations": round(float(np.mean(share)), 4),
+                "mask": "true activations z = W1 x + b1 > 0 (fp32, PyTorch), fed through the output bias"})
+    del c2s
+    return out
+
+
+def config_bench(key, steps, warmup, stride=1, cpu_seconds=4.0):
+    """One configuration at batch 1: its own layer stack (every `stride`-th layer when stride > 1,
+    which keeps the spread of per-layer densities and hidden sizes; tokens/s then scales the mean
+    per-layer time to every layer), the stage timings and a bounded oracle baseline."""
+    import torch
+    import synth
+    from synth.device import DeviceLayer
+    cfg = synth.CONFIGS[key]
+    t0 = time.time()
+    layers = list(range(0, cfg.n_layers, stride))
+    specs = [synth.layer_spec(cfg, L) for L in layers]
+    dls = [DeviceLayer(s, "cuda:0") for s in specs]
+    torch.cuda.synchronize()
+    out = stack_timing(cfg, specs, dls, steps, warmup)
+    scale = cfg.n_layers / len(layers)
+    ms = out["ms_per_step_timed_layers"] * scale
+    out.update({"workload": cfg.desc, "layers": cfg.n_layers, "layers_timed": len(layers),
+                "layer_stride": stride, "tokens_per_s": round(1e3 / ms, 2), "ms_per_step": round(ms, 4),
+                "step_bytes": round(out["step_bytes_timed_layers"] * scale),
+                "mean_predictor_hidden": float(np.mean([s.H for s in specs])),
+                "mean_density": round(float(np.mean([s.rho for s in specs])), 4)})
+    del dls
+    torch.cuda.empty_cache()
+    out["cpu_baseline"] = cpu_baseline(cfg, 1, cpu_seconds, 2)
+    out["setup_and_run_s"] = round(time.time() - t0, 1)
+    log(f"config {key}: {out['tokens_per_s']} tokens/s ({out['ms_per_step']} ms/step over {cfg.n_layers} layers, "
+        f"{out['layers_timed']} timed), step frac {out['step_frac_of_peak']}, dominant {out['dominant_stage']} at "
+        f"{out['dominant_frac_of_peak']}")
+    return out
+
+
 def i4pred_bench(cfg, specs, dls, steps, warmup):
     """Predictor-cost variant: the same stack, inputs and FFN weights with int4-g128 predictor
     weights (P1 as int4 rows; P2's fp16 values quantised hidden-major, groups along N), through
@@ -1003,56 +1219,51 @@ def main():
             dense_bytes += p + f + sm
     dense_bytes /= args.steps
 
-    # per-stage durations: pi_ffn_layer records events between its kernels, over a few eager steps
-    # (each layer call synchronised, so every interval holds one kernel and its launch)
-    kern_ms = {k: [] for k in STAGES}
-    kern_bytes = {k: [] for k in STAGES}
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    handles = pi.event_handles(evs)
-    n_inst = min(4, S)
-    for t in range(S - n_inst, S):
-        for L in range(n_layers):
-            layer_call(t, L, events=handles)
-            torch.cuda.synchronize()
-            iv = [evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[3]), evs[3].elapsed_time(evs[4]),
-                  evs[4].elapsed_time(evs[5])]
-            for k, v in zip(STAGES, iv):
-                kern_ms[k].append(v)
-            r = rows[t, L].cpu().numpy()
-            kb = kernel_bytes(specs[L], B, int(Ks[t, L].item()), int(Kcs[t, L].item()), int(r[0]), int(r[1]))
-            for k in STAGES:
-                kern_bytes[k].append(kb[k])
-    mean_ms = {k: float(np.mean(v)) for k, v in kern_ms.items()}
-    mean_bytes = {k: float(np.mean(v)) for k, v in kern_bytes.items()}
-    achieved = {k: (mean_bytes[k] / (mean_ms[k] * 1e-3) / 1e9 if mean_ms[k] > 0 else 0.0) for k in STAGES}
-    # The dominant kernel (predictor output layer + activation decision + FC1, one launch per layer)
-    # timed on its own: re-run alone, back to back over the layers between two events on the launch
-    # stream, on the state the last step left in each layer's workspace (so each launch repeats that
-    # step's work exactly and its bytes are that step's).
-    dom = "output+fc1"
+    # per-stage durations: each stage set re-run alone, back to back over the layers in one HIP graph
+    # (launch overhead not timed) between two events on the launch stream, on the state the last
+    # step left in each layer's workspace (so each launch repeats that step's work exactly and its
+    # bytes are that step's).  At batch 1 the output layer, the activation decision and FC1 are
+    # one kernel (the dominant one).
     last = S - 1
-    dom_bytes = float(np.mean([kernel_bytes(specs[L], B, int(Kh[last, L]), int(Kch[last, L]), int(Rh[last, L, 0]),
-                                            int(Rh[last, L, 1]))[dom] for L in range(n_layers)]))
-
-    # at batch 1 one kernel; at larger batches the output layer, the lists and FC1 (several kernels)
-    dom_stages = pi.PI_STAGE_OUTPUT if B == 1 else (pi.PI_STAGE_OUTPUT | pi.PI_STAGE_FC1)
-
-    def dom_pass():
-        for L in range(n_layers):
-            layer_call(last, L, stages=dom_stages)
-    dom_pass()
-    torch.cuda.synchronize()
-    reps = 5
     d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record()
-    for _ in range(reps):
-        dom_pass()
-    d1.record()
-    torch.cuda.synchronize()
+
+    def stage_graph_ms(bits, reps):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for L in range(n_layers):
+                layer_call(last, L, stages=bits)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                for L in range(n_layers):
+                    layer_call(last, L, stages=bits)
+        g.replay()
+        torch.cuda.synchronize()
+        d0.record()
+        g.replay()
+        d1.record()
+        torch.cuda.synchronize()
+        del g
+        return d0.elapsed_time(d1) / (reps * n_layers)
+
+    stage_bits = {"hidden": pi.PI_STAGE_HIDDEN,
+                  "output+fc1": pi.PI_STAGE_OUTPUT if B == 1 else (pi.PI_STAGE_OUTPUT | pi.PI_STAGE_FC1),
+                  "fc2+lists": pi.PI_STAGE_FC2, "sum+merge": pi.PI_STAGE_SUM}
+    kb_last = [kernel_bytes(specs[L], B, int(Kh[last, L]), int(Kch[last, L]), int(Rh[last, L, 0]), int(Rh[last, L, 1]))
+               for L in range(n_layers)]
+    mean_ms = {k: stage_graph_ms(b, 5) for k, b in stage_bits.items()}
+    mean_bytes = {k: float(np.mean([kb[k] for kb in kb_last])) for k in STAGES}
+    achieved = {k: (mean_bytes[k] / (mean_ms[k] * 1e-3) / 1e9 if mean_ms[k] > 0 else 0.0) for k in STAGES}
+    # the dominant kernel, timed on its own as above
+    dom = "output+fc1"
     iso = dom + " (isolated)"
-    mean_ms[iso] = d0.elapsed_time(d1) / (reps * n_layers)
-    mean_bytes[iso] = dom_bytes
-    achieved[iso] = dom_bytes / (mean_ms[iso] * 1e-3) / 1e9
+    mean_ms[iso] = mean_ms[dom]
+    mean_bytes[iso] = mean_bytes[dom]
+    achieved[iso] = achieved[dom]
+    dom_bytes = mean_bytes[dom]
     traffic = committed_traffic(DOMINANT) if (cfg.key == "opt-30b" and B == 1) else None
     roofline = {"bound": "hbm", "achieved": round(achieved[iso], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved[iso] / HBM_PEAK_GBS, 4),
@@ -1117,6 +1328,18 @@ def main():
         log("chained layers ...")
         chained = chained_bench(cfg, specs, dls, args.chained_steps, 3)
 
+    truth = None
+    if args.truth_steps > 0 and B == 1 and cfg.wdtype != 2:
+        log("truth mode (the true activation set as the mask) ...")
+        truth = truth_bench(cfg, specs, dls, args.truth_steps, 2)
+        log(f"truth mode: {truth['tokens_per_s']} tokens/s, FC2 rows read {truth['mean_fc2_rows_read']:.0f} of "
+            f"{truth['mean_K']:.0f} listed, true density {truth['true_density']}")
+
+    configs = {}
+    for item in [v for v in args.configs.split(",") if v.strip()] if B == 1 else []:
+        key, _, stride = item.partition(":")
+        configs[key] = config_bench(key, args.config_steps, 2, int(stride or 1))
+
     placement = None
     if args.placement and B == 1:
         log("placement solver (host) ...")
@@ -1164,7 +1387,8 @@ def main():
                    "stream_read_gbps": stream_read,
                    "dominant_frac_of_stream_read": round(achieved[iso] / dom_ref, 4),
                    "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead, "chained": chained, "int4_predictor": i4pred,
-                   "placement": placement},
+                   "placement": placement, "truth": truth, "rho20": configs.pop("opt-30b-rho20", None),
+                   "configs": configs or None},
     }
     print(json.dumps(out), flush=True)
 

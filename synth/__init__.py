@@ -162,6 +162,13 @@ CONFIGS["opt-30b-i4pred"] = Config(
     (1,), 64, 4)
 
 
+# The OPT-30B stack at density 0.20 (the summary's background figure of about 80% of OPT-30B's
+# neurons inactive), for the sensitivity of the batch-1 throughput to the density.
+CONFIGS["opt-30b-rho20"] = Config(
+    "opt-30b-rho20", "OPT-30B-shaped FFN stack, 48 layers, 7168/28672, fp16, density 0.20, 40% of neurons on the GPU",
+    48, 7168, 28672, F16, F16, F16, False, (0.20, 0.20), 1.1, (1024, 1024), 0.4, (1,), 64, 4)
+
+
 def i4_quantize_rows(bits16: np.ndarray):
     """fp16 values [rows, cols] (uint16 bits), cols a multiple of 128 -> int4-g128 rows: per
     group of 128 the scale s = fp16(max|w| / 7) and q = clamp(rint(w / s), -8, 7), both in fp32
