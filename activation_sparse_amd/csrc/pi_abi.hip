@@ -29,6 +29,12 @@ bool valid_vector(const pi_vector& v) { return !v.data || v.dtype == PI_F32 || v
 
 bool valid_batch(int32_t B) { return B >= 1 && B <= PI_MAX_BATCH; }
 
+// Two byte ranges [a, a + na) and [b, b + nb) share a byte (compared as integer addresses).
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return PI_OK;
   g_last_hip_error = (int32_t)e;
@@ -608,7 +614,10 @@ int pi_ffn_layer_ahead(void* stream, const pi_layer* L, int32_t B, const float* 
   if (!ws_next || !aligned16(ws_next)) return PI_EWORKSPACE;
   const LayerWs wn = layer_ws_layout(ws_next, B, next->d, next->H, next->N, next->n_g);
   if (ws_next_bytes < wn.bytes) return PI_EWORKSPACE;
-  if (ws_next == ws) return PI_EINVAL;                  // the next layer's h would overwrite this one's
+  // the next layer's h must not overwrite this one's workspace, and the next layer's hidden layer,
+  // which may run after this layer's y is written, must still read this layer's input
+  if (ranges_overlap(ws, ws_bytes, ws_next, wn.bytes)) return PI_EINVAL;
+  if (L->d > 0 && valid_batch(B) && ranges_overlap(x, (size_t)B * L->d * 4, y, (size_t)B * L->d * 4)) return PI_EINVAL;
   Ahead ah{next, wn.h, wn.partials, h_layout(B, next->d, next->H, next->N, next->P1, next->P2)};
   return layer_stages(stream, L, B, x, tau, y_c, y, logits, A_g, K, A_c, K_c, ws, ws_bytes, nullptr, stages, nullptr,
                       &ah);

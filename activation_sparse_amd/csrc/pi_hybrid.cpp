@@ -111,6 +111,9 @@ extern "C" int pi_hybrid_layer_ahead(void* stream, const pi_layer* L, const pi_h
   const int cur = s->cur, nxt = 1 - cur;
   const int32_t d = L->d;
   const size_t xb = (size_t)B * d * sizeof(float);
+  // the next layer is predicted from x after this layer's output is written: y must not overlap x
+  const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
+  if (d > 0 && xa < ya + xb && ya < xa + xb) return PI_EINVAL;
   if (K_c_out) *K_c_out = 0;
   int r;
   if ((r = hip_ok(hipMemcpyAsync(s->x_host, x, xb, hipMemcpyDeviceToHost, st))) != PI_OK) return r;

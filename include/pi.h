@@ -41,8 +41,9 @@
  *    this thread's last failure).  Device faults surface at the caller's next
  *    synchronisation.  No entry point prints, aborts or throws.
  *  - Results are bitwise repeatable: the same inputs give the same bits.
- *  - The library holds no mutable global state; calls on different streams
- *    with disjoint outputs and workspaces may run concurrently.
+ *  - The library holds no mutable global state other than each thread's
+ *    last HIP error (pi_last_hip_error); calls on different streams with
+ *    disjoint outputs and workspaces may run concurrently.
  */
 #ifndef PI_H
 #define PI_H
@@ -90,8 +91,9 @@ typedef struct pi_vector {
  * logits [B x N] fp32, written.   h lives in the workspace.
  * Precision: fp32 accumulation.  With fp16 weights and B >= 2 the matrix
  * cores take x and h each as two fp16 parts, hi = fp16(v) and lo =
- * fp16(v - hi) (about 22 bits; every product exact), so |x| must stay below
- * 65504.
+ * fp16(v - hi) (about 22 bits; every product exact), so |x| and |h| must
+ * stay below 65504, fp16's largest value: a larger value becomes infinite,
+ * and so do the logits it reaches.
  * ws: at least pi_workspace_bytes(PI_OP_PREDICT, B, d, H, N, 0) bytes.
  * Errors: PI_EINVAL for a NULL required pointer, B outside 1..PI_MAX_BATCH,
  * a non-positive size, a column count the dtype forbids (d for P1, N for P2)
@@ -140,11 +142,12 @@ int pi_compact(void* stream, int32_t B, int32_t N, const float* logits, float ta
  * x [B x d] fp32; b1 [n_g]; y_g [B x d] fp32, fully written (zero if K = 0).
  * A_g entries must be < n_g; *K <= n_g.
  * Precision: accumulation is fp32.  With fp16 weights and B >= 2 the matrix
- * cores take x rounded to fp16 for FC1 and a rounded to fp16 for FC2 (each
- * product of two fp16 values is exact), so |x| must stay below 65504; the
+ * cores take x rounded to fp16 for FC1, and from B >= 3 the FC1 outputs a
+ * (after the gate's product) rounded to fp16 for FC2 (each product of two
+ * fp16 values is exact), so |x| and |a| must stay below 65504, fp16's
+ * largest value: a larger value becomes infinite, and so does y.  The
  * predictor's logits keep near-fp32 precision (x and h enter it as two fp16
- * parts each).
- * Other cases use fp32 products.
+ * parts each).  Other cases use fp32 products.
  * ws: at least pi_workspace_bytes(PI_OP_SPARSE_FFN, B, d, 0, 0, n_g) bytes.
  * Errors: as pi_predict, plus PI_EINVAL for a kind outside PI_RELU /
  * PI_GATED_RELU or a gated call without Wup, and PI_EUNSUPPORTED when W1,
@@ -265,8 +268,11 @@ int pi_ffn_layer_stages(void* stream, const pi_layer* layer, int32_t B, const fl
  * next: d equal to layer->d; its P1, c1, H, N and n_g are used.  ws_next:
  * pi_workspace_bytes(PI_OP_FFN_LAYER, B, d, next->H, next->N, next->n_g)
  * bytes, not ws.
+ * x and y may not overlap (the next layer's hidden layer can run after y is
+ * written), and neither may ws and ws_next (compared as byte ranges).
  * Errors: as pi_ffn_layer_stages; PI_EINVAL for a NULL next, another d, a bad
- * P1 / c1 of next, or ws_next == ws; PI_EWORKSPACE for a short ws_next. */
+ * P1 / c1 of next, x overlapping y, or ws overlapping ws_next; PI_EWORKSPACE
+ * for a short ws_next. */
 int pi_ffn_layer_ahead(void* stream, const pi_layer* layer, int32_t B, const float* x, float tau,
                        const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
                        int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, uint32_t stages,

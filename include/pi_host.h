@@ -167,10 +167,13 @@ typedef struct pi_hybrid_ahead_scratch {
  * The GPU's predictor work thus leaves the path between two layers: the
  * thread waits only for the copy of x.  cold: the CPU rows of `layer` (NULL:
  * none).  Returns with the merge enqueued; *K_c_out (optional) gets K_c.
+ * y may not overlap x (the next layer is predicted from x after y is
+ * written).
  * Errors: PI_EINVAL for a NULL required pointer or buffer, B outside
- * 1..PI_MAX_BATCH, or cur outside 0..1; those of the calls it makes; PI_EHIP
- * when a copy, an event record or a wait fails.  After an error the list sets
- * may be partly written: call pi_hybrid_prime again before the next layer. */
+ * 1..PI_MAX_BATCH, cur outside 0..1, or y overlapping x; those of the calls it
+ * makes; PI_EHIP when a copy, an event record or a wait fails.  After an error
+ * the list sets may be partly written: call pi_hybrid_prime again before the
+ * next layer. */
 int pi_hybrid_prime(void* stream, const pi_layer* layer, const int32_t* T_g, const int32_t* T_c, int32_t n_c,
                     int32_t B, const float* x, float tau, pi_hybrid_ahead_scratch* scratch);
 int pi_hybrid_layer_ahead(void* stream, const pi_layer* layer, const pi_host_cold* cold, const pi_layer* next,

@@ -145,13 +145,17 @@ def test_ffn_layer_ahead_rejects_bad_arguments():
     L = _layer()
     ws = 1 << 30
 
-    def call(next_layer=L, ws_next=FAKE + (1 << 24), nbytes=ws, layer=L):
-        return status(pi.pi_ffn_layer_ahead, layer, 1, FAKE, 0.0, None, FAKE, None, FAKE, FAKE, None, None, FAKE,
+    X, Y, WS = FAKE, FAKE + (1 << 20), FAKE + (1 << 24)
+
+    def call(next_layer=L, ws_next=WS + 2 * ws, nbytes=ws, layer=L, y=Y):
+        return status(pi.pi_ffn_layer_ahead, layer, 1, X, 0.0, None, y, None, FAKE, FAKE, None, None, WS,
                       pi.PI_STAGE_ALL, next_layer, ws_next, ws, nbytes, 0)
 
     assert call(next_layer=_layer(d=512)) == pi.PI_EINVAL          # another d
     assert call(next_layer=_layer(n_g=2048)) == pi.PI_EINVAL       # more GPU neurons than N
-    assert call(ws_next=FAKE) == pi.PI_EINVAL                      # the same workspace
+    assert call(ws_next=WS) == pi.PI_EINVAL                        # the same workspace
+    assert call(ws_next=WS + 4096) == pi.PI_EINVAL                 # a workspace overlapping the other
+    assert call(y=X) == pi.PI_EINVAL and call(y=X + 512) == pi.PI_EINVAL   # y overlapping x (1 KB)
     assert call(ws_next=None) == pi.PI_EWORKSPACE
     assert call(nbytes=64) == pi.PI_EWORKSPACE
     assert call(layer=_layer(N=1020)) == pi.PI_EINVAL              # this layer's own checks still apply

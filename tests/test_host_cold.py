@@ -188,13 +188,14 @@ def test_lookahead_hybrid_rejects_bad_arguments():
     def prime(s=full, n_c=10, T_c=FAKE, B=1):
         return L.pi_hybrid_prime(0, C.byref(lay), FAKE, T_c, n_c, B, FAKE, 0.0, C.byref(s))
 
-    def ahead(s=full, nxt=lay, T_g_next=FAKE, B=1, y=FAKE):
+    def ahead(s=full, nxt=lay, T_g_next=FAKE, B=1, y=FAKE + (1 << 24)):
         return L.pi_hybrid_layer_ahead(0, C.byref(lay), None, C.byref(nxt) if nxt is not None else None, T_g_next,
                                        FAKE, 10, B, FAKE, 0.0, y, C.byref(s), 0, None)
 
     assert prime(n_c=-1) == pi.PI_EINVAL and prime(T_c=None) == pi.PI_EINVAL and prime(B=0) == pi.PI_EINVAL
     assert ahead(T_g_next=None) == pi.PI_EINVAL and ahead(y=None) == pi.PI_EINVAL
     assert ahead(B=pi.PI_MAX_BATCH + 1) == pi.PI_EINVAL
+    assert ahead(y=FAKE) == pi.PI_EINVAL and ahead(y=FAKE + 512) == pi.PI_EINVAL   # y overlapping x (1 KB)
     bad = host._HybridAheadScratch.from_buffer_copy(full)
     bad.cur = 2
     assert prime(s=bad) == pi.PI_EINVAL and ahead(s=bad) == pi.PI_EINVAL

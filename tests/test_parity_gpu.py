@@ -145,8 +145,14 @@ def test_outputs_are_bitwise_repeatable():
 
 # --------------------------------------------------------------------------- full-size workloads, one layer each
 
+# The layers whose density and predictor hidden size are the smallest and largest of their stack
+# (LLaMA-13B-gated: layer 3, rho 0.113 / H 640, and layer 14, rho 0.206 / H 960; OPT-175B-int4:
+# layer 15, rho 0.056 / H 1408, and layer 14, rho 0.090 / H 3520) are among them; tests/test_synth.py
+# checks that they still are.
+EXTREME_LAYERS = {"llama-13b-gated": (3, 14), "opt-175b-int4": (15, 14)}
 FULL = [("opt-768", 0, 1), ("opt-6.7b", 5, 1), ("llama-13b-gated", 7, 1), ("opt-30b", 3, 1), ("opt-30b", 3, 4),
         ("opt-30b", 11, 16), ("opt-30b", 11, 32), ("opt-175b-int4", 42, 1), ("opt-30b-i4pred", 3, 1)]
+FULL += [(k, l, 1) for k, ls in EXTREME_LAYERS.items() for l in ls]
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
@@ -154,6 +160,18 @@ FULL = [("opt-768", 0, 1), ("opt-6.7b", 5, 1), ("llama-13b-gated", 7, 1), ("opt-
 def test_full_size_layer_parity(key, layer, B, fused):
     _dev()
     _run(synth.CONFIGS[key], layer=layer, step=3, B=B, fused=fused)
+
+
+# A seeded sample of the OPT-30B stack's (step, layer) pairs of the benchmark (64 steps, 48 layers):
+# numpy.random.default_rng(2026), four pairs at batch 1, then two at batch 32.
+SAMPLED = [(54, 17, 1), (11, 22, 1), (1, 3, 1), (40, 17, 1), (41, 39, 32), (22, 37, 32)]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("step,layer,B", SAMPLED, ids=[f"S{s}-L{l}-B{b}" for s, l, b in SAMPLED])
+def test_opt30b_sampled_step_layer_parity(step, layer, B, fused):
+    _dev()
+    _run(synth.CONFIGS["opt-30b"], layer=layer, step=step, B=B, fused=fused)
 
 
 @pytest.mark.parametrize("B", [1, 3])
@@ -190,3 +208,40 @@ def test_predict_output_logits_and_mask(cfg, B):
     assert not tail.any()
     near = np.min(np.abs(ref), axis=0) <= ph.BAND
     assert np.array_equal(bits[~near], (ref > 0).any(axis=0)[~near])
+
+
+# --------------------------------------------------------------------------- fp16 range of the matrix-core path
+
+def test_matrix_core_activations_near_the_fp16_range():
+    """At batch >= 3 with fp16 weights, FC2 on the matrix cores takes the FC1 outputs a rounded to fp16
+    (and the predictor's output layer takes h as two fp16 parts), so pi.h bounds |a| and |h| by fp16's
+    largest value, 65504.  A gated layer at batch 4 with its inputs scaled by 40 drives a into the tens
+    of thousands (checked on the oracle's own FC1 outputs), and the result stays within the parity
+    bounds, the logits' absolute bound scaled with the inputs."""
+    torch = _dev()
+    import oracle as orc
+    cfg = SMALL[4]                       # gated fp16, d=512, N=1536
+    assert cfg.gated and cfg.wdtype == synth.F16
+    B, scale = 4, 40.0
+    x = synth.host_x(cfg.seed, 0, 0, B, cfg.d) * np.float32(scale)
+    r = ph.run_layer_parity(cfg, layer=0, step=0, B=B, x_override=x, fused=True)
+    print(f"[parity] large inputs -> {r}", flush=True)
+    assert r["ascending"] and r["list_outside_band"] == 0, r
+    assert r["logit_max_abs_err"] <= ph.LOGIT_ATOL * scale, r
+    assert r["rel_err_ffn"] <= ph.RTOL and r["rel_err"] <= ph.RTOL, r
+    # the oracle's FC1 outputs over the predicted GPU-resident neurons
+    spec = synth.layer_spec(cfg, 0)
+    logits, _ = ph.oracle_predict(spec, x)
+    A_g, _ = orc.compact(logits, 0.0, spec.T_g, None)
+    ids = spec.T_g[A_g]
+    sig = spec.sigmas()
+    w1 = synth.host_rows(synth.F16, cfg.seed, synth.TAG_W1, 0, cfg.d, sig[synth.TAG_W1], row_ids=ids)[0]
+    wu = synth.host_rows(synth.F16, cfg.seed, synth.TAG_WUP, 0, cfg.d, sig[synth.TAG_WUP], row_ids=ids)[0]
+    w1 = w1.view(np.float16).astype(np.float64)
+    wu = wu.view(np.float16).astype(np.float64)
+    b1 = synth.stored_to_f64(spec.b1[ids], cfg.bdtype)
+    z = x.astype(np.float64) @ w1.T + b1
+    a = np.maximum(z, 0.0) * (x.astype(np.float64) @ wu.T)
+    a_max = float(np.max(np.abs(a)))
+    print(f"[parity] largest |a| = {a_max:.1f}", flush=True)
+    assert 1e4 <= a_max < 65504.0, a_max

@@ -125,3 +125,15 @@ def test_int4_quantiser_rule_and_packing():
     q0 = int(packed[4, 3] & 0xF)                       # element 6 (even): low nibble
     q1 = int(packed[4, 3] >> 4)                        # element 7 (odd): high nibble, the -0.5
     assert (q1 - 16 if q1 >= 8 else q1) == -7 and v[4, 6] == ((q0 - 16 if q0 >= 8 else q0) * s[4, 0])
+
+
+def test_extreme_layers_of_the_parity_cases():
+    """The full-size parity cases name the layers of smallest and largest density (and predictor
+    hidden size) of the stacks whose layers vary; they must still be those layers."""
+    from tests.test_parity_gpu import EXTREME_LAYERS
+    for key, (lo, hi) in EXTREME_LAYERS.items():
+        cfg = synth.CONFIGS[key]
+        rho = np.array([cfg.rho(L) for L in range(cfg.n_layers)])
+        H = np.array([cfg.hidden(L) for L in range(cfg.n_layers)])
+        assert int(rho.argmin()) == lo and int(rho.argmax()) == hi
+        assert H[lo] == H.min() and H[hi] == H.max()
