@@ -28,7 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libpi.so")
 EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes",
            "pi_table_prepare", "pi_ffn_layer", "pi_ffn_layer_stages", "pi_workspace_bytes", "pi_status_string",
            "pi_last_hip_error", "pi_abi_version", "pi_read_probe", "pi_ffn_layer_ahead",
-           "pi_layer_norm")
+           "pi_layer_norm", "pi_ffn_layer_static")
+PI_STATIC_WORKSPACE_BYTES = 16 << 20
 
 
 class PiError(RuntimeError):
@@ -76,6 +77,8 @@ def load():
         L.pi_table_prepare.restype = C.c_int
         L.pi_ffn_layer.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P, P, C.c_size_t, P]
         L.pi_ffn_layer.restype = C.c_int
+        L.pi_ffn_layer_static.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P]
+        L.pi_ffn_layer_static.restype = C.c_int
         L.pi_ffn_layer_stages.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P, P, C.c_size_t, P,
                                           C.c_uint32, P]
         L.pi_ffn_layer_stages.restype = C.c_int
@@ -254,6 +257,14 @@ def pi_ffn_layer(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_
     _check(load().pi_ffn_layer(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
                                _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c), _ptr(ws), nbytes, events),
            "pi_ffn_layer")
+
+
+def pi_ffn_layer_static(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_c, K_c, stream=None,
+                        _cstruct=None) -> None:
+    """pi_ffn_layer with the library's static workspace (no caller workspace; allocates nothing)."""
+    cl = _cstruct if _cstruct is not None else layer._c()
+    _check(load().pi_ffn_layer_static(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
+                                      _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c)), "pi_ffn_layer_static")
 
 
 def pi_ffn_layer_ahead(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_c, K_c, ws, stages: int,

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
+#include <atomic>
 #include <cmath>
 #include "../../include/pi.h"
 #include "pi_internal.h"
@@ -628,6 +629,55 @@ int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, flo
                  void* const* events) {
   return pi_ffn_layer_stages(stream, L, B, x, tau, y_c, y, logits, A_g, K, A_c, K_c, ws, ws_bytes, events,
                              PI_STAGE_ALL, nullptr);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The layer call without a caller workspace (pi_ffn_layer_static).  Its workspace
+// is this file-scope device array: each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` is a host-side stand-in,
+// not a device address, so host code never passes it: it passes the address
+// hipGetSymbolAddress gives, looked up once per device (with that device
+// current) on the entry point's first call there and kept per device.
+static __device__ __align__(256) unsigned char scratch[PI_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];   // static storage: starts null
+
+// The current device's copy of `scratch` (looked up on the first call per device).
+int static_workspace(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PI_EUNSUPPORTED;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return PI_EHIP;
+    g_scratch_addr[dev].store(p, std::memory_order_release);   // the same address from any thread
+  }
+  *out = p;
+  return PI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pi_ffn_layer_static(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c,
+                        float* y, float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c) {
+  if (!L) return PI_EINVAL;
+  if (pi_workspace_bytes(PI_OP_FFN_LAYER, B, L->d, L->H, L->N, L->n_g) > (size_t)PI_STATIC_WORKSPACE_BYTES)
+    return PI_EWORKSPACE;
+  void* ws = nullptr;
+  const int st = static_workspace(&ws);
+  if (st != PI_OK) return st;
+  return pi_ffn_layer(stream, L, B, x, tau, y_c, y, logits, A_g, K, A_c, K_c, ws, PI_STATIC_WORKSPACE_BYTES,
+                      nullptr);
 }
 
 }  // extern "C"

@@ -42,8 +42,10 @@
  *    synchronisation.  No entry point prints, aborts or throws.
  *  - Results are bitwise repeatable: the same inputs give the same bits.
  *  - The library holds no mutable global state other than each thread's
- *    last HIP error (pi_last_hip_error); calls on different streams with
- *    disjoint outputs and workspaces may run concurrently.
+ *    last HIP error (pi_last_hip_error) and the static workspace of
+ *    pi_ffn_layer_static (one per GPU, with its address kept per device);
+ *    calls on different streams with disjoint outputs and workspaces may run
+ *    concurrently.
  */
 #ifndef PI_H
 #define PI_H
@@ -226,6 +228,28 @@ typedef struct pi_layer {
 int pi_ffn_layer(void* stream, const pi_layer* layer, int32_t B, const float* x, float tau,
                  const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
                  int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes, void* const* events);
+
+/* pi_ffn_layer for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same call without ws / ws_bytes / events: the workspace is a static
+ * device array of PI_STATIC_WORKSPACE_BYTES inside the library, one per GPU,
+ * held until the process ends; the entry point allocates nothing and frees
+ * nothing (its first call on a device looks up that device's array address).
+ * 16 MiB holds batch 1 at every shape this library is measured on (up to
+ * d = 12288, N = 49152, H = 4096) and batch 4 at d = 7168, N = 28672.
+ * Every call on one GPU shares that GPU's array and the array keeps the last
+ * call's contents: calls that overlap on one GPU (other streams or threads)
+ * race and give undefined results.  No part of the array needs to start at
+ * zero (each call writes what it reads).
+ * Errors: PI_EWORKSPACE when pi_workspace_bytes(PI_OP_FFN_LAYER, B, d, H, N,
+ * n_g) exceeds PI_STATIC_WORKSPACE_BYTES (nothing enqueued; use pi_ffn_layer
+ * with a caller workspace); PI_EUNSUPPORTED for a device index of 64 or more;
+ * PI_EHIP when the device or the array's address cannot be read; otherwise as
+ * pi_ffn_layer. */
+#define PI_STATIC_WORKSPACE_BYTES (16u << 20)
+int pi_ffn_layer_static(void* stream, const pi_layer* layer, int32_t B, const float* x, float tau,
+                        const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K, int32_t* A_c,
+                        int32_t* K_c);
 
 /* Stages of pi_ffn_layer, as bits. */
 enum pi_stage {
