@@ -1,13 +1,19 @@
 // pi_mfma.hip - the batched GEMMs on the matrix cores.
 //
-// The predictor's layers and FC2 use the fp32-input instruction
-// (v_mfma_f32_16x16x4_f32): the weights are widened to fp32 in registers and
-// x, h and a stay fp32, so the arithmetic is the VALU path's (fp32 products,
-// fp32 accumulation) with the operand reuse of a matrix tile; the logits keep
-// the precision the activation decision's parity band is set by.  FC1 with
-// fp16 weights uses the fp16 instruction (v_mfma_f32_16x16x32_f16, ten times
-// the fp32 instruction's measured rate): x is rounded to fp16, the products
-// of two fp16 values are exact and accumulate in fp32 (k_mm_rowdot16).
+// fp16 weights (every layer of the fp16 configurations) run on the fp16
+// instruction v_mfma_f32_16x16x32_f16, whose products of two fp16 values are
+// exact and accumulate in fp32:
+//  * FC1: x is rounded to fp16 (k_mm_rowdot16);
+//  * FC2: the activations a are fp16, written so by the FC1 finish;
+//  * the predictor's two layers keep near-fp32 operands as two fp16 parts,
+//    hi + lo (about 22 bits), with two exact products per weight: x for the
+//    hidden layer (k_mm_rowdot16 with HILO), h for the output layer
+//    (k_mm_axpy16 with LO), so the logits stay inside the activation
+//    decision's parity band.
+// Other weight types (fp32, int4 groups) keep the fp32-input instruction
+// v_mfma_f32_16x16x4_f32: the weights are widened to fp32 in registers, x, h
+// and a stay fp32, and the arithmetic is the VALU path's with the operand
+// reuse of a matrix tile (k_mm_rowdot, k_mm_axpy).
 //
 // One 16x16x4 instruction sums over k = 4 lane groups g = lane / 16.  Each lane
 // loads one 16-byte weight vector (E consecutive elements along k) and feeds
