@@ -55,6 +55,12 @@ def parse():
                          "the host CPU) over this many steps; 0 = skip")
     ap.add_argument("--no-placement", dest="placement", action="store_false",
                     help="skip the host-side placement-solver report")
+    ap.add_argument("--leg", default=None, metavar="NAME",
+                    help="run one leg alone and print its result instead of the benchmark line: truth, "
+                         "placement or config:KEY[:STRIDE] (for a profiler run over just its kernels)")
+    ap.add_argument("--placement-steps", type=int, default=16,
+                    help="steps of the fixed-rule vs solver-table timing on the LLaMA-13B gated 40%% stack, "
+                         "GPU side and hybrid (0 = skip)")
     ap.add_argument("--i4pred-steps", type=int, default=16,
                     help="after the batch-1 measurement, time the stack with int4-g128 predictor weights over "
                          "this many steps; 0 = skip")
@@ -818,7 +824,7 @@ def truth_bench(cfg, specs, dls, steps, warmup):
     return out
 
 
-def config_bench(key, steps, warmup, stride=1, cpu_seconds=4.0):
+def config_bench(key, steps, warmup, stride=1, cpu_seconds=4.0, cpu=True):
     """One configuration at batch 1: its own layer stack (every `stride`-th layer when stride > 1,
     which keeps the spread of per-layer densities and hidden sizes; tokens/s then scales the mean
     per-layer time to every layer), the stage timings and a bounded oracle baseline."""
@@ -841,7 +847,7 @@ def config_bench(key, steps, warmup, stride=1, cpu_seconds=4.0):
                 "mean_density": round(float(np.mean([s.rho for s in specs])), 4)})
     del dls
     torch.cuda.empty_cache()
-    out["cpu_baseline"] = cpu_baseline(cfg, 1, cpu_seconds, 2)
+    out["cpu_baseline"] = cpu_baseline(cfg, 1, cpu_seconds, 2) if cpu else None
     out["setup_and_run_s"] = round(time.time() - t0, 1)
     log(f"config {key}: {out['tokens_per_s']} tokens/s ({out['ms_per_step']} ms/step over {cfg.n_layers} layers, "
         f"{out['layers_timed']} timed), step frac {out['step_frac_of_peak']}, dominant {out['dominant_stage']} at "
@@ -980,7 +986,44 @@ def placement_report(keys):
     return out
 
 
-def hybrid_bench(cfg, specs, dls, steps, warmup):
+def placement_bench(key, steps, warmup, hybrid_steps):
+    """The offline placement solver's tables against the fixed per-layer top-share rule on the
+    GPU, on the same stack (`key`, whose gpu_frac sets the budget): each variant's layers are built
+    with its GPU tables and timed through the batch-1 layer stack (GPU side, cold partials given)
+    and through the hybrid executor (cold neurons on the host CPU, per-layer calls and the native
+    look-ahead stack), with the GPU's expected share of all activations beside them."""
+    import math
+    import torch
+    import synth
+    from synth.device import DeviceLayer
+    from activation_sparse_amd.placement import solve_placement, gpu_impact_share
+    cfg = synth.CONFIGS[key]
+    t0 = time.time()
+    fixed = [synth.layer_spec(cfg, l) for l in range(cfg.n_layers)]
+    k = int(math.floor(cfg.gpu_frac * cfg.N))
+    tables = solve_placement([s.counts for s in fixed], [1] * cfg.n_layers, k * cfg.n_layers)
+    solved = [synth.with_table(s, t) for s, t in zip(fixed, tables)]
+    p = [s.p for s in fixed]
+    out = {"workload": cfg.desc, "layers": cfg.n_layers, "budget_neurons": k * cfg.n_layers}
+    for name, specs in (("fixed_top_share", fixed), ("solver", solved)):
+        dls = [DeviceLayer(s, "cuda:0") for s in specs]
+        torch.cuda.synchronize()
+        gpu = stack_timing(cfg, specs, dls, steps, warmup)
+        hyb = hybrid_bench(cfg, specs, dls, hybrid_steps, 1, light=True) if hybrid_steps > 0 else None
+        n_g = [s.n_g for s in specs]
+        out[name] = {"gpu_activation_share": round(gpu_impact_share(p, [s.T_g for s in specs]), 4),
+                     "n_g_min": min(n_g), "n_g_max": max(n_g),
+                     "gpu_side_tokens_per_s": round(1e3 / gpu["ms_per_step_timed_layers"], 2),
+                     "gpu_side_mean_K": gpu["mean_K"], "gpu_side_step_frac_of_peak": gpu["step_frac_of_peak"],
+                     "hybrid": hyb}
+        del dls
+        torch.cuda.empty_cache()
+        log(f"placement {name}: {out[name]}")
+    out["setup_and_run_s"] = round(time.time() - t0, 1)
+    return out
+
+
+def hybrid_bench(cfg, specs, dls, steps, warmup, light=False):
     """The pages' hybrid layer at batch 1: the CPU-table neurons live in host memory and run on the
     host CPU (libpi_host) while the GPU runs the predictor, the compaction and its own neurons; the
     CPU's partial is copied over and merged on the GPU (skipped when it has no active neuron).
@@ -1040,6 +1083,13 @@ def hybrid_bench(cfg, specs, dls, steps, warmup):
     torch.cuda.synchronize()
     el_native = time.perf_counter() - t4
     del stk
+    if light:   # the three timings only (no CPU-alone timing, no host read probe)
+        out = {"tokens_per_s": round(steps / el, 2), "ms_per_step": round(el * 1e3 / steps, 3),
+               "lookahead_native_tokens_per_s": round(steps / el_native, 2),
+               "lookahead_tokens_per_s": round(steps / el_ahead, 2), "steps": steps,
+               "mean_K_c": float(np.mean(kcs)), "host_weights_gib": round(host_bytes / 2**30, 2)}
+        del hys, hls
+        return out
     # the CPU side alone: each layer's last cold list and input again, through pi_cold_ffn
     y_h = np.empty((1, d), np.float32)
     t2 = time.perf_counter()
@@ -1088,6 +1138,30 @@ def hybrid_bench(cfg, specs, dls, steps, warmup):
     return out
 
 
+def run_leg(args):
+    """One leg alone, so that a profiler run holds just its kernels: 'truth' (on --config's stack),
+    'placement', or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
+    import torch
+    import synth
+    from synth.device import DeviceLayer
+    name, _, rest = args.leg.partition(":")
+    torch.cuda.set_device(0)
+    if name == "config":
+        key, _, stride = rest.partition(":")
+        res = config_bench(key, args.config_steps, 2, int(stride or 1), cpu=not args.no_cpu_baseline)
+    elif name == "truth":
+        cfg = synth.CONFIGS[args.config]
+        specs = [synth.layer_spec(cfg, L) for L in range(args.layers or cfg.n_layers)]
+        dls = [DeviceLayer(s, "cuda:0") for s in specs]
+        torch.cuda.synchronize()
+        res = truth_bench(cfg, specs, dls, args.truth_steps, 2)
+    elif name == "placement":
+        res = placement_bench("llama-13b-gated-40", args.placement_steps, 2, args.placement_steps)
+    else:
+        raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, placement, config:KEY[:STRIDE])")
+    return {"leg": args.leg, "result": res}
+
+
 def main():
     args = parse()
     if args.rocprof_summary:
@@ -1097,6 +1171,9 @@ def main():
         print("bench.py: this build runs on exactly one GPU; --gpus N with N > 1 is not supported "
               "(the multi-GPU sharding is a design note only).", file=sys.stderr)
         sys.exit(2)
+    if args.leg:
+        print(json.dumps(run_leg(args)), flush=True)
+        return
     import torch
     import synth
     import activation_sparse_amd as pi
@@ -1344,6 +1421,10 @@ def main():
     if args.placement and B == 1:
         log("placement solver (host) ...")
         placement = placement_report([cfg.key] + (["llama-13b-gated"] if cfg.key != "llama-13b-gated" else []))
+        if args.placement_steps > 0:
+            log("placement solver's tables against the fixed rule on the GPU (llama-13b-gated-40) ...")
+            placement["llama-13b-gated-40"] = placement_bench("llama-13b-gated-40", args.placement_steps, 2,
+                                                              args.placement_steps)
 
     sweep = None
     batches = [int(v) for v in args.sweep.split(",") if v.strip()] if args.sweep else []

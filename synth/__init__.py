@@ -28,7 +28,7 @@ import ctypes as C
 import functools
 import math
 import os
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Optional, Tuple
 
 import numpy as np
@@ -167,6 +167,13 @@ CONFIGS["opt-30b-i4pred"] = Config(
 CONFIGS["opt-30b-rho20"] = Config(
     "opt-30b-rho20", "OPT-30B-shaped FFN stack, 48 layers, 7168/28672, fp16, density 0.20, 40% of neurons on the GPU",
     48, 7168, 28672, F16, F16, F16, False, (0.20, 0.20), 1.1, (1024, 1024), 0.4, (1,), 64, 4)
+
+# The LLaMA-13B gated stack with 40% of its neurons in the GPU tables and the rest on the CPU:
+# the same layers (seed, per-layer density and hidden size) as "llama-13b-gated", so that the
+# offline placement solver's per-layer tables can be set against the fixed per-layer rule.
+CONFIGS["llama-13b-gated-40"] = Config(
+    "llama-13b-gated-40", "LLaMA-13B-shaped ReLU gated FFN, 40 layers, 5120/13824, fp16, 40% of neurons on the GPU",
+    40, 5120, 13824, F16, F16, F16, True, (0.08, 0.25), 1.1, (512, 1120), 0.4, (1,), 64, 3)
 
 
 def i4_quantize_rows(bits16: np.ndarray):
@@ -319,6 +326,18 @@ def layer_spec(cfg: Config, layer: int) -> LayerSpec:
     c2 = to_stored(sd * ndtri(p) - mu, cfg.bdtype)
     T_g, T_c, counts = _table(cfg, layer, p)
     return LayerSpec(cfg, layer, rho, H, c, p, b1, c2, T_g, T_c, counts)
+
+
+def with_table(spec: LayerSpec, T_g: np.ndarray) -> LayerSpec:
+    """The same layer with another GPU table (e.g. one the placement solver chose): T_g as given
+    (sorted ascending), T_c its complement."""
+    N = spec.cfg.N
+    T_g = np.sort(np.asarray(T_g, dtype=np.int64)).astype(np.int32)
+    if len(T_g) and (T_g[0] < 0 or T_g[-1] >= N or np.any(np.diff(T_g) == 0)):
+        raise ValueError("T_g must hold distinct neuron ids in [0, N)")
+    mask = np.zeros(N, bool)
+    mask[T_g] = True
+    return replace(spec, T_g=T_g, T_c=np.flatnonzero(~mask).astype(np.int32))
 
 
 # ----------------------------------------------------------------------------- host tensors

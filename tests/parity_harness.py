@@ -177,10 +177,12 @@ def _gpu_stages(dl, buf, B, tau, with_cold, fused, y_c=None):
 
 def run_layer_parity(cfg: synth.Config, layer: int = 0, step: int = 0, B: int = 1, tau: float = 0.0,
                      device="cuda:0", with_cold=True, x_override: Optional[np.ndarray] = None,
-                     tau_all_active: bool = False, fused: bool = False):
-    """Full parity of one layer at batch B; returns a report dict."""
+                     tau_all_active: bool = False, fused: bool = False, spec: Optional[synth.LayerSpec] = None):
+    """Full parity of one layer at batch B; returns a report dict.  spec, when given, replaces
+    the config's own spec of the layer (another GPU table, e.g. the placement solver's)."""
     torch = _torch()
-    spec = synth.layer_spec(cfg, layer)
+    if spec is None:
+        spec = synth.layer_spec(cfg, layer)
     d, N = cfg.d, cfg.N
     n_c = len(spec.T_c)
     x = synth.host_x(cfg.seed, layer, step, B, d) if x_override is None else np.ascontiguousarray(x_override, np.float32)

@@ -102,3 +102,29 @@ def test_bad_arguments():
         solve_placement([np.ones(4)], [0], 4)
     with pytest.raises(ValueError):
         solve_placement([np.ones(4)], [1], 4, min_frac=1.5)
+
+
+def test_solver_tables_of_the_small_gated_stack():
+    """The stack the GPU test runs: the solver moves budget between its layers (n_g differs from
+    layer to layer), spends all of it, and each table is a valid partition with its complement."""
+    from tests.placement_cases import SMALL, solver_specs
+    specs = solver_specs(SMALL)
+    n_g = [specs[l].n_g for l in range(SMALL.n_layers)]
+    k = int(math.floor(SMALL.gpu_frac * SMALL.N))
+    assert sum(n_g) == k * SMALL.n_layers
+    assert len(set(n_g)) > 1 and max(n_g) - min(n_g) > 64
+    for s in specs.values():
+        both = np.concatenate([s.T_g, s.T_c])
+        assert np.array_equal(np.sort(both), np.arange(SMALL.N))
+        assert np.all(np.diff(s.T_g) > 0) and np.all(np.diff(s.T_c) > 0)
+        # the solver keeps the hottest neurons: every GPU neuron's count >= every CPU neuron's
+        if s.n_g and len(s.T_c):
+            assert s.counts[s.T_g].min() >= s.counts[s.T_c].max()
+
+
+def test_with_table_rejects_bad_ids():
+    spec = synth.layer_spec(synth.CONFIGS["opt-768"], 0)
+    with pytest.raises(ValueError):
+        synth.with_table(spec, np.array([3, 3], np.int32))
+    with pytest.raises(ValueError):
+        synth.with_table(spec, np.array([spec.cfg.N], np.int32))
