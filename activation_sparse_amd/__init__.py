@@ -17,6 +17,7 @@ PI_F32, PI_F16, PI_I4G128 = 0, 1, 2
 PI_RELU, PI_GATED_RELU = 0, 1
 PI_OK, PI_EINVAL, PI_EWORKSPACE, PI_EUNSUPPORTED, PI_EHIP = 0, 1, 2, 3, 4
 PI_OP_PREDICT, PI_OP_COMPACT, PI_OP_SPARSE_FFN, PI_OP_MERGE, PI_OP_FFN_LAYER, PI_OP_PREDICT_OUTPUT = 0, 1, 2, 3, 4, 5
+PI_OP_FFN_LAYER_NORMED = 6
 PI_STAGE_HIDDEN, PI_STAGE_OUTPUT, PI_STAGE_FC1, PI_STAGE_FC2, PI_STAGE_SUM, PI_STAGE_ALL = 1, 2, 4, 8, 16, 31
 PI_MAX_BATCH = 32
 PI_MAX_NEURONS = 65536
@@ -28,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libpi.so")
 EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes",
            "pi_table_prepare", "pi_ffn_layer", "pi_ffn_layer_stages", "pi_workspace_bytes", "pi_status_string",
            "pi_last_hip_error", "pi_abi_version", "pi_read_probe", "pi_ffn_layer_ahead",
-           "pi_layer_norm", "pi_ffn_layer_static")
+           "pi_layer_norm", "pi_ffn_layer_static", "pi_ffn_layer_normed")
 PI_STATIC_WORKSPACE_BYTES = 16 << 20
 
 
@@ -85,6 +86,9 @@ def load():
         L.pi_ffn_layer_ahead.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, P, P, P, P, P, P, P, P, C.c_size_t,
                                          C.c_uint32, C.POINTER(_Layer), P, C.c_size_t]
         L.pi_ffn_layer_ahead.restype = C.c_int
+        L.pi_ffn_layer_normed.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, C.c_float, P, P, P, P, P, P, P, P,
+                                          P, C.c_size_t]
+        L.pi_ffn_layer_normed.restype = C.c_int
         L.pi_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.pi_workspace_bytes.restype = C.c_size_t
         L.pi_status_string.argtypes = [I]
@@ -278,6 +282,16 @@ def pi_ffn_layer_ahead(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g,
     _check(load().pi_ffn_layer_ahead(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
                                      _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c), _ptr(ws), nbytes,
                                      int(stages), C.byref(cn), _ptr(ws_next), nnext), "pi_ffn_layer_ahead")
+
+
+def pi_ffn_layer_normed(layer: Layer, B: int, y_prev, eps: float, tau: float, y_c, y, logits, A_g, K, A_c, K_c, ws,
+                        x_out=None, ws_bytes=None, stream=None, _cstruct=None) -> None:
+    """pi_ffn_layer on the layer normalisation of y_prev (the chained-layer input), in the layer's own kernels."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    cl = _cstruct if _cstruct is not None else layer._c()
+    _check(load().pi_ffn_layer_normed(_stream(stream), C.byref(cl), B, _ptr(y_prev), float(eps), float(tau),
+                                      _ptr(y_c), _ptr(y), _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c),
+                                      _ptr(x_out), _ptr(ws), nbytes), "pi_ffn_layer_normed")
 
 
 def pi_ffn_layer_stages(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g, K, A_c, K_c, ws, stages: int,

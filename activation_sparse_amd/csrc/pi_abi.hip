@@ -179,6 +179,28 @@ LayerWs layer_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, in
   return w;
 }
 
+// pi_ffn_layer_normed's workspace: the layer's, then the normalisation statistics and the
+// normalised input (used when the layer does not run the batch-1 kernels).
+struct NormedWs {
+  void* layer;
+  size_t layer_bytes;
+  float* stats;
+  float* xn;
+  size_t bytes;
+};
+
+NormedWs normed_ws_layout(void* ws, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g) {
+  NormedWs n{};
+  n.layer = ws;
+  n.layer_bytes = layer_ws_layout(nullptr, B, d, H, N, n_g).bytes;
+  Carver c{static_cast<char*>(ws)};
+  c.off = n.layer_bytes;
+  n.stats = c.take<float>(256);
+  n.xn = c.take<float>((size_t)(B > 0 ? B : 1) * (size_t)d * 4);
+  n.bytes = c.off;
+  return n;
+}
+
 // The predictor's hidden layer, h[b,m] = max(0, P1[m].x_b + c1[m]): batch 1 on the
 // register-x GEMV, batches of kMmRowMinBatch and more on the matrix cores (split-K
 // partials in `partials`), others on the LDS-x row-dot kernel.
@@ -192,15 +214,26 @@ int h_layout(int32_t B, int32_t d, int32_t H, int32_t N, const pi_matrix& P1, co
   return pi::mm_axpy16_supported(P2.dtype, N) ? 2 : 1;
 }
 
+// The chained-layer input of pi_ffn_layer_normed when the batch-1 kernels normalise it themselves:
+// the hidden-layer kernel computes the statistics and leaves them in `stats` for the output-layer +
+// FC1 kernel.
+struct LnIn {
+  float eps;
+  float* stats;    // 2 floats in the workspace
+  float* x_out;    // optional normalised row
+};
+
 int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* x, const pi_matrix& P1,
-                   const pi_vector& c1, float* h, float* partials, int h_lay) {
+                   const pi_vector& c1, float* h, float* partials, int h_lay, const LnIn* ln = nullptr) {
   const bool h_tr = h_lay != 0;
   if (B == 1 && pi::b1_supported(P1.dtype, d)) {
     pi::B1Gemv g{};
     g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
     g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
+    if (ln) { g.ln_stats = ln->stats; g.ln_eps = ln->eps; g.x_out = ln->x_out; }
     return hip_status(pi::launch_hidden_b1(g, s));
   }
+  if (ln) return PI_EINVAL;   // only the batch-1 kernel normalises its input
   if (use_mm_row(B) && pi::mm_rowdot_supported(P1.dtype, H, d)) {
     pi::MmRowArgs m{};
     m.W = P1.data; m.Ws = P1.scales; m.dt = P1.dtype; m.gated = 0; m.cols = d; m.n_rows = H; m.list = nullptr;
@@ -296,6 +329,8 @@ size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N
       return d > 0 ? ffn_ws_layout(nullptr, B, d, n_g).bytes : 0;
     case PI_OP_FFN_LAYER:
       return (d > 0 && N > 0) ? layer_ws_layout(nullptr, B, d, H > 0 ? H : 1, N, n_g).bytes : 0;
+    case PI_OP_FFN_LAYER_NORMED:
+      return (d > 0 && N > 0) ? normed_ws_layout(nullptr, B, d, H > 0 ? H : 1, N, n_g).bytes : 0;
     default: return 0;
   }
 }
@@ -492,9 +527,20 @@ struct Ahead {
   int h_lay;
 };
 
+// The batch-1 layer runs as the fused tile kernels (output layer + decision + FC1, then the segment
+// FC2 and the ordered sum) for these formats and sizes.
+bool b1_fused(const pi_layer* L, int32_t B) {
+  const bool gated = L->kind == PI_GATED_RELU;
+  const int bdt = L->b1.data ? L->b1.dtype : (L->c2.data ? L->c2.dtype : PI_F16);
+  const int c2dt = L->c2.data ? L->c2.dtype : bdt;
+  return B == 1 && pi::b1_supported(L->W1.dtype, L->d) && n_groups64(L->N) <= (size_t)64 * pi::kSegChunks &&
+         pi::pred_fc1_supported(L->P2.dtype, L->W1.dtype, bdt, c2dt, gated, L->H, L->N, L->d);
+}
+
 int layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, float tau, const float* y_c, float* y,
                  float* logits, int32_t* A_g, int32_t* K, int32_t* A_c, int32_t* K_c, void* ws, size_t ws_bytes,
-                 void* const* events, uint32_t stages, int32_t* rows_read, const Ahead* ah) {
+                 void* const* events, uint32_t stages, int32_t* rows_read, const Ahead* ah,
+                 const LnIn* ln = nullptr) {
   if (!L) return PI_EINVAL;
   const int32_t d = L->d, N = L->N, H = L->H, n_g = L->n_g;
   if (N <= 0 || H <= 0 || n_g > N) return PI_EINVAL;
@@ -520,15 +566,15 @@ int layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, flo
   const bool gated = L->kind == PI_GATED_RELU;
   const int32_t ngroups = (int32_t)n_groups64(N);
   const int bdt = L->b1.data ? L->b1.dtype : (L->c2.data ? L->c2.dtype : PI_F16);
-  const int c2dt = L->c2.data ? L->c2.dtype : bdt;
-  const bool fused = B == 1 && pi::b1_supported(L->W1.dtype, d) && ngroups <= 64 * pi::kSegChunks &&
-                     pi::pred_fc1_supported(L->P2.dtype, L->W1.dtype, bdt, c2dt, gated, H, N, d);
+  const bool fused = b1_fused(L, B);
+  if (ln && (!fused || !pi::b1_supported(L->P1.dtype, d) || stages != PI_STAGE_ALL || ah)) return PI_EINVAL;
   float* lg = logits ? logits : w.logits;
 
   if ((st = record(0)) != PI_OK) return st;
   // predictor hidden layer
   const int h_lay = h_layout(B, d, H, N, L->P1, L->P2);
-  if (want(PI_STAGE_HIDDEN) && (st = enqueue_hidden(s, B, d, H, x, L->P1, L->c1, w.h, w.partials, h_lay)) != PI_OK)
+  if (want(PI_STAGE_HIDDEN) &&
+      (st = enqueue_hidden(s, B, d, H, x, L->P1, L->c1, w.h, w.partials, h_lay, ln)) != PI_OK)
     return st;
   if ((st = record(1)) != PI_OK) return st;
 
@@ -542,7 +588,7 @@ int layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, flo
       a.gbits = static_cast<const uint32_t*>(L->table);
       a.gpre = reinterpret_cast<const int32_t*>(a.gbits + table_words(N));
       a.W1 = L->W1.data; a.W1s = L->W1.scales; a.Wu = L->Wup.data; a.Wus = L->Wup.scales; a.dt = L->W1.dtype;
-      a.d = d; a.n_g = n_g; a.x = x; a.b1 = L->b1.data; a.b1_dt = L->b1.dtype;
+      a.d = d; a.n_g = n_g; a.x = x; a.ln_stats = ln ? ln->stats : nullptr; a.b1 = L->b1.data; a.b1_dt = L->b1.dtype;
       a.seg_slot = w.seg_slot; a.seg_cold = w.seg_cold; a.pos_slot = w.pos_slot; a.pos_a = w.pos_a; a.cnt = w.cnt;
       a.rows_read = rows_read;
       // the next layer's hidden layer rides in this launch when its rows have the FC1 weights' format
@@ -629,6 +675,32 @@ int pi_ffn_layer(void* stream, const pi_layer* L, int32_t B, const float* x, flo
                  void* const* events) {
   return pi_ffn_layer_stages(stream, L, B, x, tau, y_c, y, logits, A_g, K, A_c, K_c, ws, ws_bytes, events,
                              PI_STAGE_ALL, nullptr);
+}
+
+int pi_ffn_layer_normed(void* stream, const pi_layer* L, int32_t B, const float* y_prev, float eps, float tau,
+                        const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K, int32_t* A_c,
+                        int32_t* K_c, float* x_out, void* ws, size_t ws_bytes) {
+  if (!L || !y_prev || !aligned16(y_prev) || (x_out && !aligned16(x_out))) return PI_EINVAL;
+  if (!valid_batch(B) || L->d <= 0 || L->N <= 0 || L->H <= 0 || !(eps >= 0.f) || !std::isfinite(eps))
+    return PI_EINVAL;
+  const size_t row = (size_t)B * (size_t)L->d * 4;
+  // the normalised row is written before y_prev is read again and y is written last
+  if (x_out && (ranges_overlap(x_out, row, y_prev, row) || (y && ranges_overlap(x_out, row, y, row))))
+    return PI_EINVAL;
+  if (!ws || !aligned16(ws)) return PI_EWORKSPACE;
+  const NormedWs n = normed_ws_layout(ws, B, L->d, L->H, L->N, L->n_g);
+  if (ws_bytes < n.bytes) return PI_EWORKSPACE;
+  if (b1_fused(L, B) && pi::b1_supported(L->P1.dtype, L->d)) {
+    LnIn ln{eps, n.stats, x_out};
+    return layer_stages(stream, L, B, y_prev, tau, y_c, y, logits, A_g, K, A_c, K_c, n.layer, n.layer_bytes, nullptr,
+                        PI_STAGE_ALL, nullptr, nullptr, &ln);
+  }
+  // other shapes: the normalisation kernel first, then the layer on its output
+  float* xn = x_out ? x_out : n.xn;
+  const int st = pi_layer_norm(stream, B, L->d, y_prev, eps, xn);
+  if (st != PI_OK) return st;
+  return layer_stages(stream, L, B, xn, tau, y_c, y, logits, A_g, K, A_c, K_c, n.layer, n.layer_bytes, nullptr,
+                      PI_STAGE_ALL, nullptr, nullptr);
 }
 
 }  // extern "C"

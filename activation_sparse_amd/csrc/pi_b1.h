@@ -22,6 +22,12 @@ struct B1Gemv {
   float* out;
   const int32_t* list;       // FC1
   const int32_t* Kp;         // FC1
+  // hidden layer only: x is a raw row to normalise first (layer normalisation, unit gain, zero
+  // bias) when ln_stats != NULL; the kernel writes the mean and 1/sqrt(var + ln_eps) it used to
+  // ln_stats[0..1] and, when x_out != NULL, the normalised row to x_out [cols]
+  float* ln_stats;
+  float ln_eps;
+  float* x_out;
 };
 bool b1_supported(int dt, int64_t cols);
 hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s);
@@ -55,6 +61,7 @@ struct PredFc1Args {
   int d;
   int n_g;
   const float* x;
+  const float* ln_stats;     // NULL, or the mean and 1/sqrt(var + eps) to normalise x with
   const void* b1;
   int b1_dt;
   int32_t* seg_slot;         // [groups x 64] ascending slots of each group's active GPU-resident neurons

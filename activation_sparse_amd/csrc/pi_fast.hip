@@ -92,26 +92,103 @@ struct LaneRow {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
 
-// h[j] = max(0, W[j].x + bias[j]) for j < rows: one row per wave.
+// Layer normalisation of the register-held x slice (the lane's vectors v = u*64 + lane, E
+// elements each, zeros past nvec, where the weights read zeros too) of every wave of the block:
+// x <- fma(x, inv, -mean * inv) with
+// inv = 1 / sqrt(var + eps), mean and population variance over the n elements.  The four waves
+// share the work: wave w sums the slice vectors u = w, w + 4, ... (fp32, in slice order), the
+// wave butterfly and the sum over the waves in wave order give the mean, then the same for the
+// squared deviations (two passes).  Every block runs the same partition, so every wave of the
+// grid gets the same two values.  Every wave of the block must call this (it has barriers).
+// stats / x_out (wave-uniform, may be NULL) receive the mean and inv, and the normalised row.
+template <int DT, int NV>
+__device__ __forceinline__ void layer_norm_xreg(float (&xr)[NV][Fmt<DT>::E], int nvec, int n, float eps, int lane,
+                                                int wave, float* stats, float* x_out) {
+  constexpr int E = Fmt<DT>::E;
+  __shared__ float part[2][kWpb];
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+    if (u % kWpb == wave)                         // wave-uniform
+#pragma unroll
+      for (int e = 0; e < E; ++e) s += xr[u][e];  // past nvec: zeros
+  s = wave_sum(s);
+  if (lane == 0) part[0][wave] = s;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWpb; ++w) tot += part[0][w];
+  const float mu = tot / (float)n;
+  float q = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+    if (u % kWpb == wave) {
+      const bool ok = u * kWave + lane < nvec;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float dv = xr[u][e] - mu;
+        q += ok ? dv * dv : 0.f;
+      }
+    }
+  q = wave_sum(q);
+  if (lane == 0) part[1][wave] = q;
+  __syncthreads();
+  float var = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWpb; ++w) var += part[1][w];
+  const float inv = 1.0f / sqrtf(var / (float)n + eps);
+  const float nm = -mu * inv;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int v = u * kWave + lane;
+    const bool ok = v < nvec;
+    // past nvec the row reads zeros, so those elements need no mask
+#pragma unroll
+    for (int e = 0; e < E; ++e) xr[u][e] = fmaf(xr[u][e], inv, nm);
+    if (x_out && ok) {
+#pragma unroll
+      for (int q4 = 0; q4 < E / 4; ++q4)
+        *reinterpret_cast<float4v*>(x_out + (int64_t)E * v + 4 * q4) =
+            float4v{xr[u][4 * q4], xr[u][4 * q4 + 1], xr[u][4 * q4 + 2], xr[u][4 * q4 + 3]};
+    }
+  }
+  if (stats && lane == 0) { stats[0] = mu; stats[1] = inv; }
+}
+
+// h[j] = max(0, W[j].x + bias[j]) for j < rows: one row per wave.  With ln_stats, x is first
+// replaced by its layer normalisation (mean and population variance over the cols elements),
+// computed by each block's waves together from the x every wave holds (the same bits in every
+// block); the grid's first wave writes the two statistics (and the normalised row to x_out) for
+// the kernels after it.
 template <int DT, int NV, int BDT>
 __global__ __launch_bounds__(kT) void k_hidden_b1(const void* __restrict__ W, const uint16_t* __restrict__ Ws,
                                                    int rows, int cols, const float* __restrict__ x,
-                                                   const void* __restrict__ bias, float* __restrict__ out) {
+                                                   const void* __restrict__ bias, float* __restrict__ out,
+                                                   float* __restrict__ ln_stats, float ln_eps,
+                                                   float* __restrict__ x_out) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
   const int gw = blockIdx.x * kWpb + wave;
-  if (gw >= rows) return;
+  // waves past the rows still take part in the block's normalisation (it has barriers)
+  if (gw >= rows && !ln_stats) return;
+  const bool row_ok = gw < rows;
   const int64_t rb = row_bytes(DT, cols);
   const int nvec = (int)(rb / 16);
   const int groups = cols / 128;
   const Bias<BDT> bias_at(bias, (uint32_t)rows);
-  const int j = gw;                 // the grid has one wave per row
+  const int j = row_ok ? gw : 0;    // the grid has one wave per row
   const float bj = bias_at(j);
-  LaneRow<DT, NV> r;
-  r.issue(reinterpret_cast<const char*>(W) + (int64_t)j * rb, DT == 2 ? Ws + (int64_t)j * groups : nullptr, nvec,
-          lane);
+  // x (from L2) is issued before the weight row (from HBM): the normalisation below waits only
+  // for x and runs while the row is still arriving
   float xr[NV][Fmt<DT>::E];
   load_xreg<DT, NV>(x, nvec, lane, xr);
-  __builtin_amdgcn_sched_barrier(0);   // all of x in flight before the first FMA
+  LaneRow<DT, NV> r;
+  r.issue(row_ok ? reinterpret_cast<const char*>(W) + (int64_t)j * rb : nullptr,
+          DT == 2 && row_ok ? Ws + (int64_t)j * groups : nullptr, nvec, lane);
+  if (ln_stats) {
+    layer_norm_xreg<DT, NV>(xr, nvec, cols, ln_eps, lane, wave, gw == 0 ? ln_stats : nullptr,
+                            gw == 0 ? x_out : nullptr);
+    if (!row_ok) return;
+  }
   float z = wave_sum(r.dot(xr)) + bj;
   z = z > 0.f ? z : 0.f;
   if (lane == 0) out[j] = z;
@@ -235,6 +312,10 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   const int nvec = FC1 ? (int)(row_bytes(DT, a.d) / 16) : 0;
   const int npad = (nvec + kWave - 1) & ~(kWave - 1);
   float4v xq[FC1 ? XQ : 1];
+  // x given raw with the statistics the hidden-layer kernel left: normalised on the way into LDS
+  // with the same two values and the same fma, so FC1 sees the hidden layer's x bit for bit
+  float ln_inv = 1.f, ln_nm = 0.f;
+  if (FC1 && a.ln_stats) { ln_inv = a.ln_stats[1]; ln_nm = -a.ln_stats[0] * ln_inv; }
   if constexpr (FC1) {
     const int nq = a.d / 4;
     const float4v* x4 = reinterpret_cast<const float4v*>(a.x);
@@ -261,7 +342,14 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
 #pragma unroll
     for (int r = 0; r < XQ; ++r) {
       const int q = r * NT + tid;
-      if (q < nq) xs[(q % P) * npad + q / P] = xq[r];
+      if (q < nq) {
+        float4v v = xq[r];
+        if (a.ln_stats) {
+          v.x = fmaf(v.x, ln_inv, ln_nm); v.y = fmaf(v.y, ln_inv, ln_nm);
+          v.z = fmaf(v.z, ln_inv, ln_nm); v.w = fmaf(v.w, ln_inv, ln_nm);
+        }
+        xs[(q % P) * npad + q / P] = v;
+      }
     }
   }
 
@@ -525,9 +613,11 @@ hipError_t hidden_dt(const B1Gemv& g, hipStream_t s) {
 #define PI_HID(NVV)                                                                                        \
   do {                                                                                                      \
     if (g.bias && g.bias_dt == 0)                                                                          \
-      hipLaunchKernelGGL((k_hidden_b1<DT, NVV, 0>), gr, bl, 0, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out); \
+      hipLaunchKernelGGL((k_hidden_b1<DT, NVV, 0>), gr, bl, 0, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out, \
+                         g.ln_stats, g.ln_eps, g.x_out);                                                   \
     else                                                                                                    \
-      hipLaunchKernelGGL((k_hidden_b1<DT, NVV, 1>), gr, bl, 0, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out); \
+      hipLaunchKernelGGL((k_hidden_b1<DT, NVV, 1>), gr, bl, 0, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out, \
+                         g.ln_stats, g.ln_eps, g.x_out);                                                   \
   } while (0)
   switch (pick_nv<DT>(nvec)) {
     case 1: PI_HID(1); break;

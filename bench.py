@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--no-placement", dest="placement", action="store_false",
                     help="skip the host-side placement-solver report")
     ap.add_argument("--leg", default=None, metavar="NAME",
-                    help="run one leg alone and print its result instead of the benchmark line: truth, "
+                    help="run one leg alone and print its result instead of the benchmark line: truth, chained, "
                          "placement or config:KEY[:STRIDE] (for a profiler run over just its kernels)")
     ap.add_argument("--placement-steps", type=int, default=16,
                     help="steps of the fixed-rule vs solver-table timing on the LLaMA-13B gated 40%% stack, "
@@ -528,12 +528,13 @@ def lookahead_bench(cfg, specs, dls, steps, warmup, B=1):
 
 
 def chained_bench(cfg, specs, dls, steps, warmup, B=1, eps=1e-5):
-    """Chained layers: layer L+1's input is the layer normalisation of layer L's output
-    (pi_layer_norm on the GPU), so every layer's input is made by the step itself; layer 0's input
-    is seeded per step.  Timed with exact prediction (pi_ffn_layer) and with look-ahead prediction
-    (pi_ffn_layer_ahead: layer L+1's predictor hidden layer from layer L's input).  The cold
-    partials stay seeded, as in the measured run.  One HIP graph per step; returns tokens/s of both
-    and the normalisation kernel's own time."""
+    """Chained layers: layer L+1's input is the layer normalisation of layer L's output, so every
+    layer's input is made by the step itself; layer 0's input is seeded per step.  Timed three
+    ways: exact prediction with the normalisation inside the layer call (pi_ffn_layer_normed, the
+    reported figure), exact prediction with pi_layer_norm between the layer calls, and look-ahead
+    prediction (pi_ffn_layer_ahead: layer L+1's predictor hidden layer from layer L's input, with
+    pi_layer_norm).  The cold partials stay seeded, as in the measured run.  One HIP graph per
+    step; returns tokens/s of each and the normalisation kernel's own time."""
     import torch
     import synth
     import activation_sparse_amd as pi
@@ -544,7 +545,8 @@ def chained_bench(cfg, specs, dls, steps, warmup, B=1, eps=1e-5):
     n_c = max(len(s.T_c) for s in specs)
     d, N = cfg.d, cfg.N
     S = warmup + steps
-    ws_bytes = max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, B, d, maxH, N, n_g), 256)
+    # the normalising call's workspace begins with the plain layer call's
+    ws_bytes = max(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER_NORMED, B, d, maxH, N, n_g), 256)
     wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(n_layers)]
     x0 = torch.empty((S, B, d), dtype=torch.float32, device=dev)
     xl = torch.empty((n_layers, B, d), dtype=torch.float32, device=dev)
@@ -570,6 +572,17 @@ def chained_bench(cfg, specs, dls, steps, warmup, B=1, eps=1e-5):
         for L in range(n_layers):
             x = x0[t] if L == 0 else xl[L]
             cold = len(specs[L].T_c) > 0
+            if ahead == "normed":
+                # the layer normalises the previous output itself (in place: y_prev is y)
+                if L == 0:
+                    pi.pi_ffn_layer(dls[0].layer, B, x, 0.0, ycs[t, 0] if cold else None, y, None, A_g,
+                                    Ks[t, 0:1], A_c if cold else None, Kcs[t, 0:1] if cold else None, wss[0],
+                                    _cstruct=dls[0].layer_c)
+                else:
+                    pi.pi_ffn_layer_normed(dls[L].layer, B, y, eps, 0.0, ycs[t, L] if cold else None, y, None, A_g,
+                                           Ks[t, L:L + 1], A_c if cold else None, Kcs[t, L:L + 1] if cold else None,
+                                           wss[L], _cstruct=dls[L].layer_c)
+                continue
             args = (B, x, 0.0, ycs[t, L] if cold else None, y, None, A_g, Ks[t, L:L + 1], A_c if cold else None,
                     Kcs[t, L:L + 1] if cold else None, wss[L])
             if ahead and L == 0:
@@ -610,6 +623,8 @@ def chained_bench(cfg, specs, dls, steps, warmup, B=1, eps=1e-5):
 
     ms_exact = timed(False)
     K_exact = float(Ks[warmup:].float().mean().item())
+    ms_normed = timed("normed")
+    K_normed = float(Ks[warmup:].float().mean().item())
     ms_ahead = timed(True)
     K_ahead = float(Ks[warmup:].float().mean().item())
     # the normalisation alone: a graph of back-to-back calls on [B x d] (kernel + the gap to the next)
@@ -633,12 +648,16 @@ def chained_bench(cfg, specs, dls, steps, warmup, B=1, eps=1e-5):
     torch.cuda.synchronize()
     del g
     out = {"batch": B, "steps": steps, "eps": eps,
-           "tokens_per_s": round(B * 1e3 / ms_exact, 2), "ms_per_step": round(ms_exact, 4), "mean_K": K_exact,
+           "tokens_per_s": round(B * 1e3 / ms_normed, 2), "ms_per_step": round(ms_normed, 4), "mean_K": K_normed,
+           "normalisation": "inside the layer call (pi_ffn_layer_normed)",
+           "separate_norm_tokens_per_s": round(B * 1e3 / ms_exact, 2),
+           "separate_norm_ms_per_step": round(ms_exact, 4), "separate_norm_mean_K": K_exact,
            "lookahead_tokens_per_s": round(B * 1e3 / ms_ahead, 2), "lookahead_ms_per_step": round(ms_ahead, 4),
            "lookahead_mean_K": K_ahead,
            "layer_norm_us": round(e0.elapsed_time(e1) * 1e3 / n_norm, 2),
            "input": "layer 0 seeded per step; layer L+1 = layer norm of layer L's output (unit gain, zero bias)"}
-    log(f"chained layers: exact {out['ms_per_step']} ms/step, {out['tokens_per_s']} tokens/s; look-ahead "
+    log(f"chained layers: exact, normalised in the layer call {out['ms_per_step']} ms/step, {out['tokens_per_s']} "
+        f"tokens/s; with pi_layer_norm between calls {out['separate_norm_ms_per_step']} ms/step; look-ahead "
         f"{out['lookahead_ms_per_step']} ms/step, {out['lookahead_tokens_per_s']} tokens/s; "
         f"layer norm {out['layer_norm_us']} us")
     return out
@@ -1139,8 +1158,8 @@ def hybrid_bench(cfg, specs, dls, steps, warmup, light=False):
 
 
 def run_leg(args):
-    """One leg alone, so that a profiler run holds just its kernels: 'truth' (on --config's stack),
-    'placement', or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
+    """One leg alone, so that a profiler run holds just its kernels: 'truth' or 'chained' (on
+    --config's stack), 'placement', or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
     import torch
     import synth
     from synth.device import DeviceLayer
@@ -1155,10 +1174,16 @@ def run_leg(args):
         dls = [DeviceLayer(s, "cuda:0") for s in specs]
         torch.cuda.synchronize()
         res = truth_bench(cfg, specs, dls, args.truth_steps, 2)
+    elif name == "chained":
+        cfg = synth.CONFIGS[args.config]
+        specs = [synth.layer_spec(cfg, L) for L in range(args.layers or cfg.n_layers)]
+        dls = [DeviceLayer(s, "cuda:0") for s in specs]
+        torch.cuda.synchronize()
+        res = chained_bench(cfg, specs, dls, args.chained_steps, 3)
     elif name == "placement":
         res = placement_bench("llama-13b-gated-40", args.placement_steps, 2, args.placement_steps)
     else:
-        raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, placement, config:KEY[:STRIDE])")
+        raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, config:KEY[:STRIDE])")
     return {"leg": args.leg, "result": res}
 
 

@@ -67,7 +67,7 @@ enum pi_dtype { PI_F32 = 0, PI_F16 = 1, PI_I4G128 = 2 };
 enum pi_ffn_kind { PI_RELU = 0, PI_GATED_RELU = 1 };
 enum pi_status { PI_OK = 0, PI_EINVAL = 1, PI_EWORKSPACE = 2, PI_EUNSUPPORTED = 3, PI_EHIP = 4 };
 enum pi_op { PI_OP_PREDICT = 0, PI_OP_COMPACT = 1, PI_OP_SPARSE_FFN = 2, PI_OP_MERGE = 3, PI_OP_FFN_LAYER = 4,
-             PI_OP_PREDICT_OUTPUT = 5 };
+             PI_OP_PREDICT_OUTPUT = 5, PI_OP_FFN_LAYER_NORMED = 6 };
 
 /* A weight matrix on the device.  `scales` is used by PI_I4G128 only. */
 typedef struct pi_matrix {
@@ -317,6 +317,31 @@ int pi_ffn_layer_ahead(void* stream, const pi_layer* layer, int32_t B, const flo
  * Errors: PI_EINVAL for a NULL pointer, B <= 0, d outside 1..2^30, eps
  * negative or not finite, or x overlapping y without being equal to it. */
 int pi_layer_norm(void* stream, int32_t B, int32_t d, const float* y, float eps, float* x);
+
+/* Chained layers without the separate normalisation launch: pi_ffn_layer on
+ * x = the layer normalisation of y_prev (as pi_layer_norm: unit gain, zero
+ * bias, population variance, eps), with y_prev being the previous layer's
+ * output.  At batch 1, where the layer runs its fused kernels, the predictor's
+ * hidden-layer kernel normalises the row it holds and leaves the mean and
+ * 1/sqrt(var + eps) in the workspace, and the output-layer + FC1 kernel
+ * normalises x with those same two values, so the predictor and FC1 see the
+ * same x bit for bit; no other launch is added.  Other batches and formats run
+ * pi_layer_norm into the workspace (or x_out) first, then the layer.  The
+ * statistics are fp32 sums in a fixed order, so results are bitwise
+ * repeatable; the batch-1 sums run in another order than pi_layer_norm's, so
+ * they may differ from pi_layer_norm + pi_ffn_layer in the last bits.
+ * y_prev: device [B x d] fp32, 16-byte aligned; it may be y itself (or overlap
+ * it): every read of y_prev comes before y is written.  x_out: NULL, or device
+ * [B x d] fp32, 16-byte aligned, receiving the normalised input (e.g. for a
+ * host-side cold FFN); it may overlap neither y_prev nor y.  Other arguments as
+ * pi_ffn_layer.  ws: pi_workspace_bytes(PI_OP_FFN_LAYER_NORMED, B, d, H, N,
+ * n_g) bytes.
+ * Errors: as pi_ffn_layer and pi_layer_norm; PI_EINVAL for a NULL or
+ * unaligned y_prev, an unaligned x_out, x_out overlapping y_prev or y, or eps
+ * negative or not finite; PI_EWORKSPACE for a short or unaligned ws. */
+int pi_ffn_layer_normed(void* stream, const pi_layer* layer, int32_t B, const float* y_prev, float eps,
+                        float tau, const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
+                        int32_t* A_c, int32_t* K_c, float* x_out, void* ws, size_t ws_bytes);
 
 /* The streaming-read reference that the kernels' bandwidths are read against:
  * reads `bytes` bytes of `buf` once, in 16-byte vectors, with `blocks`

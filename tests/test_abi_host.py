@@ -161,6 +161,30 @@ def test_ffn_layer_ahead_rejects_bad_arguments():
     assert call(layer=_layer(N=1020)) == pi.PI_EINVAL              # this layer's own checks still apply
 
 
+def test_ffn_layer_normed_rejects_bad_arguments():
+    L = _layer()
+    need = pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER_NORMED, 1, 256, 64, 1024, 1024)
+    assert need >= pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, 1, 256, 64, 1024, 1024) + 256 + 256 * 4
+    YP, Y, XO, WS = FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (1 << 24)
+
+    def call(y_prev=YP, eps=1e-5, y=Y, x_out=XO, nbytes=need, layer=L, B=1, ws=WS):
+        return status(pi.pi_ffn_layer_normed, layer, B, y_prev, eps, 0.0, None, y, None, FAKE, FAKE, None, None, ws,
+                      x_out, nbytes, 0)
+
+    assert call(y_prev=None) == pi.PI_EINVAL
+    assert call(y_prev=YP + 4) == pi.PI_EINVAL                     # unaligned input
+    assert call(x_out=XO + 8) == pi.PI_EINVAL                      # unaligned normalised row
+    for eps in (-1e-5, float("nan"), float("inf")):
+        assert call(eps=eps) == pi.PI_EINVAL
+    assert call(B=0) == pi.PI_EINVAL and call(B=pi.PI_MAX_BATCH + 1) == pi.PI_EINVAL
+    assert call(x_out=YP + 512) == pi.PI_EINVAL                    # x_out overlapping y_prev (1 KB row)
+    assert call(x_out=Y) == pi.PI_EINVAL                           # x_out overlapping y
+    assert call(ws=None) == pi.PI_EWORKSPACE
+    assert call(ws=WS + 8) == pi.PI_EWORKSPACE                     # unaligned workspace
+    assert call(nbytes=need - 16) == pi.PI_EWORKSPACE
+    assert call(layer=_layer(N=1020)) == pi.PI_EINVAL              # the layer's own checks still apply
+
+
 def test_table_prepare_validates_and_builds_bitmap_and_prefix():
     import numpy as np
     N = 200

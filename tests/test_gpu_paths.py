@@ -628,13 +628,14 @@ def test_layer_norm_constant_rows_give_zeros():
     assert not np.any(x.cpu().numpy())
 
 
-@pytest.mark.parametrize("B,ahead", [(1, False), (1, True), (4, False), (4, True)])
+@pytest.mark.parametrize("B,ahead", [(1, False), (1, True), (4, False), (4, True), (1, "normed"), (4, "normed")])
 def test_chained_layers(B, ahead):
     """Three chained layers: layer l+1's input is the layer normalisation of layer l's output, made
-    on the GPU (pi_layer_norm).  Exact prediction (pi_ffn_layer) or look-ahead (pi_ffn_layer_ahead:
-    layer l+1's hidden layer from layer l's input).  Each layer against the oracle on the input the
-    GPU gave it: logits and lists from the predictor's input, the output over the GPU's list, and
-    the next input against the oracle's normalisation of the GPU's output."""
+    on the GPU (pi_layer_norm, or inside the layer call with pi_ffn_layer_normed).  Exact prediction
+    (pi_ffn_layer) or look-ahead (pi_ffn_layer_ahead: layer l+1's hidden layer from layer l's
+    input).  Each layer against the oracle on the input the GPU gave it: logits and lists from the
+    predictor's input, the output over the GPU's list, and the next input against the oracle's
+    normalisation of the GPU's output."""
     import activation_sparse_amd as pi
     torch = _dev()
     cfg = ph.small_case("cold40", d=512, N=2048, H=128, wdtype=synth.F16, gpu_frac=0.4, seed=29)
@@ -646,20 +647,33 @@ def test_chained_layers(B, ahead):
     torch.cuda.synchronize()
     rest = pi.PI_STAGE_ALL & ~pi.PI_STAGE_HIDDEN
     print(f"chained layers B={B} ahead={ahead}", flush=True)
-    if ahead:
-        b0 = bufs[0]
-        pi.pi_ffn_layer_stages(dls[0].layer, B, b0.x, 0.0, None, b0.y, b0.logits, b0.A_g, b0.K, b0.A_c, b0.K_c,
-                               b0.ws_layer, pi.PI_STAGE_HIDDEN)
-    for l in range(nl):
-        b = bufs[l]
-        if ahead and l + 1 < nl:
-            pi.pi_ffn_layer_ahead(dls[l].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c,
-                                  b.ws_layer, rest, dls[l + 1].layer, bufs[l + 1].ws_layer)
-        else:
-            pi.pi_ffn_layer_stages(dls[l].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c,
-                                   b.ws_layer, rest if ahead else pi.PI_STAGE_ALL)
-        if l + 1 < nl:
-            pi.pi_layer_norm(B, cfg.d, b.y, bufs[l + 1].x, 1e-5)
+    if ahead == "normed":
+        # layer l >= 1 normalises layer l-1's output itself and reports the row it used in x
+        ahead = False
+        for l in range(nl):
+            b = bufs[l]
+            if l == 0:
+                pi.pi_ffn_layer(dls[0].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c, b.ws_layer)
+                continue
+            need = pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER_NORMED, B, cfg.d, specs[l].H, cfg.N, specs[l].n_g)
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+            pi.pi_ffn_layer_normed(dls[l].layer, B, bufs[l - 1].y, 1e-5, 0.0, None, b.y, b.logits, b.A_g, b.K,
+                                   b.A_c, b.K_c, ws, x_out=b.x)
+    else:
+        if ahead:
+            b0 = bufs[0]
+            pi.pi_ffn_layer_stages(dls[0].layer, B, b0.x, 0.0, None, b0.y, b0.logits, b0.A_g, b0.K, b0.A_c, b0.K_c,
+                                   b0.ws_layer, pi.PI_STAGE_HIDDEN)
+        for l in range(nl):
+            b = bufs[l]
+            if ahead and l + 1 < nl:
+                pi.pi_ffn_layer_ahead(dls[l].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c,
+                                      b.ws_layer, rest, dls[l + 1].layer, bufs[l + 1].ws_layer)
+            else:
+                pi.pi_ffn_layer_stages(dls[l].layer, B, b.x, 0.0, None, b.y, b.logits, b.A_g, b.K, b.A_c, b.K_c,
+                                       b.ws_layer, rest if ahead else pi.PI_STAGE_ALL)
+            if l + 1 < nl:
+                pi.pi_layer_norm(B, cfg.d, b.y, bufs[l + 1].x, 1e-5)
     torch.cuda.synchronize()
     xs = [b.x.cpu().numpy() for b in bufs]
     for l in range(nl):
@@ -677,3 +691,65 @@ def test_chained_layers(B, ahead):
         assert ph.rel_err(y, ph.oracle_ffn_on_ids(spec, xs[l], spec.T_g[A_g])) <= ph.RTOL, l
         if l + 1 < nl:
             assert np.max(np.abs(xs[l + 1].astype(np.float64) - orc.layer_norm(y, 1e-5))) <= LN_ATOL, l
+
+
+@pytest.mark.parametrize("case,B", [("opt-30b", 1), ("gated", 1), ("i4ffn", 1), ("opt-30b", 4), ("gated", 3)])
+def test_normed_layer_is_the_layer_on_its_normalised_input(case, B):
+    """pi_ffn_layer_normed(y_prev) gives bit for bit what pi_ffn_layer gives on the normalised row it
+    reports in x_out (at batch 1 the predictor's kernel and the FC1 kernel normalise with the same
+    two statistics, so both see x_out's values); x_out is the oracle's layer normalisation within
+    the normalisation bound; the result against the oracle on that x; y_prev == y (in place) gives
+    the same bits.  Batch 1 runs the fused kernels, other batches normalise first (x_out then equals
+    pi_layer_norm's output bit for bit)."""
+    import activation_sparse_amd as pi
+    torch = _dev()
+    if case == "opt-30b":
+        cfg, layer = synth.CONFIGS["opt-30b"], 7
+    elif case == "gated":
+        cfg, layer = ph.small_case("ln-gated", d=1024, N=4096, H=256, wdtype=synth.F16, gated=True, seed=41), 0
+    else:
+        cfg, layer = ph.small_case("ln-i4", d=1024, N=4096, H=256, wdtype=synth.I4G128, pdtype=synth.F16,
+                                   bdtype=synth.F16, gpu_frac=0.4, seed=43), 0
+    spec = synth.layer_spec(cfg, layer)
+    d, N = cfg.d, cfg.N
+    rng = np.random.default_rng(B * 131 + d)
+    y_prev = (rng.standard_normal((B, d)) * 0.07 + 0.02).astype(np.float32)
+    dl = ph.DeviceLayer(spec)
+    n_c = len(spec.T_c)
+    b1, b2, b3 = (ph.DeviceBuffers(cfg, spec.H, spec.n_g, n_c, B) for _ in range(3))
+    ws = torch.empty(pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER_NORMED, B, d, spec.H, N, spec.n_g), dtype=torch.uint8,
+                     device="cuda")
+    yp = torch.from_numpy(y_prev).cuda()
+    x_out = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    print(f"normed layer {case} B={B} d={d} N={N}", flush=True)
+    pi.pi_ffn_layer_normed(dl.layer, B, yp, 1e-5, 0.0, None, b1.y, b1.logits, b1.A_g, b1.K, b1.A_c, b1.K_c, ws,
+                           x_out=x_out)
+    b2.x.copy_(x_out)
+    pi.pi_ffn_layer(dl.layer, B, b2.x, 0.0, None, b2.y, b2.logits, b2.A_g, b2.K, b2.A_c, b2.K_c, b2.ws_layer)
+    yi = yp.clone()                                   # in place: y_prev is y
+    pi.pi_ffn_layer_normed(dl.layer, B, yi, 1e-5, 0.0, None, yi, None, b3.A_g, b3.K, b3.A_c, b3.K_c, ws)
+    ln_ref = torch.empty_like(yp)
+    pi.pi_layer_norm(B, d, yp, ln_ref, 1e-5)
+    torch.cuda.synchronize()
+    x = x_out.cpu().numpy()
+    assert np.max(np.abs(x.astype(np.float64) - orc.layer_norm(y_prev, 1e-5))) <= LN_ATOL
+    if B > 1:
+        assert np.array_equal(x.view(np.uint32), ln_ref.cpu().numpy().view(np.uint32))
+    K = int(b1.K.cpu()[0])
+    assert K == int(b2.K.cpu()[0]) and np.array_equal(b1.A_g.cpu().numpy()[:K], b2.A_g.cpu().numpy()[:K])
+    if n_c:
+        K_c = int(b1.K_c.cpu()[0])
+        assert K_c == int(b2.K_c.cpu()[0])
+        assert np.array_equal(b1.A_c.cpu().numpy()[:K_c], b2.A_c.cpu().numpy()[:K_c])
+    y1 = b1.y.cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), b2.y.cpu().numpy().view(np.uint32))
+    assert np.array_equal(b1.logits.cpu().numpy().view(np.uint32), b2.logits.cpu().numpy().view(np.uint32))
+    assert np.array_equal(y1.view(np.uint32), yi.cpu().numpy().view(np.uint32))
+    # against the oracle on the reported x
+    logits_or, _ = ph.oracle_predict(spec, x)
+    assert np.max(np.abs(b1.logits.cpu().numpy().astype(np.float64) - logits_or)) <= ph.LOGIT_ATOL
+    A_g = b1.A_g.cpu().numpy()[:K]
+    A_g_or, _ = orc.compact(logits_or, 0.0, spec.T_g, None)
+    _, out_g, asc_g = ph.list_check(A_g, A_g_or, spec.T_g, logits_or, 0.0)
+    assert K > 0 and out_g == 0 and asc_g
+    assert ph.rel_err(y1, ph.oracle_ffn_on_ids(spec, x, spec.T_g[A_g])) <= ph.RTOL
