@@ -18,10 +18,11 @@ PI_RELU, PI_GATED_RELU = 0, 1
 PI_OK, PI_EINVAL, PI_EWORKSPACE, PI_EUNSUPPORTED, PI_EHIP = 0, 1, 2, 3, 4
 PI_OP_PREDICT, PI_OP_COMPACT, PI_OP_SPARSE_FFN, PI_OP_MERGE, PI_OP_FFN_LAYER, PI_OP_PREDICT_OUTPUT = 0, 1, 2, 3, 4, 5
 PI_OP_FFN_LAYER_NORMED = 6
+PI_READ_PROBE_DEPTH, PI_READ_PROBE_BLOCKS_PER_CU = 16, 8
 PI_STAGE_HIDDEN, PI_STAGE_OUTPUT, PI_STAGE_FC1, PI_STAGE_FC2, PI_STAGE_SUM, PI_STAGE_ALL = 1, 2, 4, 8, 16, 31
 PI_MAX_BATCH = 32
 PI_MAX_NEURONS = 65536
-PI_ABI_VERSION = 2
+PI_ABI_VERSION = 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpi.so")
@@ -70,7 +71,7 @@ def load():
         L.pi_merge.argtypes = [P, I, I, P, P, P, _Vec]
         L.pi_layer_norm.argtypes = [P, I, I, P, C.c_float, P]
         L.pi_layer_norm.restype = C.c_int
-        L.pi_read_probe.argtypes = [P, P, C.c_size_t, I, P]
+        L.pi_read_probe.argtypes = [P, P, C.c_size_t, I, I, P]
         L.pi_read_probe.restype = C.c_int
         L.pi_table_bytes.argtypes = [I]
         L.pi_table_bytes.restype = C.c_size_t
@@ -185,9 +186,10 @@ def pi_sparse_ffn(B, d, n_g, kind, x, W1: Matrix, b1: Vector, Wup: Optional[Matr
            "pi_sparse_ffn")
 
 
-def pi_read_probe(buf, nbytes: int, out, blocks: int = 0, stream=None) -> None:
-    """Streaming read of nbytes of buf (the bandwidth reference); out: uint32 [4 * blocks]."""
-    _check(load().pi_read_probe(_stream(stream), _ptr(buf), int(nbytes), int(blocks), _ptr(out)), "pi_read_probe")
+def pi_read_probe(buf, nbytes: int, out, blocks: int = 0, stream=None, depth: int = 0) -> None:
+    """The streaming-read reference: read nbytes of buf once (blocks / depth 0: the library's defaults)."""
+    _check(load().pi_read_probe(_stream(stream), _ptr(buf), int(nbytes), int(blocks), int(depth), _ptr(out)),
+           "pi_read_probe")
 
 
 def pi_layer_norm(B, d, y, x, eps: float = 1e-5, stream=None) -> None:

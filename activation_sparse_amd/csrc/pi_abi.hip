@@ -511,10 +511,12 @@ int pi_layer_norm(void* stream, int32_t B, int32_t d, const float* y, float eps,
   return hip_status(pi::launch_layer_norm(B, d, y, eps, x, static_cast<hipStream_t>(stream)));
 }
 
-int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, uint32_t* out) {
+int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, int32_t depth, uint32_t* out) {
   if (!buf || !out || bytes == 0 || bytes % 16 != 0 || !aligned16(buf) || blocks > 65536) return PI_EINVAL;
-  if (blocks <= 0) blocks = 8 * pi::kNumCU;
-  return hip_status(pi::launch_read_probe(buf, (int64_t)bytes, blocks, out, static_cast<hipStream_t>(stream)));
+  if (depth == 0) depth = PI_READ_PROBE_DEPTH;
+  if (depth != 4 && depth != 8 && depth != 16 && depth != 32) return PI_EINVAL;
+  if (blocks <= 0) blocks = PI_READ_PROBE_BLOCKS_PER_CU * pi::kNumCU;
+  return hip_status(pi::launch_read_probe(buf, (int64_t)bytes, blocks, depth, out, static_cast<hipStream_t>(stream)));
 }
 
 namespace {

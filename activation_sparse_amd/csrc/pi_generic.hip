@@ -204,17 +204,18 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(int B, int N, const
 }
 
 // Streaming read: 256 threads per block, grid-stride over 16-byte vectors,
-// eight loads per lane in flight; each wave's XOR of what it read is stored.
+// D loads per lane in flight; each wave's XOR of what it read is stored.
+template <int D>
 __global__ __launch_bounds__(256) void k_read_probe(const uint4* __restrict__ p, int64_t n16, uint32_t* out) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
-    uint4 v[8];
+  for (; i + (D - 1) * stride < n16; i += D * stride) {
+    uint4 v[D];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = p[i + q * stride];
+    for (int q = 0; q < D; ++q) v[q] = p[i + q * stride];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
+    for (int q = 0; q < D; ++q) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
   }
   for (; i < n16; i += stride) {
     const uint4 v = p[i];
@@ -422,9 +423,16 @@ hipError_t launch_compact(int B, int N, const float* logits, float tau, const in
   return hipGetLastError();
 }
 
-hipError_t launch_read_probe(const void* buf, int64_t bytes, int blocks, uint32_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)blocks), dim3(256), 0, s, static_cast<const uint4*>(buf),
-                     bytes / 16, out);
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int blocks, int depth, uint32_t* out, hipStream_t s) {
+  const uint4* p = static_cast<const uint4*>(buf);
+  const dim3 g((unsigned)blocks), t(256);
+  switch (depth) {
+    case 4: hipLaunchKernelGGL(k_read_probe<4>, g, t, 0, s, p, bytes / 16, out); break;
+    case 8: hipLaunchKernelGGL(k_read_probe<8>, g, t, 0, s, p, bytes / 16, out); break;
+    case 16: hipLaunchKernelGGL(k_read_probe<16>, g, t, 0, s, p, bytes / 16, out); break;
+    case 32: hipLaunchKernelGGL(k_read_probe<32>, g, t, 0, s, p, bytes / 16, out); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -40,7 +40,7 @@ hipError_t launch_compact(int B, int N, const float* logits, float tau, const in
 
 // The lists from the activation words.
 hipError_t launch_layer_norm(int B, int d, const float* y, float eps, float* x, hipStream_t s);
-hipError_t launch_read_probe(const void* buf, int64_t bytes, int blocks, uint32_t* out, hipStream_t s);
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int blocks, int depth, uint32_t* out, hipStream_t s);
 hipError_t launch_list(const ListCtx& c, int n_g, hipStream_t s);
 
 // Neuron-major axpy over listed rows: out[b,:] += a[b, j] * W[list[j], :]

@@ -57,7 +57,7 @@ def parse():
                     help="skip the host-side placement-solver report")
     ap.add_argument("--leg", default=None, metavar="NAME",
                     help="run one leg alone and print its result instead of the benchmark line: truth, chained, "
-                         "placement or config:KEY[:STRIDE] (for a profiler run over just its kernels)")
+                         "placement, read-probe or config:KEY[:STRIDE] (for a profiler run over just its kernels)")
     ap.add_argument("--placement-steps", type=int, default=16,
                     help="steps of the fixed-rule vs solver-table timing on the LLaMA-13B gated 40%% stack, "
                          "GPU side and hybrid (0 = skip)")
@@ -297,6 +297,7 @@ def rocprof_summary(roots, copy_mib):
     import statistics as st
     out = []
     scaled = {}
+    rdreq = {}
     for root in roots:
         for path in sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)):
             rows = list(csv.DictReader(open(path)))
@@ -327,8 +328,12 @@ def rocprof_summary(roots, copy_mib):
             for r in rows:
                 k = _short_kernel(r["Kernel_Name"])
                 per.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
+                if r["Counter_Name"].startswith("TCC_EA0_RDREQ"):
+                    rdreq.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
             out.append(f"counters: {path} ({len(rows)} records)")
             for c in sorted({c for c, _ in per}):
+                if c.startswith("TCC_"):       # raw request counts: summarised by size below
+                    continue
                 scale = None
                 copy = per.get((c, "__amd_rocclr_copyBuffer"))
                 if copy:
@@ -346,6 +351,28 @@ def rocprof_summary(roots, copy_mib):
                         line += f"  scaled={b / 1e6:9.3f} MB per dispatch"
                     out.append(line)
             out.append("")
+    # read requests by size (a second reading of the read traffic, independent of FETCH_SIZE's formula):
+    # bytes = 128 * RDREQ_128B + 64 * RDREQ_64B + 32 * RDREQ_32B per dispatch
+    sized = {c: w for c, w in (("TCC_EA0_RDREQ_128B_sum", 128), ("TCC_EA0_RDREQ_64B_sum", 64),
+                               ("TCC_EA0_RDREQ_32B_sum", 32))}
+    if all(any(c == cc for cc, _ in rdreq) for c in sized):
+        out.append("read requests by size (TCC_EA0_RDREQ_{128B,64B,32B}_sum), bytes per dispatch:")
+        for k in sorted({k for _, k in rdreq}):
+            if not (k.startswith("k_") or k == "__amd_rocclr_copyBuffer"):
+                continue
+            b = sum(w * st.mean(rdreq[(c, k)]) for c, w in sized.items() if (c, k) in rdreq)
+            tot = st.mean(rdreq[("TCC_EA0_RDREQ_sum", k)]) if ("TCC_EA0_RDREQ_sum", k) in rdreq else float("nan")
+            n128 = st.mean(rdreq[("TCC_EA0_RDREQ_128B_sum", k)]) if ("TCC_EA0_RDREQ_128B_sum", k) in rdreq else 0.0
+            line = f"  {k:26s} {b / 1e6:10.3f} MB  (requests {tot:12.0f}, of them 128-byte {n128:12.0f})"
+            if k == "__amd_rocclr_copyBuffer":
+                copies = [v for v in rdreq[("TCC_EA0_RDREQ_128B_sum", k)]]
+                big = max(copies)
+                sel = [i for i, v in enumerate(copies) if v >= 0.99 * big]
+                bb = sum(w * st.mean([rdreq[(c, k)][i] for i in sel]) for c, w in sized.items() if (c, k) in rdreq)
+                line = (f"  plain copy of {copy_mib} MiB ({len(sel)} dispatches): {bb / 1e6:.3f} MB read by these "
+                        f"requests, {bb / (copy_mib * 2**20):.4f} of its true bytes")
+            out.append(line)
+        out.append("")
     ks = sorted({k for _, k in scaled})
     if any(("FETCH_SIZE", k) in scaled and ("WRITE_SIZE", k) in scaled for k in ks):
         out.append("HBM traffic per dispatch (scaled FETCH_SIZE + WRITE_SIZE):")
@@ -1005,6 +1032,39 @@ def placement_report(keys):
     return out
 
 
+def read_probe_sweep(sizes=(63137536, 2**30), depths=(4, 8, 16, 32), per_cu=(1, 2, 4, 8, 16, 32), n_rep=20):
+    """The streaming-read reference over its settings: loads in flight per lane x workgroups per
+    compute unit, for a kernel-sized read and 1 GiB.  Successive launches read different regions of
+    a 2 GiB buffer (no launch finds its bytes in the 256 MB last-level cache from the one before),
+    back to back after one warm-up launch; GB/s of each setting and the best."""
+    import torch
+    import activation_sparse_amd as pi
+    probe = torch.empty(2**29 + 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(4 * 256 * max(per_cu), dtype=torch.int32, device="cuda")
+    res = {}
+    for nb in sizes:
+        nb = nb // 16 * 16
+        regions = 2**31 // nb
+        views = [probe[k * (nb // 4):(k + 1) * (nb // 4)] for k in range(regions)]
+        table = {}
+        for depth in depths:
+            for pc in per_cu:
+                blocks = 256 * pc
+                pi.pi_read_probe(views[0], nb, out, blocks, depth=depth)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for k in range(n_rep):
+                    pi.pi_read_probe(views[(k + 1) % regions], nb, out, blocks, depth=depth)
+                e1.record()
+                torch.cuda.synchronize()
+                table[f"depth {depth} x {pc}/CU"] = round(nb * n_rep / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        best = max(table, key=table.get)
+        res[f"{nb / 1e6:.1f} MB"] = {"gbps": table, "best": best, "best_gbps": table[best]}
+        log(f"read probe {nb / 1e6:.1f} MB: best {best} at {table[best]} GB/s")
+    del probe, out
+    return res
+
+
 def placement_bench(key, steps, warmup, hybrid_steps):
     """The offline placement solver's tables against the fixed per-layer top-share rule on the
     GPU, on the same stack (`key`, whose gpu_frac sets the budget): each variant's layers are built
@@ -1159,7 +1219,8 @@ def hybrid_bench(cfg, specs, dls, steps, warmup, light=False):
 
 def run_leg(args):
     """One leg alone, so that a profiler run holds just its kernels: 'truth' or 'chained' (on
-    --config's stack), 'placement', or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
+    --config's stack), 'placement', 'read-probe' (the streaming-read reference's sweep), or
+    'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
     import torch
     import synth
     from synth.device import DeviceLayer
@@ -1180,10 +1241,13 @@ def run_leg(args):
         dls = [DeviceLayer(s, "cuda:0") for s in specs]
         torch.cuda.synchronize()
         res = chained_bench(cfg, specs, dls, args.chained_steps, 3)
+    elif name == "read-probe":
+        res = read_probe_sweep()
     elif name == "placement":
         res = placement_bench("llama-13b-gated-40", args.placement_steps, 2, args.placement_steps)
     else:
-        raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, config:KEY[:STRIDE])")
+        raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, read-probe, "
+                         "config:KEY[:STRIDE])")
     return {"leg": args.leg, "result": res}
 
 
@@ -1377,7 +1441,8 @@ def main():
                 "bytes_per_launch": round(mean_bytes[iso]), "avg_launch_us": round(mean_ms[iso] * 1e3, 2)}
 
     # the streaming-read reference: a plain read of the dominant kernel's bytes per launch, of one
-    # layer-token's bytes and of 1 GiB, best over a few grid sizes, back to back on the launch stream.
+    # layer-token's bytes and of 1 GiB, best over loads in flight per lane and grid sizes, back to
+    # back on the launch stream.
     # Successive launches read different regions of a 2 GiB buffer, as the layers read different
     # weights, so that no launch finds its bytes in the last-level cache (256 MB) from the one before.
     stream_read = {}
@@ -1388,13 +1453,13 @@ def main():
         best = 0.0
         regions = 2**31 // nb
         views = [probe[k * (nb // 4):(k + 1) * (nb // 4)] for k in range(regions)]
-        for blocks in (1024, 2048, 4096, 8192):
-            pi.pi_read_probe(views[0], nb, probe_out, blocks)
+        for depth, blocks in [(dp, 256 * pc) for dp in (8, 16) for pc in (1, 2, 4, 8, 16, 32)]:
+            pi.pi_read_probe(views[0], nb, probe_out, blocks, depth=depth)
             r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             n_rep = 20
             r0.record()
             for k in range(n_rep):
-                pi.pi_read_probe(views[(k + 1) % regions], nb, probe_out, blocks)
+                pi.pi_read_probe(views[(k + 1) % regions], nb, probe_out, blocks, depth=depth)
             r1.record()
             torch.cuda.synchronize()
             best = max(best, nb * n_rep / (r0.elapsed_time(r1) * 1e-3) / 1e9)

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PI_ABI_VERSION 2
+#define PI_ABI_VERSION 3
 #define PI_MAX_BATCH 32
 /* Largest neuron count N of pi_compact and the layer entry points: each
  * workgroup that builds the active lists holds the activation decision of
@@ -344,14 +344,19 @@ int pi_ffn_layer_normed(void* stream, const pi_layer* layer, int32_t B, const fl
                         int32_t* A_c, int32_t* K_c, float* x_out, void* ws, size_t ws_bytes);
 
 /* The streaming-read reference that the kernels' bandwidths are read against:
- * reads `bytes` bytes of `buf` once, in 16-byte vectors, with `blocks`
- * workgroups of 256 threads (blocks <= 0: 8 per compute unit) each keeping
- * eight loads per lane in flight, and writes the XOR of the words each wave
- * read to out[4 * block + wave] (so that no load can be dropped).
+ * reads `bytes` bytes of `buf` once, in 16-byte vectors, grid-stride, with
+ * `blocks` workgroups of 256 threads (blocks <= 0: PI_READ_PROBE_BLOCKS_PER_CU
+ * per compute unit) each keeping `depth` loads per lane in flight (4, 8, 16
+ * or 32; 0: PI_READ_PROBE_DEPTH), and writes the XOR of the words each wave
+ * read to out[4 * block + wave] (so that no load can be dropped).  The
+ * defaults are the fastest setting of a sweep over depth and grid size on
+ * MI355X.
  * buf: device, 16-byte aligned; bytes a multiple of 16; out: device uint32
  * [4 * blocks].  Errors: PI_EINVAL for a NULL pointer, bytes == 0 or not a
- * multiple of 16, or blocks > 65536. */
-int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, uint32_t* out);
+ * multiple of 16, blocks > 65536, or another depth. */
+#define PI_READ_PROBE_DEPTH 16
+#define PI_READ_PROBE_BLOCKS_PER_CU 8
+int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, int32_t depth, uint32_t* out);
 
 /* Workspace bytes an entry point needs for these sizes (0 when none).
  * Arguments an op does not use are ignored. */

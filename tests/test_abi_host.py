@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     L = pi.load()
     for name in declared_symbols():
         assert hasattr(L, name), name
-    assert L.pi_abi_version() == pi.PI_ABI_VERSION == 2
+    assert L.pi_abi_version() == pi.PI_ABI_VERSION == 3
 
 
 def test_status_strings():
@@ -210,6 +210,8 @@ def test_read_probe_rejects_bad_arguments():
     assert status(pi.pi_read_probe, FAKE, 1024, FAKE, 65537, 0) == pi.PI_EINVAL
     assert status(pi.pi_read_probe, FAKE, 1024, None, 0, 0) == pi.PI_EINVAL
     assert status(pi.pi_read_probe, FAKE + 8, 1024, FAKE, 0, 0) == pi.PI_EINVAL      # unaligned
+    for depth in (1, 3, 12, 64, -8):
+        assert status(pi.pi_read_probe, FAKE, 1024, FAKE, 0, 0, depth) == pi.PI_EINVAL   # unknown depth
 
 
 def test_layer_norm_rejects_bad_arguments():

@@ -306,8 +306,10 @@ def test_lookahead_prediction_on_two_streams(B):
         assert ph.rel_err(b.y.cpu().numpy(), y_or) <= ph.RTOL, l
 
 
-@pytest.mark.parametrize("nbytes,blocks", [(16, 1), (4096 + 48, 3), (63 * 2**20 + 16, 0), (2**26, 4096)])
-def test_read_probe_reads_every_word(nbytes, blocks):
+@pytest.mark.parametrize("nbytes,blocks,depth", [(16, 1, 0), (4096 + 48, 3, 4), (63 * 2**20 + 16, 0, 0),
+                                                  (2**26, 4096, 8), (2**26 + 16 * 37, 512, 16),
+                                                  (2**20 + 16 * 5, 2048, 32), (16 * 31, 1, 32)])
+def test_read_probe_reads_every_word(nbytes, blocks, depth):
     """The streaming-read reference reads each 16-byte vector once: the XOR of what every wave
     reports equals the XOR of all the buffer's words (a skipped or repeated vector changes it)."""
     import activation_sparse_amd as pi
@@ -315,10 +317,10 @@ def test_read_probe_reads_every_word(nbytes, blocks):
     g = np.random.default_rng(nbytes)
     host = g.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
     buf = torch.from_numpy(host.view(np.int32)).cuda()
-    nb = blocks if blocks > 0 else 8 * 256
+    nb = blocks if blocks > 0 else pi.PI_READ_PROBE_BLOCKS_PER_CU * 256
     out = torch.zeros(4 * nb, dtype=torch.int32, device="cuda")
-    print(f"read probe {nbytes} B, {nb} blocks", flush=True)
-    pi.pi_read_probe(buf, nbytes, out, blocks)
+    print(f"read probe {nbytes} B, {nb} blocks, depth {depth}", flush=True)
+    pi.pi_read_probe(buf, nbytes, out, blocks, depth=depth)
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
