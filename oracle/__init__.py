@@ -59,6 +59,11 @@ def lib():
         L.or_dense_ffn.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, _OrMat, _OrVec, _OrMat, _OrMat, _OrVec, P]
         L.or_merge.argtypes = [C.c_int, C.c_int, P, P, C.c_int, _OrVec, P]
         L.or_layer_norm.argtypes = [C.c_int, C.c_int, P, C.c_double, P]
+        L.or_double_to_f16.argtypes = [C.c_double]
+        L.or_double_to_f16.restype = C.c_uint16
+        L.or_attn_decode.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, _OrMat, _OrVec, _OrMat, _OrVec,
+                                     C.c_float, _OrMat, _OrVec, _OrMat, _OrVec, _OrMat, _OrVec, _OrMat, _OrVec, P, P,
+                                     C.c_int, P, P, P, P, P, P]
         L.or_set_threads.argtypes = [C.c_int]
         L.or_get_threads.restype = C.c_int
         _lib = L
@@ -198,3 +203,35 @@ def layer_norm(y: np.ndarray, eps: float) -> np.ndarray:
     x = np.empty((B, d), np.float64)
     lib().or_layer_norm(B, d, y.ctypes.data, float(eps), x.ctypes.data)
     return x
+
+
+def double_to_f16(v: float) -> int:
+    """fp16 bits of v, round to nearest even (the oracle's own conversion)."""
+    return int(lib().or_double_to_f16(float(v)))
+
+
+def attn_decode(x: np.ndarray, Pa1: Mat, ca1: Vec, Pa2: Mat, ca2: Vec, tau: float, Wq: Mat, bq: Vec, Wk: Mat,
+                bk: Vec, Wv: Mat, bv: Vec, WoT: Mat, bo: Vec, Kc: np.ndarray, Vc: np.ndarray, n_heads: int,
+                d_h: int, t: int) -> dict:
+    """Self-attention block with head sparsity at decode (see or_attn_decode in oracle.h).
+    x: [d] float32; Kc, Vc: uint16 fp16 bits [n_heads, L_max, d_h] (positions < t are read).
+    Returns head_logits [n_heads] float64, heads (ascending active heads) int32, k_new and v_new
+    [d] uint16 fp16 bits (this token's cache entry), y [d] float64."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    d = x.shape[0]
+    Kc = np.ascontiguousarray(Kc, dtype=np.uint16)
+    Vc = np.ascontiguousarray(Vc, dtype=np.uint16)
+    L_max = Kc.shape[1]
+    assert Kc.shape == (n_heads, L_max, d_h) and Vc.shape == Kc.shape and n_heads * d_h == d and 0 <= t < L_max
+    Ha = Pa1.rows
+    logits = np.empty(n_heads, np.float64)
+    heads = np.empty(n_heads, np.int32)
+    na = np.zeros(1, np.int32)
+    k_new = np.empty(d, np.uint16)
+    v_new = np.empty(d, np.uint16)
+    y = np.empty(d, np.float64)
+    lib().or_attn_decode(d, n_heads, d_h, Ha, int(t), x.ctypes.data, Pa1._c(), ca1._c(), Pa2._c(), ca2._c(),
+                         float(tau), Wq._c(), bq._c(), Wk._c(), bk._c(), Wv._c(), bv._c(), WoT._c(), bo._c(),
+                         Kc.ctypes.data, Vc.ctypes.data, L_max, logits.ctypes.data, heads.ctypes.data, na.ctypes.data,
+                         k_new.ctypes.data, v_new.ctypes.data, y.ctypes.data)
+    return {"head_logits": logits, "heads": heads[:int(na[0])].copy(), "k_new": k_new, "v_new": v_new, "y": y}

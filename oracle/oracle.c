@@ -154,3 +154,83 @@ void or_layer_norm(int B, int d, const float* y, double eps, double* x) {
     for (int k = 0; k < d; ++k) x[(size_t)b * d + k] = ((double)r[k] - mu) / sd;
   }
 }
+
+uint16_t or_double_to_f16(double v) {
+  const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+  if (isnan(v)) return 0x7e00u;
+  const double a = fabs(v);
+  if (a >= 65520.0) return sign | 0x7c00u;   /* at or past the midpoint above 65504: infinity */
+  int e = 0;
+  (void)frexp(a, &e);                        /* a = m 2^e, m in [0.5, 1) */
+  if (a != 0.0 && e - 1 >= -14) {            /* normal: a = (1 + f / 1024) 2^E */
+    int E = e - 1;
+    double r = nearbyint(ldexp(a, 10 - E));  /* in [1024, 2048], ties to even */
+    if (r >= 2048.0) { r = 1024.0; E += 1; }
+    if (E > 15) return sign | 0x7c00u;
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)r - 1024));
+  }
+  const double r = nearbyint(ldexp(a, 24));  /* subnormal: k 2^-24, ties to even */
+  if (r >= 1024.0) return (uint16_t)(sign | 0x0400u);
+  return (uint16_t)(sign | (uint16_t)r);
+}
+
+void or_attn_decode(int d, int n_heads, int d_h, int Ha, int t, const float* x, or_mat Pa1, or_vec ca1,
+                    or_mat Pa2, or_vec ca2, float tau, or_mat Wq, or_vec bq, or_mat Wk, or_vec bk, or_mat Wv,
+                    or_vec bv, or_mat WoT, or_vec bo, const uint16_t* Kc, const uint16_t* Vc, int L_max,
+                    double* head_logits, int32_t* heads, int32_t* n_active, uint16_t* k_new, uint16_t* v_new,
+                    double* y) {
+  /* the head predictor is the FFN predictor's MLP with one output per head */
+  or_predict(1, d, Ha, n_heads, x, Pa1, ca1, Pa2, ca2, NULL, head_logits);
+  int na = 0;
+  for (int h = 0; h < n_heads; ++h)
+    if ((float)head_logits[h] > tau) heads[na++] = h;
+  *n_active = na;
+  /* this token's cache entry, every head */
+#pragma omp parallel for schedule(static) num_threads(OR_NT)
+  for (int r = 0; r < d; ++r) {
+    k_new[r] = or_double_to_f16(dot_row(Wk, r, x, d) + or_vec_at(bk, r));
+    v_new[r] = or_double_to_f16(dot_row(Wv, r, x, d) + or_vec_at(bv, r));
+  }
+  /* the active heads' outputs */
+  double* o = (double*)calloc((size_t)n_heads * d_h, sizeof(double));
+  const double scale = 1.0 / sqrt((double)d_h);
+#pragma omp parallel for schedule(dynamic) num_threads(OR_NT)
+  for (int a = 0; a < na; ++a) {
+    const int h = heads[a];
+    double* q = (double*)malloc(sizeof(double) * (size_t)d_h);
+    double* e = (double*)malloc(sizeof(double) * (size_t)(t + 1));
+    for (int i = 0; i < d_h; ++i) q[i] = dot_row(Wq, (int64_t)h * d_h + i, x, d) + or_vec_at(bq, (int64_t)h * d_h + i);
+    double mx = -INFINITY;
+    for (int j = 0; j <= t; ++j) {
+      double s = 0.0;
+      for (int i = 0; i < d_h; ++i) {
+        const uint16_t kb = j < t ? Kc[((size_t)h * L_max + j) * d_h + i] : k_new[(size_t)h * d_h + i];
+        s += q[i] * or_f16_to_double(kb);
+      }
+      e[j] = s * scale;
+      if (e[j] > mx) mx = e[j];
+    }
+    double z = 0.0;
+    for (int j = 0; j <= t; ++j) { e[j] = exp(e[j] - mx); z += e[j]; }
+    for (int i = 0; i < d_h; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j <= t; ++j) {
+        const uint16_t vb = j < t ? Vc[((size_t)h * L_max + j) * d_h + i] : v_new[(size_t)h * d_h + i];
+        acc += e[j] * or_f16_to_double(vb);
+      }
+      o[(size_t)h * d_h + i] = acc / z;
+    }
+    free(q);
+    free(e);
+  }
+#pragma omp parallel for schedule(static) num_threads(OR_NT)
+  for (int c = 0; c < d; ++c) {
+    double s = or_vec_at(bo, c);
+    for (int a = 0; a < na; ++a) {
+      const int h = heads[a];
+      for (int i = 0; i < d_h; ++i) s += o[(size_t)h * d_h + i] * or_mat_at(WoT, (int64_t)h * d_h + i, c);
+    }
+    y[c] = s;
+  }
+  free(o);
+}

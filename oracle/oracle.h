@@ -22,6 +22,9 @@
  *    active neuron).
  *  - same page, section "神经元-觉察算子" (first decide whether a neuron is
  *    active, then process its row or column of the weight matrix).
+ *  - same page, background part on activation sparsity and section
+ *    "自适应稀疏预测器": or_attn_decode, the self-attention block with head
+ *    sparsity (see its declaration).
  *  - same page, background part on the MLP block (its output goes on to the
  *    next layer): or_layer_norm, the normalisation that turns one layer's
  *    output into the next layer's input in a chained stack, is not on the
@@ -80,6 +83,36 @@ void or_merge(int B, int d, const double* y_g, const double* y_c, int K_c, or_ve
  * mean and var_b the population variance (divided by d) of row b of y [B x d].
  * In-place use (x aliasing y) is not supported: y is fp32, x is double. */
 void or_layer_norm(int B, int d, const float* y, double eps, double* x);
+
+/* fp16 bits of v, rounded to nearest with ties to even (IEEE binary16: overflow to
+ * infinity, gradual underflow to subnormals). */
+uint16_t or_double_to_f16(double v);
+
+/* Self-attention block with head sparsity at decode, one new token at position t
+ * (CSDN summary, background part on activation sparsity: in the self-attention
+ * block nearly half of the heads contribute little, a sparsity of its own; section
+ * "自适应稀疏预测器": each layer has a predictor for the self-attention block beside
+ * the one for the MLP block, and computation is limited to what is predicted active).
+ *   head predictor  s_h = ca2[h] + sum_m Pa2[h,m] max(0, Pa1[m].x + ca1[m])  (or_predict
+ *                   with N = n_heads); head h active iff (float)s_h > tau; heads[] the
+ *                   active heads ascending, *n_active their count;
+ *   cache entry     k_new = fp16(Wk.x + bk), v_new = fp16(Wv.x + bv) for every head (the
+ *                   entry at position t, which later tokens attend to whatever this
+ *                   token's prediction);
+ *   attention       for active h with q = (Wq.x + bq)[h d_h .. h d_h + d_h - 1]:
+ *                   e_j = q . K_h[j] / sqrt(d_h) for j = 0..t, where K_h[j] is the cache's
+ *                   entry for j < t and k_new's head-h part for j = t (likewise V);
+ *                   o_h = sum_j softmax(e)_j V_h[j];
+ *   output          y = bo + sum over active h and i < d_h of o_h[i] WoT[h d_h + i, :].
+ * Weights: Wq, Wk, Wv [d x d] with row r the output element r (head r / d_h); WoT [d x d]
+ * with row h d_h + i the output-projection weights of head h's element i; Pa1 [Ha x d],
+ * Pa2 [n_heads x Ha].  Kc, Vc: fp16 bits [n_heads x L_max x d_h] (positions 0..t-1 read).
+ * head_logits [n_heads], heads [n_heads], k_new, v_new [d] (fp16 bits), y [d]. */
+void or_attn_decode(int d, int n_heads, int d_h, int Ha, int t, const float* x, or_mat Pa1, or_vec ca1,
+                    or_mat Pa2, or_vec ca2, float tau, or_mat Wq, or_vec bq, or_mat Wk, or_vec bk, or_mat Wv,
+                    or_vec bv, or_mat WoT, or_vec bo, const uint16_t* Kc, const uint16_t* Vc, int L_max,
+                    double* head_logits, int32_t* heads, int32_t* n_active, uint16_t* k_new, uint16_t* v_new,
+                    double* y);
 
 /* Threads the oracle's OpenMP loops may use (0 = library default). */
 void or_set_threads(int n);
