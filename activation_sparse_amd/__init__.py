@@ -30,7 +30,8 @@ LIB_PATH = os.path.join(_HERE, "libpi.so")
 EXPORTS = ("pi_predict", "pi_predict_output", "pi_compact", "pi_sparse_ffn", "pi_merge", "pi_table_bytes",
            "pi_table_prepare", "pi_ffn_layer", "pi_ffn_layer_stages", "pi_workspace_bytes", "pi_status_string",
            "pi_last_hip_error", "pi_abi_version", "pi_read_probe", "pi_ffn_layer_ahead",
-           "pi_layer_norm", "pi_ffn_layer_static", "pi_ffn_layer_normed")
+           "pi_layer_norm", "pi_ffn_layer_static", "pi_ffn_layer_normed", "pi_attn_decode",
+           "pi_attn_workspace_bytes")
 PI_STATIC_WORKSPACE_BYTES = 16 << 20
 
 
@@ -50,6 +51,13 @@ class _Layer(C.Structure):
     _fields_ = [("d", C.c_int32), ("N", C.c_int32), ("H", C.c_int32), ("n_g", C.c_int32), ("kind", C.c_int32),
                 ("cold", C.c_int32), ("P1", _Mat), ("c1", _Vec), ("P2", _Mat), ("c2", _Vec), ("table", C.c_void_p),
                 ("W1", _Mat), ("b1", _Vec), ("Wup", _Mat), ("W2", _Mat), ("b2", _Vec)]
+
+
+class _Attn(C.Structure):
+    _fields_ = [("d", C.c_int32), ("n_heads", C.c_int32), ("dh", C.c_int32), ("Ha", C.c_int32), ("L_max", C.c_int32),
+                ("Pa1", _Mat), ("ca1", _Vec), ("Pa2", _Mat), ("ca2", _Vec), ("Wq", _Mat), ("bq", _Vec), ("Wk", _Mat),
+                ("bk", _Vec), ("Wv", _Mat), ("bv", _Vec), ("WoT", _Mat), ("bo", _Vec), ("Kc", C.c_void_p),
+                ("Vc", C.c_void_p)]
 
 
 _lib = None
@@ -90,6 +98,10 @@ def load():
         L.pi_ffn_layer_normed.argtypes = [P, C.POINTER(_Layer), I, P, C.c_float, C.c_float, P, P, P, P, P, P, P, P,
                                           P, C.c_size_t]
         L.pi_ffn_layer_normed.restype = C.c_int
+        L.pi_attn_decode.argtypes = [P, C.POINTER(_Attn), I, P, C.c_float, P, P, P, P, P, C.c_size_t]
+        L.pi_attn_decode.restype = C.c_int
+        L.pi_attn_workspace_bytes.argtypes = [C.POINTER(_Attn)]
+        L.pi_attn_workspace_bytes.restype = C.c_size_t
         L.pi_workspace_bytes.argtypes = [I, I, I, I, I, I]
         L.pi_workspace_bytes.restype = C.c_size_t
         L.pi_status_string.argtypes = [I]
@@ -304,3 +316,49 @@ def pi_ffn_layer_stages(layer: Layer, B: int, x, tau: float, y_c, y, logits, A_g
     _check(load().pi_ffn_layer_stages(_stream(stream), C.byref(cl), B, _ptr(x), float(tau), _ptr(y_c), _ptr(y),
                                       _ptr(logits), _ptr(A_g), _ptr(K), _ptr(A_c), _ptr(K_c), _ptr(ws), nbytes,
                                       events, int(stages), _ptr(rows_read)), "pi_ffn_layer_stages")
+
+
+@dataclass
+class Attn:
+    """The self-attention block of pi_attn_decode: fp16 matrices (Pa1 [Ha, d], Pa2 [n_heads, Ha],
+    Wq / Wk / Wv [d, d] with row = output element, WoT [d, d] with row = head element), fp16 or
+    absent biases, and the fp16 caches Kc / Vc [n_heads, L_max, dh]."""
+    d: int
+    n_heads: int
+    dh: int
+    Ha: int
+    L_max: int
+    Pa1: Matrix
+    Pa2: Matrix
+    Wq: Matrix
+    Wk: Matrix
+    Wv: Matrix
+    WoT: Matrix
+    Kc: object
+    Vc: object
+    ca1: Optional[Vector] = None
+    ca2: Optional[Vector] = None
+    bq: Optional[Vector] = None
+    bk: Optional[Vector] = None
+    bv: Optional[Vector] = None
+    bo: Optional[Vector] = None
+
+    def _c(self) -> _Attn:
+        v = lambda b: (b or Vector(None, PI_F16))._c()
+        return _Attn(self.d, self.n_heads, self.dh, self.Ha, self.L_max, self.Pa1._c(), v(self.ca1), self.Pa2._c(),
+                     v(self.ca2), self.Wq._c(), v(self.bq), self.Wk._c(), v(self.bk), self.Wv._c(), v(self.bv),
+                     self.WoT._c(), v(self.bo), _ptr(self.Kc), _ptr(self.Vc))
+
+
+def pi_attn_workspace_bytes(attn: Attn) -> int:
+    c = attn._c()
+    return int(load().pi_attn_workspace_bytes(C.byref(c)))
+
+
+def pi_attn_decode(attn: Attn, t: int, x, tau: float, y, head_logits, heads, n_active, ws, ws_bytes=None,
+                   stream=None, _cstruct=None) -> None:
+    """One decode step of the attention block with head sparsity (position t)."""
+    nbytes = ws_bytes if ws_bytes is not None else ws.numel() * ws.element_size()
+    c = _cstruct if _cstruct is not None else attn._c()
+    _check(load().pi_attn_decode(_stream(stream), C.byref(c), int(t), _ptr(x), float(tau), _ptr(y),
+                                 _ptr(head_logits), _ptr(heads), _ptr(n_active), _ptr(ws), nbytes), "pi_attn_decode")

@@ -23,7 +23,7 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              # packed fp32 instructions stay off (the compiler would otherwise form them)
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-PI_SOURCES = ["pi_generic.hip", "pi_fast.hip", "pi_fc2.hip", "pi_mfma.hip", "pi_abi.hip"]
+PI_SOURCES = ["pi_generic.hip", "pi_fast.hip", "pi_fc2.hip", "pi_mfma.hip", "pi_attn.hip", "pi_abi.hip"]
 LIBHOST = os.path.join(PKG, "libpi_host.so")
 # the host (CPU) operator: no target-wide vector flags (its AVX2 path is chosen at run time),
 # no contraction of separate multiplies and adds (its sums have one fixed rounding order)

@@ -7,6 +7,7 @@
 #include <cmath>
 #include "../../include/pi.h"
 #include "pi_internal.h"
+#include "pi_attn.h"
 
 namespace {
 
@@ -509,6 +510,72 @@ int pi_layer_norm(void* stream, int32_t B, int32_t d, const float* y, float eps,
   const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
   if (xa != ya && xa < ya + nb && ya < xa + nb) return PI_EINVAL;   // partial overlap
   return hip_status(pi::launch_layer_norm(B, d, y, eps, x, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+// pi_attn_decode's workspace: g, q, the flags, the head logits, the chunk partials and the
+// heads' output-projection contributions.
+struct AttnWs {
+  float* g;
+  float* q;
+  int32_t* flag;
+  float* hlogit;
+  float* part;
+  float* ypart;
+  size_t bytes;
+};
+
+AttnWs attn_ws_layout(void* ws, const pi_attn& A) {
+  Carver c{static_cast<char*>(ws)};
+  AttnWs w{};
+  w.g = c.take<float>((size_t)A.Ha * 4);
+  w.q = c.take<float>((size_t)A.d * 4);
+  w.flag = c.take<int32_t>((size_t)A.n_heads * 4);
+  w.hlogit = c.take<float>((size_t)A.n_heads * 4);
+  w.part = c.take<float>((size_t)A.n_heads * pi::attn_chunks(A.L_max) * (A.dh + 2) * 4);
+  w.ypart = c.take<float>((size_t)A.n_heads * A.d * 4);
+  w.bytes = c.off;
+  return w;
+}
+
+bool f16_matrix(const pi_matrix& m) { return m.data && m.dtype == PI_F16 && aligned16(m.data); }
+bool f16_bias(const pi_vector& v) { return !v.data || v.dtype == PI_F16; }
+
+}  // namespace
+
+size_t pi_attn_workspace_bytes(const pi_attn* A) {
+  if (!A || A->d <= 0 || A->n_heads <= 0 || A->dh <= 0 || A->Ha <= 0 || A->L_max <= 0) return 0;
+  return attn_ws_layout(nullptr, *A).bytes;
+}
+
+int pi_attn_decode(void* stream, const pi_attn* A, int32_t t, const float* x, float tau, float* y,
+                   float* head_logits, int32_t* heads, int32_t* n_active, void* ws, size_t ws_bytes) {
+  if (!A || !x || !y || !heads || !n_active || !aligned16(x) || !aligned16(y)) return PI_EINVAL;
+  if (A->d <= 0 || A->n_heads <= 0 || A->dh <= 0 || A->Ha <= 0 || A->L_max <= 0 ||
+      (int64_t)A->n_heads * A->dh != A->d || t < 0 || t >= A->L_max)
+    return PI_EINVAL;
+  if (!pi::attn_supported(A->d, A->n_heads, A->dh, A->Ha)) return PI_EUNSUPPORTED;
+  if (!f16_matrix(A->Pa1) || !f16_matrix(A->Pa2) || !f16_matrix(A->Wq) || !f16_matrix(A->Wk) ||
+      !f16_matrix(A->Wv) || !f16_matrix(A->WoT) || !f16_bias(A->ca1) || !f16_bias(A->ca2) || !f16_bias(A->bq) ||
+      !f16_bias(A->bk) || !f16_bias(A->bv) || !f16_bias(A->bo) || !A->Kc || !A->Vc || !aligned16(A->Kc) ||
+      !aligned16(A->Vc))
+    return PI_EINVAL;
+  // the cache rows of a head are addressed with 32-bit offsets
+  if ((int64_t)A->L_max * A->dh * 2 >= ((int64_t)1 << 31)) return PI_EUNSUPPORTED;
+  if (ranges_overlap(x, (size_t)A->d * 4, y, (size_t)A->d * 4)) return PI_EINVAL;
+  if (!ws || !aligned16(ws)) return PI_EWORKSPACE;
+  const AttnWs w = attn_ws_layout(ws, *A);
+  if (ws_bytes < w.bytes) return PI_EWORKSPACE;
+  pi::AttnArgs a{};
+  a.d = A->d; a.n_heads = A->n_heads; a.dh = A->dh; a.Ha = A->Ha; a.L_max = A->L_max; a.t = t;
+  a.n_chunks = pi::attn_chunks(A->L_max); a.tau = tau; a.x = x;
+  a.Pa1 = A->Pa1.data; a.ca1 = A->ca1.data; a.Pa2 = A->Pa2.data; a.ca2 = A->ca2.data;
+  a.Wq = A->Wq.data; a.bq = A->bq.data; a.Wk = A->Wk.data; a.bk = A->bk.data; a.Wv = A->Wv.data; a.bv = A->bv.data;
+  a.WoT = A->WoT.data; a.bo = A->bo.data; a.Kc = A->Kc; a.Vc = A->Vc;
+  a.g = w.g; a.q = w.q; a.flag = w.flag; a.hlogit = w.hlogit; a.part = w.part; a.ypart = w.ypart;
+  a.y = y; a.logits_out = head_logits; a.heads = heads; a.n_active = n_active;
+  return hip_status(pi::launch_attn(a, static_cast<hipStream_t>(stream)));
 }
 
 int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, int32_t depth, uint32_t* out) {

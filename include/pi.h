@@ -343,6 +343,64 @@ int pi_ffn_layer_normed(void* stream, const pi_layer* layer, int32_t B, const fl
                         float tau, const float* y_c, float* y, float* logits, int32_t* A_g, int32_t* K,
                         int32_t* A_c, int32_t* K_c, float* x_out, void* ws, size_t ws_bytes);
 
+/* ---- Self-attention block with head sparsity at decode (batch 1) ----
+ * The pages note that in the self-attention block nearly half of the heads
+ * contribute little, a sparsity of its own beside the MLP block's (CSDN
+ * summary, background part on activation sparsity), and that a predictor per
+ * block (self-attention and MLP) limits the computation to what it predicts
+ * active (same page, section 自适应稀疏预测器).  One new token at position t:
+ *   head predictor  s_h = ca2[h] + Pa2[h] . max(0, Pa1 x + ca1) (the MLP of
+ *                   pi_predict with one output per head); head h is active iff
+ *                   s_h > tau (in fp32);
+ *   cache entry     K and V rows of every head: Kc[h][t] = fp16(Wk x + bk)
+ *                   (head h's part), Vc likewise (later tokens attend to this
+ *                   position whatever this token's prediction);
+ *   attention       active h only: q_h = (Wq x + bq)[h*dh ..]; over positions
+ *                   j = 0..t of the cache, softmax(q_h . Kc[h][j] / sqrt(dh))
+ *                   weights the rows Vc[h][j] into o_h;
+ *   output          y = bo + sum over active h of WoT[h*dh + i, :] o_h[i].
+ * A predicted-inactive head reads none of its query or output-projection
+ * rows and none of its cached positions. */
+typedef struct {
+  int32_t d;       /* model width, n_heads * dh */
+  int32_t n_heads; /* 1 .. 256 */
+  int32_t dh;      /* 64 or 128 */
+  int32_t Ha;      /* head predictor hidden size: a multiple of 4, at most 1024 */
+  int32_t L_max;   /* cache capacity in positions */
+  pi_matrix Pa1;   /* [Ha x d] */
+  pi_vector ca1;   /* [Ha] or NULL */
+  pi_matrix Pa2;   /* [n_heads x Ha], row per head */
+  pi_vector ca2;   /* [n_heads] or NULL */
+  pi_matrix Wq;    /* [d x d], row r = query element r (head r / dh) */
+  pi_vector bq;
+  pi_matrix Wk;    /* [d x d] */
+  pi_vector bk;
+  pi_matrix Wv;    /* [d x d] */
+  pi_vector bv;
+  pi_matrix WoT;   /* [d x d], row h*dh + i = output-projection weights of head h's element i */
+  pi_vector bo;
+  uint16_t* Kc;    /* device fp16 [n_heads x L_max x dh]: a head's positions are contiguous */
+  uint16_t* Vc;    /* device fp16 [n_heads x L_max x dh] */
+} pi_attn;
+
+/* One decode step of the attention block above.  Every matrix is fp16
+ * (PI_F16) and every bias fp16 or NULL; d at most 8192.  x [d] fp32, y [d]
+ * fp32 written; head_logits [n_heads] fp32 (optional, NULL = not stored);
+ * heads [n_heads] and *n_active (device int32) receive the ascending active
+ * heads and their count.  Positions 0..t-1 of the caches are read, position t
+ * is written for every head, and no other position is touched.
+ * ws: pi_attn_workspace_bytes(A) bytes, 16-byte aligned.  All pointers are
+ * device pointers except A.  Results are bitwise repeatable.
+ * Errors: PI_EINVAL for a NULL or unaligned pointer, t outside 0..L_max-1,
+ * inconsistent sizes, a matrix or bias of another dtype, or y overlapping x;
+ * PI_EUNSUPPORTED for dh other than 64 / 128, d above 8192, more than 256
+ * heads or Ha outside the bounds; PI_EWORKSPACE for a short workspace. */
+int pi_attn_decode(void* stream, const pi_attn* A, int32_t t, const float* x, float tau, float* y,
+                   float* head_logits, int32_t* heads, int32_t* n_active, void* ws, size_t ws_bytes);
+
+/* Workspace bytes of pi_attn_decode for this block (0 for NULL). */
+size_t pi_attn_workspace_bytes(const pi_attn* A);
+
 /* The streaming-read reference that the kernels' bandwidths are read against:
  * reads `bytes` bytes of `buf` once, in 16-byte vectors, grid-stride, with
  * `blocks` workgroups of 256 threads (blocks <= 0: PI_READ_PROBE_BLOCKS_PER_CU

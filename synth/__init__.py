@@ -35,6 +35,8 @@ import numpy as np
 
 F32, F16, I4G128 = 0, 1, 2
 TAG_P1, TAG_P2, TAG_W1, TAG_W2, TAG_WUP, TAG_X, TAG_YC, TAG_PERM, TAG_PROF, TAG_LAYER = range(1, 11)
+# the self-attention block's streams
+TAG_PA1, TAG_PA2, TAG_WQ, TAG_WK, TAG_WV, TAG_WO, TAG_KC, TAG_VC, TAG_XA, TAG_ABIAS, TAG_HEADS = range(11, 22)
 P_CAP = 0.95
 SQRT3 = math.sqrt(3.0)
 
@@ -338,6 +340,90 @@ def with_table(spec: LayerSpec, T_g: np.ndarray) -> LayerSpec:
     mask = np.zeros(N, bool)
     mask[T_g] = True
     return replace(spec, T_g=T_g, T_c=np.flatnonzero(~mask).astype(np.int32))
+
+
+# ----------------------------------------------------------------------------- attention blocks
+
+@dataclass(frozen=True)
+class AttnConfig:
+    """Self-attention blocks with head sparsity at decode: d = n_heads * dh, a head predictor with
+    Ha hidden units, fp16 weights and cache of L_max positions; head h active with probability
+    p_h, the p_h of a layer spread evenly over [p_lo, p_hi] in a seeded order of the heads."""
+    key: str
+    desc: str
+    n_layers: int
+    n_heads: int
+    dh: int
+    Ha: int
+    L_max: int
+    p_head: Tuple[float, float]
+    seed: int
+    bias_sigma: float = 0.02
+
+    @property
+    def d(self) -> int:
+        return self.n_heads * self.dh
+
+
+ATTN_CONFIGS = {
+    "attn-small": AttnConfig("attn-small", "small attention block, 8 heads x 64, d 512", 2, 8, 64, 64, 256, (0.2, 0.8), 31),
+    "attn-mid": AttnConfig("attn-mid", "attention block, 8 heads x 128, d 1024", 2, 8, 128, 128, 200, (0.2, 0.8), 32),
+    "attn-opt-30b": AttnConfig("attn-opt-30b", "OPT-30B-shaped self-attention, 48 layers, 56 heads x 128, d 7168, "
+                               "fp16, 1024 cached positions", 48, 56, 128, 256, 1024, (0.2, 0.8), 33),
+}
+
+
+@dataclass
+class AttnSpec:
+    cfg: AttnConfig
+    layer: int
+    p: np.ndarray               # per head activation probability
+    ca2: np.ndarray             # fp16 bits, the head predictor's output bias
+
+    def sigmas(self):
+        c = self.cfg
+        return {TAG_PA1: 1 / math.sqrt(c.d), TAG_PA2: 1 / math.sqrt(c.Ha), TAG_WQ: 1 / math.sqrt(c.d),
+                TAG_WK: 1 / math.sqrt(c.d), TAG_WV: 1 / math.sqrt(c.d), TAG_WO: 1 / math.sqrt(c.d),
+                TAG_KC: 1.0, TAG_VC: 1.0, TAG_XA: 1.0, TAG_ABIAS: c.bias_sigma}
+
+
+@functools.lru_cache(maxsize=64)
+def attn_spec(cfg: AttnConfig, layer: int) -> AttnSpec:
+    """Head probabilities and the head predictor's calibrated output bias: with x of unit variance
+    and ca1 = 0, g = ReLU(Pa1 x) has mean 1/sqrt(2 pi) and variance 1/2 - 1/(2 pi) per unit, so
+    logit_h = ca2_h + Pa2[h] . g is about normal with mean mu_h + ca2_h and deviation sd_h from the
+    stored row's sum and sum of squares; ca2_h = sd_h Phi^-1(p_h) - mu_h makes P(logit_h > 0) = p_h."""
+    lo, hi = cfg.p_head
+    order = permutation(cfg.seed, 1000 + layer, cfg.n_heads)
+    p = lo + (hi - lo) * (order.astype(np.float64) + 0.5) / cfg.n_heads
+    s1, s2 = row_stats(F16, cfg.seed, TAG_PA2, layer, cfg.n_heads, cfg.Ha, 1 / math.sqrt(cfg.Ha))
+    mu = s1 / math.sqrt(2 * math.pi)
+    sd = np.sqrt(s2 * (0.5 - 1 / (2 * math.pi)))
+    ca2 = to_stored(sd * ndtri(p) - mu, F16)
+    return AttnSpec(cfg, layer, p, ca2)
+
+
+def attn_x(cfg: AttnConfig, layer: int, step: int) -> np.ndarray:
+    data, _ = host_rows(F32, cfg.seed, TAG_XA, layer, cfg.d, 1.0, row_ids=x_row_ids(step, 1))
+    return data[0]
+
+
+def attn_host(spec: AttnSpec) -> dict:
+    """The block's stored values on the host (fp16 bits): Pa1 [Ha, d], Pa2 [n_heads, Ha], Wq / Wk /
+    Wv / WoT [d, d], biases bq / bk / bv / bo (row b of the bias stream), ca2, and the caches Kc /
+    Vc [n_heads, L_max, dh] (row h * L_max + j of their streams)."""
+    c, L, sg = spec.cfg, spec.layer, spec.sigmas()
+    out = {}
+    for name, tag, rows, cols in (("Pa1", TAG_PA1, c.Ha, c.d), ("Pa2", TAG_PA2, c.n_heads, c.Ha),
+                                  ("Wq", TAG_WQ, c.d, c.d), ("Wk", TAG_WK, c.d, c.d), ("Wv", TAG_WV, c.d, c.d),
+                                  ("WoT", TAG_WO, c.d, c.d)):
+        out[name] = host_rows(F16, c.seed, tag, L, cols, sg[tag], nrows=rows)[0]
+    b, _ = host_rows(F16, c.seed, TAG_ABIAS, L, c.d, sg[TAG_ABIAS], nrows=4)
+    out.update(bq=b[0].copy(), bk=b[1].copy(), bv=b[2].copy(), bo=b[3].copy(), ca2=spec.ca2)
+    for name, tag in (("Kc", TAG_KC), ("Vc", TAG_VC)):
+        out[name] = host_rows(F16, c.seed, tag, L, c.dh, 1.0, nrows=c.n_heads * c.L_max)[0].reshape(
+            c.n_heads, c.L_max, c.dh)
+    return out
 
 
 # ----------------------------------------------------------------------------- host tensors

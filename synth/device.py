@@ -133,3 +133,35 @@ class HostColdLayer:
         self.Wup = host_rows(synth.TAG_WUP) if cfg.gated else None
         b = np.ascontiguousarray(spec.b1[spec.T_c] if n_c else spec.b1[:1])
         self.b1 = Vector(b if cfg.bdtype == synth.F32 else b.view(np.uint16), PI_F32 if cfg.bdtype == synth.F32 else PI_F16)
+
+
+class DeviceAttn:
+    """One attention block's weights and caches, generated on the device (the host's bits)."""
+
+    def __init__(self, spec: synth.AttnSpec, device="cuda:0"):
+        torch = _torch()
+        from activation_sparse_amd import Attn, Matrix as M, Vector as V, PI_F16
+        c, L, sg = spec.cfg, spec.layer, spec.sigmas()
+        self.spec = spec
+        mats = {}
+        for name, tag, rows, cols in (("Pa1", synth.TAG_PA1, c.Ha, c.d), ("Pa2", synth.TAG_PA2, c.n_heads, c.Ha),
+                                      ("Wq", synth.TAG_WQ, c.d, c.d), ("Wk", synth.TAG_WK, c.d, c.d),
+                                      ("Wv", synth.TAG_WV, c.d, c.d), ("WoT", synth.TAG_WO, c.d, c.d)):
+            m = dev_matrix(rows, cols, synth.F16, device)
+            fill_matrix(m, synth.F16, c.seed, tag, L, cols, sg[tag])
+            mats[name] = m
+        bias = dev_matrix(4, c.d, synth.F16, device)
+        fill_matrix(bias, synth.F16, c.seed, synth.TAG_ABIAS, L, c.d, sg[synth.TAG_ABIAS])
+        self.bias = bias
+        self.caches = []
+        for tag in (synth.TAG_KC, synth.TAG_VC):
+            m = dev_matrix(c.n_heads * c.L_max, c.dh, synth.F16, device)
+            fill_matrix(m, synth.F16, c.seed, tag, L, c.dh, 1.0)
+            self.caches.append(m.data.view(c.n_heads, c.L_max, c.dh))
+        self.ca2 = dev_vector(spec.ca2, synth.F16, device)
+        self.mats = mats
+        self.attn = Attn(c.d, c.n_heads, c.dh, c.Ha, c.L_max, mats["Pa1"], mats["Pa2"], mats["Wq"], mats["Wk"],
+                         mats["Wv"], mats["WoT"], self.caches[0], self.caches[1], ca1=None, ca2=self.ca2,
+                         bq=V(bias.data[0], PI_F16), bk=V(bias.data[1], PI_F16), bv=V(bias.data[2], PI_F16),
+                         bo=V(bias.data[3], PI_F16))
+        self.attn_c = self.attn._c()

@@ -239,3 +239,93 @@ def assert_report(r: dict) -> None:
     assert r["logit_max_abs_err"] <= LOGIT_ATOL, r
     assert r["rel_err_ffn"] <= RTOL, r
     assert r["rel_err"] <= RTOL, r
+
+
+# ----------------------------------------------------------------------------- attention blocks
+
+def attn_oracle_inputs(h: dict, d: int):
+    """Oracle matrices and vectors of an attention block from synth.attn_host's fp16 bits."""
+    M = lambda k, cols: orc.Mat(h[k], orc.F16, cols)
+    V = lambda k: orc.Vec(h[k], orc.F16)
+    return dict(Pa1=M("Pa1", d), ca1=orc.Vec(None, orc.F16), Pa2=M("Pa2", h["Pa1"].shape[0]), ca2=V("ca2"),
+                Wq=M("Wq", d), bq=V("bq"), Wk=M("Wk", d), bk=V("bk"), Wv=M("Wv", d), bv=V("bv"), WoT=M("WoT", d),
+                bo=V("bo"))
+
+
+def f16_ulps(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance in fp16 units in the last place between two arrays of finite fp16 bits."""
+    def key(u):
+        u = u.astype(np.int32)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(key(np.asarray(a, np.uint16)) - key(np.asarray(b, np.uint16)))
+
+
+def run_attn_parity(cfg, layer: int = 0, t: int = 0, step: int = 0, tau: float = 0.0, device="cuda:0",
+                    dl=None, host=None):
+    """One decode step of an attention block on the GPU (pi_attn_decode) against the oracle: head
+    logits, the head list (exact outside the 1e-3 band around tau), y given the GPU's head set,
+    this position's cache entry (normwise within 1e-3 of the oracle's, about two fp16 units at its
+    largest element) and every other cache position untouched.  Returns a report dict."""
+    torch = _torch()
+    import activation_sparse_amd as pi
+    spec = synth.attn_spec(cfg, layer)
+    h = host if host is not None else synth.attn_host(spec)
+    if dl is None:
+        dl = synth.device.DeviceAttn(spec, device)
+    d, nh = cfg.d, cfg.n_heads
+    x = synth.attn_x(cfg, layer, step)
+    Kc0 = dl.caches[0].cpu().numpy().view(np.uint16).copy()
+    Vc0 = dl.caches[1].cpu().numpy().view(np.uint16).copy()
+    xd = torch.from_numpy(x).to(device)
+    y = torch.empty(d, dtype=torch.float32, device=device)
+    lg = torch.empty(nh, dtype=torch.float32, device=device)
+    heads = torch.full((nh,), -1, dtype=torch.int32, device=device)
+    na = torch.zeros(1, dtype=torch.int32, device=device)
+    ws = torch.empty(max(pi.pi_attn_workspace_bytes(dl.attn), 256), dtype=torch.uint8, device=device)
+    pi.pi_attn_decode(dl.attn, t, xd, tau, y, lg, heads, na, ws, _cstruct=dl.attn_c)
+    torch.cuda.synchronize()
+    n_act = int(na.cpu()[0])
+    heads_gpu = heads.cpu().numpy()[:n_act].copy()
+    Kc = dl.caches[0].cpu().numpy().view(np.uint16)
+    Vc = dl.caches[1].cpu().numpy().view(np.uint16)
+    o = attn_oracle_inputs(h, d)
+    ref = orc.attn_decode(x, o["Pa1"], o["ca1"], o["Pa2"], o["ca2"], tau, o["Wq"], o["bq"], o["Wk"], o["bk"], o["Wv"],
+                          o["bv"], o["WoT"], o["bo"], Kc0, Vc0, nh, cfg.dh, t)
+    logits_gpu = lg.cpu().numpy()
+    band = np.abs(ref["head_logits"] - tau) < 1e-3
+    on_gpu = np.zeros(nh, bool)
+    on_gpu[heads_gpu] = True
+    on_or = np.zeros(nh, bool)
+    on_or[ref["heads"]] = True
+    report = dict(cfg=cfg.key, layer=layer, t=t, n_active=n_act, n_active_oracle=len(ref["heads"]),
+                  logit_max_abs_err=float(np.max(np.abs(logits_gpu.astype(np.float64) - ref["head_logits"]))),
+                  list_outside_band=int(np.sum((on_gpu != on_or) & ~band)),
+                  ascending=bool(np.all(np.diff(heads_gpu) > 0)))
+    if not np.array_equal(on_gpu, on_or):
+        # the oracle again with the GPU's head set (output-bias sentinels select it)
+        ca2 = orc.Vec(np.where(on_gpu, 30000.0, -30000.0).astype(np.float16).view(np.uint16), orc.F16)
+        ref = orc.attn_decode(x, o["Pa1"], o["ca1"], o["Pa2"], ca2, 0.0, o["Wq"], o["bq"], o["Wk"], o["bk"], o["Wv"],
+                              o["bv"], o["WoT"], o["bo"], Kc0, Vc0, nh, cfg.dh, t)
+    report["rel_err"] = rel_err(y.cpu().numpy()[None, :], ref["y"][None, :])
+    report["cache_ulps"] = int(max(f16_ulps(Kc[:, t].reshape(-1), ref["k_new"]).max(),
+                                   f16_ulps(Vc[:, t].reshape(-1), ref["v_new"]).max()))
+    # normwise: entries near zero may sit several fp16 units from the oracle's rounding, since an
+    # fp32 dot product over d terms errs by far more than one fp16 unit of a small value
+    f = lambda b: np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+    report["cache_rel_err"] = float(max(
+        np.max(np.abs(f(Kc[:, t].reshape(-1)) - f(ref["k_new"]))) / np.max(np.abs(f(ref["k_new"]))),
+        np.max(np.abs(f(Vc[:, t].reshape(-1)) - f(ref["v_new"]))) / np.max(np.abs(f(ref["v_new"])))))
+    others = np.ones(cfg.L_max, bool)
+    others[t] = False
+    report["cache_others_untouched"] = bool(np.array_equal(Kc[:, others], Kc0[:, others]) and
+                                            np.array_equal(Vc[:, others], Vc0[:, others]))
+    return report
+
+
+def assert_attn_report(r: dict) -> None:
+    assert r["ascending"], r
+    assert r["list_outside_band"] == 0, r
+    assert r["logit_max_abs_err"] <= LOGIT_ATOL, r
+    assert r["rel_err"] <= RTOL, r
+    assert r["cache_rel_err"] <= 1e-3, r
+    assert r["cache_others_untouched"], r

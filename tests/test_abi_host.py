@@ -240,3 +240,36 @@ def test_compact_and_merge_reject_bad_arguments():
     assert status(pi.pi_merge, 1, 16, None, FAKE, None, None, 0) == pi.PI_EINVAL
     # nothing to add: accepted without any launch
     assert status(pi.pi_merge, 1, 16, FAKE, None, None, None, 0) == pi.PI_OK
+
+
+def test_attn_decode_rejects_bad_arguments():
+    def attn(**kw):
+        base = dict(d=512, n_heads=8, dh=64, Ha=64, L_max=256)
+        base.update(kw)
+        m = lambda: pi.Matrix(FAKE, pi.PI_F16)
+        return pi.Attn(base["d"], base["n_heads"], base["dh"], base["Ha"], base["L_max"], m(), m(), m(), m(), m(),
+                       m(), FAKE, FAKE)
+    X, Y, WS = FAKE, FAKE + (1 << 20), FAKE + (1 << 24)
+    need = pi.pi_attn_workspace_bytes(attn())
+    assert need > 0
+
+    def call(A=None, t=10, x=X, y=Y, nbytes=need, ws=WS):
+        return status(pi.pi_attn_decode, A or attn(), t, x, 0.0, y, None, FAKE, FAKE, ws, nbytes, 0)
+
+    assert call(t=-1) == pi.PI_EINVAL and call(t=256) == pi.PI_EINVAL          # outside the cache
+    assert call(A=attn(d=500)) == pi.PI_EINVAL                                  # d != n_heads * dh
+    assert call(A=attn(dh=32, d=256)) == pi.PI_EUNSUPPORTED
+    assert call(A=attn(Ha=2000)) == pi.PI_EUNSUPPORTED and call(A=attn(Ha=6)) == pi.PI_EUNSUPPORTED
+    assert call(A=attn(n_heads=80, d=80 * 128, dh=128)) == pi.PI_EUNSUPPORTED  # d above 8192
+    assert call(x=X + 4) == pi.PI_EINVAL and call(y=None) == pi.PI_EINVAL
+    assert call(y=X + 1024) == pi.PI_EINVAL                                     # y overlapping x
+    A = attn()
+    A.Wq = pi.Matrix(FAKE, pi.PI_F32)
+    assert call(A=A) == pi.PI_EINVAL                                            # fp16 weights only
+    A = attn()
+    A.bo = pi.Vector(FAKE, pi.PI_F32)
+    assert call(A=A) == pi.PI_EINVAL
+    A = attn()
+    A.Kc = None
+    assert call(A=A) == pi.PI_EINVAL
+    assert call(nbytes=need - 16) == pi.PI_EWORKSPACE and call(ws=None) == pi.PI_EWORKSPACE

@@ -137,3 +137,20 @@ def test_extreme_layers_of_the_parity_cases():
         H = np.array([cfg.hidden(L) for L in range(cfg.n_layers)])
         assert int(rho.argmin()) == lo and int(rho.argmax()) == hi
         assert H[lo] == H.min() and H[hi] == H.max()
+
+
+def test_attention_head_predictor_is_calibrated():
+    """With the calibrated output bias, head h is predicted active for a fraction p_h of seeded
+    inputs (the oracle's head logits over 3,000 inputs, within 4.5 binomial deviations)."""
+    import oracle as orc
+    cfg = synth.ATTN_CONFIGS["attn-small"]
+    spec = synth.attn_spec(cfg, 0)
+    h = synth.attn_host(spec)
+    n = 3000
+    X, _ = synth.host_rows(synth.F32, cfg.seed, synth.TAG_XA, 0, cfg.d, 1.0, row0=10_000, nrows=n)
+    logits = orc.predict(X, orc.Mat(h["Pa1"], orc.F16, cfg.d), orc.Vec(None, orc.F16),
+                         orc.Mat(h["Pa2"], orc.F16, cfg.Ha), orc.Vec(h["ca2"], orc.F16))
+    freq = (logits.astype(np.float32) > 0).mean(axis=0)
+    sd = np.sqrt(spec.p * (1 - spec.p) / n)
+    assert np.all(np.abs(freq - spec.p) <= 4.5 * sd + 0.01), (freq, spec.p)
+    assert abs(spec.p.mean() - 0.5) < 1e-12          # half the heads active on average
