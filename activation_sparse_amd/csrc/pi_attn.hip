@@ -9,8 +9,9 @@
 //   k_attn_rows   : the predictor's hidden layer and the K and V projections, R
 //                   rows per wave with x held in registers; K and V rounded to
 //                   fp16 into the cache at position t
-//   k_attn_q      : per wave, its head's logit (Pa2 row . g) and decision; the
-//                   active heads' query rows
+//   k_attn_q      : per workgroup of 8 waves (8 rows of one head), the head's
+//                   logit (Pa2 row . g) and decision; the active heads' query
+//                   rows, one per wave, x staged once in LDS
 //   k_attn_part   : per (chunk of 64 cached positions, active head): scores,
 //                   the chunk's max, exp2 weights, their sum and the weighted
 //                   sum of the value rows
@@ -130,31 +131,62 @@ __device__ __forceinline__ float head_logit(const AttnArgs& a, int h, int lane) 
   return wave_sum(s) + ca2(h);
 }
 
-// Query rows: each wave takes kRowsPerWave rows of one head, decides the head first and loads x
-// only when it is active.  The head's first wave stores the logit and the decision.
+// Query rows: one row per wave, kQW waves per workgroup, all of one head.  Every wave computes its
+// head's logit (the same bits) from the L2-resident Pa2 row and g while x streams in for LDS; an
+// inactive head's workgroup leaves before any weight load, an active one issues its rows' loads,
+// stores x to LDS, and the dots read x from there.  NV is the fewest 16-byte vectors per lane
+// that cover a row, so no dead vector takes registers.  The head's first workgroup stores the
+// logit and the decision.
+constexpr int kQW = 8;
+constexpr int kQRows = kQW;              // rows per workgroup
 template <int NV>
-__global__ __launch_bounds__(kAT) void k_attn_q(AttnArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int r0 = (blockIdx.x * kAW + wave_index()) * kRowsPerWave;
-  if (r0 >= a.d) return;
-  const int h = r0 / a.dh;
+__global__ __launch_bounds__(kQW * kWave) void k_attn_q(AttnArgs a) {
+  extern __shared__ float4v xs[];
+  const int lane = threadIdx.x & (kWave - 1), wave = wave_index();
+  const int r = blockIdx.x * kQRows + wave;                   // d % kQRows == 0: every wave has a row
+  const int h = (blockIdx.x * kQRows) / a.dh;                 // kQRows divides dh: one head per workgroup
+  const int nvec = a.d / 8, nq = a.d / 4;
+  float4v xv[4];
+  {
+    const rsrc_t rx = make_rsrc(uniform_ptr(a.x), (uint32_t)nq * 16u);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {                             // d <= 8192: at most 2048 float4, 4 per thread
+      const uint4 t4 = bload16(rx, (uint32_t)(k * kQW * kWave + threadIdx.x) * 16u);
+      xv[k] = float4v{__uint_as_float(t4.x), __uint_as_float(t4.y), __uint_as_float(t4.z), __uint_as_float(t4.w)};
+    }
+  }
   const float lg = head_logit(a, h, lane);
   const bool on = lg > a.tau;
-  if (r0 % a.dh == 0 && lane == 0) {
+  if ((blockIdx.x * kQRows) % a.dh == 0 && threadIdx.x == 0) {
     a.hlogit[h] = lg;
     a.flag[h] = on ? 1 : 0;
   }
-  if (!on) return;
-  const int nvec = a.d / 8;
-  float xr[NV][8];
-  x_regs<NV>(a.x, nvec, lane, xr);
-  const Bias<1> bq(a.bq, (uint32_t)a.d);
-#pragma unroll 1
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    const int r = r0 + k;
-    const float z = row_dot<NV>(static_cast<const char*>(a.Wq) + (int64_t)r * a.d * 2, nvec, lane, xr) + bq(r);
-    if (lane == 0) a.q[r] = z;
+  if (!on) return;                                            // the same decision in every wave
+  const rsrc_t rw = make_rsrc(uniform_ptr(static_cast<const char*>(a.Wq) + (int64_t)r * a.d * 2), (uint32_t)nvec * 16u);
+  uint4 w[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) w[u] = bload16(rw, (uint32_t)(u * kWave + lane) * 16u);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int q = k * kQW * kWave + threadIdx.x;
+    if (q < nq) xs[q] = xv[k];
   }
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int v = u * kWave + lane;                           // 8 elements: float4 2v and 2v + 1
+    const float4v x0 = v < nvec ? xs[2 * v] : float4v{0.f, 0.f, 0.f, 0.f};
+    const float4v x1 = v < nvec ? xs[2 * v + 1] : float4v{0.f, 0.f, 0.f, 0.f};
+    float wf[8];
+    widen<1>(w[u], 1.f, wf);
+    acc = fmaf(wf[0], x0.x, acc); acc = fmaf(wf[1], x0.y, acc); acc = fmaf(wf[2], x0.z, acc);
+    acc = fmaf(wf[3], x0.w, acc); acc = fmaf(wf[4], x1.x, acc); acc = fmaf(wf[5], x1.y, acc);
+    acc = fmaf(wf[6], x1.z, acc); acc = fmaf(wf[7], x1.w, acc);
+  }
+  const Bias<1> bq(a.bq, (uint32_t)a.d);
+  const float z = wave_sum(acc) + bq(r);
+  if (lane == 0) a.q[r] = z;
 }
 
 // One chunk of kChunk cached positions of one active head.  LPP = DH/8 lanes per position (one
@@ -261,7 +293,20 @@ __global__ __launch_bounds__(kAT) void k_attn_out(AttnArgs a) {
   const int lane = threadIdx.x & (kWave - 1), wave = wave_index();
   const float* ph = a.part + (int64_t)h * a.n_chunks * (DH + 2);
   const int nc = (a.t + 1 + kChunk - 1) / kChunk;
-  // issue this wave's weight rows before the combine
+  // the combine's operands (from L2) are loaded before the weight rows (from HBM), so that the
+  // in-order wait for them does not wait for the rows: up to kCombine chunks in registers
+  constexpr int kCombine = 16;
+  float cm[kCombine], cl[kCombine], co[kCombine];
+  const int ti = threadIdx.x < DH ? threadIdx.x : 0;
+#pragma unroll
+  for (int c = 0; c < kCombine; ++c) {
+    const bool in = c < nc;
+    const int cc = in ? c : 0;                             // every address inside this head's chunks
+    const float m = ph[cc * (DH + 2)], l = ph[cc * (DH + 2) + 1], o = ph[cc * (DH + 2) + 2 + ti];
+    cm[c] = in ? m : -INFINITY;
+    cl[c] = in ? l : 0.f;
+    co[c] = in ? o : 0.f;
+  }
   const int64_t col0 = (int64_t)tile * kColTile;
   const rsrc_t rw = make_rsrc(uniform_ptr(static_cast<const char*>(a.WoT) + ((int64_t)h * DH * a.d + col0) * 2),
                               (uint32_t)((int64_t)DH * a.d * 2 - col0 * 2));
@@ -275,9 +320,17 @@ __global__ __launch_bounds__(kAT) void k_attn_out(AttnArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   if (threadIdx.x < DH) {
     float M = -INFINITY;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, ph[c * (DH + 2)]);
+#pragma unroll
+    for (int c = 0; c < kCombine; ++c) M = fmaxf(M, cm[c]);
+    for (int c = kCombine; c < nc; ++c) M = fmaxf(M, ph[c * (DH + 2)]);
     float L = 0.f, o = 0.f;
-    for (int c = 0; c < nc; ++c) {
+#pragma unroll
+    for (int c = 0; c < kCombine; ++c) {                  // chunk order; chunks past nc add 0
+      const float f = c < nc ? exp2f(cm[c] - M) : 0.f;
+      L = fmaf(cl[c], f, L);
+      o = fmaf(co[c], f, o);
+    }
+    for (int c = kCombine; c < nc; ++c) {
       const float f = exp2f(ph[c * (DH + 2)] - M);
       L = fmaf(ph[c * (DH + 2) + 1], f, L);
       o = fmaf(ph[c * (DH + 2) + 2 + threadIdx.x], f, o);
@@ -308,27 +361,48 @@ __global__ __launch_bounds__(kAT) void k_attn_out(AttnArgs a) {
   }
 }
 
-// y = bo + the active heads' tiles in head order; workgroup 0 also writes the ascending head list,
-// its count and (optionally) the head logits.
+// y = bo + the active heads' tiles in head order.  Each workgroup first lists the active heads in
+// LDS (ascending, by ballots), then every thread issues its column's partials eight at a time;
+// workgroup 0 also writes the list, its count and (optionally) the head logits.
 __global__ __launch_bounds__(kAT) void k_attn_reduce(AttnArgs a) {
-  const int64_t cidx = (int64_t)blockIdx.x * kAT + threadIdx.x;
-  if (blockIdx.x == 0 && threadIdx.x < kWave) {
+  __shared__ int s_list[kMaxAttnHeads];
+  __shared__ int s_n;
+  if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     int base = 0;
     for (int h0 = 0; h0 < a.n_heads; h0 += kWave) {
       const int h = h0 + lane;
       const bool on = h < a.n_heads && a.flag[h];
       const uint64_t bits = __ballot(on);
-      if (on) a.heads[base + __popcll(bits & ((1ull << lane) - 1ull))] = h;
-      if (a.logits_out && h < a.n_heads) a.logits_out[h] = a.hlogit[h];
+      const int pos = base + __popcll(bits & ((1ull << lane) - 1ull));
+      if (on) {
+        s_list[pos] = h;
+        if (blockIdx.x == 0) a.heads[pos] = h;
+      }
+      if (blockIdx.x == 0 && a.logits_out && h < a.n_heads) a.logits_out[h] = a.hlogit[h];
       base += __popcll(bits);
     }
-    if (lane == 0) *a.n_active = base;
+    if (lane == 0) {
+      s_n = base;
+      if (blockIdx.x == 0) *a.n_active = base;
+    }
   }
+  __syncthreads();
+  const int64_t cidx = (int64_t)blockIdx.x * kAT + threadIdx.x;
   if (cidx >= a.d) return;
+  const int n = s_n;
   float s = load_bias(a.bo, 1, cidx);
-  for (int h = 0; h < a.n_heads; ++h)
-    if (a.flag[h]) s += a.ypart[(int64_t)h * a.d + cidx];
+  for (int k0 = 0; k0 < n; k0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int hj = s_list[k0 + j < n ? k0 + j : n - 1];   // a listed head at every slot
+      v[j] = a.ypart[(int64_t)hj * a.d + cidx];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k0 + j < n) s += v[j];
+  }
   a.y[cidx] = s;
 }
 
@@ -339,12 +413,19 @@ int pick_nv_attn(int d) {
   return 0;
 }
 
+// The query kernel's 16-byte vectors per lane and row: the fewest that cover the row (two rows'
+// loads are held at once, so no dead vector is carried).
+int pick_nv_q(int d) {
+  const int nvec = d / 8;
+  for (int nv : {1, 2, 4, 6, 8, 10, 12, 14, 16})
+    if (nv * kWave >= nvec) return nv;
+  return 0;
+}
+
 template <int NV>
 hipError_t launch_nv(const AttnArgs& a, hipStream_t s) {
   const int rows_blocks = (a.Ha + 2 * a.d + kAW * kRowsPerWave - 1) / (kAW * kRowsPerWave);
   hipLaunchKernelGGL(k_attn_rows<NV>, dim3((unsigned)rows_blocks), dim3(kAT), 0, s, a);
-  const int q_blocks = (a.d + kAW * kRowsPerWave - 1) / (kAW * kRowsPerWave);
-  hipLaunchKernelGGL(k_attn_q<NV>, dim3((unsigned)q_blocks), dim3(kAT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -368,6 +449,21 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  {
+    const dim3 gq((unsigned)(a.d / kQRows)), tq(kQW * kWave);
+    const size_t shq = (size_t)a.d * 4;
+    switch (pick_nv_q(a.d)) {
+      case 1: hipLaunchKernelGGL(k_attn_q<1>, gq, tq, shq, s, a); break;
+      case 2: hipLaunchKernelGGL(k_attn_q<2>, gq, tq, shq, s, a); break;
+      case 4: hipLaunchKernelGGL(k_attn_q<4>, gq, tq, shq, s, a); break;
+      case 6: hipLaunchKernelGGL(k_attn_q<6>, gq, tq, shq, s, a); break;
+      case 8: hipLaunchKernelGGL(k_attn_q<8>, gq, tq, shq, s, a); break;
+      case 10: hipLaunchKernelGGL(k_attn_q<10>, gq, tq, shq, s, a); break;
+      case 12: hipLaunchKernelGGL(k_attn_q<12>, gq, tq, shq, s, a); break;
+      case 14: hipLaunchKernelGGL(k_attn_q<14>, gq, tq, shq, s, a); break;
+      default: hipLaunchKernelGGL(k_attn_q<16>, gq, tq, shq, s, a); break;
+    }
+  }
   const dim3 gp((unsigned)((a.t + 1 + kChunk - 1) / kChunk), (unsigned)a.n_heads);
   const dim3 go((unsigned)((a.d + kColTile - 1) / kColTile), (unsigned)a.n_heads);
   if (a.dh == 128) {

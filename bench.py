@@ -57,7 +57,10 @@ def parse():
                     help="skip the host-side placement-solver report")
     ap.add_argument("--leg", default=None, metavar="NAME",
                     help="run one leg alone and print its result instead of the benchmark line: truth, chained, "
-                         "placement, read-probe or config:KEY[:STRIDE] (for a profiler run over just its kernels)")
+                         "placement, attention, read-probe or config:KEY[:STRIDE] (for a profiler run over just "
+                         "its kernels)")
+    ap.add_argument("--attn-steps", type=int, default=8,
+                    help="steps of the self-attention stack with head sparsity (0 = skip)")
     ap.add_argument("--placement-steps", type=int, default=16,
                     help="steps of the fixed-rule vs solver-table timing on the LLaMA-13B gated 40%% stack, "
                          "GPU side and hybrid (0 = skip)")
@@ -1032,6 +1035,114 @@ def placement_report(keys):
     return out
 
 
+def attn_bench(steps, warmup, key="attn-opt-30b", cpu=True):
+    """The self-attention stack with head sparsity at decode (pi_attn_decode), batch 1, every layer at
+    the last cache position (1,024 cached positions): one HIP graph per step of all layers, timed
+    with the head predictor's decisions (tau = 0) and with every head active (tau = -3e38, the
+    dense block).  Algorithmic bytes per layer: the head predictor, every K and V row, and per
+    active head its query and output-projection rows and its cached keys and values."""
+    import torch
+    import synth
+    import activation_sparse_amd as pi
+    from synth.device import DeviceAttn
+    cfg = synth.ATTN_CONFIGS[key]
+    dev = "cuda:0"
+    t0 = time.time()
+    L, d, nh, dh = cfg.n_layers, cfg.d, cfg.n_heads, cfg.dh
+    t = cfg.L_max - 1
+    dls = [DeviceAttn(synth.attn_spec(cfg, l), dev) for l in range(L)]
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    S = warmup + steps
+    xs = torch.empty((S, L, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for st in range(S):
+        rid = torch.from_numpy(synth.x_row_ids(st, 1)).to(dev)
+        for l in range(L):
+            synth.dev_fill(xs[st, l].data_ptr(), None, synth.F32, cfg.seed, synth.TAG_XA, l, d, 1.0,
+                           row_ids_ptr=rid.data_ptr(), nrows=1, stream=stream)
+    ws = torch.empty(pi.pi_attn_workspace_bytes(dls[0].attn), dtype=torch.uint8, device=dev)
+    y = torch.empty(d, dtype=torch.float32, device=dev)
+    heads = torch.empty(nh, dtype=torch.int32, device=dev)
+    nas = torch.zeros((S, L), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def timed(tau):
+        def step(st):
+            for l in range(L):
+                pi.pi_attn_decode(dls[l].attn, t, xs[st, l], tau, y, None, heads, nas[st, l:l + 1], ws,
+                                  _cstruct=dls[l].attn_c)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        gs = []
+        for st in range(S):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(st)
+            gs.append(g)
+        for st in range(warmup):
+            gs[st].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for st in range(warmup, S):
+            gs[st].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del gs
+        ms = e0.elapsed_time(e1) / steps
+        na = nas[warmup:].float().mean().item()
+        per_layer = (cfg.Ha * d * 2 + nh * cfg.Ha * 2 + 2 * d * d * 2 + na * (2 * dh * d * 2 + 2 * (t + 1) * dh * 2)
+                     + 5 * d * 2 + 2 * d * 4 + 2 * d * 2)
+        return ms, na, per_layer * L
+
+    ms_s, na_s, b_s = timed(0.0)
+    ms_d, na_d, b_d = timed(-3.0e38)
+    out = {"workload": cfg.desc, "layers": L, "cached_positions": t + 1, "batch": 1,
+           "tokens_per_s": round(1e3 / ms_s, 2), "ms_per_step": round(ms_s, 4), "mean_active_heads": round(na_s, 2),
+           "heads": nh, "step_bytes": round(b_s), "step_gbps": round(b_s / (ms_s * 1e-3) / 1e9, 1),
+           "step_frac_of_peak": round(b_s / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "dense_tokens_per_s": round(1e3 / ms_d, 2), "dense_ms_per_step": round(ms_d, 4),
+           "dense_step_bytes": round(b_d), "dense_step_gbps": round(b_d / (ms_d * 1e-3) / 1e9, 1),
+           "dense_step_frac_of_peak": round(b_d / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "speedup_over_dense": round(ms_d / ms_s, 3), "weight_generation_s": round(gen_s, 1)}
+    del dls, xs, ws
+    torch.cuda.empty_cache()
+    if cpu:
+        out["cpu_baseline"] = attn_cpu_baseline(cfg, 3.0)
+    log(f"attention: {out['tokens_per_s']} tokens/s with {out['mean_active_heads']} of {nh} heads, "
+        f"{out['dense_tokens_per_s']} with every head; step frac {out['step_frac_of_peak']}")
+    return out
+
+
+def attn_cpu_baseline(cfg, seconds):
+    """The attention oracle on the host threads over a bounded sample of the same workload (layers in
+    turn, the last cache position), scaled to the stack's layers per token."""
+    import synth
+    import oracle as orc
+    from tests import parity_harness as ph
+    t = cfg.L_max - 1
+    done, el, l = 0, 0.0, 0
+    while el < seconds and done < 8:
+        spec = synth.attn_spec(cfg, l % cfg.n_layers)
+        h = synth.attn_host(spec)
+        o = ph.attn_oracle_inputs(h, cfg.d)
+        x = synth.attn_x(cfg, l % cfg.n_layers, 0)
+        t1 = time.perf_counter()
+        orc.attn_decode(x, o["Pa1"], o["ca1"], o["Pa2"], o["ca2"], 0.0, o["Wq"], o["bq"], o["Wk"], o["bk"], o["Wv"],
+                        o["bv"], o["WoT"], o["bo"], h["Kc"], h["Vc"], cfg.n_heads, cfg.dh, t)
+        el += time.perf_counter() - t1
+        done += 1
+        l += 1
+    return {"value": round(done / el / cfg.n_layers, 4), "unit": "tokens/s", "cores": orc.get_threads(),
+            "kind": "oracle", "sample": f"{done} layer-steps (layers 0..{done - 1}, the last cache position) in "
+                                        f"{el:.1f} s, scaled to {cfg.n_layers} layers per token; weight generation not timed"}
+
+
 def read_probe_sweep(sizes=(63137536, 2**30), depths=(4, 8, 16, 32), per_cu=(1, 2, 4, 8, 16, 32), n_rep=20):
     """The streaming-read reference over its settings: loads in flight per lane x workgroups per
     compute unit, for a kernel-sized read and 1 GiB.  Successive launches read different regions of
@@ -1219,8 +1330,8 @@ def hybrid_bench(cfg, specs, dls, steps, warmup, light=False):
 
 def run_leg(args):
     """One leg alone, so that a profiler run holds just its kernels: 'truth' or 'chained' (on
-    --config's stack), 'placement', 'read-probe' (the streaming-read reference's sweep), or
-    'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
+    --config's stack), 'placement', 'attention', 'read-probe' (the streaming-read reference's
+    sweep), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
     import torch
     import synth
     from synth.device import DeviceLayer
@@ -1241,13 +1352,15 @@ def run_leg(args):
         dls = [DeviceLayer(s, "cuda:0") for s in specs]
         torch.cuda.synchronize()
         res = chained_bench(cfg, specs, dls, args.chained_steps, 3)
+    elif name == "attention":
+        res = attn_bench(args.attn_steps, 2, cpu=not args.no_cpu_baseline)
     elif name == "read-probe":
         res = read_probe_sweep()
     elif name == "placement":
         res = placement_bench("llama-13b-gated-40", args.placement_steps, 2, args.placement_steps)
     else:
-        raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, read-probe, "
-                         "config:KEY[:STRIDE])")
+        raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, attention, "
+                         "read-probe, config:KEY[:STRIDE])")
     return {"leg": args.leg, "result": res}
 
 
@@ -1507,6 +1620,11 @@ def main():
         key, _, stride = item.partition(":")
         configs[key] = config_bench(key, args.config_steps, 2, int(stride or 1))
 
+    attention = None
+    if args.attn_steps > 0 and B == 1:
+        log("self-attention stack with head sparsity ...")
+        attention = attn_bench(args.attn_steps, 2, cpu=not args.no_cpu_baseline)
+
     placement = None
     if args.placement and B == 1:
         log("placement solver (host) ...")
@@ -1558,7 +1676,7 @@ def main():
                    "stream_read_gbps": stream_read,
                    "dominant_frac_of_stream_read": round(achieved[iso] / dom_ref, 4),
                    "batch_sweep": sweep, "hybrid": hybrid, "lookahead": lookahead, "chained": chained, "int4_predictor": i4pred,
-                   "placement": placement, "truth": truth, "rho20": configs.pop("opt-30b-rho20", None),
+                   "placement": placement, "attention": attention, "truth": truth, "rho20": configs.pop("opt-30b-rho20", None),
                    "configs": configs or None},
     }
     print(json.dumps(out), flush=True)
