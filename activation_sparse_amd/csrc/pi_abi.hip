@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
+#include <stdlib.h>
 #include <atomic>
 #include <cmath>
 #include "../../include/pi.h"
@@ -63,8 +64,26 @@ struct FfnWs {
 
 // Partial sums of the batched matrix-core GEMMs, bounded over the weight dtypes
 // (workspace sizes are asked for without them).
-bool use_mm_row(int32_t B) { return B >= pi::kMmRowMinBatch; }
-bool use_mm_axpy(int32_t B) { return B >= pi::kMmAxpyMinBatch; }
+// The smallest batches that take the matrix-core GEMMs: kMmRowMinBatch / kMmAxpyMinBatch, or
+// both raised to PI_MATRIX_CORE_MIN_BATCH when that is set (read once; a value above the largest
+// batch keeps every batch on the VALU kernels, for comparisons).
+int mm_min_batch_env() {
+  static const int v = [] {
+    const char* e = getenv("PI_MATRIX_CORE_MIN_BATCH");
+    if (!e || !*e) return 0;
+    const long n = strtol(e, nullptr, 10);
+    return n < 1 ? 0 : (n > 1000 ? 1000 : (int)n);
+  }();
+  return v;
+}
+bool use_mm_row(int32_t B) {
+  const int e = mm_min_batch_env();
+  return B >= (e > pi::kMmRowMinBatch ? e : pi::kMmRowMinBatch);
+}
+bool use_mm_axpy(int32_t B) {
+  const int e = mm_min_batch_env();
+  return B >= (e > pi::kMmAxpyMinBatch ? e : pi::kMmAxpyMinBatch);
+}
 // Rows of an activation buffer (h, a): B, or the padded batch 16 * nbt when the
 // matrix-core kernels keep it neuron-major (a in fp16 also pads the neurons to 32).
 size_t act_rows(int32_t B) {

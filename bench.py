@@ -57,8 +57,8 @@ def parse():
                     help="skip the host-side placement-solver report")
     ap.add_argument("--leg", default=None, metavar="NAME",
                     help="run one leg alone and print its result instead of the benchmark line: truth, chained, "
-                         "placement, attention, read-probe or config:KEY[:STRIDE] (for a profiler run over just "
-                         "its kernels)")
+                         "placement, attention, batch-sweep, read-probe or config:KEY[:STRIDE] (for a profiler "
+                         "run over just its kernels)")
     ap.add_argument("--attn-steps", type=int, default=8,
                     help="steps of the self-attention stack with head sparsity (0 = skip)")
     ap.add_argument("--placement-steps", type=int, default=16,
@@ -1330,8 +1330,8 @@ def hybrid_bench(cfg, specs, dls, steps, warmup, light=False):
 
 def run_leg(args):
     """One leg alone, so that a profiler run holds just its kernels: 'truth' or 'chained' (on
-    --config's stack), 'placement', 'attention', 'read-probe' (the streaming-read reference's
-    sweep), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
+    --config's stack), 'placement', 'attention', 'batch-sweep' (--sweep's batches on --config's
+    stack), 'read-probe' (the streaming-read reference's sweep), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
     import torch
     import synth
     from synth.device import DeviceLayer
@@ -1352,6 +1352,14 @@ def run_leg(args):
         dls = [DeviceLayer(s, "cuda:0") for s in specs]
         torch.cuda.synchronize()
         res = chained_bench(cfg, specs, dls, args.chained_steps, 3)
+    elif name == "batch-sweep":
+        cfg = synth.CONFIGS[args.config]
+        specs = [synth.layer_spec(cfg, L) for L in range(args.layers or cfg.n_layers)]
+        dls = [DeviceLayer(s, "cuda:0") for s in specs]
+        torch.cuda.synchronize()
+        batches = [int(v) for v in args.sweep.split(",") if v.strip()]
+        res = batch_sweep(cfg, specs, dls, batches, args.sweep_steps, 2)
+        res["matrix_core_min_batch_env"] = os.environ.get("PI_MATRIX_CORE_MIN_BATCH")
     elif name == "attention":
         res = attn_bench(args.attn_steps, 2, cpu=not args.no_cpu_baseline)
     elif name == "read-probe":
@@ -1360,7 +1368,7 @@ def run_leg(args):
         res = placement_bench("llama-13b-gated-40", args.placement_steps, 2, args.placement_steps)
     else:
         raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, attention, "
-                         "read-probe, config:KEY[:STRIDE])")
+                         "batch-sweep, read-probe, config:KEY[:STRIDE])")
     return {"leg": args.leg, "result": res}
 
 

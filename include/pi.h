@@ -416,6 +416,12 @@ size_t pi_attn_workspace_bytes(const pi_attn* A);
 #define PI_READ_PROBE_BLOCKS_PER_CU 8
 int pi_read_probe(void* stream, const void* buf, size_t bytes, int32_t blocks, int32_t depth, uint32_t* out);
 
+/* Environment: PI_MATRIX_CORE_MIN_BATCH, read once at the first call, raises
+ * the smallest batch that takes the matrix-core GEMMs (by default batch 2 for
+ * the row-dot GEMMs, the predictor's hidden layer and FC1, and batch 3 for the
+ * axpy GEMMs, the output layer and FC2); a value above 32 keeps every batch on
+ * the VALU kernels.  It exists for comparisons; pi_workspace_bytes follows it. */
+
 /* Workspace bytes an entry point needs for these sizes (0 when none).
  * Arguments an op does not use are ignored. */
 size_t pi_workspace_bytes(int32_t op, int32_t B, int32_t d, int32_t H, int32_t N, int32_t n_g);

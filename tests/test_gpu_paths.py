@@ -152,7 +152,7 @@ def test_output_layer_two_passes(fused):
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
-@pytest.mark.parametrize("B", [8, 9, 17, 31])
+@pytest.mark.parametrize("B", [2, 3, 8, 9, 17, 31])
 def test_matrix_core_batches(B, fused):
     _dev()
     r = ph.run_layer_parity(RAGGED_B, layer=0, step=2, B=B, fused=fused)

@@ -151,7 +151,8 @@ def test_outputs_are_bitwise_repeatable():
 # checks that they still are.
 EXTREME_LAYERS = {"llama-13b-gated": (3, 14), "opt-175b-int4": (15, 14)}
 FULL = [("opt-768", 0, 1), ("opt-6.7b", 5, 1), ("llama-13b-gated", 7, 1), ("opt-30b", 3, 1), ("opt-30b", 3, 4),
-        ("opt-30b", 11, 16), ("opt-30b", 11, 32), ("opt-175b-int4", 42, 1), ("opt-30b-i4pred", 3, 1)]
+        ("opt-30b", 11, 16), ("opt-30b", 11, 32), ("opt-175b-int4", 42, 1), ("opt-30b-i4pred", 3, 1),
+        ("opt-30b", 20, 2), ("llama-13b-gated", 9, 2)]
 FULL += [(k, l, 1) for k, ls in EXTREME_LAYERS.items() for l in ls]
 
 
