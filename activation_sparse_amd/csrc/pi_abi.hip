@@ -616,12 +616,13 @@ struct Ahead {
 };
 
 // The batch-1 layer runs as the fused tile kernels (output layer + decision + FC1, then the segment
-// FC2 and the ordered sum) for these formats and sizes.
+// FC2 and the ordered sum) for these formats and sizes; its hidden layer takes the register-x
+// kernel when the predictor's rows fit it and the LDS-x row-dot otherwise.
 bool b1_fused(const pi_layer* L, int32_t B) {
   const bool gated = L->kind == PI_GATED_RELU;
   const int bdt = L->b1.data ? L->b1.dtype : (L->c2.data ? L->c2.dtype : PI_F16);
   const int c2dt = L->c2.data ? L->c2.dtype : bdt;
-  return B == 1 && pi::b1_supported(L->W1.dtype, L->d) && n_groups64(L->N) <= (size_t)64 * pi::kSegChunks &&
+  return B == 1 && n_groups64(L->N) <= (size_t)64 * pi::kSegChunks &&
          pi::pred_fc1_supported(L->P2.dtype, L->W1.dtype, bdt, c2dt, gated, L->H, L->N, L->d);
 }
 

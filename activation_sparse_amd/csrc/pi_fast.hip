@@ -593,6 +593,17 @@ int pick_nv(int nvec) {
   return 0;
 }
 
+// Vectors per lane of the fused kernel's FC1 rows, whose x is in LDS (not registers): the row's
+// loads alone bound it, 16 vectors for fp32 / fp16 rows and 8 for int4 rows (32 weights each).
+template <int DT>
+int pick_nv_fused(int nvec) {
+  for (int nv : {4, 8, 16}) {
+    if (DT == 2 && nv > 8) break;
+    if (nv * kWave >= nvec) return nv;
+  }
+  return 0;
+}
+
 int pick_nv_rt(int dt, int nvec) {
   switch (dt) {
     case 0: return pick_nv<0>(nvec);
@@ -686,10 +697,10 @@ hipError_t pred_out_pdt(const PredFc1Args& a, hipStream_t s) {
 // kernels.
 template <int PDT, int DT, int BDT, bool GATED>
 hipError_t pred_fc1_combo(const PredFc1Args& a, hipStream_t s) {
-  const int nv = pick_nv<DT>((int)(row_bytes(DT, a.d) / 16));
+  const int nv = pick_nv_fused<DT>((int)(row_bytes(DT, a.d) / 16));
 #define PI_PF(NVV) return pf_launch<PDT, DT, NVV, GATED, BDT, kTile, true>(a, s)
   switch (nv) {
-    case 1: case 2: case 4: PI_PF(4);
+    case 4: PI_PF(4);
     case 8: PI_PF(8);
     case 16: if constexpr (Fmt<DT>::E <= 8) PI_PF(16);
     default: return hipErrorInvalidValue;
@@ -915,7 +926,8 @@ hipError_t launch_pred_out_b1(const PredFc1Args& a, hipStream_t s) {
 bool pred_fc1_supported(int pdt, int dt, int bdt, int c2dt, bool gated, int H, int N, int64_t d) {
   if (!pred_out_b1_supported(pdt, H, N)) return false;
   if (bdt != c2dt) return false;
-  const int nv = pick_nv_rt(dt, (int)(row_bytes(dt, d) / 16));
+  const int nvec = (int)(row_bytes(dt, d) / 16);
+  const int nv = dt == 0 ? pick_nv_fused<0>(nvec) : dt == 1 ? pick_nv_fused<1>(nvec) : pick_nv_fused<2>(nvec);
   if (nv == 0) return false;
   if (pdt == 0 && dt == 0 && bdt == 0) return !gated;
   if (pdt == 1 && (dt == 1 || dt == 2) && bdt == 1) return true;
