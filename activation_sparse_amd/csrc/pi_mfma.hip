@@ -42,6 +42,10 @@ typedef float float4v_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMmWaves = 4;
 constexpr int kMmThreads = kMmWaves * kWave;
+constexpr int kOutWaves = 8;   // the predictor output layer's one-row-chunk axpy (k_mm_axpy16)
+// its row ids take 4 bytes each of dynamic LDS beside the eight waves' 80 KB (at 32 batch rows):
+// past this many hidden units the four-wave block (48 KB) takes the layer
+constexpr int64_t kOutWavesMaxRows = 16384;
 
 __device__ __forceinline__ float4v_t mfma4(float a, float b, float4v_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -490,14 +494,18 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy(MmAxpyArgs a) {
 // 256-byte loads into the wave's LDS tile and the B operands are gathered from
 // it 2 bytes at a time.  The tile's 16-byte chunks are stored at chunk
 // c ^ 2 ((row / 8) & 3): the four lane groups, reading rows 8 g + i, then fall
-// in different banks.  The block's four waves take interleaved row steps and
+// in different banks.  The block's WV waves take interleaved row steps and
 // are summed in LDS in wave order.  With LO, a = hi + lo in two fp16 parts
 // (about 22 bits): two exact products per weight, for the predictor's output
-// layer, whose logits keep near-fp32 precision.
-template <int NBT, bool LO>
-__global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
+// layer, whose logits keep near-fp32 precision.  That layer is one row chunk
+// over all H rows with one block per 128 columns (fewer blocks than compute
+// units at these sizes), so it takes eight waves per block: half the rounds of
+// dependent loads per wave.  FC2 keeps four, with several blocks per unit.
+template <int NBT, bool LO, int WV>
+__global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
   constexpr int DS = 2;                     // row steps in flight per wave
-  __shared__ uint4 wt[kMmWaves][32 * 16];
+  constexpr int kThreads = WV * kWave;
+  __shared__ uint4 wt[WV][32 * 16];
   __shared__ float red[NBT * 8 * 4][kWave];
   extern __shared__ int32_t ax_rows[];     // the chunk's row ids (rows_per_chunk entries)
   const int lane = threadIdx.x & (kWave - 1);
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
   const int64_t r0 = (int64_t)rchunk * rpc;
   int64_t r1 = r0 + rpc;
   r1 = r1 < count ? r1 : count;
-  for (int64_t j = r0 + threadIdx.x; j < r1; j += kMmThreads) {
+  for (int64_t j = r0 + threadIdx.x; j < r1; j += kThreads) {
     const int64_t row = a.list ? (int64_t)a.list[j] : j;
     ax_rows[j - r0] = (row >= 0 && row < a.n_rows) ? (int32_t)row : -1;
   }
@@ -538,7 +546,7 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
   for (int t = 0; t < NBT; ++t)
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2) acc[t][s2] = float4v_t{0.f, 0.f, 0.f, 0.f};
-  constexpr int kBlockStep = 32 * kMmWaves;
+  constexpr int kBlockStep = 32 * WV;
   for (int64_t j0 = r0 + 32 * wave; j0 < r1; j0 += (int64_t)kBlockStep * DS) {
     uint4 wv[DS][8], av[DS][NBT], al[DS][NBT];
 #pragma unroll
@@ -584,7 +592,7 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
     }
   }
   // sum the four waves in wave order; lane holds D[m = 4g + r][n = nl] of each (t, s2)
-  for (int w = 0; w < kMmWaves; ++w) {
+  for (int w = 0; w < WV; ++w) {
     if (wave == w) {
 #pragma unroll
       for (int t = 0; t < NBT; ++t)
@@ -625,7 +633,7 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy16(MmAxpyArgs a) {
     }
     return;
   }
-  for (int q = threadIdx.x; q < NBT * 8 * 4 * kWave; q += kMmThreads) {
+  for (int q = threadIdx.x; q < NBT * 8 * 4 * kWave; q += kThreads) {
     const int ln = q % kWave, idx = q / kWave;
     const int r = idx % 4, ts = idx / 4, s2 = ts % 8, t = ts / 8;
     const int b = 16 * t + 4 * (ln / 16) + r;
@@ -669,12 +677,16 @@ hipError_t axpy_dt(const MmAxpyArgs& a, hipStream_t s) {
   const dim3 g((unsigned)mm_axpy_col_chunks(a.dt, a.cols), (unsigned)a.row_chunks), t(kMmThreads);
   const size_t shm = (size_t)a.rows_per_chunk * 4;
   if (DT == 1 && a.a_h8) {
-    if (a.a_lo) {
-      if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1, true>), g, t, shm, s, a);
-      else hipLaunchKernelGGL((k_mm_axpy16<2, true>), g, t, shm, s, a);
+    if (a.a_lo && a.final_out && a.rows_per_chunk <= kOutWavesMaxRows) {
+      const dim3 t8(kOutWaves * kWave);
+      if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1, true, kOutWaves>), g, t8, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_axpy16<2, true, kOutWaves>), g, t8, shm, s, a);
+    } else if (a.a_lo) {
+      if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1, true, kMmWaves>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_axpy16<2, true, kMmWaves>), g, t, shm, s, a);
     } else {
-      if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1, false>), g, t, shm, s, a);
-      else hipLaunchKernelGGL((k_mm_axpy16<2, false>), g, t, shm, s, a);
+      if (a.nbt == 1) hipLaunchKernelGGL((k_mm_axpy16<1, false, kMmWaves>), g, t, shm, s, a);
+      else hipLaunchKernelGGL((k_mm_axpy16<2, false, kMmWaves>), g, t, shm, s, a);
     }
     return hipGetLastError();
   }

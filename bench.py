@@ -57,7 +57,7 @@ def parse():
                     help="skip the host-side placement-solver report")
     ap.add_argument("--leg", default=None, metavar="NAME",
                     help="run one leg alone and print its result instead of the benchmark line: truth, chained, "
-                         "placement, attention, batch-sweep, read-probe or config:KEY[:STRIDE] (for a profiler "
+                         "placement, attention, batch-sweep, read-probe, boundary or config:KEY[:STRIDE] (for a profiler "
                          "run over just its kernels)")
     ap.add_argument("--attn-steps", type=int, default=8,
                     help="steps of the self-attention stack with head sparsity (0 = skip)")
@@ -301,6 +301,8 @@ def rocprof_summary(roots, copy_mib):
     out = []
     scaled = {}
     rdreq = {}
+    durs = {}                  # kernel -> {dispatch: us} from the counter runs
+    allc = {}                  # (counter, kernel) -> values over every counter file
     for root in roots:
         for path in sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True)):
             rows = list(csv.DictReader(open(path)))
@@ -331,11 +333,20 @@ def rocprof_summary(roots, copy_mib):
             for r in rows:
                 k = _short_kernel(r["Kernel_Name"])
                 per.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
+                allc.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
                 if r["Counter_Name"].startswith("TCC_EA0_RDREQ"):
                     rdreq.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
+                durs.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             out.append(f"counters: {path} ({len(rows)} records)")
             for c in sorted({c for c, _ in per}):
-                if c.startswith("TCC_"):       # raw request counts: summarised by size below
+                if c.startswith("TCC_EA0_RDREQ"):   # raw request counts: summarised below
+                    continue
+                if c not in ("FETCH_SIZE", "WRITE_SIZE"):
+                    # other counters: the raw mean per dispatch
+                    out.append(f"{c}: mean per dispatch")
+                    for (cc, k), v in sorted(per.items()):
+                        if cc == c and k.startswith("k_"):
+                            out.append(f"  {k:24s} n={len(v):5d} mean={st.mean(v):14.1f}")
                     continue
                 scale = None
                 copy = per.get((c, "__amd_rocclr_copyBuffer"))
@@ -375,6 +386,37 @@ def rocprof_summary(roots, copy_mib):
                 line = (f"  plain copy of {copy_mib} MiB ({len(sel)} dispatches): {bb / 1e6:.3f} MB read by these "
                         f"requests, {bb / (copy_mib * 2**20):.4f} of its true bytes")
             out.append(line)
+        out.append("")
+    # read latency at the memory side: TCC_EA0_RDREQ_LEVEL accumulates the reads in flight every cycle, so
+    # LEVEL / RDREQ is the mean cycles a read waits; with the requests per microsecond, their product is
+    # proportional to the mean number in flight (the clock cancels in a ratio between kernels)
+    if any(c == "TCC_EA0_RDREQ_LEVEL_sum" for c, _ in rdreq):
+        out.append("reads at the memory side (TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum), per dispatch:")
+        ref = None
+        lines = []
+        for k in sorted({k for c, k in rdreq if c == "TCC_EA0_RDREQ_LEVEL_sum"}):
+            if not k.startswith("k_") or ("TCC_EA0_RDREQ_sum", k) not in rdreq:
+                continue
+            lev, req = st.mean(rdreq[("TCC_EA0_RDREQ_LEVEL_sum", k)]), st.mean(rdreq[("TCC_EA0_RDREQ_sum", k)])
+            us = st.mean(durs[k].values()) if durs.get(k) else float("nan")
+            if req <= 0 or not us > 0:
+                continue
+            lat, rate = lev / req, req / us
+            if k == "k_read_probe":
+                ref = lat * rate
+            lines.append((k, us, req, lat, rate))
+        for k, us, req, lat, rate in lines:
+            rel = f"  in flight {lat * rate / ref:5.2f} x the streaming read's" if ref else ""
+            out.append(f"  {k:24s} {us:8.2f} us  {req:11.0f} reads  {lat:7.0f} cycles each  {rate:9.0f} per us{rel}")
+        out.append("")
+    if ("TCP_UTCL1_TRANSLATION_MISS_sum" in {c for c, _ in allc}) and ("TCP_UTCL1_REQUEST_sum" in {c for c, _ in allc}):
+        out.append("address translation (TCP_UTCL1_TRANSLATION_MISS_sum / TCP_UTCL1_REQUEST_sum), per dispatch:")
+        for k in sorted({k for c, k in allc if c == "TCP_UTCL1_REQUEST_sum"}):
+            if not k.startswith("k_") or ("TCP_UTCL1_TRANSLATION_MISS_sum", k) not in allc:
+                continue
+            req, miss = st.mean(allc[("TCP_UTCL1_REQUEST_sum", k)]), st.mean(allc[("TCP_UTCL1_TRANSLATION_MISS_sum", k)])
+            if req > 0:
+                out.append(f"  {k:24s} {req:11.0f} requests  {miss:9.0f} misses  ({miss / req:.4%})")
         out.append("")
     ks = sorted({k for _, k in scaled})
     if any(("FETCH_SIZE", k) in scaled and ("WRITE_SIZE", k) in scaled for k in ks):
@@ -1328,10 +1370,66 @@ def hybrid_bench(cfg, specs, dls, steps, warmup, light=False):
     return out
 
 
+def boundary_probe(reps=200):
+    """What one dependent kernel boundary costs inside a HIP graph, from torch's own small kernels
+    (no library code): a 256-element add alone; the same add after a fill of X bytes (a kernel that
+    leaves X bytes written); and a column sum over a [32 x 7168] fp32 array (the shape of the batch-1
+    layer's FC2 partials) right after a fill of that same array or of another one.  Each figure is
+    the graph time per repetition (best of five replays of reps repetitions) minus that of the
+    graph without the measured kernel."""
+    import torch
+    dev = "cuda:0"
+
+    def graph(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        return g
+
+    def per_rep(g):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(5):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / reps)
+        return best
+
+    small = torch.zeros(256, device=dev)
+    big = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    out = {"tiny_kernel_alone_us": round(per_rep(graph(lambda: small.add_(1.0))), 3), "tiny_after_write_us": {}}
+    for X in (4 << 10, 1 << 20, 8 << 20, 64 << 20):
+        v = big[:X]
+        tf = per_rep(graph(lambda: v.fill_(1)))
+        tfa = per_rep(graph(lambda: (v.fill_(1), small.add_(1.0))))
+        out["tiny_after_write_us"][f"{X >> 10} KiB"] = round(tfa - tf, 3)
+    P = torch.randn(32, 7168, device=dev)
+    Q = torch.randn(32, 7168, device=dev)
+    y = torch.zeros(7168, device=dev)
+    colsum = lambda: torch.sum(P, dim=0, out=y)
+    out["column_sum_alone_us"] = round(per_rep(graph(colsum)), 3)
+    for name, src in (("same_array", P), ("other_array", Q)):
+        tw = per_rep(graph(lambda: src.fill_(0.5)))
+        twr = per_rep(graph(lambda: (src.fill_(0.5), colsum())))
+        out[f"column_sum_after_fill_of_{name}_us"] = round(twr - tw, 3)
+    del big, P, Q
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_leg(args):
     """One leg alone, so that a profiler run holds just its kernels: 'truth' or 'chained' (on
     --config's stack), 'placement', 'attention', 'batch-sweep' (--sweep's batches on --config's
-    stack), 'read-probe' (the streaming-read reference's sweep), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
+    stack), 'read-probe' (the streaming-read reference's sweep), 'boundary' (the cost of a dependent
+    kernel boundary in a graph), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
     import torch
     import synth
     from synth.device import DeviceLayer
@@ -1366,9 +1464,11 @@ def run_leg(args):
         res = read_probe_sweep()
     elif name == "placement":
         res = placement_bench("llama-13b-gated-40", args.placement_steps, 2, args.placement_steps)
+    elif name == "boundary":
+        res = boundary_probe()
     else:
         raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, attention, "
-                         "batch-sweep, read-probe, config:KEY[:STRIDE])")
+                         "batch-sweep, read-probe, boundary, config:KEY[:STRIDE])")
     return {"leg": args.leg, "result": res}
 
 
