@@ -336,7 +336,8 @@ def rocprof_summary(roots, copy_mib):
                 allc.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
                 if r["Counter_Name"].startswith("TCC_EA0_RDREQ"):
                     rdreq.setdefault((r["Counter_Name"], k), []).append(float(r["Counter_Value"]))
-                durs.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                if r.get("End_Timestamp") and r.get("Start_Timestamp") and r.get("Dispatch_Id"):
+                    durs.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             out.append(f"counters: {path} ({len(rows)} records)")
             for c in sorted({c for c, _ in per}):
                 if c.startswith("TCC_EA0_RDREQ"):   # raw request counts: summarised below

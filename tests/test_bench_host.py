@@ -85,6 +85,26 @@ def test_counter_scaling_by_the_plain_copy(tmp_path):
     assert f"{31000.0 * 2 * 1024 / 1e6:9.3f} MB" in line
 
 
+def test_memory_side_latency_and_translation_summary(tmp_path):
+    d = tmp_path / "pmc"
+    d.mkdir()
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(hdr)
+        # the streaming read: 1000 reads in 10 us waiting 2000 cycles each; the kernel: 400 reads in
+        # 10 us waiting 1000 cycles each -> 0.2 times the reads in flight
+        for disp, (k, req, lev) in enumerate([("k_read_probe", 1000, 2.0e6), ("k_pred_fc1<...>(...)", 400, 4.0e5)]):
+            for c, v in (("TCC_EA0_RDREQ_sum", req), ("TCC_EA0_RDREQ_LEVEL_sum", lev),
+                         ("TCP_UTCL1_REQUEST_sum", 10000), ("TCP_UTCL1_TRANSLATION_MISS_sum", 25)):
+                w.writerow([disp, f"void pi::(anonymous namespace)::{k}", c, v, 1000, 11000])
+    out = bench.rocprof_summary([str(d)], 256)
+    line = [l for l in out.splitlines() if l.strip().startswith("k_pred_fc1") and "cycles each" in l][0]
+    assert "1000 cycles each" in line and "40 per us" in line and "0.20 x the streaming read's" in line
+    tl = [l for l in out.splitlines() if l.strip().startswith("k_pred_fc1") and "misses" in l][0]
+    assert "(0.2500%)" in tl
+
+
 def test_layer_bytes_count_what_the_method_reads():
     cfg = synth.CONFIGS["opt-30b"]
     spec = synth.layer_spec(cfg, 0)
