@@ -57,7 +57,7 @@ def parse():
                     help="skip the host-side placement-solver report")
     ap.add_argument("--leg", default=None, metavar="NAME",
                     help="run one leg alone and print its result instead of the benchmark line: truth, chained, "
-                         "placement, attention, batch-sweep, read-probe, boundary or config:KEY[:STRIDE] (for a profiler "
+                         "placement, attention, batch-sweep, read-probe, boundary, warm or config:KEY[:STRIDE] (for a profiler "
                          "run over just its kernels)")
     ap.add_argument("--attn-steps", type=int, default=8,
                     help="steps of the self-attention stack with head sparsity (0 = skip)")
@@ -1426,11 +1426,81 @@ def boundary_probe(reps=200):
     return out
 
 
+def warm_probe(cfg, specs, dls, reps=10):
+    """The batch-1 layer's latency floor: one HIP graph over the stack's layers, one call each (their
+    bytes come from HBM), against graphs that call each layer two and three times in a row (the
+    repeated calls find the layer's bytes in the caches), and against one that runs each layer's
+    hidden-layer stage alone just before its call (only the predictor's hidden-layer rows warm).
+    Per-layer figures are differences of whole-graph times (best of `reps` replays)."""
+    import torch
+    import activation_sparse_amd as pi
+    dev = "cuda:0"
+    nl = len(specs)
+    d, N = cfg.d, cfg.N
+    n_g = max(s.n_g for s in specs)
+    n_c = max(len(s.T_c) for s in specs)
+    H = max(s.H for s in specs)
+    ws_bytes = pi.pi_workspace_bytes(pi.PI_OP_FFN_LAYER, 1, d, H, N, n_g)
+    wss = [torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(nl)]
+    g0 = torch.Generator(device="cpu").manual_seed(5)
+    xs = torch.randn((nl, d), generator=g0).to(dev)
+    yc = (torch.randn((nl, d), generator=g0) * 0.05).to(dev)
+    y = torch.empty(d, device=dev)
+    A_g = torch.empty(max(n_g, 1), dtype=torch.int32, device=dev)
+    A_c = torch.empty(max(n_c, 1), dtype=torch.int32, device=dev)
+    K = torch.zeros(nl, dtype=torch.int32, device=dev)
+    K_c = torch.zeros(nl, dtype=torch.int32, device=dev)
+
+    def call(L, st):
+        cold = len(specs[L].T_c) > 0
+        pi.pi_ffn_layer_stages(dls[L].layer, 1, xs[L], 0.0, yc[L] if cold else None, y, None, A_g, K[L:L + 1],
+                               A_c if cold else None, K_c[L:L + 1] if cold else None, wss[L], st,
+                               _cstruct=dls[L].layer_c)
+
+    def graph_time(seq):
+        for L, st in seq:
+            call(L, st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for L, st in seq:
+                call(L, st)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(reps):
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3)
+        del g
+        return best
+
+    A, Hs = pi.PI_STAGE_ALL, pi.PI_STAGE_HIDDEN
+    t1 = graph_time([(L, A) for L in range(nl)])
+    t2 = graph_time([(L, A) for L in range(nl) for _ in range(2)])
+    t3 = graph_time([(L, A) for L in range(nl) for _ in range(3)])
+    th = graph_time([(L, Hs) for L in range(nl)])
+    tha = graph_time([(L, s) for L in range(nl) for s in (Hs, A)])
+    out = {"layers": nl, "cold_us_per_layer": round(t1 / nl, 2),
+           "warm_second_call_us_per_layer": round((t2 - t1) / nl, 2),
+           "warm_third_call_us_per_layer": round((t3 - t2) / nl, 2),
+           "hidden_stage_alone_us_per_layer": round(th / nl, 2),
+           "after_hidden_stage_us_per_layer": round((tha - th) / nl, 2)}
+    out["warm_tokens_per_s_bound"] = round(1e6 / (out["warm_second_call_us_per_layer"] * nl), 1)
+    del wss
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_leg(args):
     """One leg alone, so that a profiler run holds just its kernels: 'truth' or 'chained' (on
     --config's stack), 'placement', 'attention', 'batch-sweep' (--sweep's batches on --config's
     stack), 'read-probe' (the streaming-read reference's sweep), 'boundary' (the cost of a dependent
-    kernel boundary in a graph), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
+    kernel boundary in a graph), 'warm' (the layer with its bytes already in the caches, on --config's
+    stack), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
     import torch
     import synth
     from synth.device import DeviceLayer
@@ -1467,9 +1537,15 @@ def run_leg(args):
         res = placement_bench("llama-13b-gated-40", args.placement_steps, 2, args.placement_steps)
     elif name == "boundary":
         res = boundary_probe()
+    elif name == "warm":
+        cfg = synth.CONFIGS[args.config]
+        specs = [synth.layer_spec(cfg, L) for L in range(args.layers or cfg.n_layers)]
+        dls = [DeviceLayer(s, "cuda:0") for s in specs]
+        torch.cuda.synchronize()
+        res = warm_probe(cfg, specs, dls)
     else:
         raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, attention, "
-                         "batch-sweep, read-probe, boundary, config:KEY[:STRIDE])")
+                         "batch-sweep, read-probe, boundary, warm, config:KEY[:STRIDE])")
     return {"leg": args.leg, "result": res}
 
 
