@@ -254,6 +254,12 @@ int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* 
     return hip_status(pi::launch_hidden_b1(g, s));
   }
   if (ln) return PI_EINVAL;   // only the batch-1 kernel normalises its input
+  if (B == 1 && pi::hidden_lds_supported(P1.dtype, d)) {
+    pi::B1Gemv g{};
+    g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
+    g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
+    return hip_status(pi::launch_hidden_lds(g, s));
+  }
   if (use_mm_row(B) && pi::mm_rowdot_supported(P1.dtype, H, d)) {
     pi::MmRowArgs m{};
     m.W = P1.data; m.Ws = P1.scales; m.dt = P1.dtype; m.gated = 0; m.cols = d; m.n_rows = H; m.list = nullptr;

@@ -31,6 +31,10 @@ struct B1Gemv {
 };
 bool b1_supported(int dt, int64_t cols);
 hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s);
+// the batch-1 hidden layer for rows past k_hidden_b1's register-held x (x staged in LDS; no
+// normalisation of the input)
+bool hidden_lds_supported(int dt, int64_t cols);
+hipError_t launch_hidden_lds(const B1Gemv& g, hipStream_t s);
 hipError_t launch_fc1_b1(const B1Gemv& g, bool gated, hipStream_t s);
 
 // Batch 1: the predictor output layer over the active hidden units (P2 stored

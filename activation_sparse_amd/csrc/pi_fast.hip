@@ -194,6 +194,73 @@ __global__ __launch_bounds__(kT) void k_hidden_b1(const void* __restrict__ W, co
   if (lane == 0) out[j] = z;
 }
 
+// h[j] = max(0, W[j].x + bias[j]) for rows past the register-held x of k_hidden_b1 (up to 32 KB,
+// NV 16-byte vectors per lane): one row per wave, its whole row's loads in flight, x staged once per
+// workgroup in LDS planes (plane p, index v holds x[E*v + 4p .. +3]).  x (from L2) is issued before
+// the row (from HBM), so the staging waits only for x.  Lanes past the row end read zero weights and
+// take zero x.  The dot runs over the lane's vectors in order, then the wave sum, as k_hidden_b1's.
+constexpr int kHidLdsWaves = 8;
+template <int DT, int NV, int BDT>
+__global__ __launch_bounds__(kHidLdsWaves * kWave) void k_hidden_lds(const void* __restrict__ W,
+                                                                      const uint16_t* __restrict__ Ws, int rows,
+                                                                      int cols, const float* __restrict__ x,
+                                                                      const void* __restrict__ bias,
+                                                                      float* __restrict__ out) {
+  constexpr int E = Fmt<DT>::E;
+  constexpr int P = E / 4;                                 // x planes
+  constexpr int NT = kHidLdsWaves * kWave;
+  constexpr int XQ = (NV * kWave * P + NT - 1) / NT;       // x float4 per thread
+  extern __shared__ __attribute__((aligned(16))) char hl_smem[];
+  float4v* xs = reinterpret_cast<float4v*>(hl_smem);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
+  const int j = blockIdx.x * kHidLdsWaves + wave;
+  const bool row_ok = j < rows;
+  const int64_t rb = row_bytes(DT, cols);
+  const int nvec = (int)(rb / 16);
+  const int npad = (nvec + kWave - 1) & ~(kWave - 1);
+  const int nq = cols / 4;
+  const float4v* x4 = reinterpret_cast<const float4v*>(x);
+  float4v xq[XQ];
+#pragma unroll
+  for (int r = 0; r < XQ; ++r) {
+    const int q = r * NT + tid;
+    xq[r] = x4[q < nq ? q : 0];
+  }
+  const Bias<BDT> bias_at(bias, (uint32_t)rows);
+  const float bj = bias_at(row_ok ? j : 0);
+  LaneRow<DT, NV> rw;
+  rw.issue(row_ok ? reinterpret_cast<const char*>(W) + (int64_t)j * rb : nullptr,
+           DT == 2 && row_ok ? Ws + (int64_t)j * (cols / 128) : nullptr, nvec, lane);
+#pragma unroll
+  for (int r = 0; r < XQ; ++r) {
+    const int q = r * NT + tid;
+    if (q < nq) xs[(q % P) * npad + q / P] = xq[r];
+  }
+  __syncthreads();
+  if (!row_ok) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int v = u * kWave + lane;
+    const bool vin = v < nvec;
+    const int vc = vin ? v : 0;
+    float xv[E];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const float4v t4 = xs[p * npad + vc];
+      xv[4 * p] = vin ? t4.x : 0.f; xv[4 * p + 1] = vin ? t4.y : 0.f;
+      xv[4 * p + 2] = vin ? t4.z : 0.f; xv[4 * p + 3] = vin ? t4.w : 0.f;
+    }
+    float wf[E];
+    widen<DT>(rw.w[u], DT == 2 ? rw.sc[u] : 1.f, wf);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc = fmaf(wf[e], xv[e], acc);
+  }
+  float z = wave_sum(acc) + bj;
+  z = z > 0.f ? z : 0.f;
+  if (lane == 0) out[j] = z;
+}
+
 // a[j] = max(0, W1[s].x + b1[s]) (* Wup[s].x if GATED), s = list[j], j < *Kp: one row per wave.
 template <int DT, int NV, bool GATED, int BDT>
 __global__ __launch_bounds__(kT) void k_fc1_b1(const void* __restrict__ W, const uint16_t* __restrict__ Ws,
@@ -642,6 +709,41 @@ hipError_t hidden_dt(const B1Gemv& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Vectors per lane of k_hidden_lds for a row of nvec 16-byte vectors (0 = unsupported): 8, 16, 24
+// or 32 (int4: 8 or 16, whose x takes a quarter of the registers per vector).
+template <int DT>
+int pick_nv_lds(int nvec) {
+  for (int nv : {8, 16, 24, 32}) {
+    if (DT == 2 && nv > 16) break;
+    if (nv * kWave >= nvec) return nv;
+  }
+  return 0;
+}
+
+template <int DT>
+hipError_t hidden_lds_dt(const B1Gemv& g, hipStream_t s) {
+  const int nvec = (int)(row_bytes(DT, g.cols) / 16);
+  const int npad = (nvec + kWave - 1) & ~(kWave - 1);
+  const size_t shm = (size_t)npad * (Fmt<DT>::E / 4) * 16;
+  const dim3 gr((unsigned)((g.rows + kHidLdsWaves - 1) / kHidLdsWaves)), bl(kHidLdsWaves * kWave);
+#define PI_HL(NVV)                                                                                          \
+  do {                                                                                                      \
+    if (g.bias && g.bias_dt == 0)                                                                          \
+      hipLaunchKernelGGL((k_hidden_lds<DT, NVV, 0>), gr, bl, shm, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out); \
+    else                                                                                                    \
+      hipLaunchKernelGGL((k_hidden_lds<DT, NVV, 1>), gr, bl, shm, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out); \
+  } while (0)
+  switch (pick_nv_lds<DT>(nvec)) {
+    case 8: PI_HL(8); break;
+    case 16: PI_HL(16); break;
+    case 24: if constexpr (DT != 2) PI_HL(24); break;
+    case 32: if constexpr (DT != 2) PI_HL(32); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef PI_HL
+  return hipGetLastError();
+}
+
 template <int DT, bool GATED>
 hipError_t fc1_dt(const B1Gemv& g, hipStream_t s) {
   const int nvec = (int)(row_bytes(DT, g.cols) / 16);
@@ -891,6 +993,20 @@ __global__ __launch_bounds__(kWave) void k_reduce_y(ReduceYArgs r) {
 bool b1_supported(int dt, int64_t cols) {
   const int nvec = (int)(row_bytes(dt, cols) / 16);
   return pick_nv_rt(dt, nvec) != 0;
+}
+
+bool hidden_lds_supported(int dt, int64_t cols) {
+  if (cols % 4 != 0) return false;
+  const int nvec = (int)(row_bytes(dt, cols) / 16);
+  return (dt == 0 ? pick_nv_lds<0>(nvec) : dt == 1 ? pick_nv_lds<1>(nvec) : pick_nv_lds<2>(nvec)) != 0;
+}
+
+hipError_t launch_hidden_lds(const B1Gemv& g, hipStream_t s) {
+  switch (g.dt) {
+    case 0: return hidden_lds_dt<0>(g, s);
+    case 1: return hidden_lds_dt<1>(g, s);
+    default: return hidden_lds_dt<2>(g, s);
+  }
 }
 
 hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s) {

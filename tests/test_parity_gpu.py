@@ -82,6 +82,24 @@ def test_small_layer_parity(cfg, B, fused):
     _run(cfg, layer=0, step=1, B=B, fused=fused)
 
 
+# rows past the register-held x of the batch-1 hidden-layer kernel: the LDS-x kernel at each of its
+# vector counts (24, 32, 24 and 8 vectors per lane), with row counts that leave its last workgroup
+# part empty
+WIDE = [
+    ph.small_case("wide-f16", d=8264, N=1024, H=37, wdtype=synth.F16, seed=21),
+    ph.small_case("wide-f16-32", d=16384, N=640, H=20, wdtype=synth.F16, seed=22),
+    ph.small_case("wide-f32", d=4104, N=768, H=24, wdtype=synth.F32, seed=23),
+    ph.small_case("wide-i4pred", d=8320, N=1024, H=40, wdtype=synth.F16, pdtype=synth.I4G128, seed=24),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("cfg", WIDE, ids=[c.key for c in WIDE])
+def test_wide_row_hidden_layer_parity(cfg, fused):
+    _dev()
+    _run(cfg, layer=0, step=1, B=1, fused=fused)
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("B", [16, 32])
 def test_large_batch_union(B, fused):
