@@ -30,8 +30,12 @@ constexpr int kWpb = kT / kWave;
 constexpr int kSegUnroll = 16;   // W2 rows in flight per wave in the segment FC2
 
 // Column tiles of 64 16-byte vectors over a row of d elements.
+// Column tiles of the segment FC2: one 16-byte vector per lane of each row (fp32 / fp16), one
+// 32-bit word (8 weights) per lane for int4 rows, whose decode would otherwise leave few waves
+// with much work each.
 __host__ __device__ inline int seg_tiles(int dt, int64_t d) {
-  return (int)((row_bytes(dt, d) / 16 + kWave - 1) / kWave);
+  const int64_t per_lane = dt == 2 ? 4 : 16;
+  return (int)((row_bytes(dt, d) / per_lane + kWave - 1) / kWave);
 }
 
 // The lane's slice of x (x[E*v .. E*v + E-1] for v = u*64 + lane) into
@@ -585,6 +589,46 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
         ru.issue(s >= 0 ? Wu + (int64_t)s * rb : nullptr, DT == 2 && s >= 0 ? a.Wus + (int64_t)s * groups : nullptr,
                  nvec, lane);
       float a0 = 0.f, g0 = 0.f;
+      if constexpr (DT == 2) {
+        // int4: one 32-bit word (8 weights, x planes 2i and 2i+1) at a time, the next word's x read
+        // from LDS before this word is decoded; each weight is (float)q * scale as widen gives it,
+        // in the same order, so the bits are widen's
+        auto xword = [&](int u, int i, float (&xo)[8]) {
+          const int v = u * kWave + lane;
+          const bool vin = v < nvec;
+          const int vc = vin ? v : 0;
+          const float4v t0 = xs[(2 * i) * npad + vc], t1 = xs[(2 * i + 1) * npad + vc];
+          xo[0] = vin ? t0.x : 0.f; xo[1] = vin ? t0.y : 0.f; xo[2] = vin ? t0.z : 0.f; xo[3] = vin ? t0.w : 0.f;
+          xo[4] = vin ? t1.x : 0.f; xo[5] = vin ? t1.y : 0.f; xo[6] = vin ? t1.z : 0.f; xo[7] = vin ? t1.w : 0.f;
+        };
+        auto word = [](const uint4& w, int i) { return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w; };
+        float xa[8], xb[8];
+        xword(0, 0, xa);
+#pragma unroll
+        for (int c = 0; c < 4 * NV; ++c) {
+          const int u = c / 4, i = c % 4;
+          if (c + 1 < 4 * NV) xword((c + 1) / 4, (c + 1) % 4, xb);
+          const uint32_t wa = word(rw.w[u], i);
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            int q = (int)((wa >> (4 * n)) & 0xF);
+            q = (q ^ 8) - 8;
+            a0 = fmaf((float)q * rw.sc[u], xa[n], a0);
+          }
+          if constexpr (GATED) {
+            const uint32_t wg = word(ru.w[u], i);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+              int q = (int)((wg >> (4 * n)) & 0xF);
+              q = (q ^ 8) - 8;
+              g0 = fmaf((float)q * ru.sc[u], xa[n], g0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int n = 0; n < 8; ++n) xa[n] = xb[n];
+        }
+      } else {
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
         const int v = u * kWave + lane;
@@ -609,6 +653,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
         // x is read from LDS vector by vector: keeps only the row's weights in
         // registers (other waves cover the LDS latency)
         __builtin_amdgcn_sched_barrier(0);
+      }
       }
       float z = wave_sum(a0) + bs;
       z = z > 0.f ? z : 0.f;
@@ -815,13 +860,13 @@ hipError_t pred_fc1_combo(const PredFc1Args& a, hipStream_t s) {
 // chunk) takes the groups [c * ngroups / C, (c + 1) * ngroups / C); its rows are
 // those groups' (slot, a) pairs with a != 0 in group order (ascending slots),
 // gathered into LDS first (one round trip), then the listed W2 rows are
-// streamed over the block's column tile: 16-byte loads, kSegUnroll rows in
+// streamed over the block's column tile: 16-byte loads (a 32-bit word for int4), kSegUnroll rows in
 // flight per wave.  It writes one partial per chunk.  The other blocks each
 // place 256 entries (four groups) of the ascending lists A_g / A_c, at offsets
 // from the counts of the groups below; list block 0 writes K and K_c.
 template <int DT>
 __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
-  constexpr int E = Fmt<DT>::E;
+  constexpr int E = DT == 2 ? 8 : Fmt<DT>::E;   // columns per lane (int4: one 32-bit word)
   extern __shared__ int32_t fsm[];
   __shared__ float red[kWpb][kWave * E];
   __shared__ int s_cnt[64], s_off[65];
@@ -921,9 +966,11 @@ __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
   const int R = s_off[nb];
   const int64_t d = a.d;
   const int64_t rb = row_bytes(DT, d);
-  const int nvec = (int)(rb / 16);
+  // the lane's unit of each row: a 16-byte vector, or for int4 a 32-bit word (8 weights)
+  constexpr int UB = DT == 2 ? 4 : 16;
+  const int nunit = (int)(rb / UB);
   const int v = tile * kWave + lane;
-  const bool vok = v < nvec;
+  const bool vok = v < nunit;
   const int64_t groups = d / 128;
   const int64_t tile_col0 = (int64_t)tile * kWave * E;
   const char* W2 = reinterpret_cast<const char*>(a.W2);
@@ -931,7 +978,8 @@ __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   for (int jb = wave; jb < R; jb += kWpb * kSegUnroll) {
-    uint4 w[kSegUnroll];
+    uint4 w[DT == 2 ? 1 : kSegUnroll];
+    uint32_t wq[DT == 2 ? kSegUnroll : 1];
     float scl[kSegUnroll], ab[kSegUnroll];
 #pragma unroll
     for (int u = 0; u < kSegUnroll; ++u) {
@@ -942,18 +990,30 @@ __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
       s = __builtin_amdgcn_readfirstlane(s < a.n_g ? s : -1);
       ab[u] = j < R ? c_a[j] : 0.f;
       const rsrc_t rw = make_rsrc(W2 + (s >= 0 ? (int64_t)s * rb : 0), s >= 0 ? (uint32_t)rb : 0u);
-      w[u] = bload16(rw, (uint32_t)v * 16u);
       if constexpr (DT == 2) {
+        wq[u] = __builtin_amdgcn_raw_buffer_load_b32(rw, (int)(v * UB), 0, 0);
         const rsrc_t rs = make_rsrc(a.W2s + (s >= 0 ? (int64_t)s * groups : 0), s >= 0 ? (uint32_t)groups * 2u : 0u);
-        scl[u] = h2f(bload2(rs, (uint32_t)(v / 4) * 2u));
+        scl[u] = h2f(bload2(rs, (uint32_t)(v / 16) * 2u));   // 16 words per 128-weight group
+      } else {
+        w[u] = bload16(rw, (uint32_t)v * 16u);
       }
     }
 #pragma unroll
     for (int u = 0; u < kSegUnroll; ++u) {
-      float wf[E];
-      widen<DT>(w[u], DT == 2 ? scl[u] : 1.f, wf);
+      if constexpr (DT == 2) {
+        // each weight is (float)q * scale, as widen gives it
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(ab[u], wf[e], acc[e]);
+        for (int n = 0; n < 8; ++n) {
+          int q = (int)((wq[u] >> (4 * n)) & 0xF);
+          q = (q ^ 8) - 8;
+          acc[n] = fmaf(ab[u], (float)q * scl[u], acc[n]);
+        }
+      } else {
+        float wf[E];
+        widen<DT>(w[u], 1.f, wf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = fmaf(ab[u], wf[e], acc[e]);
+      }
     }
   }
 #pragma unroll
