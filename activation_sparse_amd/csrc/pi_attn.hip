@@ -172,17 +172,30 @@ __global__ __launch_bounds__(kQW * kWave) void k_attn_q(AttnArgs a) {
     if (q < nq) xs[q] = xv[k];
   }
   __syncthreads();
+  // x is read from LDS one vector ahead of the dot (8 elements: float4 2v and 2v + 1), and each
+  // vector's step closes with a scheduling barrier, so the reads are not all hoisted into registers
   float acc = 0.f;
+  float4v xa0, xa1, xb0, xb1;
+  auto xread = [&](int u, float4v& x0, float4v& x1) {
+    const int v = u * kWave + lane;
+    const bool vin = v < nvec;
+    const int vc = vin ? v : 0;                               // read unconditionally, then select
+    const float4v t0 = xs[2 * vc], t1 = xs[2 * vc + 1];
+    const float4v z{0.f, 0.f, 0.f, 0.f};
+    x0 = vin ? t0 : z;
+    x1 = vin ? t1 : z;
+  };
+  xread(0, xa0, xa1);
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
-    const int v = u * kWave + lane;                           // 8 elements: float4 2v and 2v + 1
-    const float4v x0 = v < nvec ? xs[2 * v] : float4v{0.f, 0.f, 0.f, 0.f};
-    const float4v x1 = v < nvec ? xs[2 * v + 1] : float4v{0.f, 0.f, 0.f, 0.f};
+    if (u + 1 < NV) xread(u + 1, xb0, xb1);
     float wf[8];
     widen<1>(w[u], 1.f, wf);
-    acc = fmaf(wf[0], x0.x, acc); acc = fmaf(wf[1], x0.y, acc); acc = fmaf(wf[2], x0.z, acc);
-    acc = fmaf(wf[3], x0.w, acc); acc = fmaf(wf[4], x1.x, acc); acc = fmaf(wf[5], x1.y, acc);
-    acc = fmaf(wf[6], x1.z, acc); acc = fmaf(wf[7], x1.w, acc);
+    acc = fmaf(wf[0], xa0.x, acc); acc = fmaf(wf[1], xa0.y, acc); acc = fmaf(wf[2], xa0.z, acc);
+    acc = fmaf(wf[3], xa0.w, acc); acc = fmaf(wf[4], xa1.x, acc); acc = fmaf(wf[5], xa1.y, acc);
+    acc = fmaf(wf[6], xa1.z, acc); acc = fmaf(wf[7], xa1.w, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    xa0 = xb0; xa1 = xb1;
   }
   const Bias<1> bq(a.bq, (uint32_t)a.d);
   const float z = wave_sum(acc) + bq(r);
