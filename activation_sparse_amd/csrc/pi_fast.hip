@@ -4,6 +4,8 @@
 // the list-driven FC1 of pi_sparse_ffn): every lane owns the same column
 // slice of every row (vectors v = u*64 + lane), so its slice of x is loaded
 // once and reused; all 16-byte loads of a row are issued before the first FMA.
+// Hidden-layer rows too long for x in registers take the same dot with x
+// staged once per workgroup in LDS.
 //
 // The predictor's output layer with its weights stored hidden-major (row m =
 // hidden unit m's weights to the N outputs): only the rows of hidden units
@@ -18,6 +20,11 @@
 // FC2 of the batch-1 layer over those segments (only rows with a non-zero FC1
 // output), with the assembly of the ascending lists, writes one partial per
 // chunk of groups; the last launch sums the chunks in order with the merge.
+//
+// int4 rows (32 weights per 16-byte vector) are decoded one 32-bit word of 8
+// weights at a time where registers are scarce (FC1 of the fused layer), and
+// FC2 gives each lane one word of each row, so that the decode spreads over
+// more waves; each weight is (float)q * scale in the same order either way.
 #include "../../include/pi.h"
 #include "pi_device.h"
 #include "pi_b1.h"
