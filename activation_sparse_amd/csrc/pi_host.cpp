@@ -148,35 +148,65 @@ PI_AVX2 float tree32_avx2(__m256 a0, __m256 a1, __m256 a2, __m256 a3) {
   return _mm_cvtss_f32(_mm_add_ss(v, _mm_shuffle_ps(v, v, 1)));
 }
 
-PI_AVX2 void dots_avx2(const Rows& w, int64_t r, const float* x, int B, int64_t d, float* dot) {
-  for (int b0 = 0; b0 < B; b0 += 4) {
-    const int nb = B - b0 < 4 ? B - b0 : 4;
-    __m256 acc[4][4];
-    for (int i = 0; i < 4; ++i)
-      for (int q = 0; q < 4; ++q) acc[i][q] = _mm256_setzero_ps();
-    const char* rowp = w.row(r);
-    for (int64_t k0 = 0; k0 < d; k0 += 32) {
-      // the row's lines kRowPrefetchBytes ahead (the hardware prefetchers stop at page ends)
-      const int64_t po = k0 * w.rb / d + kRowPrefetchBytes;
-      if (po < w.rb) _mm_prefetch(rowp + po, _MM_HINT_T0);
-      const int nq = (d - k0) / 8 < 4 ? (int)((d - k0) / 8) : 4;
-      for (int q = 0; q < nq; ++q) {
-        const __m256 wv = load8_avx2(w, r, k0 + 8 * q);
-        for (int i = 0; i < nb; ++i)
-          acc[i][q] = _mm256_fmadd_ps(wv, _mm256_loadu_ps(x + (int64_t)(b0 + i) * d + k0 + 8 * q), acc[i][q]);
+// NB batch rows of one row's dot (NB a compile-time count, so the 4 * NB accumulators stay in
+// registers instead of a stack array reloaded and stored around every fma).
+template <int NB>
+PI_AVX2 inline void dots_avx2_nb(const Rows& w, int64_t r, const float* x, int64_t d, float* dot) {
+  __m256 acc[NB][4];
+  for (int i = 0; i < NB; ++i)
+    for (int q = 0; q < 4; ++q) acc[i][q] = _mm256_setzero_ps();
+  const char* rowp = w.row(r);
+  // the row's lines kRowPrefetchBytes ahead (the hardware prefetchers stop at page ends); 32
+  // columns are pstep bytes of every format (128, 64 or 16), so the offset advances by addition
+  const int64_t pstep = w.rb * 32 / d;
+  int64_t po = kRowPrefetchBytes;
+  int64_t k0 = 0;
+  // whole 32-column blocks, every index known at compile time
+  for (; k0 + 32 <= d; k0 += 32, po += pstep) {
+    if (po < w.rb) _mm_prefetch(rowp + po, _MM_HINT_T0);
+    __m256 wv[4];
+    for (int q = 0; q < 4; ++q) wv[q] = load8_avx2(w, r, k0 + 8 * q);
+    for (int i = 0; i < NB; ++i)
+      for (int q = 0; q < 4; ++q)
+        acc[i][q] = _mm256_fmadd_ps(wv[q], _mm256_loadu_ps(x + (int64_t)i * d + k0 + 8 * q), acc[i][q]);
+  }
+  // a tail of 8, 16 or 24 columns (d is a multiple of 8) into the first accumulators
+  if (k0 < d) {
+    const int nq = (int)((d - k0) / 8);
+    for (int q = 0; q < 3; ++q) {
+      if (q < nq) {
+        const __m256 wq = load8_avx2(w, r, k0 + 8 * q);
+        for (int i = 0; i < NB; ++i)
+          acc[i][q] = _mm256_fmadd_ps(wq, _mm256_loadu_ps(x + (int64_t)i * d + k0 + 8 * q), acc[i][q]);
       }
     }
-    for (int i = 0; i < nb; ++i) dot[b0 + i] = tree32_avx2(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+  }
+  for (int i = 0; i < NB; ++i) dot[i] = tree32_avx2(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+}
+
+PI_AVX2 void dots_avx2(const Rows& w, int64_t r, const float* x, int B, int64_t d, float* dot) {
+  for (int b0 = 0; b0 < B; b0 += 4) {
+    const float* xb = x + (int64_t)b0 * d;
+    switch (B - b0 < 4 ? B - b0 : 4) {
+      case 1: dots_avx2_nb<1>(w, r, xb, d, dot + b0); break;
+      case 2: dots_avx2_nb<2>(w, r, xb, d, dot + b0); break;
+      case 3: dots_avx2_nb<3>(w, r, xb, d, dot + b0); break;
+      default: dots_avx2_nb<4>(w, r, xb, d, dot + b0); break;
+    }
   }
 }
 
 PI_AVX2 void axpy_avx2(const Rows& w, int64_t r, const float* a, int B, int64_t d, int64_t c0, int64_t c1, float* y) {
   const char* rowp = w.row(r);
   const int64_t end = c1 * w.rb / d;
+  // one line per 32 columns of fp16 (two of fp32): the first multiple of 32 at or after c0, then
+  // pstep bytes (128, 64 or 16) per 32 columns, by addition
+  const int64_t pstep = w.rb * 32 / d;
+  int64_t po = ((c0 + 31) & ~(int64_t)31) * w.rb / d + kRowPrefetchBytes;
   for (int64_t c = c0; c < c1; c += 8) {
-    if ((c & 31) == 0) {             // one line per 32 columns of fp16 (two of fp32)
-      const int64_t po = c * w.rb / d + kRowPrefetchBytes;
+    if ((c & 31) == 0) {
       if (po < end) _mm_prefetch(rowp + po, _MM_HINT_T0);
+      po += pstep;
     }
     const __m256 wv = load8_avx2(w, r, c);
     for (int b = 0; b < B; ++b) {

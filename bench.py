@@ -57,7 +57,7 @@ def parse():
                     help="skip the host-side placement-solver report")
     ap.add_argument("--leg", default=None, metavar="NAME",
                     help="run one leg alone and print its result instead of the benchmark line: truth, chained, "
-                         "placement, attention, batch-sweep, read-probe, boundary, warm or config:KEY[:STRIDE] (for a profiler "
+                         "placement, attention, batch-sweep, read-probe, boundary, warm, host-cold or config:KEY[:STRIDE] (for a profiler "
                          "run over just its kernels)")
     ap.add_argument("--attn-steps", type=int, default=8,
                     help="steps of the self-attention stack with head sparsity (0 = skip)")
@@ -1495,12 +1495,53 @@ def warm_probe(cfg, specs, dls, reps=10):
     return out
 
 
+def host_cold_scaling(threads=(1, 2, 4, 8, 16), reps=300):
+    """The host cold FFN (pi_cold_ffn, batch 1) at the OPT-30B cold table's shape, by thread count:
+    FC1 alone (every FC1 output zero, so FC2 is skipped) over 497 listed rows of a 17,204 x 7,168 fp16
+    table, with the rows streamed from DRAM (four tables and 64 lists in turn) or cached (one table, one
+    list), and the full call (half the outputs non-zero) streamed.  Seeded normal weights (the time does
+    not depend on their values).  Median microseconds per call, from Python (a call with one listed
+    neuron gives the fixed cost)."""
+    import time
+    import numpy as np
+    from activation_sparse_amd import host, Matrix, Vector, PI_F16, PI_F32
+    d, n_c, K_c, NT = 7168, 17204, 497, 4
+    rng = np.random.default_rng(0)
+
+    def table():
+        a = np.empty((n_c, d), np.float16)
+        for i in range(0, n_c, 2048):
+            a[i:i + 2048] = (rng.standard_normal((min(2048, n_c - i), d), dtype=np.float32) / np.sqrt(d)).astype(np.float16)
+        return Matrix(a, PI_F16)
+    W1 = [table() for _ in range(NT)]
+    W2 = table()
+    x = rng.standard_normal((1, d), dtype=np.float32)
+    y = np.zeros((1, d), np.float32)
+    b_mid = Vector(np.zeros(n_c, np.float32), PI_F32)
+    b_off = Vector(np.full(n_c, -1e9, np.float32), PI_F32)
+    lists = [np.sort(rng.choice(n_c, K_c, replace=False)).astype(np.int32) for _ in range(64)]
+
+    def med(b1, rotate, T, k=K_c):
+        ts = []
+        for i in range(reps):
+            W, lst = (W1[i % NT], lists[i % 64]) if rotate else (W1[0], lists[0])
+            t0 = time.perf_counter()
+            host.pi_cold_ffn(1, d, n_c, x, W, b1, W2, lst[:k], k, y, threads=T)
+            ts.append(time.perf_counter() - t0)
+        return round(float(np.median(ts[reps // 10:])) * 1e6, 1)
+    out = {"vector_path": host.vector_path(), "fixed_us": med(b_off, False, 0, k=1), "by_threads": {}}
+    for T in threads:
+        out["by_threads"][str(T)] = {"fc1_streamed_us": med(b_off, True, T), "fc1_cached_us": med(b_off, False, T),
+                                      "full_streamed_us": med(b_mid, True, T)}
+    return out
+
+
 def run_leg(args):
     """One leg alone, so that a profiler run holds just its kernels: 'truth' or 'chained' (on
     --config's stack), 'placement', 'attention', 'batch-sweep' (--sweep's batches on --config's
     stack), 'read-probe' (the streaming-read reference's sweep), 'boundary' (the cost of a dependent
     kernel boundary in a graph), 'warm' (the layer with its bytes already in the caches, on --config's
-    stack), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
+    stack), 'host-cold' (the host cold FFN by thread count), or 'config:KEY[:STRIDE]'.  Returns that leg's result (not the benchmark line)."""
     import torch
     import synth
     from synth.device import DeviceLayer
@@ -1537,6 +1578,8 @@ def run_leg(args):
         res = placement_bench("llama-13b-gated-40", args.placement_steps, 2, args.placement_steps)
     elif name == "boundary":
         res = boundary_probe()
+    elif name == "host-cold":
+        res = host_cold_scaling()
     elif name == "warm":
         cfg = synth.CONFIGS[args.config]
         specs = [synth.layer_spec(cfg, L) for L in range(args.layers or cfg.n_layers)]
@@ -1545,7 +1588,7 @@ def run_leg(args):
         res = warm_probe(cfg, specs, dls)
     else:
         raise SystemExit(f"bench.py: unknown leg {args.leg!r} (truth, chained, placement, attention, "
-                         "batch-sweep, read-probe, boundary, warm, config:KEY[:STRIDE])")
+                         "batch-sweep, read-probe, boundary, warm, host-cold, config:KEY[:STRIDE])")
     return {"leg": args.leg, "result": res}
 
 

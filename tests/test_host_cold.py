@@ -80,8 +80,11 @@ def test_cold_ffn_matches_the_oracle(key, dt, gated, B):
     assert ph.rel_err(y.astype(np.float64), ref) <= 1e-5
 
 
-def test_bits_do_not_depend_on_threads_or_vector_unit():
-    n_c, d, B = 900, 1024, 4
+# batch counts that take each register block of the vector dot (1-4 rows, and 4 + 1, 4 + 2) and
+# row lengths that end in a partial 32-column block (8, 16 and 24 columns) or none
+@pytest.mark.parametrize("B,d", [(4, 1024), (1, 1048), (2, 1032), (3, 1040), (5, 1024), (6, 1048)])
+def test_bits_do_not_depend_on_threads_or_vector_unit(B, d):
+    n_c = 900
     W1, b1, _, W2 = _case(synth.F16, n_c, d, 5)
     g = np.random.default_rng(11)
     A_c = np.sort(g.choice(n_c, size=400, replace=False)).astype(np.int32)
