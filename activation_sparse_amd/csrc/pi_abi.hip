@@ -246,20 +246,15 @@ struct LnIn {
 int enqueue_hidden(hipStream_t s, int32_t B, int32_t d, int32_t H, const float* x, const pi_matrix& P1,
                    const pi_vector& c1, float* h, float* partials, int h_lay, const LnIn* ln = nullptr) {
   const bool h_tr = h_lay != 0;
-  if (B == 1 && pi::b1_supported(P1.dtype, d)) {
-    pi::B1Gemv g{};
-    g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
-    g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
-    if (ln) { g.ln_stats = ln->stats; g.ln_eps = ln->eps; g.x_out = ln->x_out; }
-    return hip_status(pi::launch_hidden_b1(g, s));
-  }
-  if (ln) return PI_EINVAL;   // only the batch-1 kernel normalises its input
+  // batch 1: x staged once per workgroup in LDS, normalised there first when ln is given
   if (B == 1 && pi::hidden_lds_supported(P1.dtype, d)) {
     pi::B1Gemv g{};
     g.W = P1.data; g.Ws = P1.scales; g.dt = P1.dtype; g.rows = H; g.cols = d; g.x = x;
     g.bias = c1.data; g.bias_dt = c1.dtype; g.out = h;
+    if (ln) { g.ln_stats = ln->stats; g.ln_eps = ln->eps; g.x_out = ln->x_out; }
     return hip_status(pi::launch_hidden_lds(g, s));
   }
+  if (ln) return PI_EINVAL;   // only the batch-1 kernel normalises its input
   if (use_mm_row(B) && pi::mm_rowdot_supported(P1.dtype, H, d)) {
     pi::MmRowArgs m{};
     m.W = P1.data; m.Ws = P1.scales; m.dt = P1.dtype; m.gated = 0; m.cols = d; m.n_rows = H; m.list = nullptr;
@@ -662,7 +657,7 @@ int layer_stages(void* stream, const pi_layer* L, int32_t B, const float* x, flo
   const int32_t ngroups = (int32_t)n_groups64(N);
   const int bdt = L->b1.data ? L->b1.dtype : (L->c2.data ? L->c2.dtype : PI_F16);
   const bool fused = b1_fused(L, B);
-  if (ln && (!fused || !pi::b1_supported(L->P1.dtype, d) || stages != PI_STAGE_ALL || ah)) return PI_EINVAL;
+  if (ln && (!fused || !pi::hidden_lds_supported(L->P1.dtype, d) || stages != PI_STAGE_ALL || ah)) return PI_EINVAL;
   float* lg = logits ? logits : w.logits;
 
   if ((st = record(0)) != PI_OK) return st;
@@ -785,7 +780,7 @@ int pi_ffn_layer_normed(void* stream, const pi_layer* L, int32_t B, const float*
   if (!ws || !aligned16(ws)) return PI_EWORKSPACE;
   const NormedWs n = normed_ws_layout(ws, B, L->d, L->H, L->N, L->n_g);
   if (ws_bytes < n.bytes) return PI_EWORKSPACE;
-  if (b1_fused(L, B) && pi::b1_supported(L->P1.dtype, L->d)) {
+  if (b1_fused(L, B) && pi::hidden_lds_supported(L->P1.dtype, L->d)) {
     LnIn ln{eps, n.stats, x_out};
     return layer_stages(stream, L, B, y_prev, tau, y_c, y, logits, A_g, K, A_c, K_c, n.layer, n.layer_bytes, nullptr,
                         PI_STAGE_ALL, nullptr, nullptr, &ln);

@@ -30,9 +30,8 @@ struct B1Gemv {
   float* x_out;
 };
 bool b1_supported(int dt, int64_t cols);
-hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s);
-// the batch-1 hidden layer for rows past k_hidden_b1's register-held x (x staged in LDS; no
-// normalisation of the input)
+// the batch-1 hidden layer with x staged in LDS (rows up to 32 KB); with ln_stats, x is first
+// normalised (layer normalisation, unit gain, zero bias) and the statistics and x_out written
 bool hidden_lds_supported(int dt, int64_t cols);
 hipError_t launch_hidden_lds(const B1Gemv& g, hipStream_t s);
 hipError_t launch_fc1_b1(const B1Gemv& g, bool gated, hipStream_t s);

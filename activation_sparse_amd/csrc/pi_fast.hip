@@ -4,8 +4,8 @@
 // the list-driven FC1 of pi_sparse_ffn): every lane owns the same column
 // slice of every row (vectors v = u*64 + lane), so its slice of x is loaded
 // once and reused; all 16-byte loads of a row are issued before the first FMA.
-// Hidden-layer rows too long for x in registers take the same dot with x
-// staged once per workgroup in LDS.
+// The batch-1 hidden layer takes the same dot with x staged once per
+// workgroup in LDS (the register-held x serves the call that normalises x).
 //
 // The predictor's output layer with its weights stored hidden-major (row m =
 // hidden unit m's weights to the N outputs): only the rows of hidden units
@@ -103,120 +103,22 @@ struct LaneRow {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
 
-// Layer normalisation of the register-held x slice (the lane's vectors v = u*64 + lane, E
-// elements each, zeros past nvec, where the weights read zeros too) of every wave of the block:
-// x <- fma(x, inv, -mean * inv) with
-// inv = 1 / sqrt(var + eps), mean and population variance over the n elements.  The four waves
-// share the work: wave w sums the slice vectors u = w, w + 4, ... (fp32, in slice order), the
-// wave butterfly and the sum over the waves in wave order give the mean, then the same for the
-// squared deviations (two passes).  Every block runs the same partition, so every wave of the
-// grid gets the same two values.  Every wave of the block must call this (it has barriers).
-// stats / x_out (wave-uniform, may be NULL) receive the mean and inv, and the normalised row.
-template <int DT, int NV>
-__device__ __forceinline__ void layer_norm_xreg(float (&xr)[NV][Fmt<DT>::E], int nvec, int n, float eps, int lane,
-                                                int wave, float* stats, float* x_out) {
-  constexpr int E = Fmt<DT>::E;
-  __shared__ float part[2][kWpb];
-  float s = 0.f;
-#pragma unroll
-  for (int u = 0; u < NV; ++u)
-    if (u % kWpb == wave)                         // wave-uniform
-#pragma unroll
-      for (int e = 0; e < E; ++e) s += xr[u][e];  // past nvec: zeros
-  s = wave_sum(s);
-  if (lane == 0) part[0][wave] = s;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWpb; ++w) tot += part[0][w];
-  const float mu = tot / (float)n;
-  float q = 0.f;
-#pragma unroll
-  for (int u = 0; u < NV; ++u)
-    if (u % kWpb == wave) {
-      const bool ok = u * kWave + lane < nvec;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float dv = xr[u][e] - mu;
-        q += ok ? dv * dv : 0.f;
-      }
-    }
-  q = wave_sum(q);
-  if (lane == 0) part[1][wave] = q;
-  __syncthreads();
-  float var = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWpb; ++w) var += part[1][w];
-  const float inv = 1.0f / sqrtf(var / (float)n + eps);
-  const float nm = -mu * inv;
-#pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const int v = u * kWave + lane;
-    const bool ok = v < nvec;
-    // past nvec the row reads zeros, so those elements need no mask
-#pragma unroll
-    for (int e = 0; e < E; ++e) xr[u][e] = fmaf(xr[u][e], inv, nm);
-    if (x_out && ok) {
-#pragma unroll
-      for (int q4 = 0; q4 < E / 4; ++q4)
-        *reinterpret_cast<float4v*>(x_out + (int64_t)E * v + 4 * q4) =
-            float4v{xr[u][4 * q4], xr[u][4 * q4 + 1], xr[u][4 * q4 + 2], xr[u][4 * q4 + 3]};
-    }
-  }
-  if (stats && lane == 0) { stats[0] = mu; stats[1] = inv; }
-}
-
-// h[j] = max(0, W[j].x + bias[j]) for j < rows: one row per wave.  With ln_stats, x is first
-// replaced by its layer normalisation (mean and population variance over the cols elements),
-// computed by each block's waves together from the x every wave holds (the same bits in every
-// block); the grid's first wave writes the two statistics (and the normalised row to x_out) for
-// the kernels after it.
-template <int DT, int NV, int BDT>
-__global__ __launch_bounds__(kT) void k_hidden_b1(const void* __restrict__ W, const uint16_t* __restrict__ Ws,
-                                                   int rows, int cols, const float* __restrict__ x,
-                                                   const void* __restrict__ bias, float* __restrict__ out,
-                                                   float* __restrict__ ln_stats, float ln_eps,
-                                                   float* __restrict__ x_out) {
-  const int lane = threadIdx.x & (kWave - 1), wave = wave_id();
-  const int gw = blockIdx.x * kWpb + wave;
-  // waves past the rows still take part in the block's normalisation (it has barriers)
-  if (gw >= rows && !ln_stats) return;
-  const bool row_ok = gw < rows;
-  const int64_t rb = row_bytes(DT, cols);
-  const int nvec = (int)(rb / 16);
-  const int groups = cols / 128;
-  const Bias<BDT> bias_at(bias, (uint32_t)rows);
-  const int j = row_ok ? gw : 0;    // the grid has one wave per row
-  const float bj = bias_at(j);
-  // x (from L2) is issued before the weight row (from HBM): the normalisation below waits only
-  // for x and runs while the row is still arriving
-  float xr[NV][Fmt<DT>::E];
-  load_xreg<DT, NV>(x, nvec, lane, xr);
-  LaneRow<DT, NV> r;
-  r.issue(row_ok ? reinterpret_cast<const char*>(W) + (int64_t)j * rb : nullptr,
-          DT == 2 && row_ok ? Ws + (int64_t)j * groups : nullptr, nvec, lane);
-  if (ln_stats) {
-    layer_norm_xreg<DT, NV>(xr, nvec, cols, ln_eps, lane, wave, gw == 0 ? ln_stats : nullptr,
-                            gw == 0 ? x_out : nullptr);
-    if (!row_ok) return;
-  }
-  float z = wave_sum(r.dot(xr)) + bj;
-  z = z > 0.f ? z : 0.f;
-  if (lane == 0) out[j] = z;
-}
-
-// h[j] = max(0, W[j].x + bias[j]) for rows past the register-held x of k_hidden_b1 (up to 32 KB,
-// NV 16-byte vectors per lane): one row per wave, its whole row's loads in flight, x staged once per
-// workgroup in LDS planes (plane p, index v holds x[E*v + 4p .. +3]).  x (from L2) is issued before
-// the row (from HBM), so the staging waits only for x.  Lanes past the row end read zero weights and
-// take zero x.  The dot runs over the lane's vectors in order, then the wave sum, as k_hidden_b1's.
-constexpr int kHidLdsWaves = 8;
-template <int DT, int NV, int BDT>
+// h[j] = max(0, W[j].x + bias[j]) at batch 1, rows up to 32 KB (NV 16-byte vectors per lane): one
+// row per wave, its whole row's loads in flight, x staged once per four-wave workgroup in LDS planes
+// (plane p, index v holds x[E*v + 4p .. +3]), x (from L2) issued before the row (from HBM) so that
+// the staging waits only for x.  Lanes past the row end read zero weights and take zero x.  The dot
+// runs over the lane's vectors in order, then the wave sum.  With LN, x is first replaced by its layer
+// normalisation, and the grid's first workgroup writes the mean, 1/sqrt(var + eps) and the
+// normalised row for the kernels after it.
+constexpr int kHidLdsWaves = 4;
+template <int DT, int NV, int BDT, bool LN>
 __global__ __launch_bounds__(kHidLdsWaves * kWave) void k_hidden_lds(const void* __restrict__ W,
                                                                       const uint16_t* __restrict__ Ws, int rows,
                                                                       int cols, const float* __restrict__ x,
                                                                       const void* __restrict__ bias,
-                                                                      float* __restrict__ out) {
+                                                                      float* __restrict__ out,
+                                                                      float* __restrict__ ln_stats, float ln_eps,
+                                                                      float* __restrict__ x_out) {
   constexpr int E = Fmt<DT>::E;
   constexpr int P = E / 4;                                 // x planes
   constexpr int NT = kHidLdsWaves * kWave;
@@ -242,6 +144,55 @@ __global__ __launch_bounds__(kHidLdsWaves * kWave) void k_hidden_lds(const void*
   LaneRow<DT, NV> rw;
   rw.issue(row_ok ? reinterpret_cast<const char*>(W) + (int64_t)j * rb : nullptr,
            DT == 2 && row_ok ? Ws + (int64_t)j * (cols / 128) : nullptr, nvec, lane);
+  if constexpr (LN) {
+    // x replaced by its layer normalisation (unit gain, zero bias): the mean, then the population
+    // variance, each summed over the thread's staged values in order, the wave butterfly and the
+    // waves in wave order (every workgroup the same partition, so the same two values), while the
+    // row is still arriving; x becomes fma(x, inv, -mean * inv), the form the next kernel applies
+    // to its own copy with the two values written here
+    __shared__ float part[2][kHidLdsWaves];
+    float sa = 0.f;
+#pragma unroll
+    for (int r = 0; r < XQ; ++r)
+      if (r * NT + tid < nq) { sa += xq[r].x; sa += xq[r].y; sa += xq[r].z; sa += xq[r].w; }
+    sa = wave_sum(sa);
+    if (lane == 0) part[0][wave] = sa;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kHidLdsWaves; ++w) tot += part[0][w];
+    const float mu = tot / (float)cols;
+    float sq = 0.f;
+#pragma unroll
+    for (int r = 0; r < XQ; ++r)
+      if (r * NT + tid < nq) {
+        const float d0 = xq[r].x - mu, d1 = xq[r].y - mu, d2 = xq[r].z - mu, d3 = xq[r].w - mu;
+        sq += d0 * d0; sq += d1 * d1; sq += d2 * d2; sq += d3 * d3;
+      }
+    sq = wave_sum(sq);
+    if (lane == 0) part[1][wave] = sq;
+    __syncthreads();
+    float var = 0.f;
+#pragma unroll
+    for (int w = 0; w < kHidLdsWaves; ++w) var += part[1][w];
+    const float inv = 1.0f / sqrtf(var / (float)cols + ln_eps);
+    const float nm = -mu * inv;
+#pragma unroll
+    for (int r = 0; r < XQ; ++r) {
+      xq[r].x = fmaf(xq[r].x, inv, nm); xq[r].y = fmaf(xq[r].y, inv, nm);
+      xq[r].z = fmaf(xq[r].z, inv, nm); xq[r].w = fmaf(xq[r].w, inv, nm);
+    }
+    if (blockIdx.x == 0) {               // the grid's first workgroup reports them
+      if (x_out) {
+#pragma unroll
+        for (int r = 0; r < XQ; ++r) {
+          const int q = r * NT + tid;
+          if (q < nq) reinterpret_cast<float4v*>(x_out)[q] = xq[r];
+        }
+      }
+      if (tid == 0) { ln_stats[0] = mu; ln_stats[1] = inv; }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < XQ; ++r) {
     const int q = r * NT + tid;
@@ -736,31 +687,6 @@ int grid_for(int64_t waves, int cap) {
   return (int)(b < 1 ? 1 : (b > cap ? cap : b));
 }
 
-template <int DT>
-hipError_t hidden_dt(const B1Gemv& g, hipStream_t s) {
-  const int nvec = (int)(row_bytes(DT, g.cols) / 16);
-  const dim3 gr((unsigned)grid_for(g.rows, 1 << 30)), bl(kT);
-#define PI_HID(NVV)                                                                                        \
-  do {                                                                                                      \
-    if (g.bias && g.bias_dt == 0)                                                                          \
-      hipLaunchKernelGGL((k_hidden_b1<DT, NVV, 0>), gr, bl, 0, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out, \
-                         g.ln_stats, g.ln_eps, g.x_out);                                                   \
-    else                                                                                                    \
-      hipLaunchKernelGGL((k_hidden_b1<DT, NVV, 1>), gr, bl, 0, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out, \
-                         g.ln_stats, g.ln_eps, g.x_out);                                                   \
-  } while (0)
-  switch (pick_nv<DT>(nvec)) {
-    case 1: PI_HID(1); break;
-    case 2: PI_HID(2); break;
-    case 4: PI_HID(4); break;
-    case 8: if constexpr (Fmt<DT>::E <= 16) PI_HID(8); break;
-    case 16: if constexpr (Fmt<DT>::E <= 8) PI_HID(16); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef PI_HID
-  return hipGetLastError();
-}
-
 // Vectors per lane of k_hidden_lds for a row of nvec 16-byte vectors (0 = unsupported): 8, 16, 24
 // or 32 (int4: 8 or 16, whose x takes a quarter of the registers per vector).
 template <int DT>
@@ -778,12 +704,19 @@ hipError_t hidden_lds_dt(const B1Gemv& g, hipStream_t s) {
   const int npad = (nvec + kWave - 1) & ~(kWave - 1);
   const size_t shm = (size_t)npad * (Fmt<DT>::E / 4) * 16;
   const dim3 gr((unsigned)((g.rows + kHidLdsWaves - 1) / kHidLdsWaves)), bl(kHidLdsWaves * kWave);
+#define PI_HL_LN(NVV, BB)                                                                                   \
+  do {                                                                                                      \
+    if (g.ln_stats)                                                                                         \
+      hipLaunchKernelGGL((k_hidden_lds<DT, NVV, BB, true>), gr, bl, shm, s, g.W, g.Ws, g.rows, g.cols, g.x,   \
+                         g.bias, g.out, g.ln_stats, g.ln_eps, g.x_out);                                     \
+    else                                                                                                    \
+      hipLaunchKernelGGL((k_hidden_lds<DT, NVV, BB, false>), gr, bl, shm, s, g.W, g.Ws, g.rows, g.cols, g.x,  \
+                         g.bias, g.out, nullptr, 0.f, nullptr);                                             \
+  } while (0)
 #define PI_HL(NVV)                                                                                          \
   do {                                                                                                      \
-    if (g.bias && g.bias_dt == 0)                                                                          \
-      hipLaunchKernelGGL((k_hidden_lds<DT, NVV, 0>), gr, bl, shm, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out); \
-    else                                                                                                    \
-      hipLaunchKernelGGL((k_hidden_lds<DT, NVV, 1>), gr, bl, shm, s, g.W, g.Ws, g.rows, g.cols, g.x, g.bias, g.out); \
+    if (g.bias && g.bias_dt == 0) PI_HL_LN(NVV, 0);                                                         \
+    else PI_HL_LN(NVV, 1);                                                                                  \
   } while (0)
   switch (pick_nv_lds<DT>(nvec)) {
     case 8: PI_HL(8); break;
@@ -793,6 +726,7 @@ hipError_t hidden_lds_dt(const B1Gemv& g, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
 #undef PI_HL
+#undef PI_HL_LN
   return hipGetLastError();
 }
 
@@ -1073,14 +1007,6 @@ hipError_t launch_hidden_lds(const B1Gemv& g, hipStream_t s) {
     case 0: return hidden_lds_dt<0>(g, s);
     case 1: return hidden_lds_dt<1>(g, s);
     default: return hidden_lds_dt<2>(g, s);
-  }
-}
-
-hipError_t launch_hidden_b1(const B1Gemv& g, hipStream_t s) {
-  switch (g.dt) {
-    case 0: return hidden_dt<0>(g, s);
-    case 1: return hidden_dt<1>(g, s);
-    default: return hidden_dt<2>(g, s);
   }
 }
 
