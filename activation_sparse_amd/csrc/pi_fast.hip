@@ -665,9 +665,11 @@ int pick_nv(int nvec) {
 
 // Vectors per lane of the fused kernel's FC1 rows, whose x is in LDS (not registers): the row's
 // loads alone bound it, 16 vectors for fp32 / fp16 rows and 8 for int4 rows (32 weights each).
+// The steps of 10 and 12 keep a gated layer's two rows (W1 and Wup, both in flight) to the
+// registers they need: at d = 5,120 fp16, 121 VGPRs (four waves per SIMD) against 187 (two).
 template <int DT>
 int pick_nv_fused(int nvec) {
-  for (int nv : {4, 8, 16}) {
+  for (int nv : {4, 8, 10, 12, 16}) {
     if (DT == 2 && nv > 8) break;
     if (nv * kWave >= nvec) return nv;
   }
@@ -790,6 +792,8 @@ hipError_t pred_fc1_combo(const PredFc1Args& a, hipStream_t s) {
   switch (nv) {
     case 4: PI_PF(4);
     case 8: PI_PF(8);
+    case 10: if constexpr (Fmt<DT>::E <= 8) PI_PF(10);
+    case 12: if constexpr (Fmt<DT>::E <= 8) PI_PF(12);
     case 16: if constexpr (Fmt<DT>::E <= 8) PI_PF(16);
     default: return hipErrorInvalidValue;
   }

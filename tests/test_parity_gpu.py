@@ -100,6 +100,22 @@ def test_wide_row_hidden_layer_parity(cfg, fused):
     _run(cfg, layer=0, step=1, B=1, fused=fused)
 
 
+# rows of the fused kernel's FC1 at 10 and 12 vectors per lane (fp16 rows of 640 and 704 / 768
+# vectors, fp32 rows of 640), gated and not
+FC1_WIDTHS = [
+    ph.small_case("nv10-f16-gated", d=5120, N=1024, H=40, wdtype=synth.F16, gated=True, rho=0.15, seed=31),
+    ph.small_case("nv12-f16", d=5632, N=1088, H=48, wdtype=synth.F16, seed=32),
+    ph.small_case("nv12-f16-gated", d=6144, N=960, H=36, wdtype=synth.F16, gated=True, seed=33),
+    ph.small_case("nv10-f32", d=2560, N=1024, H=40, wdtype=synth.F32, seed=34),
+]
+
+
+@pytest.mark.parametrize("cfg", FC1_WIDTHS, ids=[c.key for c in FC1_WIDTHS])
+def test_fused_fc1_row_widths(cfg):
+    _dev()
+    _run(cfg, layer=0, step=1, B=1, fused=True)
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("B", [16, 32])
 def test_large_batch_union(B, fused):
