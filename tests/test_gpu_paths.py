@@ -695,7 +695,8 @@ def test_chained_layers(B, ahead):
             assert np.max(np.abs(xs[l + 1].astype(np.float64) - orc.layer_norm(y, 1e-5))) <= LN_ATOL, l
 
 
-@pytest.mark.parametrize("case,B", [("opt-30b", 1), ("gated", 1), ("i4ffn", 1), ("opt-30b", 4), ("gated", 3)])
+@pytest.mark.parametrize("case,B", [("opt-30b", 1), ("gated", 1), ("i4ffn", 1), ("wide-i4ffn", 1), ("i4pred", 1),
+                                    ("opt-30b", 4), ("gated", 3)])
 def test_normed_layer_is_the_layer_on_its_normalised_input(case, B):
     """pi_ffn_layer_normed(y_prev) gives bit for bit what pi_ffn_layer gives on the normalised row it
     reports in x_out (at batch 1 the predictor's kernel and the FC1 kernel normalise with the same
@@ -709,6 +710,12 @@ def test_normed_layer_is_the_layer_on_its_normalised_input(case, B):
         cfg, layer = synth.CONFIGS["opt-30b"], 7
     elif case == "gated":
         cfg, layer = ph.small_case("ln-gated", d=1024, N=4096, H=256, wdtype=synth.F16, gated=True, seed=41), 0
+    elif case == "wide-i4ffn":     # 24 KB predictor rows: the hidden-layer kernel at 24 vectors per lane
+        cfg, layer = ph.small_case("ln-wide-i4", d=12288, N=1024, H=40, wdtype=synth.I4G128, pdtype=synth.F16,
+                                   bdtype=synth.F16, seed=44), 0
+    elif case == "i4pred":         # int4 predictor rows in the normalising hidden-layer kernel
+        cfg, layer = ph.small_case("ln-i4pred", d=2048, N=2048, H=128, wdtype=synth.F16, pdtype=synth.I4G128,
+                                   gpu_frac=0.4, seed=45), 0
     else:
         cfg, layer = ph.small_case("ln-i4", d=1024, N=4096, H=256, wdtype=synth.I4G128, pdtype=synth.F16,
                                    bdtype=synth.F16, gpu_frac=0.4, seed=43), 0
