@@ -278,6 +278,16 @@ __device__ __forceinline__ int nth_set_bit64(uint64_t x, int r) {
   return base;
 }
 
+// Workgroups go to the eight dies round robin by index, and each die has its own L2.  Tile t of
+// the first (n / 8) * 8 runs on die t / (n / 8): neighbouring tiles share a die, so a cache line
+// that holds several tiles' slices (an int4 P2 row: 32 bytes per 64-id tile) is fetched into one L2.
+__device__ __forceinline__ int xcd_tile(int b, int n) {
+  constexpr int kDies = 8;
+  const int per = n / kDies;
+  if (b >= per * kDies) return b;
+  return (b % kDies) * per + b / kDies;
+}
+
 // Geometry of the output-layer tile kernel for T neuron ids per block.
 template <int T>
 struct TileGeom {
@@ -322,7 +332,10 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
   const int H = a.H, N = a.N;
   const int ngroups = (N + 63) / 64;
-  const int64_t i0 = (int64_t)blockIdx.x * T;
+  const int ntl = (N + T - 1) / T;
+  // int4 P2 rows give each tile a 32-byte slice: its neighbours share the line, so they share a die
+  const int tile = PDT == 2 && (int)blockIdx.x < ntl ? xcd_tile((int)blockIdx.x, ntl) : (int)blockIdx.x;
+  const int64_t i0 = (int64_t)tile * T;
   float4v* xs = reinterpret_cast<float4v*>(pf_smem);
 
   // ---- issue: table words, bias, x, h
@@ -330,7 +343,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   int gp[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const int grp = blockIdx.x * NG + g;
+    const int grp = tile * NG + g;
     const bool in = FC1 && grp < ngroups;
     Gb[g] = in ? ((uint64_t)a.gbits[2 * grp] | ((uint64_t)a.gbits[2 * grp + 1] << 32)) : 0ull;
     gp[g] = in ? a.gpre[grp] : 0;
@@ -427,7 +440,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   {
     const int64_t prb = row_bytes(PDT, N);
     const int pvec = (int)(prb / 16);
-    int colv = blockIdx.x * LPR + cl;
+    int colv = tile * LPR + cl;
     colv = colv < pvec ? colv : pvec - 1;          // past the row end: discarded ids
     const int pgroups = N / 128;
     // the whole matrix as one buffer (the host keeps H * row bytes below 2^31)
@@ -477,16 +490,29 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
         }
       }
     }
-    // the RPL row groups of the wave hold partial sums of the same ids: butterfly
-    // sum (every lane ends with the same bits)
+    // the RPL row groups of the wave hold partial sums of the same ids: a reduce-scatter over
+    // them, whose pairwise sums are a butterfly's (partner groups sub and sub ^ 2^s, s ascending),
+    // each computed once, in the lane that keeps that id.  At step s a lane holds n = EP >> s ids
+    // and keeps the half that bit s of sub selects, so lane (cl, sub) ends with EP / RPL ids'
+    // sums: log2(RPL) steps of n / 2 exchanges (31 for int4 rows, against 160 for every lane
+    // summing all EP ids), the same bits.
+    static_assert(EP % RPL == 0 && (RPL & (RPL - 1)) == 0, "row groups: a power of two dividing EP");
+    int base = 0;
 #pragma unroll
-    for (int off = LPR; off < kWave; off <<= 1)
+    for (int st = 0; (LPR << st) < kWave; ++st) {
+      const int h = (EP >> st) / 2;
+      const bool up = ((sub >> st) & 1) != 0;
 #pragma unroll
-      for (int e = 0; e < EP; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
-    if (sub == 0)
+      for (int i = 0; i < h; ++i) {
+        const float keep = up ? acc[h + i] : acc[i];
+        const float give = up ? acc[i] : acc[h + i];
+        acc[i] = keep + __shfl_xor(give, LPR << st, kWave);
+      }
+      base += up ? h : 0;
+    }
 #pragma unroll
-      for (int e = 0; e < EP; ++e) red[wave][cl * EP + e] = acc[e];
-    if (a.rows_read && blockIdx.x == 0) {
+    for (int i = 0; i < EP / RPL; ++i) red[wave][cl * EP + base + i] = acc[i];
+    if (a.rows_read && tile == 0) {
       int c = cl == 0 ? nact : 0;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
@@ -494,7 +520,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     }
   }
   __syncthreads();
-  if (a.rows_read && blockIdx.x == 0 && tid == 0) {
+  if (a.rows_read && tile == 0 && tid == 0) {
     int c = 0;
     for (int w2 = 0; w2 < W; ++w2) c += s_cnt[w2];
     *a.rows_read = c;
@@ -508,7 +534,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     if (a.logits && valid) a.logits[id] = z;
     const uint64_t bits = __ballot(valid && z > a.tau);
     if (lane == 0) s_M[wave] = bits;
-    const int grp = blockIdx.x * NG + wave;
+    const int grp = tile * NG + wave;
     if (!FC1 && a.mask && lane == 0 && grp < ngroups) {
       a.mask[2 * grp] = (uint32_t)bits;
       a.mask[2 * grp + 1] = (uint32_t)(bits >> 32);
@@ -627,7 +653,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   // ---- segments of each 64-id group, by wave g
   if (wave < NG) {
     const int g = wave;
-    const int grp = blockIdx.x * NG + g;
+    const int grp = tile * NG + g;
     if (grp < ngroups) {
       const int r0 = g == 0 ? 0 : kg[0];
       const int k = kg[g];
@@ -690,10 +716,12 @@ int grid_for(int64_t waves, int cap) {
 }
 
 // Vectors per lane of k_hidden_lds for a row of nvec 16-byte vectors (0 = unsupported): 8, 16, 24
-// or 32 (int4: 8 or 16, whose x takes a quarter of the registers per vector).
+// or 32 (int4: 4, 8 or 16, whose x takes a quarter of the registers per vector; a 3.5 KB int4 row
+// at d = 7,168 fills 3.5 vectors per lane, and at 8 the unused half still cost registers and work).
 template <int DT>
 int pick_nv_lds(int nvec) {
-  for (int nv : {8, 16, 24, 32}) {
+  for (int nv : {4, 8, 16, 24, 32}) {
+    if (DT != 2 && nv < 8) continue;
     if (DT == 2 && nv > 16) break;
     if (nv * kWave >= nvec) return nv;
   }
@@ -721,6 +749,7 @@ hipError_t hidden_lds_dt(const B1Gemv& g, hipStream_t s) {
     else PI_HL_LN(NVV, 1);                                                                                  \
   } while (0)
   switch (pick_nv_lds<DT>(nvec)) {
+    case 4: if constexpr (DT == 2) PI_HL(4); break;
     case 8: PI_HL(8); break;
     case 16: PI_HL(16); break;
     case 24: if constexpr (DT != 2) PI_HL(24); break;
