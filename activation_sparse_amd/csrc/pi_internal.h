@@ -114,7 +114,8 @@ struct MmRowArgs {              // out[b, pos] = finish(sum_k W[row(pos), k] x[b
   int64_t out_stride;           // [count_max x 16 nbt] neuron-major (zeros past B)
   int out_tr;
   int out_h8;                   // with out_tr: fp16 [pos / 8][16 nbt][8] (zeros past B and up to the next
-                                // multiple of 32 positions), the activations of the fp16 axpy
+                                // multiple of 32 positions), the activations of the fp16 axpy; vector q
+                                // of each 32-position block holds positions q, q + 4, .., q + 28
   float* out_lo;                // with out_h8, optional: the same layout holding fp16(z - fp16(z))
   int x_f16;                    // fp16 weights: x may be rounded to fp16 (fp16 matrix cores; FC1 only)
   int x_hilo;                   // fp16 weights: x as two fp16 parts, hi = fp16(x) and lo = fp16(x - hi),

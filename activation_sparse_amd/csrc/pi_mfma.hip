@@ -326,13 +326,15 @@ __global__ __launch_bounds__(256) void k_mm_finish_tr(MmRowArgs a) {
     count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
   }
   // the fp16 layout is written up to the next multiple of 32 positions (zeros), so
-  // that the axpy's 8-position vectors never hold stale values
+  // that the axpy's 8-position vectors never hold stale values.  Within each block of 32
+  // positions, vector q (of four) holds positions q, q + 4, ..., q + 28: the rows that lane
+  // group q of the axpy loads, in the order of its k slots
   const int64_t npos = a.out_h8 ? (count + 31) / 32 * 32 : count;
   const int64_t n = npos * NBP;
   for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
     const int64_t pos = t / NBP;
     const int b = (int)(t % NBP);
-    const int64_t h8 = ((pos / 8) * NBP + b) * 8 + pos % 8;
+    const int64_t h8 = (((pos / 32) * 4 + pos % 4) * NBP + b) * 8 + (pos % 32) / 4;
     if (pos >= count) {
       reinterpret_cast<_Float16*>(a.out)[h8] = (_Float16)0.f;
       if (a.out_lo) reinterpret_cast<_Float16*>(a.out_lo)[h8] = (_Float16)0.f;
@@ -487,26 +489,29 @@ __global__ __launch_bounds__(kMmThreads) void k_mm_axpy(MmAxpyArgs a) {
 }
 
 // fp16 weights, fp16 activations (FC2 of the batched path): one
-// v_mfma_f32_16x16x32_f16 sums 32 listed rows: A = a (batch row lane % 16,
-// rows 8 g .. 8 g + 7, one 16-byte vector of the fp16 activation layout),
-// B = W (the same 8 rows at column lane % 16).  A W column is not contiguous, so
-// each row step (32 rows x the wave's 128 columns) is read as eight 4-row x
-// 256-byte loads into the wave's LDS tile and the B operands are gathered from
-// it 2 bytes at a time.  The tile's 16-byte chunks are stored at chunk
-// c ^ 2 ((row / 8) & 3): the four lane groups, reading rows 8 g + i, then fall
-// in different banks.  The block's WV waves take interleaved row steps and
+// v_mfma_f32_16x16x32_f16 sums 32 listed rows.  Lane (g = lane / 16, n = lane % 16)
+// of a row step loads rows js + 4 i + g (i = 0 .. 7), each row's 16-byte vector n of
+// the block's 128 columns: 8 rows x 8 columns in its own registers.  Those rows are
+// its k slots 8 g .. 8 g + 7, so instruction s2 takes half s2 of each row vector as
+// B (column 8 n + s2; a transpose in registers, no LDS), and A = a for batch row
+// lane % 16 at the same 8 rows, one 16-byte vector of the fp16 activation layout
+// (which stores positions q, q + 4, .., q + 28 of each 32-block in vector q).  The
+// block's WV waves take interleaved row steps and
 // are summed in LDS in wave order.  With LO, a = hi + lo in two fp16 parts
 // (about 22 bits): two exact products per weight, for the predictor's output
 // layer, whose logits keep near-fp32 precision.  That layer is one row chunk
 // over all H rows with one block per 128 columns (fewer blocks than compute
 // units at these sizes), so it takes eight waves per block: half the rounds of
 // dependent loads per wave.  FC2 keeps four, with several blocks per unit.
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 template <int NBT, bool LO, int WV>
 __global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
   constexpr int DS = 2;                     // row steps in flight per wave
   constexpr int kThreads = WV * kWave;
-  __shared__ uint4 wt[WV][32 * 16];
-  __shared__ float red[NBT * 8 * 4][kWave];
+  __shared__ float red[NBT * 8 * 4][kWave + 1];
   extern __shared__ int32_t ax_rows[];     // the chunk's row ids (rows_per_chunk entries)
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
@@ -539,8 +544,6 @@ __global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
   const rsrc_t rA = make_rsrc(a.a, abytes);
   const rsrc_t rL = make_rsrc(LO ? (const void*)a.a_lo : (const void*)a.a, LO ? abytes : 0u);
   constexpr uint32_t kOut = 0xFFFFFFF0u;
-  uint4* tw = wt[wave];
-  const _Float16* th = reinterpret_cast<const _Float16*>(wt[wave]);
   float4v_t acc[NBT][8];
 #pragma unroll
   for (int t = 0; t < NBT; ++t)
@@ -560,8 +563,8 @@ __global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < NBT; ++t) {
-        const int64_t jv = js + 8 * g;      // the lane's 8 rows (positions), a multiple of 8
-        const uint32_t ao = jv < r1 ? (uint32_t)(((jv / 8) * NBP + 16 * t + nl) * 16) : kOut;
+        // the lane's k slots are rows js + 4 i + g: vector g of the 32-position block at js
+        const uint32_t ao = js < r1 ? (uint32_t)((((js / 32) * 4 + g) * NBP + 16 * t + nl) * 16) : kOut;
         av[st][t] = bload16(rA, ao);
         if constexpr (LO) al[st][t] = bload16(rL, ao);
       }
@@ -571,21 +574,21 @@ __global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
     for (int st = 0; st < DS; ++st) {
       if (j0 + (int64_t)kBlockStep * st < r1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int lr = 4 * i + g;
-          tw[lr * 16 + (nl ^ (2 * ((lr >> 3) & 3)))] = wv[st][i];
-        }
-#pragma unroll
         for (int s2 = 0; s2 < 8; ++s2) {
-          // column 16 s2 + nl of rows 8 g .. 8 g + 7: chunk 2 s2 + nl / 8, swizzled by 2 g
-          const int pc = (2 * s2 + nl / 8) ^ (2 * g);
-          half8_t wb;
+          // the lane's 8 rows (k slots 8 g .. 8 g + 7) hold its columns 8 nl .. 8 nl + 7:
+          // instruction s2 takes column 8 nl + s2, half s2 of each row vector (a transpose in
+          // registers; output column n = nl of instruction s2 is column 8 nl + s2)
+          uint32_t wb[4];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) wb[i] = th[((8 * g + i) * 16 + pc) * 8 + nl % 8];
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = word_of(wv[st][2 * p], s2 / 2), hi = word_of(wv[st][2 * p + 1], s2 / 2);
+            wb[p] = (s2 & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+          }
+          const half8_t wh = __builtin_bit_cast(half8_t, uint4{wb[0], wb[1], wb[2], wb[3]});
 #pragma unroll
           for (int t = 0; t < NBT; ++t) {
-            acc[t][s2] = mfma16(__builtin_bit_cast(half8_t, av[st][t]), wb, acc[t][s2]);
-            if constexpr (LO) acc[t][s2] = mfma16(__builtin_bit_cast(half8_t, al[st][t]), wb, acc[t][s2]);
+            acc[t][s2] = mfma16(__builtin_bit_cast(half8_t, av[st][t]), wh, acc[t][s2]);
+            if constexpr (LO) acc[t][s2] = mfma16(__builtin_bit_cast(half8_t, al[st][t]), wh, acc[t][s2]);
           }
         }
       }
@@ -612,7 +615,7 @@ __global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
     // waves takes column c0 + cc over every batch row, so each wave's ballot is
     // the union word of one 64-column group.
     if (threadIdx.x < 128) {
-      const int cc = threadIdx.x, s2 = cc / 16, n = cc % 16;
+      const int cc = threadIdx.x, s2 = cc % 8, n = cc / 8;   // column 8 n + s2 of the tile
       const int64_t c = (int64_t)cchunk * 128 + cc;
       const bool cin = c < cols;
       const float cb = (a.bias && cin) ? load_bias(a.bias, a.bias_dt, c) : 0.f;
@@ -633,12 +636,13 @@ __global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
     }
     return;
   }
+  // thread q: column 8 n + s2 of the tile (consecutive threads, consecutive columns), batch row
+  // 16 t + 4 g + r
   for (int q = threadIdx.x; q < NBT * 8 * 4 * kWave; q += kThreads) {
-    const int ln = q % kWave, idx = q / kWave;
-    const int r = idx % 4, ts = idx / 4, s2 = ts % 8, t = ts / 8;
-    const int b = 16 * t + 4 * (ln / 16) + r;
-    const int64_t c = (int64_t)cchunk * 128 + 16 * s2 + ln % 16;
-    if (b < a.B && c < cols) a.partials[((int64_t)rchunk * a.B + b) * cols + c] = red[idx][ln];
+    const int s2 = q % 8, n = (q / 8) % 16, r = (q / 128) % 4, g2 = (q / 512) % 4, t = q / 2048;
+    const int b = 16 * t + 4 * g2 + r;
+    const int64_t c = (int64_t)cchunk * 128 + 8 * n + s2;
+    if (b < a.B && c < cols) a.partials[((int64_t)rchunk * a.B + b) * cols + c] = red[(t * 8 + s2) * 4 + r][16 * g2 + n];
   }
 }
 
