@@ -43,8 +43,8 @@ typedef float float4v_t __attribute__((ext_vector_type(4)));
 constexpr int kMmWaves = 4;
 constexpr int kMmThreads = kMmWaves * kWave;
 constexpr int kOutWaves = 8;   // the predictor output layer's one-row-chunk axpy (k_mm_axpy16)
-// its row ids take 4 bytes each of dynamic LDS beside the eight waves' 80 KB (at 32 batch rows):
-// past this many hidden units the four-wave block (48 KB) takes the layer
+// its row ids take 4 bytes each of dynamic LDS beside the waves' sums; it is measured up to this
+// many hidden units (more than any predictor here), and past them the four-wave block takes the layer
 constexpr int64_t kOutWavesMaxRows = 16384;
 
 __device__ __forceinline__ float4v_t mfma4(float a, float b, float4v_t c) {
