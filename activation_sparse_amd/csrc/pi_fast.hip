@@ -203,15 +203,15 @@ __global__ __launch_bounds__(kHidLdsWaves * kWave) void k_hidden_lds(const void*
   float acc = 0.f;
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
+    // past the row's end the weights read zeros, and x is read at index 0 (a written, finite
+    // slot): fma(0, x, acc) leaves acc as it is, so x needs no select
     const int v = u * kWave + lane;
-    const bool vin = v < nvec;
-    const int vc = vin ? v : 0;
+    const int vc = v < nvec ? v : 0;
     float xv[E];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const float4v t4 = xs[p * npad + vc];
-      xv[4 * p] = vin ? t4.x : 0.f; xv[4 * p + 1] = vin ? t4.y : 0.f;
-      xv[4 * p + 2] = vin ? t4.z : 0.f; xv[4 * p + 3] = vin ? t4.w : 0.f;
+      xv[4 * p] = t4.x; xv[4 * p + 1] = t4.y; xv[4 * p + 2] = t4.z; xv[4 * p + 3] = t4.w;
     }
     float wf[E];
     widen<DT>(rw.w[u], DT == 2 ? rw.sc[u] : 1.f, wf);
@@ -413,14 +413,12 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
           const int v = u * kWave + lane;
-          const bool vin = v < nvec;
-          const int vc = vin ? v : 0;
+          const int vc = v < nvec ? v : 0;   // past the row's end: zero weights, x[0] (no select)
           float xv[E];
 #pragma unroll
           for (int p = 0; p < P; ++p) {
             const float4v t4 = xs[p * npad + vc];
-            xv[4 * p] = vin ? t4.x : 0.f; xv[4 * p + 1] = vin ? t4.y : 0.f;
-            xv[4 * p + 2] = vin ? t4.z : 0.f; xv[4 * p + 3] = vin ? t4.w : 0.f;
+            xv[4 * p] = t4.x; xv[4 * p + 1] = t4.y; xv[4 * p + 2] = t4.z; xv[4 * p + 3] = t4.w;
           }
           float wf[E];
           widen<DT>(rw.w[u], DT == 2 ? rw.sc[u] : 1.f, wf);
@@ -579,11 +577,10 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
         // in the same order, so the bits are widen's
         auto xword = [&](int u, int i, float (&xo)[8]) {
           const int v = u * kWave + lane;
-          const bool vin = v < nvec;
-          const int vc = vin ? v : 0;
+          const int vc = v < nvec ? v : 0;   // past the row's end: zero weights, x[0] (no select)
           const float4v t0 = xs[(2 * i) * npad + vc], t1 = xs[(2 * i + 1) * npad + vc];
-          xo[0] = vin ? t0.x : 0.f; xo[1] = vin ? t0.y : 0.f; xo[2] = vin ? t0.z : 0.f; xo[3] = vin ? t0.w : 0.f;
-          xo[4] = vin ? t1.x : 0.f; xo[5] = vin ? t1.y : 0.f; xo[6] = vin ? t1.z : 0.f; xo[7] = vin ? t1.w : 0.f;
+          xo[0] = t0.x; xo[1] = t0.y; xo[2] = t0.z; xo[3] = t0.w;
+          xo[4] = t1.x; xo[5] = t1.y; xo[6] = t1.z; xo[7] = t1.w;
         };
         auto word = [](const uint4& w, int i) { return i == 0 ? w.x : i == 1 ? w.y : i == 2 ? w.z : w.w; };
         float xa[8], xb[8];
@@ -616,14 +613,12 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
         const int v = u * kWave + lane;
-        const bool vin = v < nvec;
-        const int vc = vin ? v : 0;
+        const int vc = v < nvec ? v : 0;     // past the row's end: zero weights, x[0] (no select)
         float xv[E];
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           const float4v t4 = xs[p * npad + vc];
-          xv[4 * p] = vin ? t4.x : 0.f; xv[4 * p + 1] = vin ? t4.y : 0.f;
-          xv[4 * p + 2] = vin ? t4.z : 0.f; xv[4 * p + 3] = vin ? t4.w : 0.f;
+          xv[4 * p] = t4.x; xv[4 * p + 1] = t4.y; xv[4 * p + 2] = t4.z; xv[4 * p + 3] = t4.w;
         }
         float wf[E];
         widen<DT>(rw.w[u], DT == 2 ? rw.sc[u] : 1.f, wf);
