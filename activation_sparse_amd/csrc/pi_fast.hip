@@ -323,7 +323,6 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   constexpr int P = E / 4;             // x planes
   constexpr int XQ = (NV * kWave * P + NT - 1) / NT;   // x float4 per thread
   extern __shared__ __attribute__((aligned(16))) char pf_smem[];
-  __shared__ int s_cnt[W];
   __shared__ float red[W][T];
   __shared__ uint64_t s_M[NG];
   __shared__ float s_a[T];
@@ -448,7 +447,6 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     float acc[EP];
 #pragma unroll
     for (int e = 0; e < EP; ++e) acc[e] = 0.f;
-    int nact = 0;                                  // this lane's rows with h > 0 (counted where cl == 0)
     for (int m0 = 0; m0 < H; m0 += RP) {
       if (m0 > 0) {
 #pragma unroll
@@ -462,14 +460,14 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
       for (int i = 0; i < U; ++i) {
         const int m = m0 + (i * W + wave) * RPL + sub;
         const bool ok = hv[i] > 0.f;               // rows past H read h = 0
-        nact += ok ? 1 : 0;
         w[i] = bload16(rP, ok ? (uint32_t)m * (uint32_t)prb + (uint32_t)colv * 16u : pbytes);
         if constexpr (PDT == 2) sc[i] = h2f(bload2(rS, ok ? (uint32_t)(m * pgroups + colv / 4) * 2u : 0xFFFFFFF0u));
         else sc[i] = 1.f;
       }
 #pragma unroll
       for (int i = 0; i < U; ++i) {
-        const float hs = hv[i] > 0.f ? hv[i] : 0.f;
+        // h is a ReLU output (>= +0), and a row not read has zero weights: h needs no select
+        const float hs = hv[i];
         if constexpr (PDT == 2) {
           // int4: the group scale folds into h once per row, and each weight is one
           // signed bit-field extract, one convert and one fma
@@ -510,19 +508,15 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     }
 #pragma unroll
     for (int i = 0; i < EP / RPL; ++i) red[wave][cl * EP + base + i] = acc[i];
-    if (a.rows_read && tile == 0) {
-      int c = cl == 0 ? nact : 0;
+  }
+  if (a.rows_read && tile == 0 && wave == 0) {   // the P2 rows read: hidden units with h > 0
+    int c = 0;
+    for (int m = lane; m < H; m += kWave) c += a.h[m] > 0.f ? 1 : 0;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
-      if (lane == 0) s_cnt[wave] = c;
-    }
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, kWave);
+    if (lane == 0) *a.rows_read = c;
   }
   __syncthreads();
-  if (a.rows_read && tile == 0 && tid == 0) {
-    int c = 0;
-    for (int w2 = 0; w2 < W; ++w2) c += s_cnt[w2];
-    *a.rows_read = c;
-  }
   if (tid < T) {                      // waves 0 .. NG-1, one per 64-id group
     float z = red[0][tid];
 #pragma unroll
