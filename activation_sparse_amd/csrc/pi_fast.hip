@@ -680,11 +680,13 @@ int pick_nv(int nvec) {
 
 // Vectors per lane of the fused kernel's FC1 rows, whose x is in LDS (not registers): the row's
 // loads alone bound it, 16 vectors for fp32 / fp16 rows and 8 for int4 rows (32 weights each).
-// The steps of 10 and 12 keep a gated layer's two rows (W1 and Wup, both in flight) to the
-// registers they need: at d = 5,120 fp16, 121 VGPRs (four waves per SIMD) against 187 (two).
+// The steps of 10, 12 and 14 keep a gated layer's two rows (W1 and Wup, both in flight) to the
+// registers they need (at d = 5,120 fp16, 121 VGPRs, four waves per SIMD, against 187, two), and
+// every row's dot to the vectors it has (14 at d = 7,168 fp16: a vector past the row's end still
+// costs its LDS reads and fmas).
 template <int DT>
 int pick_nv_fused(int nvec) {
-  for (int nv : {4, 8, 10, 12, 16}) {
+  for (int nv : {4, 8, 10, 12, 14, 16}) {
     if (DT == 2 && nv > 8) break;
     if (nv * kWave >= nvec) return nv;
   }
@@ -704,13 +706,16 @@ int grid_for(int64_t waves, int cap) {
   return (int)(b < 1 ? 1 : (b > cap ? cap : b));
 }
 
-// Vectors per lane of k_hidden_lds for a row of nvec 16-byte vectors (0 = unsupported): 8, 16, 24
-// or 32 (int4: 4, 8 or 16, whose x takes a quarter of the registers per vector; a 3.5 KB int4 row
-// at d = 7,168 fills 3.5 vectors per lane, and at 8 the unused half still cost registers and work).
+// Vectors per lane of k_hidden_lds for a row of nvec 16-byte vectors (0 = unsupported): 8, 10, 12,
+// 14, 16, 24 or 32 (int4: 4, 8 or 16, whose x takes a quarter of the registers per vector).  A
+// vector past the row's end still costs registers and its share of the dot, so the steps follow
+// the common widths: 10 at d = 5,120 and 14 at d = 7,168 fp16, 4 for the 3.5 KB int4 rows at
+// d = 7,168 (123 VGPRs at 8, 64 of them for x on its way to LDS).
 template <int DT>
 int pick_nv_lds(int nvec) {
-  for (int nv : {4, 8, 16, 24, 32}) {
+  for (int nv : {4, 8, 10, 12, 14, 16, 24, 32}) {
     if (DT != 2 && nv < 8) continue;
+    if (DT == 2 && nv > 8 && nv < 16) continue;
     if (DT == 2 && nv > 16) break;
     if (nv * kWave >= nvec) return nv;
   }
@@ -740,6 +745,9 @@ hipError_t hidden_lds_dt(const B1Gemv& g, hipStream_t s) {
   switch (pick_nv_lds<DT>(nvec)) {
     case 4: if constexpr (DT == 2) PI_HL(4); break;
     case 8: PI_HL(8); break;
+    case 10: if constexpr (DT != 2) PI_HL(10); break;
+    case 12: if constexpr (DT != 2) PI_HL(12); break;
+    case 14: if constexpr (DT != 2) PI_HL(14); break;
     case 16: PI_HL(16); break;
     case 24: if constexpr (DT != 2) PI_HL(24); break;
     case 32: if constexpr (DT != 2) PI_HL(32); break;
@@ -812,6 +820,7 @@ hipError_t pred_fc1_combo(const PredFc1Args& a, hipStream_t s) {
     case 8: PI_PF(8);
     case 10: if constexpr (Fmt<DT>::E <= 8) PI_PF(10);
     case 12: if constexpr (Fmt<DT>::E <= 8) PI_PF(12);
+    case 14: if constexpr (Fmt<DT>::E <= 8) PI_PF(14);
     case 16: if constexpr (Fmt<DT>::E <= 8) PI_PF(16);
     default: return hipErrorInvalidValue;
   }

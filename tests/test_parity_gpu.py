@@ -100,13 +100,16 @@ def test_wide_row_hidden_layer_parity(cfg, fused):
     _run(cfg, layer=0, step=1, B=1, fused=fused)
 
 
-# rows of the fused kernel's FC1 at 10 and 12 vectors per lane (fp16 rows of 640 and 704 / 768
-# vectors, fp32 rows of 640), gated and not
+# rows of the fused kernel's FC1 and of the hidden-layer kernel at 10, 12 and 14 vectors per lane
+# (fp16 rows of 640, 704 / 768 and 832 vectors, fp32 rows of 640, 768 and 896), gated and not
 FC1_WIDTHS = [
     ph.small_case("nv10-f16-gated", d=5120, N=1024, H=40, wdtype=synth.F16, gated=True, rho=0.15, seed=31),
     ph.small_case("nv12-f16", d=5632, N=1088, H=48, wdtype=synth.F16, seed=32),
     ph.small_case("nv12-f16-gated", d=6144, N=960, H=36, wdtype=synth.F16, gated=True, seed=33),
+    ph.small_case("nv14-f16", d=6656, N=1024, H=44, wdtype=synth.F16, seed=35),
     ph.small_case("nv10-f32", d=2560, N=1024, H=40, wdtype=synth.F32, seed=34),
+    ph.small_case("nv12-f32", d=3072, N=1024, H=40, wdtype=synth.F32, seed=36),
+    ph.small_case("nv14-f32", d=3584, N=1024, H=40, wdtype=synth.F32, seed=37),
 ]
 
 
