@@ -1010,9 +1010,13 @@ __global__ __launch_bounds__(kWave) void k_reduce_y(ReduceYArgs r) {
   const int kc = r.K_c ? *r.K_c : 1;
   const float yc = r.y_c ? r.y_c[t] : 0.f;
   const float bb = r.b2 ? load_bias(r.b2, r.b2_dt, t) : 0.f;
+  // the partials through one buffer: the column's byte offset per lane and each chunk's as a
+  // scalar, so the 32 loads go out with no address arithmetic between them
+  const rsrc_t rp = make_rsrc(r.partials, (uint32_t)(kSegChunks * r.d * 4));
   float p[kSegChunks];
 #pragma unroll
-  for (int c = 0; c < kSegChunks; ++c) p[c] = r.partials[(int64_t)c * r.d + t];
+  for (int c = 0; c < kSegChunks; ++c)
+    p[c] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, (int)(t * 4), (int)(c * r.d * 4), 0));
   float sum = 0.f;
 #pragma unroll
   for (int c = 0; c < kSegChunks; ++c) sum += p[c];
