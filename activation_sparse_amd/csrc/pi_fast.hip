@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kHidLdsWaves * kWave) void k_hidden_lds(const void*
   const bool row_ok = j < rows;
   const int64_t rb = row_bytes(DT, cols);
   const int nvec = (int)(rb / 16);
-  const int npad = (nvec + kWave - 1) & ~(kWave - 1);
+  const int npad = NV * kWave;                             // plane stride: every u < NV in bounds
   const int nq = cols / 4;
   const float4v* x4 = reinterpret_cast<const float4v*>(x);
   float4v xq[XQ];
@@ -198,19 +198,22 @@ __global__ __launch_bounds__(kHidLdsWaves * kWave) void k_hidden_lds(const void*
     const int q = r * NT + tid;
     if (q < nq) xs[(q % P) * npad + q / P] = xq[r];
   }
+  // the planes past the row's end hold zeros, so the dot reads them unconditionally
+  for (int q = nvec + tid; q < npad; q += NT) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) xs[p * npad + q] = float4v{0.f, 0.f, 0.f, 0.f};
+  }
   __syncthreads();
   if (!row_ok) return;
   float acc = 0.f;
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
-    // past the row's end the weights read zeros, and x is read at index 0 (a written, finite
-    // slot): fma(0, x, acc) leaves acc as it is, so x needs no select
+    // past the row's end the weights and x both read zeros: no index clamp, no select
     const int v = u * kWave + lane;
-    const int vc = v < nvec ? v : 0;
     float xv[E];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const float4v t4 = xs[p * npad + vc];
+      const float4v t4 = xs[p * npad + v];
       xv[4 * p] = t4.x; xv[4 * p + 1] = t4.y; xv[4 * p + 2] = t4.z; xv[4 * p + 3] = t4.w;
     }
     float wf[E];
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   const Bias<BDT> c2_at(a.c2, (uint32_t)N);
   const float c2v = c2_at(tid < T && id < N ? id : 0);
   const int nvec = FC1 ? (int)(row_bytes(DT, a.d) / 16) : 0;
-  const int npad = (nvec + kWave - 1) & ~(kWave - 1);
+  const int npad = FC1 ? NV * kWave : 0;                  // plane stride: every u < NV in bounds
   float4v xq[FC1 ? XQ : 1];
   // x given raw with the statistics the hidden-layer kernel left: normalised on the way into LDS
   // with the same two values and the same fma, so FC1 sees the hidden layer's x bit for bit
@@ -392,6 +395,11 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
         xs[(q % P) * npad + q / P] = v;
       }
     }
+    // the planes past the row's end hold zeros, so the row dots read them unconditionally
+    for (int q = nvec + tid; q < npad; q += NT) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) xs[p * npad + q] = float4v{0.f, 0.f, 0.f, 0.f};
+    }
   }
 
   if constexpr (FC1) {
@@ -411,12 +419,11 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
         float a0 = 0.f;
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-          const int v = u * kWave + lane;
-          const int vc = v < nvec ? v : 0;   // past the row's end: zero weights, x[0] (no select)
+          const int v = u * kWave + lane;    // past the row's end: zero weights and zero x
           float xv[E];
 #pragma unroll
           for (int p = 0; p < P; ++p) {
-            const float4v t4 = xs[p * npad + vc];
+            const float4v t4 = xs[p * npad + v];
             xv[4 * p] = t4.x; xv[4 * p + 1] = t4.y; xv[4 * p + 2] = t4.z; xv[4 * p + 3] = t4.w;
           }
           float wf[E];
@@ -570,9 +577,8 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
         // from LDS before this word is decoded; each weight is (float)q * scale as widen gives it,
         // in the same order, so the bits are widen's
         auto xword = [&](int u, int i, float (&xo)[8]) {
-          const int v = u * kWave + lane;
-          const int vc = v < nvec ? v : 0;   // past the row's end: zero weights, x[0] (no select)
-          const float4v t0 = xs[(2 * i) * npad + vc], t1 = xs[(2 * i + 1) * npad + vc];
+          const int v = u * kWave + lane;    // past the row's end: zero weights and zero x
+          const float4v t0 = xs[(2 * i) * npad + v], t1 = xs[(2 * i + 1) * npad + v];
           xo[0] = t0.x; xo[1] = t0.y; xo[2] = t0.z; xo[3] = t0.w;
           xo[4] = t1.x; xo[5] = t1.y; xo[6] = t1.z; xo[7] = t1.w;
         };
@@ -606,12 +612,11 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
       } else {
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
-        const int v = u * kWave + lane;
-        const int vc = v < nvec ? v : 0;     // past the row's end: zero weights, x[0] (no select)
+        const int v = u * kWave + lane;      // past the row's end: zero weights and zero x
         float xv[E];
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          const float4v t4 = xs[p * npad + vc];
+          const float4v t4 = xs[p * npad + v];
           xv[4 * p] = t4.x; xv[4 * p + 1] = t4.y; xv[4 * p + 2] = t4.z; xv[4 * p + 3] = t4.w;
         }
         float wf[E];
@@ -725,8 +730,7 @@ int pick_nv_lds(int nvec) {
 template <int DT>
 hipError_t hidden_lds_dt(const B1Gemv& g, hipStream_t s) {
   const int nvec = (int)(row_bytes(DT, g.cols) / 16);
-  const int npad = (nvec + kWave - 1) & ~(kWave - 1);
-  const size_t shm = (size_t)npad * (Fmt<DT>::E / 4) * 16;
+  const size_t shm = (size_t)pick_nv_lds<DT>(nvec) * kWave * (Fmt<DT>::E / 4) * 16;   // planes of NV * 64
   const dim3 gr((unsigned)((g.rows + kHidLdsWaves - 1) / kHidLdsWaves)), bl(kHidLdsWaves * kWave);
 #define PI_HL_LN(NVV, BB)                                                                                   \
   do {                                                                                                      \
@@ -793,11 +797,7 @@ hipError_t pf_launch(const PredFc1Args& a, hipStream_t s) {
   unsigned blocks = (unsigned)((a.N + T - 1) / T);
   if (FC1 && a.nh) blocks += (unsigned)((a.nH + 7) / 8);   // look-ahead rows, T / 8 = 8 waves per block
   size_t shm = 0;                     // x in E/4 planes of float4 when FC1 runs
-  if constexpr (FC1) {
-    const int nvec = (int)(row_bytes(DT, a.d) / 16);
-    const int npad = (nvec + kWave - 1) & ~(kWave - 1);
-    shm += (size_t)(Fmt<DT>::E / 4) * npad * 16;
-  }
+  if constexpr (FC1) shm += (size_t)(Fmt<DT>::E / 4) * NV * kWave * 16;   // planes of NV * 64 vectors
   hipLaunchKernelGGL((k_pred_fc1<PDT, DT, NV, GATED, BDT, T, FC1>), dim3(blocks), dim3(T * 8), shm, s, a);
   return hipGetLastError();
 }
