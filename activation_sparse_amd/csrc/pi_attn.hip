@@ -171,6 +171,9 @@ __global__ __launch_bounds__(kQW * kWave) void k_attn_q(AttnArgs a) {
     const int q = k * kQW * kWave + threadIdx.x;
     if (q < nq) xs[q] = xv[k];
   }
+  // zeros past the row's end, up to the NV * 64 vectors the dot reads (no index clamp, no select:
+  // the weights there read zeros too)
+  for (int q = nq + (int)threadIdx.x; q < 2 * NV * kWave; q += kQW * kWave) xs[q] = float4v{0.f, 0.f, 0.f, 0.f};
   __syncthreads();
   // x is read from LDS one vector ahead of the dot (8 elements: float4 2v and 2v + 1), and each
   // vector's step closes with a scheduling barrier, so the reads are not all hoisted into registers
@@ -178,12 +181,8 @@ __global__ __launch_bounds__(kQW * kWave) void k_attn_q(AttnArgs a) {
   float4v xa0, xa1, xb0, xb1;
   auto xread = [&](int u, float4v& x0, float4v& x1) {
     const int v = u * kWave + lane;
-    const bool vin = v < nvec;
-    const int vc = vin ? v : 0;                               // read unconditionally, then select
-    const float4v t0 = xs[2 * vc], t1 = xs[2 * vc + 1];
-    const float4v z{0.f, 0.f, 0.f, 0.f};
-    x0 = vin ? t0 : z;
-    x1 = vin ? t1 : z;
+    x0 = xs[2 * v];
+    x1 = xs[2 * v + 1];
   };
   xread(0, xa0, xa1);
 #pragma unroll
@@ -464,7 +463,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   {
     const dim3 gq((unsigned)(a.d / kQRows)), tq(kQW * kWave);
-    const size_t shq = (size_t)a.d * 4;
+    const size_t shq = (size_t)pick_nv_q(a.d) * kWave * 32;   // x as 2 float4 per vector, NV * 64 vectors
     switch (pick_nv_q(a.d)) {
       case 1: hipLaunchKernelGGL(k_attn_q<1>, gq, tq, shq, s, a); break;
       case 2: hipLaunchKernelGGL(k_attn_q<2>, gq, tq, shq, s, a); break;
