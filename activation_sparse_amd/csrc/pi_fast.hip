@@ -1,19 +1,22 @@
 // pi_fast.hip - batch-1 kernels.
 //
-// Row dots with the input held in registers (the predictor's hidden layer and
-// the list-driven FC1 of pi_sparse_ffn): every lane owns the same column
-// slice of every row (vectors v = u*64 + lane), so its slice of x is loaded
-// once and reused; all 16-byte loads of a row are issued before the first FMA.
-// The batch-1 hidden layer takes the same dot with x staged once per
-// workgroup in LDS (the register-held x serves the call that normalises x).
+// Row dots: every lane owns the same column slice of every row (vectors
+// v = u*64 + lane), and all 16-byte loads of a row are issued before the first
+// FMA.  The list-driven FC1 of pi_sparse_ffn holds its slice of x in
+// registers; the batch-1 hidden layer stages x once per four-wave workgroup in
+// LDS planes that hold zeros past the row's end (so the dot reads them with no
+// clamp or select), and normalises it on the way in for the chaining call.
 //
 // The predictor's output layer with its weights stored hidden-major (row m =
 // hidden unit m's weights to the N outputs): only the rows of hidden units
 // whose ReLU output is positive are read, since a zero hidden unit adds
 // nothing to any logit.  One block owns a tile of 64 or 128 neuron ids: each
 // lane reads h for its rows and then only the row slices of positive hidden
-// units (the others are skipped through the buffer range check), and the block
-// decides the tile's activations.  In the fused layer the same block then
+// units (the others are skipped through the buffer range check), a
+// reduce-scatter across the wave's row groups and a sum over the waves give
+// the tile's logits, and the block decides the tile's activations.  With int4
+// rows a tile's slice is a quarter of a cache line, so neighbouring tiles run
+// on one die.  In the fused layer the same block then
 // runs FC1 for the tile's active GPU-resident neurons (x staged in LDS) and
 // writes the tile's list segments, so no block waits for another.
 //

@@ -227,14 +227,23 @@ DOMINANT = "k_pred_fc1"
 TRAFFIC_PROFILE = "profiles/k_pred_fc1.opt-30b.b1.hbm_traffic.txt"
 
 
+def code_text(src):
+    """C++ source without its comments and blank lines, trailing spaces removed: the text a change of
+    code changes and a change of comments does not (none of these sources has // or /* in a string)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(l.rstrip() for l in src.split("\n") if l.strip())
+
+
 def kernel_source_digest():
-    """sha256 over the sources the batch-1 kernels are built from (a counter reading taken on other
-    sources no longer describes the kernel)."""
+    """sha256 over the code of the sources the batch-1 kernels are built from, comments left out (a
+    counter reading taken on other code no longer describes the kernel)."""
     import hashlib
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()
 
 
