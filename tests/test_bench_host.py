@@ -121,3 +121,18 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_traffic_digest_follows_code_not_comments():
+    """The counter digest: a comment edit leaves it, a code edit changes it, and the committed
+    traffic figure is the committed summary's while the code is that of the passes."""
+    src = "// header\nint f(int a) {  /* two\n lines */\n  return a + 1;   // note\n}\n"
+    same = "// another header\n\nint f(int a) {\n  return a + 1;\n}\n"
+    other = "int f(int a) {\n  return a + 2;\n}\n"
+    assert bench.code_text(src) == bench.code_text(same)
+    assert bench.code_text(src) != bench.code_text(other)
+    assert "return a + 1;" in bench.code_text(src) and "note" not in bench.code_text(src)
+    with open(os.path.join(ROOT, bench.TRAFFIC_PROFILE)) as fh:
+        recorded = [l.split(":", 1)[1].strip() for l in fh if l.startswith("kernel sources sha256: ")][-1]
+    if recorded == bench.kernel_source_digest():
+        assert bench.committed_traffic(bench.DOMINANT) is not None
