@@ -119,6 +119,21 @@ def test_fused_fc1_row_widths(cfg):
     _run(cfg, layer=0, step=1, B=1, fused=True)
 
 
+# int4 P2 tiles are placed die by die for the first (tiles / 8) * 8 of them and in order after: 42
+# tiles leave 2 in that tail, 6 tiles (fewer than the dies) keep their order
+I4_TILE_ORDER = [
+    ph.small_case("i4p-42-tiles", d=512, N=2688, H=96, wdtype=synth.F16, pdtype=synth.I4G128, seed=38),
+    ph.small_case("i4p-6-tiles", d=512, N=384, H=64, wdtype=synth.F16, pdtype=synth.I4G128, seed=39),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("cfg", I4_TILE_ORDER, ids=[c.key for c in I4_TILE_ORDER])
+def test_int4_predictor_tile_order(cfg, fused):
+    _dev()
+    _run(cfg, layer=0, step=1, B=1, fused=fused)
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("B", [16, 32])
 def test_large_batch_union(B, fused):
