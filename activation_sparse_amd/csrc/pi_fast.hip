@@ -330,7 +330,6 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   constexpr int XQ = (NV * kWave * P + NT - 1) / NT;   // x float4 per thread
   extern __shared__ __attribute__((aligned(16))) char pf_smem[];
   __shared__ float red[W][T];
-  __shared__ uint64_t s_M[NG];
   __shared__ float s_a[T];
   __shared__ int s_slot[T];
 
@@ -353,9 +352,15 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     Gb[g] = in ? ((uint64_t)a.gbits[2 * grp] | ((uint64_t)a.gbits[2 * grp + 1] << 32)) : 0ull;
     gp[g] = in ? a.gpre[grp] : 0;
   }
-  const int64_t id = i0 + tid;
+  // every wave takes the tile's activation decision itself (the same sums in the same order, so
+  // the same bits in every wave): c2 of the lane's id in each 64-id group
   const Bias<BDT> c2_at(a.c2, (uint32_t)N);
-  const float c2v = c2_at(tid < T && id < N ? id : 0);
+  float c2v[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int64_t idg = i0 + g * kWave + lane;
+    c2v[g] = c2_at(idg < N ? idg : 0);
+  }
   const int nvec = FC1 ? (int)(row_bytes(DT, a.d) / 16) : 0;
   const int npad = FC1 ? NV * kWave : 0;                  // plane stride: every u < NV in bounds
   float4v xq[FC1 ? XQ : 1];
@@ -527,23 +532,27 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
     if (lane == 0) *a.rows_read = c;
   }
   __syncthreads();
-  if (tid < T) {                      // waves 0 .. NG-1, one per 64-id group
-    float z = red[0][tid];
+  uint64_t Mb[NG];
 #pragma unroll
-    for (int w2 = 1; w2 < W; ++w2) z += red[w2][tid];
-    z += c2v;
-    const bool valid = id < N;
-    if (a.logits && valid) a.logits[id] = z;
-    const uint64_t bits = __ballot(valid && z > a.tau);
-    if (lane == 0) s_M[wave] = bits;
-    const int grp = tile * NG + wave;
-    if (!FC1 && a.mask && lane == 0 && grp < ngroups) {
-      a.mask[2 * grp] = (uint32_t)bits;
-      a.mask[2 * grp + 1] = (uint32_t)(bits >> 32);
+  for (int g = 0; g < NG; ++g) {
+    const int c = g * kWave + lane;
+    float z = red[0][c];
+#pragma unroll
+    for (int w2 = 1; w2 < W; ++w2) z += red[w2][c];
+    z += c2v[g];
+    const int64_t idg = i0 + c;
+    const bool valid = idg < N;
+    Mb[g] = __ballot(valid && z > a.tau);
+    if (wave == g) {                  // wave g reports group g
+      if (a.logits && valid) a.logits[idg] = z;
+      const int grp = tile * NG + g;
+      if (!FC1 && a.mask && lane == 0 && grp < ngroups) {
+        a.mask[2 * grp] = (uint32_t)Mb[g];
+        a.mask[2 * grp + 1] = (uint32_t)(Mb[g] >> 32);
+      }
     }
   }
   if constexpr (!FC1) return;
-  __syncthreads();
 
   // ---- FC1 of the tile's active GPU-resident neurons, row r by wave r % W
   uint64_t act[NG];
@@ -551,7 +560,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
   int R = 0;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    act[g] = s_M[g] & Gb[g];
+    act[g] = Mb[g] & Gb[g];
     kg[g] = __popcll(act[g]);
     R += kg[g];
   }
@@ -667,7 +676,7 @@ __global__ __launch_bounds__(T * 8) void k_pred_fc1(PredFc1Args a) {
         a.pos_slot[base + p] = s;
         a.pos_a[base + p] = av;
       }
-      const uint64_t ac = s_M[g] & ~Gb[g];
+      const uint64_t ac = Mb[g] & ~Gb[g];
       if ((ac >> lane) & 1ull)
         a.seg_cold[base + __popcll(ac & lt)] = (int32_t)(base + lane - (gp[g] + __popcll(Gb[g] & lt)));
       if (lane == 0) a.cnt[grp] = (uint32_t)k | ((uint32_t)__popcll(ac) << 8) | ((uint32_t)__popcll(bn) << 16);
