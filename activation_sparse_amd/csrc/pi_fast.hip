@@ -853,7 +853,7 @@ __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
   constexpr int E = DT == 2 ? 8 : Fmt<DT>::E;   // columns per lane (int4: one 32-bit word)
   extern __shared__ int32_t fsm[];
   __shared__ float red[kWpb][kWave * E];
-  __shared__ int s_cnt[64], s_off[65];
+  __shared__ int s_cnt[64];
   __shared__ int s_red[5][kWpb];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -911,8 +911,12 @@ __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
   const int nb = b1 - b0;
   int32_t* c_slot = fsm;
   float* c_a = reinterpret_cast<float*>(fsm + nb * 64);
-  // each thread's share of the raw (slot, a) entries, loaded together with the counts
-  constexpr int RQ = 16;   // entries per thread: nb * 64 <= RQ * kT
+  // the group counts first, then each thread's share of the raw (slot, a) entries: wave w takes
+  // the entries of groups w, w + 4, ... (lane = entry in the group), so every group is one wave's.
+  // Each wave scans the counts itself (the same offsets in every wave), so the compaction needs
+  // one barrier, after the entries are placed.
+  constexpr int RQ = 16;   // groups per wave: nb <= RQ * kWpb
+  const int cv = lane < nb ? (int)cnt_nz(a.cnt[b0 + lane]) : 0;
   int32_t rs[RQ];
   float ra[RQ];
 #pragma unroll
@@ -921,33 +925,26 @@ __global__ __launch_bounds__(kT) void k_fc2_seg(Fc2SegArgs a, int tiles) {
     rs[q] = e < nb * 64 ? a.pos_slot[(int64_t)b0 * 64 + e] : -1;
     ra[q] = e < nb * 64 ? a.pos_a[(int64_t)b0 * 64 + e] : 0.f;
   }
-  if (tid < nb) s_cnt[tid] = (int)cnt_nz(a.cnt[b0 + tid]);
-  __syncthreads();
-  if (wave == 0) {
-    const int v = lane < nb ? s_cnt[lane] : 0;
-    int incl = v;
+  int incl = cv;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += t;
-    }
-    if (lane < nb) s_off[lane] = incl - v;
-    if (lane == kWave - 1) s_off[nb] = incl;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
   }
-  __syncthreads();
+  const int excl = incl - cv;
+  const int R = __builtin_amdgcn_readlane(incl, kWave - 1);
 #pragma unroll
   for (int q = 0; q < RQ; ++q) {
-    const int e = q * kT + tid;
-    if (e < nb * 64) {
-      const int bb = e / 64, i = e % 64;
-      if (i < s_cnt[bb]) {
-        c_slot[s_off[bb] + i] = rs[q];
-        c_a[s_off[bb] + i] = ra[q];
+    const int bb = q * kWpb + wave;          // this wave's group at step q (wave-uniform)
+    if (bb < nb) {
+      const int cb = __builtin_amdgcn_readlane(cv, bb), ob = __builtin_amdgcn_readlane(excl, bb);
+      if (lane < cb) {
+        c_slot[ob + lane] = rs[q];
+        c_a[ob + lane] = ra[q];
       }
     }
   }
   __syncthreads();
-  const int R = s_off[nb];
   const int64_t d = a.d;
   const int64_t rb = row_bytes(DT, d);
   // the lane's unit of each row: a 16-byte vector, or for int4 a 32-bit word (8 weights)
