@@ -316,25 +316,28 @@ __global__ __launch_bounds__(256) void k_mm_finish(MmRowArgs a) {
   }
 }
 
-// The same, written neuron-major: out[pos * NBP + b], zeros for b >= B.
-template <bool GATED>
+// The same, written neuron-major: out[pos * NBP + b], zeros for b >= B.  NBP is a compile-time 16
+// or 32, so the element's position and batch row are a shift and a mask; the indices fit 32 bits
+// (PI_MAX_NEURONS positions x 32 batch rows x the split-K chunks of both products, under 2^31).
+template <bool GATED, int NBT>
 __global__ __launch_bounds__(256) void k_mm_finish_tr(MmRowArgs a) {
-  const int NBP = 16 * a.nbt;
-  int64_t count = a.count_max;
+  constexpr int NBP = 16 * NBT;
+  int count = (int)a.count_max;
   if (a.list) {
     const int64_t kd = *a.count_dev;
-    count = kd < 0 ? 0 : (kd < a.count_max ? kd : a.count_max);
+    count = kd < 0 ? 0 : (kd < a.count_max ? (int)kd : (int)a.count_max);
   }
   // the fp16 layout is written up to the next multiple of 32 positions (zeros), so
   // that the axpy's 8-position vectors never hold stale values.  Within each block of 32
   // positions, vector q (of four) holds positions q, q + 4, ..., q + 28: the rows that lane
   // group q of the axpy loads, in the order of its k slots
-  const int64_t npos = a.out_h8 ? (count + 31) / 32 * 32 : count;
-  const int64_t n = npos * NBP;
-  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < n; t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t pos = t / NBP;
-    const int b = (int)(t % NBP);
-    const int64_t h8 = (((pos / 32) * 4 + pos % 4) * NBP + b) * 8 + (pos % 32) / 4;
+  const int npos = a.out_h8 ? (count + 31) / 32 * 32 : count;
+  const int n = npos * NBP;
+  const int cmax = (int)a.count_max;
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < n; t += gridDim.x * blockDim.x) {
+    const int pos = t / NBP;
+    const int b = t % NBP;
+    const int h8 = (((pos / 32) * 4 + pos % 4) * NBP + b) * 8 + (pos % 32) / 4;
     if (pos >= count) {
       reinterpret_cast<_Float16*>(a.out)[h8] = (_Float16)0.f;
       if (a.out_lo) reinterpret_cast<_Float16*>(a.out_lo)[h8] = (_Float16)0.f;
@@ -345,9 +348,9 @@ __global__ __launch_bounds__(256) void k_mm_finish_tr(MmRowArgs a) {
       float p[8], q[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = k0 + i < a.ks ? a.partials[((int64_t)(k0 + i) * a.count_max + pos) * NBP + b] : 0.f;
+        p[i] = k0 + i < a.ks ? a.partials[((k0 + i) * cmax + pos) * NBP + b] : 0.f;
         if constexpr (GATED)
-          q[i] = k0 + i < a.ks ? a.partials[((int64_t)(a.ks + k0 + i) * a.count_max + pos) * NBP + b] : 0.f;
+          q[i] = k0 + i < a.ks ? a.partials[((a.ks + k0 + i) * cmax + pos) * NBP + b] : 0.f;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -785,8 +788,13 @@ hipError_t launch_mm_rowdot(const MmRowArgs& a, hipStream_t s) {
   int64_t blocks = (n + 255) / 256;
   blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
   if (a.out_tr) {
-    if (a.gated) hipLaunchKernelGGL(k_mm_finish_tr<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_mm_finish_tr<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if (a.nbt == 1) {
+      if (a.gated) hipLaunchKernelGGL((k_mm_finish_tr<true, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_mm_finish_tr<false, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    } else {
+      if (a.gated) hipLaunchKernelGGL((k_mm_finish_tr<true, 2>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_mm_finish_tr<false, 2>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    }
   } else {
     if (a.gated) hipLaunchKernelGGL(k_mm_finish<true>, dim3((unsigned)blocks), dim3(256), 0, s, a);
     else hipLaunchKernelGGL(k_mm_finish<false>, dim3((unsigned)blocks), dim3(256), 0, s, a);
