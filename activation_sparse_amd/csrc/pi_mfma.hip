@@ -202,19 +202,33 @@ __global__ __launch_bounds__(r16_waves(NBT) * kWave) void k_mm_rowdot16(MmRowArg
   const int kn = (int)(k1 - k0);            // a multiple of 32
   const int xs = (int)a.kc + 8;             // LDS row stride (halves)
   {
-    const int q4 = kn / 4;
-    for (int idx = threadIdx.x; idx < NBP * q4; idx += NT) {
-      const int b = idx / q4, q = idx % q4;
-      float4v v = float4v{0.f, 0.f, 0.f, 0.f};
-      if (b < a.B) v = *reinterpret_cast<const float4v*>(a.x + (int64_t)b * a.cols + k0 + 4 * q);
-      half4_t h;
-      h[0] = (_Float16)v[0]; h[1] = (_Float16)v[1]; h[2] = (_Float16)v[2]; h[3] = (_Float16)v[3];
-      *reinterpret_cast<half4_t*>(xh + b * xs + 4 * q) = h;
-      if constexpr (HILO) {
-        half4_t l;
+    // eight of the thread's float4 of x in flight at a time (a loop of one load each waited for
+    // every load in turn)
+    const int q4 = kn / 4, tot = NBP * q4;
+    for (int base = threadIdx.x; base < tot; base += 8 * NT) {
+      float4v v[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) l[e] = (_Float16)(v[e] - (float)h[e]);
-        *reinterpret_cast<half4_t*>(xh + (NBP + b) * xs + 4 * q) = l;
+      for (int k = 0; k < 8; ++k) {
+        const int idx = base + k * NT;
+        const int b = idx / q4, q = idx - b * q4;
+        v[k] = float4v{0.f, 0.f, 0.f, 0.f};
+        if (idx < tot && b < a.B) v[k] = *reinterpret_cast<const float4v*>(a.x + (int64_t)b * a.cols + k0 + 4 * q);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int idx = base + k * NT;
+        if (idx < tot) {
+          const int b = idx / q4, q = idx - b * q4;
+          half4_t h;
+          h[0] = (_Float16)v[k][0]; h[1] = (_Float16)v[k][1]; h[2] = (_Float16)v[k][2]; h[3] = (_Float16)v[k][3];
+          *reinterpret_cast<half4_t*>(xh + b * xs + 4 * q) = h;
+          if constexpr (HILO) {
+            half4_t l;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) l[e] = (_Float16)(v[k][e] - (float)h[e]);
+            *reinterpret_cast<half4_t*>(xh + (NBP + b) * xs + 4 * q) = l;
+          }
+        }
       }
     }
   }
