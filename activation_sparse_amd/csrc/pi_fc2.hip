@@ -115,6 +115,9 @@ __global__ __launch_bounds__(kT) void k_reduce(ReduceArgs r) {
   const int64_t n = (int64_t)r.B * r.d;
   const bool add_c = r.y_c && (!r.K_c || *r.K_c != 0);
   for (int64_t t = blockIdx.x * (int64_t)kT + threadIdx.x; t < n; t += (int64_t)gridDim.x * kT) {
+    // the cold partial and the bias are loaded with the first chunks, not after the sum
+    const float yc = add_c ? r.y_c[t] : 0.f;
+    const float bb = r.b2 ? load_bias(r.b2, r.b2_dt, t % r.d) : 0.f;
     float sum = 0.f;
     for (int c0 = 0; c0 < r.chunks; c0 += 16) {
       float p[16];
@@ -123,8 +126,8 @@ __global__ __launch_bounds__(kT) void k_reduce(ReduceArgs r) {
 #pragma unroll
       for (int c = 0; c < 16; ++c) sum += p[c];
     }
-    if (add_c) sum += r.y_c[t];
-    if (r.b2) sum += load_bias(r.b2, r.b2_dt, t % r.d);
+    if (add_c) sum += yc;
+    if (r.b2) sum += bb;
     r.y[t] = sum;
   }
 }
