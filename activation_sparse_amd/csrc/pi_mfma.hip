@@ -551,6 +551,10 @@ __global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
     ax_rows[j - r0] = (row >= 0 && row < a.n_rows) ? (int32_t)row : -1;
   }
   __syncthreads();
+  // with the logits written here, thread cc < 128 adds the output bias of column 128 cchunk + cc:
+  // loaded now, so it is not a round trip after the sums
+  const float cb_early = (a.final_out && a.bias && threadIdx.x < 128 && (int64_t)cchunk * 128 + threadIdx.x < a.cols)
+                             ? load_bias(a.bias, a.bias_dt, (int64_t)cchunk * 128 + threadIdx.x) : 0.f;
   const int NBP = 16 * NBT;
   const int64_t rb = a.cols * 2;
   const int nvec = (int)(rb / 16);
@@ -635,7 +639,7 @@ __global__ __launch_bounds__(WV * kWave) void k_mm_axpy16(MmAxpyArgs a) {
       const int cc = threadIdx.x, s2 = cc % 8, n = cc / 8;   // column 8 n + s2 of the tile
       const int64_t c = (int64_t)cchunk * 128 + cc;
       const bool cin = c < cols;
-      const float cb = (a.bias && cin) ? load_bias(a.bias, a.bias_dt, c) : 0.f;
+      const float cb = cb_early;
       bool f = false;
       for (int b = 0; b < a.B; ++b) {
         const int t = b / 16, g2 = (b % 16) / 4, r = b % 4;
